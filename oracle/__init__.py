@@ -1,0 +1,167 @@
+"""CPU oracle for the DSA hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check in __graft_entry__ and the CPU-baseline leg of
+bench.py may import this package.  The product library never does, and the
+oracle never imports the product: the two share nothing except the seeded
+input generators in dsa_inputs.py.
+
+Thin ctypes/numpy wrappers around oracle/dsa_oracle.c (fp64 definitions of
+the THD metadata, indexer top-k, sparse MLA forward and backward).  bf16
+tensors are passed as their uint16 bit patterns.  See dsa_oracle.c for the
+page passages each function follows.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        L = C.CDLL(path)
+        i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+        u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+        f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+        f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+        L.oracle_thd_metadata.argtypes = [i32p, C.c_int32, C.c_int64, C.c_int32, i32p, i32p, i32p,
+                                          C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
+        L.oracle_thd_metadata.restype = C.c_int
+        L.oracle_indexer_score.argtypes = [u16p, u16p, f32p, C.c_int32, C.c_int32, C.c_int64,
+                                           C.c_int64]
+        L.oracle_indexer_score.restype = C.c_double
+        L.oracle_indexer_topk.argtypes = [u16p, u16p, f32p, i32p, C.c_int32, C.c_int64, C.c_int32,
+                                          C.c_int32, C.c_int32, C.c_int64, C.c_int64, i32p, i32p,
+                                          C.c_void_p]
+        L.oracle_indexer_topk.restype = C.c_int
+        L.oracle_sparse_mla_fwd.argtypes = [u16p, u16p, i32p, C.c_void_p, C.c_int64, C.c_int64,
+                                            C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
+                                            C.c_int64, C.c_int64, f64p, f64p]
+        L.oracle_sparse_mla_fwd.restype = C.c_int
+        L.oracle_sparse_mla_bwd.argtypes = [u16p, u16p, i32p, C.c_void_p, u16p, C.c_int64,
+                                            C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                            C.c_double, C.c_int64, C.c_int64, f64p, f64p]
+        L.oracle_sparse_mla_bwd.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _u16(x):
+    """Accept a torch bf16 tensor or a uint16 numpy array of bf16 bits."""
+    if hasattr(x, "dtype") and str(x.dtype) == "torch.bfloat16":
+        import torch  # noqa: F401
+        x = x.detach().to("cpu").contiguous().view(__import__("torch").int16).numpy()
+    x = np.ascontiguousarray(x)
+    return x.view(np.uint16)
+
+
+def _np(x, dtype):
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").numpy()
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its inputs (code {rc})")
+
+
+def thd_metadata(cu_seqlens, T: int, K: int):
+    cu = _np(cu_seqlens, np.int32)
+    B = cu.shape[0] - 1
+    ss = np.zeros(T, np.int32)
+    cl = np.zeros(T, np.int32)
+    tl = np.zeros(T, np.int32)
+    mx = C.c_int32(0)
+    ne = C.c_int32(0)
+    _check(lib().oracle_thd_metadata(cu, B, T, K, ss, cl, tl, C.byref(mx), C.byref(ne)),
+           "thd_metadata")
+    return dict(seq_start=ss, causal_len=cl, topk_length=tl, max_seqlen=mx.value,
+                all_rows_nonempty=bool(ne.value))
+
+
+def indexer_score(q_idx, k_idx, w, t: int, s: int) -> float:
+    q = _u16(q_idx)
+    k = _u16(k_idx)
+    wt = _np(w, np.float32)
+    T, H, D = q.shape
+    return lib().oracle_indexer_score(q.reshape(-1), k.reshape(-1), wt.reshape(-1), H, D, t, s)
+
+
+def indexer_topk(q_idx, k_idx, w, cu_seqlens, K: int, rows=None):
+    """Top-k for rows [r0, r1) (default all): (idx [n,K] int32, len [n] int32, kth [n] f64)."""
+    q = _u16(q_idx)
+    k = _u16(k_idx)
+    wt = _np(w, np.float32)
+    cu = _np(cu_seqlens, np.int32)
+    T, H, D = q.shape
+    r0, r1 = (0, T) if rows is None else rows
+    n = r1 - r0
+    idx = np.zeros((n, K), np.int32)
+    ln = np.zeros(n, np.int32)
+    kth = np.zeros(n, np.float64)
+    _check(lib().oracle_indexer_topk(q.reshape(-1), k.reshape(-1), wt.reshape(-1), cu,
+                                     cu.shape[0] - 1, T, H, D, K, r0, r1, idx, ln,
+                                     kth.ctypes.data), "indexer_topk")
+    return idx, ln, kth
+
+
+def _opt_i32(x):
+    if x is None:
+        return None, None
+    a = _np(x, np.int32)
+    return a, a.ctypes.data
+
+
+def sparse_mla_fwd(q, kv, idx, topk_length, scale: float, d_v: int, rows=None):
+    """Returns (out [n,H,Dv] f64, lse [n,H] f64) for query rows [r0, r1)."""
+    qa = _u16(q)
+    kva = _u16(kv).reshape(kv.shape[0], -1)
+    ia = _np(idx, np.int32).reshape(qa.shape[0], -1)
+    tl, tlp = _opt_i32(topk_length)
+    Tq, H, Dqk = qa.shape
+    Tkv = kva.shape[0]
+    K = ia.shape[1]
+    r0, r1 = (0, Tq) if rows is None else rows
+    out = np.zeros((r1 - r0, H, d_v), np.float64)
+    lse = np.zeros((r1 - r0, H), np.float64)
+    _check(lib().oracle_sparse_mla_fwd(qa.reshape(-1), kva.reshape(-1), ia.reshape(-1), tlp, Tq,
+                                       Tkv, H, Dqk, d_v, K, float(scale), r0, r1, out, lse),
+           "sparse_mla_fwd")
+    del tl
+    return out, lse
+
+
+def sparse_mla_bwd(q, kv, idx, topk_length, dout, scale: float, rows=None, dkv=None):
+    """Returns (dq [n,H,Dqk] f64, dkv [T_kv,Dqk] f64) for query rows [r0, r1).
+
+    dkv accumulates the contributions of the given rows only (pass ``dkv`` to
+    keep accumulating into an existing buffer)."""
+    qa = _u16(q)
+    kva = _u16(kv).reshape(kv.shape[0], -1)
+    ia = _np(idx, np.int32).reshape(qa.shape[0], -1)
+    da = _u16(dout)
+    tl, tlp = _opt_i32(topk_length)
+    Tq, H, Dqk = qa.shape
+    Tkv = kva.shape[0]
+    K = ia.shape[1]
+    Dv = da.shape[2]
+    r0, r1 = (0, Tq) if rows is None else rows
+    dq = np.zeros((r1 - r0, H, Dqk), np.float64)
+    if dkv is None:
+        dkv = np.zeros((Tkv, Dqk), np.float64)
+    _check(lib().oracle_sparse_mla_bwd(qa.reshape(-1), kva.reshape(-1), ia.reshape(-1), tlp,
+                                       da.reshape(-1), Tq, Tkv, H, Dqk, Dv, K, float(scale), r0,
+                                       r1, dq, dkv), "sparse_mla_bwd")
+    del tl
+    return dq, dkv

@@ -1,0 +1,347 @@
+/*
+ * dsa_oracle.c -- plain CPU oracle for the DeepSeek Sparse Attention hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; it exists so that tests/, the smoke check and the CPU
+ * baseline leg of the benchmark can check the HIP kernels against an
+ * obviously correct definition.  It shares no code, header or table with the
+ * HIP library.
+ *
+ * Every quantity is computed from its definition, in double precision, with
+ * no blocking, fusion or reordering: bf16 inputs are widened exactly to
+ * double, products and sums are formed in double, and results are returned
+ * in double.  Rows are independent, so the only parallelism is an OpenMP
+ * loop over query rows.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [GLM52]  NVIDIA "Accelerating GLM-5.2 Long-Context Training with cuDNN
+ *            Fused DSA Kernels and THD-Packed Context Parallelism using
+ *            Megatron Bridge", sections "How DSA works" and "Why DSA needs
+ *            fused kernels".
+ *   [API]    NeMo AutoModel API reference, module
+ *            nemo_automodel.components.models.glm_moe_dsa.kernels.cudnn_dsa:
+ *            entries prepare_cudnn_dsa_packed_metadata, cudnn_indexer_topk,
+ *            _compact_and_sort_indices, cudnn_sparse_attention,
+ *            _CudnnSparseAttention.forward / .backward.
+ *   [PR2388] SkyRL PR 2388 (GLM-5.3-Flash NoPE sparse MLA), "Why", "Change".
+ *   [PR2423] SkyRL PR 2423 (query-chunked sparse attention), "Summary".
+ *
+ * The indexer score itself is not written out on the pages ([GLM52] only says
+ * the indexer "scores the query-key relevance" per query); the reading taken is
+ *     I(t,s) = sum_h w[t,h] * max(0, sum_d q[t,h,d] * k[s,d]),
+ * with the head weights used exactly as handed over ([API] cudnn_indexer_topk,
+ * head_weights: the caller owns the 1/sqrt(H) and 1/sqrt(D) scaling).
+ *
+ * Parity status: every function below is pinned by tests in tests/ against
+ * brute force, closed forms, library routines or finite differences.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL -1
+#define ORACLE_ENOMEM -2
+
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* THD metadata ([API] prepare_cudnn_dsa_packed_metadata: per-query starts   */
+/* and real causal lengths from cumulative sequence offsets).                */
+/* ------------------------------------------------------------------------ */
+
+/* Validates cu_seqlens (starts at 0, non-decreasing, ends at T) and returns
+ * for every token t of sequence b: seq_start[t] = cu[b], causal_len[t] =
+ * t - cu[b] + 1 (keys s with cu[b] <= s <= t, diagonal included) and
+ * topk_len[t] = min(K, causal_len[t]).  *max_seqlen is the longest sequence and
+ * *all_rows_nonempty is 1 when every row has at least one key (always true
+ * for a causal row that includes itself; 1 also for T == 0). */
+int oracle_thd_metadata(const int32_t *cu, int32_t B, int64_t T, int32_t K,
+                        int32_t *seq_start, int32_t *causal_len, int32_t *topk_len,
+                        int32_t *max_seqlen, int32_t *all_rows_nonempty) {
+  if (B < 1 || T < 0 || K < 1) return ORACLE_EINVAL;
+  if (cu[0] != 0 || (int64_t)cu[B] != T) return ORACLE_EINVAL;
+  int32_t mx = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (cu[b + 1] < cu[b]) return ORACLE_EINVAL;
+    int32_t len = cu[b + 1] - cu[b];
+    if (len > mx) mx = len;
+    for (int32_t t = cu[b]; t < cu[b + 1]; ++t) {
+      seq_start[t] = cu[b];
+      causal_len[t] = t - cu[b] + 1;
+      topk_len[t] = causal_len[t] < K ? causal_len[t] : K;
+    }
+  }
+  *max_seqlen = mx;
+  *all_rows_nonempty = 1;
+  for (int64_t t = 0; t < T; ++t)
+    if (causal_len[t] <= 0) *all_rows_nonempty = 0;
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Lightning indexer score and per-row top-k ([GLM52] "How DSA works";       */
+/* [API] cudnn_indexer_topk, _compact_and_sort_indices).                      */
+/* ------------------------------------------------------------------------ */
+
+/* One score I(t,s) in double. */
+double oracle_indexer_score(const uint16_t *q, const uint16_t *k, const float *w,
+                            int32_t H, int32_t D, int64_t t, int64_t s) {
+  double total = 0.0;
+  for (int32_t h = 0; h < H; ++h) {
+    double dot = 0.0;
+    const uint16_t *qr = q + ((size_t)t * H + h) * D;
+    const uint16_t *kr = k + (size_t)s * D;
+    for (int32_t d = 0; d < D; ++d) dot += bf16_to_double(qr[d]) * bf16_to_double(kr[d]);
+    double relu = dot > 0.0 ? dot : 0.0;
+    total += (double)w[(size_t)t * H + h] * relu;
+  }
+  return total + 0.0; /* folds a -0.0 sum to +0.0 */
+}
+
+typedef struct {
+  double score;
+  int32_t pos;
+} scored_key;
+
+/* Ranking: higher score first; equal scores -> lower key position first. */
+static int by_rank(const void *a, const void *b) {
+  const scored_key *x = (const scored_key *)a, *y = (const scored_key *)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+static int by_pos(const void *a, const void *b) {
+  const scored_key *x = (const scored_key *)a, *y = (const scored_key *)b;
+  return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+/* For query rows [row_begin, row_end): score every causal key of the row's
+ * own sequence, keep the n = min(K, L_t) best (ties -> lower position), and
+ * write them as a compact ascending prefix of global key positions followed
+ * by -1 ([API] _compact_and_sort_indices "canonicalize ... return valid
+ * lengths").  idx_out is [(row_end-row_begin) x K], len_out is
+ * [row_end-row_begin].  kth_score (nullable) receives the n-th best score of
+ * each row (the selection threshold). */
+int oracle_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
+                        const int32_t *cu, int32_t B, int64_t T, int32_t H, int32_t D,
+                        int32_t K, int64_t row_begin, int64_t row_end, int32_t *idx_out,
+                        int32_t *len_out, double *kth_score) {
+  if (B < 1 || H < 1 || D < 1 || K < 1 || row_begin < 0 || row_end > T || row_begin > row_end)
+    return ORACLE_EINVAL;
+  if (cu[0] != 0 || (int64_t)cu[B] != T) return ORACLE_EINVAL;
+  for (int32_t b = 0; b < B; ++b)
+    if (cu[b + 1] < cu[b]) return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = row_begin; t < row_end; ++t) {
+    int32_t b = 0;
+    while (!(cu[b] <= t && t < cu[b + 1])) ++b;
+    int64_t start = cu[b];
+    int64_t L = t - start + 1;
+    scored_key *keys = (scored_key *)malloc(sizeof(scored_key) * (size_t)L);
+    if (!keys) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+      continue;
+    }
+    for (int64_t s = start; s <= t; ++s) {
+      keys[s - start].score = oracle_indexer_score(q, k, w, H, D, t, s);
+      keys[s - start].pos = (int32_t)s;
+    }
+    qsort(keys, (size_t)L, sizeof(scored_key), by_rank);
+    int64_t n = L < K ? L : K;
+    if (kth_score) kth_score[t - row_begin] = keys[n - 1].score;
+    qsort(keys, (size_t)n, sizeof(scored_key), by_pos);
+    int32_t *row = idx_out + (size_t)(t - row_begin) * K;
+    for (int64_t j = 0; j < K; ++j) row[j] = j < n ? keys[j].pos : -1;
+    len_out[t - row_begin] = (int32_t)n;
+    free(keys);
+  }
+  return err;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Absorbed sparse MLA ([GLM52] "Why DSA needs fused kernels": all heads of  */
+/* a query share one top-k set, MQA-style; [API] cudnn_sparse_attention:     */
+/* q [T_q,H,576] = 512 latent + 64 rope, kv_latent [T_kv,1,576], values are   */
+/* the first 512 channels, -1 slots are invalid, topk_length limits the row   */
+/* to a valid prefix, softmax_scale is applied unchanged; [PR2388] NoPE      */
+/* width 512 with value = the same 512 channels).                            */
+/* ------------------------------------------------------------------------ */
+
+/* Valid slots of one row: j < (topk_length ? topk_length[t] : K) and
+ * idx[t,j] != -1.  Returns the count, or -1 if an index is out of range. */
+static int64_t row_slots(const int32_t *idx, const int32_t *topk_length, int64_t t, int32_t K,
+                         int64_t T_kv, int32_t *slots) {
+  int64_t lim = K;
+  if (topk_length) {
+    lim = topk_length[t];
+    if (lim < 0 || lim > K) return -1;
+  }
+  int64_t n = 0;
+  for (int64_t j = 0; j < lim; ++j) {
+    int32_t s = idx[(size_t)t * K + j];
+    if (s == -1) continue;
+    if (s < 0 || s >= T_kv) return -1;
+    slots[n++] = s;
+  }
+  return n;
+}
+
+/* Softmax statistics and output of one (t,h): logits z_j = scale *
+ * <q[t,h,:Dqk], kv[s_j,:Dqk]>, lse = log sum_j exp(z_j) (natural log), and
+ * out = sum_j exp(z_j - lse) * kv[s_j,:Dv].  An empty row gives out = 0 and
+ * lse = -inf.  z receives the logits. */
+static void attend_one(const uint16_t *q, const uint16_t *kv, const int32_t *slots, int64_t n,
+                       int64_t t, int32_t h, int32_t H, int32_t Dqk, int32_t Dv, double scale,
+                       double *z, double *out, double *lse) {
+  const uint16_t *qr = q + ((size_t)t * H + h) * Dqk;
+  for (int32_t c = 0; c < Dv; ++c) out[c] = 0.0;
+  if (n == 0) {
+    *lse = -INFINITY;
+    return;
+  }
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j) {
+    const uint16_t *kr = kv + (size_t)slots[j] * Dqk;
+    double dot = 0.0;
+    for (int32_t d = 0; d < Dqk; ++d) dot += bf16_to_double(qr[d]) * bf16_to_double(kr[d]);
+    z[j] = scale * dot;
+    if (z[j] > m) m = z[j];
+  }
+  double sum = 0.0;
+  for (int64_t j = 0; j < n; ++j) sum += exp(z[j] - m);
+  *lse = m + log(sum);
+  for (int64_t j = 0; j < n; ++j) {
+    double p = exp(z[j] - *lse);
+    const uint16_t *kr = kv + (size_t)slots[j] * Dqk;
+    for (int32_t c = 0; c < Dv; ++c) out[c] += p * bf16_to_double(kr[c]);
+  }
+}
+
+/* Forward for query rows [row_begin, row_end).  out is [(rows) x H x Dv],
+ * lse is [(rows) x H], both double, row-relative. */
+int oracle_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                          const int32_t *topk_length, int64_t T_q, int64_t T_kv, int32_t H,
+                          int32_t Dqk, int32_t Dv, int32_t K, double scale, int64_t row_begin,
+                          int64_t row_end, double *out, double *lse) {
+  if (H < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk || K < 1 || row_begin < 0 || row_end > T_q ||
+      row_begin > row_end)
+    return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    int32_t *slots = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    double *z = (double *)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t t = row_begin; t < row_end; ++t) {
+      if (!slots || !z) {
+#pragma omp atomic write
+        err = ORACLE_ENOMEM;
+        continue;
+      }
+      int64_t n = row_slots(idx, topk_length, t, K, T_kv, slots);
+      if (n < 0) {
+#pragma omp atomic write
+        err = ORACLE_EINVAL;
+        continue;
+      }
+      for (int32_t h = 0; h < H; ++h) {
+        size_t r = (size_t)(t - row_begin) * H + h;
+        attend_one(q, kv, slots, n, t, h, H, Dqk, Dv, scale, z, out + r * Dv, lse + r);
+      }
+    }
+    free(slots);
+    free(z);
+  }
+  return err;
+}
+
+/* Backward for query rows [row_begin, row_end) ([API] _CudnnSparseAttention
+ * .backward: gradients for the query [T_q,H,576] and the gathered latent
+ * rows; [PR2423] "Summary": key gradients of independent query chunks sum).
+ *
+ * The row's own forward is recomputed here in double.  With P_j =
+ * exp(z_j - lse), dP_j = <dO[t,h], kv[s_j,:Dv]>, Delta = <dO[t,h], O[t,h]>,
+ * dZ_j = P_j (dP_j - Delta):
+ *   dq[t,h,:Dqk]   = scale * sum_j dZ_j kv[s_j,:Dqk]
+ *   dkv[s_j,:Dqk] += scale * dZ_j q[t,h,:Dqk]      (summed over h and t)
+ *   dkv[s_j,:Dv]  += P_j dO[t,h,:]
+ * dq is [(rows) x H x Dqk] (row-relative); dkv is the full [T_kv x Dqk]
+ * buffer and is accumulated into (the caller zeroes it).  dkv of a key row is
+ * complete only when every query row that selects it is inside the range. */
+int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                          const int32_t *topk_length, const uint16_t *dout, int64_t T_q,
+                          int64_t T_kv, int32_t H, int32_t Dqk, int32_t Dv, int32_t K,
+                          double scale, int64_t row_begin, int64_t row_end, double *dq,
+                          double *dkv) {
+  if (H < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk || K < 1 || row_begin < 0 || row_end > T_q ||
+      row_begin > row_end)
+    return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    int32_t *slots = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    double *z = (double *)malloc(sizeof(double) * (size_t)K);
+    double *o = (double *)malloc(sizeof(double) * (size_t)Dv);
+    /* this row's contribution to dkv, one Dqk vector per valid slot */
+    double *contrib = (double *)malloc(sizeof(double) * (size_t)K * Dqk);
+    /* rows add their contributions into dkv in row order, so dkv does not
+     * depend on the thread count or scheduling */
+#pragma omp for schedule(dynamic, 1) ordered
+    for (int64_t t = row_begin; t < row_end; ++t) {
+      int64_t n = (!slots || !z || !o || !contrib)
+                      ? -2 : row_slots(idx, topk_length, t, K, T_kv, slots);
+      if (n < 0) {
+#pragma omp atomic write
+        err = n == -2 ? ORACLE_ENOMEM : ORACLE_EINVAL;
+#pragma omp ordered
+        {}
+        continue;
+      }
+      memset(contrib, 0, sizeof(double) * (size_t)n * Dqk);
+      for (int32_t h = 0; h < H; ++h) {
+        double lse;
+        attend_one(q, kv, slots, n, t, h, H, Dqk, Dv, scale, z, o, &lse);
+        const uint16_t *qr = q + ((size_t)t * H + h) * Dqk;
+        const uint16_t *dor = dout + ((size_t)t * H + h) * Dv;
+        double *dqr = dq + ((size_t)(t - row_begin) * H + h) * Dqk;
+        for (int32_t d = 0; d < Dqk; ++d) dqr[d] = 0.0;
+        double delta = 0.0;
+        for (int32_t c = 0; c < Dv; ++c) delta += bf16_to_double(dor[c]) * o[c];
+        for (int64_t j = 0; j < n; ++j) {
+          const uint16_t *kr = kv + (size_t)slots[j] * Dqk;
+          double p = exp(z[j] - lse);
+          double dp = 0.0;
+          for (int32_t c = 0; c < Dv; ++c) dp += bf16_to_double(dor[c]) * bf16_to_double(kr[c]);
+          double dz = p * (dp - delta);
+          double *cj = contrib + (size_t)j * Dqk;
+          for (int32_t d = 0; d < Dqk; ++d) {
+            dqr[d] += scale * dz * bf16_to_double(kr[d]);
+            cj[d] += scale * dz * bf16_to_double(qr[d]);
+          }
+          for (int32_t c = 0; c < Dv; ++c) cj[c] += p * bf16_to_double(dor[c]);
+        }
+      }
+#pragma omp ordered
+      for (int64_t j = 0; j < n; ++j) {
+        double *dst = dkv + (size_t)slots[j] * Dqk;
+        const double *cj = contrib + (size_t)j * Dqk;
+        for (int32_t d = 0; d < Dqk; ++d) dst[d] += cj[d];
+      }
+    }
+    free(slots);
+    free(z);
+    free(o);
+    free(contrib);
+  }
+  return err;
+}

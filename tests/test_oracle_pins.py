@@ -1,0 +1,355 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+CPU only.  Each test checks oracle/ against something other than itself:
+hand-derived worked examples (tests/golden), brute force over the full score
+matrix, closed forms, a library routine (torch SDPA + autograd in float64),
+central finite differences, and the invariances the pages state (-1 slots are
+masked, zero-padding q/k from 512 to 576 channels is exact, -1 padding of the
+top-k width is exact, query chunks are independent and their key gradients
+sum).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as gen
+import oracle
+from tests import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16(a):
+    return torch.tensor(a, dtype=torch.float32).to(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------
+# metadata
+# ----------------------------------------------------------------------------
+
+def test_metadata_thd_cfg3():
+    w = gen.workload(3)
+    md = oracle.thd_metadata(np.array(w.cu_seqlens, np.int32), w.T, 2048)
+    cu = w.cu_seqlens
+    assert md["max_seqlen"] == 16384
+    assert md["all_rows_nonempty"]
+    for b in range(4):
+        for t in (cu[b], cu[b] + 1, cu[b + 1] - 1):
+            assert md["seq_start"][t] == cu[b]
+            assert md["causal_len"][t] == t - cu[b] + 1
+            assert md["topk_length"][t] == min(2048, t - cu[b] + 1)
+    # sum of causal lengths = sum of triangular numbers of the sequence lengths
+    lens = np.diff(cu)
+    assert md["causal_len"].astype(np.int64).sum() == int((lens * (lens + 1) // 2).sum())
+
+
+@pytest.mark.parametrize("cu", [[1, 4], [0, 3, 2, 4], [0, 2, 5]])
+def test_metadata_rejects_bad_offsets(cu):
+    with pytest.raises(ValueError):
+        oracle.thd_metadata(np.array(cu, np.int32), 4, 8)
+
+
+# ----------------------------------------------------------------------------
+# indexer
+# ----------------------------------------------------------------------------
+
+def test_indexer_golden():
+    g = json.load(open(os.path.join(GOLDEN, "indexer_tiny.json")))
+    q, k = _bf16(g["q"]), _bf16(g["k"])
+    w = torch.tensor(g["w"], dtype=torch.float32)
+    cu = np.array(g["cu_seqlens"], np.int32)
+    idx, ln, _ = oracle.indexer_topk(q, k, w, cu, g["K"])
+    assert idx.tolist() == g["expect_idx"]
+    assert ln.tolist() == g["expect_len"]
+    for t, row in g["expect_scores"].items():
+        for s, v in row.items():
+            assert oracle.indexer_score(q, k, w, int(t), int(s)) == v
+
+
+@pytest.mark.parametrize("int_inputs", [True, False])
+@pytest.mark.parametrize("cu,K,H,D", [([0, 97], 16, 4, 64), ([0, 40, 41, 130], 24, 8, 32),
+                                      ([0, 64, 200], 64, 4, 16)])
+def test_indexer_matches_brute_force(int_inputs, cu, K, H, D):
+    T = cu[-1]
+    g = torch.Generator().manual_seed(1234 + T + K)
+    if int_inputs:
+        q = torch.randint(-4, 5, (T, H, D), generator=g).to(torch.bfloat16)
+        k = torch.randint(-4, 5, (T, D), generator=g).to(torch.bfloat16)
+        w = torch.tensor([0.5, 1.0, 2.0])[torch.randint(0, 3, (T, H), generator=g)]
+    else:
+        q = torch.randn((T, H, D), generator=g).to(torch.bfloat16)
+        k = torch.randn((T, D), generator=g).to(torch.bfloat16)
+        w = torch.randn((T, H), generator=g) / 8
+    cua = np.array(cu, np.int32)
+    idx, ln, kth = oracle.indexer_topk(q, k, w, cua, K)
+    scores = pins.brute_indexer_scores(q, k, w, cua)
+    bidx, bln = pins.brute_topk(scores, K)
+    np.testing.assert_array_equal(idx, bidx)
+    np.testing.assert_array_equal(ln, bln)
+    # threshold = n-th best score of the row
+    for t in range(T):
+        row = np.sort(scores[t][np.isfinite(scores[t])])[::-1]
+        assert kth[t] == pytest.approx(row[ln[t] - 1], rel=1e-12, abs=1e-12)
+
+
+def test_indexer_short_rows_closed_form():
+    """Rows with at most K causal keys return exactly their whole prefix."""
+    w_ = gen.workload(1)
+    inp = gen.indexer_inputs(1)
+    idx, ln, _ = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"],
+                                     inp["cu_seqlens"], w_.topk, rows=(0, 80))
+    for t in range(80):
+        n = min(64, t + 1)
+        assert ln[t] == n
+        if t + 1 <= 64:
+            assert idx[t, :t + 1].tolist() == list(range(t + 1))
+            assert (idx[t, t + 1:] == -1).all()
+
+
+def test_indexer_head_permutation_invariance():
+    inp = gen.indexer_inputs(1)
+    perm = torch.randperm(4, generator=torch.Generator().manual_seed(7))
+    a = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"], inp["cu_seqlens"], 64,
+                            rows=(100, 160))
+    b = oracle.indexer_topk(inp["q_idx"][:, perm].contiguous(), inp["k_idx"],
+                            inp["w"][:, perm].contiguous(), inp["cu_seqlens"], 64,
+                            rows=(100, 160))
+    np.testing.assert_array_equal(a[0], b[0])
+
+
+def test_indexer_structure_float_thd():
+    cu = [0, 50, 300, 330]
+    inp = gen.indexer_inputs(3, cu_seqlens=cu)
+    K = 96
+    idx, ln, _ = oracle.indexer_topk(inp["q_idx"][:, :8].contiguous(), inp["k_idx"][:, :32]
+                                     .contiguous(), inp["w"][:, :8].contiguous(),
+                                     inp["cu_seqlens"], K)
+    start = pins.segment_of(np.array(cu), cu[-1])
+    for t in range(cu[-1]):
+        n = ln[t]
+        assert n == min(K, t - start[t] + 1)
+        row = idx[t]
+        assert (row[n:] == -1).all()
+        v = row[:n]
+        assert (np.diff(v) > 0).all()
+        assert v.min() >= start[t] and v.max() <= t
+
+
+# ----------------------------------------------------------------------------
+# sparse MLA forward
+# ----------------------------------------------------------------------------
+
+def test_attention_golden():
+    g = json.load(open(os.path.join(GOLDEN, "attention_tiny.json")))
+    q, kv, dout = _bf16(g["q"]), _bf16(g["kv"]), _bf16(g["dout"])
+    idx = np.array(g["idx"], np.int32)
+    out, lse = oracle.sparse_mla_fwd(q, kv, idx, None, g["scale"], g["d_v"])
+    np.testing.assert_allclose(out, g["expect_out"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, g["expect_lse"], rtol=0, atol=1e-15)
+    dq, dkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, g["scale"])
+    np.testing.assert_allclose(dq, g["expect_dq"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(dkv, g["expect_dkv"], rtol=0, atol=1e-15)
+
+
+def _all_causal_indices(cu, K):
+    T = cu[-1]
+    start = pins.segment_of(np.array(cu), T)
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        L = t - start[t] + 1
+        assert L <= K
+        idx[t, :L] = np.arange(start[t], t + 1)
+    return idx
+
+
+@pytest.mark.parametrize("cu,H,Dqk,Dv", [([0, 48], 4, 576, 512), ([0, 20, 33, 64], 3, 64, 48),
+                                         ([0, 40], 2, 512, 512)])
+def test_fwd_bwd_equals_dense_when_k_covers_causal(cu, H, Dqk, Dv):
+    """Sparse over every causal key == dense block-causal attention (SDPA, autograd)."""
+    T = cu[-1]
+    g = torch.Generator().manual_seed(99 + T)
+    q = (torch.randn((T, H, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    kv = (torch.randn((T, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    dout = torch.randn((T, H, Dv), generator=g).to(torch.bfloat16)
+    scale = 1 / math.sqrt(Dqk)
+    K = max(np.diff(cu)) + 3          # extra -1 slots on every row
+    idx = _all_causal_indices(cu, K)
+    out, lse = oracle.sparse_mla_fwd(q, kv, idx, None, scale, Dv)
+    ref = pins.dense_attention(q, kv, cu, scale, Dv, dout=dout)
+    np.testing.assert_allclose(out, ref["out"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, ref["lse"], rtol=1e-12, atol=1e-12)
+    dq, dkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, scale)
+    np.testing.assert_allclose(dq, ref["dq"], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dkv, ref["dkv"], rtol=1e-10, atol=1e-11)
+
+
+def test_fwd_single_slot_closed_form():
+    """First token of a sequence: O = kv[s, :Dv] and LSE = scale * q.kv[s]."""
+    inp = gen.attention_inputs(1, cu_seqlens=[0, 8])
+    q, kv = inp["q"], inp["kv"]
+    idx = np.full((8, 5), -1, np.int32)
+    idx[:, 2] = np.arange(8)[::-1]          # one valid slot per row, in the middle
+    out, lse = oracle.sparse_mla_fwd(q, kv, idx, None, inp["scale"], 512)
+    qd, kvd = pins.bf16_to_f64(q), pins.bf16_to_f64(kv)
+    for t in range(8):
+        s = 7 - t
+        np.testing.assert_array_equal(out[t], np.broadcast_to(kvd[s, :512], out[t].shape))
+        np.testing.assert_allclose(lse[t], inp["scale"] * qd[t] @ kvd[s], rtol=1e-13, atol=1e-14)
+
+
+def _rand_indices(T, Tkv, n_valid, K, g):
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        idx[t, :n_valid] = g.choice(Tkv, size=n_valid, replace=False)
+    return idx
+
+
+def test_fwd_minus_one_slots_and_order_invariance():
+    rng = np.random.default_rng(5)
+    inp = gen.attention_inputs(1, cu_seqlens=[0, 64], heads=4)
+    q, kv = inp["q"], inp["kv"]
+    idx = _rand_indices(64, 64, 20, 20, rng)
+    base_o, base_l = oracle.sparse_mla_fwd(q, kv, idx, None, inp["scale"], 512)
+    # scatter -1 slots among the valid ones and permute the valid ones
+    wide = np.full((64, 37), -1, np.int32)
+    for t in range(64):
+        pos = np.sort(rng.choice(37, size=20, replace=False))
+        wide[t, pos] = rng.permutation(idx[t])
+    o2, l2 = oracle.sparse_mla_fwd(q, kv, wide, None, inp["scale"], 512)
+    np.testing.assert_allclose(o2, base_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, base_l, rtol=1e-13, atol=1e-13)
+    # topk_length: only the prefix is read, garbage after it is ignored
+    garbage = idx.copy()
+    garbage = np.concatenate([garbage, rng.integers(0, 64, (64, 9)).astype(np.int32)], axis=1)
+    lens = np.full(64, 20, np.int32)
+    o3, l3 = oracle.sparse_mla_fwd(q, kv, garbage, lens, inp["scale"], 512)
+    np.testing.assert_array_equal(o3, base_o)
+    np.testing.assert_array_equal(l3, base_l)
+
+
+def test_empty_row_and_bad_index():
+    inp = gen.attention_inputs(1, cu_seqlens=[0, 4], heads=2)
+    idx = np.full((4, 3), -1, np.int32)
+    idx[1, 0] = 0
+    out, lse = oracle.sparse_mla_fwd(inp["q"], inp["kv"], idx, None, inp["scale"], 512)
+    assert np.isneginf(lse[0]).all() and (out[0] == 0).all()
+    dq, dkv = oracle.sparse_mla_bwd(inp["q"], inp["kv"], idx, None, inp["dout"], inp["scale"])
+    assert (dq[0] == 0).all() and (dq[2] == 0).all()
+    assert (dkv[1:] == 0).all()
+    idx[2, 1] = 4                      # out of range
+    with pytest.raises(ValueError):
+        oracle.sparse_mla_fwd(inp["q"], inp["kv"], idx, None, inp["scale"], 512)
+
+
+def test_nope_zero_padding_and_topk_padding_are_exact():
+    """SkyRL PR 2388 'Change': q/k zero-padded 512->576 and -1 padding of the top-k width."""
+    T = 48
+    inp = gen.attention_inputs(4, cu_seqlens=[0, T])
+    q, kv, dout = inp["q"], inp["kv"], inp["dout"]
+    K = 2051 if T > 2051 else 11
+    idx = gen.kpool_indices(T, topk=K, tail=3)
+    o, l = oracle.sparse_mla_fwd(q, kv, idx, None, inp["scale"], 512)
+    qp = torch.cat([q, torch.zeros(T, q.shape[1], 64, dtype=q.dtype)], dim=2)
+    kvp = torch.cat([kv, torch.zeros(T, 64, dtype=kv.dtype)], dim=1)
+    pad = (-K) % 64
+    idxp = torch.cat([idx, torch.full((T, pad), -1, dtype=torch.int32)], dim=1)
+    op, lp = oracle.sparse_mla_fwd(qp, kvp, idxp, None, inp["scale"], 512)
+    np.testing.assert_array_equal(op, o)
+    np.testing.assert_array_equal(lp, l)
+    dq, dkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, inp["scale"])
+    dqp, dkvp = oracle.sparse_mla_bwd(qp, kvp, idxp, None, dout, inp["scale"])
+    np.testing.assert_array_equal(dqp[..., :512], dq)
+    np.testing.assert_array_equal(dkvp[:, :512], dkv)
+    assert (dqp[..., 512:] == 0).all() and (dkvp[:, 512:] == 0).all()
+
+
+def test_query_chunks_are_independent_and_key_grads_sum():
+    """SkyRL PR 2423 'Summary': chunked == one-shot; key grads of the chunks sum."""
+    T = 70
+    inp = gen.attention_inputs(4, cu_seqlens=[0, T])
+    idx = gen.kpool_indices(T, topk=19, tail=3)
+    q, kv, dout, sc = inp["q"], inp["kv"], inp["dout"], inp["scale"]
+    o, l = oracle.sparse_mla_fwd(q, kv, idx, None, sc, 512)
+    dq, dkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, sc)
+    dkv_c = np.zeros_like(dkv)
+    for r0, r1 in [(0, 32), (32, 64), (64, 70)]:
+        oc, lc = oracle.sparse_mla_fwd(q, kv, idx, None, sc, 512, rows=(r0, r1))
+        np.testing.assert_array_equal(oc, o[r0:r1])
+        np.testing.assert_array_equal(lc, l[r0:r1])
+        dqc, dkv_c = oracle.sparse_mla_bwd(q, kv, idx, None, dout, sc, rows=(r0, r1), dkv=dkv_c)
+        np.testing.assert_array_equal(dqc, dq[r0:r1])
+    np.testing.assert_allclose(dkv_c, dkv, rtol=1e-12, atol=1e-13)
+
+
+def test_bwd_central_finite_differences():
+    """d/dx of L = sum(dout * out) by central differences with Richardson extrapolation.
+
+    Inputs sit on a 1/8 grid in (-2, 2) so that x +- 2^-6 and x +- 2^-7 are exact
+    bfloat16 values; the oracle forward is evaluated at the perturbed inputs."""
+    rng = np.random.default_rng(11)
+    T, H, Dqk, Dv, K = 10, 2, 8, 4, 6
+    q = torch.tensor(rng.integers(-15, 16, (T, H, Dqk)) / 8.0).to(torch.bfloat16)
+    kv = torch.tensor(rng.integers(-15, 16, (T, Dqk)) / 8.0).to(torch.bfloat16)
+    dout = torch.tensor(rng.integers(-15, 16, (T, H, Dv)) / 8.0).to(torch.bfloat16)
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        n = min(t + 1, 4)
+        idx[t, rng.choice(K, n, replace=False)] = rng.choice(t + 1, n, replace=False)
+    sc = 0.5
+    dq, dkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, sc)
+    d64 = pins.bf16_to_f64(dout)
+
+    def loss(qx, kvx):
+        o, _ = oracle.sparse_mla_fwd(qx, kvx, idx, None, sc, Dv)
+        return float((o * d64).sum())
+
+    def fd(which, pos):
+        vals = []
+        for h in (2.0 ** -6, 2.0 ** -7):
+            res = []
+            for sgn in (1, -1):
+                qx, kvx = q.clone(), kv.clone()
+                tgt = qx if which == "q" else kvx
+                tgt[pos] = (tgt[pos].float() + sgn * h).to(torch.bfloat16)
+                assert float(tgt[pos]) == float((q if which == "q" else kv)[pos]) + sgn * h
+                res.append(loss(qx, kvx))
+            vals.append((res[0] - res[1]) / (2 * h))
+        return (4 * vals[1] - vals[0]) / 3
+
+    for pos in [(3, 1, 2), (9, 0, 7), (5, 1, 0)]:
+        assert fd("q", pos) == pytest.approx(dq[pos], rel=1e-5, abs=1e-7)
+    for pos in [(0, 0), (2, 3), (4, 6), (7, 1)]:
+        assert fd("kv", pos) == pytest.approx(dkv[pos], rel=1e-5, abs=1e-7)
+
+
+def test_bwd_logit_shift_gradient_vanishes():
+    """sum_j dZ_j = 0: shifting every logit of a row by the same amount changes nothing,
+    so the gradient along q[t,h] parallel to a direction that shifts all keys equally is 0.
+    With a constant extra channel c in every key, dL/dq[t,h,c] = scale*c*sum_j dZ_j = 0."""
+    T, H, D = 12, 3, 16
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn((T, H, D), generator=g).to(torch.bfloat16)
+    kv = torch.randn((T, D), generator=g).to(torch.bfloat16)
+    kv[:, D - 1] = 1.0                                  # constant key channel
+    dout = torch.randn((T, H, 8), generator=g).to(torch.bfloat16)
+    idx = np.array([[s if s <= t else -1 for s in range(T)] for t in range(T)], np.int32)
+    dq, _ = oracle.sparse_mla_bwd(q, kv, idx, None, dout, 0.25)
+    np.testing.assert_allclose(dq[..., D - 1], 0.0, atol=1e-14)
+
+
+def test_kpool_generator_structure():
+    T, K = 40, 11
+    idx = gen.kpool_indices(T, topk=K, tail=3).numpy()
+    for t in range(T):
+        row = idx[t]
+        if t + 1 <= K:
+            assert row[:t + 1].tolist() == list(range(t + 1)) and (row[t + 1:] == -1).all()
+        else:
+            assert row[-3:].tolist() == [t - 2, t - 1, t]
+            head = row[:-3]
+            assert (np.diff(head) > 0).all() and head.max() <= t - 3 and head.min() >= 0
