@@ -1,0 +1,284 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input: THD metadata,
+lightning indexer + top-k, sparse MLA forward, sparse MLA backward (delta, dq, dkv).
+
+Default workload: the packed THD batch of 32768 tokens (sequences of 1024, 3072, 12288 and
+16384 tokens), indexer 64 heads x 128 with k = 2048, attention H = 64 over 576-wide latent
+rows (values = first 512 channels).  Inputs are generated on the GPU before timing and stay
+resident in HBM.
+
+Prints one JSON line.  `value` is hot-path tokens per second (query tokens through indexer,
+forward and backward per second); `components` breaks it down per stage with algorithmic
+TFLOP/s and the fraction of the bf16 dense MFMA peak; `roofline` describes the kernel with the
+largest share of the step time, timed with HIP events recorded by the library around each of
+its kernel launches; `cpu_baseline` times the CPU oracle on a bounded row sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "sparse-MLA fwd/bwd TFLOP/s + indexer top-k tokens/s at T=32K,k=2048; % roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle sample")
+    return ap.parse_args()
+
+
+class KernelTimer:
+    """Arms dsa_record_kernel_events with a pool of HIP events (created through the HIP
+    runtime that torch already loaded)."""
+
+    def __init__(self, dsa_lib, n_slots: int):
+        self.hip = C.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.lib = dsa_lib
+
+        class Slot(C.Structure):
+            _fields_ = [("start", C.c_void_p), ("stop", C.c_void_p), ("name", C.c_char_p)]
+
+        self.slots = (Slot * n_slots)()
+        for s in self.slots:
+            a, b = C.c_void_p(), C.c_void_p()
+            assert self.hip.hipEventCreate(C.byref(a)) == 0
+            assert self.hip.hipEventCreate(C.byref(b)) == 0
+            s.start, s.stop = a, b
+        self.n = n_slots
+        self.used = C.c_int(0)
+        self.lib.dsa_record_kernel_events.argtypes = [C.c_void_p, C.c_int, C.POINTER(C.c_int)]
+
+    def arm(self):
+        assert self.lib.dsa_record_kernel_events(C.byref(self.slots), self.n,
+                                                 C.byref(self.used)) == 0
+
+    def disarm(self):
+        self.lib.dsa_record_kernel_events(None, 0, None)
+
+    def totals(self):
+        """{kernel name: [durations in ms]} for the recorded launches (after a sync)."""
+        out = {}
+        for i in range(self.used.value):
+            s = self.slots[i]
+            ms = C.c_float(0)
+            assert self.hip.hipEventElapsedTime(C.byref(ms), s.start, s.stop) == 0
+            out.setdefault(s.name.decode(), []).append(ms.value)
+        return out
+
+
+def workload_counts(md_host, cfg, H_i, D_i, K, H, Dqk, Dv, kpool=None):
+    """Algorithmic work of one step (see the module docstring of the pass)."""
+    import numpy as np
+    cu = np.array(cfg.cu_seqlens, np.int64)
+    lens = np.diff(cu)
+    # indexer: rows with L > K need every causal score; rows with L <= K are decided
+    # without scoring (they keep their whole prefix)
+    idx_pairs = 0
+    for L in lens:
+        if L > K:
+            idx_pairs += (L * (L + 1) // 2) - (K * (K + 1) // 2)
+    valid = md_host["total_valid"] if kpool is None else kpool
+    return dict(
+        idx_pairs=int(idx_pairs),
+        idx_flops=float(idx_pairs) * 2 * H_i * D_i,
+        valid=int(valid),
+        fwd_flops=float(valid) * 2 * H * (Dqk + Dv),
+        bwd_flops=float(valid) * 2 * H * (3 * Dqk + 2 * Dv),
+        bwd_dq_flops=float(valid) * 2 * H * (2 * Dqk + Dv),
+        bwd_dkv_flops=float(valid) * 2 * H * (Dqk + Dv),
+    )
+
+
+def cpu_baseline(inputs, counts, T, K, budget_s):
+    """Time the oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    import torch
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    q_idx = inputs["q_idx"].cpu()
+    k_idx = inputs["k_idx"].cpu()
+    w = inputs["w"].cpu()
+    cu = inputs["cu_seqlens"].cpu()
+    last = int(cu[-1]) - 1
+    # indexer sample: a few of the longest rows (the scoring cost is proportional to L)
+    n_idx_rows = max(1, threads // 2)
+    t0 = time.perf_counter()
+    oracle.indexer_topk(q_idx, k_idx, w, cu, K, rows=(last - n_idx_rows + 1, last + 1))
+    t_idx = time.perf_counter() - t0
+    L = last - int(cu[-2]) + 1
+    idx_rate = n_idx_rows * L * 2.0 * q_idx.shape[1] * q_idx.shape[2] / t_idx  # flop/s
+    # attention sample: rows with full K valid slots, forward then backward
+    rows = (last - threads + 1, last + 1)
+    sl = slice(rows[0], rows[1])
+    q = inputs["q"][sl].cpu()
+    idx = inputs["idx"][sl].cpu()
+    ln = inputs["len"][sl].cpu()
+    dout = inputs["dout"][sl].cpu()
+    kv = inputs["kv"].cpu()
+    nvalid = int(ln.sum())
+    H, Dqk = q.shape[1], q.shape[2]
+    t0 = time.perf_counter()
+    oracle.sparse_mla_fwd(q, kv, idx, ln, inputs["scale"], 512)
+    t_fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.sparse_mla_bwd(q, kv, idx, ln, dout, inputs["scale"])
+    t_bwd = time.perf_counter() - t0
+    fwd_rate = nvalid * 2.0 * H * (Dqk + 512) / t_fwd
+    bwd_rate = nvalid * 2.0 * H * (3 * Dqk + 2 * 512) / t_bwd
+    full_s = counts["idx_flops"] / idx_rate + counts["fwd_flops"] / fwd_rate + \
+        counts["bwd_flops"] / bwd_rate
+    return {
+        "value": T / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"fp64 oracle, {n_idx_rows} indexer rows of L={L} ({t_idx:.1f}s) and "
+                   f"{rows[1] - rows[0]} attention rows with {nvalid} valid slots, forward "
+                   f"({t_fwd:.1f}s) and backward ({t_bwd:.1f}s); per-stage flop rates "
+                   f"extrapolated to the whole step"),
+        "indexer_tflops": idx_rate / 1e12, "fwd_tflops": fwd_rate / 1e12,
+        "bwd_tflops": bwd_rate / 1e12,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by query rows; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import dsa_inputs as gen
+    import sparse_attention_12_amd as dsa
+
+    dev = "cuda"
+    cfg = gen.workload(args.config)
+    T, K = cfg.T, cfg.topk
+    torch.manual_seed(0)
+    cu = gen.cu_seqlens_tensor(cfg, dev)
+    has_indexer = cfg.idx_heads is not None
+    inputs = dict(cu_seqlens=cu, scale=cfg.scale)
+    if has_indexer:
+        inputs.update(gen.indexer_inputs(args.config, device=dev))
+    att = gen.attention_inputs(args.config, device=dev)
+    inputs.update(q=att["q"], kv=att["kv"], dout=att["dout"])
+    H, Dqk, Dv = cfg.heads, cfg.d_qk, cfg.d_v
+    idx_buf = torch.empty((T, K), dtype=torch.int32, device=dev)
+    len_buf = torch.empty((T,), dtype=torch.int32, device=dev)
+    out_buf = torch.empty((T, H, Dv), dtype=torch.bfloat16, device=dev)
+    lse_buf = torch.empty((T, H), dtype=torch.float32, device=dev)
+    dq_buf = torch.empty_like(att["q"])
+    dkv_buf = torch.empty((T, Dqk), dtype=torch.float32, device=dev)
+    ws = torch.empty(dsa.lib().dsa_sparse_mla_bwd_workspace_size(T, T, H, Dqk),
+                     dtype=torch.uint8, device=dev)
+    kpool_valid = None
+    if not has_indexer:
+        kp = gen.kpool_indices(T, topk=K, tail=cfg.kpool_tail, device=dev)
+        idx_buf.copy_(kp)
+        len_buf.copy_((kp >= 0).sum(1).to(torch.int32))
+        kpool_valid = int(len_buf.sum().item())
+        del kp
+
+    def step():
+        md = dsa.prepare_thd_metadata(cu, K, T=T)
+        if has_indexer:
+            dsa.indexer_topk(inputs["q_idx"], inputs["k_idx"], inputs["w"], md, K, idx=idx_buf,
+                             length=len_buf)
+        dsa.sparse_mla_fwd(att["q"], att["kv"], idx_buf, cfg.scale, len_buf, out=out_buf,
+                           lse=lse_buf)
+        dsa.sparse_mla_bwd(att["q"], att["kv"], idx_buf, out_buf, lse_buf, att["dout"],
+                           cfg.scale, len_buf, dkv=dkv_buf, dq=dq_buf, workspace=ws)
+        return md
+
+    for _ in range(args.warmup):
+        md = step()
+    torch.cuda.synchronize()
+    md_host = dict(total_valid=md.total_valid)
+    counts = workload_counts(md_host, cfg, cfg.idx_heads or 0, cfg.idx_dim or 0, K, H, Dqk, Dv,
+                             kpool_valid)
+
+    timer = KernelTimer(dsa.lib(), 16 * args.steps)
+    timer.arm()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timer.disarm()
+    per_kernel = timer.totals()
+
+    ms_step = elapsed * 1e3 / args.steps
+    value = T * args.steps / elapsed
+
+    def avg(name):
+        v = per_kernel.get(name, [])
+        return sum(v) / len(v) if v else float("nan")
+
+    t_idx = avg("indexer_topk")
+    t_fwd = avg("sparse_mla_fwd")
+    t_bwd = sum(avg(n) for n in ("dkv_zero", "sparse_mla_bwd_delta", "sparse_mla_bwd_dq",
+                                 "sparse_mla_bwd_dkv") if n in per_kernel)
+    comp = {
+        "fwd": {"ms": t_fwd, "tflops": counts["fwd_flops"] / t_fwd / 1e9,
+                "frac_mfma_peak": counts["fwd_flops"] / t_fwd / 1e9 / PEAK_BF16_TFLOPS},
+        "bwd": {"ms": t_bwd, "tflops": counts["bwd_flops"] / t_bwd / 1e9,
+                "frac_mfma_peak": counts["bwd_flops"] / t_bwd / 1e9 / PEAK_BF16_TFLOPS},
+    }
+    if has_indexer:
+        comp["indexer"] = {"ms": t_idx, "tokens_per_s": T / (t_idx * 1e-3),
+                           "tflops": counts["idx_flops"] / t_idx / 1e9,
+                           "frac_mfma_peak": counts["idx_flops"] / t_idx / 1e9 / PEAK_BF16_TFLOPS}
+    kernels = {n: {"avg_ms": sum(v) / len(v), "launches": len(v)} for n, v in per_kernel.items()}
+
+    work = {"indexer_topk": counts["idx_flops"], "sparse_mla_fwd": counts["fwd_flops"],
+            "sparse_mla_bwd_dq": counts["bwd_dq_flops"],
+            "sparse_mla_bwd_dkv": counts["bwd_dkv_flops"]}
+    dom = max((n for n in work if n in per_kernel), key=lambda n: sum(per_kernel[n]))
+    achieved = work[dom] / avg(dom) / 1e9
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "cu_seqlens": list(cfg.cu_seqlens),
+                   "indexer": (f"{cfg.idx_heads}x{cfg.idx_dim}" if has_indexer else None),
+                   "topk": K, "heads": H, "d_qk": Dqk, "d_v": Dv, "parallelism": "none"},
+        "components": comp, "kernels": kernels, "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        inputs.update(idx=idx_buf, len=len_buf)
+        try:
+            res["cpu_baseline"] = cpu_baseline(inputs, counts, T, K, args.cpu_seconds)
+        except Exception as e:  # the GPU figure stands on its own
+            res["cpu_baseline"] = {"error": repr(e)}
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * dsa.h -- C ABI of libdsa: the DeepSeek Sparse Attention (DSA) hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Two stages:
+ *   1. the lightning indexer, which scores every causal key of each query and
+ *      keeps the k best per query (NVIDIA "Accelerating GLM-5.2 Long-Context
+ *      Training with cuDNN Fused DSA Kernels ...", section "How DSA works";
+ *      NeMo AutoModel cudnn_dsa API reference, cudnn_indexer_topk);
+ *   2. absorbed sparse MLA, where all heads of a query attend one gathered set
+ *      of latent rows, forward and backward (same page, "Why DSA needs fused
+ *      kernels"; API reference cudnn_sparse_attention and
+ *      _CudnnSparseAttention.forward / .backward).
+ *
+ * Conventions shared by every call
+ *   - All tensor arguments are DEVICE pointers to contiguous row-major
+ *     buffers owned by the caller, aligned to 16 bytes.  bf16 tensors are
+ *     passed as uint16_t* holding the bf16 bit patterns.  The library never
+ *     allocates or frees device memory: scratch space comes from a caller
+ *     buffer sized by the matching *_workspace_size() query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; results are valid once the stream has
+ *     executed the work.  The single exception is dsa_prepare_thd_metadata,
+ *     which synchronises once to read the sequence offsets.
+ *   - Every call returns a dsa_status.  On error nothing is enqueued and a
+ *     message for the calling thread is available from dsa_last_error().
+ *     Argument checks never read device memory (no hidden synchronisation);
+ *     index CONTENTS are trusted: an index outside [0, T_kv) other than -1 is
+ *     undefined behaviour unless DSA_DEBUG_CHECK_INDICES is set in `flags`.
+ *   - Outputs that depend on floating-point summation order: O, LSE and dq are
+ *     bitwise reproducible run to run; dkv is accumulated with atomics and is
+ *     reproducible only up to summation order.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_VALUE = 1, /* shape, size, alignment or value out of range */
+  DSA_ERR_UNSUPPORTED = 2,   /* device is not gfx950, or the combination is not built */
+  DSA_ERR_WORKSPACE = 3,     /* workspace pointer missing or smaller than required */
+  DSA_ERR_HIP = 4            /* a HIP runtime call failed (message carries its text) */
+} dsa_status;
+
+/* Flags for dsa_sparse_mla_bwd. */
+#define DSA_BWD_ACCUMULATE_DKV 0x1u   /* add into dkv instead of overwriting it */
+#define DSA_DEBUG_CHECK_INDICES 0x100u /* validate index contents on the device
+                                          (adds one synchronisation); debugging only */
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char *dsa_last_error(void);
+
+/* 1 if `device` is an AMD gfx950 GPU this library was built for, else 0. */
+int dsa_device_supported(int device);
+
+/* Largest top-k width the indexer accepts (GLM-5.2's fixed selection width:
+ * cudnn_dsa API reference, _validate_topk / _MAX_TOPK). */
+#define DSA_MAX_INDEXER_TOPK 2048
+
+/* --------------------------------------------------------------------------
+ * THD metadata (API reference: prepare_cudnn_dsa_packed_metadata -- per-query
+ * starts and real causal lengths of a packed variable-length batch, built once
+ * with one device-to-host synchronisation and reused by every indexer and
+ * attention layer; CudnnDsaPackedMetadata).
+ * ------------------------------------------------------------------------ */
+typedef struct dsa_thd_metadata {
+  /* device arrays inside the caller's workspace, valid while it lives */
+  int32_t *seq_start;   /* [T]  first token of the row's sequence            */
+  int32_t *causal_len;  /* [T]  L_t = t - seq_start[t] + 1 keys (s <= t)     */
+  int32_t *topk_length; /* [T]  min(K, L_t)                                  */
+  int32_t *row_order;   /* [T]  query rows ordered by decreasing L_t (work schedule) */
+  int32_t *groups;      /* [n_groups] indexer work groups: last row of each run of up to 4
+                           consecutive rows of one sequence, ordered by decreasing cost */
+  /* host values */
+  int64_t T;            /* total tokens (= cu_seqlens[B])                    */
+  int32_t B;            /* number of sequences                               */
+  int32_t K;            /* top-k width the lengths were computed for         */
+  int32_t max_seqlen;   /* longest sequence                                  */
+  int32_t all_rows_nonempty; /* 1 when every row has at least one valid slot */
+  int64_t total_pairs;  /* sum_t L_t   (causal query-key pairs)              */
+  int64_t total_valid;  /* sum_t min(K, L_t)                                  */
+  int32_t n_groups;     /* sum over sequences of ceil(length / 4)             */
+} dsa_thd_metadata;
+
+/* Bytes of workspace the metadata for T tokens needs. */
+size_t dsa_thd_metadata_workspace_size(int64_t T);
+
+/* Builds `md` from cu_seqlens (device int32 [B+1], cumulative sequence
+ * lengths: cu[0] = 0, non-decreasing, cu[B] = T; zero-length sequences are
+ * allowed).  K in [1, 2048] is the width topk_length is clipped to.  Copies
+ * cu_seqlens to the host and synchronises `stream` once; everything else runs
+ * on the stream.  Errors: DSA_ERR_INVALID_VALUE for bad B/T/K or offsets;
+ * DSA_ERR_WORKSPACE if ws is NULL or ws_bytes too small. */
+int dsa_prepare_thd_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t K,
+                             void *ws, size_t ws_bytes, dsa_thd_metadata *md, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Lightning indexer + top-k (GLM-5.2 page, "How DSA works": the indexer
+ * scores query-key relevance and emits the top-k token indices per query;
+ * API reference cudnn_indexer_topk and _compact_and_sort_indices).
+ *
+ * Score of query row t and key s of the same sequence with s <= t:
+ *     I(t,s) = sum_h w[t,h] * max(0, sum_d q_idx[t,h,d] * k_idx[s,d])
+ * computed with bf16 products accumulated in fp32; ReLU, weighting and the
+ * head sum are fp32.  The weights are used exactly as given (the caller owns
+ * the 1/sqrt(H) and 1/sqrt(D) scaling, cudnn_indexer_topk head_weights).
+ *
+ * Output for row t: the n = min(K, L_t) keys with the largest I (equal scores:
+ * lower position first), written as ascending global row positions in
+ * idx[t, 0:n], idx[t, n:K] = -1, len[t] = n.  No score matrix is stored.
+ *
+ *   q_idx [T, H_i, D_i] bf16   k_idx [T, D_i] bf16   w [T, H_i] fp32
+ *   idx   [T, K] int32 (out)   len [T] int32 (out)
+ * Supported: 1 <= H_i <= 64, D_i in {64, 128}, 1 <= K <= 2048.
+ * ------------------------------------------------------------------------ */
+size_t dsa_indexer_topk_workspace_size(int64_t T, int32_t H_i, int32_t D_i, int32_t K);
+int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
+                     const dsa_thd_metadata *md, int32_t H_i, int32_t D_i, int32_t K,
+                     int32_t *idx, int32_t *len, void *ws, size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Absorbed sparse MLA forward (API reference cudnn_sparse_attention and
+ * _CudnnSparseAttention.forward; SkyRL PR 2388 "Why"/"Change" for the NoPE
+ * width 512 and top-k widths that are not a multiple of 64).
+ *
+ * For query row t and head h, the valid slots are j < (topk_length ?
+ * topk_length[t] : K) with idx[t,j] != -1.  With logits
+ * z_j = scale * <q[t,h,0:D_qk], kv[idx[t,j], 0:D_qk]>:
+ *     lse[t,h] = log sum_j exp(z_j)                      (natural log)
+ *     out[t,h] = sum_j exp(z_j - lse[t,h]) * kv[idx[t,j], 0:D_v]
+ * A row with no valid slot gives out = 0 and lse = -inf.
+ *
+ *   q   [T_q, H, D_qk] bf16     kv [T_kv, D_qk] bf16 (one latent row per key)
+ *   idx [T_q, K] int32          topk_length [T_q] int32 or NULL
+ *   out [T_q, H, D_v] bf16 (out)   lse [T_q, H] fp32 (out)
+ * `scale` is applied unchanged.  Supported: 1 <= H <= 128, D_qk in {512, 576},
+ * D_v = 512, any K >= 1.  When topk_length is given the prefix must hold
+ * valid indices (it is read without checking for -1 beyond the -1 test).
+ * ------------------------------------------------------------------------ */
+int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                       const int32_t *topk_length, int64_t T_q, int64_t T_kv, int32_t H,
+                       int32_t D_qk, int32_t D_v, int32_t K, float scale, uint16_t *out,
+                       float *lse, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Absorbed sparse MLA backward (API reference _CudnnSparseAttention.backward:
+ * gradients for the query [T_q, H, 576] and the latent rows; SkyRL PR 2423
+ * "Summary": query chunks are independent and their key gradients sum).
+ *
+ * With P_j = exp(z_j - lse), dP_j = <dout[t,h], kv[s_j, 0:D_v]>,
+ * Delta = <dout[t,h], out[t,h]> (from the bf16 `out` given), and
+ * dZ_j = P_j (dP_j - Delta):
+ *     dq[t,h,0:D_qk]   = scale * sum_j dZ_j kv[s_j, 0:D_qk]
+ *     dkv[s_j, 0:D_qk] += scale * dZ_j q[t,h,0:D_qk]   (over all h, t)
+ *     dkv[s_j, 0:D_v]  += P_j dout[t,h]
+ *
+ *   out, lse: the forward's outputs; dout [T_q, H, D_v] bf16
+ *   dq  [T_q, H, D_qk] bf16 (out)   dkv [T_kv, D_qk] fp32 (out / accumulated)
+ * flags: DSA_BWD_ACCUMULATE_DKV adds into dkv (query-chunked execution);
+ * without it dkv is overwritten.  Workspace: dsa_sparse_mla_bwd_workspace_size.
+ * ------------------------------------------------------------------------ */
+size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk);
+int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                       const int32_t *topk_length, const uint16_t *out, const float *lse,
+                       const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H,
+                       int32_t D_qk, int32_t D_v, int32_t K, float scale, uint16_t *dq,
+                       float *dkv, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Benchmark support (changes no result).  While armed, every kernel the library
+ * enqueues records slots[i].start on its stream just before the kernel and
+ * slots[i].stop just after it, and sets slots[i].name to a static string naming
+ * the kernel, for i = 0, 1, ... < n_slots; *n_used counts the slots filled
+ * (kernels beyond n_slots are not recorded).  start/stop are hipEvent_t handles
+ * created by the caller with timing enabled.  Call with slots = NULL to disarm.
+ * The state is per calling thread.  Returns DSA_ERR_INVALID_VALUE if n_slots < 0
+ * or n_used is NULL while slots is not.
+ * ------------------------------------------------------------------------ */
+typedef struct dsa_kernel_timing {
+  void *start;      /* hipEvent_t */
+  void *stop;       /* hipEvent_t */
+  const char *name; /* set by the library */
+} dsa_kernel_timing;
+
+int dsa_record_kernel_events(dsa_kernel_timing *slots, int n_slots, int *n_used);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,314 @@
+// C ABI of libdsa: argument validation, workspace layout, error reporting and launches.
+// The contracts are documented in include/dsa.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dsa.h"
+#include "dsa_common.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct TimingState {
+  dsa_kernel_timing *slots = nullptr;
+  int n_slots = 0;
+  int *n_used = nullptr;
+  bool open = false;
+};
+thread_local TimingState g_timing;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (!dsa_device_supported(dev))
+    return fail(DSA_ERR_UNSUPPORTED, "device %d is not an AMD gfx950 GPU", dev);
+  return DSA_OK;
+}
+
+int32_t n_index_groups(const std::vector<int32_t> &cu) {
+  int64_t n = 0;
+  for (size_t b = 0; b + 1 < cu.size(); ++b)
+    n += (cu[b + 1] - cu[b] + dsa::kIdxRowsPerGroup - 1) / dsa::kIdxRowsPerGroup;
+  return static_cast<int32_t>(n);
+}
+
+}  // namespace
+
+namespace dsa {
+
+void kernel_begin(hipStream_t s, const char *name) {
+  TimingState &st = g_timing;
+  st.open = false;
+  if (!st.slots || *st.n_used >= st.n_slots) return;
+  dsa_kernel_timing &slot = st.slots[*st.n_used];
+  slot.name = name;
+  hipEventRecord(static_cast<hipEvent_t>(slot.start), s);
+  st.open = true;
+}
+
+void kernel_end(hipStream_t s) {
+  TimingState &st = g_timing;
+  if (!st.open) return;
+  hipEventRecord(static_cast<hipEvent_t>(st.slots[*st.n_used].stop), s);
+  ++*st.n_used;
+  st.open = false;
+}
+
+}  // namespace dsa
+
+extern "C" {
+
+int dsa_record_kernel_events(dsa_kernel_timing *slots, int n_slots, int *n_used) {
+  g_last_error.clear();
+  if (slots && (n_slots < 0 || !n_used))
+    return fail(DSA_ERR_INVALID_VALUE, "record_kernel_events: bad slot count or counter");
+  g_timing.slots = slots;
+  g_timing.n_slots = slots ? n_slots : 0;
+  g_timing.n_used = slots ? n_used : nullptr;
+  g_timing.open = false;
+  if (n_used) *n_used = 0;
+  return DSA_OK;
+}
+
+const char *dsa_last_error(void) { return g_last_error.c_str(); }
+
+int dsa_device_supported(int device) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
+  return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+// ---------------------------------------------------------------------------------------
+// workspace: seq_start | causal_len | topk_length | row_order | groups   (each 256-B aligned)
+size_t dsa_thd_metadata_workspace_size(int64_t T) {
+  if (T < 0) return 0;
+  const size_t a = align_up(static_cast<size_t>(T) * sizeof(int32_t));
+  return 5 * a + 256;
+}
+
+int dsa_prepare_thd_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t K,
+                             void *ws, size_t ws_bytes, dsa_thd_metadata *md, void *stream) {
+  g_last_error.clear();
+  if (!md) return fail(DSA_ERR_INVALID_VALUE, "prepare_thd_metadata: md is NULL");
+  if (B < 1) return fail(DSA_ERR_INVALID_VALUE, "prepare_thd_metadata: B=%d must be >= 1", B);
+  if (T < 0 || T > INT32_MAX)
+    return fail(DSA_ERR_INVALID_VALUE, "prepare_thd_metadata: T=%lld out of range",
+                static_cast<long long>(T));
+  if (K < 1 || K > DSA_MAX_INDEXER_TOPK)
+    return fail(DSA_ERR_INVALID_VALUE, "prepare_thd_metadata: K=%d not in [1, %d]", K,
+                DSA_MAX_INDEXER_TOPK);
+  if (!cu_seqlens) return fail(DSA_ERR_INVALID_VALUE, "prepare_thd_metadata: cu_seqlens is NULL");
+  const size_t need = dsa_thd_metadata_workspace_size(T);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "prepare_thd_metadata: workspace needs %zu bytes, got %zu",
+                need, ws ? ws_bytes : static_cast<size_t>(0));
+  if (int rc = check_device()) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // the one synchronisation: read the offsets on the host
+  std::vector<int32_t> cu(static_cast<size_t>(B) + 1);
+  hipError_t e = hipMemcpyAsync(cu.data(), cu_seqlens, cu.size() * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "prepare_thd_metadata: copy of cu_seqlens");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "prepare_thd_metadata: stream synchronize");
+  if (cu[0] != 0) return fail(DSA_ERR_INVALID_VALUE, "cu_seqlens[0]=%d, expected 0", cu[0]);
+  int32_t max_len = 0;
+  int64_t pairs = 0, valid = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (cu[b + 1] < cu[b])
+      return fail(DSA_ERR_INVALID_VALUE, "cu_seqlens decreases at %d (%d > %d)", b, cu[b],
+                  cu[b + 1]);
+    const int64_t len = cu[b + 1] - cu[b];
+    if (len > max_len) max_len = static_cast<int32_t>(len);
+    pairs += len * (len + 1) / 2;
+    const int64_t full = len < K ? len : K;  // rows 1..full have L <= K
+    valid += full * (full + 1) / 2 + (len - full) * K;
+  }
+  if (cu[B] != T)
+    return fail(DSA_ERR_INVALID_VALUE, "cu_seqlens[B]=%d does not match T=%lld", cu[B],
+                static_cast<long long>(T));
+
+  char *base = static_cast<char *>(ws);
+  const size_t a = align_up(static_cast<size_t>(T) * sizeof(int32_t));
+  base = reinterpret_cast<char *>(align_up(reinterpret_cast<uintptr_t>(base)));
+  md->seq_start = reinterpret_cast<int32_t *>(base);
+  md->causal_len = reinterpret_cast<int32_t *>(base + a);
+  md->topk_length = reinterpret_cast<int32_t *>(base + 2 * a);
+  md->row_order = reinterpret_cast<int32_t *>(base + 3 * a);
+  int32_t *groups = reinterpret_cast<int32_t *>(base + 4 * a);
+  md->T = T;
+  md->B = B;
+  md->K = K;
+  md->max_seqlen = max_len;
+  md->all_rows_nonempty = 1;  // causal rows always include their own key
+  md->total_pairs = pairs;
+  md->total_valid = valid;
+  const int32_t ng = n_index_groups(cu);
+  md->groups = groups;
+  md->n_groups = ng;
+  e = dsa::launch_thd_metadata(cu_seqlens, B, T, K, md->seq_start, md->causal_len,
+                               md->topk_length, md->row_order, groups, ng, s);
+  if (e != hipSuccess) return hip_fail(e, "prepare_thd_metadata: launch");
+  return DSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+size_t dsa_indexer_topk_workspace_size(int64_t T, int32_t H_i, int32_t D_i, int32_t K) {
+  (void)T;
+  (void)H_i;
+  (void)D_i;
+  (void)K;
+  return 0;  // the candidate buffers live in LDS
+}
+
+int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
+                     const dsa_thd_metadata *md, int32_t H_i, int32_t D_i, int32_t K,
+                     int32_t *idx, int32_t *len, void *ws, size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  (void)ws;
+  (void)ws_bytes;
+  if (!md || (md->T > 0 && (!md->seq_start || !md->groups)))
+    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: metadata missing");
+  if (H_i < 1 || H_i > 64)
+    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: H_i=%d not in [1, 64]", H_i);
+  if (D_i != 64 && D_i != 128)
+    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: D_i=%d must be 64 or 128", D_i);
+  if (K < 1 || K > DSA_MAX_INDEXER_TOPK)
+    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: K=%d not in [1, %d]", K,
+                DSA_MAX_INDEXER_TOPK);
+  const int64_t T = md->T;
+  if (T == 0) return DSA_OK;
+  if (!q_idx || !k_idx || !w || !idx || !len)
+    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: NULL tensor pointer");
+  if (!aligned16(q_idx) || !aligned16(k_idx))
+    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: q_idx/k_idx must be 16-byte aligned");
+  if (int rc = check_device()) return rc;
+  hipError_t e = dsa::launch_indexer_topk(q_idx, k_idx, w, md->seq_start, md->groups,
+                                          md->n_groups, T, H_i, D_i, K, idx, len,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "indexer_topk: launch");
+  return DSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+static int check_attention_args(const char *who, const uint16_t *q, const uint16_t *kv,
+                                const int32_t *idx, int64_t T_q, int64_t T_kv, int32_t H,
+                                int32_t D_qk, int32_t D_v, int32_t K, float scale, int32_t max_h) {
+  if (T_q < 0 || T_kv < 0 || T_q > INT32_MAX || T_kv > INT32_MAX)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: T_q=%lld / T_kv=%lld out of range", who,
+                static_cast<long long>(T_q), static_cast<long long>(T_kv));
+  if (H < 1 || H > max_h)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: H=%d not in [1, %d]", who, H, max_h);
+  if (D_qk != 576 && D_qk != 512)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: D_qk=%d must be 576 or 512", who, D_qk);
+  if (D_v != 512) return fail(DSA_ERR_INVALID_VALUE, "%s: D_v=%d must be 512", who, D_v);
+  if (K < 1) return fail(DSA_ERR_INVALID_VALUE, "%s: K=%d must be >= 1", who, K);
+  if (!(scale > 0.0f) || scale != scale || scale == INFINITY)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: scale must be a positive finite number", who);
+  if (T_q > 0 && (!q || !idx || (T_kv > 0 && !kv)))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: NULL tensor pointer", who);
+  if (!aligned16(q) || !aligned16(kv))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: q/kv must be 16-byte aligned", who);
+  return DSA_OK;
+}
+
+// Debug-only validation of index contents; `flag` is 4 bytes of caller workspace.
+static int debug_check_indices(const int32_t *idx, const int32_t *topk_length, int64_t T_q,
+                               int32_t K, int64_t T_kv, int32_t *flag, hipStream_t s) {
+  int32_t bad = 0;
+  hipError_t e = dsa::launch_check_indices(idx, topk_length, T_q, K, T_kv, flag, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&bad, flag, sizeof bad, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "debug index check");
+  if (bad) return fail(DSA_ERR_INVALID_VALUE, "index or topk_length out of range");
+  return DSA_OK;
+}
+
+int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                       const int32_t *topk_length, int64_t T_q, int64_t T_kv, int32_t H,
+                       int32_t D_qk, int32_t D_v, int32_t K, float scale, uint16_t *out,
+                       float *lse, void *stream) {
+  g_last_error.clear();
+  if (int rc = check_attention_args("sparse_mla_fwd", q, kv, idx, T_q, T_kv, H, D_qk, D_v, K,
+                                    scale, 128))
+    return rc;
+  if (T_q > 0 && (!out || !lse))
+    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_fwd: NULL output pointer");
+  if (int rc = check_device()) return rc;
+  hipError_t e = dsa::launch_sparse_mla_fwd(q, kv, idx, topk_length, T_q, H, D_qk, K, scale, out,
+                                            lse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparse_mla_fwd: launch");
+  return DSA_OK;
+}
+
+size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk) {
+  (void)T_kv;
+  (void)D_qk;
+  if (T_q < 0 || H < 0) return 0;
+  // Delta [T_q, H] fp32, then one int32 flag for the debug index check
+  return align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float)) + 512;
+}
+
+int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                       const int32_t *topk_length, const uint16_t *out, const float *lse,
+                       const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H,
+                       int32_t D_qk, int32_t D_v, int32_t K, float scale, uint16_t *dq,
+                       float *dkv, uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  if (int rc = check_attention_args("sparse_mla_bwd", q, kv, idx, T_q, T_kv, H, D_qk, D_v, K,
+                                    scale, 64))
+    return rc;
+  if (flags & ~(DSA_BWD_ACCUMULATE_DKV | DSA_DEBUG_CHECK_INDICES))
+    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: unknown flags 0x%x", flags);
+  if (T_q > 0 && (!out || !lse || !dout || !dq))
+    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: NULL tensor pointer");
+  if (T_kv > 0 && !dkv) return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: dkv is NULL");
+  if (!aligned16(out) || !aligned16(dout))
+    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: out/dout must be 16-byte aligned");
+  const size_t need = dsa_sparse_mla_bwd_workspace_size(T_q, T_kv, H, D_qk);
+  if (T_q > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "sparse_mla_bwd: workspace needs %zu bytes, got %zu", need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  if (int rc = check_device()) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *delta = reinterpret_cast<float *>(align_up(reinterpret_cast<uintptr_t>(ws)));
+  if ((flags & DSA_DEBUG_CHECK_INDICES) && T_q > 0) {
+    int32_t *flag = reinterpret_cast<int32_t *>(
+        reinterpret_cast<char *>(delta) +
+        align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float)));
+    if (int rc = debug_check_indices(idx, topk_length, T_q, K, T_kv, flag, s)) return rc;
+  }
+  hipError_t e = dsa::launch_sparse_mla_bwd(q, kv, idx, topk_length, out, lse, dout, T_q, T_kv,
+                                            H, D_qk, K, scale, dq, dkv,
+                                            (flags & DSA_BWD_ACCUMULATE_DKV) != 0, delta, s);
+  if (e != hipSuccess) return hip_fail(e, "sparse_mla_bwd: launch");
+  return DSA_OK;
+}
+
+}  // extern "C"

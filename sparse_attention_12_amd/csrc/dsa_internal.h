@@ -1,0 +1,51 @@
+// Launchers shared between the kernel translation units and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Benchmark event hooks around every kernel launch (no-ops unless armed through
+// dsa_record_kernel_events on the calling thread).
+void kernel_begin(hipStream_t s, const char *name);
+void kernel_end(hipStream_t s);
+
+// Launch `kern` with the event hooks around it.
+#define DSA_LAUNCH(name, kern, grid, block, smem, stream, ...)                   \
+  do {                                                                            \
+    ::dsa::kernel_begin(stream, name);                                            \
+    hipLaunchKernelGGL(kern, grid, block, smem, stream, __VA_ARGS__);             \
+    ::dsa::kernel_end(stream);                                                    \
+  } while (0)
+
+// Rows of one indexer work group (consecutive query rows of one sequence).
+constexpr int kIdxRowsPerGroup = 4;
+
+hipError_t launch_thd_metadata(const int32_t *cu, int32_t B, int64_t T, int32_t K,
+                               int32_t *seq_start, int32_t *causal_len, int32_t *topk_length,
+                               int32_t *row_order, int32_t *groups, int32_t n_groups,
+                               hipStream_t s);
+
+hipError_t launch_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
+                               const int32_t *seq_start, const int32_t *groups, int32_t n_groups,
+                               int64_t T, int32_t H, int32_t D, int32_t K, int32_t *idx,
+                               int32_t *len, hipStream_t s);
+
+hipError_t launch_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                                 const int32_t *topk_length, int64_t T_q, int32_t H,
+                                 int32_t D_qk, int32_t K, float scale, uint16_t *out, float *lse,
+                                 hipStream_t s);
+
+hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                                 const int32_t *topk_length, const uint16_t *out,
+                                 const float *lse, const uint16_t *dout, int64_t T_q,
+                                 int64_t T_kv, int32_t H, int32_t D_qk, int32_t K, float scale,
+                                 uint16_t *dq, float *dkv, bool accumulate, float *delta_ws,
+                                 hipStream_t s);
+
+hipError_t launch_check_indices(const int32_t *idx, const int32_t *topk_length, int64_t T_q,
+                                int32_t K, int64_t T_kv, int32_t *bad_flag, hipStream_t s);
+
+}  // namespace dsa

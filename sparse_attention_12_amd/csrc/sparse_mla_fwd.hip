@@ -1,0 +1,217 @@
+// Absorbed sparse MLA forward (NVIDIA GLM-5.2 cuDNN DSA page, "Why DSA needs fused kernels":
+// all heads of a query attend one top-k set, so the MMA M axis is tiled from heads in an
+// MQA-style layout; NeMo AutoModel cudnn_dsa API reference, cudnn_sparse_attention: q
+// [T_q,H,576], latent rows [T_kv,576], values = first 512 channels, -1 slots masked, optional
+// valid-prefix lengths, softmax_scale applied unchanged; SkyRL PR 2388 for the 512-wide NoPE
+// layout and top-k widths that are not a multiple of 64).
+//
+// Work group = one query row, ceil(H/16) waves, wave w owning heads [16w, 16w+16).  The row's
+// valid slots are processed in chunks of 32: the 32 latent rows are gathered into LDS with
+// 16-byte loads, then each wave computes
+//   S^T[32 slots x 16 heads] = rows . q^T          (16x16x32 bf16 MFMA, A = LDS rows,
+//                                                   B = the wave's q block held in registers)
+// runs the online softmax in fp32 (base 2), and accumulates
+//   O[16 heads x 512] += P . V                       (A = P straight from the S^T registers,
+//                                                   B = V read from the same row-major LDS
+//                                                   tile with transposing LDS reads)
+// The slot order inside the P.V contraction is permuted so that P needs no data movement:
+// the lane holding S^T rows (lane/16)*4 + [0,4) of both 16-slot halves supplies exactly the
+// eight contraction indices it owns in the MFMA A layout, and the transposing reads fetch V
+// rows in the same order.
+#include "dsa_common.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kSlots = 32;  // slots per chunk
+constexpr int kDv = 512;
+
+template <int DQK>
+struct FwdCfg {
+  static constexpr int kStride = DQK + 16;  // bf16 elements per LDS row (+32 B)
+  static constexpr int kKSteps = DQK / 32;  // S^T contraction steps
+  static constexpr int kChunksPerRow = DQK / 8;
+};
+
+template <int DQK, int NW>
+__global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
+    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
+  using C = FwdCfg<DQK>;
+  __shared__ __align__(16) uint16_t tile[kSlots * C::kStride];
+  __shared__ int32_t srow[kSlots];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = blockIdx.x;
+  const int h0 = wave * 16;
+  const int g = lane >> 4;     // lane group
+  const int hl = lane & 15;    // head within the wave's tile (S^T column)
+  const int lim = topk_length ? topk_length[t] : K;
+  const int32_t *irow = idx + t * K;
+
+  // q block of this wave as MFMA B operand: lane -> head hl, dims ks*32 + g*8 + [0,8)
+  bf16x8 qf[C::kKSteps];
+  {
+    const int h = h0 + hl;
+#pragma unroll
+    for (int ks = 0; ks < C::kKSteps; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (h < H) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+
+  f32x4 o[kDv / 16];
+#pragma unroll
+  for (int n = 0; n < kDv / 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max (base-2 logits) of head hl
+  float l_run = 0.0f;       // this lane's partial softmax denominator of head hl
+
+  for (int c0 = 0; c0 < lim; c0 += kSlots) {
+    // ---- gather the chunk's latent rows (invalid slots -> zero rows)
+    for (int c = threadIdx.x; c < kSlots * C::kChunksPerRow; c += NW * 64) {
+      const int j = c / C::kChunksPerRow;
+      const int col = (c % C::kChunksPerRow) * 8;
+      const int slot = c0 + j;
+      const int32_t r = slot < lim ? irow[slot] : -1;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (r >= 0) v = *reinterpret_cast<const u32x4 *>(kv + static_cast<int64_t>(r) * DQK + col);
+      *reinterpret_cast<u32x4 *>(&tile[j * C::kStride + col]) = v;
+      if (col == 0) srow[j] = r;
+    }
+    __syncthreads();
+
+    // ---- S^T = rows . q^T   (acc[mt][i] = S^T[16mt + 4g + i][hl])
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < C::kKSteps; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+            &tile[(mt * 16 + hl) * C::kStride + ks * 32 + g * 8]));
+        acc[mt] = mfma16(a, qf[ks], acc[mt]);
+      }
+    }
+
+    // ---- online softmax (base 2); lanes hl, hl^16, hl^32, hl^48 share head hl
+    float x[2][4];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = srow[mt * 16 + g * 4 + i] >= 0;
+        x[mt][i] = valid ? acc[mt][i] * scale_log2 : -INFINITY;
+        cmax = fmaxf(cmax, x[mt][i]);
+      }
+    cmax = fmaxf(cmax, xor_lane(cmax, 16));
+    cmax = fmaxf(cmax, xor_lane(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const bool none = m_new == -INFINITY;
+    const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float p[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[mt][i] = none ? 0.0f : __builtin_amdgcn_exp2f(x[mt][i] - m_new);
+        psum += p[mt][i];
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // ---- rescale O rows (O row (4g + i) belongs to head 4g + i, held by lane 4g + i)
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a_i = __shfl(alpha, g * 4 + i, 64);
+#pragma unroll
+        for (int n = 0; n < kDv / 16; ++n) o[n][i] *= a_i;
+      }
+    }
+
+    // ---- O += P . V
+    u32x4 pw;
+    pw[0] = pack_bf16x2(p[0][0], p[0][1]);
+    pw[1] = pack_bf16x2(p[0][2], p[0][3]);
+    pw[2] = pack_bf16x2(p[1][0], p[1][1]);
+    pw[3] = pack_bf16x2(p[1][2], p[1][3]);
+    const bf16x8 pa = as_bf16x8(pw);
+    const int r = (lane & 15) >> 2;  // 4-lane block within the 16-lane group
+    const int cq = lane & 3;
+    const uint16_t *v0 = &tile[(g * 4 + r) * C::kStride + cq * 4];
+    const uint16_t *v1 = &tile[(16 + g * 4 + r) * C::kStride + cq * 4];
+#pragma unroll
+    for (int n = 0; n < kDv / 16; ++n) {
+      const u32x2 lo = lds_read_tr16(v0 + n * 16);
+      const u32x2 hi = lds_read_tr16(v1 + n * 16);
+      const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
+      o[n] = mfma16(pa, as_bf16x8(b), o[n]);
+    }
+    __syncthreads();
+  }
+
+  // ---- finalize: denominator over the four lane groups, normalise, write
+  float l_tot = l_run + xor_lane(l_run, 16);
+  l_tot += xor_lane(l_tot, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (g == 0 && h0 + hl < H) {
+    lse[t * H + h0 + hl] =
+        l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = h0 + g * 4 + i;
+    const float s_i = __shfl(inv, g * 4 + i, 64);
+    if (h < H) {
+      uint16_t *orow = out + (t * H + h) * kDv + hl;
+#pragma unroll
+      for (int n = 0; n < kDv / 16; ++n) orow[n * 16] = f32_to_bf16(o[n][i] * s_i);
+    }
+  }
+}
+
+template <int DQK, int NW>
+hipError_t launch(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                  const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K, float scale,
+                  uint16_t *out, float *lse, hipStream_t s) {
+  DSA_LAUNCH("sparse_mla_fwd", (sparse_mla_fwd_kernel<DQK, NW>), dim3(static_cast<unsigned>(T_q)),
+                     dim3(NW * 64), 0, s, q, kv, idx, topk_length, H, K, scale * kLog2e, out,
+                     lse);
+  return hipGetLastError();
+}
+
+template <int DQK>
+hipError_t launch_w(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                    const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K, float scale,
+                    uint16_t *out, float *lse, hipStream_t s) {
+  const int nw = (H + 15) / 16;
+  switch (nw) {
+    case 1: return launch<DQK, 1>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+    case 2: return launch<DQK, 2>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+    case 3: return launch<DQK, 3>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+    case 4: return launch<DQK, 4>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+    case 8: return launch<DQK, 8>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+    default: break;
+  }
+  if (nw <= 8) return launch<DQK, 8>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                                 const int32_t *topk_length, int64_t T_q, int32_t H,
+                                 int32_t D_qk, int32_t K, float scale, uint16_t *out, float *lse,
+                                 hipStream_t s) {
+  if (T_q == 0) return hipSuccess;
+  if (D_qk == 576) return launch_w<576>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  if (D_qk == 512) return launch_w<512>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

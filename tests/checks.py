@@ -1,0 +1,66 @@
+"""Comparison rules shared by the GPU parity tests (host side, numpy).
+
+Tolerances (the stated parity bar of the DSA hot path): indices bit-exact when the indexer
+inputs are exactly representable small integers with power-of-two weights; on float inputs a
+top-k set mismatch is allowed only for keys whose exact score lies within 1e-5 (relative) of
+the row's k-th score; attention output, dq and dkv within 2e-2 max-abs of the fp64 oracle;
+LSE within 1e-3.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+ATOL_OUT = 2e-2
+ATOL_LSE = 1e-3
+NEAR_TIE_REL = 1e-5
+
+
+def check_topk_structure(idx: np.ndarray, ln: np.ndarray, rows: np.ndarray, start: np.ndarray,
+                         K: int):
+    """Exact structure of every given row: len = min(K, L), ascending, unique, causal, -1 tail."""
+    for r, t in enumerate(rows):
+        L = t - start[r] + 1
+        n = min(K, L)
+        assert ln[r] == n, f"row {t}: len {ln[r]} != {n}"
+        row = idx[r]
+        assert (row[n:] == -1).all(), f"row {t}: -1 suffix broken"
+        v = row[:n]
+        assert (np.diff(v) > 0).all(), f"row {t}: not strictly ascending"
+        assert v.min() >= start[r] and v.max() <= t, f"row {t}: non-causal index"
+
+
+def check_topk_near_tie(q_idx, k_idx, w, gpu_idx: np.ndarray, ora_idx: np.ndarray,
+                        kth: np.ndarray, rows: np.ndarray):
+    """Set equality up to near-ties; returns the number of mismatching keys."""
+    mism = 0
+    for r, t in enumerate(rows):
+        g = set(gpu_idx[r][gpu_idx[r] >= 0].tolist())
+        o = set(ora_idx[r][ora_idx[r] >= 0].tolist())
+        diff = g ^ o
+        if not diff:
+            continue
+        tau = kth[r]
+        for s in diff:
+            score = oracle.indexer_score(q_idx, k_idx, w, int(t), int(s))
+            assert abs(score - tau) <= NEAR_TIE_REL * abs(tau), (
+                f"row {t} key {s}: score {score} vs k-th {tau} is not a near tie")
+        mism += len(diff)
+    return mism
+
+
+def max_abs(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        d = np.where(both_inf, 0.0, np.abs(a - b))
+    return float(np.nanmax(d)) if d.size else 0.0
+
+
+def assert_close(name, gpu, ref, atol):
+    err = max_abs(gpu, ref)
+    assert np.isfinite(err) and err <= atol, f"{name}: max-abs error {err:.3e} > {atol:.1e}"
+    return err

@@ -1,0 +1,110 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point, and rejects
+bad arguments before touching a device (no GPU is needed for any of this)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(dsa_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_12_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        from sparse_attention_12_amd import build
+        build.build()
+    return pkg.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ["dsa_prepare_thd_metadata", "dsa_indexer_topk", "dsa_sparse_mla_fwd",
+                     "dsa_sparse_mla_bwd", "dsa_last_error", "dsa_device_supported",
+                     "dsa_thd_metadata_workspace_size", "dsa_indexer_topk_workspace_size",
+                     "dsa_sparse_mla_bwd_workspace_size"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(dsa):
+    for name in _declared_functions():
+        assert hasattr(dsa, name), f"libdsa.so does not export {name}"
+
+
+def test_workspace_queries(dsa):
+    assert dsa.dsa_thd_metadata_workspace_size(32768) >= 5 * 32768 * 4
+    assert dsa.dsa_thd_metadata_workspace_size(-1) == 0
+    assert dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576) >= 1000 * 64 * 4
+    assert dsa.dsa_indexer_topk_workspace_size(1000, 64, 128, 2048) == 0
+
+
+def _err(dsa):
+    return dsa.dsa_last_error().decode()
+
+
+def test_argument_errors_without_device(dsa):
+    import sparse_attention_12_amd as pkg
+    md = pkg._Metadata()
+    # metadata: bad B / K / missing workspace
+    assert dsa.dsa_prepare_thd_metadata(None, 0, 10, 16, None, 0, C.byref(md), None) == \
+        pkg.DSA_ERR_INVALID_VALUE
+    assert "B=0" in _err(dsa)
+    assert dsa.dsa_prepare_thd_metadata(C.c_void_p(16), 1, 10, 4096, None, 0, C.byref(md),
+                                        None) == pkg.DSA_ERR_INVALID_VALUE
+    assert dsa.dsa_prepare_thd_metadata(C.c_void_p(16), 1, 10, 16, None, 0, C.byref(md),
+                                        None) == pkg.DSA_ERR_WORKSPACE
+    # indexer: K above the fixed maximum, unsupported head dim, too many heads
+    md.T = 8
+    md.seq_start = 16
+    md.groups = 16
+    assert dsa.dsa_indexer_topk(16, 16, 16, C.byref(md), 64, 128, 2049, 16, 16, None, 0,
+                                None) == pkg.DSA_ERR_INVALID_VALUE
+    assert dsa.dsa_indexer_topk(16, 16, 16, C.byref(md), 64, 96, 16, 16, 16, None, 0,
+                                None) == pkg.DSA_ERR_INVALID_VALUE
+    assert dsa.dsa_indexer_topk(16, 16, 16, C.byref(md), 65, 128, 16, 16, 16, None, 0,
+                                None) == pkg.DSA_ERR_INVALID_VALUE
+    # forward: width, value width, heads, K, scale, alignment
+    args = dict(q=16, kv=16, idx=16, tl=None, Tq=4, Tkv=4, H=16, Dqk=576, Dv=512, K=8, sc=0.1,
+                out=16, lse=16, s=None)
+
+    def fwd(**kw):
+        a = {**args, **kw}
+        return dsa.dsa_sparse_mla_fwd(a["q"], a["kv"], a["idx"], a["tl"], a["Tq"], a["Tkv"],
+                                      a["H"], a["Dqk"], a["Dv"], a["K"], a["sc"], a["out"],
+                                      a["lse"], a["s"])
+    assert fwd(Dqk=640) == pkg.DSA_ERR_INVALID_VALUE and "D_qk" in _err(dsa)
+    assert fwd(Dv=256) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(H=0) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(H=129) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(K=0) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(sc=-1.0) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(sc=float("nan")) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(q=24) == pkg.DSA_ERR_INVALID_VALUE and "aligned" in _err(dsa)
+    assert fwd(out=None) == pkg.DSA_ERR_INVALID_VALUE
+    # backward: unknown flag, missing workspace, too many heads
+    def bwd(flags=0, ws=16, ws_bytes=1 << 30, H=64):
+        return dsa.dsa_sparse_mla_bwd(16, 16, 16, None, 16, 16, 16, 4, 4, H, 576, 512, 8, 0.1,
+                                      16, 16, flags, ws, ws_bytes, None)
+    assert bwd(flags=0x8) == pkg.DSA_ERR_INVALID_VALUE
+    assert bwd(ws=None) == pkg.DSA_ERR_WORKSPACE
+    assert bwd(ws_bytes=4) == pkg.DSA_ERR_WORKSPACE
+    assert bwd(H=65) == pkg.DSA_ERR_INVALID_VALUE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import sparse_attention_12_amd as pkg
+    monkeypatch.setattr(pkg, "_lib", None)
+    monkeypatch.setattr(pkg, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        pkg.lib()
+    assert not pkg.is_available()

@@ -1,0 +1,300 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle, small and ragged sizes.
+
+Every input comes from dsa_inputs (seeded); expected values come from oracle/ only.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as gen
+import oracle
+from tests import checks
+
+pytestmark = pytest.mark.gpu
+
+dev = "cuda"
+
+
+def _dsa():
+    import sparse_attention_12_amd as dsa
+    return dsa
+
+
+def _np(t):
+    return t.detach().to("cpu").numpy()
+
+
+# ----------------------------------------------------------------------------------------
+# metadata
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cu", [[0, 1024, 4096, 16384, 32768], [0, 0, 5, 5, 9, 300, 301],
+                                [0, 7], [0, 2049, 2050, 6000]])
+def test_metadata_matches_oracle(cu):
+    dsa = _dsa()
+    T = cu[-1]
+    K = 2048
+    md = dsa.prepare_thd_metadata(torch.tensor(cu, dtype=torch.int32, device=dev), K)
+    torch.cuda.synchronize()
+    ref = oracle.thd_metadata(np.array(cu, np.int32), T, K)
+    np.testing.assert_array_equal(_np(md.seq_start), ref["seq_start"])
+    np.testing.assert_array_equal(_np(md.causal_len), ref["causal_len"])
+    np.testing.assert_array_equal(_np(md.topk_length), ref["topk_length"])
+    assert md.max_seqlen == ref["max_seqlen"]
+    assert md.total_pairs == int(ref["causal_len"].astype(np.int64).sum())
+    assert md.total_valid == int(ref["topk_length"].astype(np.int64).sum())
+    order = _np(md.row_order)
+    assert sorted(order.tolist()) == list(range(T))
+    L = ref["causal_len"][order]
+    assert (np.diff(L) <= 0).all()
+    groups = _np(md.groups)
+    lens = np.diff(cu)
+    assert md.n_groups == int(((lens + 3) // 4).sum())
+    # every row is covered by exactly one group of <= 4 consecutive rows
+    covered = np.zeros(T, np.int32)
+    for last in groups:
+        s = ref["seq_start"][last]
+        covered[max(s, last - 3): last + 1] += 1
+    assert (covered == 1).all()
+    costs = ref["causal_len"][groups]
+    assert (np.diff(costs) <= 0).all()
+
+
+def test_metadata_rejects_bad_offsets():
+    dsa = _dsa()
+    with pytest.raises(ValueError):
+        dsa.prepare_thd_metadata(torch.tensor([0, 5, 3], dtype=torch.int32, device=dev))
+    with pytest.raises(ValueError):
+        dsa.prepare_thd_metadata(torch.tensor([1, 5], dtype=torch.int32, device=dev))
+
+
+# ----------------------------------------------------------------------------------------
+# indexer
+# ----------------------------------------------------------------------------------------
+
+def _run_indexer(inp, K):
+    dsa = _dsa()
+    md = dsa.prepare_thd_metadata(inp["cu_seqlens"].to(dev).to(torch.int32), K)
+    idx, ln = dsa.indexer_topk(inp["q_idx"].to(dev), inp["k_idx"].to(dev), inp["w"].to(dev),
+                               md, K)
+    torch.cuda.synchronize()
+    return _np(idx), _np(ln)
+
+
+def test_indexer_integer_inputs_bit_exact():
+    """Tiny workload (T=256, 4 heads x 64, integers in [-4,4], weights in {0.5,1,2}, k=64)."""
+    w = gen.workload(1)
+    inp = gen.indexer_inputs(1)
+    idx, ln = _run_indexer(inp, w.topk)
+    ridx, rln, _ = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"], inp["cu_seqlens"],
+                                       w.topk)
+    np.testing.assert_array_equal(ln, rln)
+    np.testing.assert_array_equal(idx, ridx)
+
+
+@pytest.mark.parametrize("cu,K,H,D", [([0, 700], 64, 64, 128), ([0, 100, 1000, 1300], 256, 64, 128),
+                                      ([0, 3000], 2048, 64, 128), ([0, 5000], 1000, 40, 64),
+                                      ([0, 4200], 1, 8, 128)])
+def test_indexer_float_inputs_near_tie(cu, K, H, D):
+    inp = gen.indexer_inputs(2, cu_seqlens=cu)
+    inp = dict(inp, q_idx=inp["q_idx"][:, :H].contiguous(), w=inp["w"][:, :H].contiguous())
+    if D != inp["k_idx"].shape[1]:
+        inp = dict(inp, q_idx=inp["q_idx"][..., :D].contiguous(),
+                   k_idx=inp["k_idx"][:, :D].contiguous())
+    idx, ln = _run_indexer(inp, K)
+    T = cu[-1]
+    rows = np.arange(T)
+    start = oracle.thd_metadata(np.array(cu, np.int32), T, K)["seq_start"]
+    checks.check_topk_structure(idx, ln, rows, start, K)
+    # oracle on a sample: the longest rows and a spread of others
+    samp = np.unique(np.concatenate([np.arange(max(0, T - 12), T),
+                                     np.linspace(0, T - 1, 24).astype(np.int64)]))
+    for t in samp:
+        ridx, rln, kth = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"],
+                                             inp["cu_seqlens"], K, rows=(int(t), int(t) + 1))
+        assert rln[0] == ln[t]
+        checks.check_topk_near_tie(inp["q_idx"], inp["k_idx"], inp["w"], idx[t:t + 1], ridx,
+                                   kth, np.array([t]))
+
+
+def test_indexer_integer_inputs_thd_long_rows_bit_exact():
+    """Integer inputs over long rows (many compaction rounds) and several sequences: exact."""
+    cu = [0, 70, 2500, 2501, 9000]
+    g = torch.Generator().manual_seed(77)
+    T, H, D, K = cu[-1], 64, 128, 512
+    q = torch.randint(-4, 5, (T, H, D), generator=g).to(torch.bfloat16)
+    k = torch.randint(-4, 5, (T, D), generator=g).to(torch.bfloat16)
+    w = torch.tensor([0.5, 1.0, 2.0, 0.25])[torch.randint(0, 4, (T, H), generator=g)]
+    inp = dict(q_idx=q, k_idx=k, w=w, cu_seqlens=torch.tensor(cu, dtype=torch.int32))
+    idx, ln = _run_indexer(inp, K)
+    rows = (0, 10, 69, 70, 71, 600, 2499, 2500, 2501, 2600, 5000, 8997, 8998, 8999)
+    for t in rows:
+        ridx, rln, _ = oracle.indexer_topk(q, k, w, inp["cu_seqlens"], K, rows=(t, t + 1))
+        assert rln[0] == ln[t], t
+        np.testing.assert_array_equal(idx[t], ridx[0], err_msg=f"row {t}")
+
+
+# ----------------------------------------------------------------------------------------
+# sparse MLA forward / backward
+# ----------------------------------------------------------------------------------------
+
+def _random_indices(T, Tkv, K, n_valid, seed, minus_one_frac=0.0, causal=True):
+    g = np.random.default_rng(seed)
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        hi = (t + 1) if causal else Tkv
+        n = min(n_valid, hi)
+        sel = np.sort(g.choice(hi, size=n, replace=False))
+        idx[t, :n] = sel
+        if minus_one_frac > 0:
+            pos = g.random(K) < minus_one_frac
+            row = idx[t].copy()
+            idx[t] = -1
+            keep = row[row >= 0]
+            slots = np.flatnonzero(~pos)[: keep.size]
+            idx[t, slots] = keep[: slots.size]
+    return idx
+
+
+def _fwd_bwd_case(T, H, Dqk, K, n_valid, seed, minus_one_frac=0.0, use_len=False,
+                  check_bwd=True, Tkv=None):
+    dsa = _dsa()
+    Tkv = Tkv or T
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn((T, H, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    kv = (torch.randn((Tkv, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    idx = _random_indices(T, Tkv, K, n_valid, seed, minus_one_frac, causal=Tkv == T)
+    lens = None
+    if use_len:
+        lens = (idx >= 0).sum(1).astype(np.int32)
+        # canonical prefix: move valid entries to the front, garbage after the prefix
+        idx = np.where(np.arange(K)[None, :] < lens[:, None], np.sort(np.where(idx >= 0, idx,
+                       np.iinfo(np.int32).max), axis=1), 12345 % Tkv).astype(np.int32)
+    scale = 1.0 / math.sqrt(Dqk)
+    idx_t = torch.from_numpy(idx)
+    len_t = None if lens is None else torch.from_numpy(lens)
+    out, lse = dsa.sparse_mla_fwd(q.to(dev), kv.to(dev), idx_t.to(dev), scale,
+                                  None if len_t is None else len_t.to(dev))
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_mla_fwd(q, kv, idx, lens, scale, 512)
+    checks.assert_close("out", _np(out.float()), ro, checks.ATOL_OUT)
+    checks.assert_close("lse", _np(lse), rl, checks.ATOL_LSE)
+    if not check_bwd:
+        return
+    dq, dkv = dsa.sparse_mla_bwd(q.to(dev), kv.to(dev), idx_t.to(dev), out, lse, dout.to(dev),
+                                 scale, None if len_t is None else len_t.to(dev))
+    torch.cuda.synchronize()
+    rdq, rdkv = oracle.sparse_mla_bwd(q, kv, idx, lens, dout, scale)
+    checks.assert_close("dq", _np(dq.float()), rdq, checks.ATOL_OUT)
+    checks.assert_close("dkv", _np(dkv), rdkv, checks.ATOL_OUT)
+
+
+@pytest.mark.parametrize("T,H,Dqk,K,n_valid", [(96, 16, 576, 64, 64), (200, 64, 576, 128, 77),
+                                               (130, 8, 512, 75, 70), (64, 20, 576, 40, 33),
+                                               (50, 64, 512, 2051, 2051)])
+def test_fwd_bwd_matches_oracle(T, H, Dqk, K, n_valid):
+    _fwd_bwd_case(T, H, Dqk, K, n_valid, seed=T * 7 + H)
+
+
+def test_fwd_bwd_minus_one_slots_scattered():
+    _fwd_bwd_case(120, 64, 576, 96, 50, seed=3, minus_one_frac=0.3)
+
+
+def test_fwd_bwd_topk_length_prefix():
+    _fwd_bwd_case(150, 16, 576, 100, 60, seed=4, use_len=True)
+
+
+def test_fwd_bwd_query_rows_differ_from_key_rows():
+    """Local queries against a larger gathered key set (T_q != T_kv)."""
+    _fwd_bwd_case(40, 64, 576, 64, 64, seed=5, Tkv=333)
+
+
+def test_tiny_workload_end_to_end():
+    """Tiny workload: indexer (bit-exact) -> forward -> backward vs the oracle."""
+    dsa = _dsa()
+    w = gen.workload(1)
+    ii = gen.indexer_inputs(1)
+    ai = gen.attention_inputs(1)
+    md = dsa.prepare_thd_metadata(ii["cu_seqlens"].to(dev), w.topk)
+    idx, ln = dsa.indexer_topk(ii["q_idx"].to(dev), ii["k_idx"].to(dev), ii["w"].to(dev), md,
+                               w.topk)
+    out, lse = dsa.sparse_mla_fwd(ai["q"].to(dev), ai["kv"].to(dev), idx, ai["scale"], ln)
+    dq, dkv = dsa.sparse_mla_bwd(ai["q"].to(dev), ai["kv"].to(dev), idx, out, lse,
+                                 ai["dout"].to(dev), ai["scale"], ln)
+    torch.cuda.synchronize()
+    ridx, rln, _ = oracle.indexer_topk(ii["q_idx"], ii["k_idx"], ii["w"], ii["cu_seqlens"],
+                                       w.topk)
+    np.testing.assert_array_equal(_np(idx), ridx)
+    ro, rl = oracle.sparse_mla_fwd(ai["q"], ai["kv"], ridx, rln, ai["scale"], 512)
+    checks.assert_close("out", _np(out.float()), ro, checks.ATOL_OUT)
+    checks.assert_close("lse", _np(lse), rl, checks.ATOL_LSE)
+    rdq, rdkv = oracle.sparse_mla_bwd(ai["q"], ai["kv"], ridx, rln, ai["dout"], ai["scale"])
+    checks.assert_close("dq", _np(dq.float()), rdq, checks.ATOL_OUT)
+    checks.assert_close("dkv", _np(dkv), rdkv, checks.ATOL_OUT)
+
+
+def test_empty_rows_and_single_slot_rows():
+    dsa = _dsa()
+    T, H, D = 6, 16, 576
+    g = torch.Generator().manual_seed(9)
+    q = (torch.randn((T, H, D), generator=g) * 0.5).to(torch.bfloat16)
+    kv = (torch.randn((T, D), generator=g) * 0.5).to(torch.bfloat16)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    idx = np.full((T, 5), -1, np.int32)
+    idx[1, 3] = 0
+    idx[3, 0] = 2
+    idx[4, :2] = [1, 4]
+    out, lse = dsa.sparse_mla_fwd(q.to(dev), kv.to(dev), torch.from_numpy(idx).to(dev), 0.04)
+    dq, dkv = dsa.sparse_mla_bwd(q.to(dev), kv.to(dev), torch.from_numpy(idx).to(dev), out, lse,
+                                 dout.to(dev), 0.04)
+    torch.cuda.synchronize()
+    o, l = _np(out.float()), _np(lse)
+    for t in (0, 2, 5):
+        assert (o[t] == 0).all() and np.isneginf(l[t]).all() and (_np(dq[t].float()) == 0).all()
+    # single valid slot: out equals the value row (bf16 exact)
+    np.testing.assert_array_equal(o[1], np.broadcast_to(_np(kv[0, :512].float()), o[1].shape))
+    ro, rl = oracle.sparse_mla_fwd(q, kv, idx, None, 0.04, 512)
+    checks.assert_close("lse", l, rl, checks.ATOL_LSE)
+    rdq, rdkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, 0.04)
+    checks.assert_close("dq", _np(dq.float()), rdq, checks.ATOL_OUT)
+    checks.assert_close("dkv", _np(dkv), rdkv, checks.ATOL_OUT)
+
+
+def test_chunked_equals_one_shot():
+    """SkyRL PR 2423: query chunks are independent; key gradients summed over chunks
+    (accumulate flag) equal the one-shot key gradients up to summation order."""
+    dsa = _dsa()
+    T = 700
+    ai = gen.attention_inputs(4, cu_seqlens=[0, T])
+    idx = gen.kpool_indices(T, topk=131, tail=3).to(dev)
+    q, kv, dout = ai["q"].to(dev), ai["kv"].to(dev), ai["dout"].to(dev)
+    out, lse = dsa.sparse_mla_fwd(q, kv, idx, ai["scale"])
+    dq, dkv = dsa.sparse_mla_bwd(q, kv, idx, out, lse, dout, ai["scale"])
+    dkv_c = torch.zeros_like(dkv)
+    for r0, r1 in [(0, 256), (256, 512), (512, 700)]:
+        oc, lc = dsa.sparse_mla_fwd(q[r0:r1], kv, idx[r0:r1].contiguous(), ai["scale"])
+        assert torch.equal(oc, out[r0:r1]) and torch.equal(lc, lse[r0:r1])
+        dqc, _ = dsa.sparse_mla_bwd(q[r0:r1], kv, idx[r0:r1].contiguous(), oc, lc,
+                                    dout[r0:r1].contiguous(), ai["scale"], dkv=dkv_c,
+                                    accumulate=True)
+        assert torch.equal(dqc, dq[r0:r1])
+    torch.cuda.synchronize()
+    assert (dkv_c - dkv).abs().max().item() <= 1e-3
+
+
+def test_debug_index_check_rejects_out_of_range():
+    dsa = _dsa()
+    T, H, D = 8, 16, 576
+    q = torch.zeros((T, H, D), dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros((T, D), dtype=torch.bfloat16, device=dev)
+    idx = torch.zeros((T, 4), dtype=torch.int32, device=dev)
+    out, lse = dsa.sparse_mla_fwd(q, kv, idx, 0.1)
+    bad = idx.clone()
+    bad[3, 2] = T  # out of range: only caught by the debug check, before any kernel reads it
+    with pytest.raises(ValueError, match="out of range"):
+        dsa.sparse_mla_bwd(q, kv, bad, out, lse, torch.zeros_like(out), 0.1,
+                           check_indices=True)
