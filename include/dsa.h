@@ -140,8 +140,8 @@ int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *
  *   q   [T_q, H, D_qk] bf16     kv [T_kv, D_qk] bf16 (one latent row per key)
  *   idx [T_q, K] int32          topk_length [T_q] int32 or NULL
  *   out [T_q, H, D_v] bf16 (out)   lse [T_q, H] fp32 (out)
- * `scale` is applied unchanged.  Supported: 1 <= H <= 128, D_qk in {512, 576},
- * D_v = 512, any K >= 1.  When topk_length is given the prefix must hold
+ * `scale` is applied unchanged.  Supported: 1 <= H <= 64, D_qk in {512, 576},
+ * D_v = 512, 1 <= K <= 4096, T_kv >= 1 whenever T_q > 0.  When topk_length is given the prefix must hold
  * valid indices (it is read without checking for -1 beyond the -1 test).
  * ------------------------------------------------------------------------ */
 int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,

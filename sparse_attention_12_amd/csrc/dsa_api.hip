@@ -231,7 +231,9 @@ static int check_attention_args(const char *who, const uint16_t *q, const uint16
   if (K < 1) return fail(DSA_ERR_INVALID_VALUE, "%s: K=%d must be >= 1", who, K);
   if (!(scale > 0.0f) || scale != scale || scale == INFINITY)
     return fail(DSA_ERR_INVALID_VALUE, "%s: scale must be a positive finite number", who);
-  if (T_q > 0 && (!q || !idx || (T_kv > 0 && !kv)))
+  if (T_q > 0 && T_kv < 1)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: T_kv must be >= 1 when T_q > 0", who);
+  if (T_q > 0 && (!q || !idx || !kv))
     return fail(DSA_ERR_INVALID_VALUE, "%s: NULL tensor pointer", who);
   if (!aligned16(q) || !aligned16(kv))
     return fail(DSA_ERR_INVALID_VALUE, "%s: q/kv must be 16-byte aligned", who);
@@ -256,8 +258,9 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                        float *lse, void *stream) {
   g_last_error.clear();
   if (int rc = check_attention_args("sparse_mla_fwd", q, kv, idx, T_q, T_kv, H, D_qk, D_v, K,
-                                    scale, 128))
+                                    scale, 64))
     return rc;
+  if (K > 4096) return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_fwd: K=%d exceeds 4096", K);
   if (T_q > 0 && (!out || !lse))
     return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_fwd: NULL output pointer");
   if (int rc = check_device()) return rc;

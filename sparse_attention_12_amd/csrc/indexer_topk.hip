@@ -5,42 +5,61 @@
 //
 //   I(t,s) = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:])      for seq_start(t) <= s <= t
 //
-// Work group = 4 waves = 4 consecutive query rows of one sequence (one wave per row).  The
-// group streams the rows' common causal key range in tiles of 64 keys through LDS; each wave
-// multiplies its row's [H x D] query block by the tile with 32x32x16 bf16 MFMAs (heads on the
-// M axis, keys on N), so the ReLU, the head weights and the head sum are applied to fp32
-// accumulators in registers: a lane ends up holding the partial sum over 32 heads of one key,
-// and one cross-half exchange finishes it.
+// Work group = 8 waves = 4 consecutive query rows of one sequence, two waves per row.  The
+// group streams the rows' common causal key range in tiles of 64 keys, loaded straight into
+// LDS (double buffered); the two waves of a row take the lower and upper 32 keys of each tile.
+// A wave multiplies its row's [H x D] query block by its 32 keys with 32x32x16 bf16 MFMAs
+// (heads on the M axis, keys on N), so the ReLU, the head weights and the head sum are applied
+// to fp32 accumulators in registers: a lane ends up holding the partial sum over 32 heads of
+// one key, and one cross-half exchange finishes it.  The two waves of a row sit on the same
+// SIMD, so one's VALU epilogue overlaps the other's MFMAs.
 //
 // Streaming top-k: each row owns a candidate buffer of (orderable score, key position) in LDS.
-// Keys arrive in ascending position order and are appended in that order when their score
-// exceeds the row's threshold tau (initially none).  When the buffer nears capacity the wave
-// runs an exact radix select (4 passes of 8 bits over the orderable uint32 scores) for the
-// K-th largest score, and a stable partition keeps the K best, ties resolved to the lower
-// position because the buffer is in position order.  tau becomes the K-th score; later keys
-// have higher positions, so a later key with score == tau can never enter the top K and the
-// strict test score > tau is exact.  The buffer therefore always holds the exact running top
-// K in ascending position order, which is also the required output order.
+// Keys arrive in ascending position order (tile by tile, lower half before upper half, lane
+// order inside a half) and are appended in that order when their score exceeds the row's
+// threshold tau (initially none).  When the buffer nears capacity one wave of the row runs an
+// exact radix select (4 passes of 8 bits over the orderable uint32 scores) for the K-th
+// largest score, and a stable partition keeps the K best, ties resolved to the lower position
+// because the buffer is in position order.  tau becomes the K-th score; later keys have higher
+// positions, so a later key with score == tau can never enter the top K and the strict test
+// score > tau is exact.  The buffer therefore always holds the exact running top K in
+// ascending position order, which is also the required output order.
 //
 // Rows with L_t <= K select their whole causal prefix, which is written without scoring.
 #include "dsa_common.h"
 #include "dsa_internal.h"
+#include "tile.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kWaves = kIdxRowsPerGroup;  // one wave per query row
+constexpr int kRows = kIdxRowsPerGroup;  // query rows per work group
+constexpr int kWaves = 2 * kRows;        // two waves per row
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileKeys = 64;
-constexpr int kCap = 4096;  // candidate entries per row
 constexpr int kBins = 256;
 
 template <int D>
+struct IndexerCfg {
+  // candidate entries per row: as many as fit next to two key tiles
+  static constexpr int kCap = D == 128 ? 3840 : 4096;
+  static constexpr int kChunks = D / 8;                      // 16-byte chunks per key
+  static constexpr int kTileBytes = kTileKeys * D * 2;
+  static constexpr int kLoads = kTileKeys * kChunks / 64;    // wave-wide DMAs per tile
+  static constexpr int kLoadsPerWave = kLoads / kWaves;
+  static_assert(kLoads % kWaves == 0, "tile loads must split evenly");
+  __device__ static __forceinline__ int swz(int key) { return key & (kChunks - 1); }
+};
+
+template <int D>
 struct IndexerSmem {
-  uint32_t cand_key[kWaves][kCap];
-  int32_t cand_pos[kWaves][kCap];
-  uint32_t hist[kWaves][kBins];
-  uint16_t tile[kTileKeys][D + 8];  // 16-byte pad keeps 16-lane b128 reads conflict free
+  uint32_t cand_key[kRows][IndexerCfg<D>::kCap];
+  int32_t cand_pos[kRows][IndexerCfg<D>::kCap];
+  uint32_t hist[kRows][kBins];
+  int32_t exch[2][kRows][2];  // per-tile candidate counts of the two halves (double buffered)
+  uint32_t tau[kRows];
+  int32_t has_tau[kRows];
+  __align__(16) unsigned char tile[2][IndexerCfg<D>::kTileBytes];
 };
 
 // Monotone map float -> uint32 (larger float -> larger key); +0 and -0 map alike.
@@ -51,7 +70,7 @@ __device__ __forceinline__ uint32_t orderable(float f) {
 }
 
 // Keep the K best of the wave's `cnt` candidates (in place, order preserving) and return the
-// K-th largest key.  Requires cnt >= K.
+// K-th largest key.  Requires cnt >= K.  Executed by one wave.
 __device__ uint32_t select_top_k(uint32_t *ck, int32_t *cp, uint32_t *hist, int cnt, int K) {
   const int lane = __lane_id();
   wave_sync();
@@ -60,9 +79,20 @@ __device__ uint32_t select_top_k(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int b = lane; b < kBins; b += 64) hist[b] = 0u;
     wave_sync();
-    for (int e = lane; e < cnt; e += 64) {
-      const uint32_t u = ck[e];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xFFu], 1u);
+    for (int e0 = 0; e0 < cnt; e0 += 64) {
+      const int e = e0 + lane;
+      const uint32_t u = e < cnt ? ck[e] : 0u;
+      const bool in = e < cnt && (u & pmask) == prefix;
+      const uint32_t d = (u >> shift) & 0xFFu;
+      // all matching lanes on one digit (common for the leading digit): one add
+      const uint64_t inm = __ballot(in);
+      const uint32_t d0 = __shfl(d, __ffsll(static_cast<unsigned long long>(inm | 1ull)) - 1, 64);
+      const uint64_t same = __ballot(in && d == d0);
+      if (same == inm) {
+        if (inm != 0 && lane == 0) atomicAdd(&hist[d0], static_cast<uint32_t>(__popcll(inm)));
+      } else if (in) {
+        atomicAdd(&hist[d], 1u);
+      }
     }
     wave_sync();
     // lane l owns bins 255-4l .. 252-4l, scanned from the top
@@ -126,30 +156,50 @@ __device__ uint32_t select_top_k(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
   return tau;
 }
 
+// DMA this wave's share of key tile [kb, kb + 64) (keys beyond `last` repeat key `last`; they
+// are never selected because they lie beyond every row of the group).
+template <int D>
+__device__ __forceinline__ void issue_key_tile(unsigned char *tile, const uint16_t *k, int64_t kb,
+                                               int64_t last, int wave) {
+  using C = IndexerCfg<D>;
+  const int lane = __lane_id();
+#pragma unroll
+  for (int i = 0; i < C::kLoadsPerWave; ++i) {
+    const int ld = wave * C::kLoadsPerWave + i;
+    const int pos = ld * 64 + lane;
+    const int key = pos / C::kChunks;
+    const int chunk = (pos % C::kChunks) ^ C::swz(key);
+    int64_t s = kb + key;
+    s = s <= last ? s : last;
+    dma16(k + s * D + chunk * 8, tile + ld * 1024);
+  }
+}
+
 template <int NMT, int D>
 __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ seq_start, const int32_t *__restrict__ groups, int64_t T, int H,
     int K, int32_t *__restrict__ idx_out, int32_t *__restrict__ len_out) {
-  constexpr int NKK = D / 16;                        // k-steps of the 32x32x16 MFMA
-  constexpr int kChunks = kTileKeys * D / 8 / kThreads;  // 16-byte chunks per thread per tile
-  constexpr int kChunksPerKey = D / 8;
+  using C = IndexerCfg<D>;
+  constexpr int NKK = D / 16;  // k-steps of the 32x32x16 MFMA
   extern __shared__ __align__(16) unsigned char smem_raw[];
   IndexerSmem<D> &sm = *reinterpret_cast<IndexerSmem<D> *>(smem_raw);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int row = wave & (kRows - 1);  // waves w and w + 4 share a row (and a SIMD)
+  const int half = wave >> 2;
   const int64_t last = groups[blockIdx.x];
   const int64_t start = seq_start[last];
-  const int64_t first = last - (kWaves - 1) > start ? last - (kWaves - 1) : start;
-  const int64_t t = first + wave;
+  const int64_t first = last - (kRows - 1) > start ? last - (kRows - 1) : start;
+  const int64_t t = first + row;
   const bool row_ok = t <= last;
   const int64_t L = row_ok ? t - start + 1 : 0;
   const bool compute = row_ok && L > K;
 
-  if (row_ok && !compute) {
-    int32_t *row = idx_out + t * K;
-    for (int j = lane; j < K; j += 64) row[j] = j < L ? static_cast<int32_t>(start + j) : -1;
+  if (row_ok && !compute && half == 0) {
+    int32_t *out = idx_out + t * K;
+    for (int j = lane; j < K; j += 64) out[j] = j < L ? static_cast<int32_t>(start + j) : -1;
     if (lane == 0) len_out[t] = static_cast<int32_t>(L);
   }
   if (last - start + 1 <= K) return;  // every row of the group is a whole prefix (uniform)
@@ -173,50 +223,45 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
       wv[m][i] = (compute && hh < H) ? w[t * H + hh] : 0.0f;
     }
   }
-
-  uint32_t *ck = sm.cand_key[wave];
-  int32_t *cp = sm.cand_pos[wave];
-  uint32_t *hist = sm.hist[wave];
-  int cnt = 0;
-  uint32_t tau = 0u;
-  bool has_tau = false;
+  if (threadIdx.x < kRows) {
+    sm.has_tau[threadIdx.x] = 0;
+    sm.tau[threadIdx.x] = 0u;
+  }
+  uint32_t *ck = sm.cand_key[row];
+  int32_t *cp = sm.cand_pos[row];
+  // candidate counts of all four rows, tracked identically by every wave
+  int cnt[kRows] = {0, 0, 0, 0};
   const uint64_t lt = lanemask_lt();
 
-  u32x4 pf[kChunks];
-  auto load_tile = [&](int64_t kb) {
-#pragma unroll
-    for (int r = 0; r < kChunks; ++r) {
-      const int c = threadIdx.x + r * kThreads;
-      const int64_t key = kb + c / kChunksPerKey;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key <= last) v = *reinterpret_cast<const u32x4 *>(k + key * D + (c % kChunksPerKey) * 8);
-      pf[r] = v;
-    }
-  };
-  load_tile(start);
+  issue_key_tile<D>(sm.tile[0], k, start, last, wave);
+  wait_tile();      // the tile loads are invisible to the compiler: wait for them explicitly
+  __syncthreads();  // q, w, tau init and the first tile have landed
 
-  for (int64_t kb = start; kb <= last; kb += kTileKeys) {
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kChunks; ++r) {
-      const int c = threadIdx.x + r * kThreads;
-      *reinterpret_cast<u32x4 *>(&sm.tile[c / kChunksPerKey][(c % kChunksPerKey) * 8]) = pf[r];
+  int it = 0;
+  for (int64_t kb = start; kb <= last; kb += kTileKeys, ++it) {
+    const int buf = it & 1;
+    if (it > 0) {
+      wait_tile();
+      lds_barrier();  // tile `it` complete; compactions of the previous tile finished
     }
-    __syncthreads();
-    if (kb + kTileKeys <= last) load_tile(kb + kTileKeys);
-    if (!compute) continue;
+    if (kb + kTileKeys <= last) issue_key_tile<D>(sm.tile[buf ^ 1], k, kb + kTileKeys, last, wave);
 
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int64_t kbase = kb + sub * 32;
-      if (kbase > t) break;
+    int n_pass = 0;
+    uint64_t pm = 0;
+    uint32_t u = 0;
+    const int64_t kbase = kb + half * 32;
+    const int64_t key = kbase + (lane & 31);
+    if (compute && kbase <= t) {
+      const unsigned char *tile = sm.tile[buf];
       f32x16 acc[NMT];
 #pragma unroll
       for (int m = 0; m < NMT; ++m) acc[m] = f32x16{};
+      const int krow = half * 32 + (lane & 31);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
+        const int chunk = (2 * kk + (lane >> 5)) ^ C::swz(krow);
         const bf16x8 b = as_bf16x8(
-            *reinterpret_cast<const u32x4 *>(&sm.tile[sub * 32 + (lane & 31)][kk * 16 + (lane >> 5) * 8]));
+            *reinterpret_cast<const u32x4 *>(tile + krow * (D * 2) + chunk * 16));
 #pragma unroll
         for (int m = 0; m < NMT; ++m) acc[m] = mfma32(qa[m][kk], b, acc[m]);
       }
@@ -226,32 +271,48 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) s = fmaf(wv[m][i], fmaxf(acc[m][i], 0.0f), s);
       s += swap_halves(s);
-      const int64_t key = kbase + (lane & 31);
-      const uint32_t u = orderable(s);
+      u = orderable(s);
+      const bool has_tau = sm.has_tau[row] != 0;
+      const uint32_t tau = sm.tau[row];
       const bool pass = lane < 32 && key <= t && (!has_tau || u > tau);
-      const uint64_t pm = __ballot(pass);
-      if (pass) {
-        const int p = cnt + __popcll(pm & lt);
+      pm = __ballot(pass);
+      n_pass = __popcll(pm);
+    }
+    if (lane == 0) sm.exch[buf][row][half] = n_pass;
+    lds_barrier();
+    int need_compact = 0;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int n0 = sm.exch[buf][r][0], n1 = sm.exch[buf][r][1];
+      if (r == row && (pm >> lane) & 1ull) {
+        const int p = cnt[r] + (half ? n0 : 0) + __popcll(pm & lt);
         ck[p] = u;
         cp[p] = static_cast<int32_t>(key);
       }
-      cnt += __popcll(pm);
+      cnt[r] += n0 + n1;
+      need_compact |= cnt[r] > C::kCap - kTileKeys;
     }
-    if (cnt > kCap - kTileKeys) {
-      tau = select_top_k(ck, cp, hist, cnt, K);
-      cnt = K;
-      has_tau = true;
+    if (need_compact) {
+      lds_barrier();  // both halves' appends are visible
+      if (half == 0 && cnt[row] > C::kCap - kTileKeys) {
+        const uint32_t tau = select_top_k(ck, cp, sm.hist[row], cnt[row], K);
+        if (lane == 0) {
+          sm.tau[row] = tau;
+          sm.has_tau[row] = 1;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRows; ++r)
+        if (cnt[r] > C::kCap - kTileKeys) cnt[r] = K;
     }
   }
 
-  if (compute) {
-    if (cnt > K) {
-      select_top_k(ck, cp, hist, cnt, K);
-      cnt = K;
-    }
+  lds_barrier();
+  if (compute && half == 0) {
+    if (cnt[row] > K) select_top_k(ck, cp, sm.hist[row], cnt[row], K);
     wave_sync();
-    int32_t *row = idx_out + t * K;
-    for (int j = lane; j < K; j += 64) row[j] = cp[j];
+    int32_t *out = idx_out + t * K;
+    for (int j = lane; j < K; j += 64) out[j] = cp[j];
     if (lane == 0) len_out[t] = K;
   }
 }
@@ -266,8 +327,8 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const float *w, const in
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  DSA_LAUNCH("indexer_topk", kern, dim3(n_groups), dim3(kThreads), smem, s, q, k, w, seq_start, groups,
-                     T, H, K, idx, len);
+  DSA_LAUNCH("indexer_topk", kern, dim3(n_groups), dim3(kThreads), smem, s, q, k, w, seq_start,
+             groups, T, H, K, idx, len);
   return hipGetLastError();
 }
 

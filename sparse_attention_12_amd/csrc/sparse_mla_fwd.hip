@@ -20,28 +20,48 @@
 // rows in the same order.
 #include "dsa_common.h"
 #include "dsa_internal.h"
+#include "tile.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kSlots = 32;  // slots per chunk
 constexpr int kDv = 512;
+constexpr int kMaxK = 4096;  // largest top-k width whose index row fits the LDS copy
 
-template <int DQK>
-struct FwdCfg {
-  static constexpr int kStride = DQK + 16;  // bf16 elements per LDS row (+32 B)
-  static constexpr int kKSteps = DQK / 32;  // S^T contraction steps
-  static constexpr int kChunksPerRow = DQK / 8;
-};
+// Tile buffers in flight: a wave with few loads per tile keeps NBUF - 1 tiles in flight.
+template <int NW>
+constexpr int fwd_buffers() { return NW == 1 ? 2 : 4; }
+
+template <int DQK, int NW>
+constexpr size_t fwd_smem_bytes() {
+  return static_cast<size_t>(fwd_buffers<NW>()) * Tile<DQK>::kBytes + kMaxK * sizeof(int32_t);
+}
+
+// Wait for tile c when `ahead` later tiles (each L loads per wave) may stay in flight.
+template <int L, int NBUF>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  if constexpr (NBUF >= 4) {
+    if (ahead >= 2) { wait_vm<2 * L>(); return; }
+  }
+  if constexpr (NBUF >= 3) {
+    if (ahead >= 1) { wait_vm<L>(); return; }
+  }
+  wait_vm<0>();
+}
 
 template <int DQK, int NW>
 __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
     float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
-  using C = FwdCfg<DQK>;
-  __shared__ __align__(16) uint16_t tile[kSlots * C::kStride];
-  __shared__ int32_t srow[kSlots];
+  using TL = Tile<DQK>;
+  constexpr int kKSteps = DQK / 32;
+  constexpr int NBUF = fwd_buffers<NW>();
+  constexpr int L = TL::kLoads / NW;  // DMA loads per wave per tile
+  static_assert(TL::kLoads % NW == 0, "loads must split evenly over the waves");
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + NBUF * TL::kBytes);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -51,47 +71,59 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
   const int hl = lane & 15;    // head within the wave's tile (S^T column)
   const int lim = topk_length ? topk_length[t] : K;
   const int32_t *irow = idx + t * K;
+  const int nchunks = (lim + kSlots - 1) / kSlots;
 
   // q block of this wave as MFMA B operand: lane -> head hl, dims ks*32 + g*8 + [0,8)
-  bf16x8 qf[C::kKSteps];
+  bf16x8 qf[kKSteps];
   {
     const int h = h0 + hl;
 #pragma unroll
-    for (int ks = 0; ks < C::kKSteps; ++ks) {
+    for (int ks = 0; ks < kKSteps; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (h < H) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
       qf[ks] = as_bf16x8(v);
     }
   }
+  // the query's slot -> latent row map, then the first NBUF - 1 tiles
+  for (int j = threadIdx.x; j < lim; j += NW * 64) slot_rows[j] = irow[j];
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NBUF - 1; ++c)
+    if (c < nchunks) TL::template issue<NW>(smem + c * TL::kBytes, kv, slot_rows, c * kSlots, lim, wave);
 
   f32x4 o[kDv / 16];
 #pragma unroll
   for (int n = 0; n < kDv / 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;  // running max (base-2 logits) of head hl
   float l_run = 0.0f;       // this lane's partial softmax denominator of head hl
+  const int r4 = (lane & 15) >> 2;  // 4-lane block within the 16-lane group
+  const int cq = lane & 3;
 
-  for (int c0 = 0; c0 < lim; c0 += kSlots) {
-    // ---- gather the chunk's latent rows (invalid slots -> zero rows)
-    for (int c = threadIdx.x; c < kSlots * C::kChunksPerRow; c += NW * 64) {
-      const int j = c / C::kChunksPerRow;
-      const int col = (c % C::kChunksPerRow) * 8;
-      const int slot = c0 + j;
-      const int32_t r = slot < lim ? irow[slot] : -1;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r >= 0) v = *reinterpret_cast<const u32x4 *>(kv + static_cast<int64_t>(r) * DQK + col);
-      *reinterpret_cast<u32x4 *>(&tile[j * C::kStride + col]) = v;
-      if (col == 0) srow[j] = r;
-    }
-    __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int ahead = min(NBUF - 2, nchunks - 1 - c);  // later tiles already issued
+    wait_tiles_ahead<L, NBUF>(ahead);
+    lds_barrier();  // tile c is complete in LDS; buffer (c - 1) % NBUF is free
+    if (c + NBUF - 1 < nchunks)
+      TL::template issue<NW>(smem + ((c + NBUF - 1) % NBUF) * TL::kBytes, kv, slot_rows,
+                             (c + NBUF - 1) * kSlots, lim, wave);
+    const unsigned char *tile = smem + (c % NBUF) * TL::kBytes;
+    bool valid[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = c * kSlots + mt * 16 + g * 4 + i;
+        valid[mt][i] = slot < lim && slot_rows[slot] >= 0;
+      }
 
-    // ---- S^T = rows . q^T   (acc[mt][i] = S^T[16mt + 4g + i][hl])
+  // ---- S^T = rows . q^T   (acc[mt][i] = S^T[16mt + 4g + i][hl])
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < C::kKSteps; ++ks) {
+    for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-            &tile[(mt * 16 + hl) * C::kStride + ks * 32 + g * 8]));
+            tile + TL::chunk_off(mt * 16 + hl, ks * 4 + g)));
         acc[mt] = mfma16(a, qf[ks], acc[mt]);
       }
     }
@@ -103,8 +135,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool valid = srow[mt * 16 + g * 4 + i] >= 0;
-        x[mt][i] = valid ? acc[mt][i] * scale_log2 : -INFINITY;
+        x[mt][i] = valid[mt][i] ? acc[mt][i] * scale_log2 : -INFINITY;
         cmax = fmaxf(cmax, x[mt][i]);
       }
     cmax = fmaxf(cmax, xor_lane(cmax, 16));
@@ -134,25 +165,21 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
       }
     }
 
-    // ---- O += P . V
+    // ---- O += P . V   (slot k-index 8g + j <-> tile row 4g + j (j < 4), 16 + 4g + j - 4)
     u32x4 pw;
     pw[0] = pack_bf16x2(p[0][0], p[0][1]);
     pw[1] = pack_bf16x2(p[0][2], p[0][3]);
     pw[2] = pack_bf16x2(p[1][0], p[1][1]);
     pw[3] = pack_bf16x2(p[1][2], p[1][3]);
     const bf16x8 pa = as_bf16x8(pw);
-    const int r = (lane & 15) >> 2;  // 4-lane block within the 16-lane group
-    const int cq = lane & 3;
-    const uint16_t *v0 = &tile[(g * 4 + r) * C::kStride + cq * 4];
-    const uint16_t *v1 = &tile[(16 + g * 4 + r) * C::kStride + cq * 4];
+    const int row0 = g * 4 + r4, row1 = 16 + g * 4 + r4;
 #pragma unroll
     for (int n = 0; n < kDv / 16; ++n) {
-      const u32x2 lo = lds_read_tr16(v0 + n * 16);
-      const u32x2 hi = lds_read_tr16(v1 + n * 16);
+      const u32x2 lo = lds_read_tr16(tile + TL::elem_off(row0, n * 16 + cq * 4));
+      const u32x2 hi = lds_read_tr16(tile + TL::elem_off(row1, n * 16 + cq * 4));
       const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
       o[n] = mfma16(pa, as_bf16x8(b), o[n]);
     }
-    __syncthreads();
   }
 
   // ---- finalize: denominator over the four lane groups, normalise, write
@@ -179,9 +206,14 @@ template <int DQK, int NW>
 hipError_t launch(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                   const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K, float scale,
                   uint16_t *out, float *lse, hipStream_t s) {
-  DSA_LAUNCH("sparse_mla_fwd", (sparse_mla_fwd_kernel<DQK, NW>), dim3(static_cast<unsigned>(T_q)),
-                     dim3(NW * 64), 0, s, q, kv, idx, topk_length, H, K, scale * kLog2e, out,
-                     lse);
+  constexpr size_t smem = fwd_smem_bytes<DQK, NW>();
+  auto kern = sparse_mla_fwd_kernel<DQK, NW>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(smem));
+  if (e != hipSuccess) return e;
+  DSA_LAUNCH("sparse_mla_fwd", kern, dim3(static_cast<unsigned>(T_q)), dim3(NW * 64), smem, s,
+             q, kv, idx, topk_length, H, K, scale * kLog2e, out, lse);
   return hipGetLastError();
 }
 
@@ -189,16 +221,9 @@ template <int DQK>
 hipError_t launch_w(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                     const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K, float scale,
                     uint16_t *out, float *lse, hipStream_t s) {
-  const int nw = (H + 15) / 16;
-  switch (nw) {
-    case 1: return launch<DQK, 1>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-    case 2: return launch<DQK, 2>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-    case 3: return launch<DQK, 3>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-    case 4: return launch<DQK, 4>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-    case 8: return launch<DQK, 8>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-    default: break;
-  }
-  if (nw <= 8) return launch<DQK, 8>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  if (H <= 16) return launch<DQK, 1>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  if (H <= 32) return launch<DQK, 2>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  if (H <= 64) return launch<DQK, 4>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
   return hipErrorInvalidValue;
 }
 

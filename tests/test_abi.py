@@ -85,7 +85,8 @@ def test_argument_errors_without_device(dsa):
     assert fwd(Dqk=640) == pkg.DSA_ERR_INVALID_VALUE and "D_qk" in _err(dsa)
     assert fwd(Dv=256) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(H=0) == pkg.DSA_ERR_INVALID_VALUE
-    assert fwd(H=129) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(H=65) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(K=4097) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(K=0) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(sc=-1.0) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(sc=float("nan")) == pkg.DSA_ERR_INVALID_VALUE
