@@ -156,24 +156,108 @@ __device__ uint32_t select_top_k(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
   return tau;
 }
 
-// DMA this wave's share of key tile [kb, kb + 64) (keys beyond `last` repeat key `last`; they
-// are never selected because they lie beyond every row of the group).
-template <int D>
-__device__ __forceinline__ void issue_key_tile(unsigned char *tile, const uint16_t *k, int64_t kb,
-                                               int64_t last, int wave) {
-  using C = IndexerCfg<D>;
+// Streaming compaction: drop candidates that can no longer reach the top K, keeping at least
+// K of them, in one counting pass.  With lo = the current threshold (or the smallest key) and
+// hi = the largest key, the keys are binned by (u - lo) >> shift into at most 256 bins; the
+// bin holding the K-th largest key gives a new threshold tau' = lo + (bin << shift) - 1 with
+// at least K keys above it (so tau' never exceeds the true K-th largest key, and a later key
+// at or below tau' can never enter the top K).  Keys <= tau' are removed with an order
+// preserving partition.  Returns tau'; `cnt` becomes the number kept (>= K).
+__device__ uint32_t prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int &cnt, int K,
+                                     bool has_tau, uint32_t tau) {
   const int lane = __lane_id();
-#pragma unroll
-  for (int i = 0; i < C::kLoadsPerWave; ++i) {
-    const int ld = wave * C::kLoadsPerWave + i;
-    const int pos = ld * 64 + lane;
-    const int key = pos / C::kChunks;
-    const int chunk = (pos % C::kChunks) ^ C::swz(key);
-    int64_t s = kb + key;
-    s = s <= last ? s : last;
-    dma16(k + s * D + chunk * 8, tile + ld * 1024);
+  wave_sync();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int e = lane; e < cnt; e += 64) {
+    const uint32_t u = ck[e];
+    lo = min(lo, u);
+    hi = max(hi, u);
   }
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off, 64)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off, 64)));
+  }
+  if (has_tau) lo = tau + 1u;  // every candidate is above the current threshold
+  const uint32_t span = hi - lo;
+  const int shift = span < 256u ? 0 : 32 - __clz(span) - 8;
+  for (int b = lane; b < kBins; b += 64) hist[b] = 0u;
+  wave_sync();
+  for (int e = lane; e < cnt; e += 64) atomicAdd(&hist[(ck[e] - lo) >> shift], 1u);
+  wave_sync();
+  // bins scanned from the top: lane l owns bins 255-4l .. 252-4l
+  const uint32_t h0 = hist[255 - 4 * lane], h1 = hist[254 - 4 * lane];
+  const uint32_t h2 = hist[253 - 4 * lane], h3 = hist[252 - 4 * lane];
+  const uint32_t c = h0 + h1 + h2 + h3;
+  uint32_t incl = c;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  const uint32_t excl = incl - c;
+  const uint32_t n = static_cast<uint32_t>(K);
+  const bool mine = excl < n && n <= incl;
+  const uint64_t owner = __ballot(mine);
+  const int src = __ffsll(static_cast<unsigned long long>(owner)) - 1;
+  uint32_t bin = 0;
+  if (mine) {
+    uint32_t a = excl;
+    if (a + h0 >= n) bin = 255 - 4 * lane;
+    else if ((a += h0) + h1 >= n) bin = 254 - 4 * lane;
+    else if ((a += h1) + h2 >= n) bin = 253 - 4 * lane;
+    else bin = 252 - 4 * lane;
+  }
+  bin = __shfl(bin, src, 64);
+  const uint32_t floor_key = lo + (bin << shift);  // keys >= floor_key: at least K of them
+  int written = 0;
+  const uint64_t lt = lanemask_lt();
+  for (int base = 0; base < cnt; base += 64) {
+    const int e = base + lane;
+    const bool in = e < cnt;
+    const uint32_t u = in ? ck[e] : 0u;
+    const int32_t p = in ? cp[e] : 0;
+    const bool keep = in && u >= floor_key;
+    const uint64_t km = __ballot(keep);
+    if (keep) {
+      const int o = written + __popcll(km & lt);
+      ck[o] = u;
+      cp[o] = p;
+    }
+    written += __popcll(km);
+  }
+  wave_sync();
+  cnt = written;
+  return floor_key - 1u;  // floor_key > lo >= 1 whenever keys were dropped
 }
+
+// DMA targets of this wave's loads of a key tile: key index inside the tile and byte offset
+// inside the key row (keys beyond `last` repeat key `last`; they lie beyond every row of the
+// group and are never selected).
+template <int D>
+struct KeyTileLoads {
+  int key[IndexerCfg<D>::kLoadsPerWave];
+  int off[IndexerCfg<D>::kLoadsPerWave];
+  __device__ __forceinline__ void init(int wave) {
+    using C = IndexerCfg<D>;
+    const int lane = __lane_id();
+#pragma unroll
+    for (int i = 0; i < C::kLoadsPerWave; ++i) {
+      const int pos = (wave * C::kLoadsPerWave + i) * 64 + lane;
+      key[i] = pos / C::kChunks;
+      off[i] = ((pos % C::kChunks) ^ C::swz(key[i])) * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(unsigned char *tile, const uint16_t *k, int64_t kb,
+                                        int64_t last, int wave) const {
+    using C = IndexerCfg<D>;
+#pragma unroll
+    for (int i = 0; i < C::kLoadsPerWave; ++i) {
+      int64_t s = kb + key[i];
+      s = s <= last ? s : last;
+      dma16(reinterpret_cast<const unsigned char *>(k) + s * (D * 2) + off[i],
+            tile + (wave * C::kLoadsPerWave + i) * 1024);
+    }
+  }
+};
 
 template <int NMT, int D>
 __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
@@ -232,8 +316,16 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   // candidate counts of all four rows, tracked identically by every wave
   int cnt[kRows] = {0, 0, 0, 0};
   const uint64_t lt = lanemask_lt();
+  // B-operand LDS offsets of this lane (key row half*32 + lane%32, dims kk*16 + (lane/32)*8)
+  const int krow = half * 32 + (lane & 31);
+  int boff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    boff[kk] = krow * (D * 2) + (((2 * kk + (lane >> 5)) ^ C::swz(krow)) << 4);
+  KeyTileLoads<D> loads;
+  loads.init(wave);
 
-  issue_key_tile<D>(sm.tile[0], k, start, last, wave);
+  loads.issue(sm.tile[0], k, start, last, wave);
   wait_tile();      // the tile loads are invisible to the compiler: wait for them explicitly
   __syncthreads();  // q, w, tau init and the first tile have landed
 
@@ -244,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
       wait_tile();
       lds_barrier();  // tile `it` complete; compactions of the previous tile finished
     }
-    if (kb + kTileKeys <= last) issue_key_tile<D>(sm.tile[buf ^ 1], k, kb + kTileKeys, last, wave);
+    if (kb + kTileKeys <= last) loads.issue(sm.tile[buf ^ 1], k, kb + kTileKeys, last, wave);
 
     int n_pass = 0;
     uint64_t pm = 0;
@@ -255,15 +347,10 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
       const unsigned char *tile = sm.tile[buf];
       f32x16 acc[NMT];
 #pragma unroll
-      for (int m = 0; m < NMT; ++m) acc[m] = f32x16{};
-      const int krow = half * 32 + (lane & 31);
-#pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const int chunk = (2 * kk + (lane >> 5)) ^ C::swz(krow);
-        const bf16x8 b = as_bf16x8(
-            *reinterpret_cast<const u32x4 *>(tile + krow * (D * 2) + chunk * 16));
+        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4 *>(tile + boff[kk]));
 #pragma unroll
-        for (int m = 0; m < NMT; ++m) acc[m] = mfma32(qa[m][kk], b, acc[m]);
+        for (int m = 0; m < NMT; ++m) acc[m] = mfma32(qa[m][kk], b, kk == 0 ? f32x16{} : acc[m]);
       }
       float s = 0.0f;
 #pragma unroll
@@ -295,15 +382,23 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     if (need_compact) {
       lds_barrier();  // both halves' appends are visible
       if (half == 0 && cnt[row] > C::kCap - kTileKeys) {
-        const uint32_t tau = select_top_k(ck, cp, sm.hist[row], cnt[row], K);
+        int c2 = cnt[row];
+        uint32_t tau = prune_candidates(ck, cp, sm.hist[row], c2, K, sm.has_tau[row] != 0,
+                                        sm.tau[row]);
+        if (c2 > C::kCap - 2 * kTileKeys) {  // too many ties to make room: exact selection
+          tau = select_top_k(ck, cp, sm.hist[row], c2, K);
+          c2 = K;
+        }
         if (lane == 0) {
           sm.tau[row] = tau;
           sm.has_tau[row] = 1;
+          sm.exch[buf][row][0] = c2;
         }
       }
+      lds_barrier();  // new thresholds and counts are visible
 #pragma unroll
       for (int r = 0; r < kRows; ++r)
-        if (cnt[r] > C::kCap - kTileKeys) cnt[r] = K;
+        if (cnt[r] > C::kCap - kTileKeys) cnt[r] = sm.exch[buf][r][0];
     }
   }
 

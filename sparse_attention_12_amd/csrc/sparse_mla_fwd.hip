@@ -68,12 +68,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
   const int64_t t = blockIdx.x;
   const int h0 = wave * 16;
   const int g = lane >> 4;     // lane group
-  const int hl = lane & 15;    // head within the wave's tile (S^T column)
+  const int hl = lane & 15;    // head within the wave's tile
   const int lim = topk_length ? topk_length[t] : K;
   const int32_t *irow = idx + t * K;
   const int nchunks = (lim + kSlots - 1) / kSlots;
 
-  // q block of this wave as MFMA B operand: lane -> head hl, dims ks*32 + g*8 + [0,8)
+  // q block of this wave as the MFMA B operand: lane -> head hl, dims ks*32 + g*8 + [0,8)
   bf16x8 qf[kKSteps];
   {
     const int h = h0 + hl;
@@ -84,120 +84,142 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
       qf[ks] = as_bf16x8(v);
     }
   }
-  // the query's slot -> latent row map, then the first NBUF - 1 tiles
-  for (int j = threadIdx.x; j < lim; j += NW * 64) slot_rows[j] = irow[j];
+  // the query's slot -> latent row map (tail of the last chunk marked invalid)
+  for (int j = threadIdx.x; j < nchunks * kSlots; j += NW * 64)
+    slot_rows[j] = j < lim ? irow[j] : -1;
   __syncthreads();
+
+  // Per-lane LDS offsets, fixed for the whole kernel (the swizzle only permutes the low four
+  // bits of a chunk index, so a chunk 16*a + b lands at (16*a + (b ^ swz)) * 16).
+  //   S^T A operand, tile row mt*16 + hl, chunk ks*4 + g:  sbase[mt][ks & 3] + (ks >> 2) * 256
+  //   V (transposing reads), rows 4g + r4 and 16 + 4g + r4, element col n*16 + cq*4:
+  //                                                        vbase[j][n & 7] + (n >> 3) * 256
+  const int r4 = (lane & 15) >> 2;
+  const int cq = lane & 3;
+  int sbase[2][4], vbase[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sbase[mt][j] = TL::chunk_off(mt * 16 + hl, j * 4 + g);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    vbase[0][j] = TL::elem_off(g * 4 + r4, j * 16 + cq * 4);
+    vbase[1][j] = TL::elem_off(16 + g * 4 + r4, j * 16 + cq * 4);
+  }
+  // this lane's DMA targets: (tile row, byte offset inside the row) for each of its L loads
+  int dma_row[L], dma_off[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int pos = (i * NW + wave) * 64 + lane;
+    dma_row[i] = pos / TL::kChunks;
+    dma_off[i] = ((pos % TL::kChunks) ^ TL::swz(dma_row[i])) * 16;
+  }
+  auto issue = [&](int c) {
+    unsigned char *tile = smem + (c % NBUF) * TL::kBytes;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      int r = slot_rows[c * kSlots + dma_row[i]];
+      r = r < 0 ? 0 : r;
+      const unsigned char *src =
+          reinterpret_cast<const unsigned char *>(kv) + static_cast<int64_t>(r) * TL::kRowBytes +
+          dma_off[i];
+      dma16(src, tile + (i * NW + wave) * 1024);
+    }
+  };
 #pragma unroll
   for (int c = 0; c < NBUF - 1; ++c)
-    if (c < nchunks) TL::template issue<NW>(smem + c * TL::kBytes, kv, slot_rows, c * kSlots, lim, wave);
+    if (c < nchunks) issue(c);
 
-  f32x4 o[kDv / 16];
+  f32x4 o[kDv / 16];  // O^T tiles: o[n][i] = O[head hl][channel 16n + 4g + i]
 #pragma unroll
   for (int n = 0; n < kDv / 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max (base-2 logits) of head hl
+  // reference max (base-2 logits) of head hl; a finite floor keeps exp2(x - m_run) = 0 for
+  // masked slots (x = -inf) even before the first valid slot
+  float m_run = -1e30f;
   float l_run = 0.0f;       // this lane's partial softmax denominator of head hl
-  const int r4 = (lane & 15) >> 2;  // 4-lane block within the 16-lane group
-  const int cq = lane & 3;
 
   for (int c = 0; c < nchunks; ++c) {
     const int ahead = min(NBUF - 2, nchunks - 1 - c);  // later tiles already issued
     wait_tiles_ahead<L, NBUF>(ahead);
     lds_barrier();  // tile c is complete in LDS; buffer (c - 1) % NBUF is free
-    if (c + NBUF - 1 < nchunks)
-      TL::template issue<NW>(smem + ((c + NBUF - 1) % NBUF) * TL::kBytes, kv, slot_rows,
-                             (c + NBUF - 1) * kSlots, lim, wave);
+    if (c + NBUF - 1 < nchunks) issue(c + NBUF - 1);
     const unsigned char *tile = smem + (c % NBUF) * TL::kBytes;
-    bool valid[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot = c * kSlots + mt * 16 + g * 4 + i;
-        valid[mt][i] = slot < lim && slot_rows[slot] >= 0;
-      }
 
-  // ---- S^T = rows . q^T   (acc[mt][i] = S^T[16mt + 4g + i][hl])
+    // ---- S^T = rows . q^T   (acc[mt][i] = S^T[slot 16mt + 4g + i][head hl])
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-            tile + TL::chunk_off(mt * 16 + hl, ks * 4 + g)));
+            tile + sbase[mt][ks & 3] + (ks >> 2) * 256));
         acc[mt] = mfma16(a, qf[ks], acc[mt]);
       }
     }
 
-    // ---- online softmax (base 2); lanes hl, hl^16, hl^32, hl^48 share head hl
+    // ---- online softmax (base 2) with a lazily raised reference max: the reference only
+    // moves when the running max exceeds it by more than 2^8, so P <= 256 and O is rescaled
+    // only a handful of times per row.  Lanes hl, hl^16, hl^32, hl^48 share head hl.
+    const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(&slot_rows[c * kSlots + g * 4]);
+    const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(&slot_rows[c * kSlots + 16 + g * 4]);
     float x[2][4];
     float cmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[mt][i] = valid[mt][i] ? acc[mt][i] * scale_log2 : -INFINITY;
-        cmax = fmaxf(cmax, x[mt][i]);
-      }
-    cmax = fmaxf(cmax, xor_lane(cmax, 16));
-    cmax = fmaxf(cmax, xor_lane(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const bool none = m_new == -INFINITY;
-    const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[2][4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[mt][i] = none ? 0.0f : __builtin_amdgcn_exp2f(x[mt][i] - m_new);
-        psum += p[mt][i];
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // ---- rescale O rows (O row (4g + i) belongs to head 4g + i, held by lane 4g + i)
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a_i = __shfl(alpha, g * 4 + i, 64);
-#pragma unroll
-        for (int n = 0; n < kDv / 16; ++n) o[n][i] *= a_i;
-      }
+    for (int i = 0; i < 4; ++i) {
+      x[0][i] = static_cast<int32_t>(rv0[i]) >= 0 ? acc[0][i] * scale_log2 : -INFINITY;
+      x[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? acc[1][i] * scale_log2 : -INFINITY;
+      cmax = fmaxf(cmax, fmaxf(x[0][i], x[1][i]));
     }
+    cmax = fmaxf(cmax, xor_lane(cmax, 16));
+    cmax = fmaxf(cmax, swap_halves(cmax));
+    if (__ballot(cmax > m_run + 8.0f)) {
+      const float m_new = cmax > m_run + 8.0f ? cmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first raise
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < kDv / 16; ++n) o[n] *= alpha;
+      m_run = m_new;
+    }
+    float p[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[mt][i] = __builtin_amdgcn_exp2f(x[mt][i] - m_run);  // 0 for masked slots
+        l_run += p[mt][i];
+      }
 
-    // ---- O += P . V   (slot k-index 8g + j <-> tile row 4g + j (j < 4), 16 + 4g + j - 4)
+    // ---- O^T += V^T . P^T   (slot k-index 8g + j <-> tile row 4g + j (j < 4), 16 + 4g + j - 4)
     u32x4 pw;
     pw[0] = pack_bf16x2(p[0][0], p[0][1]);
     pw[1] = pack_bf16x2(p[0][2], p[0][3]);
     pw[2] = pack_bf16x2(p[1][0], p[1][1]);
     pw[3] = pack_bf16x2(p[1][2], p[1][3]);
-    const bf16x8 pa = as_bf16x8(pw);
-    const int row0 = g * 4 + r4, row1 = 16 + g * 4 + r4;
+    const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
     for (int n = 0; n < kDv / 16; ++n) {
-      const u32x2 lo = lds_read_tr16(tile + TL::elem_off(row0, n * 16 + cq * 4));
-      const u32x2 hi = lds_read_tr16(tile + TL::elem_off(row1, n * 16 + cq * 4));
-      const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
-      o[n] = mfma16(pa, as_bf16x8(b), o[n]);
+      const u32x2 lo = lds_read_tr16(tile + vbase[0][n & 7] + (n >> 3) * 256);
+      const u32x2 hi = lds_read_tr16(tile + vbase[1][n & 7] + (n >> 3) * 256);
+      const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+      o[n] = mfma16(as_bf16x8(va), pb, o[n]);
     }
   }
 
   // ---- finalize: denominator over the four lane groups, normalise, write
   float l_tot = l_run + xor_lane(l_run, 16);
-  l_tot += xor_lane(l_tot, 32);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (g == 0 && h0 + hl < H) {
-    lse[t * H + h0 + hl] =
-        l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  }
+  l_tot += swap_halves(l_tot);
+  const int h = h0 + hl;
+  if (h < H) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (g == 0)
+      lse[t * H + h] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    uint16_t *orow = out + (t * H + h) * kDv + g * 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = h0 + g * 4 + i;
-    const float s_i = __shfl(inv, g * 4 + i, 64);
-    if (h < H) {
-      uint16_t *orow = out + (t * H + h) * kDv + hl;
-#pragma unroll
-      for (int n = 0; n < kDv / 16; ++n) orow[n * 16] = f32_to_bf16(o[n][i] * s_i);
+    for (int n = 0; n < kDv / 16; ++n) {
+      u32x2 v;
+      v[0] = pack_bf16x2(o[n][0] * inv, o[n][1] * inv);
+      v[1] = pack_bf16x2(o[n][2] * inv, o[n][3] * inv);
+      *reinterpret_cast<u32x2 *>(orow + n * 16) = v;
     }
   }
 }
