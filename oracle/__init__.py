@@ -44,6 +44,10 @@ def lib():
                                           C.c_int32, C.c_int32, C.c_int64, C.c_int64, i32p, i32p,
                                           C.c_void_p]
         L.oracle_indexer_topk.restype = C.c_int
+        L.oracle_indexer_topk_rows.argtypes = [u16p, u16p, f32p, i32p, C.c_int32, C.c_int64,
+                                               C.c_int32, C.c_int32, C.c_int32, C.c_int64,
+                                               C.c_int64, C.c_int64, i32p, i32p, C.c_void_p]
+        L.oracle_indexer_topk_rows.restype = C.c_int
         L.oracle_sparse_mla_fwd.argtypes = [u16p, u16p, i32p, C.c_void_p, C.c_int64, C.c_int64,
                                             C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
                                             C.c_int64, C.c_int64, f64p, f64p]
@@ -114,6 +118,33 @@ def indexer_topk(q_idx, k_idx, w, cu_seqlens, K: int, rows=None):
                                      cu.shape[0] - 1, T, H, D, K, r0, r1, idx, ln,
                                      kth.ctypes.data), "indexer_topk")
     return idx, ln, kth
+
+
+def indexer_topk_rows(q_rows, k_idx, w_rows, cu_seqlens, K: int, row_begin: int):
+    """Top-k of rows [row_begin, row_begin + len(q_rows)) given only those rows' q and w."""
+    q = _u16(q_rows)
+    k = _u16(k_idx)
+    wt = _np(w_rows, np.float32)
+    cu = _np(cu_seqlens, np.int32)
+    n, H, D = q.shape
+    T = k.shape[0]
+    idx = np.zeros((n, K), np.int32)
+    ln = np.zeros(n, np.int32)
+    kth = np.zeros(n, np.float64)
+    _check(lib().oracle_indexer_topk_rows(q.reshape(-1), k.reshape(-1), wt.reshape(-1), cu,
+                                          cu.shape[0] - 1, T, H, D, K, row_begin, row_begin + n,
+                                          row_begin, idx, ln, kth.ctypes.data),
+           "indexer_topk_rows")
+    return idx, ln, kth
+
+
+def indexer_score_rows(q_row, k_idx, w_row, s: int) -> float:
+    """Score of one query row (q_row [H,D], w_row [H]) against key s."""
+    q = _u16(q_row)
+    k = _u16(k_idx)
+    wt = _np(w_row, np.float32)
+    H, D = q.shape
+    return lib().oracle_indexer_score(q.reshape(-1), k.reshape(-1), wt.reshape(-1), H, D, 0, s)
 
 
 def _opt_i32(x):

@@ -90,19 +90,24 @@ int oracle_thd_metadata(const int32_t *cu, int32_t B, int64_t T, int32_t K,
 /* [API] cudnn_indexer_topk, _compact_and_sort_indices).                      */
 /* ------------------------------------------------------------------------ */
 
-/* One score I(t,s) in double. */
-double oracle_indexer_score(const uint16_t *q, const uint16_t *k, const float *w,
-                            int32_t H, int32_t D, int64_t t, int64_t s) {
+/* One score I(t,s) in double; q and w hold query rows starting at global row q_row0. */
+static double indexer_score_rows(const uint16_t *q, const uint16_t *k, const float *w, int32_t H,
+                                 int32_t D, int64_t q_row0, int64_t t, int64_t s) {
   double total = 0.0;
   for (int32_t h = 0; h < H; ++h) {
     double dot = 0.0;
-    const uint16_t *qr = q + ((size_t)t * H + h) * D;
+    const uint16_t *qr = q + ((size_t)(t - q_row0) * H + h) * D;
     const uint16_t *kr = k + (size_t)s * D;
     for (int32_t d = 0; d < D; ++d) dot += bf16_to_double(qr[d]) * bf16_to_double(kr[d]);
     double relu = dot > 0.0 ? dot : 0.0;
-    total += (double)w[(size_t)t * H + h] * relu;
+    total += (double)w[(size_t)(t - q_row0) * H + h] * relu;
   }
   return total + 0.0; /* folds a -0.0 sum to +0.0 */
+}
+
+double oracle_indexer_score(const uint16_t *q, const uint16_t *k, const float *w,
+                            int32_t H, int32_t D, int64_t t, int64_t s) {
+  return indexer_score_rows(q, k, w, H, D, 0, t, s);
 }
 
 typedef struct {
@@ -129,11 +134,12 @@ static int by_pos(const void *a, const void *b) {
  * by -1 ([API] _compact_and_sort_indices "canonicalize ... return valid
  * lengths").  idx_out is [(row_end-row_begin) x K], len_out is
  * [row_end-row_begin].  kth_score (nullable) receives the n-th best score of
- * each row (the selection threshold). */
-int oracle_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
-                        const int32_t *cu, int32_t B, int64_t T, int32_t H, int32_t D,
-                        int32_t K, int64_t row_begin, int64_t row_end, int32_t *idx_out,
-                        int32_t *len_out, double *kth_score) {
+ * each row (the selection threshold).  q and w hold the query rows from global row q_row0
+ * on (0 for full arrays; row_begin when only the selected rows are passed). */
+int oracle_indexer_topk_rows(const uint16_t *q, const uint16_t *k, const float *w,
+                             const int32_t *cu, int32_t B, int64_t T, int32_t H, int32_t D,
+                             int32_t K, int64_t row_begin, int64_t row_end, int64_t q_row0,
+                             int32_t *idx_out, int32_t *len_out, double *kth_score) {
   if (B < 1 || H < 1 || D < 1 || K < 1 || row_begin < 0 || row_end > T || row_begin > row_end)
     return ORACLE_EINVAL;
   if (cu[0] != 0 || (int64_t)cu[B] != T) return ORACLE_EINVAL;
@@ -153,7 +159,7 @@ int oracle_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
       continue;
     }
     for (int64_t s = start; s <= t; ++s) {
-      keys[s - start].score = oracle_indexer_score(q, k, w, H, D, t, s);
+      keys[s - start].score = indexer_score_rows(q, k, w, H, D, q_row0, t, s);
       keys[s - start].pos = (int32_t)s;
     }
     qsort(keys, (size_t)L, sizeof(scored_key), by_rank);
@@ -166,6 +172,14 @@ int oracle_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
     free(keys);
   }
   return err;
+}
+
+int oracle_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
+                        const int32_t *cu, int32_t B, int64_t T, int32_t H, int32_t D,
+                        int32_t K, int64_t row_begin, int64_t row_end, int32_t *idx_out,
+                        int32_t *len_out, double *kth_score) {
+  return oracle_indexer_topk_rows(q, k, w, cu, B, T, H, D, K, row_begin, row_end, 0, idx_out,
+                                  len_out, kth_score);
 }
 
 /* ------------------------------------------------------------------------ */
