@@ -141,8 +141,11 @@ int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *
  *   idx [T_q, K] int32          topk_length [T_q] int32 or NULL
  *   out [T_q, H, D_v] bf16 (out)   lse [T_q, H] fp32 (out)
  * `scale` is applied unchanged.  Supported: 1 <= H <= 64, D_qk in {512, 576},
- * D_v = 512, 1 <= K <= 4096, T_kv >= 1 whenever T_q > 0.  When topk_length is given the prefix must hold
- * valid indices (it is read without checking for -1 beyond the -1 test).
+ * D_v = 512, 1 <= K <= 4096, T_kv >= 1 whenever T_q > 0, and kv below 4 GiB
+ * (T_kv * D_qk * 2 <= 2^32 - 1; latent rows are addressed with 32-bit byte
+ * offsets).  Anything else returns DSA_ERR_INVALID_VALUE.  When topk_length is
+ * given the prefix must hold valid indices (it is read without checking for -1
+ * beyond the -1 test).
  * ------------------------------------------------------------------------ */
 int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                        const int32_t *topk_length, int64_t T_q, int64_t T_kv, int32_t H,
@@ -165,6 +168,7 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
  *   dq  [T_q, H, D_qk] bf16 (out)   dkv [T_kv, D_qk] fp32 (out / accumulated)
  * flags: DSA_BWD_ACCUMULATE_DKV adds into dkv (query-chunked execution);
  * without it dkv is overwritten.  Workspace: dsa_sparse_mla_bwd_workspace_size.
+ * Same shape limits as dsa_sparse_mla_fwd.
  * ------------------------------------------------------------------------ */
 size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk);
 int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,

@@ -233,6 +233,10 @@ static int check_attention_args(const char *who, const uint16_t *q, const uint16
     return fail(DSA_ERR_INVALID_VALUE, "%s: scale must be a positive finite number", who);
   if (T_q > 0 && T_kv < 1)
     return fail(DSA_ERR_INVALID_VALUE, "%s: T_kv must be >= 1 when T_q > 0", who);
+  // latent rows are addressed with 32-bit byte offsets from kv
+  if (T_kv * static_cast<int64_t>(D_qk) * 2 > static_cast<int64_t>(UINT32_MAX))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: kv [%lld, %d] exceeds 4 GiB", who,
+                static_cast<long long>(T_kv), D_qk);
   if (T_q > 0 && (!q || !idx || !kv))
     return fail(DSA_ERR_INVALID_VALUE, "%s: NULL tensor pointer", who);
   if (!aligned16(q) || !aligned16(kv))

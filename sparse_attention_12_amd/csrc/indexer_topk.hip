@@ -7,23 +7,24 @@
 //
 // Work group = 8 waves = 4 consecutive query rows of one sequence, two waves per row.  The
 // group streams the rows' common causal key range in tiles of 64 keys, loaded straight into
-// LDS (double buffered); the two waves of a row take the lower and upper 32 keys of each tile.
+// LDS (three buffers, so a tile's loads have two tiles of compute to land); the two waves of a
+// row take the lower and upper 32 keys of each tile.
 // A wave multiplies its row's [H x D] query block by its 32 keys with 32x32x16 bf16 MFMAs
 // (heads on the M axis, keys on N), so the ReLU, the head weights and the head sum are applied
 // to fp32 accumulators in registers: a lane ends up holding the partial sum over 32 heads of
 // one key, and one cross-half exchange finishes it.  The two waves of a row sit on the same
 // SIMD, so one's VALU epilogue overlaps the other's MFMAs.
 //
-// Streaming top-k: each row owns a candidate buffer of (orderable score, key position) in LDS.
-// Keys arrive in ascending position order (tile by tile, lower half before upper half, lane
-// order inside a half) and are appended in that order when their score exceeds the row's
-// threshold tau (initially none).  When the buffer nears capacity one wave of the row runs an
-// exact radix select (4 passes of 8 bits over the orderable uint32 scores) for the K-th
-// largest score, and a stable partition keeps the K best, ties resolved to the lower position
-// because the buffer is in position order.  tau becomes the K-th score; later keys have higher
-// positions, so a later key with score == tau can never enter the top K and the strict test
-// score > tau is exact.  The buffer therefore always holds the exact running top K in
-// ascending position order, which is also the required output order.
+// Streaming top-k: each row owns a candidate buffer of (orderable score, key position) pairs in
+// LDS.  A key is appended (at a slot taken with an LDS atomic, so in no particular order) when
+// its score exceeds the row's threshold tau (initially none).  When a row nears capacity it is
+// pruned with one 256-bin counting pass: the bin holding the K-th largest score gives a new
+// tau that never exceeds the true K-th largest score, and every candidate at or below it is
+// dropped.  Keys arrive in ascending position order, so a later key equal to the K-th score
+// would lose the tie to the candidates already kept: the strict test score > tau is exact.  At
+// the end an exact selection (256-bin histograms narrowing the K-th score, ties resolved to the
+// lower positions) keeps exactly K candidates, and a bitmap over the row's key range writes
+// their positions in ascending order.
 //
 // Rows with L_t <= K select their whole causal prefix, which is written without scoring.
 #include "dsa_common.h"
@@ -41,8 +42,9 @@ constexpr int kBins = 256;
 
 template <int D>
 struct IndexerCfg {
-  // candidate entries per row: as many as fit next to two key tiles
-  static constexpr int kCap = D == 128 ? 3840 : 4096;
+  static constexpr int kNBuf = 3;  // key tile buffers
+  // candidate entries per row: as many as fit next to the key tiles in 160 KB of LDS
+  static constexpr int kCap = D == 128 ? 3328 : 4096;
   static constexpr int kChunks = D / 8;                      // 16-byte chunks per key
   static constexpr int kTileBytes = kTileKeys * D * 2;
   static constexpr int kLoads = kTileKeys * kChunks / 64;    // wave-wide DMAs per tile
@@ -55,11 +57,11 @@ template <int D>
 struct IndexerSmem {
   uint32_t cand_key[kRows][IndexerCfg<D>::kCap];
   int32_t cand_pos[kRows][IndexerCfg<D>::kCap];
-  uint32_t hist[kRows][kBins];
-  int32_t exch[2][kRows][2];  // per-tile candidate counts of the two halves (double buffered)
-  uint32_t tau[kRows];
+  __align__(16) uint32_t hist[kRows][kBins];
+  __align__(16) int32_t cnt[kRows];  // candidates per row (appended with LDS atomics)
+  uint32_t tau[kRows];                // per-row threshold: later keys enter only if above it
   int32_t has_tau[kRows];
-  __align__(16) unsigned char tile[2][IndexerCfg<D>::kTileBytes];
+  __align__(16) unsigned char tile[IndexerCfg<D>::kNBuf][IndexerCfg<D>::kTileBytes];
 };
 
 // Monotone map float -> uint32 (larger float -> larger key); +0 and -0 map alike.
@@ -69,173 +71,275 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Keep the K best of the wave's `cnt` candidates (in place, order preserving) and return the
-// K-th largest key.  Requires cnt >= K.  Executed by one wave.
-__device__ uint32_t select_top_k(uint32_t *ck, int32_t *cp, uint32_t *hist, int cnt, int K) {
+// ---- per-row candidate selection, executed by one wave ------------------------------------
+// A row's candidates are (key, position) pairs in two LDS arrays, in no particular order.
+// Loops read four consecutive entries per lane (ds_read_b128); entries at or beyond `cnt`
+// are masked.  Capacities are multiples of 4, so such reads stay inside the arrays.
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   const int lane = __lane_id();
-  wave_sync();
-  int need = K;
-  uint32_t prefix = 0, pmask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = lane; b < kBins; b += 64) hist[b] = 0u;
-    wave_sync();
-    for (int e0 = 0; e0 < cnt; e0 += 64) {
-      const int e = e0 + lane;
-      const uint32_t u = e < cnt ? ck[e] : 0u;
-      const bool in = e < cnt && (u & pmask) == prefix;
-      const uint32_t d = (u >> shift) & 0xFFu;
-      // all matching lanes on one digit (common for the leading digit): one add
-      const uint64_t inm = __ballot(in);
-      const uint32_t d0 = __shfl(d, __ffsll(static_cast<unsigned long long>(inm | 1ull)) - 1, 64);
-      const uint64_t same = __ballot(in && d == d0);
-      if (same == inm) {
-        if (inm != 0 && lane == 0) atomicAdd(&hist[d0], static_cast<uint32_t>(__popcll(inm)));
-      } else if (in) {
-        atomicAdd(&hist[d], 1u);
-      }
-    }
-    wave_sync();
-    // lane l owns bins 255-4l .. 252-4l, scanned from the top
-    const uint32_t h0 = hist[255 - 4 * lane], h1 = hist[254 - 4 * lane];
-    const uint32_t h2 = hist[253 - 4 * lane], h3 = hist[252 - 4 * lane];
-    const uint32_t c = h0 + h1 + h2 + h3;
-    uint32_t incl = c;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    const uint32_t excl = incl - c;
-    const bool mine = excl < static_cast<uint32_t>(need) && static_cast<uint32_t>(need) <= incl;
-    const uint64_t owner = __ballot(mine);
-    const int src = __ffsll(static_cast<unsigned long long>(owner)) - 1;
-    uint32_t digit = 0, above = 0;
-    if (mine) {
-      uint32_t a = excl;
-      const uint32_t n = static_cast<uint32_t>(need);
-      if (a + h0 >= n) {
-        digit = 255 - 4 * lane;
-      } else if ((a += h0) + h1 >= n) {
-        digit = 254 - 4 * lane;
-      } else if ((a += h1) + h2 >= n) {
-        digit = 253 - 4 * lane;
-      } else {
-        a += h2;
-        digit = 252 - 4 * lane;
-      }
-      above = a;
-    }
-    digit = __shfl(digit, src, 64);
-    above = __shfl(above, src, 64);
-    need -= static_cast<int>(above);
-    prefix |= digit << shift;
-    pmask |= 0xFFu << shift;
-    wave_sync();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = __shfl_up(v, off, 64);
+    if (lane >= off) v += x;
   }
-  const uint32_t tau = prefix;  // exact K-th largest key; `need` copies of it are kept
-  int written = 0, eq_seen = 0;
-  const uint64_t lt = lanemask_lt();
-  for (int base = 0; base < cnt; base += 64) {
-    const int e = base + lane;
-    const bool in = e < cnt;
-    const uint32_t u = in ? ck[e] : 0u;
-    const int32_t p = in ? cp[e] : 0;
-    const bool gt = in && u > tau;
-    const bool eq = in && u == tau;
-    const uint64_t eqm = __ballot(eq);
-    const bool keep = gt || (eq && eq_seen + __popcll(eqm & lt) < need);
-    const uint64_t km = __ballot(keep);
-    if (keep) {
-      const int o = written + __popcll(km & lt);
-      ck[o] = u;
-      cp[o] = p;
-    }
-    written += __popcll(km);
-    eq_seen += __popcll(eqm);
-  }
-  wave_sync();
-  return tau;
+  return v;
 }
 
-// Streaming compaction: drop candidates that can no longer reach the top K, keeping at least
-// K of them, in one counting pass.  With lo = the current threshold (or the smallest key) and
-// hi = the largest key, the keys are binned by (u - lo) >> shift into at most 256 bins; the
-// bin holding the K-th largest key gives a new threshold tau' = lo + (bin << shift) - 1 with
-// at least K keys above it (so tau' never exceeds the true K-th largest key, and a later key
-// at or below tau' can never enter the top K).  Keys <= tau' are removed with an order
-// preserving partition.  Returns tau'; `cnt` becomes the number kept (>= K).
-__device__ uint32_t prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int &cnt, int K,
-                                     bool has_tau, uint32_t tau) {
+// Smallest and largest of ck[0, cnt) (cnt >= 1).
+__device__ __forceinline__ void key_range(const uint32_t *ck, int cnt, uint32_t &lo,
+                                          uint32_t &hi) {
   const int lane = __lane_id();
-  wave_sync();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int e = lane; e < cnt; e += 64) {
-    const uint32_t u = ck[e];
-    lo = min(lo, u);
-    hi = max(hi, u);
+  lo = 0xFFFFFFFFu;
+  hi = 0u;
+  for (int e = 4 * lane; e < cnt; e += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(ck + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e + j < cnt) {
+        lo = min(lo, v[j]);
+        hi = max(hi, v[j]);
+      }
   }
+#pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off, 64)));
     hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off, 64)));
   }
-  if (has_tau) lo = tau + 1u;  // every candidate is above the current threshold
-  const uint32_t span = hi - lo;
-  const int shift = span < 256u ? 0 : 32 - __clz(span) - 8;
-  for (int b = lane; b < kBins; b += 64) hist[b] = 0u;
-  wave_sync();
-  for (int e = lane; e < cnt; e += 64) atomicAdd(&hist[(ck[e] - lo) >> shift], 1u);
-  wave_sync();
-  // bins scanned from the top: lane l owns bins 255-4l .. 252-4l
-  const uint32_t h0 = hist[255 - 4 * lane], h1 = hist[254 - 4 * lane];
-  const uint32_t h2 = hist[253 - 4 * lane], h3 = hist[252 - 4 * lane];
-  const uint32_t c = h0 + h1 + h2 + h3;
-  uint32_t incl = c;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
-  const uint32_t excl = incl - c;
-  const uint32_t n = static_cast<uint32_t>(K);
-  const bool mine = excl < n && n <= incl;
-  const uint64_t owner = __ballot(mine);
-  const int src = __ffsll(static_cast<unsigned long long>(owner)) - 1;
-  uint32_t bin = 0;
-  if (mine) {
-    uint32_t a = excl;
-    if (a + h0 >= n) bin = 255 - 4 * lane;
-    else if ((a += h0) + h1 >= n) bin = 254 - 4 * lane;
-    else if ((a += h1) + h2 >= n) bin = 253 - 4 * lane;
-    else bin = 252 - 4 * lane;
-  }
-  bin = __shfl(bin, src, 64);
-  const uint32_t floor_key = lo + (bin << shift);  // keys >= floor_key: at least K of them
-  int written = 0;
-  const uint64_t lt = lanemask_lt();
-  for (int base = 0; base < cnt; base += 64) {
-    const int e = base + lane;
-    const bool in = e < cnt;
-    const uint32_t u = in ? ck[e] : 0u;
-    const int32_t p = in ? cp[e] : 0;
-    const bool keep = in && u >= floor_key;
-    const uint64_t km = __ballot(keep);
-    if (keep) {
-      const int o = written + __popcll(km & lt);
-      ck[o] = u;
-      cp[o] = p;
-    }
-    written += __popcll(km);
-  }
-  wave_sync();
-  cnt = written;
-  return floor_key - 1u;  // floor_key > lo >= 1 whenever keys were dropped
 }
 
-// DMA targets of this wave's loads of a key tile: key index inside the tile and byte offset
-// inside the key row (keys beyond `last` repeat key `last`; they lie beyond every row of the
-// group and are never selected).
+// Bin width exponent for the key range [lo, hi]: (hi - lo) >> shift < 256.
+__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
+  const uint32_t span = hi - lo;
+  return span < 256u ? 0 : 32 - __clz(static_cast<int>(span)) - 8;
+}
+
+// 256-bin histogram of the keys in [lo, hi], bin = (u - lo) >> shift.
+__device__ void key_histogram(const uint32_t *ck, int cnt, uint32_t lo, uint32_t hi, int shift,
+                              uint32_t *hist) {
+  const int lane = __lane_id();
+  *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+  wave_sync();
+  for (int e = 4 * lane; e < cnt; e += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(ck + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e + j < cnt && v[j] >= lo && v[j] <= hi) atomicAdd(&hist[(v[j] - lo) >> shift], 1u);
+  }
+  wave_sync();
+}
+
+// The bin holding the need-th largest key of a 256-bin histogram (1 <= need <= total); `above`
+// receives the number of keys in higher bins.
+__device__ __forceinline__ uint32_t bin_from_top(const uint32_t *hist, uint32_t need,
+                                                 uint32_t &above) {
+  const int lane = __lane_id();
+  // lane l owns bins 255-4l .. 252-4l, i.e. hist[252-4l .. 255-4l] read as one vector
+  const u32x4 hv = *reinterpret_cast<const u32x4 *>(hist + 252 - 4 * lane);
+  const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
+  const uint32_t incl = wave_incl_scan(c);
+  const uint32_t excl = incl - c;
+  const bool mine = excl < need && need <= incl;
+  const int src = __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
+  uint32_t bin = 0, a = excl;
+  if (mine) {
+    if (a + hv[3] >= need) {
+      bin = 255 - 4 * lane;
+    } else if ((a += hv[3]) + hv[2] >= need) {
+      bin = 254 - 4 * lane;
+    } else if ((a += hv[2]) + hv[1] >= need) {
+      bin = 253 - 4 * lane;
+    } else {
+      a += hv[1];
+      bin = 252 - 4 * lane;
+    }
+  }
+  above = __shfl(a, src, 64);
+  return __shfl(bin, src, 64);
+}
+
+// Keeps the entries for which keep(key, position) holds, packed at the front (order not
+// preserved); returns their number.  In place: an iteration writes below the end of the block
+// it has just read, and a wave's LDS operations complete in order.
+template <typename Keep>
+__device__ int compact_candidates(uint32_t *ck, int32_t *cp, int cnt, Keep keep) {
+  const int lane = __lane_id();
+  const uint64_t lt = lanemask_lt();
+  int written = 0;
+  for (int base = 0; base < cnt; base += 256) {
+    const int e = base + 4 * lane;
+    u32x4 v = {0u, 0u, 0u, 0u}, p = {0u, 0u, 0u, 0u};
+    if (e < cnt) {
+      v = *reinterpret_cast<const u32x4 *>(ck + e);
+      p = *reinterpret_cast<const u32x4 *>(cp + e);
+    }
+    bool kp[4];
+    uint64_t m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kp[j] = e + j < cnt && keep(v[j], static_cast<int32_t>(p[j]));
+      m[j] = __ballot(kp[j]);
+    }
+    int off = written;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kp[j]) {
+        const int o = off + __popcll(m[j] & lt);
+        ck[o] = v[j];
+        cp[o] = static_cast<int32_t>(p[j]);
+      }
+      off += __popcll(m[j]);
+    }
+    written = off;
+  }
+  wave_sync();
+  return written;
+}
+
+// Number of entries with key == tau and position <= pcut.
+__device__ int count_ties_upto(const uint32_t *ck, const int32_t *cp, int cnt, uint32_t tau,
+                               int64_t pcut) {
+  const int lane = __lane_id();
+  int c = 0;
+  for (int e = 4 * lane; e < cnt; e += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(ck + e);
+    const u32x4 p = *reinterpret_cast<const u32x4 *>(cp + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      c += (e + j < cnt && v[j] == tau && static_cast<int32_t>(p[j]) <= pcut) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  return c;
+}
+
+// Exact selection: keeps the K largest keys of ck[0, cnt) (cnt >= K), ties at the K-th key
+// resolved to the lower positions, and returns the K-th largest key.  The key is narrowed one
+// 256-bin histogram at a time (at most four levels); a tie straddling the cut is resolved by a
+// bisection on position.  `pos_lo`/`pos_hi` bound the positions.
+__device__ uint32_t select_exact(uint32_t *ck, int32_t *cp, uint32_t *hist, int &cnt, int K,
+                                 int64_t pos_lo, int64_t pos_hi) {
+  uint32_t lo, hi;
+  key_range(ck, cnt, lo, hi);
+  uint32_t need = static_cast<uint32_t>(K);
+  uint32_t tau = lo;
+  for (int level = 0; level < 4; ++level) {
+    if (hi == lo) {
+      tau = lo;
+      break;
+    }
+    const int shift = range_shift(lo, hi);
+    key_histogram(ck, cnt, lo, hi, shift, hist);
+    uint32_t above;
+    const uint32_t bin = bin_from_top(hist, need, above);
+    need -= above;
+    const uint32_t nlo = lo + (bin << shift);
+    const uint64_t nhi = static_cast<uint64_t>(nlo) + ((1ull << shift) - 1ull);
+    lo = nlo;
+    hi = nhi < hi ? static_cast<uint32_t>(nhi) : hi;
+    tau = lo;
+    if (shift == 0) break;
+  }
+  // `need` keys equal to tau belong to the top K
+  const int eq = count_ties_upto(ck, cp, cnt, tau, pos_hi);
+  if (eq == static_cast<int>(need)) {
+    cnt = compact_candidates(ck, cp, cnt, [tau](uint32_t u, int32_t) { return u >= tau; });
+    return tau;
+  }
+  // smallest position cut with `need` tied keys at or below it
+  int64_t a = pos_lo, b = pos_hi;
+  while (a < b) {
+    const int64_t mid = a + ((b - a) >> 1);
+    if (count_ties_upto(ck, cp, cnt, tau, mid) >= static_cast<int>(need)) b = mid;
+    else a = mid + 1;
+  }
+  const int64_t pcut = a;
+  cnt = compact_candidates(ck, cp, cnt, [tau, pcut](uint32_t u, int32_t p) {
+    return u > tau || (u == tau && p <= pcut);
+  });
+  return tau;
+}
+
+// Streaming compaction: drops candidates that can no longer reach the top K, keeping at least
+// K of them, in one counting pass.  With lo = the current threshold + 1 (or the smallest key)
+// and hi = the largest key, the keys are binned by (u - lo) >> shift; the bin holding the K-th
+// largest key gives floor_key = lo + (bin << shift) with at least K keys at or above it, so
+// floor_key never exceeds the true K-th largest key and a later key below it can never enter
+// the top K.  Keys below floor_key are removed.  Returns the new threshold floor_key - 1 (or
+// the old one when nothing could be dropped); `cnt` becomes the number kept (>= K).
+__device__ uint32_t prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int &cnt, int K,
+                                     bool has_tau, uint32_t tau) {
+  uint32_t lo, hi;
+  key_range(ck, cnt, lo, hi);
+  if (has_tau) lo = tau + 1u;  // every candidate is above the current threshold
+  const int shift = range_shift(lo, hi);
+  key_histogram(ck, cnt, lo, hi, shift, hist);
+  uint32_t above;
+  const uint32_t bin = bin_from_top(hist, static_cast<uint32_t>(K), above);
+  const uint32_t floor_key = lo + (bin << shift);
+  if (bin == 0) return has_tau ? tau : 0u;  // nothing below the K-th key's bin (0: no filter)
+  cnt = compact_candidates(ck, cp, cnt, [floor_key](uint32_t u, int32_t) {
+    return u >= floor_key;
+  });
+  return floor_key - 1u;
+}
+
+// Writes the positions of cp[0, K) (distinct, inside [start, t]) to out[0, K) in ascending
+// order: each 32768-position window is marked in a bitmap (1024 words of LDS) and read back
+// with a scan of per-lane bit counts.
+__device__ void write_sorted_positions(const int32_t *cp, int K, int64_t start, int64_t t,
+                                       uint32_t *bm, int32_t *out) {
+  const int lane = __lane_id();
+  constexpr int kWords = 1024;
+  constexpr int64_t kWin = 32 * kWords;
+  int done = 0;
+  for (int64_t w0 = start; w0 <= t; w0 += kWin) {
+#pragma unroll
+    for (int i = 0; i < kWords / 256; ++i)
+      *reinterpret_cast<u32x4 *>(bm + 4 * (lane + 64 * i)) = u32x4{0u, 0u, 0u, 0u};
+    wave_sync();
+    for (int e = lane; e < K; e += 64) {
+      const int64_t rel = cp[e] - w0;
+      if (rel >= 0 && rel < kWin) atomicOr(&bm[rel >> 5], 1u << (rel & 31));
+    }
+    wave_sync();
+    // lane l owns words [16 l, 16 l + 16)
+    uint32_t wv[16];
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(bm + 16 * lane + 4 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wv[4 * i + j] = v[j];
+        c += __popc(v[j]);
+      }
+    }
+    const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(c)));
+    int o = done + incl - c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t bits = wv[i];
+      while (bits) {
+        const int b = __ffs(static_cast<int>(bits)) - 1;
+        if (o < K) out[o] = static_cast<int32_t>(w0 + (16 * lane + i) * 32 + b);
+        ++o;
+        bits &= bits - 1u;
+      }
+    }
+    done += __shfl(incl, 63, 64);
+    wave_sync();
+  }
+}
+
+// This wave's share of the loads of one key tile: lane byte offsets relative to the tile's
+// first key, for the i-th load (key index inside the tile and swizzled 16-byte chunk).  Keys
+// beyond `last` (only in a group's final tile) are clamped to key `last`; they lie beyond every
+// row of the group and are never selected.
 template <int D>
 struct KeyTileLoads {
+  uint32_t voff[IndexerCfg<D>::kLoadsPerWave];
   int key[IndexerCfg<D>::kLoadsPerWave];
-  int off[IndexerCfg<D>::kLoadsPerWave];
   __device__ __forceinline__ void init(int wave) {
     using C = IndexerCfg<D>;
     const int lane = __lane_id();
@@ -243,18 +347,25 @@ struct KeyTileLoads {
     for (int i = 0; i < C::kLoadsPerWave; ++i) {
       const int pos = (wave * C::kLoadsPerWave + i) * 64 + lane;
       key[i] = pos / C::kChunks;
-      off[i] = ((pos % C::kChunks) ^ C::swz(key[i])) * 16;
+      voff[i] = key[i] * (D * 2) + ((pos % C::kChunks) ^ C::swz(key[i])) * 16;
     }
   }
-  __device__ __forceinline__ void issue(unsigned char *tile, const uint16_t *k, int64_t kb,
+  // tile_lds: LDS byte address of the destination tile buffer
+  __device__ __forceinline__ void issue(uint32_t tile_lds, const uint16_t *k, int64_t kb,
                                         int64_t last, int wave) const {
     using C = IndexerCfg<D>;
+    const unsigned char *base = reinterpret_cast<const unsigned char *>(k) + kb * (D * 2);
+    const uint32_t dst = tile_lds + wave * C::kLoadsPerWave * 1024;
+    if (kb + (kTileKeys - 1) <= last) {
 #pragma unroll
-    for (int i = 0; i < C::kLoadsPerWave; ++i) {
-      int64_t s = kb + key[i];
-      s = s <= last ? s : last;
-      dma16(reinterpret_cast<const unsigned char *>(k) + s * (D * 2) + off[i],
-            tile + (wave * C::kLoadsPerWave + i) * 1024);
+      for (int i = 0; i < C::kLoadsPerWave; ++i) dma16_sv(base, voff[i], dst + i * 1024);
+    } else {
+      const int lim = static_cast<int>(last - kb);  // in [0, 63)
+#pragma unroll
+      for (int i = 0; i < C::kLoadsPerWave; ++i) {
+        const int over = key[i] - lim;
+        dma16_sv(base, voff[i] - (over > 0 ? over * (D * 2) : 0), dst + i * 1024);
+      }
     }
   }
 };
@@ -270,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   IndexerSmem<D> &sm = *reinterpret_cast<IndexerSmem<D> *>(smem_raw);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = wave & (kRows - 1);  // waves w and w + 4 share a row (and a SIMD)
   const int half = wave >> 2;
   const int64_t last = groups[blockIdx.x];
@@ -287,6 +398,14 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     if (lane == 0) len_out[t] = static_cast<int32_t>(L);
   }
   if (last - start + 1 <= K) return;  // every row of the group is a whole prefix (uniform)
+
+  // tiles 0 and 1 in flight while the query block loads; tile it+2 is issued at the top of
+  // iteration it
+  const uint32_t tile_lds = lds_addr(&sm.tile[0][0]);
+  KeyTileLoads<D> loads;
+  loads.init(wave);
+  loads.issue(tile_lds, k, start, last, wave);
+  if (start + kTileKeys <= last) loads.issue(tile_lds + C::kTileBytes, k, start + kTileKeys, last, wave);
 
   // ---- this row's query block (A operand) and head weights
   bf16x8 qa[NMT][NKK];
@@ -310,11 +429,12 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   if (threadIdx.x < kRows) {
     sm.has_tau[threadIdx.x] = 0;
     sm.tau[threadIdx.x] = 0u;
+    sm.cnt[threadIdx.x] = 0;
   }
   uint32_t *ck = sm.cand_key[row];
   int32_t *cp = sm.cand_pos[row];
-  // candidate counts of all four rows, tracked identically by every wave
-  int cnt[kRows] = {0, 0, 0, 0};
+  uint32_t my_tau = 0u;  // this row's threshold (wave-uniform copy)
+  bool my_has_tau = false;
   const uint64_t lt = lanemask_lt();
   // B-operand LDS offsets of this lane (key row half*32 + lane%32, dims kk*16 + (lane/32)*8)
   const int krow = half * 32 + (lane & 31);
@@ -322,25 +442,57 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
     boff[kk] = krow * (D * 2) + (((2 * kk + (lane >> 5)) ^ C::swz(krow)) << 4);
-  KeyTileLoads<D> loads;
-  loads.init(wave);
 
-  loads.issue(sm.tile[0], k, start, last, wave);
-  wait_tile();      // the tile loads are invisible to the compiler: wait for them explicitly
-  __syncthreads();  // q, w, tau init and the first tile have landed
+  // finish the query block loads here (and, with them, the first two tiles) so that no
+  // compiler-visible load is pending inside the loop
+#pragma unroll
+  for (int m = 0; m < NMT; ++m) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) settle(qa[m][kk]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) settle(wv[m][i]);
+  }
+  wait_tile();
+  __syncthreads();  // q, w, counters and the first tiles have landed
 
-  int it = 0;
-  for (int64_t kb = start; kb <= last; kb += kTileKeys, ++it) {
-    const int buf = it & 1;
-    if (it > 0) {
-      wait_tile();
-      lds_barrier();  // tile `it` complete; compactions of the previous tile finished
+  int buf = 0;
+  for (int64_t kb = start; kb <= last; kb += kTileKeys) {
+    if (kb > start) {
+      if (kb + kTileKeys <= last) wait_vm<C::kLoadsPerWave>();  // the next tile may stay in flight
+      else wait_tile();
+      lds_barrier();  // this tile is complete everywhere; the previous one is free; every
+                      // append of the previous tile is visible
     }
-    if (kb + kTileKeys <= last) loads.issue(sm.tile[buf ^ 1], k, kb + kTileKeys, last, wave);
+    if (kb + 2 * kTileKeys <= last) {
+      const int nb = buf >= C::kNBuf - 2 ? buf + 2 - C::kNBuf : buf + 2;
+      loads.issue(tile_lds + nb * C::kTileBytes, k, kb + 2 * kTileKeys, last, wave);
+    }
 
-    int n_pass = 0;
-    uint64_t pm = 0;
-    uint32_t u = 0;
+    // ---- compaction, when a row may not have room for this tile's keys.  Every row far
+    // enough above K is compacted in the same round, so the rows of a group (whose counts grow
+    // alike) rarely stop the group more than once per round.
+    const int4 cv = *reinterpret_cast<const int4 *>(sm.cnt);
+    const int c0 = __builtin_amdgcn_readfirstlane(cv.x), c1 = __builtin_amdgcn_readfirstlane(cv.y);
+    const int c2 = __builtin_amdgcn_readfirstlane(cv.z), c3 = __builtin_amdgcn_readfirstlane(cv.w);
+    if (max(max(c0, c1), max(c2, c3)) > C::kCap - kTileKeys) {
+      const int mine = row == 0 ? c0 : row == 1 ? c1 : row == 2 ? c2 : c3;
+      if (half == 0 && mine > (C::kCap + K) / 2) {
+        int n = mine;
+        uint32_t tau = prune_candidates(ck, cp, sm.hist[row], n, K, my_has_tau, my_tau);
+        if (n > C::kCap - 2 * kTileKeys)  // too many ties to make room: exact selection
+          tau = select_exact(ck, cp, sm.hist[row], n, K, start, t);
+        if (lane == 0) {
+          sm.tau[row] = tau;
+          sm.has_tau[row] = 1;
+          sm.cnt[row] = n;
+        }
+      }
+      lds_barrier();  // new thresholds and counts are visible
+      my_has_tau = __builtin_amdgcn_readfirstlane(sm.has_tau[row]) != 0;
+      my_tau = __builtin_amdgcn_readfirstlane(sm.tau[row]);
+    }
+
+    // ---- scores of this wave's 32 keys, appended when above the row's threshold
     const int64_t kbase = kb + half * 32;
     const int64_t key = kbase + (lane & 31);
     if (compute && kbase <= t) {
@@ -352,62 +504,39 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
 #pragma unroll
         for (int m = 0; m < NMT; ++m) acc[m] = mfma32(qa[m][kk], b, kk == 0 ? f32x16{} : acc[m]);
       }
-      float s = 0.0f;
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
       for (int m = 0; m < NMT; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s = fmaf(wv[m][i], fmaxf(acc[m][i], 0.0f), s);
-      s += swap_halves(s);
-      u = orderable(s);
-      const bool has_tau = sm.has_tau[row] != 0;
-      const uint32_t tau = sm.tau[row];
-      const bool pass = lane < 32 && key <= t && (!has_tau || u > tau);
-      pm = __ballot(pass);
-      n_pass = __popcll(pm);
-    }
-    if (lane == 0) sm.exch[buf][row][half] = n_pass;
-    lds_barrier();
-    int need_compact = 0;
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const int n0 = sm.exch[buf][r][0], n1 = sm.exch[buf][r][1];
-      if (r == row && (pm >> lane) & 1ull) {
-        const int p = cnt[r] + (half ? n0 : 0) + __popcll(pm & lt);
-        ck[p] = u;
-        cp[p] = static_cast<int32_t>(key);
-      }
-      cnt[r] += n0 + n1;
-      need_compact |= cnt[r] > C::kCap - kTileKeys;
-    }
-    if (need_compact) {
-      lds_barrier();  // both halves' appends are visible
-      if (half == 0 && cnt[row] > C::kCap - kTileKeys) {
-        int c2 = cnt[row];
-        uint32_t tau = prune_candidates(ck, cp, sm.hist[row], c2, K, sm.has_tau[row] != 0,
-                                        sm.tau[row]);
-        if (c2 > C::kCap - 2 * kTileKeys) {  // too many ties to make room: exact selection
-          tau = select_top_k(ck, cp, sm.hist[row], c2, K);
-          c2 = K;
+        for (int i = 0; i < 16; i += 2) {
+          s0 = fmaf(wv[m][i], fmaxf(acc[m][i], 0.0f), s0);
+          s1 = fmaf(wv[m][i + 1], fmaxf(acc[m][i + 1], 0.0f), s1);
         }
-        if (lane == 0) {
-          sm.tau[row] = tau;
-          sm.has_tau[row] = 1;
-          sm.exch[buf][row][0] = c2;
+      float sc = s0 + s1;
+      sc += swap_halves(sc);
+      const uint32_t u = orderable(sc);
+      const bool pass = lane < 32 && key <= t && (!my_has_tau || u > my_tau);
+      const uint64_t pm = __ballot(pass);
+      if (pm) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&sm.cnt[row], __popcll(pm));
+        base = __builtin_amdgcn_readfirstlane(base);
+        if (pass) {
+          const int o = base + __popcll(pm & lt);
+          ck[o] = u;
+          cp[o] = static_cast<int32_t>(key);
         }
       }
-      lds_barrier();  // new thresholds and counts are visible
-#pragma unroll
-      for (int r = 0; r < kRows; ++r)
-        if (cnt[r] > C::kCap - kTileKeys) cnt[r] = sm.exch[buf][r][0];
     }
+    buf = buf == C::kNBuf - 1 ? 0 : buf + 1;
   }
 
-  lds_barrier();
+  lds_barrier();  // every append is visible; no tile load is in flight
   if (compute && half == 0) {
-    if (cnt[row] > K) select_top_k(ck, cp, sm.hist[row], cnt[row], K);
-    wave_sync();
-    int32_t *out = idx_out + t * K;
-    for (int j = lane; j < K; j += 64) out[j] = cp[j];
+    int n = __builtin_amdgcn_readfirstlane(sm.cnt[row]);
+    if (n > K) select_exact(ck, cp, sm.hist[row], n, K, start, t);
+    uint32_t *bm = reinterpret_cast<uint32_t *>(&sm.tile[0][0]) + row * 1024;
+    write_sorted_positions(cp, K, start, t, bm, idx_out + t * K);
     if (lane == 0) len_out[t] = K;
   }
 }

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
   int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + NBUF * TL::kBytes);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t t = blockIdx.x;
   const int h0 = wave * 16;
   const int g = lane >> 4;     // lane group
@@ -87,6 +87,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
   // the query's slot -> latent row map (tail of the last chunk marked invalid)
   for (int j = threadIdx.x; j < nchunks * kSlots; j += NW * 64)
     slot_rows[j] = j < lim ? irow[j] : -1;
+  // finish the q loads before the first tile load (see settle())
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) settle(qf[ks]);
   __syncthreads();
 
   // Per-lane LDS offsets, fixed for the whole kernel (the swizzle only permutes the low four
@@ -106,7 +109,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
     vbase[0][j] = TL::elem_off(g * 4 + r4, j * 16 + cq * 4);
     vbase[1][j] = TL::elem_off(16 + g * 4 + r4, j * 16 + cq * 4);
   }
-  // this lane's DMA targets: (tile row, byte offset inside the row) for each of its L loads
+  // this lane's DMA targets: (tile row, byte offset inside the row) for each of its L loads;
+  // the latent tensor is below 4 GiB (checked by the host), so a 32-bit offset from its base
+  // addresses any row
   int dma_row[L], dma_off[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) {
@@ -114,16 +119,15 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
     dma_row[i] = pos / TL::kChunks;
     dma_off[i] = ((pos % TL::kChunks) ^ TL::swz(dma_row[i])) * 16;
   }
+  const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int c) {
-    unsigned char *tile = smem + (c % NBUF) * TL::kBytes;
+    const uint32_t tile = smem_lds + (c % NBUF) * TL::kBytes + wave * 1024;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       int r = slot_rows[c * kSlots + dma_row[i]];
       r = r < 0 ? 0 : r;
-      const unsigned char *src =
-          reinterpret_cast<const unsigned char *>(kv) + static_cast<int64_t>(r) * TL::kRowBytes +
-          dma_off[i];
-      dma16(src, tile + (i * NW + wave) * 1024);
+      dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + dma_off[i],
+               tile + i * NW * 1024);
     }
   };
 #pragma unroll

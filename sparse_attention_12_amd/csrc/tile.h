@@ -38,6 +38,34 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
       : "memory");
 }
 
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+
+// As dma16, with the global address split into a wave-uniform base (SGPR pair) and a 32-bit
+// per-lane byte offset, and the destination given as a wave-uniform LDS byte address, so that
+// moving to the next tile is scalar arithmetic only.
+__device__ __forceinline__ void dma16_sv(const void *base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+
+// Make the compiler finish every load that produced `v` here (the value is pinned to VGPRs at
+// this point).  Used before a kernel's main loop: the tile loads are invisible to the
+// compiler, so a prologue load still pending at the loop header would make it wait for all
+// vector-memory traffic (tile loads included) at the first use inside every iteration.
+template <typename T>
+__device__ __forceinline__ void settle(T &v) {
+  asm volatile("" : "+v"(v));
+}
+
 // Wait until at most N vector-memory operations of this wave (including dma16) are still in
 // flight (they complete in issue order).
 template <int N>

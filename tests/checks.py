@@ -32,9 +32,15 @@ def check_topk_structure(idx: np.ndarray, ln: np.ndarray, rows: np.ndarray, star
         assert v.min() >= start[r] and v.max() <= t, f"row {t}: non-causal index"
 
 
-def check_topk_near_tie(q_idx, k_idx, w, gpu_idx: np.ndarray, ora_idx: np.ndarray,
+def check_topk_near_tie(q_rows, k_idx, w_rows, gpu_idx: np.ndarray, ora_idx: np.ndarray,
                         kth: np.ndarray, rows: np.ndarray):
-    """Set equality up to near-ties; returns the number of mismatching keys."""
+    """Set equality up to near-ties; returns the number of mismatching keys.
+
+    q_rows [n,H,D] / w_rows [n,H] hold the inputs of the n checked query rows (global row
+    numbers ``rows``); gpu_idx, ora_idx and kth are per checked row."""
+    q_rows = oracle._u16(q_rows)
+    k_idx = oracle._u16(k_idx)
+    w_rows = np.ascontiguousarray(oracle._np(w_rows, np.float32))
     mism = 0
     for r, t in enumerate(rows):
         g = set(gpu_idx[r][gpu_idx[r] >= 0].tolist())
@@ -44,11 +50,31 @@ def check_topk_near_tie(q_idx, k_idx, w, gpu_idx: np.ndarray, ora_idx: np.ndarra
             continue
         tau = kth[r]
         for s in diff:
-            score = oracle.indexer_score(q_idx, k_idx, w, int(t), int(s))
+            score = oracle.indexer_score_rows(q_rows[r], k_idx, w_rows[r], int(s))
             assert abs(score - tau) <= NEAR_TIE_REL * abs(tau), (
                 f"row {t} key {s}: score {score} vs k-th {tau} is not a near tie")
         mism += len(diff)
     return mism
+
+
+def check_topk_structure_device(idx, ln, seq_start, K: int):
+    """check_topk_structure over every row at once, with torch ops on the tensors' device."""
+    import torch
+    T = idx.shape[0]
+    t = torch.arange(T, device=idx.device, dtype=torch.int64)
+    L = t - seq_start.to(torch.int64) + 1
+    n = torch.clamp(L, max=K)
+    bad = (ln.to(torch.int64) != n).nonzero()
+    assert bad.numel() == 0, f"len wrong at rows {bad[:8].flatten().tolist()}"
+    pos = torch.arange(K, device=idx.device, dtype=torch.int64)
+    valid = pos[None, :] < n[:, None]
+    iv = idx.to(torch.int64)
+    assert bool(((iv == -1) | valid).all()), "-1 suffix broken"
+    lo_ok = (iv >= seq_start.to(torch.int64)[:, None]) & (iv <= t[:, None])
+    assert bool((lo_ok | ~valid).all()), "non-causal index"
+    if K > 1:
+        asc = (iv[:, 1:] > iv[:, :-1]) | ~valid[:, 1:]
+        assert bool(asc.all()), "prefix not strictly ascending"
 
 
 def max_abs(a, b) -> float:

@@ -87,6 +87,7 @@ def test_argument_errors_without_device(dsa):
     assert fwd(H=0) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(H=65) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(K=4097) == pkg.DSA_ERR_INVALID_VALUE
+    assert fwd(Tkv=(1 << 32) // 1152 + 1) == pkg.DSA_ERR_INVALID_VALUE and "4 GiB" in _err(dsa)
     assert fwd(K=0) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(sc=-1.0) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(sc=float("nan")) == pkg.DSA_ERR_INVALID_VALUE

@@ -1,0 +1,256 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The oracle cannot run whole workloads in seconds, so these tests check
+  * every row's top-k structure (len = min(K, L_t), ascending, unique, causal, -1 suffix),
+  * a sample of indexer rows (the longest rows of each sequence, rows around L_t = K, spread
+    rows) against the oracle under the near-tie rule,
+  * O, LSE and dq of sampled query rows against the oracle,
+  * dkv of the last rows of each sequence: under causal selection a key row s is only read by
+    query rows t >= s of its own sequence, so the oracle run over a sequence's last R query rows
+    yields the complete gradient of its last R key rows,
+  * the properties the pages state at any size: query chunks are independent and their key
+    gradients sum (one-shot == chunked), and zero-padding NoPE rows from 512 to 576 leaves the
+    result unchanged.
+
+All inputs come from dsa_inputs (seeded, drawn on the device); expected values come from
+oracle/ only.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as gen
+import oracle
+from tests import checks
+
+pytestmark = pytest.mark.gpu
+
+dev = "cuda"
+
+
+def _dsa():
+    import sparse_attention_12_amd as dsa
+    return dsa
+
+
+def _np(t):
+    return t.detach().to("cpu").numpy()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _indexer_sample(cu, K, n_spread=8, seed=0):
+    """Rows to check: the last 2 rows of each sequence, rows with L_t around K, spread rows."""
+    cu = list(cu)
+    rows = set()
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
+        if e == s:
+            continue
+        rows.update(r for r in (e - 2, e - 1, s, s + K - 2, s + K - 1, s + K) if s <= r < e)
+    g = np.random.default_rng(seed)
+    rows.update(g.integers(0, cu[-1], n_spread).tolist())
+    return np.array(sorted(rows), np.int64)
+
+
+def _attention_sample(cu, n_spread=6, seed=1):
+    cu = list(cu)
+    rows = set()
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
+        if e > s:
+            rows.update((s, e - 1))
+    g = np.random.default_rng(seed)
+    rows.update(g.integers(0, cu[-1], n_spread).tolist())
+    return np.array(sorted(rows), np.int64)
+
+
+def _check_indexer(inp, idx, ln, md, K, rows):
+    checks.check_topk_structure_device(idx, ln, md.seq_start, K)
+    rows_t = torch.from_numpy(rows).to(dev)
+    q_rows = inp["q_idx"][rows_t].cpu()
+    w_rows = inp["w"][rows_t].cpu()
+    k_all = oracle._u16(inp["k_idx"].cpu())
+    cu = _np(inp["cu_seqlens"])
+    gi, gl = _np(idx[rows_t]), _np(ln[rows_t])
+    mism = 0
+    for r, t in enumerate(rows):
+        ridx, rln, kth = oracle.indexer_topk_rows(q_rows[r:r + 1], k_all, w_rows[r:r + 1], cu, K,
+                                                  int(t))
+        assert rln[0] == gl[r], f"row {t}"
+        mism += checks.check_topk_near_tie(q_rows[r:r + 1], k_all, w_rows[r:r + 1],
+                                           gi[r:r + 1], ridx, kth, np.array([t]))
+    _log(f"indexer: {len(rows)} sampled rows, {mism} near-tie swaps")
+
+
+def _check_rows_fwd_bwd(att, idx, ln, out, lse, dq, rows, scale, d_v):
+    """O, LSE (and dq when given) of the query rows ``rows`` against the oracle."""
+    rows_t = torch.from_numpy(rows).to(dev)
+    q = att["q"][rows_t].cpu()
+    kv = att["kv"].cpu()
+    ii = _np(idx[rows_t])
+    ll = None if ln is None else _np(ln[rows_t])
+    ro, rl = oracle.sparse_mla_fwd(q, kv, ii, ll, scale, d_v)
+    e_o = checks.assert_close("out", _np(out[rows_t].float()), ro, checks.ATOL_OUT)
+    e_l = checks.assert_close("lse", _np(lse[rows_t]), rl, checks.ATOL_LSE)
+    msg = f"fwd rows {len(rows)}: out {e_o:.2e} lse {e_l:.2e}"
+    if dq is not None:
+        rdq, _ = oracle.sparse_mla_bwd(q, kv, ii, ll, att["dout"][rows_t].cpu(), scale)
+        e_q = checks.assert_close("dq", _np(dq[rows_t].float()), rdq, checks.ATOL_OUT)
+        msg += f" dq {e_q:.2e}"
+    _log(msg)
+
+
+def _check_dkv_tails(att, idx, ln, dkv, cu, scale, R):
+    """dkv of the last R key rows of every sequence (complete from the last R query rows)."""
+    kv = att["kv"].cpu()
+    worst = 0.0
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
+        r0 = max(s, e - R)
+        if e == r0:
+            continue
+        sl = slice(r0, e)
+        _, rdkv = oracle.sparse_mla_bwd(att["q"][sl].cpu(), kv, _np(idx[sl]),
+                                        None if ln is None else _np(ln[sl]),
+                                        att["dout"][sl].cpu(), scale)
+        worst = max(worst, checks.assert_close(f"dkv rows [{r0},{e})", _np(dkv[sl]),
+                                               rdkv[r0:e], checks.ATOL_OUT))
+    _log(f"dkv tails (R={R}): {worst:.2e}")
+
+
+class _Bufs:
+    """Output buffers and workspace laid out as the benchmark allocates them."""
+
+    def __init__(self, T, K, H, Dqk, Dv):
+        dsa = _dsa()
+        self.idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        self.len = torch.empty((T,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, H, Dv), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.dq = torch.empty((T, H, Dqk), dtype=torch.bfloat16, device=dev)
+        self.dkv = torch.empty((T, Dqk), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(dsa.lib().dsa_sparse_mla_bwd_workspace_size(T, T, H, Dqk),
+                              dtype=torch.uint8, device=dev)
+
+
+def _run_indexer(cfg_id, b):
+    dsa = _dsa()
+    w = gen.workload(cfg_id)
+    inp = gen.indexer_inputs(cfg_id, device=dev)
+    md = dsa.prepare_thd_metadata(inp["cu_seqlens"], w.topk, T=w.T)
+    dsa.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"], md, w.topk, idx=b.idx, length=b.len)
+    torch.cuda.synchronize()
+    return inp, md
+
+
+def _run_attention(att, b, scale, backward):
+    dsa = _dsa()
+    dsa.sparse_mla_fwd(att["q"], att["kv"], b.idx, scale, b.len, out=b.out, lse=b.lse)
+    if backward:
+        dsa.sparse_mla_bwd(att["q"], att["kv"], b.idx, b.out, b.lse, att["dout"], scale, b.len,
+                           dkv=b.dkv, dq=b.dq, workspace=b.ws)
+    torch.cuda.synchronize()
+
+
+def test_full_v32_T8192_indexer_and_forward():
+    """8192-token sequence, indexer 64x128, k=2048, attention H=64 576/512, forward only."""
+    w = gen.workload(2)
+    _log(f"workload {w.name}")
+    b = _Bufs(w.T, w.topk, w.heads, w.d_qk, w.d_v)
+    inp, md = _run_indexer(2, b)
+    _check_indexer(inp, b.idx, b.len, md, w.topk, _indexer_sample(w.cu_seqlens, w.topk))
+    del inp
+    att = gen.attention_inputs(2, device=dev)
+    _run_attention(att, b, w.scale, backward=False)
+    _check_rows_fwd_bwd(att, b.idx, b.len, b.out, b.lse, None, _attention_sample(w.cu_seqlens),
+                        w.scale, w.d_v)
+
+
+def test_full_thd_T32768_step():
+    """Packed THD batch of 32768 tokens (1024/3072/12288/16384): indexer -> fwd -> bwd."""
+    w = gen.workload(3)
+    _log(f"workload {w.name}")
+    b = _Bufs(w.T, w.topk, w.heads, w.d_qk, w.d_v)
+    inp, md = _run_indexer(3, b)
+    _check_indexer(inp, b.idx, b.len, md, w.topk, _indexer_sample(w.cu_seqlens, w.topk))
+    del inp
+    att = gen.attention_inputs(3, device=dev)
+    _run_attention(att, b, w.scale, backward=True)
+    _check_rows_fwd_bwd(att, b.idx, b.len, b.out, b.lse, b.dq, _attention_sample(w.cu_seqlens),
+                        w.scale, w.d_v)
+    _check_dkv_tails(att, b.idx, b.len, b.dkv, list(w.cu_seqlens), w.scale, R=6)
+
+
+def test_full_nope_kpool_T65536():
+    """NoPE shard: T=65536, H=8, width 512, k-pool top-k width 2051; one-shot, chunked (8192 and
+    ragged 6000) and zero-padded to 576."""
+    dsa = _dsa()
+    w = gen.workload(4)
+    _log(f"workload {w.name}")
+    T, K = w.T, w.topk
+    b = _Bufs(T, K, w.heads, w.d_qk, w.d_v)
+    kp = gen.kpool_indices(T, topk=K, tail=w.kpool_tail, device=dev)
+    b.idx.copy_(kp)
+    b.len.copy_((kp >= 0).sum(1).to(torch.int32))
+    del kp
+    att = gen.attention_inputs(4, device=dev)
+    _run_attention(att, b, w.scale, backward=True)
+    _check_rows_fwd_bwd(att, b.idx, b.len, b.out, b.lse, b.dq,
+                        _attention_sample(w.cu_seqlens, n_spread=10), w.scale, w.d_v)
+    _check_dkv_tails(att, b.idx, b.len, b.dkv, list(w.cu_seqlens), w.scale, R=16)
+
+    # query chunks: forward and dq bitwise equal to one-shot; key gradients sum over chunks
+    for chunk in (8192, 6000):
+        dkv_c = torch.zeros_like(b.dkv)
+        for r0 in range(0, T, chunk):
+            r1 = min(T, r0 + chunk)
+            q, ii, ll = att["q"][r0:r1], b.idx[r0:r1], b.len[r0:r1]
+            oc, lc = dsa.sparse_mla_fwd(q, att["kv"], ii, w.scale, ll)
+            dqc, _ = dsa.sparse_mla_bwd(q, att["kv"], ii, oc, lc, att["dout"][r0:r1], w.scale,
+                                        ll, dkv=dkv_c, accumulate=True)
+            assert torch.equal(oc, b.out[r0:r1]) and torch.equal(lc, b.lse[r0:r1]), (chunk, r0)
+            assert torch.equal(dqc, b.dq[r0:r1]), (chunk, r0)
+        torch.cuda.synchronize()
+        err = (dkv_c - b.dkv).abs().max().item()
+        scale_ref = b.dkv.abs().max().item()
+        assert err <= 1e-5 * scale_ref + 1e-4, f"chunk {chunk}: dkv diff {err} (max {scale_ref})"
+        _log(f"chunk {chunk}: dkv diff {err:.2e} of max {scale_ref:.2e}")
+
+    # zero-padding 512 -> 576 is exact for attention; padded channels get zero gradient
+    pad = lambda x: torch.nn.functional.pad(x, (0, 64))  # noqa: E731
+    q6, kv6 = pad(att["q"]), pad(att["kv"])
+    o6, l6 = dsa.sparse_mla_fwd(q6, kv6, b.idx, w.scale, b.len)
+    dq6, dkv6 = dsa.sparse_mla_bwd(q6, kv6, b.idx, o6, l6, att["dout"], w.scale, b.len)
+    torch.cuda.synchronize()
+    checks.assert_close("padded out", _np(o6.float()), _np(b.out.float()), checks.ATOL_OUT)
+    checks.assert_close("padded lse", _np(l6), _np(b.lse), checks.ATOL_LSE)
+    checks.assert_close("padded dq", _np(dq6[..., :512].float()), _np(b.dq.float()),
+                        checks.ATOL_OUT)
+    checks.assert_close("padded dkv", _np(dkv6[:, :512]), _np(b.dkv), checks.ATOL_OUT)
+    assert not dq6[..., 512:].any() and not dkv6[:, 512:].any()
+
+
+def test_full_indexshare_T131072_four_layers():
+    """IndexShare block: T=131072, indexer once, four attention layers fwd+bwd on its indices."""
+    w = gen.workload(5)
+    _log(f"workload {w.name}")
+    b = _Bufs(w.T, w.topk, w.heads, w.d_qk, w.d_v)
+    inp, md = _run_indexer(5, b)
+    _check_indexer(inp, b.idx, b.len, md, w.topk,
+                   _indexer_sample(w.cu_seqlens, w.topk, n_spread=4))
+    del inp
+    torch.cuda.empty_cache()
+    for layer in range(w.layers):
+        att = gen.attention_inputs(5, device=dev, layer=layer)
+        _run_attention(att, b, w.scale, backward=True)
+        _log(f"layer {layer}")
+        _check_rows_fwd_bwd(att, b.idx, b.len, b.out, b.lse, b.dq,
+                            _attention_sample(w.cu_seqlens, n_spread=3, seed=layer), w.scale,
+                            w.d_v)
+        _check_dkv_tails(att, b.idx, b.len, b.dkv, list(w.cu_seqlens), w.scale, R=4)
+        del att
+        torch.cuda.empty_cache()

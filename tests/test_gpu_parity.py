@@ -116,8 +116,8 @@ def test_indexer_float_inputs_near_tie(cu, K, H, D):
         ridx, rln, kth = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"],
                                              inp["cu_seqlens"], K, rows=(int(t), int(t) + 1))
         assert rln[0] == ln[t]
-        checks.check_topk_near_tie(inp["q_idx"], inp["k_idx"], inp["w"], idx[t:t + 1], ridx,
-                                   kth, np.array([t]))
+        checks.check_topk_near_tie(inp["q_idx"][t:t + 1], inp["k_idx"], inp["w"][t:t + 1],
+                                   idx[t:t + 1], ridx, kth, np.array([t]))
 
 
 def test_indexer_integer_inputs_thd_long_rows_bit_exact():
