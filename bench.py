@@ -192,7 +192,8 @@ def main():
     lse_buf = torch.empty((T, H), dtype=torch.float32, device=dev)
     dq_buf = torch.empty_like(att["q"])
     dkv_buf = torch.empty((T, Dqk), dtype=torch.float32, device=dev)
-    ws = torch.empty(dsa.lib().dsa_sparse_mla_bwd_workspace_size(T, T, H, Dqk),
+    # one backward pass over all query rows (staging T x K x D_qk fp32)
+    ws = torch.empty(dsa.bwd_workspace_bytes(T, T, H, Dqk, K, rows_per_pass=0),
                      dtype=torch.uint8, device=dev)
     kpool_valid = None
     if not has_indexer:

@@ -67,7 +67,7 @@ def lib():
         L.dsa_sparse_mla_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, f32, vp, vp,
                                          vp]
         L.dsa_sparse_mla_bwd_workspace_size.restype = sz
-        L.dsa_sparse_mla_bwd_workspace_size.argtypes = [i64, i64, i32, i32]
+        L.dsa_sparse_mla_bwd_workspace_size.argtypes = [i64, i64, i32, i32, i32, i64]
         L.dsa_sparse_mla_bwd.restype = C.c_int
         L.dsa_sparse_mla_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
                                          f32, vp, vp, u32, vp, sz, vp]
@@ -265,13 +265,28 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, topk_indices: torch.Tensor
     return out, lse
 
 
+# staged key-gradient contributions per backward pass when the caller brings no workspace
+DEFAULT_BWD_STAGE_BYTES = 16 << 30
+
+
+def bwd_workspace_bytes(T_q: int, T_kv: int, H: int, D_qk: int, K: int,
+                        rows_per_pass: int | None = None) -> int:
+    """Workspace bytes of dsa_sparse_mla_bwd for passes of `rows_per_pass` query rows
+    (0: all rows in one pass; None: as many rows as DEFAULT_BWD_STAGE_BYTES of staging hold)."""
+    if rows_per_pass is None:
+        rows_per_pass = max(1, min(max(T_q, 1), DEFAULT_BWD_STAGE_BYTES // (K * D_qk * 4)))
+    return lib().dsa_sparse_mla_bwd_workspace_size(T_q, T_kv, H, D_qk, K, rows_per_pass)
+
+
 def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
                    topk_length=None, dkv=None, accumulate: bool = False, dq=None,
                    check_indices: bool = False, workspace=None):
     """dsa_sparse_mla_bwd -> (dq bf16 [T_q,H,D_qk], dkv fp32 [T_kv,D_qk]).
 
     With accumulate=True the gradients of the latent rows are added into `dkv`
-    (query-chunked execution); otherwise dkv is overwritten."""
+    (query-chunked execution); otherwise dkv is overwritten.  `workspace` (uint8 device
+    tensor) sets how many query rows a pass stages (see bwd_workspace_bytes); by default one
+    of DEFAULT_BWD_STAGE_BYTES is allocated."""
     op = "sparse_mla_bwd"
     _require(op, q, kv, topk_indices, out, lse, dout, topk_length, dkv)
     kv2, idx, Tq, H, Dqk, Tkv, K = _attn_shapes(op, q, kv, topk_indices, topk_length)
@@ -290,9 +305,9 @@ def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
         raise ValueError(f"{op}: dkv must hold [T_kv, D_qk] fp32")
     if dq is None:
         dq = torch.empty_like(q)
-    ws_bytes = lib().dsa_sparse_mla_bwd_workspace_size(Tq, Tkv, H, Dqk)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(Tq, Tkv, H, Dqk, K), 1),
+                                dtype=torch.uint8, device=q.device)
     flags = (DSA_BWD_ACCUMULATE_DKV if accumulate else 0) | (
         DSA_DEBUG_CHECK_INDICES if check_indices else 0)
     _call(lib().dsa_sparse_mla_bwd, op, q.data_ptr(), kv2.data_ptr(), idx.data_ptr(),

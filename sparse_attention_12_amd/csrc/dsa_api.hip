@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -274,12 +275,25 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   return DSA_OK;
 }
 
-size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk) {
-  (void)T_kv;
-  (void)D_qk;
-  if (T_q < 0 || H < 0) return 0;
-  // Delta [T_q, H] fp32, then one int32 flag for the debug index check
-  return align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float)) + 512;
+// Backward workspace layout: delta [T_q, H] fp32 | debug flag | off [T_kv + 1] | cursor [T_kv]
+// | list [R * K] int32 | stage [R * K, D_qk] fp32, each segment 256-byte aligned.
+static size_t bwd_fixed_bytes(int64_t T_q, int64_t T_kv, int32_t H) {
+  return align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float)) + 256 +
+         align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t)) +
+         align_up(static_cast<size_t>(T_kv) * sizeof(int32_t)) + 256 /* base alignment */;
+}
+
+static size_t bwd_pass_bytes(int64_t rows, int32_t D_qk, int32_t K) {
+  const size_t pairs = static_cast<size_t>(rows) * static_cast<size_t>(K);
+  return align_up(pairs * sizeof(int32_t)) + align_up(pairs * D_qk * sizeof(float));
+}
+
+size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk,
+                                         int32_t K, int64_t rows_per_pass) {
+  if (T_q < 0 || T_kv < 0 || H < 0 || D_qk < 0 || K < 1) return 0;
+  int64_t R = rows_per_pass <= 0 || rows_per_pass > T_q ? T_q : rows_per_pass;
+  R = std::min<int64_t>(R, INT32_MAX / K);
+  return bwd_fixed_bytes(T_q, T_kv, H) + bwd_pass_bytes(std::max<int64_t>(R, 1), D_qk, K);
 }
 
 int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
@@ -296,24 +310,42 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   if (T_q > 0 && (!out || !lse || !dout || !dq))
     return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: NULL tensor pointer");
   if (T_kv > 0 && !dkv) return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: dkv is NULL");
-  if (!aligned16(out) || !aligned16(dout))
-    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: out/dout must be 16-byte aligned");
-  const size_t need = dsa_sparse_mla_bwd_workspace_size(T_q, T_kv, H, D_qk);
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dkv))
+    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: out/dout/dkv must be 16-byte aligned");
+  // rows per pass: as many as the workspace holds (pair ids are int32)
+  const size_t fixed = bwd_fixed_bytes(T_q, T_kv, H);
+  const size_t per_row = bwd_pass_bytes(1, D_qk, K);
+  const size_t need = fixed + per_row;
   if (T_q > 0 && (!ws || ws_bytes < need))
-    return fail(DSA_ERR_WORKSPACE, "sparse_mla_bwd: workspace needs %zu bytes, got %zu", need,
-                ws ? ws_bytes : static_cast<size_t>(0));
+    return fail(DSA_ERR_WORKSPACE, "sparse_mla_bwd: workspace needs at least %zu bytes, got %zu",
+                need, ws ? ws_bytes : static_cast<size_t>(0));
+  int64_t R = 0;
+  if (T_q > 0) {
+    R = std::min<int64_t>({T_q, static_cast<int64_t>((ws_bytes - fixed) / per_row),
+                           static_cast<int64_t>(INT32_MAX / K)});
+    while (R > 1 && fixed + bwd_pass_bytes(R, D_qk, K) > ws_bytes) --R;  // alignment slack
+  }
   if (int rc = check_device()) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float *delta = reinterpret_cast<float *>(align_up(reinterpret_cast<uintptr_t>(ws)));
-  if ((flags & DSA_DEBUG_CHECK_INDICES) && T_q > 0) {
-    int32_t *flag = reinterpret_cast<int32_t *>(
-        reinterpret_cast<char *>(delta) +
-        align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float)));
-    if (int rc = debug_check_indices(idx, topk_length, T_q, K, T_kv, flag, s)) return rc;
-  }
+  char *p = reinterpret_cast<char *>(align_up(reinterpret_cast<uintptr_t>(ws)));
+  dsa::BwdWorkspace w;
+  w.delta = reinterpret_cast<float *>(p);
+  p += align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float));
+  w.flag = reinterpret_cast<int32_t *>(p);
+  p += 256;
+  w.off = reinterpret_cast<int32_t *>(p);
+  p += align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t));
+  w.cursor = reinterpret_cast<int32_t *>(p);
+  p += align_up(static_cast<size_t>(T_kv) * sizeof(int32_t));
+  w.list = reinterpret_cast<int32_t *>(p);
+  p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) * sizeof(int32_t));
+  w.stage = reinterpret_cast<float *>(p);
+  w.rows_per_pass = R;
+  if ((flags & DSA_DEBUG_CHECK_INDICES) && T_q > 0)
+    if (int rc = debug_check_indices(idx, topk_length, T_q, K, T_kv, w.flag, s)) return rc;
   hipError_t e = dsa::launch_sparse_mla_bwd(q, kv, idx, topk_length, out, lse, dout, T_q, T_kv,
                                             H, D_qk, K, scale, dq, dkv,
-                                            (flags & DSA_BWD_ACCUMULATE_DKV) != 0, delta, s);
+                                            (flags & DSA_BWD_ACCUMULATE_DKV) != 0, w, s);
   if (e != hipSuccess) return hip_fail(e, "sparse_mla_bwd: launch");
   return DSA_OK;
 }

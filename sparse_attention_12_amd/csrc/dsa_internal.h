@@ -38,12 +38,23 @@ hipError_t launch_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const in
                                  int32_t D_qk, int32_t K, float scale, uint16_t *out, float *lse,
                                  hipStream_t s);
 
+// Backward workspace carved from the caller's buffer.
+struct BwdWorkspace {
+  float *delta;           // [T_q, H]
+  int32_t *flag;          // debug index check
+  int32_t *off;           // [T_kv + 1] per latent row: contribution count, then list offset
+  int32_t *cursor;        // [T_kv]
+  int32_t *list;          // [rows_per_pass * K] pair ids grouped by latent row
+  float *stage;           // [rows_per_pass * K, D_qk] staged contributions
+  int64_t rows_per_pass;  // query rows per pass (>= 1)
+};
+
 hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                                  const int32_t *topk_length, const uint16_t *out,
                                  const float *lse, const uint16_t *dout, int64_t T_q,
                                  int64_t T_kv, int32_t H, int32_t D_qk, int32_t K, float scale,
-                                 uint16_t *dq, float *dkv, bool accumulate, float *delta_ws,
-                                 hipStream_t s);
+                                 uint16_t *dq, float *dkv, bool accumulate,
+                                 const BwdWorkspace &ws, hipStream_t s);
 
 hipError_t launch_check_indices(const int32_t *idx, const int32_t *topk_length, int64_t T_q,
                                 int32_t K, int64_t T_kv, int32_t *bad_flag, hipStream_t s);

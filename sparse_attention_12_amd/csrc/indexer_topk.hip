@@ -27,6 +27,8 @@
 // their positions in ascending order.
 //
 // Rows with L_t <= K select their whole causal prefix, which is written without scoring.
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_internal.h"
 #include "tile.h"
@@ -63,6 +65,8 @@ struct IndexerSmem {
   int32_t has_tau[kRows];
   __align__(16) unsigned char tile[IndexerCfg<D>::kNBuf][IndexerCfg<D>::kTileBytes];
 };
+// after the key stream the tile buffers hold 4 rows x (4 KB bitmap + 2 KB scratch list)
+static_assert(IndexerCfg<64>::kNBuf * IndexerCfg<64>::kTileBytes >= 4 * (4096 + 2048), "tile area");
 
 // Monotone map float -> uint32 (larger float -> larger key); +0 and -0 map alike.
 __device__ __forceinline__ uint32_t orderable(float f) {
@@ -159,13 +163,16 @@ __device__ __forceinline__ uint32_t bin_from_top(const uint32_t *hist, uint32_t 
 }
 
 // Keeps the entries for which keep(key, position) holds, packed at the front (order not
-// preserved); returns their number.  In place: an iteration writes below the end of the block
-// it has just read, and a wave's LDS operations complete in order.
+// preserved); returns their number and sets `dropped_max` to the largest key removed (0 if
+// none).  In place: an iteration writes below the end of the block it has just read, and a
+// wave's LDS operations complete in order.
 template <typename Keep>
-__device__ int compact_candidates(uint32_t *ck, int32_t *cp, int cnt, Keep keep) {
+__device__ int compact_candidates(uint32_t *ck, int32_t *cp, int cnt, Keep keep,
+                                  uint32_t &dropped_max) {
   const int lane = __lane_id();
   const uint64_t lt = lanemask_lt();
   int written = 0;
+  uint32_t dmax = 0u;
   for (int base = 0; base < cnt; base += 256) {
     const int e = base + 4 * lane;
     u32x4 v = {0u, 0u, 0u, 0u}, p = {0u, 0u, 0u, 0u};
@@ -177,7 +184,9 @@ __device__ int compact_candidates(uint32_t *ck, int32_t *cp, int cnt, Keep keep)
     uint64_t m[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      kp[j] = e + j < cnt && keep(v[j], static_cast<int32_t>(p[j]));
+      const bool in = e + j < cnt;
+      kp[j] = in && keep(v[j], static_cast<int32_t>(p[j]));
+      if (in && !kp[j]) dmax = max(dmax, v[j]);
       m[j] = __ballot(kp[j]);
     }
     int off = written;
@@ -192,6 +201,10 @@ __device__ int compact_candidates(uint32_t *ck, int32_t *cp, int cnt, Keep keep)
     }
     written = off;
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    dmax = max(dmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dmax), off, 64)));
+  dropped_max = dmax;
   wave_sync();
   return written;
 }
@@ -242,8 +255,9 @@ __device__ uint32_t select_exact(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
   }
   // `need` keys equal to tau belong to the top K
   const int eq = count_ties_upto(ck, cp, cnt, tau, pos_hi);
+  uint32_t dmax;
   if (eq == static_cast<int>(need)) {
-    cnt = compact_candidates(ck, cp, cnt, [tau](uint32_t u, int32_t) { return u >= tau; });
+    cnt = compact_candidates(ck, cp, cnt, [tau](uint32_t u, int32_t) { return u >= tau; }, dmax);
     return tau;
   }
   // smallest position cut with `need` tied keys at or below it
@@ -256,79 +270,224 @@ __device__ uint32_t select_exact(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
   const int64_t pcut = a;
   cnt = compact_candidates(ck, cp, cnt, [tau, pcut](uint32_t u, int32_t p) {
     return u > tau || (u == tau && p <= pcut);
-  });
+  }, dmax);
   return tau;
 }
 
+// Inverse of orderable() (the +0 key maps back to +0).
+__device__ __forceinline__ float key_to_float(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// 256 bins of equal width in score value over [lo, hi] (keys).  bin(u) is non-decreasing in
+// u (a rounded subtraction and a product with a positive constant are monotone), so
+// {u : bin(u) >= b} is a set of keys at or above some key.
+struct ValueBins {
+  float flo, scale;
+  __device__ __forceinline__ bool init(uint32_t lo, uint32_t hi) {
+    flo = key_to_float(lo);
+    const float fhi = key_to_float(hi);
+    scale = 256.0f / (fhi - flo);
+    return fhi > flo && scale < INFINITY;
+  }
+  __device__ __forceinline__ int operator()(uint32_t u) const {
+    return max(min(static_cast<int>((key_to_float(u) - flo) * scale), 255), 0);
+  }
+};
+
+// 256-bin histogram of ck[0, cnt) (all keys within the bins' range).
+__device__ void value_histogram(const uint32_t *ck, int cnt, const ValueBins &vb,
+                                uint32_t *hist) {
+  const int lane = __lane_id();
+  *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+  wave_sync();
+  for (int e = 4 * lane; e < cnt; e += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(ck + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e + j < cnt) atomicAdd(&hist[vb(v[j])], 1u);
+  }
+  wave_sync();
+}
+
 // Streaming compaction: drops candidates that can no longer reach the top K, keeping at least
-// K of them, in one counting pass.  With lo = the current threshold + 1 (or the smallest key)
-// and hi = the largest key, the keys are binned by (u - lo) >> shift; the bin holding the K-th
-// largest key gives floor_key = lo + (bin << shift) with at least K keys at or above it, so
-// floor_key never exceeds the true K-th largest key and a later key below it can never enter
-// the top K.  Keys below floor_key are removed.  Returns the new threshold floor_key - 1 (or
-// the old one when nothing could be dropped); `cnt` becomes the number kept (>= K).
-__device__ uint32_t prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int &cnt, int K,
-                                     bool has_tau, uint32_t tau) {
+// K of them, in one counting pass.  The keys above the current threshold are binned by value
+// over [threshold, largest key]; the bin b holding the K-th largest key leaves at least K keys
+// in bins >= b, so every key in a lower bin lies below the K-th largest and can be dropped,
+// and so can any later key that is not above the largest dropped key, which becomes the new
+// threshold `tau`.  Returns whether a threshold is set; `cnt` becomes the number kept (>= K).
+__device__ bool prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int &cnt, int K,
+                                 bool has_tau, uint32_t &tau) {
   uint32_t lo, hi;
   key_range(ck, cnt, lo, hi);
   if (has_tau) lo = tau + 1u;  // every candidate is above the current threshold
-  const int shift = range_shift(lo, hi);
-  key_histogram(ck, cnt, lo, hi, shift, hist);
+  ValueBins vb;
+  if (!vb.init(lo, hi)) return has_tau;
+  value_histogram(ck, cnt, vb, hist);
   uint32_t above;
-  const uint32_t bin = bin_from_top(hist, static_cast<uint32_t>(K), above);
-  const uint32_t floor_key = lo + (bin << shift);
-  if (bin == 0) return has_tau ? tau : 0u;  // nothing below the K-th key's bin (0: no filter)
-  cnt = compact_candidates(ck, cp, cnt, [floor_key](uint32_t u, int32_t) {
-    return u >= floor_key;
-  });
-  return floor_key - 1u;
+  const int b = static_cast<int>(bin_from_top(hist, static_cast<uint32_t>(K), above));
+  if (b == 0) return has_tau;  // nothing below the K-th key's bin
+  uint32_t dmax;
+  cnt = compact_candidates(ck, cp, cnt, [vb, b](uint32_t u, int32_t) { return vb(u) >= b; },
+                           dmax);
+  tau = has_tau ? max(tau, dmax) : dmax;
+  return true;
 }
 
-// Writes the positions of cp[0, K) (distinct, inside [start, t]) to out[0, K) in ascending
-// order: each 32768-position window is marked in a bitmap (1024 words of LDS) and read back
-// with a scan of per-lane bit counts.
-__device__ void write_sorted_positions(const int32_t *cp, int K, int64_t start, int64_t t,
-                                       uint32_t *bm, int32_t *out) {
+// Final selection of exactly K of the row's cnt >= K candidates and their output in ascending
+// position order.  One value histogram finds the bin b of the K-th largest key: every
+// candidate in a higher bin is selected, and the `need` best of the bin-b candidates (copied
+// to a scratch list of at most kScratch entries, ranked by key and then lower position) are
+// added.  If bin b is too populous (massive ties), select_exact() runs on the whole buffer.
+// The selected positions (all inside [start, t]) are marked in a bitmap one 32768-position
+// window at a time and read back in order with a scan of per-lane bit counts.
+constexpr int kScratch = 256;
+
+__device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, int cnt, int K,
+                                 bool has_tau, uint32_t tau, int64_t start, int64_t t,
+                                 uint32_t *bm, uint32_t *sk, int32_t *sp, int32_t *out) {
   const int lane = __lane_id();
+  ValueBins vb;
+  int b = -1;        // bin of the K-th key; -1: every candidate in ck[0, cnt) is selected
+  int nb = 0;        // scratch entries
+  uint32_t keep4 = 0u;  // bit r: scratch entry lane + 64 r is selected
+  if (cnt > K) {
+    uint32_t lo, hi;
+    key_range(ck, cnt, lo, hi);
+    if (has_tau) lo = tau + 1u;
+    bool fast = vb.init(lo, hi);
+    uint32_t need = 0u;
+    if (fast) {
+      value_histogram(ck, cnt, vb, hist);
+      uint32_t above;
+      b = static_cast<int>(bin_from_top(hist, static_cast<uint32_t>(K), above));
+      need = static_cast<uint32_t>(K) - above;
+      nb = static_cast<int>(hist[b]);
+      fast = nb <= kScratch;
+    }
+    if (fast) {
+      // copy bin b to the scratch list
+      const uint64_t lt = lanemask_lt();
+      int w = 0;
+      for (int e = 4 * lane; e - 4 * lane < cnt; e += 256) {
+        u32x4 v = {0u, 0u, 0u, 0u}, p = {0u, 0u, 0u, 0u};
+        if (e < cnt) {
+          v = *reinterpret_cast<const u32x4 *>(ck + e);
+          p = *reinterpret_cast<const u32x4 *>(cp + e);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool in = e + j < cnt && vb(v[j]) == b;
+          const uint64_t m = __ballot(in);
+          if (in) {
+            const int o = w + __popcll(m & lt);
+            sk[o] = v[j];
+            sp[o] = static_cast<int32_t>(p[j]);
+          }
+          w += __popcll(m);
+        }
+      }
+      wave_sync();
+      // rank of each scratch entry among the bin: larger key first, then lower position
+#pragma unroll
+      for (int r = 0; r < kScratch / 64; ++r) {
+        const int i = lane + 64 * r;
+        if (i < nb) {
+          const uint32_t ki = sk[i];
+          const int32_t pi = sp[i];
+          uint32_t rank = 0u;
+          for (int j = 0; j < nb; ++j) {
+            const uint32_t kj = sk[j];
+            rank += (kj > ki || (kj == ki && sp[j] < pi)) ? 1u : 0u;
+          }
+          if (rank < need) keep4 |= 1u << r;
+        }
+      }
+    } else {
+      int n = cnt;
+      select_exact(ck, cp, hist, n, K, start, t);
+      cnt = K;
+      b = -1;
+      nb = 0;
+    }
+  }
+  // ---- ascending output through a bitmap of each 32768-position window.  Lane l produces the
+  // output slots [l S, l S + S) (S = ceil(K / 64)): it finds the set bit of its first slot
+  // from per-lane prefix counts and walks on from there, so the work is even however dense
+  // the selection is.  A single-window row stages its output in cp (free by then) and copies
+  // it out with wide stores.
   constexpr int kWords = 1024;
   constexpr int64_t kWin = 32 * kWords;
+  const int S = (K + 63) >> 6;
+  const bool single = t - start < kWin;
+  uint32_t *lp = hist;  // per-lane exclusive prefix counts of the window (hist is free now)
   int done = 0;
   for (int64_t w0 = start; w0 <= t; w0 += kWin) {
 #pragma unroll
     for (int i = 0; i < kWords / 256; ++i)
       *reinterpret_cast<u32x4 *>(bm + 4 * (lane + 64 * i)) = u32x4{0u, 0u, 0u, 0u};
     wave_sync();
-    for (int e = lane; e < K; e += 64) {
+    for (int e = lane; e < cnt; e += 64) {
       const int64_t rel = cp[e] - w0;
-      if (rel >= 0 && rel < kWin) atomicOr(&bm[rel >> 5], 1u << (rel & 31));
+      if (rel >= 0 && rel < kWin && (b < 0 || vb(ck[e]) > b))
+        atomicOr(&bm[rel >> 5], 1u << (rel & 31));
+    }
+#pragma unroll
+    for (int r = 0; r < kScratch / 64; ++r) {
+      const int i = lane + 64 * r;
+      if (i < nb && ((keep4 >> r) & 1u)) {
+        const int64_t rel = sp[i] - w0;
+        if (rel >= 0 && rel < kWin) atomicOr(&bm[rel >> 5], 1u << (rel & 31));
+      }
     }
     wave_sync();
     // lane l owns words [16 l, 16 l + 16)
-    uint32_t wv[16];
     int c = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 v = *reinterpret_cast<const u32x4 *>(bm + 16 * lane + 4 * i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wv[4 * i + j] = v[j];
-        c += __popc(v[j]);
-      }
+      c += __popc(v[0]) + __popc(v[1]) + __popc(v[2]) + __popc(v[3]);
     }
     const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(c)));
-    int o = done + incl - c;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t bits = wv[i];
-      while (bits) {
-        const int b = __ffs(static_cast<int>(bits)) - 1;
-        if (o < K) out[o] = static_cast<int32_t>(w0 + (16 * lane + i) * 32 + b);
-        ++o;
+    lp[lane] = static_cast<uint32_t>(incl - c);
+    const int tw = __shfl(incl, 63, 64);  // selected positions in this window
+    wave_sync();
+    int sl = max(lane * S, done);
+    const int s_end = min(min(lane * S + S, K), done + tw);
+    if (sl < s_end) {
+      const int r = sl - done;  // rank of the first slot's bit inside the window
+      int a = 0, z = 63;        // last lane whose prefix is <= r
+      while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (static_cast<int>(lp[mid]) <= r) a = mid;
+        else z = mid - 1;
+      }
+      int word = 16 * a;
+      int acc = static_cast<int>(lp[a]);
+      uint32_t bits = bm[word];
+      while (acc + __popc(bits) <= r) {
+        acc += __popc(bits);
+        bits = bm[++word];
+      }
+      for (int k = r - acc; k > 0; --k) bits &= bits - 1u;
+      for (; sl < s_end; ++sl) {
+        while (bits == 0u) bits = bm[++word];
+        const int32_t pos = static_cast<int32_t>(w0 + word * 32 + __ffs(static_cast<int>(bits)) - 1);
         bits &= bits - 1u;
+        if (single) cp[sl] = pos;
+        else out[sl] = pos;
       }
     }
-    done += __shfl(incl, 63, 64);
+    done += tw;
     wave_sync();
+  }
+  if (single) {
+    if ((K & 3) == 0) {
+      for (int j = 4 * lane; j < K; j += 256)
+        *reinterpret_cast<u32x4 *>(out + j) = *reinterpret_cast<const u32x4 *>(cp + j);
+    } else {
+      for (int j = lane; j < K; j += 64) out[j] = cp[j];
+    }
   }
 }
 
@@ -455,35 +614,101 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   wait_tile();
   __syncthreads();  // q, w, counters and the first tiles have landed
 
+  // The scores of a tile are finished one tile late: the VALU work that turns a tile's
+  // accumulators into scores (ReLU, head weights, head sum) is interleaved with the MFMAs of the
+  // next tile, so the matrix cores do not idle while it runs.  A tile's keys are therefore
+  // appended during the next tile, and the capacity check leaves room for two tiles.
+  constexpr int kElems = NMT * 16;       // accumulator elements per lane
+  constexpr int kSlice = kElems / NKK;   // of them finished per MFMA k-step
+  static_assert(kElems % NKK == 0, "score slices");
+  auto mfma_tile = [&](const unsigned char *tile, f32x16 (&cur)[NMT], const f32x16 (&prev)[NMT],
+                       auto with_prev) -> float {
+    bf16x8 bf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      bf[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tile + boff[kk]));
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int m = 0; m < NMT; ++m) cur[m] = mfma32(qa[m][kk], bf[kk], kk == 0 ? f32x16{} : cur[m]);
+      if constexpr (decltype(with_prev)::value) {
+#pragma unroll
+        for (int j = 0; j < kSlice; j += 2) {
+          const int e = kk * kSlice + j;
+          s0 = fmaf(wv[e >> 4][e & 15], fmaxf(prev[e >> 4][e & 15], 0.0f), s0);
+          s1 = fmaf(wv[(e + 1) >> 4][(e + 1) & 15], fmaxf(prev[(e + 1) >> 4][(e + 1) & 15], 0.0f), s1);
+        }
+      }
+    }
+    return s0 + s1;
+  };
+  auto score_only = [&](const f32x16 (&prev)[NMT]) -> float {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kElems; e += 2) {
+      s0 = fmaf(wv[e >> 4][e & 15], fmaxf(prev[e >> 4][e & 15], 0.0f), s0);
+      s1 = fmaf(wv[(e + 1) >> 4][(e + 1) & 15], fmaxf(prev[(e + 1) >> 4][(e + 1) & 15], 0.0f), s1);
+    }
+    return s0 + s1;
+  };
+  auto append = [&](float sc, int64_t key) {
+    sc += swap_halves(sc);
+    const uint32_t u = orderable(sc);
+    const bool pass = lane < 32 && key <= t && (!my_has_tau || u > my_tau);
+    const uint64_t pm = __ballot(pass);
+    if (pm) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sm.cnt[row], __popcll(pm));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (pass) {
+        const int o = base + __popcll(pm & lt);
+        ck[o] = u;
+        cp[o] = static_cast<int32_t>(key);
+      }
+    }
+  };
+
+  // one tile: accumulate into `cur`, finish the pending tile held in `prev`
   int buf = 0;
-  for (int64_t kb = start; kb <= last; kb += kTileKeys) {
+  bool have_prev = false;  // `prev` holds the accumulators of an unfinished tile
+  int64_t key_prev = 0;
+  auto step = [&](int64_t kb, f32x16 (&cur)[NMT], f32x16 (&prev)[NMT]) {
     if (kb > start) {
       if (kb + kTileKeys <= last) wait_vm<C::kLoadsPerWave>();  // the next tile may stay in flight
       else wait_tile();
       lds_barrier();  // this tile is complete everywhere; the previous one is free; every
-                      // append of the previous tile is visible
+                      // append made so far is visible
     }
     if (kb + 2 * kTileKeys <= last) {
       const int nb = buf >= C::kNBuf - 2 ? buf + 2 - C::kNBuf : buf + 2;
       loads.issue(tile_lds + nb * C::kTileBytes, k, kb + 2 * kTileKeys, last, wave);
     }
 
-    // ---- compaction, when a row may not have room for this tile's keys.  Every row far
+    // ---- compaction, when a row may not have room for the keys of two tiles.  Every row far
     // enough above K is compacted in the same round, so the rows of a group (whose counts grow
     // alike) rarely stop the group more than once per round.
     const int4 cv = *reinterpret_cast<const int4 *>(sm.cnt);
     const int c0 = __builtin_amdgcn_readfirstlane(cv.x), c1 = __builtin_amdgcn_readfirstlane(cv.y);
     const int c2 = __builtin_amdgcn_readfirstlane(cv.z), c3 = __builtin_amdgcn_readfirstlane(cv.w);
-    if (max(max(c0, c1), max(c2, c3)) > C::kCap - kTileKeys) {
+    if (max(max(c0, c1), max(c2, c3)) > C::kCap - 2 * kTileKeys) {
       const int mine = row == 0 ? c0 : row == 1 ? c1 : row == 2 ? c2 : c3;
       if (half == 0 && mine > (C::kCap + K) / 2) {
         int n = mine;
-        uint32_t tau = prune_candidates(ck, cp, sm.hist[row], n, K, my_has_tau, my_tau);
-        if (n > C::kCap - 2 * kTileKeys)  // too many ties to make room: exact selection
-          tau = select_exact(ck, cp, sm.hist[row], n, K, start, t);
+        uint32_t tau = my_tau;
+        bool has = prune_candidates(ck, cp, sm.hist[row], n, K, my_has_tau, tau);
+        if (n > C::kCap - 3 * kTileKeys) {  // too many ties to make room: exact selection
+          // exactly K kept, all at or above the K-th key kth (> the old threshold); a later key
+          // equal to kth loses the tie, but the threshold kth - 1 keeps every kept key above it
+          const uint32_t kth = select_exact(ck, cp, sm.hist[row], n, K, start, t);
+          if (kth > 0u) {
+            tau = kth - 1u;
+            has = true;
+          }
+        }
         if (lane == 0) {
           sm.tau[row] = tau;
-          sm.has_tau[row] = 1;
+          sm.has_tau[row] = has ? 1 : 0;
           sm.cnt[row] = n;
         }
       }
@@ -492,51 +717,43 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
       my_tau = __builtin_amdgcn_readfirstlane(sm.tau[row]);
     }
 
-    // ---- scores of this wave's 32 keys, appended when above the row's threshold
+    // ---- this wave's 32 keys of the tile
     const int64_t kbase = kb + half * 32;
-    const int64_t key = kbase + (lane & 31);
-    if (compute && kbase <= t) {
-      const unsigned char *tile = sm.tile[buf];
-      f32x16 acc[NMT];
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4 *>(tile + boff[kk]));
-#pragma unroll
-        for (int m = 0; m < NMT; ++m) acc[m] = mfma32(qa[m][kk], b, kk == 0 ? f32x16{} : acc[m]);
-      }
-      float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-      for (int m = 0; m < NMT; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          s0 = fmaf(wv[m][i], fmaxf(acc[m][i], 0.0f), s0);
-          s1 = fmaf(wv[m][i + 1], fmaxf(acc[m][i + 1], 0.0f), s1);
-        }
-      float sc = s0 + s1;
-      sc += swap_halves(sc);
-      const uint32_t u = orderable(sc);
-      const bool pass = lane < 32 && key <= t && (!my_has_tau || u > my_tau);
-      const uint64_t pm = __ballot(pass);
-      if (pm) {
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&sm.cnt[row], __popcll(pm));
-        base = __builtin_amdgcn_readfirstlane(base);
-        if (pass) {
-          const int o = base + __popcll(pm & lt);
-          ck[o] = u;
-          cp[o] = static_cast<int32_t>(key);
-        }
-      }
-    }
+    const bool do_cur = compute && kbase <= t;
+    float sc = 0.0f;
+    if (do_cur && have_prev) sc = mfma_tile(sm.tile[buf], cur, prev, std::true_type{});
+    else if (do_cur) mfma_tile(sm.tile[buf], cur, prev, std::false_type{});
+    else if (have_prev) sc = score_only(prev);
+    if (have_prev) append(sc, key_prev);
+    have_prev = do_cur;
+    key_prev = kbase + (lane & 31);
     buf = buf == C::kNBuf - 1 ? 0 : buf + 1;
+  };
+  f32x16 acc_a[NMT], acc_b[NMT];
+  int64_t kb = start;
+  while (true) {  // two tiles per trip so that the accumulator sets alternate without copies
+    step(kb, acc_a, acc_b);
+    kb += kTileKeys;
+    if (kb > last) {
+      if (have_prev) append(score_only(acc_a), key_prev);
+      break;
+    }
+    step(kb, acc_b, acc_a);
+    kb += kTileKeys;
+    if (kb > last) {
+      if (have_prev) append(score_only(acc_b), key_prev);
+      break;
+    }
   }
 
   lds_barrier();  // every append is visible; no tile load is in flight
   if (compute && half == 0) {
-    int n = __builtin_amdgcn_readfirstlane(sm.cnt[row]);
-    if (n > K) select_exact(ck, cp, sm.hist[row], n, K, start, t);
+    // the key tiles are free now: per row a 4 KB bitmap and a kScratch-entry scratch list
     uint32_t *bm = reinterpret_cast<uint32_t *>(&sm.tile[0][0]) + row * 1024;
-    write_sorted_positions(cp, K, start, t, bm, idx_out + t * K);
+    uint32_t *sk = reinterpret_cast<uint32_t *>(&sm.tile[0][0]) + 4 * 1024 + row * 2 * kScratch;
+    int32_t *sp = reinterpret_cast<int32_t *>(sk + kScratch);
+    select_and_write(ck, cp, sm.hist[row], __builtin_amdgcn_readfirstlane(sm.cnt[row]), K,
+                     my_has_tau, my_tau, start, t, bm, sk, sp, idx_out + t * K);
     if (lane == 0) len_out[t] = K;
   }
 }

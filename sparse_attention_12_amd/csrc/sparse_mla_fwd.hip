@@ -38,18 +38,6 @@ constexpr size_t fwd_smem_bytes() {
   return static_cast<size_t>(fwd_buffers<NW>()) * Tile<DQK>::kBytes + kMaxK * sizeof(int32_t);
 }
 
-// Wait for tile c when `ahead` later tiles (each L loads per wave) may stay in flight.
-template <int L, int NBUF>
-__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
-  if constexpr (NBUF >= 4) {
-    if (ahead >= 2) { wait_vm<2 * L>(); return; }
-  }
-  if constexpr (NBUF >= 3) {
-    if (ahead >= 1) { wait_vm<L>(); return; }
-  }
-  wait_vm<0>();
-}
-
 template <int DQK, int NW>
 __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,

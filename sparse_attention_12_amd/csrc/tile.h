@@ -125,4 +125,103 @@ struct Tile {
   }
 };
 
+// Wait for the oldest tile when `ahead` later tiles (each L loads per wave) may stay in flight.
+template <int L, int NBUF>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  if constexpr (NBUF >= 4) {
+    if (ahead >= 2) { wait_vm<2 * L>(); return; }
+  }
+  if constexpr (NBUF >= 3) {
+    if (ahead >= 1) { wait_vm<L>(); return; }
+  }
+  wait_vm<0>();
+}
+
+// Stream of a query's latent-row tiles through NBUF LDS buffers (tile c in buffer c % NBUF),
+// filled by the NW waves of a work group with direct loads.  slot_rows (LDS) lists the latent
+// row of every slot of the query, -1 for an invalid slot, up to a whole number of tiles; the
+// latent tensor is below 4 GiB, so a 32-bit offset from its base addresses any row.
+template <int DQK, int NW, int NBUF>
+struct TileStream {
+  using TL = Tile<DQK>;
+  static constexpr int L = TL::kLoads / NW;  // loads per wave per tile
+  static_assert(TL::kLoads % NW == 0, "loads must split evenly over the waves");
+  int dma_row[L], dma_off[L];
+  uint32_t tiles_lds;  // LDS address of buffer 0 plus this wave's first load slot
+
+  __device__ __forceinline__ void init(const void *tiles, int wave) {
+    const int lane = __lane_id();
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int pos = (i * NW + wave) * 64 + lane;
+      dma_row[i] = pos / TL::kChunks;
+      dma_off[i] = ((pos % TL::kChunks) ^ TL::swz(dma_row[i])) * 16;
+    }
+    tiles_lds = lds_addr(tiles) + wave * 1024;
+  }
+  __device__ __forceinline__ void issue(int c, const uint16_t *kv, const int32_t *slot_rows) const {
+    const uint32_t dst = tiles_lds + (c % NBUF) * TL::kBytes;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      int r = slot_rows[c * TL::kSlots + dma_row[i]];
+      r = r < 0 ? 0 : r;
+      dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + dma_off[i], dst + i * NW * 1024);
+    }
+  }
+  // Before processing tile c of nchunks: wait for it and publish it to the work group.  The
+  // barrier also means every wave is done with tile c - 1, whose buffer the caller may refill.
+  __device__ static __forceinline__ void acquire(int c, int nchunks) {
+    wait_tiles_ahead<L, NBUF>(min(NBUF - 2, nchunks - 1 - c));
+    lds_barrier();
+  }
+};
+
+// Per-lane LDS byte offsets into a Tile<DQK> for the 16x16x32 MFMA fragments of a 32-slot
+// tile (lane = 16 g + hl, r4 = hl / 4, cq = lane % 4):
+//   A operand of S^T = rows . q^T, rows mt*16 + hl, chunk 4 ks + g:
+//       a_off(mt, ks) = sbase[mt][ks & 3] + (ks >> 2) * 256
+//   transposing reads of columns 16 n + 4 cq .. + 3 of rows 4 g + r4 and 16 + 4 g + r4 (the
+//   slot order that matches a P / dZ fragment held in registers):
+//       v_off(half, n) = vbase[half][n & 7] + (n >> 3) * 256
+// (the swizzle only permutes the low four bits of a chunk index, so chunk 16 a + b lands at
+// (16 a + (b ^ swz)) * 16).
+template <int DQK>
+struct TileFrag {
+  using TL = Tile<DQK>;
+  int sbase[2][4], vbase[2][8];
+  __device__ __forceinline__ void init() {
+    const int lane = __lane_id();
+    const int g = lane >> 4, hl = lane & 15, r4 = hl >> 2, cq = lane & 3;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sbase[mt][j] = TL::chunk_off(mt * 16 + hl, j * 4 + g);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      vbase[0][j] = TL::elem_off(g * 4 + r4, j * 16 + cq * 4);
+      vbase[1][j] = TL::elem_off(16 + g * 4 + r4, j * 16 + cq * 4);
+    }
+  }
+  __device__ __forceinline__ bf16x8 a_frag(const unsigned char *tile, int mt, int ks) const {
+    return as_bf16x8(*reinterpret_cast<const u32x4 *>(tile + sbase[mt][ks & 3] + (ks >> 2) * 256));
+  }
+  // rows^T fragment (16 columns x 32 slots in the register P/dZ slot order)
+  __device__ __forceinline__ bf16x8 v_frag(const unsigned char *tile, int n) const {
+    const u32x2 lo = lds_read_tr16(tile + vbase[0][n & 7] + (n >> 3) * 256);
+    const u32x2 hi = lds_read_tr16(tile + vbase[1][n & 7] + (n >> 3) * 256);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
+};
+
+// Pack an S^T-layout fragment x[mt][i] (slot 16 mt + 4 g + i of this lane's head) into the
+// bf16 MFMA operand whose contraction index 8 g + j is slot 4 g + j (j < 4) or 16 + 4 g + j - 4.
+__device__ __forceinline__ bf16x8 pack_slots(const float x[2][4]) {
+  u32x4 w;
+  w[0] = pack_bf16x2(x[0][0], x[0][1]);
+  w[1] = pack_bf16x2(x[0][2], x[0][3]);
+  w[2] = pack_bf16x2(x[1][0], x[1][1]);
+  w[3] = pack_bf16x2(x[1][2], x[1][3]);
+  return as_bf16x8(w);
+}
+
 }  // namespace dsa
