@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
 METRIC = "sparse-MLA fwd/bwd TFLOP/s + indexer top-k tokens/s at T=32K,k=2048; % roofline"
 
@@ -241,8 +241,10 @@ def main():
 
     t_idx = avg("indexer_topk")
     t_fwd = avg("sparse_mla_fwd")
-    t_bwd = sum(avg(n) for n in ("dkv_zero", "sparse_mla_bwd_delta", "sparse_mla_bwd_dq",
-                                 "sparse_mla_bwd_dkv") if n in per_kernel)
+    bwd_kernels = ("dkv_zero", "sparse_mla_bwd_delta", "sparse_mla_bwd_rows", "pair_zero",
+                   "pair_count", "pair_scan", "pair_fill", "sparse_mla_bwd_reduce")
+    # kernels of several backward passes add up per step
+    t_bwd = sum(sum(per_kernel[n]) for n in bwd_kernels if n in per_kernel) / args.steps
     comp = {
         "fwd": {"ms": t_fwd, "tflops": counts["fwd_flops"] / t_fwd / 1e9,
                 "frac_mfma_peak": counts["fwd_flops"] / t_fwd / 1e9 / PEAK_BF16_TFLOPS},
@@ -255,13 +257,22 @@ def main():
                            "frac_mfma_peak": counts["idx_flops"] / t_idx / 1e9 / PEAK_BF16_TFLOPS}
     kernels = {n: {"avg_ms": sum(v) / len(v), "launches": len(v)} for n, v in per_kernel.items()}
 
-    work = {"indexer_topk": counts["idx_flops"], "sparse_mla_fwd": counts["fwd_flops"],
-            "sparse_mla_bwd_dq": counts["bwd_dq_flops"],
-            "sparse_mla_bwd_dkv": counts["bwd_dkv_flops"]}
+    # algorithmic work per launch of each hot kernel: MFMA flops, or HBM bytes for the
+    # reduction of the staged key-gradient contributions (read once, dkv read and written)
+    passes = max(1, len(per_kernel.get("sparse_mla_bwd_rows", [])) // args.steps)
+    work = {"indexer_topk": ("mfma", counts["idx_flops"]),
+            "sparse_mla_fwd": ("mfma", counts["fwd_flops"]),
+            "sparse_mla_bwd_rows": ("mfma", counts["bwd_flops"] / passes),
+            "sparse_mla_bwd_reduce": ("hbm", (counts["valid"] * Dqk * 4 / passes
+                                              + 2 * T * Dqk * 4))}
     dom = max((n for n in work if n in per_kernel), key=lambda n: sum(per_kernel[n]))
-    achieved = work[dom] / avg(dom) / 1e9
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+    bound, amount = work[dom]
+    if bound == "mfma":
+        achieved, peak, unit = amount / avg(dom) / 1e9, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = amount / avg(dom) / 1e6, PEAK_HBM_GBS, "GB/s"
+    roofline = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": None}
 
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

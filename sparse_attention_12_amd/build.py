@@ -30,10 +30,10 @@ CFLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
 
 
 # Per-file extra flags.  The indexer's inputs are finite by contract; without NaN semantics
-# max(x, 0) is one instruction instead of a canonicalise + max pair.  The attention kernels
-# keep their MFMA accumulators in VGPRs (MFMA VGPR form): with the default heuristic the
-# forward copies its 128 output accumulators between AGPRs and VGPRs on every chunk, and the
-# backward rows kernel spills.
+# max(x, 0) is one instruction instead of a canonicalise + max pair.  The attention kernels keep
+# their MFMA accumulators in VGPRs (MFMA VGPR form): with the default heuristic the forward
+# copies its output accumulators between AGPRs and VGPRs on every chunk and the backward rows
+# kernel spills.
 EXTRA = {"indexer_topk.hip": ["-fno-honor-nans"],
          "sparse_mla_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "sparse_mla_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

@@ -5,19 +5,22 @@
 // valid-prefix lengths, softmax_scale applied unchanged; SkyRL PR 2388 for the 512-wide NoPE
 // layout and top-k widths that are not a multiple of 64).
 //
-// Work group = one query row, ceil(H/16) waves, wave w owning heads [16w, 16w+16).  The row's
-// valid slots are processed in chunks of 32: the 32 latent rows are gathered into LDS with
-// 16-byte loads, then each wave computes
+// Work group = one query row, NW waves, wave w owning HG groups of 16 heads (32 heads per
+// wave for H = 64: every latent-row fragment read from LDS feeds two MFMAs, which halves the
+// LDS traffic per flop against one group per wave).  The row's valid slots are processed in
+// chunks of 32: the 32 latent rows are gathered into LDS with direct 16-byte loads (two
+// buffers; two work groups share a CU so one computes while the other waits), then each wave
+// computes, per head group,
 //   S^T[32 slots x 16 heads] = rows . q^T          (16x16x32 bf16 MFMA, A = LDS rows,
 //                                                   B = the wave's q block held in registers)
 // runs the online softmax in fp32 (base 2), and accumulates
-//   O[16 heads x 512] += P . V                       (A = P straight from the S^T registers,
-//                                                   B = V read from the same row-major LDS
-//                                                   tile with transposing LDS reads)
-// The slot order inside the P.V contraction is permuted so that P needs no data movement:
-// the lane holding S^T rows (lane/16)*4 + [0,4) of both 16-slot halves supplies exactly the
-// eight contraction indices it owns in the MFMA A layout, and the transposing reads fetch V
-// rows in the same order.
+//   O^T[512 x 16 heads] += V^T . P^T                (A = V^T from transposing LDS reads of the
+//                                                   same row tile, B = P straight from the S^T
+//                                                   registers)
+// The slot order inside the P.V contraction is permuted so that P needs no data movement: the
+// lane holding S^T rows (lane/16)*4 + [0,4) of both 16-slot halves supplies exactly the eight
+// contraction indices it owns in the MFMA B layout, and the transposing reads fetch V rows in
+// the same order.  The output accumulators (HG x 128 per lane) stay in AGPRs.
 #include "dsa_common.h"
 #include "dsa_internal.h"
 #include "tile.h"
@@ -27,49 +30,45 @@ namespace {
 
 constexpr int kSlots = 32;  // slots per chunk
 constexpr int kDv = 512;
-constexpr int kMaxK = 4096;  // largest top-k width whose index row fits the LDS copy
+constexpr int kNBuf = 2;    // latent-row tile buffers per work group
 
-// Tile buffers in flight: a wave with few loads per tile keeps NBUF - 1 tiles in flight.
-template <int NW>
-constexpr int fwd_buffers() { return NW == 1 ? 2 : 4; }
-
-template <int DQK, int NW>
+template <int DQK, int SLOTCAP>
 constexpr size_t fwd_smem_bytes() {
-  return static_cast<size_t>(fwd_buffers<NW>()) * Tile<DQK>::kBytes + kMaxK * sizeof(int32_t);
+  return static_cast<size_t>(kNBuf) * Tile<DQK>::kBytes + SLOTCAP * sizeof(int32_t);
 }
 
-template <int DQK, int NW>
+template <int DQK, int NW, int HG, int SLOTCAP>
 __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
     float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
   using TL = Tile<DQK>;
   constexpr int kKSteps = DQK / 32;
-  constexpr int NBUF = fwd_buffers<NW>();
-  constexpr int L = TL::kLoads / NW;  // DMA loads per wave per tile
-  static_assert(TL::kLoads % NW == 0, "loads must split evenly over the waves");
+  constexpr int kNT = kDv / 16;  // output tiles of 16 channels
+  static_assert(TL::kLoads % NW == 0, "tile loads must split evenly over the waves");
   extern __shared__ __align__(16) unsigned char smem[];
-  int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + NBUF * TL::kBytes);
+  int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + kNBuf * TL::kBytes);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t t = blockIdx.x;
-  const int h0 = wave * 16;
-  const int g = lane >> 4;     // lane group
-  const int hl = lane & 15;    // head within the wave's tile
+  const int g = lane >> 4;   // lane group
+  const int hl = lane & 15;  // head within a 16-head group
   const int lim = topk_length ? topk_length[t] : K;
   const int32_t *irow = idx + t * K;
   const int nchunks = (lim + kSlots - 1) / kSlots;
 
-  // q block of this wave as the MFMA B operand: lane -> head hl, dims ks*32 + g*8 + [0,8)
-  bf16x8 qf[kKSteps];
-  {
-    const int h = h0 + hl;
+  // q blocks of this wave's head groups as MFMA B operands: lane -> head hl of group hg,
+  // dims ks*32 + g*8 + [0,8)
+  bf16x8 qf[HG][kKSteps];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    const int h = (wave * HG + hg) * 16 + hl;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (h < H) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
-      qf[ks] = as_bf16x8(v);
+      qf[hg][ks] = as_bf16x8(v);
     }
   }
   // the query's slot -> latent row map (tail of the last chunk marked invalid)
@@ -77,151 +76,378 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
     slot_rows[j] = j < lim ? irow[j] : -1;
   // finish the q loads before the first tile load (see settle())
 #pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) settle(qf[ks]);
+  for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) settle(qf[hg][ks]);
   __syncthreads();
 
-  // Per-lane LDS offsets, fixed for the whole kernel (the swizzle only permutes the low four
-  // bits of a chunk index, so a chunk 16*a + b lands at (16*a + (b ^ swz)) * 16).
-  //   S^T A operand, tile row mt*16 + hl, chunk ks*4 + g:  sbase[mt][ks & 3] + (ks >> 2) * 256
-  //   V (transposing reads), rows 4g + r4 and 16 + 4g + r4, element col n*16 + cq*4:
-  //                                                        vbase[j][n & 7] + (n >> 3) * 256
-  const int r4 = (lane & 15) >> 2;
-  const int cq = lane & 3;
-  int sbase[2][4], vbase[2][8];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sbase[mt][j] = TL::chunk_off(mt * 16 + hl, j * 4 + g);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    vbase[0][j] = TL::elem_off(g * 4 + r4, j * 16 + cq * 4);
-    vbase[1][j] = TL::elem_off(16 + g * 4 + r4, j * 16 + cq * 4);
-  }
-  // this lane's DMA targets: (tile row, byte offset inside the row) for each of its L loads;
-  // the latent tensor is below 4 GiB (checked by the host), so a 32-bit offset from its base
-  // addresses any row
-  int dma_row[L], dma_off[L];
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int pos = (i * NW + wave) * 64 + lane;
-    dma_row[i] = pos / TL::kChunks;
-    dma_off[i] = ((pos % TL::kChunks) ^ TL::swz(dma_row[i])) * 16;
-  }
-  const uint32_t smem_lds = lds_addr(smem);
+  TileFrag<DQK> fr;
+  fr.init();
+  const uint32_t tiles_lds = lds_addr(smem);
+  // this wave's DMA loads of tile c: load k (k = wave, wave + NW, ...) fills LDS bytes
+  // [1024 k, 1024 k + 1024) of the tile, lane i the 16 bytes at 1024 k + 16 i
   auto issue = [&](int c) {
-    const uint32_t tile = smem_lds + (c % NBUF) * TL::kBytes + wave * 1024;
+    const uint32_t dst = tiles_lds + (c % kNBuf) * TL::kBytes;
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      int r = slot_rows[c * kSlots + dma_row[i]];
-      r = r < 0 ? 0 : r;
-      dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + dma_off[i],
-               tile + i * NW * 1024);
+    for (int i = 0; i < TL::kLoads / NW; ++i) {
+      const int k = i * NW + wave;
+      const int pos = k * 64 + lane;
+      const int row = pos / TL::kChunks;
+      const int chunk = (pos % TL::kChunks) ^ TL::swz(row);
+      int r = slot_rows[c * kSlots + row];
+      r = r < 0 ? 0 : r;  // invalid slots load row 0 (masked below)
+      dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + chunk * 16, dst + k * 1024);
     }
   };
-#pragma unroll
-  for (int c = 0; c < NBUF - 1; ++c)
-    if (c < nchunks) issue(c);
+  if (nchunks > 0) issue(0);
 
-  f32x4 o[kDv / 16];  // O^T tiles: o[n][i] = O[head hl][channel 16n + 4g + i]
+  f32x4 o[HG][kNT];  // O^T tiles: o[hg][n][i] = O[head hl of group hg][channel 16n + 4g + i]
 #pragma unroll
-  for (int n = 0; n < kDv / 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // reference max (base-2 logits) of head hl; a finite floor keeps exp2(x - m_run) = 0 for
+  for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+    for (int n = 0; n < kNT; ++n) o[hg][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // reference max (base-2 logits) per head; a finite floor keeps exp2(x - m_run) = 0 for
   // masked slots (x = -inf) even before the first valid slot
-  float m_run = -1e30f;
-  float l_run = 0.0f;       // this lane's partial softmax denominator of head hl
+  float m_run[HG], l_run[HG];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    m_run[hg] = -1e30f;
+    l_run[hg] = 0.0f;  // this lane's partial softmax denominator of its head
+  }
 
   for (int c = 0; c < nchunks; ++c) {
-    const int ahead = min(NBUF - 2, nchunks - 1 - c);  // later tiles already issued
-    wait_tiles_ahead<L, NBUF>(ahead);
-    lds_barrier();  // tile c is complete in LDS; buffer (c - 1) % NBUF is free
-    if (c + NBUF - 1 < nchunks) issue(c + NBUF - 1);
-    const unsigned char *tile = smem + (c % NBUF) * TL::kBytes;
+    wait_tile();    // this wave's loads of tile c (the only ones in flight)
+    lds_barrier();  // tile c is complete in LDS; every wave is done with tile c - 1
+    if (c + 1 < nchunks) issue(c + 1);
+    const unsigned char *tile = smem + (c % kNBuf) * TL::kBytes;
 
-    // ---- S^T = rows . q^T   (acc[mt][i] = S^T[slot 16mt + 4g + i][head hl])
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // ---- S^T = rows . q^T   (acc[hg][mt][i] = S^T[slot 16mt + 4g + i][head hl of group hg])
+    f32x4 acc[HG][2];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) acc[hg][0] = acc[hg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
+      const bf16x8 a0 = fr.a_frag(tile, 0, ks), a1 = fr.a_frag(tile, 1, ks);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-            tile + sbase[mt][ks & 3] + (ks >> 2) * 256));
-        acc[mt] = mfma16(a, qf[ks], acc[mt]);
+      for (int hg = 0; hg < HG; ++hg) {
+        acc[hg][0] = mfma16(a0, qf[hg][ks], acc[hg][0]);
+        acc[hg][1] = mfma16(a1, qf[hg][ks], acc[hg][1]);
       }
     }
 
     // ---- online softmax (base 2) with a lazily raised reference max: the reference only
     // moves when the running max exceeds it by more than 2^8, so P <= 256 and O is rescaled
-    // only a handful of times per row.  Lanes hl, hl^16, hl^32, hl^48 share head hl.
+    // only a handful of times per row.  Lanes hl, hl^16, hl^32, hl^48 share a head.
     const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(&slot_rows[c * kSlots + g * 4]);
     const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(&slot_rows[c * kSlots + 16 + g * 4]);
-    float x[2][4];
-    float cmax = -INFINITY;
+    bf16x8 pb[HG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[0][i] = static_cast<int32_t>(rv0[i]) >= 0 ? acc[0][i] * scale_log2 : -INFINITY;
-      x[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? acc[1][i] * scale_log2 : -INFINITY;
-      cmax = fmaxf(cmax, fmaxf(x[0][i], x[1][i]));
-    }
-    cmax = fmaxf(cmax, xor_lane(cmax, 16));
-    cmax = fmaxf(cmax, swap_halves(cmax));
-    if (__ballot(cmax > m_run + 8.0f)) {
-      const float m_new = cmax > m_run + 8.0f ? cmax : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first raise
-      l_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < kDv / 16; ++n) o[n] *= alpha;
-      m_run = m_new;
-    }
-    float p[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int hg = 0; hg < HG; ++hg) {
+      float x[2][4];
+      float cmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[mt][i] = __builtin_amdgcn_exp2f(x[mt][i] - m_run);  // 0 for masked slots
-        l_run += p[mt][i];
+        x[0][i] = static_cast<int32_t>(rv0[i]) >= 0 ? acc[hg][0][i] * scale_log2 : -INFINITY;
+        x[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? acc[hg][1][i] * scale_log2 : -INFINITY;
+        cmax = fmaxf(cmax, fmaxf(x[0][i], x[1][i]));
       }
+      cmax = fmaxf(cmax, xor_lane(cmax, 16));
+      cmax = fmaxf(cmax, swap_halves(cmax));
+      if (__ballot(cmax > m_run[hg] + 8.0f)) {
+        const float m_new = cmax > m_run[hg] + 8.0f ? cmax : m_run[hg];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[hg] - m_new);  // 0 on the first raise
+        l_run[hg] *= alpha;
+#pragma unroll
+        for (int n = 0; n < kNT; ++n) o[hg][n] *= alpha;
+        m_run[hg] = m_new;
+      }
+      float p[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[mt][i] = __builtin_amdgcn_exp2f(x[mt][i] - m_run[hg]);  // 0 for masked slots
+          l_run[hg] += p[mt][i];
+        }
+      pb[hg] = pack_slots(p);
+    }
 
     // ---- O^T += V^T . P^T   (slot k-index 8g + j <-> tile row 4g + j (j < 4), 16 + 4g + j - 4)
-    u32x4 pw;
-    pw[0] = pack_bf16x2(p[0][0], p[0][1]);
-    pw[1] = pack_bf16x2(p[0][2], p[0][3]);
-    pw[2] = pack_bf16x2(p[1][0], p[1][1]);
-    pw[3] = pack_bf16x2(p[1][2], p[1][3]);
-    const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-    for (int n = 0; n < kDv / 16; ++n) {
-      const u32x2 lo = lds_read_tr16(tile + vbase[0][n & 7] + (n >> 3) * 256);
-      const u32x2 hi = lds_read_tr16(tile + vbase[1][n & 7] + (n >> 3) * 256);
-      const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-      o[n] = mfma16(as_bf16x8(va), pb, o[n]);
+    for (int n = 0; n < kNT; ++n) {
+      const bf16x8 va = fr.v_frag(tile, n);
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) o[hg][n] = mfma16(va, pb[hg], o[hg][n]);
     }
   }
 
   // ---- finalize: denominator over the four lane groups, normalise, write
-  float l_tot = l_run + xor_lane(l_run, 16);
-  l_tot += swap_halves(l_tot);
-  const int h = h0 + hl;
-  if (h < H) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (g == 0)
-      lse[t * H + h] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    uint16_t *orow = out + (t * H + h) * kDv + g * 4;
 #pragma unroll
-    for (int n = 0; n < kDv / 16; ++n) {
-      u32x2 v;
-      v[0] = pack_bf16x2(o[n][0] * inv, o[n][1] * inv);
-      v[1] = pack_bf16x2(o[n][2] * inv, o[n][3] * inv);
-      *reinterpret_cast<u32x2 *>(orow + n * 16) = v;
+  for (int hg = 0; hg < HG; ++hg) {
+    float l_tot = l_run[hg] + xor_lane(l_run[hg], 16);
+    l_tot += swap_halves(l_tot);
+    const int h = (wave * HG + hg) * 16 + hl;
+    if (h < H) {
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      if (g == 0)
+        lse[t * H + h] =
+            l_tot > 0.0f ? (m_run[hg] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      uint16_t *orow = out + (t * H + h) * kDv + g * 4;
+#pragma unroll
+      for (int n = 0; n < kNT; ++n) {
+        u32x2 v;
+        v[0] = pack_bf16x2(o[hg][n][0] * inv, o[hg][n][1] * inv);
+        v[1] = pack_bf16x2(o[hg][n][2] * inv, o[hg][n][3] * inv);
+        *reinterpret_cast<u32x2 *>(orow + n * 16) = v;
+      }
     }
   }
 }
 
-template <int DQK, int NW>
+// ---------------------------------------------------------------------------------------
+// 33..64 heads: one work group of 8 waves per query row, split by role so that a SIMD runs
+// one wave of each kind and the two overlap:
+//   S waves 0..3 (wave = 2 hh + d): partial S^T = rows . q^T over dims half d for the 32 heads
+//     of half hh (two 16-head groups, 4 independent MFMA chains); the two halves of a head
+//     group are added through LDS, then wave (hh, d) finishes head group G = 2 hh + d: online
+//     softmax, P (bf16, already in the PV B-operand layout) and any rescale factor to LDS.
+//   PV waves 4..7 (quarter qq): O^T[channels 128 qq .. + 127 x 64 heads] += V^T . P^T; every
+//     V fragment read from LDS feeds four MFMAs (one per head group).
+// The PV waves run one chunk behind: between barriers X(c) and Y(c) the S waves compute the
+// partial S of chunk c while the PV waves consume P of chunk c - 1 (the same two barriers
+// order every buffer hand-over).  Per chunk the kernel reads each latent row's dims twice
+// from LDS and its values once, against four and four times with 16 heads per wave.
+constexpr int kRoleNBuf = 3;
+
+template <int DQK, int SLOTCAP>
+struct RoleSmem {
+  static constexpr int kTiles = kRoleNBuf * Tile<DQK>::kBytes;
+  static constexpr int kX = kTiles;                  // [4 waves][2 mt][64 lanes] f32x4
+  static constexpr int kP = kX + 4 * 2 * 64 * 16;    // [4 groups][64 lanes] bf16x8
+  static constexpr int kA = kP + 4 * 64 * 16;        // [4 groups][64 lanes] fp32 rescale factor
+  static constexpr int kI = kA + 4 * 64 * 4;         // [4 groups][64 lanes] fp32 1/l
+  static constexpr int kF = kI + 4 * 64 * 4;         // [4 groups] int32 rescale flags
+  static constexpr int kSlotRows = kF + 16;
+  static constexpr int kBytes = kSlotRows + SLOTCAP * 4;
+};
+
+template <int DQK, int SLOTCAP>
+__global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
+    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
+  using TL = Tile<DQK>;
+  using SM = RoleSmem<DQK, SLOTCAP>;
+  constexpr int kKS = DQK / 64;          // k-steps per dims half (9 or 8)
+  constexpr int kLoadsS = TL::kLoads / 4;  // tile loads per S wave
+  extern __shared__ __align__(16) unsigned char smem[];
+  f32x4 *xbuf = reinterpret_cast<f32x4 *>(smem + SM::kX);
+  bf16x8 *pbuf = reinterpret_cast<bf16x8 *>(smem + SM::kP);
+  float *abuf = reinterpret_cast<float *>(smem + SM::kA);
+  float *ibuf = reinterpret_cast<float *>(smem + SM::kI);
+  int32_t *fbuf = reinterpret_cast<int32_t *>(smem + SM::kF);
+  int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + SM::kSlotRows);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool s_wave = wave < 4;
+  const int64_t t = blockIdx.x;
+  const int g = lane >> 4;
+  const int hl = lane & 15;
+  const int lim = topk_length ? topk_length[t] : K;
+  const int32_t *irow = idx + t * K;
+  const int nchunks = (lim + kSlots - 1) / kSlots;
+  const uint32_t tiles_lds = lds_addr(smem);
+
+  for (int j = threadIdx.x; j < nchunks * kSlots; j += 512) slot_rows[j] = j < lim ? irow[j] : -1;
+
+  if (s_wave) {
+    // ================================ S waves ================================
+    const int hh = wave >> 1, d = wave & 1;
+    const int G = 2 * hh + d;  // head group this wave finishes
+    bf16x8 qf[2][kKS];         // heads 16 (2 hh + gi) + hl, dims (kKS d + ks) * 32 + g * 8
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int h = (2 * hh + gi) * 16 + hl;
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < H)
+          v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + (kKS * d + ks) * 32 + g * 8));
+        qf[gi][ks] = as_bf16x8(v);
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) settle(qf[gi][ks]);
+    __syncthreads();  // slot rows (and q) ready
+
+    TileFrag<DQK> fr;
+    fr.init();
+    auto issue = [&](int c) {  // this wave's loads k = 4 i + wave of tile c
+      const uint32_t dst = tiles_lds + (c % kRoleNBuf) * TL::kBytes;
+#pragma unroll
+      for (int i = 0; i < kLoadsS; ++i) {
+        const int k = 4 * i + wave;
+        const int pos = k * 64 + lane;
+        const int row = pos / TL::kChunks;
+        const int chunk = (pos % TL::kChunks) ^ TL::swz(row);
+        int r = slot_rows[c * kSlots + row];
+        r = r < 0 ? 0 : r;  // invalid slots load row 0 (masked below)
+        dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + chunk * 16, dst + k * 1024);
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < kRoleNBuf - 1; ++c)
+      if (c < nchunks) issue(c);
+
+    float m_run = -1e30f;  // reference max (base-2 logits) of head 16 G + hl
+    float l_run = 0.0f;    // this lane's partial softmax denominator
+    for (int c = 0; c <= nchunks; ++c) {
+      if (c < nchunks) wait_tiles_ahead<kLoadsS, kRoleNBuf>(min(kRoleNBuf - 2, nchunks - 1 - c));
+      lds_barrier();  // X(c): tile c complete; PV waves may read P(c - 1)
+      if (c == nchunks) break;
+      const unsigned char *tile = smem + (c % kRoleNBuf) * TL::kBytes;
+      // ---- partial S^T over this wave's dims half, both head groups of its half
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) acc[gi][0] = acc[gi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const bf16x8 a0 = fr.a_frag(tile, 0, kKS * d + ks), a1 = fr.a_frag(tile, 1, kKS * d + ks);
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          acc[gi][0] = mfma16(a0, qf[gi][ks], acc[gi][0]);
+          acc[gi][1] = mfma16(a1, qf[gi][ks], acc[gi][1]);
+        }
+      }
+      // hand the other group's partial to the partner wave (same hh, other d)
+      xbuf[(wave * 2 + 0) * 64 + lane] = acc[1 - d][0];
+      xbuf[(wave * 2 + 1) * 64 + lane] = acc[1 - d][1];
+      lds_barrier();  // Y(c): partials exchanged; PV waves are done with P(c - 1) and tile c - 1
+      if (c + kRoleNBuf - 1 < nchunks) issue(c + kRoleNBuf - 1);  // into tile c - 1's buffer
+      const int partner = wave ^ 1;
+      f32x4 sv[2];
+      sv[0] = acc[d][0] + xbuf[(partner * 2 + 0) * 64 + lane];
+      sv[1] = acc[d][1] + xbuf[(partner * 2 + 1) * 64 + lane];
+      // ---- online softmax (base 2) with a lazily raised reference max (see the other kernel)
+      const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(&slot_rows[c * kSlots + g * 4]);
+      const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(&slot_rows[c * kSlots + 16 + g * 4]);
+      float x[2][4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[0][i] = static_cast<int32_t>(rv0[i]) >= 0 ? sv[0][i] * scale_log2 : -INFINITY;
+        x[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? sv[1][i] * scale_log2 : -INFINITY;
+        cmax = fmaxf(cmax, fmaxf(x[0][i], x[1][i]));
+      }
+      cmax = fmaxf(cmax, xor_lane(cmax, 16));
+      cmax = fmaxf(cmax, swap_halves(cmax));
+      int rescale = 0;
+      if (__ballot(cmax > m_run + 8.0f)) {
+        const float m_new = cmax > m_run + 8.0f ? cmax : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first raise
+        l_run *= alpha;
+        m_run = m_new;
+        abuf[G * 64 + lane] = alpha;
+        rescale = 1;
+      }
+      float p[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[mt][i] = __builtin_amdgcn_exp2f(x[mt][i] - m_run);  // 0 for masked slots
+          l_run += p[mt][i];
+        }
+      pbuf[G * 64 + lane] = pack_slots(p);
+      if (lane == 0) fbuf[G] = rescale;
+    }
+    // ---- finalize: denominator over the four lane groups; 1/l for the PV waves
+    float l_tot = l_run + xor_lane(l_run, 16);
+    l_tot += swap_halves(l_tot);
+    const int h = G * 16 + hl;
+    if (h < H && g == 0)
+      lse[t * H + h] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    ibuf[G * 64 + lane] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    lds_barrier();  // Z: 1/l ready
+  } else {
+    // ================================ PV waves ===============================
+    const int qq = wave - 4;
+    __syncthreads();  // slot rows ready (S waves: same barrier)
+    TileFrag<DQK> fr;
+    fr.init();
+    f32x4 o[4][8];  // o[G][n][i] = O[head 16 G + hl][channel 128 qq + 16 n + 4 g + i]
+#pragma unroll
+    for (int G = 0; G < 4; ++G)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) o[G][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c <= nchunks; ++c) {
+      lds_barrier();  // X(c): P(c - 1) and tile c - 1 are ready
+      if (c > 0) {
+        const unsigned char *tile = smem + ((c - 1) % kRoleNBuf) * TL::kBytes;
+        const u32x4 fl = *reinterpret_cast<const u32x4 *>(fbuf);
+        bf16x8 pb[4];
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+          if (fl[G]) {  // wave-uniform
+            const float alpha = abuf[G * 64 + lane];
+#pragma unroll
+            for (int n = 0; n < 8; ++n) o[G][n] *= alpha;
+          }
+          pb[G] = pbuf[G * 64 + lane];
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const bf16x8 va = fr.v_frag(tile, 8 * qq + n);
+#pragma unroll
+          for (int G = 0; G < 4; ++G) o[G][n] = mfma16(va, pb[G], o[G][n]);
+        }
+      }
+      if (c == nchunks) break;
+      lds_barrier();  // Y(c)
+    }
+    lds_barrier();  // Z: 1/l ready
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int h = G * 16 + hl;
+      const float inv = ibuf[G * 64 + lane];
+      if (h < H) {
+        uint16_t *orow = out + (t * H + h) * kDv + 128 * qq + g * 4;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          u32x2 v;
+          v[0] = pack_bf16x2(o[G][n][0] * inv, o[G][n][1] * inv);
+          v[1] = pack_bf16x2(o[G][n][2] * inv, o[G][n][3] * inv);
+          *reinterpret_cast<u32x2 *>(orow + n * 16) = v;
+        }
+      }
+    }
+  }
+}
+
+template <int DQK, int SLOTCAP>
+hipError_t launch_roles(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                        const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K,
+                        float scale, uint16_t *out, float *lse, hipStream_t s) {
+  constexpr size_t smem = RoleSmem<DQK, SLOTCAP>::kBytes;
+  auto kern = sparse_mla_fwd_roles_kernel<DQK, SLOTCAP>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(smem));
+  if (e != hipSuccess) return e;
+  DSA_LAUNCH("sparse_mla_fwd", kern, dim3(static_cast<unsigned>(T_q)), dim3(512), smem, s, q,
+             kv, idx, topk_length, H, K, scale * kLog2e, out, lse);
+  return hipGetLastError();
+}
+
+template <int DQK, int NW, int HG, int SLOTCAP>
 hipError_t launch(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                   const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K, float scale,
                   uint16_t *out, float *lse, hipStream_t s) {
-  constexpr size_t smem = fwd_smem_bytes<DQK, NW>();
-  auto kern = sparse_mla_fwd_kernel<DQK, NW>;
+  constexpr size_t smem = fwd_smem_bytes<DQK, SLOTCAP>();
+  auto kern = sparse_mla_fwd_kernel<DQK, NW, HG, SLOTCAP>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
@@ -231,13 +457,27 @@ hipError_t launch(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
   return hipGetLastError();
 }
 
+// Index rows of up to 2048 slots keep a work group within 80 KB of LDS (two per CU).
+template <int DQK, int NW, int HG>
+hipError_t launch_k(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                    const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K, float scale,
+                    uint16_t *out, float *lse, hipStream_t s) {
+  if (K <= 2048)
+    return launch<DQK, NW, HG, 2048>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  return launch<DQK, NW, HG, 4096>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+}
+
 template <int DQK>
 hipError_t launch_w(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                     const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K, float scale,
                     uint16_t *out, float *lse, hipStream_t s) {
-  if (H <= 16) return launch<DQK, 1>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-  if (H <= 32) return launch<DQK, 2>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-  if (H <= 64) return launch<DQK, 4>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  if (H <= 16) return launch_k<DQK, 1, 1>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  if (H <= 32) return launch_k<DQK, 2, 1>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  if (H <= 64) {
+    if (K <= 2048)
+      return launch_roles<DQK, 2048>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+    return launch_roles<DQK, 4096>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
+  }
   return hipErrorInvalidValue;
 }
 

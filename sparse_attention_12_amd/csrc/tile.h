@@ -7,7 +7,7 @@
 // chunks inside each row without any register traffic:
 //     physical chunk = logical chunk ^ swz(row)
 // swz keeps a chunk inside its aligned group of 8 (576-wide rows) or 16 (512-wide rows) and
-// spreads the 16 rows read by one MFMA fragment over distinct LDS banks.
+// spreads the rows read by one MFMA fragment, row-wise or transposed, over distinct LDS banks.
 //
 // Slots whose index is -1 (or beyond the valid prefix) are filled from latent row 0 so that no
 // load is out of bounds; the kernels mask those slots (probability 0) so the values never
@@ -91,8 +91,16 @@ struct Tile {
   static constexpr int kBytes = kSlots * kRowBytes;
   static constexpr int kLoads = kSlots * kChunks / 64;  // wave-wide DMA instructions per tile
 
+  // Chunk XOR of a row.  Two read patterns must be free of LDS bank conflicts (64 banks of 4
+  // bytes = 16 chunk slots): 16-byte reads of one logical chunk from 16 consecutive rows (MFMA
+  // fragments of rows), and the transposing 8-byte reads of two adjacent chunks from 8
+  // consecutive rows (fragments of columns).  A 576-wide row is 1152 bytes, so odd rows start
+  // 8 chunk slots over: the 3-bit swz must be distinct over the rows of each parity within 16
+  // rows, and swz / 2 distinct (with the parity) within 8 rows.  512-wide rows all start on the
+  // same bank: the 4-bit swz must be distinct within 16 rows, and swz / 2 within 8 rows.
   __device__ static __forceinline__ int swz(int row) {
-    return DQK == 576 ? ((row >> 1) & 7) : (row & 15);
+    return DQK == 576 ? ((((row >> 1) & 3) << 1) | ((row >> 3) & 1))
+                      : (((row & 7) << 1) | ((row >> 3) & 1));
   }
   // byte offset of logical (row, chunk)
   __device__ static __forceinline__ int chunk_off(int row, int chunk) {
