@@ -205,52 +205,50 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// 33..64 heads: one work group of 8 waves per query row, split by role so that a SIMD runs
-// one wave of each kind and the two overlap:
-//   S waves 0..3 (wave = 2 hh + d): partial S^T = rows . q^T over dims half d for the 32 heads
-//     of half hh (two 16-head groups, 4 independent MFMA chains); the two halves of a head
-//     group are added through LDS, then wave (hh, d) finishes head group G = 2 hh + d: online
-//     softmax, P (bf16, already in the PV B-operand layout) and any rescale factor to LDS.
-//   PV waves 4..7 (quarter qq): O^T[channels 128 qq .. + 127 x 64 heads] += V^T . P^T; every
-//     V fragment read from LDS feeds four MFMAs (one per head group).
-// The PV waves run one chunk behind: between barriers X(c) and Y(c) the S waves compute the
-// partial S of chunk c while the PV waves consume P of chunk c - 1 (the same two barriers
-// order every buffer hand-over).  Per chunk the kernel reads each latent row's dims twice
-// from LDS and its values once, against four and four times with 16 heads per wave.
-constexpr int kRoleNBuf = 3;
+// 33..64 heads: one work group of 8 waves per query row, split by role so that every SIMD runs
+// one wave of each kind and their work overlaps:
+//   S waves 0..3 (head group G = wave): S^T = rows . q^T for 16 heads over all dims (four
+//     independent MFMA chains), the online softmax, and P (bf16, already in the PV B-operand
+//     layout) plus any rescale factor to LDS.
+//   PV waves 4..7 (quarter qq): O^T[channels 128 qq .. + 127 x 64 heads] += V^T . P^T one chunk
+//     behind the S waves; every V fragment read from LDS (transposing reads, the slow kind)
+//     feeds four MFMAs, one per head group.  They also fetch the slot indices three chunks
+//     ahead into a small ring.
+// One barrier per chunk: in interval c the S waves work on chunk c while the PV waves finish
+// chunk c - 1, so P, the rescale factors and the flags are double buffered, and a latent-row
+// tile stays in use for two intervals; four tile buffers keep two tiles in flight.
+constexpr int kRoleNBuf = 4;
+constexpr int kRing = 4;  // slot-index ring (tiles)
 
-template <int DQK, int SLOTCAP>
+template <int DQK>
 struct RoleSmem {
   static constexpr int kTiles = kRoleNBuf * Tile<DQK>::kBytes;
-  static constexpr int kX = kTiles;                  // [4 waves][2 mt][64 lanes] f32x4
-  static constexpr int kP = kX + 4 * 2 * 64 * 16;    // [4 groups][64 lanes] bf16x8
-  static constexpr int kA = kP + 4 * 64 * 16;        // [4 groups][64 lanes] fp32 rescale factor
-  static constexpr int kI = kA + 4 * 64 * 4;         // [4 groups][64 lanes] fp32 1/l
-  static constexpr int kF = kI + 4 * 64 * 4;         // [4 groups] int32 rescale flags
-  static constexpr int kSlotRows = kF + 16;
-  static constexpr int kBytes = kSlotRows + SLOTCAP * 4;
+  static constexpr int kP = kTiles;                  // [2][4 groups][64 lanes] bf16x8
+  static constexpr int kA = kP + 2 * 4 * 64 * 16;    // [2][4 groups][16 heads] fp32 rescale
+  static constexpr int kI = kA + 2 * 4 * 16 * 4;     // [4 groups][16 heads] fp32 1/l
+  static constexpr int kF = kI + 4 * 16 * 4;         // [2][4 groups] int32 rescale flags
+  static constexpr int kRingOff = kF + 2 * 4 * 4;    // [kRing][32] int32 slot -> latent row
+  static constexpr int kBytes = kRingOff + kRing * kSlots * 4;
 };
 
-template <int DQK, int SLOTCAP>
+template <int DQK>
 __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
     float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
   using TL = Tile<DQK>;
-  using SM = RoleSmem<DQK, SLOTCAP>;
-  constexpr int kKS = DQK / 64;          // k-steps per dims half (9 or 8)
+  using SM = RoleSmem<DQK>;
+  constexpr int kKSteps = DQK / 32;
   constexpr int kLoadsS = TL::kLoads / 4;  // tile loads per S wave
   extern __shared__ __align__(16) unsigned char smem[];
-  f32x4 *xbuf = reinterpret_cast<f32x4 *>(smem + SM::kX);
   bf16x8 *pbuf = reinterpret_cast<bf16x8 *>(smem + SM::kP);
   float *abuf = reinterpret_cast<float *>(smem + SM::kA);
   float *ibuf = reinterpret_cast<float *>(smem + SM::kI);
   int32_t *fbuf = reinterpret_cast<int32_t *>(smem + SM::kF);
-  int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + SM::kSlotRows);
+  int32_t *ring = reinterpret_cast<int32_t *>(smem + SM::kRingOff);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool s_wave = wave < 4;
   const int64_t t = blockIdx.x;
   const int g = lane >> 4;
   const int hl = lane & 15;
@@ -259,87 +257,82 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
   const int nchunks = (lim + kSlots - 1) / kSlots;
   const uint32_t tiles_lds = lds_addr(smem);
 
-  for (int j = threadIdx.x; j < nchunks * kSlots; j += 512) slot_rows[j] = j < lim ? irow[j] : -1;
+  // slot indices of tile j into the ring (one wave, lanes 0..31; -1 beyond the valid prefix)
+  auto fetch_indices = [&](int j) {
+    if (lane < kSlots) {
+      const int slot = j * kSlots + lane;
+      ring[(j % kRing) * kSlots + lane] = slot < lim ? irow[slot] : -1;
+    }
+  };
+  if (wave == 4)
+    for (int j = 0; j < kRoleNBuf - 1 && j < nchunks; ++j) fetch_indices(j);
 
-  if (s_wave) {
+  if (wave < 4) {
     // ================================ S waves ================================
-    const int hh = wave >> 1, d = wave & 1;
-    const int G = 2 * hh + d;  // head group this wave finishes
-    bf16x8 qf[2][kKS];         // heads 16 (2 hh + gi) + hl, dims (kKS d + ks) * 32 + g * 8
+    const int G = wave;
+    const int h = G * 16 + hl;
+    bf16x8 qf[kKSteps];  // head h, dims ks * 32 + g * 8 + [0, 8)
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const int h = (2 * hh + gi) * 16 + hl;
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (h < H)
-          v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + (kKS * d + ks) * 32 + g * 8));
-        qf[gi][ks] = as_bf16x8(v);
-      }
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (h < H) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
+      qf[ks] = as_bf16x8(v);
     }
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) settle(qf[gi][ks]);
-    __syncthreads();  // slot rows (and q) ready
+    for (int ks = 0; ks < kKSteps; ++ks) settle(qf[ks]);
+    __syncthreads();  // indices of the first tiles are in the ring
 
     TileFrag<DQK> fr;
     fr.init();
     auto issue = [&](int c) {  // this wave's loads k = 4 i + wave of tile c
       const uint32_t dst = tiles_lds + (c % kRoleNBuf) * TL::kBytes;
+      const int32_t *rr = ring + (c % kRing) * kSlots;
 #pragma unroll
       for (int i = 0; i < kLoadsS; ++i) {
         const int k = 4 * i + wave;
         const int pos = k * 64 + lane;
         const int row = pos / TL::kChunks;
         const int chunk = (pos % TL::kChunks) ^ TL::swz(row);
-        int r = slot_rows[c * kSlots + row];
+        int r = rr[row];
         r = r < 0 ? 0 : r;  // invalid slots load row 0 (masked below)
         dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + chunk * 16, dst + k * 1024);
       }
     };
-#pragma unroll
-    for (int c = 0; c < kRoleNBuf - 1; ++c)
-      if (c < nchunks) issue(c);
+    if (nchunks > 0) issue(0);
+    if (nchunks > 1) issue(1);
+    if (nchunks > 0) {  // tile 0 before the first barrier (tile 1 may stay in flight)
+      if (nchunks > 1) wait_vm<kLoadsS>();
+      else wait_tile();
+    }
 
-    float m_run = -1e30f;  // reference max (base-2 logits) of head 16 G + hl
+    float m_run = -1e30f;  // reference max (base-2 logits) of head h
     float l_run = 0.0f;    // this lane's partial softmax denominator
     for (int c = 0; c <= nchunks; ++c) {
-      if (c < nchunks) wait_tiles_ahead<kLoadsS, kRoleNBuf>(min(kRoleNBuf - 2, nchunks - 1 - c));
-      lds_barrier();  // X(c): tile c complete; PV waves may read P(c - 1)
+      lds_barrier();  // B(c - 1): tile c complete; PV waves are done with chunk c - 2
       if (c == nchunks) break;
+      if (c + 2 < nchunks) issue(c + 2);  // into the buffer of tile c - 2
       const unsigned char *tile = smem + (c % kRoleNBuf) * TL::kBytes;
-      // ---- partial S^T over this wave's dims half, both head groups of its half
-      f32x4 acc[2][2];
+      // ---- S^T = rows . q^T  (four chains: slot half mt, k-step parity)
+      f32x4 acc[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
+                         {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) acc[gi][0] = acc[gi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 a0 = fr.a_frag(tile, 0, kKS * d + ks), a1 = fr.a_frag(tile, 1, kKS * d + ks);
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          acc[gi][0] = mfma16(a0, qf[gi][ks], acc[gi][0]);
-          acc[gi][1] = mfma16(a1, qf[gi][ks], acc[gi][1]);
-        }
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        acc[0][ks & 1] = mfma16(fr.a_frag(tile, 0, ks), qf[ks], acc[0][ks & 1]);
+        acc[1][ks & 1] = mfma16(fr.a_frag(tile, 1, ks), qf[ks], acc[1][ks & 1]);
       }
-      // hand the other group's partial to the partner wave (same hh, other d)
-      xbuf[(wave * 2 + 0) * 64 + lane] = acc[1 - d][0];
-      xbuf[(wave * 2 + 1) * 64 + lane] = acc[1 - d][1];
-      lds_barrier();  // Y(c): partials exchanged; PV waves are done with P(c - 1) and tile c - 1
-      if (c + kRoleNBuf - 1 < nchunks) issue(c + kRoleNBuf - 1);  // into tile c - 1's buffer
-      const int partner = wave ^ 1;
-      f32x4 sv[2];
-      sv[0] = acc[d][0] + xbuf[(partner * 2 + 0) * 64 + lane];
-      sv[1] = acc[d][1] + xbuf[(partner * 2 + 1) * 64 + lane];
-      // ---- online softmax (base 2) with a lazily raised reference max (see the other kernel)
-      const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(&slot_rows[c * kSlots + g * 4]);
-      const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(&slot_rows[c * kSlots + 16 + g * 4]);
+      const f32x4 sv0 = acc[0][0] + acc[0][1], sv1 = acc[1][0] + acc[1][1];
+      // ---- online softmax (base 2) with a lazily raised reference max: the reference only
+      // moves when the running max exceeds it by more than 2^8, so P <= 256 and O is rescaled
+      // only a handful of times per row.  Lanes hl, hl^16, hl^32, hl^48 share head h.
+      const int32_t *rr = ring + (c % kRing) * kSlots;
+      const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(rr + g * 4);
+      const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(rr + 16 + g * 4);
       float x[2][4];
       float cmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[0][i] = static_cast<int32_t>(rv0[i]) >= 0 ? sv[0][i] * scale_log2 : -INFINITY;
-        x[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? sv[1][i] * scale_log2 : -INFINITY;
+        x[0][i] = static_cast<int32_t>(rv0[i]) >= 0 ? sv0[i] * scale_log2 : -INFINITY;
+        x[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? sv1[i] * scale_log2 : -INFINITY;
         cmax = fmaxf(cmax, fmaxf(x[0][i], x[1][i]));
       }
       cmax = fmaxf(cmax, xor_lane(cmax, 16));
@@ -350,7 +343,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first raise
         l_run *= alpha;
         m_run = m_new;
-        abuf[G * 64 + lane] = alpha;
+        if (g == 0) abuf[((c & 1) * 4 + G) * 16 + hl] = alpha;
         rescale = 1;
       }
       float p[2][4];
@@ -361,21 +354,23 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
           p[mt][i] = __builtin_amdgcn_exp2f(x[mt][i] - m_run);  // 0 for masked slots
           l_run += p[mt][i];
         }
-      pbuf[G * 64 + lane] = pack_slots(p);
-      if (lane == 0) fbuf[G] = rescale;
+      pbuf[((c & 1) * 4 + G) * 64 + lane] = pack_slots(p);
+      if (lane == 0) fbuf[(c & 1) * 4 + G] = rescale;
+      // tile c + 1 before the next barrier (tile c + 2 may stay in flight)
+      if (c + 2 < nchunks) wait_vm<kLoadsS>();
+      else wait_tile();
     }
     // ---- finalize: denominator over the four lane groups; 1/l for the PV waves
     float l_tot = l_run + xor_lane(l_run, 16);
     l_tot += swap_halves(l_tot);
-    const int h = G * 16 + hl;
     if (h < H && g == 0)
       lse[t * H + h] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    ibuf[G * 64 + lane] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (g == 0) ibuf[G * 16 + hl] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     lds_barrier();  // Z: 1/l ready
   } else {
     // ================================ PV waves ===============================
     const int qq = wave - 4;
-    __syncthreads();  // slot rows ready (S waves: same barrier)
+    __syncthreads();  // indices of the first tiles are in the ring
     TileFrag<DQK> fr;
     fr.init();
     f32x4 o[4][8];  // o[G][n][i] = O[head 16 G + hl][channel 128 qq + 16 n + 4 g + i]
@@ -384,19 +379,22 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
 #pragma unroll
       for (int n = 0; n < 8; ++n) o[G][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c <= nchunks; ++c) {
-      lds_barrier();  // X(c): P(c - 1) and tile c - 1 are ready
+      lds_barrier();  // B(c - 1): P and rescale factors of chunk c - 1 are ready
+      // indices of tile c + 3 into the slot of tile c - 1 (its S work ended at B(c - 1))
+      if (wave == 4 && c + kRoleNBuf - 1 < nchunks) fetch_indices(c + kRoleNBuf - 1);
       if (c > 0) {
+        const int b = (c - 1) & 1;
         const unsigned char *tile = smem + ((c - 1) % kRoleNBuf) * TL::kBytes;
-        const u32x4 fl = *reinterpret_cast<const u32x4 *>(fbuf);
+        const u32x4 fl = *reinterpret_cast<const u32x4 *>(fbuf + b * 4);
         bf16x8 pb[4];
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
           if (fl[G]) {  // wave-uniform
-            const float alpha = abuf[G * 64 + lane];
+            const float alpha = abuf[(b * 4 + G) * 16 + hl];
 #pragma unroll
             for (int n = 0; n < 8; ++n) o[G][n] *= alpha;
           }
-          pb[G] = pbuf[G * 64 + lane];
+          pb[G] = pbuf[(b * 4 + G) * 64 + lane];
         }
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
@@ -406,13 +404,12 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
         }
       }
       if (c == nchunks) break;
-      lds_barrier();  // Y(c)
     }
     lds_barrier();  // Z: 1/l ready
 #pragma unroll
     for (int G = 0; G < 4; ++G) {
       const int h = G * 16 + hl;
-      const float inv = ibuf[G * 64 + lane];
+      const float inv = ibuf[G * 16 + hl];
       if (h < H) {
         uint16_t *orow = out + (t * H + h) * kDv + 128 * qq + g * 4;
 #pragma unroll
@@ -427,12 +424,12 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
   }
 }
 
-template <int DQK, int SLOTCAP>
+template <int DQK>
 hipError_t launch_roles(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                         const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K,
                         float scale, uint16_t *out, float *lse, hipStream_t s) {
-  constexpr size_t smem = RoleSmem<DQK, SLOTCAP>::kBytes;
-  auto kern = sparse_mla_fwd_roles_kernel<DQK, SLOTCAP>;
+  constexpr size_t smem = RoleSmem<DQK>::kBytes;
+  auto kern = sparse_mla_fwd_roles_kernel<DQK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
@@ -473,11 +470,7 @@ hipError_t launch_w(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                     uint16_t *out, float *lse, hipStream_t s) {
   if (H <= 16) return launch_k<DQK, 1, 1>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
   if (H <= 32) return launch_k<DQK, 2, 1>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-  if (H <= 64) {
-    if (K <= 2048)
-      return launch_roles<DQK, 2048>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-    return launch_roles<DQK, 4096>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
-  }
+  if (H <= 64) return launch_roles<DQK>(q, kv, idx, topk_length, T_q, H, K, scale, out, lse, s);
   return hipErrorInvalidValue;
 }
 
