@@ -305,6 +305,7 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   if (int rc = check_attention_args("sparse_mla_bwd", q, kv, idx, T_q, T_kv, H, D_qk, D_v, K,
                                     scale, 64))
     return rc;
+  if (K > 4096) return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: K=%d exceeds 4096", K);
   if (flags & ~(DSA_BWD_ACCUMULATE_DKV | DSA_DEBUG_CHECK_INDICES))
     return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: unknown flags 0x%x", flags);
   if (T_q > 0 && (!out || !lse || !dout || !dq))

@@ -64,6 +64,13 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
 }
 
+// Value of `x` held by lane (lane ^ 16), without a trip through LDS (v_permlane16_swap: the
+// first result holds the even 16-lane row's values, the second the odd row's).
+__device__ __forceinline__ float xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ float xor_lane(float x, int mask) {
   return __shfl_xor(x, mask, 64);
 }

@@ -10,22 +10,10 @@
 // allows):
 //   delta  : Delta[t,h] = sum_c dO[t,h,c] O[t,h,c]          (streaming, one wave per (t,h))
 //   rows   : one launch whose even work groups compute dq and odd work groups the key-gradient
-//            contributions of the same query rows, so the LDS/MFMA-bound dq work and the
-//            HBM-bound contribution stores overlap on every CU.
-//     dq   : waves own 16 heads each.  Per 32-slot chunk the latent rows are gathered into
-//            LDS; S^T and dP^T come from 16x16x32 bf16 MFMAs with the row tile as A and the
-//            wave's q / dO blocks (registers) as B; dZ is formed in registers and dq += dZ . rows
-//            uses dZ as the A operand directly (same slot permutation as the forward's P . V)
-//            and transposing LDS reads for the rows.
-//     contributions : 4 waves.  The row's q and dO blocks are first staged through LDS and read
-//            back transposed into registers so that the head axis is the MFMA contraction
-//            axis; wave w owns a quarter of the latent channels.  Per chunk the waves recompute
-//            S^T / dP^T for their head tile, publish scale * dZ^T and P^T in LDS, each as a bf16
-//            pair hi + lo (hi = bf16(x), lo = bf16(x - hi), about 16 significant bits), and
-//            every wave then forms C[32 slots x its channels] = (scale dZ)^T . q + P^T . dO from
-//            the four bf16 products (plain bf16 rounding of P and dZ, 8 bits, would leave a
-//            visible error in latent rows picked by thousands of queries).  C is stored in fp32
-//            to a staging buffer, one row per (query, slot).
+//            contributions of the same query rows (layout of the waves below).  Both recompute
+//            S^T and dP^T per 32-slot chunk of gathered latent rows; dq work groups then form
+//            dq = scale dZ . rows, contribution work groups C = scale dZ^T . q + P^T . dO
+//            for every (query, slot) pair and store C in fp32 to a staging buffer.
 //   count / scan / fill : a counting sort of the pass's (query, slot) pairs by latent row.
 //   reduce : one work group per latent row adds up its staged contributions and adds the sum
 //            to dkv (every row has a single owner, so no atomics touch dkv).
@@ -69,323 +57,472 @@ __global__ void fill_zero_kernel(float *__restrict__ p, int64_t n) {
   for (int64_t j = i; j < n; j += stride) p[j] = 0.0f;
 }
 
-constexpr int kRowWaves = 4;  // waves of a work group of the rows launch
-constexpr int kRowBufs = 3;   // latent-row tile buffers
-constexpr int kMaxK = 4096;   // largest top-k width whose index row fits the LDS copy
+// ---------------------------------------------------------------------------------------
+// rows launch: work group 2i handles dq of query row row0 + i, 2i + 1 its key-gradient
+// contributions.  Both kinds have 8 waves split by role, so that every SIMD runs one wave of
+// each kind and their work overlaps, and one barrier per 32-slot chunk:
+//   SdP waves 0..3 (head group G = wave, 16 heads): S^T = rows . q^T and dP^T = V . dO^T
+//     (16x16x32 MFMAs, A = LDS row fragments, B = q / dO blocks in registers), then
+//     P = exp(S - lse) and dZ = P (dP - Delta).
+//   dq work group, waves 4..7 (channel quarter qq): dq^T[channels x 64 heads] += rows^T . dZ^T
+//     one chunk behind the SdP waves, dZ (bf16) of all head groups read from LDS; every
+//     transposed row fragment feeds four MFMAs.  They also issue the latent-row tile loads.
+//   contribution work group, waves 4..7 (channel quarter qq): C[32 slots x channels] =
+//     scale dZ^T . q + P^T . dO one chunk behind, with q / dO held as head-contraction
+//     fragments and scale dZ / P staged in LDS as bf16 ([slot][head]), each as a pair hi + lo
+//     (hi = bf16(x), lo = bf16(x - hi), about 16 significant bits): with either rounded to 8
+//     bits a latent row picked by many queries collects an error near the 2e-2 bar.  C is
+//     stored in fp32.
+// Tile loads (direct to LDS, waited for with explicit load counts) come from waves that issue no
+// other vector-memory operation, so that those counts stay exact and the compiler's own waits
+// never wait for tiles.  The dq work group fetches slot indices into a small ring from SdP wave
+// 0 (ordinary loads, four tiles ahead); the contribution work group, whose channel waves store
+// and whose SdP waves load tiles, reads the row's whole index list into LDS first.
+constexpr int kRowWaves = 8;
+constexpr int kDqBufs = 4;  // dq work group: a tile is read in two intervals
+constexpr int kCBufs = 3;   // contribution work group: a tile is read in one interval
+constexpr int kRing = 8;    // slot-index ring (tiles)
+constexpr int kSS = 72;     // staging row stride: 64 heads + 8 (bf16)
+constexpr int kMaxK = 4096; // largest top-k of the contribution work group's index list
 
 template <int DQK>
-using RowStream = TileStream<DQK, kRowWaves, kRowBufs>;
-
-// LDS of a rows work group: tile buffers | slot rows [kMaxK] | (contributions) dZ / P staging
-template <int DQK, int HP>
 struct RowSmem {
-  static constexpr int kTiles = kRowBufs * Tile<DQK>::kBytes;
-  static constexpr int kSlotRows = kTiles;
-  static constexpr int kStage = kSlotRows + kMaxK * 4;
-  static constexpr int kStageStride = HP + 8;  // [slot][head] bf16 rows (+16 B)
-  static constexpr int kStageBytes = 4 * kSlots * kStageStride * 2;
-  static constexpr int kBytes = kStage + kStageBytes;
-  // prologue staging of the row's q ([HP][DQK+16]) and dO ([HP][512+16]) in the tile area
+  static constexpr int kTileB = Tile<DQK>::kBytes;
+  // dq work group: tiles[4] | dZ[2][4 groups][64 lanes] bf16x8 | ring
+  static constexpr int kDqZ = kDqBufs * kTileB;
+  static constexpr int kDqRing = kDqZ + 2 * 4 * 64 * 16;
+  static constexpr int kDqBytes = kDqRing + kRing * kSlots * 4;
+  // contribution work group: tiles[3] | staging[2][zh, zl, ph, pl][32 slots][kSS] bf16 | slot
+  // rows (K entries rounded up to a whole tile);
+  // the row's q ([64][DQK + 16]) and dO ([64][512 + 16]) pass through the tile area first
+  static constexpr int kCStageBytes = 4 * kSlots * kSS * 2;
+  static constexpr int kCStage = kCBufs * kTileB;
+  static constexpr int kCRows = kCStage + 2 * kCStageBytes;
+  static constexpr int kCBytes = kCRows + kMaxK * 4;
+  static size_t bytes(int K) {
+    const size_t c = kCRows + static_cast<size_t>((K + kSlots - 1) / kSlots) * kSlots * 4;
+    return c > kDqBytes ? c : static_cast<size_t>(kDqBytes);
+  }
   static constexpr int kQStride = DQK + 16;
   static constexpr int kOStride = kDv + 16;
-  static_assert(HP * kQStride * 2 <= kTiles, "q staging must fit the tile area");
+  static_assert(64 * kQStride * 2 <= kCStage, "q staging must fit the tile area");
+  static_assert(kDqBytes <= 160 * 1024 && kCBytes <= 160 * 1024, "LDS per work group");
 };
 
-// The query row's slot -> latent row map in LDS (-1 for invalid slots, padded to whole tiles),
-// then the per-head operands shared by both row paths.
-struct RowHead {
-  int lim, nchunks;
-  float lse2, dlt;
-};
-
-template <int DQK>
-__device__ __forceinline__ RowHead row_setup(const int32_t *__restrict__ idx,
-                                             const int32_t *__restrict__ topk_length,
-                                             const float *__restrict__ lse,
-                                             const float *__restrict__ delta, int H, int K,
-                                             int64_t t, int h, int32_t *slot_rows) {
-  RowHead r;
-  r.lim = topk_length ? topk_length[t] : K;
-  r.nchunks = (r.lim + kSlots - 1) / kSlots;
-  const int32_t *irow = idx + t * K;
-  for (int j = threadIdx.x; j < r.nchunks * kSlots; j += kRowWaves * 64)
-    slot_rows[j] = j < r.lim ? irow[j] : -1;
-  const bool hok = h < H;
-  const float l0 = hok ? lse[t * H + h] : 0.0f;
-  r.lse2 = l0 == -INFINITY ? INFINITY : l0 * kLog2e;  // empty row: P = 0
-  r.dlt = hok ? delta[t * H + h] : 0.0f;
-  return r;
+// slot indices of tile j (lanes 0..31 of a wave; -1 beyond the valid prefix) and the ring slot
+__device__ __forceinline__ int32_t load_tile_indices(const int32_t *__restrict__ irow, int lim,
+                                                     int j) {
+  const int lane = __lane_id();
+  const int slot = j * kSlots + lane;
+  return lane < kSlots && slot < lim ? irow[slot] : -1;
+}
+__device__ __forceinline__ void put_tile_indices(int32_t *ring, int j, int32_t v) {
+  const int lane = __lane_id();
+  if (lane < kSlots) ring[(j % kRing) * kSlots + lane] = v;
 }
 
-// S^T and dP^T of the wave's 16-head tile over the 32 slots of `tile`, then P and dZ in the
-// S^T fragment layout (slot 16 mt + 4 g + i, head hl).
+// This wave's share (loads k = 4 i + part) of the tile-c loads into buffer c % NBUF; rr lists
+// the tile's 32 latent rows (-1: invalid slot).
+template <int DQK, int NBUF>
+__device__ __forceinline__ void issue_tile(uint32_t tiles_lds, const uint16_t *kv,
+                                           const int32_t *rr, int c, int part) {
+  using TL = Tile<DQK>;
+  constexpr int kLoadsW = TL::kLoads / 4;
+  const int lane = __lane_id();
+  const uint32_t dst = tiles_lds + (c % NBUF) * TL::kBytes;
+  // all row indices first: the loads are asm with a memory clobber, so an index read placed
+  // between two of them would be waited for on its own
+  uint32_t off[kLoadsW];
+#pragma unroll
+  for (int i = 0; i < kLoadsW; ++i) {
+    const int pos = (4 * i + part) * 64 + lane;
+    const int row = pos / TL::kChunks;
+    const int chunk = (pos % TL::kChunks) ^ TL::swz(row);
+    const int r = rr[row];
+    off[i] = static_cast<uint32_t>(r < 0 ? 0 : r) * TL::kRowBytes + chunk * 16;  // -1: row 0
+  }
+#pragma unroll
+  for (int i = 0; i < kLoadsW; ++i) dma16_sv(kv, off[i], dst + (4 * i + part) * 1024);
+}
+
+// Per-head operands of an SdP wave: q / dO blocks (B operands: lane -> head hl, dims ks*32 +
+// g*8 + [0, 8)), and lse (base 2) / Delta of its head.
 template <int DQK>
-__device__ __forceinline__ void slot_grads(const unsigned char *tile, const TileFrag<DQK> &fr,
-                                           const int32_t *slot_rows_c, const bf16x8 *qf,
-                                           const bf16x8 *df, float lse2, float dlt,
-                                           float scale_log2, float p[2][4], float dz[2][4]) {
-  const int g = __lane_id() >> 4;
-  f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+struct SdpHead {
+  bf16x8 qf[DQK / 32], df[kDv / 32];
+  float lse2, dlt;
+  __device__ __forceinline__ void load(const uint16_t *__restrict__ q,
+                                       const uint16_t *__restrict__ dout,
+                                       const float *__restrict__ lse,
+                                       const float *__restrict__ delta, int H, int64_t t, int h) {
+    const int g = __lane_id() >> 4;
+    const bool hok = h < H;
 #pragma unroll
-  for (int ks = 0; ks < DQK / 32; ++ks) {
+    for (int ks = 0; ks < DQK / 32; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hok) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
+      qf[ks] = as_bf16x8(v);
+    }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 a = fr.a_frag(tile, mt, ks);
-      s[mt] = mfma16(a, qf[ks], s[mt]);
-      if (ks < kDv / 32) dp[mt] = mfma16(a, df[ks], dp[mt]);
+    for (int ks = 0; ks < kDv / 32; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hok) v = *reinterpret_cast<const u32x4 *>(dout + ((t * H + h) * kDv + ks * 32 + g * 8));
+      df[ks] = as_bf16x8(v);
+    }
+    const float l0 = hok ? lse[t * H + h] : -INFINITY;
+    lse2 = l0 == -INFINITY ? INFINITY : l0 * kLog2e;  // empty row or padded head: P = 0
+    dlt = hok ? delta[t * H + h] : 0.0f;
+  }
+  __device__ __forceinline__ void settle_all() {
+#pragma unroll
+    for (int ks = 0; ks < DQK / 32; ++ks) settle(qf[ks]);
+#pragma unroll
+    for (int ks = 0; ks < kDv / 32; ++ks) settle(df[ks]);
+    settle(lse2);
+    settle(dlt);
+  }
+  // P and dZ of the 32 slots of `tile` in the S^T fragment layout (slot 16 mt + 4 g + i)
+  __device__ __forceinline__ void grads(const unsigned char *tile, const TileFrag<DQK> &fr,
+                                        const int32_t *rr, float scale_log2, float p[2][4],
+                                        float dz[2][4]) const {
+    constexpr int kKS = DQK / 32;
+    const int g = __lane_id() >> 4;
+    f32x4 s[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
+                     {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
+    f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // fragment reads run two k-steps ahead of the MFMAs
+    bf16x8 a0[3], a1[3];
+    a0[0] = fr.a_frag(tile, 0, 0);
+    a1[0] = fr.a_frag(tile, 1, 0);
+    a0[1] = fr.a_frag(tile, 0, 1);
+    a1[1] = fr.a_frag(tile, 1, 1);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      if (ks + 2 < kKS) {
+        a0[(ks + 2) % 3] = fr.a_frag(tile, 0, ks + 2);
+        a1[(ks + 2) % 3] = fr.a_frag(tile, 1, ks + 2);
+      }
+      s[0][ks & 1] = mfma16(a0[ks % 3], qf[ks], s[0][ks & 1]);
+      s[1][ks & 1] = mfma16(a1[ks % 3], qf[ks], s[1][ks & 1]);
+      if (ks < kDv / 32) {
+        dp[0] = mfma16(a0[ks % 3], df[ks], dp[0]);
+        dp[1] = mfma16(a1[ks % 3], df[ks], dp[1]);
+      }
+    }
+    const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(rr + g * 4);
+    const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(rr + 16 + g * 4);
+    const f32x4 s0 = s[0][0] + s[0][1], s1 = s[1][0] + s[1][1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[0][i] = static_cast<int32_t>(rv0[i]) >= 0 ? __builtin_amdgcn_exp2f(s0[i] * scale_log2 - lse2) : 0.0f;
+      p[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? __builtin_amdgcn_exp2f(s1[i] * scale_log2 - lse2) : 0.0f;
+      dz[0][i] = p[0][i] * (dp[0][i] - dlt);
+      dz[1][i] = p[1][i] * (dp[1][i] - dlt);
     }
   }
-  const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(slot_rows_c + g * 4);
-  const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(slot_rows_c + 16 + g * 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool v0 = static_cast<int32_t>(rv0[i]) >= 0, v1 = static_cast<int32_t>(rv1[i]) >= 0;
-    p[0][i] = v0 ? __builtin_amdgcn_exp2f(s[0][i] * scale_log2 - lse2) : 0.0f;
-    p[1][i] = v1 ? __builtin_amdgcn_exp2f(s[1][i] * scale_log2 - lse2) : 0.0f;
-    dz[0][i] = p[0][i] * (dp[0][i] - dlt);
-    dz[1][i] = p[1][i] * (dp[1][i] - dlt);
-  }
-}
-
-// q / dO block of the wave's head tile as MFMA B operands (lane -> head hl, dims ks*32 + g*8).
-template <int DQK>
-__device__ __forceinline__ void load_head_frags(const uint16_t *__restrict__ q,
-                                                const uint16_t *__restrict__ dout, int H,
-                                                int64_t t, int h, bf16x8 *qf, bf16x8 *df) {
-  const int g = __lane_id() >> 4;
-  const bool hok = h < H;
-#pragma unroll
-  for (int ks = 0; ks < DQK / 32; ++ks) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (hok) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
-    qf[ks] = as_bf16x8(v);
-  }
-#pragma unroll
-  for (int ks = 0; ks < kDv / 32; ++ks) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (hok) v = *reinterpret_cast<const u32x4 *>(dout + ((t * H + h) * kDv + ks * 32 + g * 8));
-    df[ks] = as_bf16x8(v);
-  }
-}
+};
 
 // ---------------------------------------------------------------------------------------
-// dq of query row t: dq^T[channels x 16 heads] += rows^T . dZ^T per tile (A = transposing
-// reads of the row tile, B = dZ packed from registers), so a lane ends with channels
-// 16 n + 4 g .. + 3 of head hl.
-template <int DQK, int HP>
+template <int DQK>
 __device__ __forceinline__ void bwd_dq_row(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
     const float *__restrict__ lse, const float *__restrict__ delta,
     const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
     uint16_t *__restrict__ dq, int64_t t, unsigned char *smem) {
-  using SM = RowSmem<DQK, HP>;
-  constexpr int kNT = DQK / 16;
-  int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + SM::kSlotRows);
+  using TL = Tile<DQK>;
+  using SM = RowSmem<DQK>;
+  constexpr int kNTq = DQK / 64;  // channel tiles per quarter (9 or 8)
+  bf16x8 *zbuf = reinterpret_cast<bf16x8 *>(smem + SM::kDqZ);
+  int32_t *ring = reinterpret_cast<int32_t *>(smem + SM::kDqRing);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, hl = lane & 15;
-  const int h = wave * 16 + hl;
-  const bool active = wave * 16 < H;  // waves without heads only help with the loads
+  const int lim = topk_length ? topk_length[t] : K;
+  const int32_t *irow = idx + t * K;
+  const int nchunks = (lim + kSlots - 1) / kSlots;
 
-  bf16x8 qf[DQK / 32], df[kDv / 32];
-  load_head_frags<DQK>(q, dout, H, t, h, qf, df);
-  const RowHead rh = row_setup<DQK>(idx, topk_length, lse, delta, H, K, t, h, slot_rows);
+  if (wave < 4) {
+    // ============================== SdP waves ==============================
+    const int G = wave;
+    int32_t pending = -1;  // wave 0: indices four tiles ahead, one interval in flight
+    if (wave == 0) {
+      int32_t first[4];
 #pragma unroll
-  for (int ks = 0; ks < DQK / 32; ++ks) settle(qf[ks]);
+      for (int j = 0; j < 4; ++j) first[j] = load_tile_indices(irow, lim, j);
+      pending = load_tile_indices(irow, lim, 4);
 #pragma unroll
-  for (int ks = 0; ks < kDv / 32; ++ks) settle(df[ks]);
-  __syncthreads();
-
-  RowStream<DQK> ts;
-  ts.init(smem, wave);
-  TileFrag<DQK> fr;
-  fr.init();
+      for (int j = 0; j < 4; ++j) put_tile_indices(ring, j, first[j]);
+    }
+    SdpHead<DQK> hd;
+    hd.load(q, dout, lse, delta, H, t, G * 16 + hl);
+    __syncthreads();  // S0: indices of the first tiles are in the ring
+    __syncthreads();  // S1: the first tiles are loaded
+    TileFrag<DQK> fr;
+    fr.init();
+    for (int c = 0; c <= nchunks; ++c) {
+      lds_barrier();  // B(c - 1)
+      if (c == nchunks) break;
+      if (wave == 0 && c + 5 <= nchunks) {  // ring slot of tile c - 4 is free
+        put_tile_indices(ring, c + 4, pending);
+        if (c + 5 < nchunks) pending = load_tile_indices(irow, lim, c + 5);
+      }
+      float p[2][4], dz[2][4];
+      hd.grads(smem + (c % kDqBufs) * TL::kBytes, fr, ring + (c % kRing) * kSlots, scale_log2,
+               p, dz);
+      zbuf[((c & 1) * 4 + G) * 64 + lane] = pack_slots(dz);
+    }
+    lds_barrier();  // Z
+  } else {
+    // ============================== dq waves ===============================
+    const int qq = wave - 4;
+    const uint32_t tiles_lds = lds_addr(smem);
+    constexpr int kLoadsW = TL::kLoads / 4;
+    __syncthreads();  // S0
+    if (nchunks > 0) issue_tile<DQK, kDqBufs>(tiles_lds, kv, ring, 0, qq);
+    if (nchunks > 1) issue_tile<DQK, kDqBufs>(tiles_lds, kv, ring + kSlots, 1, qq);
+    if (nchunks > 0) {  // tile 0 before S1 (tile 1 may stay in flight)
+      if (nchunks > 1) wait_vm<kLoadsW>();
+      else wait_tile();
+    }
+    __syncthreads();  // S1
+    ColFrags<DQK, kNTq> fr;
+    fr.init(kNTq * qq);
+    f32x4 acc[4][kNTq];  // acc[G][n][i] = dq[head 16 G + hl][channel 16 (kNTq qq + n) + 4 g + i]
 #pragma unroll
-  for (int c = 0; c < kRowBufs - 1; ++c)
-    if (c < rh.nchunks) ts.issue(c, kv, slot_rows);
-
-  f32x4 acc[kNT];
+    for (int G = 0; G < 4; ++G)
 #pragma unroll
-  for (int n = 0; n < kNT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < rh.nchunks; ++c) {
-    RowStream<DQK>::acquire(c, rh.nchunks);
-    if (c + kRowBufs - 1 < rh.nchunks) ts.issue(c + kRowBufs - 1, kv, slot_rows);
-    if (!active) continue;
-    const unsigned char *tile = smem + (c % kRowBufs) * Tile<DQK>::kBytes;
-    float p[2][4], dz[2][4];
-    slot_grads<DQK>(tile, fr, slot_rows + c * kSlots, qf, df, rh.lse2, rh.dlt, scale_log2, p,
-                    dz);
-    const bf16x8 zb = pack_slots(dz);
+      for (int n = 0; n < kNTq; ++n) acc[G][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c <= nchunks; ++c) {
+      lds_barrier();  // B(c - 1): dZ of chunk c - 1 is ready
+      if (c + 2 < nchunks) issue_tile<DQK, kDqBufs>(tiles_lds, kv, ring + ((c + 2) % kRing) * kSlots, c + 2, qq);
+      if (c > 0) {
+        const unsigned char *tile = smem + ((c - 1) % kDqBufs) * TL::kBytes;
+        bf16x8 zb[4];
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) acc[n] = mfma16(fr.v_frag(tile, n), zb, acc[n]);
-  }
-  if (active && h < H) {
-    uint16_t *row = dq + (t * H + h) * DQK + g * 4;
+        for (int G = 0; G < 4; ++G) zb[G] = zbuf[(((c - 1) & 1) * 4 + G) * 64 + lane];
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) {
-      u32x2 v;
-      v[0] = pack_bf16x2(acc[n][0] * scale, acc[n][1] * scale);
-      v[1] = pack_bf16x2(acc[n][2] * scale, acc[n][3] * scale);
-      *reinterpret_cast<u32x2 *>(row + n * 16) = v;
+        for (int n = 0; n < kNTq; ++n) {
+          const bf16x8 va = fr.frag(tile, n);
+#pragma unroll
+          for (int G = 0; G < 4; ++G) acc[G][n] = mfma16(va, zb[G], acc[G][n]);
+        }
+      }
+      if (c == nchunks) break;
+      if (c + 2 < nchunks) wait_vm<kLoadsW>();  // tile c + 1 before the next barrier
+      else wait_tile();
+    }
+    lds_barrier();  // Z
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int hh = G * 16 + hl;
+      if (hh < H) {
+        uint16_t *row = dq + (t * H + hh) * DQK + 16 * kNTq * qq + g * 4;
+#pragma unroll
+        for (int n = 0; n < kNTq; ++n) {
+          u32x2 v;
+          v[0] = pack_bf16x2(acc[G][n][0] * scale, acc[G][n][1] * scale);
+          v[1] = pack_bf16x2(acc[G][n][2] * scale, acc[G][n][3] * scale);
+          *reinterpret_cast<u32x2 *>(row + n * 16) = v;
+        }
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// Key-gradient contributions of query row t, stored to stage[slot][DQK] (fp32) for every
-// valid slot.  Wave w owns latent channels [w DQK / 4, (w + 1) DQK / 4).
-template <int DQK, int HP>  // HP: head count padded to the contraction width (32 or 64)
+// Key-gradient contributions of query row t, stored to stage[slot][DQK] (fp32) for every valid
+// slot.
+template <int DQK>
 __device__ __forceinline__ void bwd_contrib_row(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
     const float *__restrict__ lse, const float *__restrict__ delta,
     const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
-    float *__restrict__ stage, int64_t t, unsigned char *smem_raw) {
-  using SM = RowSmem<DQK, HP>;
-  constexpr int kChanPerWave = DQK / kRowWaves;  // 144 or 128
-  constexpr int kNTw = kChanPerWave / 16;        // output tiles per wave (9 or 8)
-  constexpr int kKH = HP / 32;                   // head contraction steps
-  constexpr int kSS = SM::kStageStride;
-  uint16_t *qstage = reinterpret_cast<uint16_t *>(smem_raw);  // prologue only
-  int32_t *slot_rows = reinterpret_cast<int32_t *>(smem_raw + SM::kSlotRows);
-  uint16_t *zst = reinterpret_cast<uint16_t *>(smem_raw + SM::kStage);  // scale*dZ^T hi
-  uint16_t *zsl = zst + kSlots * kSS;                                    //            lo
-  uint16_t *pst = zsl + kSlots * kSS;                                    // P^T        hi
-  uint16_t *psl = pst + kSlots * kSS;                                    //            lo
-
+    float *__restrict__ stage, int64_t t, unsigned char *smem) {
+  using TL = Tile<DQK>;
+  using SM = RowSmem<DQK>;
+  constexpr int kNTq = DQK / 64;  // channel tiles per quarter (9 or 8)
+  uint16_t *qstage = reinterpret_cast<uint16_t *>(smem);  // prologue only
+  uint16_t *stg = reinterpret_cast<uint16_t *>(smem + SM::kCStage);
+  int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + SM::kCRows);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, hl = lane & 15;
-  const int r = (lane & 15) >> 2;
-  const int cq = lane & 3;
-  const int ch0 = wave * kChanPerWave;  // first latent channel owned by this wave
-  constexpr int kThreads = kRowWaves * 64;
+  const int r = (lane & 15) >> 2, cq = lane & 3;
+  const int lim = topk_length ? topk_length[t] : K;
+  const int32_t *irow = idx + t * K;
+  const int nchunks = (lim + kSlots - 1) / kSlots;
 
-  // ---- prologue: heads-as-contraction fragments of q and dO for this wave's channels
-  bf16x8 qh[kKH][kNTw], oh[kKH][kNTw];
-  for (int c = threadIdx.x; c < HP * (DQK / 8); c += kThreads) {
-    const int hh = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (hh < H) v = *reinterpret_cast<const u32x4 *>(q + (t * H + hh) * DQK + col);
-    *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kQStride + col]) = v;
+  // ---- prologue: the row's q, then dO, through LDS into head-contraction fragments of the
+  // contribution waves' channels; padded heads are zero
+  const int qq = wave - 4;
+  const int ch0 = qq * 16 * kNTq;
+  bf16x8 qh[2][kNTq], oh[2][kNTq];
+  // every global load of the prologue first (q, dO, the index list), then the LDS stores
+  constexpr int kQV = 64 * (DQK / 8) / 512, kOV = 64 * (kDv / 8) / 512, kIV = kMaxK / 512;
+  u32x4 qv[kQV], ov[kOV];
+  int32_t iv[kIV];
+#pragma unroll
+  for (int j = 0; j < kQV; ++j) {
+    const int e = threadIdx.x + j * 512, hh = e / (DQK / 8), col = (e % (DQK / 8)) * 8;
+    qv[j] = u32x4{0u, 0u, 0u, 0u};
+    if (hh < H) qv[j] = *reinterpret_cast<const u32x4 *>(q + (t * H + hh) * DQK + col);
   }
-  __syncthreads();
 #pragma unroll
-  for (int kh = 0; kh < kKH; ++kh)
-#pragma unroll
-    for (int n = 0; n < kNTw; ++n) {
-      const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kQStride + ch0 + n * 16 + cq * 4];
-      const u32x2 lo = lds_read_tr16(base);
-      const u32x2 hi = lds_read_tr16(base + 4 * SM::kQStride);
-      qh[kh][n] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-  __syncthreads();
-  for (int c = threadIdx.x; c < HP * (kDv / 8); c += kThreads) {
-    const int hh = c / (kDv / 8), col = (c % (kDv / 8)) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (hh < H) v = *reinterpret_cast<const u32x4 *>(dout + (t * H + hh) * kDv + col);
-    *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kOStride + col]) = v;
+  for (int j = 0; j < kOV; ++j) {
+    const int e = threadIdx.x + j * 512, hh = e / (kDv / 8), col = (e % (kDv / 8)) * 8;
+    ov[j] = u32x4{0u, 0u, 0u, 0u};
+    if (hh < H) ov[j] = *reinterpret_cast<const u32x4 *>(dout + (t * H + hh) * kDv + col);
   }
-  __syncthreads();
 #pragma unroll
-  for (int kh = 0; kh < kKH; ++kh)
+  for (int j = 0; j < kIV; ++j) {
+    const int e = threadIdx.x + j * 512;
+    iv[j] = e < lim ? irow[e] : -1;
+  }
 #pragma unroll
-    for (int n = 0; n < kNTw; ++n) {
-      const int ch = ch0 + n * 16;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ch < kDv) {
-        const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kOStride + ch + cq * 4];
+  for (int j = 0; j < kQV; ++j) {
+    const int e = threadIdx.x + j * 512, hh = e / (DQK / 8), col = (e % (DQK / 8)) * 8;
+    *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kQStride + col]) = qv[j];
+  }
+  __syncthreads();  // P0
+  if (wave >= 4) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int n = 0; n < kNTq; ++n) {
+        const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kQStride + ch0 + n * 16 + cq * 4];
         const u32x2 lo = lds_read_tr16(base);
-        const u32x2 hi = lds_read_tr16(base + 4 * SM::kOStride);
-        v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        const u32x2 hi = lds_read_tr16(base + 4 * SM::kQStride);
+        qh[kh][n] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
-      oh[kh][n] = as_bf16x8(v);
+  }
+  __syncthreads();  // P1
+#pragma unroll
+  for (int j = 0; j < kOV; ++j) {
+    const int e = threadIdx.x + j * 512, hh = e / (kDv / 8), col = (e % (kDv / 8)) * 8;
+    *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kOStride + col]) = ov[j];
+  }
+  // slot rows up to a whole number of tiles (the index list lies outside the staging area)
+#pragma unroll
+  for (int j = 0; j < kIV; ++j) {
+    const int e = threadIdx.x + j * 512;
+    if (e < nchunks * kSlots) slot_rows[e] = iv[j];
+  }
+  __syncthreads();  // P2
+  if (wave >= 4) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int n = 0; n < kNTq; ++n) {
+        const int ch = ch0 + n * 16;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ch < kDv) {
+          const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kOStride + ch + cq * 4];
+          const u32x2 lo = lds_read_tr16(base);
+          const u32x2 hi = lds_read_tr16(base + 4 * SM::kOStride);
+          v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        oh[kh][n] = as_bf16x8(v);
+      }
+  }
+  __syncthreads();  // P3: the q / dO staging is read (the tile area is free)
+
+  if (wave < 4) {
+    // ============================== SdP waves ==============================
+    const int G = wave;
+    const uint32_t tiles_lds = lds_addr(smem);
+    constexpr int kLoadsW = TL::kLoads / 4;
+    SdpHead<DQK> hd;
+    hd.load(q, dout, lse, delta, H, t, G * 16 + hl);
+    hd.settle_all();  // before the first tile load (see settle())
+    if (nchunks > 0) issue_tile<DQK, kCBufs>(tiles_lds, kv, slot_rows, 0, G);
+    if (nchunks > 1) issue_tile<DQK, kCBufs>(tiles_lds, kv, slot_rows + kSlots, 1, G);
+    if (nchunks > 0) {
+      if (nchunks > 1) wait_vm<kLoadsW>();
+      else wait_tile();
     }
-  // padded heads of the staging arrays stay zero for the whole kernel
-  for (int c = threadIdx.x; c < 4 * kSlots * kSS; c += kThreads) zst[c] = 0;
-
-  // ---- this wave's head tile for the S^T / dP^T recompute (waves beyond the tiles idle)
-  const int h = wave * 16 + hl;
-  const bool tile_active = wave * 16 < H;
-  const bool hok = h < H;
-  bf16x8 qf[DQK / 32], df[kDv / 32];
-  load_head_frags<DQK>(q, dout, H, t, h, qf, df);
-  __syncthreads();  // the q / dO staging is read; the tile area may be refilled
-  const RowHead rh = row_setup<DQK>(idx, topk_length, lse, delta, H, K, t, h, slot_rows);
-#pragma unroll
-  for (int ks = 0; ks < DQK / 32; ++ks) settle(qf[ks]);
-#pragma unroll
-  for (int ks = 0; ks < kDv / 32; ++ks) settle(df[ks]);
-  __syncthreads();
-
-  RowStream<DQK> ts;
-  ts.init(smem_raw, wave);
-  TileFrag<DQK> fr;
-  fr.init();
-#pragma unroll
-  for (int c = 0; c < kRowBufs - 1; ++c)
-    if (c < rh.nchunks) ts.issue(c, kv, slot_rows);
-
-  for (int c = 0; c < rh.nchunks; ++c) {
-    RowStream<DQK>::acquire(c, rh.nchunks);  // also: every wave is done with the staging
-    if (c + kRowBufs - 1 < rh.nchunks) ts.issue(c + kRowBufs - 1, kv, slot_rows);
-    const unsigned char *tile = smem_raw + (c % kRowBufs) * Tile<DQK>::kBytes;
-    if (tile_active) {
+    __syncthreads();  // S1: tile 0 loaded
+    TileFrag<DQK> fr;
+    fr.init();
+    const int h = G * 16 + hl;
+    for (int c = 0; c <= nchunks; ++c) {
+      lds_barrier();  // B(c - 1): tile c complete; contribution waves are done with chunk c - 2
+      if (c == nchunks) break;
+      if (c + 2 < nchunks) issue_tile<DQK, kCBufs>(tiles_lds, kv, slot_rows + (c + 2) * kSlots, c + 2, G);  // tile c - 1's buffer
       float p[2][4], dz[2][4];
-      slot_grads<DQK>(tile, fr, slot_rows + c * kSlots, qf, df, rh.lse2, rh.dlt, scale_log2,
-                      p, dz);
-      if (hok) {
+      hd.grads(smem + (c % kCBufs) * TL::kBytes, fr, slot_rows + c * kSlots, scale_log2, p, dz);
+      uint16_t *zs = stg + (c & 1) * (SM::kCStageBytes / 2);
+      uint16_t *zl = zs + kSlots * kSS;
+      uint16_t *ps = zl + kSlots * kSS;
+      uint16_t *pl = ps + kSlots * kSS;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int o = (mt * 16 + g * 4 + i) * kSS + h;
+          const float z = dz[mt][i] * scale;
+          const uint16_t zh = f32_to_bf16(z), ph = f32_to_bf16(p[mt][i]);
+          zs[o] = zh;
+          zl[o] = f32_to_bf16(z - bf16_to_f32(zh));
+          ps[o] = ph;
+          pl[o] = f32_to_bf16(p[mt][i] - bf16_to_f32(ph));
+        }
+      if (c + 2 < nchunks) wait_vm<kLoadsW>();  // tile c + 1 before the next barrier
+      else wait_tile();
+    }
+    lds_barrier();  // Z
+  } else {
+    // ========================== contribution waves =========================
+    __syncthreads();  // S1
+    for (int c = 0; c <= nchunks; ++c) {
+      lds_barrier();  // B(c - 1): P / dZ of chunk c - 1 are staged
+      if (c > 0) {
+        const int cc = c - 1;
+        const uint16_t *zs = stg + (cc & 1) * (SM::kCStageBytes / 2);
+        const uint16_t *zl = zs + kSlots * kSS;
+        const uint16_t *ps = zl + kSlots * kSS;
+        const uint16_t *pl = ps + kSlots * kSS;
+        const int32_t *rr = slot_rows + cc * kSlots;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          f32x4 acc[kNTq];
+#pragma unroll
+          for (int n = 0; n < kNTq; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const int off = (mt * 16 + hl) * kSS + kh * 32 + g * 8;
+            const bf16x8 za = as_bf16x8(*reinterpret_cast<const u32x4 *>(&zs[off]));
+            const bf16x8 zb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&zl[off]));
+            const bf16x8 pa = as_bf16x8(*reinterpret_cast<const u32x4 *>(&ps[off]));
+            const bf16x8 pb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&pl[off]));
+            // four passes over the channel tiles: consecutive MFMAs are independent
+#pragma unroll
+            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(za, qh[kh][n], acc[n]);
+#pragma unroll
+            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(zb, qh[kh][n], acc[n]);
+#pragma unroll
+            for (int n = 0; n < kNTq; ++n)
+              if (ch0 + n * 16 < kDv) acc[n] = mfma16(pa, oh[kh][n], acc[n]);
+#pragma unroll
+            for (int n = 0; n < kNTq; ++n)
+              if (ch0 + n * 16 < kDv) acc[n] = mfma16(pb, oh[kh][n], acc[n]);
+          }
+          // acc[n][i] -> stage[slot cc*32 + 16mt + 4g + i][ch0 + 16n + hl] (valid slots only)
+          const u32x4 rv = *reinterpret_cast<const u32x4 *>(rr + mt * 16 + g * 4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int o = (mt * 16 + g * 4 + i) * kSS + h;
-            const float zv = dz[mt][i] * scale;
-            const uint16_t zh = f32_to_bf16(zv), ph = f32_to_bf16(p[mt][i]);
-            zst[o] = zh;
-            zsl[o] = f32_to_bf16(zv - bf16_to_f32(zh));
-            pst[o] = ph;
-            psl[o] = f32_to_bf16(p[mt][i] - bf16_to_f32(ph));
-          }
-      }
-    }
-    lds_barrier();
-    // contributions[slot][channel] for this wave's channels
+            if (static_cast<int32_t>(rv[i]) >= 0) {
+              float *dst = stage + static_cast<int64_t>(cc * kSlots + mt * 16 + g * 4 + i) * DQK + ch0 + hl;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4 acc[kNTw];
-#pragma unroll
-      for (int n = 0; n < kNTw; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kh = 0; kh < kKH; ++kh) {
-        const int off = (mt * 16 + hl) * kSS + kh * 32 + g * 8;
-        const bf16x8 za = as_bf16x8(*reinterpret_cast<const u32x4 *>(&zst[off]));
-        const bf16x8 zl = as_bf16x8(*reinterpret_cast<const u32x4 *>(&zsl[off]));
-        const bf16x8 pa = as_bf16x8(*reinterpret_cast<const u32x4 *>(&pst[off]));
-        const bf16x8 pl = as_bf16x8(*reinterpret_cast<const u32x4 *>(&psl[off]));
-#pragma unroll
-        for (int n = 0; n < kNTw; ++n) {
-          acc[n] = mfma16(za, qh[kh][n], acc[n]);
-          acc[n] = mfma16(zl, qh[kh][n], acc[n]);
-          if (ch0 + n * 16 < kDv) {
-            acc[n] = mfma16(pa, oh[kh][n], acc[n]);
-            acc[n] = mfma16(pl, oh[kh][n], acc[n]);
+              for (int n = 0; n < kNTq; ++n) dst[n * 16] = acc[n][i];
+            }
           }
         }
       }
-      // acc[n][i] -> stage[slot c*32 + 16mt + 4g + i][ch0 + 16n + hl] (valid slots only)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sl = mt * 16 + g * 4 + i;
-        if (slot_rows[c * kSlots + sl] >= 0) {
-          float *dst = stage + static_cast<int64_t>(c * kSlots + sl) * DQK + ch0 + hl;
-#pragma unroll
-          for (int n = 0; n < kNTw; ++n) dst[n * 16] = acc[n][i];
-        }
-      }
+      if (c == nchunks) break;
     }
+    lds_barrier();  // Z
   }
 }
 
@@ -406,13 +543,7 @@ __global__ void check_indices_kernel(const int32_t *__restrict__ idx,
 }
 
 // ---------------------------------------------------------------------------------------
-// rows launch: work group 2i computes dq of query row row0 + i, 2i + 1 its contributions
-template <int DQK, int HP>
-constexpr size_t rows_smem_bytes() {
-  return RowSmem<DQK, HP>::kBytes;
-}
-
-template <int DQK, int HP>
+template <int DQK>
 __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
@@ -423,11 +554,11 @@ __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
   const int64_t i = blockIdx.x >> 1;
   const int64_t t = row0 + i;
   if (blockIdx.x & 1)
-    bwd_contrib_row<DQK, HP>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2,
-                             stage + i * K * DQK, t, smem);
+    bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2,
+                         stage + i * K * DQK, t, smem);
   else
-    bwd_dq_row<DQK, HP>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2, dq,
-                        t, smem);
+    bwd_dq_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2, dq, t,
+                    smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -543,13 +674,13 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const int32_t *__restr
   }
 }
 
-template <int DQK, int HP>
+template <int DQK>
 hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                        const int32_t *topk_length, const float *lse, const float *delta,
                        const uint16_t *dout, int64_t row0, int64_t rows, int32_t H, int32_t K,
                        float scale, uint16_t *dq, float *stage, hipStream_t s) {
-  constexpr size_t smem = rows_smem_bytes<DQK, HP>();
-  auto kern = bwd_rows_kernel<DQK, HP>;
+  const size_t smem = RowSmem<DQK>::bytes(K);
+  auto kern = bwd_rows_kernel<DQK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
@@ -566,10 +697,8 @@ hipError_t launch_pass(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                        const uint16_t *dout, int64_t row0, int64_t rows, int64_t T_kv,
                        int32_t H, int32_t K, float scale, uint16_t *dq, float *dkv,
                        const BwdWorkspace &ws, hipStream_t s) {
-  hipError_t e = H <= 32 ? launch_rows<DQK, 32>(q, kv, idx, topk_length, lse, delta, dout, row0,
-                                                rows, H, K, scale, dq, ws.stage, s)
-                         : launch_rows<DQK, 64>(q, kv, idx, topk_length, lse, delta, dout, row0,
-                                                rows, H, K, scale, dq, ws.stage, s);
+  hipError_t e = launch_rows<DQK>(q, kv, idx, topk_length, lse, delta, dout, row0, rows, H, K,
+                                  scale, dq, ws.stage, s);
   if (e != hipSuccess) return e;
   const int64_t pairs = rows * K;
   const unsigned pb = static_cast<unsigned>((pairs + 255) / 256);

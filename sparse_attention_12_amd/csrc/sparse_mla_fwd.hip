@@ -88,16 +88,17 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
   // [1024 k, 1024 k + 1024) of the tile, lane i the 16 bytes at 1024 k + 16 i
   auto issue = [&](int c) {
     const uint32_t dst = tiles_lds + (c % kNBuf) * TL::kBytes;
+    uint32_t off[TL::kLoads / NW];  // row indices first (see the other kernel)
 #pragma unroll
     for (int i = 0; i < TL::kLoads / NW; ++i) {
-      const int k = i * NW + wave;
-      const int pos = k * 64 + lane;
+      const int pos = (i * NW + wave) * 64 + lane;
       const int row = pos / TL::kChunks;
       const int chunk = (pos % TL::kChunks) ^ TL::swz(row);
-      int r = slot_rows[c * kSlots + row];
-      r = r < 0 ? 0 : r;  // invalid slots load row 0 (masked below)
-      dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + chunk * 16, dst + k * 1024);
+      const int r = slot_rows[c * kSlots + row];
+      off[i] = static_cast<uint32_t>(r < 0 ? 0 : r) * TL::kRowBytes + chunk * 16;  // -1: row 0
     }
+#pragma unroll
+    for (int i = 0; i < TL::kLoads / NW; ++i) dma16_sv(kv, off[i], dst + (i * NW + wave) * 1024);
   };
   if (nchunks > 0) issue(0);
 
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
         x[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? acc[hg][1][i] * scale_log2 : -INFINITY;
         cmax = fmaxf(cmax, fmaxf(x[0][i], x[1][i]));
       }
-      cmax = fmaxf(cmax, xor_lane(cmax, 16));
+      cmax = fmaxf(cmax, xor16(cmax));
       cmax = fmaxf(cmax, swap_halves(cmax));
       if (__ballot(cmax > m_run[hg] + 8.0f)) {
         const float m_new = cmax > m_run[hg] + 8.0f ? cmax : m_run[hg];
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
   // ---- finalize: denominator over the four lane groups, normalise, write
 #pragma unroll
   for (int hg = 0; hg < HG; ++hg) {
-    float l_tot = l_run[hg] + xor_lane(l_run[hg], 16);
+    float l_tot = l_run[hg] + xor16(l_run[hg]);
     l_tot += swap_halves(l_tot);
     const int h = (wave * HG + hg) * 16 + hl;
     if (h < H) {
@@ -209,16 +210,19 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
 // one wave of each kind and their work overlaps:
 //   S waves 0..3 (head group G = wave): S^T = rows . q^T for 16 heads over all dims (four
 //     independent MFMA chains), the online softmax, and P (bf16, already in the PV B-operand
-//     layout) plus any rescale factor to LDS.
+//     layout) plus any rescale factor to LDS.  Wave 0 also fetches the slot indices of the
+//     tile four chunks ahead into a small ring.
 //   PV waves 4..7 (quarter qq): O^T[channels 128 qq .. + 127 x 64 heads] += V^T . P^T one chunk
 //     behind the S waves; every V fragment read from LDS (transposing reads, the slow kind)
-//     feeds four MFMAs, one per head group.  They also fetch the slot indices three chunks
-//     ahead into a small ring.
+//     feeds four MFMAs, one per head group.  They also issue the latent-row tile loads, two
+//     chunks ahead, which keeps the slow issue of the gathers off the S waves' path.
 // One barrier per chunk: in interval c the S waves work on chunk c while the PV waves finish
 // chunk c - 1, so P, the rescale factors and the flags are double buffered, and a latent-row
-// tile stays in use for two intervals; four tile buffers keep two tiles in flight.
+// tile stays in use for two intervals; four tile buffers keep two tiles in flight.  Only the
+// PV waves issue the (compiler-invisible) tile loads and only the S waves issue ordinary
+// global loads, so each wave's explicit load-count waits stay exact.
 constexpr int kRoleNBuf = 4;
-constexpr int kRing = 4;  // slot-index ring (tiles)
+constexpr int kRing = 8;  // slot-index ring (tiles)
 
 template <int DQK>
 struct RoleSmem {
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
   using TL = Tile<DQK>;
   using SM = RoleSmem<DQK>;
   constexpr int kKSteps = DQK / 32;
-  constexpr int kLoadsS = TL::kLoads / 4;  // tile loads per S wave
+  constexpr int kLoadsW = TL::kLoads / 4;  // tile loads per PV wave
   extern __shared__ __align__(16) unsigned char smem[];
   bf16x8 *pbuf = reinterpret_cast<bf16x8 *>(smem + SM::kP);
   float *abuf = reinterpret_cast<float *>(smem + SM::kA);
@@ -255,22 +259,26 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
   const int lim = topk_length ? topk_length[t] : K;
   const int32_t *irow = idx + t * K;
   const int nchunks = (lim + kSlots - 1) / kSlots;
-  const uint32_t tiles_lds = lds_addr(smem);
-
-  // slot indices of tile j into the ring (one wave, lanes 0..31; -1 beyond the valid prefix)
-  auto fetch_indices = [&](int j) {
-    if (lane < kSlots) {
-      const int slot = j * kSlots + lane;
-      ring[(j % kRing) * kSlots + lane] = slot < lim ? irow[slot] : -1;
-    }
-  };
-  if (wave == 4)
-    for (int j = 0; j < kRoleNBuf - 1 && j < nchunks; ++j) fetch_indices(j);
 
   if (wave < 4) {
     // ================================ S waves ================================
     const int G = wave;
     const int h = G * 16 + hl;
+    // slot indices of tile j (lanes 0..31; -1 beyond the valid prefix)
+    auto load_indices = [&](int j) -> int32_t {
+      const int slot = j * kSlots + lane;
+      return lane < kSlots && slot < lim ? irow[slot] : -1;
+    };
+    auto put_indices = [&](int j, int32_t v) {
+      if (lane < kSlots) ring[(j % kRing) * kSlots + lane] = v;
+    };
+    // wave 0 keeps one tile's indices in flight: loaded an interval before they are written
+    // to the ring (four chunks ahead of their S work), so the load latency is never waited for
+    int32_t pending = -1;
+    if (wave == 0) {
+      for (int j = 0; j < 4 && j < nchunks; ++j) put_indices(j, load_indices(j));
+      if (4 < nchunks) pending = load_indices(4);
+    }
     bf16x8 qf[kKSteps];  // head h, dims ks * 32 + g * 8 + [0, 8)
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
@@ -278,47 +286,38 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
       if (h < H) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
       qf[ks] = as_bf16x8(v);
     }
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) settle(qf[ks]);
-    __syncthreads();  // indices of the first tiles are in the ring
+    __syncthreads();  // S0: indices of the first tiles are in the ring
+    __syncthreads();  // S1: PV waves have issued the first tiles and waited for tile 0
 
     TileFrag<DQK> fr;
     fr.init();
-    auto issue = [&](int c) {  // this wave's loads k = 4 i + wave of tile c
-      const uint32_t dst = tiles_lds + (c % kRoleNBuf) * TL::kBytes;
-      const int32_t *rr = ring + (c % kRing) * kSlots;
-#pragma unroll
-      for (int i = 0; i < kLoadsS; ++i) {
-        const int k = 4 * i + wave;
-        const int pos = k * 64 + lane;
-        const int row = pos / TL::kChunks;
-        const int chunk = (pos % TL::kChunks) ^ TL::swz(row);
-        int r = rr[row];
-        r = r < 0 ? 0 : r;  // invalid slots load row 0 (masked below)
-        dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + chunk * 16, dst + k * 1024);
-      }
-    };
-    if (nchunks > 0) issue(0);
-    if (nchunks > 1) issue(1);
-    if (nchunks > 0) {  // tile 0 before the first barrier (tile 1 may stay in flight)
-      if (nchunks > 1) wait_vm<kLoadsS>();
-      else wait_tile();
-    }
-
     float m_run = -1e30f;  // reference max (base-2 logits) of head h
     float l_run = 0.0f;    // this lane's partial softmax denominator
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): tile c complete; PV waves are done with chunk c - 2
       if (c == nchunks) break;
-      if (c + 2 < nchunks) issue(c + 2);  // into the buffer of tile c - 2
+      if (wave == 0 && c + 5 <= nchunks) {  // ring slot of tile c - 4 is free
+        if (c + 4 < nchunks) put_indices(c + 4, pending);
+        if (c + 5 < nchunks) pending = load_indices(c + 5);
+      }
       const unsigned char *tile = smem + (c % kRoleNBuf) * TL::kBytes;
-      // ---- S^T = rows . q^T  (four chains: slot half mt, k-step parity)
+      // ---- S^T = rows . q^T  (four chains: slot half mt, k-step parity); fragment reads run
+      // two k-steps ahead of the MFMAs
       f32x4 acc[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
                          {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
+      bf16x8 a0[3], a1[3];
+      a0[0] = fr.a_frag(tile, 0, 0);
+      a1[0] = fr.a_frag(tile, 1, 0);
+      a0[1] = fr.a_frag(tile, 0, 1);
+      a1[1] = fr.a_frag(tile, 1, 1);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        acc[0][ks & 1] = mfma16(fr.a_frag(tile, 0, ks), qf[ks], acc[0][ks & 1]);
-        acc[1][ks & 1] = mfma16(fr.a_frag(tile, 1, ks), qf[ks], acc[1][ks & 1]);
+        if (ks + 2 < kKSteps) {
+          a0[(ks + 2) % 3] = fr.a_frag(tile, 0, ks + 2);
+          a1[(ks + 2) % 3] = fr.a_frag(tile, 1, ks + 2);
+        }
+        acc[0][ks & 1] = mfma16(a0[ks % 3], qf[ks], acc[0][ks & 1]);
+        acc[1][ks & 1] = mfma16(a1[ks % 3], qf[ks], acc[1][ks & 1]);
       }
       const f32x4 sv0 = acc[0][0] + acc[0][1], sv1 = acc[1][0] + acc[1][1];
       // ---- online softmax (base 2) with a lazily raised reference max: the reference only
@@ -335,7 +334,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
         x[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? sv1[i] * scale_log2 : -INFINITY;
         cmax = fmaxf(cmax, fmaxf(x[0][i], x[1][i]));
       }
-      cmax = fmaxf(cmax, xor_lane(cmax, 16));
+      cmax = fmaxf(cmax, xor16(cmax));
       cmax = fmaxf(cmax, swap_halves(cmax));
       int rescale = 0;
       if (__ballot(cmax > m_run + 8.0f)) {
@@ -356,12 +355,9 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
         }
       pbuf[((c & 1) * 4 + G) * 64 + lane] = pack_slots(p);
       if (lane == 0) fbuf[(c & 1) * 4 + G] = rescale;
-      // tile c + 1 before the next barrier (tile c + 2 may stay in flight)
-      if (c + 2 < nchunks) wait_vm<kLoadsS>();
-      else wait_tile();
     }
     // ---- finalize: denominator over the four lane groups; 1/l for the PV waves
-    float l_tot = l_run + xor_lane(l_run, 16);
+    float l_tot = l_run + xor16(l_run);
     l_tot += swap_halves(l_tot);
     if (h < H && g == 0)
       lse[t * H + h] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
@@ -370,7 +366,33 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
   } else {
     // ================================ PV waves ===============================
     const int qq = wave - 4;
-    __syncthreads();  // indices of the first tiles are in the ring
+    const uint32_t tiles_lds = lds_addr(smem);
+    __syncthreads();  // S0: indices of the first tiles are in the ring
+    auto issue = [&](int c) {  // this wave's loads k = 4 i + qq of tile c
+      const uint32_t dst = tiles_lds + (c % kRoleNBuf) * TL::kBytes;
+      const int32_t *rr = ring + (c % kRing) * kSlots;
+      // all row indices first: the loads are asm with a memory clobber, so an index read
+      // placed between two of them would be waited for on its own
+      uint32_t off[kLoadsW];
+#pragma unroll
+      for (int i = 0; i < kLoadsW; ++i) {
+        const int pos = (4 * i + qq) * 64 + lane;
+        const int row = pos / TL::kChunks;
+        const int chunk = (pos % TL::kChunks) ^ TL::swz(row);
+        const int r = rr[row];
+        off[i] = static_cast<uint32_t>(r < 0 ? 0 : r) * TL::kRowBytes + chunk * 16;  // -1: row 0
+      }
+#pragma unroll
+      for (int i = 0; i < kLoadsW; ++i) dma16_sv(kv, off[i], dst + (4 * i + qq) * 1024);
+    };
+    if (nchunks > 0) issue(0);
+    if (nchunks > 1) issue(1);
+    if (nchunks > 0) {  // tile 0 before S1 (tile 1 may stay in flight)
+      if (nchunks > 1) wait_vm<kLoadsW>();
+      else wait_tile();
+    }
+    __syncthreads();  // S1
+
     TileFrag<DQK> fr;
     fr.init();
     f32x4 o[4][8];  // o[G][n][i] = O[head 16 G + hl][channel 128 qq + 16 n + 4 g + i]
@@ -380,8 +402,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
       for (int n = 0; n < 8; ++n) o[G][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): P and rescale factors of chunk c - 1 are ready
-      // indices of tile c + 3 into the slot of tile c - 1 (its S work ended at B(c - 1))
-      if (wave == 4 && c + kRoleNBuf - 1 < nchunks) fetch_indices(c + kRoleNBuf - 1);
+      if (c + 2 < nchunks) issue(c + 2);  // into the buffer of tile c - 2 (PV done at B(c - 1))
       if (c > 0) {
         const int b = (c - 1) & 1;
         const unsigned char *tile = smem + ((c - 1) % kRoleNBuf) * TL::kBytes;
@@ -404,6 +425,9 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
         }
       }
       if (c == nchunks) break;
+      // tile c + 1 before the next barrier (tile c + 2 may stay in flight)
+      if (c + 2 < nchunks) wait_vm<kLoadsW>();
+      else wait_tile();
     }
     lds_barrier();  // Z: 1/l ready
 #pragma unroll

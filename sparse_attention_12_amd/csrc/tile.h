@@ -169,12 +169,16 @@ struct TileStream {
   }
   __device__ __forceinline__ void issue(int c, const uint16_t *kv, const int32_t *slot_rows) const {
     const uint32_t dst = tiles_lds + (c % NBUF) * TL::kBytes;
+    // every row index first: the loads are asm with a memory clobber, so an index read placed
+    // between two of them would be waited for on its own
+    uint32_t off[L];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      int r = slot_rows[c * TL::kSlots + dma_row[i]];
-      r = r < 0 ? 0 : r;
-      dma16_sv(kv, static_cast<uint32_t>(r) * TL::kRowBytes + dma_off[i], dst + i * NW * 1024);
+      const int r = slot_rows[c * TL::kSlots + dma_row[i]];
+      off[i] = static_cast<uint32_t>(r < 0 ? 0 : r) * TL::kRowBytes + dma_off[i];  // -1: row 0
     }
+#pragma unroll
+    for (int i = 0; i < L; ++i) dma16_sv(kv, off[i], dst + i * NW * 1024);
   }
   // Before processing tile c of nchunks: wait for it and publish it to the work group.  The
   // barrier also means every wave is done with tile c - 1, whose buffer the caller may refill.
@@ -217,6 +221,29 @@ struct TileFrag {
   __device__ __forceinline__ bf16x8 v_frag(const unsigned char *tile, int n) const {
     const u32x2 lo = lds_read_tr16(tile + vbase[0][n & 7] + (n >> 3) * 256);
     const u32x2 hi = lds_read_tr16(tile + vbase[1][n & 7] + (n >> 3) * 256);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
+};
+
+// The transposing column reads of TileFrag::v_frag for NT consecutive 16-column tiles starting
+// at tile n0 (n0 may differ between the waves of a work group: the offsets are computed, not
+// indexed, so they stay in registers).
+template <int DQK, int NT>
+struct ColFrags {
+  using TL = Tile<DQK>;
+  int off[2][NT];
+  __device__ __forceinline__ void init(int n0) {
+    const int lane = __lane_id();
+    const int g = lane >> 4, r4 = (lane & 15) >> 2, cq = lane & 3;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      off[0][n] = TL::elem_off(g * 4 + r4, (n0 + n) * 16 + cq * 4);
+      off[1][n] = TL::elem_off(16 + g * 4 + r4, (n0 + n) * 16 + cq * 4);
+    }
+  }
+  __device__ __forceinline__ bf16x8 frag(const unsigned char *tile, int n) const {
+    const u32x2 lo = lds_read_tr16(tile + off[0][n]);
+    const u32x2 hi = lds_read_tr16(tile + off[1][n]);
     return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
   }
 };

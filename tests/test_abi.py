@@ -98,14 +98,15 @@ def test_argument_errors_without_device(dsa):
     assert fwd(sc=float("nan")) == pkg.DSA_ERR_INVALID_VALUE
     assert fwd(q=24) == pkg.DSA_ERR_INVALID_VALUE and "aligned" in _err(dsa)
     assert fwd(out=None) == pkg.DSA_ERR_INVALID_VALUE
-    # backward: unknown flag, missing workspace, too many heads
-    def bwd(flags=0, ws=16, ws_bytes=1 << 30, H=64):
-        return dsa.dsa_sparse_mla_bwd(16, 16, 16, None, 16, 16, 16, 4, 4, H, 576, 512, 8, 0.1,
+    # backward: unknown flag, missing workspace, too many heads, K
+    def bwd(flags=0, ws=16, ws_bytes=1 << 30, H=64, K=8):
+        return dsa.dsa_sparse_mla_bwd(16, 16, 16, None, 16, 16, 16, 4, 4, H, 576, 512, K, 0.1,
                                       16, 16, flags, ws, ws_bytes, None)
     assert bwd(flags=0x8) == pkg.DSA_ERR_INVALID_VALUE
     assert bwd(ws=None) == pkg.DSA_ERR_WORKSPACE
     assert bwd(ws_bytes=4) == pkg.DSA_ERR_WORKSPACE
     assert bwd(H=65) == pkg.DSA_ERR_INVALID_VALUE
+    assert bwd(K=4097) == pkg.DSA_ERR_INVALID_VALUE and "4096" in _err(dsa)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
