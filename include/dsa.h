@@ -170,13 +170,14 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
  * without it dkv is overwritten.  Same shape limits as dsa_sparse_mla_fwd.
  *
  * Workspace (caller-owned device memory, contents need not be initialised):
- * the key gradient is formed by staging one fp32 contribution row of D_qk
- * values per (query, valid slot) and summing each latent row's contributions
- * after a counting sort, so no atomics touch dkv.  The query rows are
+ * the key gradient is formed by staging one contribution row of D_qk values
+ * per (query, valid slot), each value kept as the upper 24 bits of its fp32
+ * form (relative error <= 2^-16), and summing each latent row's contributions
+ * in fp32 after a counting sort, so no atomics touch dkv.  The query rows are
  * processed in passes of R rows, R being as large as ws_bytes allows:
  * dsa_sparse_mla_bwd_workspace_size(..., rows_per_pass) gives the bytes for
  * passes of rows_per_pass rows (<= 0: all T_q rows in one pass, the fastest;
- * about T_q * K * D_qk * 4 bytes).  Any ws_bytes of at least the size for
+ * about T_q * K * (D_qk * 3 + 4) bytes).  Any ws_bytes of at least the size for
  * rows_per_pass = 1 works; less returns DSA_ERR_WORKSPACE.
  * ------------------------------------------------------------------------ */
 size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk,

@@ -276,7 +276,8 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
 }
 
 // Backward workspace layout: delta [T_q, H] fp32 | debug flag | off [T_kv + 1] | cursor [T_kv]
-// | list [R * K] int32 | stage [R * K, D_qk] fp32, each segment 256-byte aligned.
+// | list [R * K] int32 | stage [R * K, D_qk] 24-bit values (3 bytes each), each segment
+// 256-byte aligned.
 static size_t bwd_fixed_bytes(int64_t T_q, int64_t T_kv, int32_t H) {
   return align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float)) + 256 +
          align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t)) +
@@ -285,7 +286,7 @@ static size_t bwd_fixed_bytes(int64_t T_q, int64_t T_kv, int32_t H) {
 
 static size_t bwd_pass_bytes(int64_t rows, int32_t D_qk, int32_t K) {
   const size_t pairs = static_cast<size_t>(rows) * static_cast<size_t>(K);
-  return align_up(pairs * sizeof(int32_t)) + align_up(pairs * D_qk * sizeof(float));
+  return align_up(pairs * sizeof(int32_t)) + align_up(pairs * D_qk * 3);
 }
 
 size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk,
@@ -340,7 +341,7 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   p += align_up(static_cast<size_t>(T_kv) * sizeof(int32_t));
   w.list = reinterpret_cast<int32_t *>(p);
   p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) * sizeof(int32_t));
-  w.stage = reinterpret_cast<float *>(p);
+  w.stage = reinterpret_cast<uint32_t *>(p);
   w.rows_per_pass = R;
   if ((flags & DSA_DEBUG_CHECK_INDICES) && T_q > 0)
     if (int rc = debug_check_indices(idx, topk_length, T_q, K, T_kv, w.flag, s)) return rc;

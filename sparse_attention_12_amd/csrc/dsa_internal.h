@@ -45,7 +45,7 @@ struct BwdWorkspace {
   int32_t *off;           // [T_kv + 1] per latent row: contribution count, then list offset
   int32_t *cursor;        // [T_kv]
   int32_t *list;          // [rows_per_pass * K] pair ids grouped by latent row
-  float *stage;           // [rows_per_pass * K, D_qk] staged contributions
+  uint32_t *stage;        // [rows_per_pass * K, D_qk * 3 / 4] staged contributions (24-bit)
   int64_t rows_per_pass;  // query rows per pass (>= 1)
 };
 

@@ -9,11 +9,11 @@
 // Kernels, for query rows processed in passes of R rows (R as large as the caller's workspace
 // allows):
 //   delta  : Delta[t,h] = sum_c dO[t,h,c] O[t,h,c]          (streaming, one wave per (t,h))
-//   rows   : one launch whose even work groups compute dq and odd work groups the key-gradient
-//            contributions of the same query rows (layout of the waves below).  Both recompute
-//            S^T and dP^T per 32-slot chunk of gathered latent rows; dq work groups then form
-//            dq = scale dZ . rows, contribution work groups C = scale dZ^T . q + P^T . dO
-//            for every (query, slot) pair and store C in fp32 to a staging buffer.
+//   rows   : one work group per query row, in two phases (layout of the waves below).  Both
+//            recompute S^T and dP^T per 32-slot chunk of gathered latent rows; the dq phase
+//            then forms dq = scale dZ . rows, the contribution phase C = scale dZ^T . q +
+//            P^T . dO for every (query, slot) pair and stores C to a staging buffer (3 bytes
+//            per channel: the upper 24 bits of the fp32 value).
 //   count / scan / fill : a counting sort of the pass's (query, slot) pairs by latent row.
 //   reduce : one work group per latent row adds up its staged contributions and adds the sum
 //            to dkv (every row has a single owner, so no atomics touch dkv).
@@ -30,6 +30,25 @@ namespace {
 
 constexpr int kSlots = 32;
 constexpr int kDv = 512;
+
+// Staged contributions are kept as the upper 24 bits of their fp32 value (sign, the full 8-bit
+// exponent, 15 stored mantissa bits; rounded to nearest even): 3 bytes per channel, relative
+// error at most 2^-16, and no range limit beyond fp32's.  Four channels pack into three words.
+__device__ __forceinline__ uint32_t f32_to_f24(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ void pack_f24x4(const f32x4 &v, uint32_t w[3]) {
+  const uint32_t a = f32_to_f24(v[0]), b = f32_to_f24(v[1]), c = f32_to_f24(v[2]),
+                 d = f32_to_f24(v[3]);
+  w[0] = a | (b << 24);
+  w[1] = (b >> 8) | (c << 16);
+  w[2] = (c >> 16) | (d << 8);
+}
+__device__ __forceinline__ f32x4 unpack_f24x4(uint32_t w0, uint32_t w1, uint32_t w2) {
+  return f32x4{__uint_as_float(w0 << 8), __uint_as_float(((w0 >> 24) | (w1 << 8)) << 8),
+               __uint_as_float(((w1 >> 16) | (w2 << 16)) << 8), __uint_as_float(w2 & 0xFFFFFF00u)};
+}
 
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restrict__ out,
@@ -58,41 +77,45 @@ __global__ void fill_zero_kernel(float *__restrict__ p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------------------
-// rows launch: work group 2i handles dq of query row row0 + i, 2i + 1 its key-gradient
-// contributions.  Both kinds have 8 waves split by role, so that every SIMD runs one wave of
-// each kind and their work overlaps, and one barrier per 32-slot chunk:
+// rows launch: one work group per query row of the pass computes the row's dq, then its
+// key-gradient contributions (the second phase re-gathers the latent rows, mostly from L2).
+// Keeping both phases in one work group gives every CU the same mix of work: with separate
+// dq and contribution work groups the hardware's round-robin placement put each kind on its
+// own half of the CUs, and the contribution half (about twice the work) set the time.  Both
+// phases have 8 waves split by role, so that every SIMD runs one wave of each role and their
+// work overlaps, and one barrier per 32-slot chunk:
 //   SdP waves 0..3 (head group G = wave, 16 heads): S^T = rows . q^T and dP^T = V . dO^T
 //     (16x16x32 MFMAs, A = LDS row fragments, B = q / dO blocks in registers), then
 //     P = exp(S - lse) and dZ = P (dP - Delta).
-//   dq work group, waves 4..7 (channel quarter qq): dq^T[channels x 64 heads] += rows^T . dZ^T
+//   dq phase, waves 4..7 (channel quarter qq): dq^T[channels x 64 heads] += rows^T . dZ^T
 //     one chunk behind the SdP waves, dZ (bf16) of all head groups read from LDS; every
 //     transposed row fragment feeds four MFMAs.  They also issue the latent-row tile loads.
-//   contribution work group, waves 4..7 (channel quarter qq): C[32 slots x channels] =
+//   contribution phase, waves 4..7 (channel quarter qq): C[32 slots x channels] =
 //     scale dZ^T . q + P^T . dO one chunk behind, with q / dO held as head-contraction
 //     fragments and scale dZ / P staged in LDS as bf16 ([slot][head]), each as a pair hi + lo
 //     (hi = bf16(x), lo = bf16(x - hi), about 16 significant bits): with either rounded to 8
 //     bits a latent row picked by many queries collects an error near the 2e-2 bar.  C is
-//     stored in fp32.
+//     stored with 24 bits per channel (see f32_to_f24).
 // Tile loads (direct to LDS, waited for with explicit load counts) come from waves that issue no
 // other vector-memory operation, so that those counts stay exact and the compiler's own waits
-// never wait for tiles.  The dq work group fetches slot indices into a small ring from SdP wave
-// 0 (ordinary loads, four tiles ahead); the contribution work group, whose channel waves store
-// and whose SdP waves load tiles, reads the row's whole index list into LDS first.
+// never wait for tiles.  The dq phase fetches slot indices into a small ring from SdP wave 0
+// (ordinary loads, four tiles ahead); the contribution phase, whose channel waves store and
+// whose SdP waves load tiles, reads the row's whole index list into LDS first.
 constexpr int kRowWaves = 8;
-constexpr int kDqBufs = 4;  // dq work group: a tile is read in two intervals
-constexpr int kCBufs = 3;   // contribution work group: a tile is read in one interval
+constexpr int kDqBufs = 4;  // dq phase: a tile is read in two intervals
+constexpr int kCBufs = 3;   // contribution phase: a tile is read in one interval
 constexpr int kRing = 8;    // slot-index ring (tiles)
 constexpr int kSS = 72;     // staging row stride: 64 heads + 8 (bf16)
-constexpr int kMaxK = 4096; // largest top-k of the contribution work group's index list
+constexpr int kMaxK = 4096; // largest top-k of the contribution phase's index list
 
 template <int DQK>
 struct RowSmem {
   static constexpr int kTileB = Tile<DQK>::kBytes;
-  // dq work group: tiles[4] | dZ[2][4 groups][64 lanes] bf16x8 | ring
+  // dq phase: tiles[4] | dZ[2][4 groups][64 lanes] bf16x8 | ring
   static constexpr int kDqZ = kDqBufs * kTileB;
   static constexpr int kDqRing = kDqZ + 2 * 4 * 64 * 16;
   static constexpr int kDqBytes = kDqRing + kRing * kSlots * 4;
-  // contribution work group: tiles[3] | staging[2][zh, zl, ph, pl][32 slots][kSS] bf16 | slot
+  // contribution phase: tiles[3] | staging[2][zh, zl, ph, pl][32 slots][kSS] bf16 | slot
   // rows (K entries rounded up to a whole tile);
   // the row's q ([64][DQK + 16]) and dO ([64][512 + 16]) pass through the tile area first
   static constexpr int kCStageBytes = 4 * kSlots * kSS * 2;
@@ -169,9 +192,28 @@ struct SdpHead {
       if (hok) v = *reinterpret_cast<const u32x4 *>(dout + ((t * H + h) * kDv + ks * 32 + g * 8));
       df[ks] = as_bf16x8(v);
     }
+    load_scalars(lse, delta, H, t, h);
+  }
+  __device__ __forceinline__ void load_scalars(const float *__restrict__ lse,
+                                               const float *__restrict__ delta, int H, int64_t t,
+                                               int h) {
+    const bool hok = h < H;
     const float l0 = hok ? lse[t * H + h] : -INFINITY;
     lse2 = l0 == -INFINITY ? INFINITY : l0 * kLog2e;  // empty row or padded head: P = 0
     dlt = hok ? delta[t * H + h] : 0.0f;
+  }
+  // q / dO blocks from a [head][stride] bf16 copy of the row in LDS
+  __device__ __forceinline__ void q_from_lds(const uint16_t *rows, int stride, int h) {
+    const int g = __lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < DQK / 32; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(rows + h * stride + ks * 32 + g * 8));
+  }
+  __device__ __forceinline__ void o_from_lds(const uint16_t *rows, int stride, int h) {
+    const int g = __lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < kDv / 32; ++ks)
+      df[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(rows + h * stride + ks * 32 + g * 8));
   }
   __device__ __forceinline__ void settle_all() {
 #pragma unroll
@@ -339,7 +381,7 @@ __device__ __forceinline__ void bwd_contrib_row(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
     const float *__restrict__ lse, const float *__restrict__ delta,
     const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
-    float *__restrict__ stage, int64_t t, unsigned char *smem) {
+    uint32_t *__restrict__ stage, int64_t t, unsigned char *smem) {
   using TL = Tile<DQK>;
   using SM = RowSmem<DQK>;
   constexpr int kNTq = DQK / 64;  // channel tiles per quarter (9 or 8)
@@ -354,12 +396,9 @@ __device__ __forceinline__ void bwd_contrib_row(
   const int32_t *irow = idx + t * K;
   const int nchunks = (lim + kSlots - 1) / kSlots;
 
-  // ---- prologue: the row's q, then dO, through LDS into head-contraction fragments of the
-  // contribution waves' channels; padded heads are zero
-  const int qq = wave - 4;
-  const int ch0 = qq * 16 * kNTq;
-  bf16x8 qh[2][kNTq], oh[2][kNTq];
-  // every global load of the prologue first (q, dO, the index list), then the LDS stores
+  // ---- prologue: the row's q, then dO, pass through LDS ([head][channel], padded heads zero):
+  // the SdP waves read their head blocks from it, the contribution waves head-contraction
+  // fragments of their channels.  Every global load of the prologue is issued first.
   constexpr int kQV = 64 * (DQK / 8) / 512, kOV = 64 * (kDv / 8) / 512, kIV = kMaxK / 512;
   u32x4 qv[kQV], ov[kOV];
   int32_t iv[kIV];
@@ -385,56 +424,36 @@ __device__ __forceinline__ void bwd_contrib_row(
     const int e = threadIdx.x + j * 512, hh = e / (DQK / 8), col = (e % (DQK / 8)) * 8;
     *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kQStride + col]) = qv[j];
   }
+  // dO and the slot rows (up to a whole number of tiles; the list lies outside the staging area)
+  auto store_o_rows = [&]() {
+#pragma unroll
+    for (int j = 0; j < kOV; ++j) {
+      const int e = threadIdx.x + j * 512, hh = e / (kDv / 8), col = (e % (kDv / 8)) * 8;
+      *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kOStride + col]) = ov[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kIV; ++j) {
+      const int e = threadIdx.x + j * 512;
+      if (e < nchunks * kSlots) slot_rows[e] = iv[j];
+    }
+  };
   __syncthreads();  // P0
-  if (wave >= 4) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int n = 0; n < kNTq; ++n) {
-        const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kQStride + ch0 + n * 16 + cq * 4];
-        const u32x2 lo = lds_read_tr16(base);
-        const u32x2 hi = lds_read_tr16(base + 4 * SM::kQStride);
-        qh[kh][n] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-      }
-  }
-  __syncthreads();  // P1
-#pragma unroll
-  for (int j = 0; j < kOV; ++j) {
-    const int e = threadIdx.x + j * 512, hh = e / (kDv / 8), col = (e % (kDv / 8)) * 8;
-    *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kOStride + col]) = ov[j];
-  }
-  // slot rows up to a whole number of tiles (the index list lies outside the staging area)
-#pragma unroll
-  for (int j = 0; j < kIV; ++j) {
-    const int e = threadIdx.x + j * 512;
-    if (e < nchunks * kSlots) slot_rows[e] = iv[j];
-  }
-  __syncthreads();  // P2
-  if (wave >= 4) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int n = 0; n < kNTq; ++n) {
-        const int ch = ch0 + n * 16;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ch < kDv) {
-          const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kOStride + ch + cq * 4];
-          const u32x2 lo = lds_read_tr16(base);
-          const u32x2 hi = lds_read_tr16(base + 4 * SM::kOStride);
-          v = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
-        oh[kh][n] = as_bf16x8(v);
-      }
-  }
-  __syncthreads();  // P3: the q / dO staging is read (the tile area is free)
 
+  // The two roles are separate branches from here on (their register sets never overlap).
   if (wave < 4) {
     // ============================== SdP waves ==============================
     const int G = wave;
+    const int h = G * 16 + hl;
+    SdpHead<DQK> hd;
+    hd.load_scalars(lse, delta, H, t, h);
+    hd.q_from_lds(qstage, SM::kQStride, h);
+    __syncthreads();  // P1
+    store_o_rows();
+    __syncthreads();  // P2
+    hd.o_from_lds(qstage, SM::kOStride, h);
+    __syncthreads();  // P3: the q / dO staging is read (the tile area is free)
     const uint32_t tiles_lds = lds_addr(smem);
     constexpr int kLoadsW = TL::kLoads / 4;
-    SdpHead<DQK> hd;
-    hd.load(q, dout, lse, delta, H, t, G * 16 + hl);
     hd.settle_all();  // before the first tile load (see settle())
     if (nchunks > 0) issue_tile<DQK, kCBufs>(tiles_lds, kv, slot_rows, 0, G);
     if (nchunks > 1) issue_tile<DQK, kCBufs>(tiles_lds, kv, slot_rows + kSlots, 1, G);
@@ -445,7 +464,6 @@ __device__ __forceinline__ void bwd_contrib_row(
     __syncthreads();  // S1: tile 0 loaded
     TileFrag<DQK> fr;
     fr.init();
-    const int h = G * 16 + hl;
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): tile c complete; contribution waves are done with chunk c - 2
       if (c == nchunks) break;
@@ -474,6 +492,36 @@ __device__ __forceinline__ void bwd_contrib_row(
     lds_barrier();  // Z
   } else {
     // ========================== contribution waves =========================
+    const int qq = wave - 4;
+    const int ch0 = qq * 16 * kNTq;
+    bf16x8 qh[2][kNTq], oh[2][kNTq];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int n = 0; n < kNTq; ++n) {
+        const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kQStride + ch0 + n * 16 + cq * 4];
+        const u32x2 lo = lds_read_tr16(base);
+        const u32x2 hi = lds_read_tr16(base + 4 * SM::kQStride);
+        qh[kh][n] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
+    __syncthreads();  // P1
+    store_o_rows();
+    __syncthreads();  // P2
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int n = 0; n < kNTq; ++n) {
+        const int ch = ch0 + n * 16;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ch < kDv) {
+          const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kOStride + ch + cq * 4];
+          const u32x2 lo = lds_read_tr16(base);
+          const u32x2 hi = lds_read_tr16(base + 4 * SM::kOStride);
+          v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        oh[kh][n] = as_bf16x8(v);
+      }
+    __syncthreads();  // P3
     __syncthreads();  // S1
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): P / dZ of chunk c - 1 are staged
@@ -496,26 +544,33 @@ __device__ __forceinline__ void bwd_contrib_row(
             const bf16x8 zb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&zl[off]));
             const bf16x8 pa = as_bf16x8(*reinterpret_cast<const u32x4 *>(&ps[off]));
             const bf16x8 pb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&pl[off]));
-            // four passes over the channel tiles: consecutive MFMAs are independent
+            // C^T = q^T . (scale dZ) + dO^T . P: the head-contraction fragments serve as the A
+            // operand (rows = channels) and the staged [slot][head] fragments as B (columns =
+            // slots), so that each lane ends with four consecutive channels of one slot.  Four
+            // passes over the channel tiles keep consecutive MFMAs independent (the dO
+            // fragments of RoPE channels are zero; skipping them would need a branch per MFMA).
 #pragma unroll
-            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(za, qh[kh][n], acc[n]);
+            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(qh[kh][n], za, acc[n]);
 #pragma unroll
-            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(zb, qh[kh][n], acc[n]);
+            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(qh[kh][n], zb, acc[n]);
 #pragma unroll
-            for (int n = 0; n < kNTq; ++n)
-              if (ch0 + n * 16 < kDv) acc[n] = mfma16(pa, oh[kh][n], acc[n]);
+            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(oh[kh][n], pa, acc[n]);
 #pragma unroll
-            for (int n = 0; n < kNTq; ++n)
-              if (ch0 + n * 16 < kDv) acc[n] = mfma16(pb, oh[kh][n], acc[n]);
+            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(oh[kh][n], pb, acc[n]);
           }
-          // acc[n][i] -> stage[slot cc*32 + 16mt + 4g + i][ch0 + 16n + hl] (valid slots only)
-          const u32x4 rv = *reinterpret_cast<const u32x4 *>(rr + mt * 16 + g * 4);
+          // acc[n][0..3] -> stage[slot cc*32 + 16mt + hl][ch0 + 16n + 4g .. + 3] (valid slots)
+          if (rr[mt * 16 + hl] >= 0) {
+            uint32_t *dst = stage + static_cast<int64_t>(cc * kSlots + mt * 16 + hl) * (DQK / 4 * 3) +
+                            (ch0 + 4 * g) / 4 * 3;
+            // plain stores: the L2 merges the 64-byte pieces of a row into whole lines (written
+            // with the non-temporal hint the pieces reach HBM separately, at about half the rate)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (static_cast<int32_t>(rv[i]) >= 0) {
-              float *dst = stage + static_cast<int64_t>(cc * kSlots + mt * 16 + g * 4 + i) * DQK + ch0 + hl;
-#pragma unroll
-              for (int n = 0; n < kNTq; ++n) dst[n * 16] = acc[n][i];
+            for (int n = 0; n < kNTq; ++n) {
+              uint32_t w[3];
+              pack_f24x4(acc[n], w);
+              dst[n * 12] = w[0];
+              dst[n * 12 + 1] = w[1];
+              dst[n * 12 + 2] = w[2];
             }
           }
         }
@@ -549,16 +604,15 @@ __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
     const float *__restrict__ lse, const float *__restrict__ delta,
     const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
-    uint16_t *__restrict__ dq, float *__restrict__ stage, int64_t row0) {
+    uint16_t *__restrict__ dq, uint32_t *__restrict__ stage, int64_t row0) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int64_t i = blockIdx.x >> 1;
+  const int64_t i = blockIdx.x;
   const int64_t t = row0 + i;
-  if (blockIdx.x & 1)
-    bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2,
-                         stage + i * K * DQK, t, smem);
-  else
-    bwd_dq_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2, dq, t,
-                    smem);
+  bwd_dq_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2, dq, t,
+                  smem);
+  __syncthreads();  // every wave is done with the dq phase's LDS
+  bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2,
+                       stage + i * K * (DQK / 4 * 3), t, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -633,7 +687,7 @@ __global__ void pair_fill_kernel(const int32_t *__restrict__ idx,
 template <int DQK>
 __global__ __launch_bounds__(256) void pair_reduce_kernel(const int32_t *__restrict__ off,
                                                           const int32_t *__restrict__ list,
-                                                          const float *__restrict__ stage,
+                                                          const uint32_t *__restrict__ stage,
                                                           int64_t n_rows, float *__restrict__ dkv) {
   constexpr int kVec = (DQK / 4 + 63) / 64;  // float4 per lane (3 for 576, 2 for 512)
   const int lane = threadIdx.x & 63;
@@ -644,26 +698,32 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const int32_t *__restr
   f32x4 acc[kVec];
 #pragma unroll
   for (int c = 0; c < kVec; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int kW = DQK / 4 * 3;  // words per staged contribution
+  // four channels 4 lane + 256 c .. + 3 of contribution row r: words 3 lane + 192 c .. + 2
+  auto load4 = [&](const uint32_t *r, int c) {
+    const uint32_t *w = r + 3 * lane + 192 * c;
+    return unpack_f24x4(w[0], w[1], w[2]);
+  };
   int k = b;
   for (; k + 1 < e; k += 2) {  // two contributions in flight per iteration
-    const float *r0 = stage + static_cast<int64_t>(list[k]) * DQK;
-    const float *r1 = stage + static_cast<int64_t>(list[k + 1]) * DQK;
+    const uint32_t *r0 = stage + static_cast<int64_t>(list[k]) * kW;
+    const uint32_t *r1 = stage + static_cast<int64_t>(list[k + 1]) * kW;
     f32x4 v0[kVec], v1[kVec];
 #pragma unroll
     for (int c = 0; c < kVec; ++c) {
       const int ch = 4 * lane + 256 * c;
-      v0[c] = ch < DQK ? *reinterpret_cast<const f32x4 *>(r0 + ch) : f32x4{0.f, 0.f, 0.f, 0.f};
-      v1[c] = ch < DQK ? *reinterpret_cast<const f32x4 *>(r1 + ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v0[c] = ch < DQK ? load4(r0, c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v1[c] = ch < DQK ? load4(r1, c) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int c = 0; c < kVec; ++c) acc[c] += v0[c] + v1[c];
   }
   if (k < e) {
-    const float *r0 = stage + static_cast<int64_t>(list[k]) * DQK;
+    const uint32_t *r0 = stage + static_cast<int64_t>(list[k]) * kW;
 #pragma unroll
     for (int c = 0; c < kVec; ++c) {
       const int ch = 4 * lane + 256 * c;
-      if (ch < DQK) acc[c] += *reinterpret_cast<const f32x4 *>(r0 + ch);
+      if (ch < DQK) acc[c] += load4(r0, c);
     }
   }
   float *d = dkv + s * DQK;
@@ -678,14 +738,14 @@ template <int DQK>
 hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                        const int32_t *topk_length, const float *lse, const float *delta,
                        const uint16_t *dout, int64_t row0, int64_t rows, int32_t H, int32_t K,
-                       float scale, uint16_t *dq, float *stage, hipStream_t s) {
+                       float scale, uint16_t *dq, uint32_t *stage, hipStream_t s) {
   const size_t smem = RowSmem<DQK>::bytes(K);
   auto kern = bwd_rows_kernel<DQK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  DSA_LAUNCH("sparse_mla_bwd_rows", kern, dim3(static_cast<unsigned>(2 * rows)),
+  DSA_LAUNCH("sparse_mla_bwd_rows", kern, dim3(static_cast<unsigned>(rows)),
              dim3(kRowWaves * 64), smem, s, q, kv, idx, topk_length, lse, delta, dout, H, K,
              scale, scale * kLog2e, dq, stage, row0);
   return hipGetLastError();

@@ -45,9 +45,10 @@ def test_workspace_queries(dsa):
     assert dsa.dsa_thd_metadata_workspace_size(32768) >= 5 * 32768 * 4
     assert dsa.dsa_thd_metadata_workspace_size(-1) == 0
     one_pass = dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576, 2048, 0)
-    assert one_pass >= 1000 * 64 * 4 + 1000 * 2048 * (576 + 1) * 4
+    assert one_pass >= 1000 * 64 * 4 + 1000 * 2048 * (576 * 3 + 4)
     one_row = dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576, 2048, 1)
-    assert 2048 * 577 * 4 <= one_row - 1000 * 64 * 4 < 2048 * 577 * 4 + 8 * 4096 + 1001 * 8
+    per_row = 2048 * (576 * 3 + 4)  # 24-bit staged contributions + pair list
+    assert per_row <= one_row - 1000 * 64 * 4 < per_row + 8 * 4096 + 1001 * 8
     assert dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576, 2048, 5000) == one_pass
     assert dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576, 0, 0) == 0
     assert dsa.dsa_indexer_topk_workspace_size(1000, 64, 128, 2048) == 0
