@@ -5,9 +5,9 @@
 // valid-prefix lengths, softmax_scale applied unchanged; SkyRL PR 2388 for the 512-wide NoPE
 // layout and top-k widths that are not a multiple of 64).
 //
-// Work group = one query row, NW waves, wave w owning HG groups of 16 heads (32 heads per
-// wave for H = 64: every latent-row fragment read from LDS feeds two MFMAs, which halves the
-// LDS traffic per flop against one group per wave).  The row's valid slots are processed in
+// Up to 32 heads: work group = one query row, NW waves (1 for H <= 16, 2 for H <= 32), wave w
+// owning HG = 1 group of 16 heads.  (33..64 heads use the role-split kernel further down.)
+// The row's valid slots are processed in
 // chunks of 32: the 32 latent rows are gathered into LDS with direct 16-byte loads (two
 // buffers; two work groups share a CU so one computes while the other waits), then each wave
 // computes, per head group,
@@ -20,7 +20,7 @@
 // The slot order inside the P.V contraction is permuted so that P needs no data movement: the
 // lane holding S^T rows (lane/16)*4 + [0,4) of both 16-slot halves supplies exactly the eight
 // contraction indices it owns in the MFMA B layout, and the transposing reads fetch V rows in
-// the same order.  The output accumulators (HG x 128 per lane) stay in AGPRs.
+// the same order.  The output accumulators (HG x 128 per lane) stay in registers.
 #include "dsa_common.h"
 #include "dsa_internal.h"
 #include "tile.h"
