@@ -221,6 +221,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
 // tile stays in use for two intervals; four tile buffers keep two tiles in flight.  Only the
 // PV waves issue the (compiler-invisible) tile loads and only the S waves issue ordinary
 // global loads, so each wave's explicit load-count waits stay exact.
+#ifndef FWD_S_AHEAD
+#define FWD_S_AHEAD 2
+#endif
+#ifndef FWD_S_FENCE
+#define FWD_S_FENCE 1
+#endif
 constexpr int kRoleNBuf = 4;
 constexpr int kRing = 8;  // slot-index ring (tiles)
 
@@ -275,9 +281,13 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
     // wave 0 keeps one tile's indices in flight: loaded an interval before they are written
     // to the ring (four chunks ahead of their S work), so the load latency is never waited for
     int32_t pending = -1;
-    if (wave == 0) {
-      for (int j = 0; j < 4 && j < nchunks; ++j) put_indices(j, load_indices(j));
-      if (4 < nchunks) pending = load_indices(4);
+    if (wave == 0) {  // all five loads in flight together, then the ring writes
+      int32_t first[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) first[j] = load_indices(j);
+      pending = load_indices(4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) put_indices(j, first[j]);
     }
     bf16x8 qf[kKSteps];  // head h, dims ks * 32 + g * 8 + [0, 8)
 #pragma unroll
@@ -301,31 +311,40 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
         if (c + 5 < nchunks) pending = load_indices(c + 5);
       }
       const unsigned char *tile = smem + (c % kRoleNBuf) * TL::kBytes;
+      // slot validity of this chunk, read before the MFMAs (the reads cannot move across the
+      // scheduling fences below)
+      const int32_t *rr = ring + (c % kRing) * kSlots;
+      const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(rr + g * 4);
+      const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(rr + 16 + g * 4);
       // ---- S^T = rows . q^T  (four chains: slot half mt, k-step parity); fragment reads run
-      // two k-steps ahead of the MFMAs
+      // kAhead k-steps ahead of the MFMAs (an LDS read under load takes longer than a few
+      // MFMAs, so a shallow read-ahead leaves the MFMA pipe waiting)
+      constexpr int kAhead = FWD_S_AHEAD;
       f32x4 acc[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
                          {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
-      bf16x8 a0[3], a1[3];
-      a0[0] = fr.a_frag(tile, 0, 0);
-      a1[0] = fr.a_frag(tile, 1, 0);
-      a0[1] = fr.a_frag(tile, 0, 1);
-      a1[1] = fr.a_frag(tile, 1, 1);
+      bf16x8 a0[kAhead + 1], a1[kAhead + 1];
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) {
+        a0[j] = fr.a_frag(tile, 0, j);
+        a1[j] = fr.a_frag(tile, 1, j);
+      }
+      // the scheduling fences keep this order (the compiler would otherwise pull each read
+      // down next to its MFMA)
+      if (FWD_S_FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        if (ks + 2 < kKSteps) {
-          a0[(ks + 2) % 3] = fr.a_frag(tile, 0, ks + 2);
-          a1[(ks + 2) % 3] = fr.a_frag(tile, 1, ks + 2);
+        if (ks + kAhead < kKSteps) {
+          a0[(ks + kAhead) % (kAhead + 1)] = fr.a_frag(tile, 0, ks + kAhead);
+          a1[(ks + kAhead) % (kAhead + 1)] = fr.a_frag(tile, 1, ks + kAhead);
         }
-        acc[0][ks & 1] = mfma16(a0[ks % 3], qf[ks], acc[0][ks & 1]);
-        acc[1][ks & 1] = mfma16(a1[ks % 3], qf[ks], acc[1][ks & 1]);
+        acc[0][ks & 1] = mfma16(a0[ks % (kAhead + 1)], qf[ks], acc[0][ks & 1]);
+        acc[1][ks & 1] = mfma16(a1[ks % (kAhead + 1)], qf[ks], acc[1][ks & 1]);
+        if (FWD_S_FENCE) __builtin_amdgcn_sched_barrier(0);
       }
       const f32x4 sv0 = acc[0][0] + acc[0][1], sv1 = acc[1][0] + acc[1][1];
       // ---- online softmax (base 2) with a lazily raised reference max: the reference only
       // moves when the running max exceeds it by more than 2^8, so P <= 256 and O is rescaled
       // only a handful of times per row.  Lanes hl, hl^16, hl^32, hl^48 share head h.
-      const int32_t *rr = ring + (c % kRing) * kSlots;
-      const u32x4 rv0 = *reinterpret_cast<const u32x4 *>(rr + g * 4);
-      const u32x4 rv1 = *reinterpret_cast<const u32x4 *>(rr + 16 + g * 4);
       float x[2][4];
       float cmax = -INFINITY;
 #pragma unroll
@@ -368,12 +387,11 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
     const int qq = wave - 4;
     const uint32_t tiles_lds = lds_addr(smem);
     __syncthreads();  // S0: indices of the first tiles are in the ring
-    auto issue = [&](int c) {  // this wave's loads k = 4 i + qq of tile c
-      const uint32_t dst = tiles_lds + (c % kRoleNBuf) * TL::kBytes;
+    // this wave's loads k = 4 i + qq of tile c: global byte offsets first (all row indices
+    // are read before any load is issued: the loads are asm with a memory clobber, so an index
+    // read placed between two of them would be waited for on its own)
+    auto offsets = [&](int c, uint32_t (&off)[kLoadsW]) {
       const int32_t *rr = ring + (c % kRing) * kSlots;
-      // all row indices first: the loads are asm with a memory clobber, so an index read
-      // placed between two of them would be waited for on its own
-      uint32_t off[kLoadsW];
 #pragma unroll
       for (int i = 0; i < kLoadsW; ++i) {
         const int pos = (4 * i + qq) * 64 + lane;
@@ -382,8 +400,15 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
         const int r = rr[row];
         off[i] = static_cast<uint32_t>(r < 0 ? 0 : r) * TL::kRowBytes + chunk * 16;  // -1: row 0
       }
+    };
+    auto load = [&](int c, int i, const uint32_t (&off)[kLoadsW]) {
+      dma16_sv(kv, off[i], tiles_lds + (c % kRoleNBuf) * TL::kBytes + (4 * i + qq) * 1024);
+    };
+    auto issue = [&](int c) {
+      uint32_t off[kLoadsW];
+      offsets(c, off);
 #pragma unroll
-      for (int i = 0; i < kLoadsW; ++i) dma16_sv(kv, off[i], dst + (4 * i + qq) * 1024);
+      for (int i = 0; i < kLoadsW; ++i) load(c, i, off);
     };
     if (nchunks > 0) issue(0);
     if (nchunks > 1) issue(1);
@@ -402,7 +427,16 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
       for (int n = 0; n < 8; ++n) o[G][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): P and rescale factors of chunk c - 1 are ready
-      if (c + 2 < nchunks) issue(c + 2);  // into the buffer of tile c - 2 (PV done at B(c - 1))
+      // tile c + 2 goes into the buffer of tile c - 2 (PV done at B(c - 1)); its loads are
+      // spread over the PV MFMAs below, so that the address unit drains them (1 KB each)
+      // while the MFMAs run instead of stalling the wave up front
+      const bool load_next = c + 2 < nchunks;
+      uint32_t off[kLoadsW];
+      if (load_next) offsets(c + 2, off);
+      if (c == 0 && load_next) {
+#pragma unroll
+        for (int i = 0; i < kLoadsW; ++i) load(c + 2, i, off);
+      }
       if (c > 0) {
         const int b = (c - 1) & 1;
         const unsigned char *tile = smem + ((c - 1) % kRoleNBuf) * TL::kBytes;
@@ -417,11 +451,22 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
           }
           pb[G] = pbuf[(b * 4 + G) * 64 + lane];
         }
+        static_assert(kLoadsW <= 16, "two loads per channel tile at most");
+        // the fragment of channel tile n + 1 is read before tile n's loads are issued (a read
+        // cannot move across those asm statements, so it would otherwise wait in full before
+        // every group of MFMAs)
+        bf16x8 va = fr.v_frag(tile, 8 * qq);
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const bf16x8 va = fr.v_frag(tile, 8 * qq + n);
+          bf16x8 vn = va;
+          if (n + 1 < 8) vn = fr.v_frag(tile, 8 * qq + n + 1);
+          if (load_next) {
+            if (n < kLoadsW) load(c + 2, n, off);
+            if (n + 8 < kLoadsW) load(c + 2, n + 8, off);
+          }
 #pragma unroll
           for (int G = 0; G < 4; ++G) o[G][n] = mfma16(va, pb[G], o[G][n]);
+          va = vn;
         }
       }
       if (c == nchunks) break;
