@@ -339,8 +339,10 @@ __device__ bool prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
 // candidate in a higher bin is selected, and the `need` best of the bin-b candidates (copied
 // to a scratch list of at most kScratch entries, ranked by key and then lower position) are
 // added.  If bin b is too populous (massive ties), select_exact() runs on the whole buffer.
-// The selected positions (all inside [start, t]) are marked in a bitmap one 32768-position
-// window at a time and read back in order with a scan of per-lane bit counts.
+// The selected positions (all inside [start, t]) are marked in a bitmap one window of kWin
+// positions at a time; lane l owns four bitmap words (128 positions), counts their bits, and
+// writes its positions from its exclusive prefix onward, so no LDS read sits inside the
+// emission loop.
 constexpr int kScratch = 256;
 
 __device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, int cnt, int K,
@@ -366,43 +368,62 @@ __device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
       fast = nb <= kScratch;
     }
     if (fast) {
-      // copy bin b to the scratch list
+      // copy bin b to the scratch list; two blocks of 256 entries are read per trip
       const uint64_t lt = lanemask_lt();
       int w = 0;
-      for (int e = 4 * lane; e - 4 * lane < cnt; e += 256) {
-        u32x4 v = {0u, 0u, 0u, 0u}, p = {0u, 0u, 0u, 0u};
-        if (e < cnt) {
-          v = *reinterpret_cast<const u32x4 *>(ck + e);
-          p = *reinterpret_cast<const u32x4 *>(cp + e);
+      for (int e0 = 0; e0 < cnt; e0 += 512) {
+        u32x4 v[2], p[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = e0 + 256 * h + 4 * lane;
+          v[h] = u32x4{0u, 0u, 0u, 0u};
+          p[h] = u32x4{0u, 0u, 0u, 0u};
+          if (e < cnt) {
+            v[h] = *reinterpret_cast<const u32x4 *>(ck + e);
+            p[h] = *reinterpret_cast<const u32x4 *>(cp + e);
+          }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool in = e + j < cnt && vb(v[j]) == b;
-          const uint64_t m = __ballot(in);
-          if (in) {
-            const int o = w + __popcll(m & lt);
-            sk[o] = v[j];
-            sp[o] = static_cast<int32_t>(p[j]);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool in = e0 + 256 * h + 4 * lane + j < cnt && vb(v[h][j]) == b;
+            const uint64_t m = __ballot(in);
+            if (in) {
+              const int o = w + __popcll(m & lt);
+              sk[o] = v[h][j];
+              sp[o] = static_cast<int32_t>(p[h][j]);
+            }
+            w += __popcll(m);
           }
-          w += __popcll(m);
-        }
       }
       wave_sync();
-      // rank of each scratch entry among the bin: larger key first, then lower position
+      // rank of each scratch entry among the bin: larger key first, then lower position (the
+      // list is read four entries at a time, the same addresses for every lane)
+      uint32_t ki[kScratch / 64], rank[kScratch / 64];
+      int32_t pi[kScratch / 64];
 #pragma unroll
       for (int r = 0; r < kScratch / 64; ++r) {
         const int i = lane + 64 * r;
-        if (i < nb) {
-          const uint32_t ki = sk[i];
-          const int32_t pi = sp[i];
-          uint32_t rank = 0u;
-          for (int j = 0; j < nb; ++j) {
-            const uint32_t kj = sk[j];
-            rank += (kj > ki || (kj == ki && sp[j] < pi)) ? 1u : 0u;
+        ki[r] = i < nb ? sk[i] : 0u;
+        pi[r] = i < nb ? sp[i] : 0;
+        rank[r] = 0u;
+      }
+      for (int j0 = 0; j0 < nb; j0 += 4) {
+        const u32x4 kj = *reinterpret_cast<const u32x4 *>(sk + j0);
+        const u32x4 pj = *reinterpret_cast<const u32x4 *>(sp + j0);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          if (j0 + jj < nb) {
+#pragma unroll
+            for (int r = 0; r < kScratch / 64; ++r)
+              rank[r] += (kj[jj] > ki[r] || (kj[jj] == ki[r] && static_cast<int32_t>(pj[jj]) < pi[r])) ? 1u : 0u;
           }
-          if (rank < need) keep4 |= 1u << r;
         }
       }
+#pragma unroll
+      for (int r = 0; r < kScratch / 64; ++r)
+        if (lane + 64 * r < nb && rank[r] < need) keep4 |= 1u << r;
     } else {
       int n = cnt;
       select_exact(ck, cp, hist, n, K, start, t);
@@ -411,26 +432,37 @@ __device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
       nb = 0;
     }
   }
-  // ---- ascending output through a bitmap of each 32768-position window.  Lane l produces the
-  // output slots [l S, l S + S) (S = ceil(K / 64)): it finds the set bit of its first slot
-  // from per-lane prefix counts and walks on from there, so the work is even however dense
-  // the selection is.  A single-window row stages its output in cp (free by then) and copies
-  // it out with wide stores.
-  constexpr int kWords = 1024;
+  // ---- ascending output, one window of kWin positions at a time.  A single-window row stages
+  // its output in cp (free by then: every candidate has been marked) and copies it out with
+  // wide stores.
+  constexpr int kWords = 256;
   constexpr int64_t kWin = 32 * kWords;
-  const int S = (K + 63) >> 6;
   const bool single = t - start < kWin;
-  uint32_t *lp = hist;  // per-lane exclusive prefix counts of the window (hist is free now)
   int done = 0;
   for (int64_t w0 = start; w0 <= t; w0 += kWin) {
-#pragma unroll
-    for (int i = 0; i < kWords / 256; ++i)
-      *reinterpret_cast<u32x4 *>(bm + 4 * (lane + 64 * i)) = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4 *>(bm + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
     wave_sync();
-    for (int e = lane; e < cnt; e += 64) {
-      const int64_t rel = cp[e] - w0;
-      if (rel >= 0 && rel < kWin && (b < 0 || vb(ck[e]) > b))
-        atomicOr(&bm[rel >> 5], 1u << (rel & 31));
+    for (int e0 = 0; e0 < cnt; e0 += 512) {
+      u32x4 v[2], p[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = e0 + 256 * h + 4 * lane;
+        v[h] = u32x4{0u, 0u, 0u, 0u};
+        p[h] = u32x4{0u, 0u, 0u, 0u};
+        if (e < cnt) {
+          v[h] = *reinterpret_cast<const u32x4 *>(ck + e);
+          p[h] = *reinterpret_cast<const u32x4 *>(cp + e);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t rel = static_cast<int32_t>(p[h][j]) - w0;
+          if (e0 + 256 * h + 4 * lane + j < cnt && rel >= 0 && rel < kWin &&
+              (b < 0 || vb(v[h][j]) > b))
+            atomicOr(&bm[rel >> 5], 1u << (rel & 31));
+        }
     }
 #pragma unroll
     for (int r = 0; r < kScratch / 64; ++r) {
@@ -441,41 +473,21 @@ __device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
       }
     }
     wave_sync();
-    // lane l owns words [16 l, 16 l + 16)
-    int c = 0;
+    const u32x4 words = *reinterpret_cast<const u32x4 *>(bm + 4 * lane);
+    const int c = __popc(words[0]) + __popc(words[1]) + __popc(words[2]) + __popc(words[3]);
+    const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(c)));
+    const int tw = __shfl(incl, 63, 64);  // selected positions in this window
+    int o = done + incl - c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(bm + 16 * lane + 4 * i);
-      c += __popc(v[0]) + __popc(v[1]) + __popc(v[2]) + __popc(v[3]);
-    }
-    const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(c)));
-    lp[lane] = static_cast<uint32_t>(incl - c);
-    const int tw = __shfl(incl, 63, 64);  // selected positions in this window
-    wave_sync();
-    int sl = max(lane * S, done);
-    const int s_end = min(min(lane * S + S, K), done + tw);
-    if (sl < s_end) {
-      const int r = sl - done;  // rank of the first slot's bit inside the window
-      int a = 0, z = 63;        // last lane whose prefix is <= r
-      while (a < z) {
-        const int mid = (a + z + 1) >> 1;
-        if (static_cast<int>(lp[mid]) <= r) a = mid;
-        else z = mid - 1;
-      }
-      int word = 16 * a;
-      int acc = static_cast<int>(lp[a]);
-      uint32_t bits = bm[word];
-      while (acc + __popc(bits) <= r) {
-        acc += __popc(bits);
-        bits = bm[++word];
-      }
-      for (int k = r - acc; k > 0; --k) bits &= bits - 1u;
-      for (; sl < s_end; ++sl) {
-        while (bits == 0u) bits = bm[++word];
-        const int32_t pos = static_cast<int32_t>(w0 + word * 32 + __ffs(static_cast<int>(bits)) - 1);
+      uint32_t bits = words[i];
+      const int32_t base = static_cast<int32_t>(w0 + 128 * lane + 32 * i);
+      while (bits != 0u) {
+        const int32_t pos = base + __ffs(static_cast<int>(bits)) - 1;
         bits &= bits - 1u;
-        if (single) cp[sl] = pos;
-        else out[sl] = pos;
+        if (single) cp[o] = pos;
+        else out[o] = pos;
+        ++o;
       }
     }
     done += tw;

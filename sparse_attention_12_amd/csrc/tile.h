@@ -48,12 +48,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // per-lane byte offset, and the destination given as a wave-uniform LDS byte address, so that
 // moving to the next tile is scalar arithmetic only.
 __device__ __forceinline__ void dma16_sv(const void *base, uint32_t voff, uint32_t lds) {
+  // the base is wave-uniform by contract; reading it from the first lane pins it to scalar
+  // registers even where the compiler has lost track of that (folded away when it is scalar)
+  // (readfirstlane yields a signed int: each half goes through uint32_t so that widening
+  // zero-extends it; sign-extending the low half would corrupt the high half of the address)
+  const uint64_t b = reinterpret_cast<uintptr_t>(base);
+  const uint32_t blo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint32_t bhi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint64_t bs = static_cast<uint64_t>(blo) | (static_cast<uint64_t>(bhi) << 32);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds))
       : "memory");
 }
 
