@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--bwd-passes", type=int, default=1,
+                    help="query-row passes of the backward (several passes overlap a pass's "
+                         "key-gradient reduction with the next pass's compute)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy a device buffer of BYTES bytes once with "
                          "an elementwise kernel (x * 1): a plain copy of known size, which "
@@ -250,8 +253,9 @@ def main():
     lse_buf = torch.empty((T, H), dtype=torch.float32, device=dev)
     dq_buf = torch.empty_like(att["q"])
     dkv_buf = torch.empty((T, Dqk), dtype=torch.float32, device=dev)
-    # one backward pass over all query rows (staging T x K x D_qk fp32)
-    ws = torch.empty(dsa.bwd_workspace_bytes(T, T, H, Dqk, K, rows_per_pass=0),
+    # backward workspace for --bwd-passes passes over the query rows
+    rows_per_pass = -(-T // max(1, args.bwd_passes))
+    ws = torch.empty(dsa.bwd_workspace_bytes(T, T, H, Dqk, K, rows_per_pass=rows_per_pass),
                      dtype=torch.uint8, device=dev)
     kpool_valid = None
     if not has_indexer:
@@ -261,6 +265,8 @@ def main():
         kpool_valid = int(len_buf.sum().item())
         del kp
 
+    bwd_events = []  # (start, stop) around each backward call while timing
+
     def step():
         md = dsa.prepare_thd_metadata(cu, K, T=T)
         if has_indexer:
@@ -268,10 +274,17 @@ def main():
                              length=len_buf)
         dsa.sparse_mla_fwd(att["q"], att["kv"], idx_buf, cfg.scale, len_buf, out=out_buf,
                            lse=lse_buf)
+        if timing:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev[0].record()
         dsa.sparse_mla_bwd(att["q"], att["kv"], idx_buf, out_buf, lse_buf, att["dout"],
                            cfg.scale, len_buf, dkv=dkv_buf, dq=dq_buf, workspace=ws)
+        if timing:
+            ev[1].record()
+            bwd_events.append(ev)
         return md
 
+    timing = False
     for _ in range(args.warmup):
         md = step()
     torch.cuda.synchronize()
@@ -279,7 +292,8 @@ def main():
     counts = workload_counts(md_host, cfg, cfg.idx_heads or 0, cfg.idx_dim or 0, K, H, Dqk, Dv,
                              kpool_valid)
 
-    timer = KernelTimer(dsa.lib(), 16 * args.steps)
+    timer = KernelTimer(dsa.lib(), 40 * args.steps)
+    timing = True
     timer.arm()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -299,10 +313,8 @@ def main():
 
     t_idx = avg("indexer_topk")
     t_fwd = avg("sparse_mla_fwd")
-    bwd_kernels = ("dkv_zero", "sparse_mla_bwd_delta", "sparse_mla_bwd_rows", "pair_zero",
-                   "pair_count", "pair_scan", "pair_fill", "sparse_mla_bwd_reduce")
-    # kernels of several backward passes add up per step
-    t_bwd = sum(sum(per_kernel[n]) for n in bwd_kernels if n in per_kernel) / args.steps
+    # the backward's own wall time (its passes overlap on two streams, so kernel times overlap)
+    t_bwd = sum(a.elapsed_time(b) for a, b in bwd_events) / len(bwd_events)
     comp = {
         "fwd": {"ms": t_fwd, "tflops": counts["fwd_flops"] / t_fwd / 1e9,
                 "frac_mfma_peak": counts["fwd_flops"] / t_fwd / 1e9 / PEAK_BF16_TFLOPS},
@@ -347,7 +359,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "cu_seqlens": list(cfg.cu_seqlens),
                    "indexer": (f"{cfg.idx_heads}x{cfg.idx_dim}" if has_indexer else None),
-                   "topk": K, "heads": H, "d_qk": Dqk, "d_v": Dv, "parallelism": "none"},
+                   "topk": K, "heads": H, "d_qk": Dqk, "d_v": Dv, "bwd_passes": args.bwd_passes,
+                   "parallelism": "none"},
         "components": comp, "kernels": kernels, "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -176,9 +176,13 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
  * in fp32 after a counting sort, so no atomics touch dkv.  The query rows are
  * processed in passes of R rows, R being as large as ws_bytes allows:
  * dsa_sparse_mla_bwd_workspace_size(..., rows_per_pass) gives the bytes for
- * passes of rows_per_pass rows (<= 0: all T_q rows in one pass, the fastest;
- * about T_q * K * (D_qk * 3 + 4) bytes).  Any ws_bytes of at least the size for
- * rows_per_pass = 1 works; less returns DSA_ERR_WORKSPACE.
+ * passes of rows_per_pass rows (<= 0: all T_q rows in one pass, about
+ * T_q * K * (D_qk * 3 + 4) bytes).  Several passes use two staging buffers:
+ * the reduction of pass p then runs on a helper stream of the library (one per
+ * calling thread and device, created on first use and kept) while pass p + 1
+ * computes on `stream`, which waits for the helper before the call's work
+ * ends.  Any ws_bytes of at least the size for rows_per_pass = 1 works; less
+ * returns DSA_ERR_WORKSPACE.
  * ------------------------------------------------------------------------ */
 size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk,
                                          int32_t K, int64_t rows_per_pass);

@@ -272,9 +272,12 @@ DEFAULT_BWD_STAGE_BYTES = 16 << 30
 def bwd_workspace_bytes(T_q: int, T_kv: int, H: int, D_qk: int, K: int,
                         rows_per_pass: int | None = None) -> int:
     """Workspace bytes of dsa_sparse_mla_bwd for passes of `rows_per_pass` query rows
-    (0: all rows in one pass; None: as many rows as DEFAULT_BWD_STAGE_BYTES of staging hold)."""
+    (0: all rows in one pass; None: as many rows as DEFAULT_BWD_STAGE_BYTES of staging hold).
+    Several passes use two staging buffers (a pass's reduction overlaps the next pass)."""
     if rows_per_pass is None:
-        rows_per_pass = max(1, min(max(T_q, 1), DEFAULT_BWD_STAGE_BYTES // (K * D_qk * 3)))
+        per_row = K * D_qk * 3
+        rows_per_pass = (T_q if T_q * per_row <= DEFAULT_BWD_STAGE_BYTES
+                         else max(1, DEFAULT_BWD_STAGE_BYTES // (2 * per_row)))
     return lib().dsa_sparse_mla_bwd_workspace_size(T_q, T_kv, H, D_qk, K, rows_per_pass)
 
 

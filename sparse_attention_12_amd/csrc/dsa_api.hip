@@ -275,18 +275,26 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   return DSA_OK;
 }
 
-// Backward workspace layout: delta [T_q, H] fp32 | debug flag | off [T_kv + 1] | cursor [T_kv]
-// | list [R * K] int32 | stage [R * K, D_qk] 24-bit values (3 bytes each), each segment
-// 256-byte aligned.
-static size_t bwd_fixed_bytes(int64_t T_q, int64_t T_kv, int32_t H) {
+// Backward workspace layout: delta [T_q, H] fp32 | debug flag | then one or two pass buffers,
+// each off [T_kv + 1] | cursor [T_kv] | list [R * K] int32 | stage [R * K, D_qk] 24-bit values
+// (3 bytes each); every segment 256-byte aligned.  One buffer when a single pass covers every
+// query row; otherwise two, so that a pass's reduction overlaps the next pass's compute.
+static size_t bwd_fixed_bytes(int64_t T_q, int32_t H) {
   return align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float)) + 256 +
-         align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t)) +
-         align_up(static_cast<size_t>(T_kv) * sizeof(int32_t)) + 256 /* base alignment */;
+         256 /* base alignment */;
 }
 
-static size_t bwd_pass_bytes(int64_t rows, int32_t D_qk, int32_t K) {
+static size_t bwd_pass_bytes(int64_t rows, int64_t T_kv, int32_t D_qk, int32_t K) {
   const size_t pairs = static_cast<size_t>(rows) * static_cast<size_t>(K);
-  return align_up(pairs * sizeof(int32_t)) + align_up(pairs * D_qk * 3);
+  return align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t)) +
+         align_up(static_cast<size_t>(T_kv) * sizeof(int32_t)) + align_up(pairs * sizeof(int32_t)) +
+         align_up(pairs * D_qk * 3);
+}
+
+static size_t bwd_total_bytes(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk, int32_t K,
+                              int64_t R) {
+  const int nbuf = R < T_q ? 2 : 1;
+  return bwd_fixed_bytes(T_q, H) + nbuf * bwd_pass_bytes(std::max<int64_t>(R, 1), T_kv, D_qk, K);
 }
 
 size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk,
@@ -294,7 +302,7 @@ size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, i
   if (T_q < 0 || T_kv < 0 || H < 0 || D_qk < 0 || K < 1) return 0;
   int64_t R = rows_per_pass <= 0 || rows_per_pass > T_q ? T_q : rows_per_pass;
   R = std::min<int64_t>(R, INT32_MAX / K);
-  return bwd_fixed_bytes(T_q, T_kv, H) + bwd_pass_bytes(std::max<int64_t>(R, 1), D_qk, K);
+  return bwd_total_bytes(T_q, T_kv, H, D_qk, K, std::max<int64_t>(R, 1));
 }
 
 int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
@@ -314,18 +322,33 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   if (T_kv > 0 && !dkv) return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: dkv is NULL");
   if (!aligned16(out) || !aligned16(dout) || !aligned16(dkv))
     return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: out/dout/dkv must be 16-byte aligned");
-  // rows per pass: as many as the workspace holds (pair ids are int32)
-  const size_t fixed = bwd_fixed_bytes(T_q, T_kv, H);
-  const size_t per_row = bwd_pass_bytes(1, D_qk, K);
-  const size_t need = fixed + per_row;
+  // rows per pass: all of them in one buffer if the workspace holds that, else as many as two
+  // buffers hold, else as many as one buffer holds (pair ids are int32)
+  const int64_t R_max = std::min<int64_t>(T_q, INT32_MAX / K);
+  const size_t need = bwd_fixed_bytes(T_q, H) + bwd_pass_bytes(1, T_kv, D_qk, K);
   if (T_q > 0 && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "sparse_mla_bwd: workspace needs at least %zu bytes, got %zu",
                 need, ws ? ws_bytes : static_cast<size_t>(0));
   int64_t R = 0;
+  int nbuf = 1;
   if (T_q > 0) {
-    R = std::min<int64_t>({T_q, static_cast<int64_t>((ws_bytes - fixed) / per_row),
-                           static_cast<int64_t>(INT32_MAX / K)});
-    while (R > 1 && fixed + bwd_pass_bytes(R, D_qk, K) > ws_bytes) --R;  // alignment slack
+    const size_t fixed = bwd_fixed_bytes(T_q, H);
+    const size_t per_row = static_cast<size_t>(K) * (D_qk * 3 + 4);
+    auto largest = [&](int nb) -> int64_t {  // rows per pass that nb buffers hold (0: none)
+      const size_t base = fixed + nb * bwd_pass_bytes(0, T_kv, D_qk, K);
+      if (ws_bytes <= base) return 0;
+      int64_t r = std::min<int64_t>(R_max, static_cast<int64_t>((ws_bytes - base) / (nb * per_row)));
+      while (r > 0 && fixed + nb * bwd_pass_bytes(r, T_kv, D_qk, K) > ws_bytes) --r;  // slack
+      return r;
+    };
+    if (R_max == T_q && fixed + bwd_pass_bytes(T_q, T_kv, D_qk, K) <= ws_bytes) {
+      R = T_q;
+    } else if ((R = largest(2)) >= 1) {
+      nbuf = 2;
+    } else {
+      R = std::max<int64_t>(largest(1), 1);
+    }
+    if (R >= T_q) nbuf = 1;
   }
   if (int rc = check_device()) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -335,13 +358,22 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   p += align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float));
   w.flag = reinterpret_cast<int32_t *>(p);
   p += 256;
-  w.off = reinterpret_cast<int32_t *>(p);
-  p += align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t));
-  w.cursor = reinterpret_cast<int32_t *>(p);
-  p += align_up(static_cast<size_t>(T_kv) * sizeof(int32_t));
-  w.list = reinterpret_cast<int32_t *>(p);
-  p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) * sizeof(int32_t));
-  w.stage = reinterpret_cast<uint32_t *>(p);
+  w.nbuf = nbuf;
+  for (int b = 0; b < 2; ++b) {
+    dsa::BwdPassBuffers &bb = w.buf[b];
+    if (b >= nbuf) {
+      bb = w.buf[0];
+      continue;
+    }
+    bb.off = reinterpret_cast<int32_t *>(p);
+    p += align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t));
+    bb.cursor = reinterpret_cast<int32_t *>(p);
+    p += align_up(static_cast<size_t>(T_kv) * sizeof(int32_t));
+    bb.list = reinterpret_cast<int32_t *>(p);
+    p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) * sizeof(int32_t));
+    bb.stage = reinterpret_cast<uint32_t *>(p);
+    p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) * D_qk * 3);
+  }
   w.rows_per_pass = R;
   if ((flags & DSA_DEBUG_CHECK_INDICES) && T_q > 0)
     if (int rc = debug_check_indices(idx, topk_length, T_q, K, T_kv, w.flag, s)) return rc;

@@ -38,14 +38,21 @@ hipError_t launch_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const in
                                  int32_t D_qk, int32_t K, float scale, uint16_t *out, float *lse,
                                  hipStream_t s);
 
-// Backward workspace carved from the caller's buffer.
+// Buffers of one backward pass (the key-gradient staging and its counting sort).
+struct BwdPassBuffers {
+  int32_t *off;     // [T_kv + 1] per latent row: contribution count, then list offset
+  int32_t *cursor;  // [T_kv]
+  int32_t *list;    // [rows_per_pass * K] pair ids grouped by latent row
+  uint32_t *stage;  // [rows_per_pass * K, D_qk * 3 / 4] staged contributions (24-bit)
+};
+
+// Backward workspace carved from the caller's buffer.  With two pass buffers the reduction of
+// pass p runs on a helper stream while pass p + 1 computes on the caller's stream.
 struct BwdWorkspace {
   float *delta;           // [T_q, H]
   int32_t *flag;          // debug index check
-  int32_t *off;           // [T_kv + 1] per latent row: contribution count, then list offset
-  int32_t *cursor;        // [T_kv]
-  int32_t *list;          // [rows_per_pass * K] pair ids grouped by latent row
-  uint32_t *stage;        // [rows_per_pass * K, D_qk * 3 / 4] staged contributions (24-bit)
+  BwdPassBuffers buf[2];
+  int nbuf;               // 1 or 2
   int64_t rows_per_pass;  // query rows per pass (>= 1)
 };
 

@@ -751,29 +751,100 @@ hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   return hipGetLastError();
 }
 
-template <int DQK>
-hipError_t launch_pass(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
-                       const int32_t *topk_length, const float *lse, const float *delta,
-                       const uint16_t *dout, int64_t row0, int64_t rows, int64_t T_kv,
-                       int32_t H, int32_t K, float scale, uint16_t *dq, float *dkv,
-                       const BwdWorkspace &ws, hipStream_t s) {
-  hipError_t e = launch_rows<DQK>(q, kv, idx, topk_length, lse, delta, dout, row0, rows, H, K,
-                                  scale, dq, ws.stage, s);
-  if (e != hipSuccess) return e;
+// Counting sort of pass [row0, row0 + rows) into buffer bb, on stream s.
+hipError_t launch_sort(const int32_t *idx, const int32_t *topk_length, int64_t row0,
+                       int64_t rows, int64_t T_kv, int32_t K, const BwdPassBuffers &bb,
+                       hipStream_t s) {
   const int64_t pairs = rows * K;
   const unsigned pb = static_cast<unsigned>((pairs + 255) / 256);
   const unsigned zb = static_cast<unsigned>(std::min<int64_t>((T_kv + 256) / 256, 65536));
-  DSA_LAUNCH("pair_zero", fill_zero_i32_kernel, dim3(zb), dim3(256), 0, s, ws.off, T_kv + 1);
+  DSA_LAUNCH("pair_zero", fill_zero_i32_kernel, dim3(zb), dim3(256), 0, s, bb.off, T_kv + 1);
   DSA_LAUNCH("pair_count", pair_count_kernel, dim3(pb), dim3(256), 0, s, idx, topk_length, row0,
-             rows, K, ws.off);
-  DSA_LAUNCH("pair_scan", pair_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws.off,
-             ws.cursor, T_kv);
+             rows, K, bb.off);
+  DSA_LAUNCH("pair_scan", pair_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, bb.off,
+             bb.cursor, T_kv);
   DSA_LAUNCH("pair_fill", pair_fill_kernel, dim3(pb), dim3(256), 0, s, idx, topk_length, row0,
-             rows, K, ws.cursor, ws.list);
-  DSA_LAUNCH("sparse_mla_bwd_reduce", pair_reduce_kernel<DQK>,
-             dim3(static_cast<unsigned>((T_kv + 3) / 4)), dim3(256), 0, s, ws.off, ws.list,
-             ws.stage, T_kv, dkv);
+             rows, K, bb.cursor, bb.list);
   return hipGetLastError();
+}
+
+template <int DQK>
+hipError_t launch_reduce(int64_t T_kv, const BwdPassBuffers &bb, float *dkv, hipStream_t s) {
+  DSA_LAUNCH("sparse_mla_bwd_reduce", pair_reduce_kernel<DQK>,
+             dim3(static_cast<unsigned>((T_kv + 3) / 4)), dim3(256), 0, s, bb.off, bb.list,
+             bb.stage, T_kv, dkv);
+  return hipGetLastError();
+}
+
+// Helper stream and events of the calling thread on the current device: created on first use
+// and kept until the process ends (they hold none of the caller's memory).
+struct BwdStreams {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, rows_done[2] = {nullptr, nullptr},
+             red_done[2] = {nullptr, nullptr};
+};
+hipError_t bwd_streams(BwdStreams *&out) {
+  thread_local BwdStreams per_dev[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  BwdStreams &b = per_dev[dev];
+  if (!b.s2) {
+    hipEvent_t *evs[6] = {&b.fork, &b.join, &b.rows_done[0], &b.rows_done[1], &b.red_done[0],
+                          &b.red_done[1]};
+    for (hipEvent_t *ev : evs)
+      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&b.s2, hipStreamNonBlocking)) != hipSuccess) return e;
+  }
+  out = &b;
+  return hipSuccess;
+}
+
+template <int DQK>
+hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                         const int32_t *topk_length, const float *lse, const float *delta,
+                         const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H, int32_t K,
+                         float scale, uint16_t *dq, float *dkv, const BwdWorkspace &ws,
+                         hipStream_t s) {
+  hipError_t e = hipSuccess;
+  const int64_t R = ws.rows_per_pass;
+  if (ws.nbuf == 1) {  // every pass in order on the caller's stream
+    for (int64_t r0 = 0; e == hipSuccess && r0 < T_q; r0 += R) {
+      const int64_t n = std::min<int64_t>(R, T_q - r0);
+      e = launch_rows<DQK>(q, kv, idx, topk_length, lse, delta, dout, r0, n, H, K, scale, dq,
+                           ws.buf[0].stage, s);
+      if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[0], s);
+      if (e == hipSuccess) e = launch_reduce<DQK>(T_kv, ws.buf[0], dkv, s);
+    }
+    return e;
+  }
+  // Two buffers: pass p computes (rows launch) on the caller's stream into buffer p % 2; its
+  // counting sort and reduction run on the helper stream, the reduction once the rows launch
+  // has finished, while the caller's stream goes on with pass p + 1.  Pass p + 2 reuses the
+  // buffer after pass p's reduction.  The helper stream forks from the caller's stream first
+  // (so that it also joins a stream capture) and the caller's stream joins it at the end.
+  BwdStreams *bs = nullptr;
+  if ((e = bwd_streams(bs)) != hipSuccess) return e;
+  if ((e = hipEventRecord(bs->fork, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(bs->s2, bs->fork, 0)) != hipSuccess) return e;
+  int p = 0;
+  for (int64_t r0 = 0; e == hipSuccess && r0 < T_q; r0 += R, ++p) {
+    const int64_t n = std::min<int64_t>(R, T_q - r0);
+    const int b = p & 1;
+    if (p >= 2 && (e = hipStreamWaitEvent(s, bs->red_done[b], 0)) != hipSuccess) break;
+    e = launch_rows<DQK>(q, kv, idx, topk_length, lse, delta, dout, r0, n, H, K, scale, dq,
+                         ws.buf[b].stage, s);
+    if (e == hipSuccess) e = hipEventRecord(bs->rows_done[b], s);
+    if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[b], bs->s2);
+    if (e == hipSuccess) e = hipStreamWaitEvent(bs->s2, bs->rows_done[b], 0);
+    if (e == hipSuccess) e = launch_reduce<DQK>(T_kv, ws.buf[b], dkv, bs->s2);
+    if (e == hipSuccess) e = hipEventRecord(bs->red_done[b], bs->s2);
+  }
+  // join (after an error too, so that no work is left unordered behind the caller's stream)
+  hipError_t j = hipEventRecord(bs->join, bs->s2);
+  if (j == hipSuccess) j = hipStreamWaitEvent(s, bs->join, 0);
+  return e != hipSuccess ? e : j;
 }
 
 }  // namespace
@@ -795,18 +866,14 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
   DSA_LAUNCH("sparse_mla_bwd_delta", bwd_delta_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0,
                      s, out, dout, rows, ws.delta);
   hipError_t e = hipGetLastError();
-  for (int64_t r0 = 0; e == hipSuccess && r0 < T_q; r0 += ws.rows_per_pass) {
-    const int64_t n = std::min<int64_t>(ws.rows_per_pass, T_q - r0);
-    if (D_qk == 576)
-      e = launch_pass<576>(q, kv, idx, topk_length, lse, ws.delta, dout, r0, n, T_kv, H, K,
-                           scale, dq, dkv, ws, s);
-    else if (D_qk == 512)
-      e = launch_pass<512>(q, kv, idx, topk_length, lse, ws.delta, dout, r0, n, T_kv, H, K,
-                           scale, dq, dkv, ws, s);
-    else
-      e = hipErrorInvalidValue;
-  }
-  return e;
+  if (e != hipSuccess) return e;
+  if (D_qk == 576)
+    return launch_passes<576>(q, kv, idx, topk_length, lse, ws.delta, dout, T_q, T_kv, H, K,
+                              scale, dq, dkv, ws, s);
+  if (D_qk == 512)
+    return launch_passes<512>(q, kv, idx, topk_length, lse, ws.delta, dout, T_q, T_kv, H, K,
+                              scale, dq, dkv, ws, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_check_indices(const int32_t *idx, const int32_t *topk_length, int64_t T_q,
