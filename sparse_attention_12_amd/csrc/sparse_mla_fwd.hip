@@ -245,7 +245,7 @@ template <int DQK>
 __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
-    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
+    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse, int redo_only) {
   using TL = Tile<DQK>;
   using SM = RoleSmem<DQK>;
   constexpr int kKSteps = DQK / 32;
@@ -265,6 +265,8 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
   const int lim = topk_length ? topk_length[t] : K;
   const int32_t *irow = idx + t * K;
   const int nchunks = (lim + kSlots - 1) / kSlots;
+  // redo mode: only the rows that the fast kernel flagged (first LSE entry NaN)
+  if (redo_only && !__builtin_isnan(lse[t * H])) return;
 
   if (wave < 4) {
     // ================================ S waves ================================
@@ -493,18 +495,318 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// 33..64 heads, fast path.  As the role-split kernel above, except that S wave w takes the 32
+// heads 32 (w >> 1) .. + 31 over the 16 slots 16 (w & 1) .. + 15 of every chunk: each
+// latent-row fragment it reads feeds two MFMAs, which halves the S waves' LDS reads.  The two
+// waves of a head pair see different slots of the same heads, so the softmax does not keep a
+// running maximum: each head uses one reference, the larger of the pair's maxima over the
+// first chunk (exchanged once in the prologue), and P = exp2(x - m_ref) needs neither
+// rescaling nor per-chunk reductions.  A row in which a later logit exceeds its reference by
+// more than kRefSlack (base 2), or whose first chunk has no valid slot for some head, is
+// flagged by a NaN in its first LSE entry and computed again by the role-split kernel.
+constexpr float kRefSlack = 24.0f;
+
+template <int DQK>
+struct PairSmem {
+  static constexpr int kTiles = kRoleNBuf * Tile<DQK>::kBytes;
+  static constexpr int kP = kTiles;                  // [2][4 groups][64 lanes] bf16x8
+  static constexpr int kX = kP + 2 * 4 * 64 * 16;    // [4 waves][32 heads] fp32 exchange
+  static constexpr int kI = kX + 4 * 32 * 4;         // [4 groups][16 heads] fp32 1/l
+  static constexpr int kF = kI + 4 * 16 * 4;         // int32 redo flag (16 bytes)
+  static constexpr int kRingOff = kF + 16;           // [kRing][32] int32 slot -> latent row
+  static constexpr int kBytes = kRingOff + kRing * kSlots * 4;
+};
+
+template <int DQK>
+__global__ __launch_bounds__(512) void sparse_mla_fwd_pair_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
+    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
+  using TL = Tile<DQK>;
+  using SM = PairSmem<DQK>;
+  constexpr int kKSteps = DQK / 32;
+  constexpr int kLoadsW = TL::kLoads / 4;  // tile loads per PV wave
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16x8 *pbuf = reinterpret_cast<bf16x8 *>(smem + SM::kP);
+  float *xbuf = reinterpret_cast<float *>(smem + SM::kX);
+  float *ibuf = reinterpret_cast<float *>(smem + SM::kI);
+  int32_t *redo = reinterpret_cast<int32_t *>(smem + SM::kF);
+  int32_t *ring = reinterpret_cast<int32_t *>(smem + SM::kRingOff);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t t = blockIdx.x;
+  const int g = lane >> 4;
+  const int hl = lane & 15;
+  const int lim = topk_length ? topk_length[t] : K;
+  const int32_t *irow = idx + t * K;
+  const int nchunks = (lim + kSlots - 1) / kSlots;
+
+  if (wave < 4) {
+    // ================================ S waves ================================
+    const int hp = wave >> 1;  // head pair: heads 32 hp .. + 31
+    const int mh = wave & 1;   // slot half: slots 16 mh .. + 15 of each chunk
+    auto load_indices = [&](int j) -> int32_t {
+      const int slot = j * kSlots + lane;
+      return lane < kSlots && slot < lim ? irow[slot] : -1;
+    };
+    auto put_indices = [&](int j, int32_t v) {
+      if (lane < kSlots) ring[(j % kRing) * kSlots + lane] = v;
+    };
+    int32_t pending = -1;
+    if (wave == 0) {  // all five loads in flight together, then the ring writes
+      int32_t first[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) first[j] = load_indices(j);
+      pending = load_indices(4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) put_indices(j, first[j]);
+      if (lane == 0) *redo = 0;
+    }
+    bf16x8 qf[2][kKSteps];  // head 32 hp + 16 hg + hl, dims ks * 32 + g * 8 + [0, 8)
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) {
+      const int h = 32 * hp + 16 * hg + hl;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < H) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
+        qf[hg][ks] = as_bf16x8(v);
+      }
+    }
+    // row fragments of this wave's slot half: rows 16 mh + hl, chunk 4 ks + g
+    int sb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sb[j] = TL::chunk_off(16 * mh + hl, j * 4 + g);
+    __syncthreads();  // S0: indices of the first tiles are in the ring
+    __syncthreads();  // S1: PV waves have issued the first tiles and waited for tile 0
+
+    // logits (base 2) of chunk c for this wave's 16 slots (4 per lane: slot 16 mh + 4 g + i)
+    // and 32 heads (hg); masked slots are -inf
+    auto logits = [&](int c, float (&x)[2][4]) {
+      const unsigned char *tile = smem + (c % kRoleNBuf) * TL::kBytes;
+      const int32_t *rr = ring + (c % kRing) * kSlots;
+      const u32x4 rv = *reinterpret_cast<const u32x4 *>(rr + 16 * mh + g * 4);
+      f32x4 acc[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
+                         {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
+      auto afrag = [&](int ks) {
+        return as_bf16x8(*reinterpret_cast<const u32x4 *>(tile + sb[ks & 3] + (ks >> 2) * 256));
+      };
+      bf16x8 a[3];
+      a[0] = afrag(0);
+      a[1] = afrag(1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        if (ks + 2 < kKSteps) a[(ks + 2) % 3] = afrag(ks + 2);
+        acc[0][ks & 1] = mfma16(a[ks % 3], qf[0][ks], acc[0][ks & 1]);
+        acc[1][ks & 1] = mfma16(a[ks % 3], qf[1][ks], acc[1][ks & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) {
+        const f32x4 sv = acc[hg][0] + acc[hg][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          x[hg][i] = static_cast<int32_t>(rv[i]) >= 0 ? sv[i] * scale_log2 : -INFINITY;
+      }
+    };
+
+    // ---- reference of each head: the larger of the two slot halves' maxima over chunk 0
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    if (nchunks > 0) {
+      float x[2][4];
+      logits(0, x);
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) {
+        float m = fmaxf(fmaxf(x[hg][0], x[hg][1]), fmaxf(x[hg][2], x[hg][3]));
+        m = fmaxf(m, xor16(m));
+        m = fmaxf(m, swap_halves(m));
+        m_ref[hg] = m;
+      }
+    }
+    if (g == 0) {
+      xbuf[wave * 32 + hl] = m_ref[0];
+      xbuf[wave * 32 + 16 + hl] = m_ref[1];
+    }
+    lds_barrier();  // P1
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) m_ref[hg] = fmaxf(m_ref[hg], xbuf[(wave ^ 1) * 32 + 16 * hg + hl]);
+    float l_run[2] = {0.0f, 0.0f};  // this lane's partial denominators
+    bool over = false;               // a logit exceeds its reference by more than kRefSlack
+    for (int c = 0; c <= nchunks; ++c) {
+      lds_barrier();  // B(c - 1): tile c complete; PV waves are done with chunk c - 2
+      if (c == nchunks) break;
+      if (wave == 0 && c + 5 <= nchunks) {  // ring slot of tile c - 4 is free
+        if (c + 4 < nchunks) put_indices(c + 4, pending);
+        if (c + 5 < nchunks) pending = load_indices(c + 5);
+      }
+      float x[2][4];
+      logits(c, x);
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = x[hg][i] != -INFINITY;
+          const float d = x[hg][i] - m_ref[hg];  // +inf if m_ref is -inf (chunk 0 had no slot)
+          over = over || (valid && !(d <= kRefSlack));
+          p[i] = valid ? __builtin_amdgcn_exp2f(d) : 0.0f;
+          l_run[hg] += p[i];
+        }
+        // P of head group 2 hp + hg: this wave supplies slots 16 mh + 4 g + i, i.e. one half
+        // of each lane's eight contraction entries (see pack_slots)
+        u32x2 w;
+        w[0] = pack_bf16x2(p[0], p[1]);
+        w[1] = pack_bf16x2(p[2], p[3]);
+        reinterpret_cast<u32x2 *>(&pbuf[((c & 1) * 4 + 2 * hp + hg) * 64 + lane])[mh] = w;
+      }
+    }
+    if (__ballot(over)) {
+      if (lane == 0) *redo = 1;  // every writer stores 1
+    }
+    // ---- finalize: denominators over the lane groups and the slot halves
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) {
+      float l = l_run[hg] + xor16(l_run[hg]);
+      l += swap_halves(l);
+      l_run[hg] = l;
+    }
+    if (g == 0) {
+      xbuf[wave * 32 + hl] = l_run[0];
+      xbuf[wave * 32 + 16 + hl] = l_run[1];
+    }
+    lds_barrier();  // Z1
+    if (mh == 0) {
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) {
+        const float l = l_run[hg] + xbuf[(wave ^ 1) * 32 + 16 * hg + hl];
+        const int h = 32 * hp + 16 * hg + hl;
+        if (g == 0) {
+          if (h < H)
+            lse[t * H + h] = l > 0.0f ? (m_ref[hg] + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+          ibuf[(2 * hp + hg) * 16 + hl] = l > 0.0f ? 1.0f / l : 0.0f;
+        }
+      }
+    }
+    lds_barrier();  // Z2: 1/l ready
+    if (wave == 0 && lane == 0 && *redo) lse[t * H] = __builtin_nanf("");
+  } else {
+    // ================================ PV waves ===============================
+    const int qq = wave - 4;
+    const uint32_t tiles_lds = lds_addr(smem);
+    __syncthreads();  // S0: indices of the first tiles are in the ring
+    auto offsets = [&](int c, uint32_t (&off)[kLoadsW]) {
+      const int32_t *rr = ring + (c % kRing) * kSlots;
+#pragma unroll
+      for (int i = 0; i < kLoadsW; ++i) {
+        const int pos = (4 * i + qq) * 64 + lane;
+        const int row = pos / TL::kChunks;
+        const int chunk = (pos % TL::kChunks) ^ TL::swz(row);
+        const int r = rr[row];
+        off[i] = static_cast<uint32_t>(r < 0 ? 0 : r) * TL::kRowBytes + chunk * 16;  // -1: row 0
+      }
+    };
+    auto load = [&](int c, int i, const uint32_t (&off)[kLoadsW]) {
+      dma16_sv(kv, off[i], tiles_lds + (c % kRoleNBuf) * TL::kBytes + (4 * i + qq) * 1024);
+    };
+    auto issue = [&](int c) {
+      uint32_t off[kLoadsW];
+      offsets(c, off);
+#pragma unroll
+      for (int i = 0; i < kLoadsW; ++i) load(c, i, off);
+    };
+    if (nchunks > 0) issue(0);
+    if (nchunks > 1) issue(1);
+    if (nchunks > 0) {  // tile 0 before S1 (tile 1 may stay in flight)
+      if (nchunks > 1) wait_vm<kLoadsW>();
+      else wait_tile();
+    }
+    __syncthreads();  // S1
+    lds_barrier();    // P1
+    TileFrag<DQK> fr;
+    fr.init();
+    f32x4 o[4][8];  // o[G][n][i] = O[head 16 G + hl][channel 128 qq + 16 n + 4 g + i]
+#pragma unroll
+    for (int G = 0; G < 4; ++G)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) o[G][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c <= nchunks; ++c) {
+      lds_barrier();  // B(c - 1): P of chunk c - 1 is ready
+      const bool load_next = c + 2 < nchunks;
+      uint32_t off[kLoadsW];
+      if (load_next) offsets(c + 2, off);
+      if (c == 0 && load_next) {
+#pragma unroll
+        for (int i = 0; i < kLoadsW; ++i) load(c + 2, i, off);
+      }
+      if (c > 0) {
+        const int b = (c - 1) & 1;
+        const unsigned char *tile = smem + ((c - 1) % kRoleNBuf) * TL::kBytes;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int G = 0; G < 4; ++G) pb[G] = pbuf[(b * 4 + G) * 64 + lane];
+        static_assert(kLoadsW <= 16, "two loads per channel tile at most");
+        bf16x8 va = fr.v_frag(tile, 8 * qq);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          bf16x8 vn = va;
+          if (n + 1 < 8) vn = fr.v_frag(tile, 8 * qq + n + 1);
+          if (load_next) {
+            if (n < kLoadsW) load(c + 2, n, off);
+            if (n + 8 < kLoadsW) load(c + 2, n + 8, off);
+          }
+#pragma unroll
+          for (int G = 0; G < 4; ++G) o[G][n] = mfma16(va, pb[G], o[G][n]);
+          va = vn;
+        }
+      }
+      if (c == nchunks) break;
+      // tile c + 1 before the next barrier (tile c + 2 may stay in flight)
+      if (c + 2 < nchunks) wait_vm<kLoadsW>();
+      else wait_tile();
+    }
+    lds_barrier();  // Z1
+    lds_barrier();  // Z2: 1/l ready
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int h = G * 16 + hl;
+      const float inv = ibuf[G * 16 + hl];
+      if (h < H) {
+        uint16_t *orow = out + (t * H + h) * kDv + 128 * qq + g * 4;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          u32x2 v;
+          v[0] = pack_bf16x2(o[G][n][0] * inv, o[G][n][1] * inv);
+          v[1] = pack_bf16x2(o[G][n][2] * inv, o[G][n][3] * inv);
+          *reinterpret_cast<u32x2 *>(orow + n * 16) = v;
+        }
+      }
+    }
+  }
+}
+
 template <int DQK>
 hipError_t launch_roles(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                         const int32_t *topk_length, int64_t T_q, int32_t H, int32_t K,
                         float scale, uint16_t *out, float *lse, hipStream_t s) {
+  constexpr size_t smem_p = PairSmem<DQK>::kBytes;
+  auto fast = sparse_mla_fwd_pair_kernel<DQK>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fast),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(smem_p));
+  if (e != hipSuccess) return e;
+  DSA_LAUNCH("sparse_mla_fwd", fast, dim3(static_cast<unsigned>(T_q)), dim3(512), smem_p, s, q,
+             kv, idx, topk_length, H, K, scale * kLog2e, out, lse);
+  // rows flagged by the fast kernel (a logit far above its reference) are computed again
   constexpr size_t smem = RoleSmem<DQK>::kBytes;
   auto kern = sparse_mla_fwd_roles_kernel<DQK>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(smem));
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  DSA_LAUNCH("sparse_mla_fwd", kern, dim3(static_cast<unsigned>(T_q)), dim3(512), smem, s, q,
-             kv, idx, topk_length, H, K, scale * kLog2e, out, lse);
+  DSA_LAUNCH("sparse_mla_fwd_redo", kern, dim3(static_cast<unsigned>(T_q)), dim3(512), smem, s,
+             q, kv, idx, topk_length, H, K, scale * kLog2e, out, lse, 1);
   return hipGetLastError();
 }
 

@@ -213,6 +213,44 @@ def test_fwd_bwd_query_rows_differ_from_key_rows():
     _fwd_bwd_case(40, 64, 576, 64, 64, seed=5, Tkv=333)
 
 
+@pytest.mark.parametrize("H", [64, 40])
+def test_fwd_rows_with_late_dominant_logits(H):
+    """Rows whose first 32 slots are all masked, or whose later logits exceed every logit of
+    the first 32 slots by far (one-hot softmax) or by about 2^20 (large unnormalised weights):
+    the forward's fast path for 33..64 heads scales each head by a reference taken from the
+    first chunk and must hand such rows to the exact path."""
+    dsa = _dsa()
+    T, Tkv, K, D = 24, 200, 96, 576
+    g = torch.Generator().manual_seed(21)
+    q = (torch.randn((T, H, D), generator=g) * 0.5)
+    kv = (torch.randn((Tkv, D), generator=g) * 0.5)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    idx = np.stack([np.sort(np.random.default_rng(t).choice(Tkv - 2, K, replace=False))
+                    for t in range(T)]).astype(np.int32)
+    idx[0, :32] = -1                      # chunk 0 fully masked
+    idx[1, :40] = -1                      # chunk 0 masked, chunk 1 partly
+    for t, row, mag in ((2, Tkv - 1, 2.0), (3, Tkv - 2, 0.6), (4, Tkv - 1, 2.0)):
+        q[t] = 1.0
+        idx[t, 70] = row                  # slot in the third chunk
+        idx[t, (idx[t] == row) & (np.arange(K) != 70)] = -1
+        kv[row] = mag
+    for t in (2, 3, 4):
+        kv[idx[t, :32][idx[t, :32] >= 0]] *= 0.02
+    q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
+    scale = 1.0 / 24.0
+    idx_t = torch.from_numpy(idx).to(dev)
+    out, lse = dsa.sparse_mla_fwd(q.to(dev), kv.to(dev), idx_t, scale)
+    dq, dkv = dsa.sparse_mla_bwd(q.to(dev), kv.to(dev), idx_t, out, lse, dout.to(dev), scale)
+    torch.cuda.synchronize()
+    assert not torch.isnan(lse).any()
+    ro, rl = oracle.sparse_mla_fwd(q, kv, idx, None, scale, 512)
+    checks.assert_close("out", _np(out.float()), ro, checks.ATOL_OUT)
+    checks.assert_close("lse", _np(lse), rl, checks.ATOL_LSE)
+    rdq, rdkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, scale)
+    checks.assert_close("dq", _np(dq.float()), rdq, checks.ATOL_OUT)
+    checks.assert_close("dkv", _np(dkv), rdkv, checks.ATOL_OUT)
+
+
 def test_tiny_workload_end_to_end():
     """Tiny workload: indexer (bit-exact) -> forward -> backward vs the oracle."""
     dsa = _dsa()
