@@ -328,13 +328,14 @@ def main():
     kernels = {n: {"avg_ms": sum(v) / len(v), "launches": len(v)} for n, v in per_kernel.items()}
 
     # algorithmic work per launch of each hot kernel: MFMA flops, or HBM bytes for the
-    # reduction of the staged key-gradient contributions (3 bytes per channel and the 4-byte
-    # pair id read once per valid pair, dkv read and written)
+    # reduction of the staged key-gradient contributions (a staged row of 2 bytes per channel
+    # and 16 exponent bytes, and the 4-byte pair id, read once per valid pair; dkv read and
+    # written)
     passes = max(1, len(per_kernel.get("sparse_mla_bwd_rows", [])) // args.steps)
     work = {"indexer_topk": ("mfma", counts["idx_flops"]),
             "sparse_mla_fwd": ("mfma", counts["fwd_flops"]),
             "sparse_mla_bwd_rows": ("mfma", counts["bwd_flops"] / passes),
-            "sparse_mla_bwd_reduce": ("hbm", (counts["valid"] * (Dqk * 3 + 4) / passes
+            "sparse_mla_bwd_reduce": ("hbm", (counts["valid"] * (Dqk * 2 + 20) / passes
                                               + 2 * T * Dqk * 4))}
     dom = max((n for n in work if n in per_kernel), key=lambda n: sum(per_kernel[n]))
     bound, amount = work[dom]

@@ -171,13 +171,14 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
  *
  * Workspace (caller-owned device memory, contents need not be initialised):
  * the key gradient is formed by staging one contribution row of D_qk values
- * per (query, valid slot), each value kept as the upper 24 bits of its fp32
- * form (relative error <= 2^-16), and summing each latent row's contributions
- * in fp32 after a counting sort, so no atomics touch dkv.  The query rows are
+ * per (query, valid slot) as 16-bit block floating point (blocks of D_qk / 16
+ * channels sharing a power-of-two scale: error <= 2^-15 of the block's largest
+ * magnitude; 2 * D_qk + 16 bytes per row), and summing each latent row's
+ * contributions in fp32 after a counting sort, so no atomics touch dkv.  The query rows are
  * processed in passes of R rows, R being as large as ws_bytes allows:
  * dsa_sparse_mla_bwd_workspace_size(..., rows_per_pass) gives the bytes for
  * passes of rows_per_pass rows (<= 0: all T_q rows in one pass, about
- * T_q * K * (D_qk * 3 + 4) bytes).  Several passes use two staging buffers:
+ * T_q * K * (2 * D_qk + 20) bytes).  Several passes use two staging buffers:
  * the reduction of pass p then runs on a helper stream of the library (one per
  * calling thread and device, created on first use and kept) while pass p + 1
  * computes on `stream`, which waits for the helper before the call's work

@@ -275,7 +275,7 @@ def bwd_workspace_bytes(T_q: int, T_kv: int, H: int, D_qk: int, K: int,
     (0: all rows in one pass; None: as many rows as DEFAULT_BWD_STAGE_BYTES of staging hold).
     Several passes use two staging buffers (a pass's reduction overlaps the next pass)."""
     if rows_per_pass is None:
-        per_row = K * D_qk * 3
+        per_row = K * (2 * D_qk + 16)
         rows_per_pass = (T_q if T_q * per_row <= DEFAULT_BWD_STAGE_BYTES
                          else max(1, DEFAULT_BWD_STAGE_BYTES // (2 * per_row)))
     return lib().dsa_sparse_mla_bwd_workspace_size(T_q, T_kv, H, D_qk, K, rows_per_pass)

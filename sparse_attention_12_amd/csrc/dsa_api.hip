@@ -276,9 +276,10 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
 }
 
 // Backward workspace layout: delta [T_q, H] fp32 | debug flag | then one or two pass buffers,
-// each off [T_kv + 1] | cursor [T_kv] | list [R * K] int32 | stage [R * K, D_qk] 24-bit values
-// (3 bytes each); every segment 256-byte aligned.  One buffer when a single pass covers every
-// query row; otherwise two, so that a pass's reduction overlaps the next pass's compute.
+// each off [T_kv + 1] | cursor [T_kv] | list [R * K] int32 | stage [R * K] rows of
+// bwd_stage_row_bytes(D_qk); every segment 256-byte aligned.  One buffer when a single pass
+// covers every query row; otherwise two, so that a pass's reduction overlaps the next pass's
+// compute.
 static size_t bwd_fixed_bytes(int64_t T_q, int32_t H) {
   return align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float)) + 256 +
          256 /* base alignment */;
@@ -288,7 +289,7 @@ static size_t bwd_pass_bytes(int64_t rows, int64_t T_kv, int32_t D_qk, int32_t K
   const size_t pairs = static_cast<size_t>(rows) * static_cast<size_t>(K);
   return align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t)) +
          align_up(static_cast<size_t>(T_kv) * sizeof(int32_t)) + align_up(pairs * sizeof(int32_t)) +
-         align_up(pairs * D_qk * 3);
+         align_up(pairs * dsa::bwd_stage_row_bytes(D_qk));
 }
 
 static size_t bwd_total_bytes(int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk, int32_t K,
@@ -333,7 +334,7 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   int nbuf = 1;
   if (T_q > 0) {
     const size_t fixed = bwd_fixed_bytes(T_q, H);
-    const size_t per_row = static_cast<size_t>(K) * (D_qk * 3 + 4);
+    const size_t per_row = static_cast<size_t>(K) * (dsa::bwd_stage_row_bytes(D_qk) + 4);
     auto largest = [&](int nb) -> int64_t {  // rows per pass that nb buffers hold (0: none)
       const size_t base = fixed + nb * bwd_pass_bytes(0, T_kv, D_qk, K);
       if (ws_bytes <= base) return 0;
@@ -372,7 +373,8 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
     bb.list = reinterpret_cast<int32_t *>(p);
     p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) * sizeof(int32_t));
     bb.stage = reinterpret_cast<uint32_t *>(p);
-    p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) * D_qk * 3);
+    p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) *
+                  dsa::bwd_stage_row_bytes(D_qk));
   }
   w.rows_per_pass = R;
   if ((flags & DSA_DEBUG_CHECK_INDICES) && T_q > 0)

@@ -43,8 +43,12 @@ struct BwdPassBuffers {
   int32_t *off;     // [T_kv + 1] per latent row: contribution count, then list offset
   int32_t *cursor;  // [T_kv]
   int32_t *list;    // [rows_per_pass * K] pair ids grouped by latent row
-  uint32_t *stage;  // [rows_per_pass * K, D_qk * 3 / 4] staged contributions (24-bit)
+  uint32_t *stage;  // [rows_per_pass * K] staged contribution rows of bwd_stage_row_bytes each
 };
+
+// Bytes of one staged key-gradient contribution row: D_qk signed 16-bit mantissas, then 16
+// exponent bytes (one per block of D_qk / 16 channels).
+constexpr size_t bwd_stage_row_bytes(int32_t D_qk) { return static_cast<size_t>(D_qk) * 2 + 16; }
 
 // Backward workspace carved from the caller's buffer.  With two pass buffers the reduction of
 // pass p runs on a helper stream while pass p + 1 computes on the caller's stream.

@@ -12,13 +12,13 @@
 //   rows   : one work group per query row, in two phases (layout of the waves below).  Both
 //            recompute S^T and dP^T per 32-slot chunk of gathered latent rows; the dq phase
 //            then forms dq = scale dZ . rows, the contribution phase C = scale dZ^T . q +
-//            P^T . dO for every (query, slot) pair and stores C to a staging buffer (3 bytes
-//            per channel: the upper 24 bits of the fp32 value).
+//            P^T . dO for every (query, slot) pair and stores C to a staging buffer (16-bit
+//            block floating point, see below).
 //   count / scan / fill : a counting sort of the pass's (query, slot) pairs by latent row.
 //   reduce : one work group per latent row adds up its staged contributions and adds the sum
 //            to dkv (every row has a single owner, so no atomics touch dkv).
 // Compared with fp32 atomics on dkv (bounded by the L2 atomic units at about one 4-byte add
-// per channel per clock), staging moves 8 bytes of HBM traffic per contribution element.
+// per channel per clock), staging moves about 4 bytes of HBM traffic per contribution element.
 #include <algorithm>
 
 #include "dsa_common.h"
@@ -31,23 +31,31 @@ namespace {
 constexpr int kSlots = 32;
 constexpr int kDv = 512;
 
-// Staged contributions are kept as the upper 24 bits of their fp32 value (sign, the full 8-bit
-// exponent, 15 stored mantissa bits; rounded to nearest even): 3 bytes per channel, relative
-// error at most 2^-16, and no range limit beyond fp32's.  Four channels pack into three words.
-__device__ __forceinline__ uint32_t f32_to_f24(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+// Staged contributions are 16-bit block floating point.  A block is the D_qk / 16 channels
+// that one lane of a contribution wave holds for one slot (channels 16 kNTq qq + 16 n + 4 g + i
+// of wave qq, lane group g).  With 2^e the smallest power of two above the block's largest
+// magnitude (e = the float exponent field of that magnitude, minus 126), channel x is kept as
+// the signed 16-bit m = round(32767 x / 2^e) and read back as m 2^e / 32767: an error of at
+// most 2^-15 of the block's largest magnitude.  A staged row is D_qk mantissas in channel
+// order, then 16 exponent bytes (byte 4 qq + g: the field of the block's largest magnitude,
+// at most 253).
+template <int DQK>
+constexpr int kStageWords = DQK / 2 + 4;  // 32-bit words per staged row
+template <int DQK>
+__device__ __forceinline__ int stage_exp_byte(int ch) {  // exponent byte of channel ch
+  return ch / (DQK / 4) * 4 + ((ch >> 2) & 3);
 }
-__device__ __forceinline__ void pack_f24x4(const f32x4 &v, uint32_t w[3]) {
-  const uint32_t a = f32_to_f24(v[0]), b = f32_to_f24(v[1]), c = f32_to_f24(v[2]),
-                 d = f32_to_f24(v[3]);
-  w[0] = a | (b << 24);
-  w[1] = (b >> 8) | (c << 16);
-  w[2] = (c >> 16) | (d << 8);
+__device__ __forceinline__ uint32_t pknorm16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(a, b));
 }
-__device__ __forceinline__ f32x4 unpack_f24x4(uint32_t w0, uint32_t w1, uint32_t w2) {
-  return f32x4{__uint_as_float(w0 << 8), __uint_as_float(((w0 >> 24) | (w1 << 8)) << 8),
-               __uint_as_float(((w1 >> 16) | (w2 << 16)) << 8), __uint_as_float(w2 & 0xFFFFFF00u)};
+__device__ __forceinline__ float stage_factor(uint32_t eb) {  // 2^e / 32767
+  return __uint_as_float((eb + 1u) << 23) * (1.0f / 32767.0f);
+}
+__device__ __forceinline__ f32x4 unpack_m16x4(const u32x2 &m, float f) {
+  return f32x4{static_cast<float>(static_cast<int32_t>(m[0] << 16) >> 16) * f,
+               static_cast<float>(static_cast<int32_t>(m[0]) >> 16) * f,
+               static_cast<float>(static_cast<int32_t>(m[1] << 16) >> 16) * f,
+               static_cast<float>(static_cast<int32_t>(m[1]) >> 16) * f};
 }
 
 // ---------------------------------------------------------------------------------------
@@ -95,7 +103,7 @@ __global__ void fill_zero_kernel(float *__restrict__ p, int64_t n) {
 //     fragments and scale dZ / P staged in LDS as bf16 ([slot][head]), each as a pair hi + lo
 //     (hi = bf16(x), lo = bf16(x - hi), about 16 significant bits): with either rounded to 8
 //     bits a latent row picked by many queries collects an error near the 2e-2 bar.  C is
-//     stored with 24 bits per channel (see f32_to_f24).
+//     stored as 16-bit block floating point (see kStageWords).
 // Tile loads (direct to LDS, waited for with explicit load counts) come from waves that issue no
 // other vector-memory operation, so that those counts stay exact and the compiler's own waits
 // never wait for tiles.  The dq phase fetches slot indices into a small ring from SdP wave 0
@@ -373,8 +381,8 @@ __device__ __forceinline__ void bwd_dq_row(
 }
 
 // ---------------------------------------------------------------------------------------
-// Key-gradient contributions of query row t, stored to stage[slot][DQK] (fp32) for every valid
-// slot.
+// Key-gradient contributions of query row t, stored to staged row `slot` of stage for every
+// valid slot.
 template <int DQK>
 __device__ __forceinline__ void bwd_contrib_row(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
@@ -467,7 +475,8 @@ __device__ __forceinline__ void bwd_contrib_row(
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): tile c complete; contribution waves are done with chunk c - 2
       if (c == nchunks) break;
-      if (c + 2 < nchunks) issue_tile<DQK, kCBufs>(tiles_lds, kv, slot_rows + (c + 2) * kSlots, c + 2, G);  // tile c - 1's buffer
+      if (c + 2 < nchunks)  // into tile c - 1's buffer
+        issue_tile<DQK, kCBufs>(tiles_lds, kv, slot_rows + (c + 2) * kSlots, c + 2, G);
       float p[2][4], dz[2][4];
       hd.grads(smem + (c % kCBufs) * TL::kBytes, fr, slot_rows + c * kSlots, scale_log2, p, dz);
       uint16_t *zs = stg + (c & 1) * (SM::kCStageBytes / 2);
@@ -558,20 +567,30 @@ __device__ __forceinline__ void bwd_contrib_row(
 #pragma unroll
             for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(oh[kh][n], pb, acc[n]);
           }
-          // acc[n][0..3] -> stage[slot cc*32 + 16mt + hl][ch0 + 16n + 4g .. + 3] (valid slots)
+          // acc[n][0..3] -> staged row cc*32 + 16mt + hl, channels ch0 + 16n + 4g .. + 3, one
+          // block per lane (valid slots only)
           if (rr[mt * 16 + hl] >= 0) {
-            uint32_t *dst = stage + static_cast<int64_t>(cc * kSlots + mt * 16 + hl) * (DQK / 4 * 3) +
-                            (ch0 + 4 * g) / 4 * 3;
-            // plain stores: the L2 merges the 64-byte pieces of a row into whole lines (written
-            // with the non-temporal hint the pieces reach HBM separately, at about half the rate)
+            float mx = 0.0f;
+#pragma unroll
+            for (int n = 0; n < kNTq; ++n)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[n][i]));
+            const uint32_t eb = min(__float_as_uint(mx) >> 23, 253u);
+            const float sc = __uint_as_float((253u - eb) << 23);  // 2^-e
+            uint32_t *row =
+                stage + static_cast<int64_t>(cc * kSlots + mt * 16 + hl) * kStageWords<DQK>;
+            uint32_t *mrow = row + ((ch0 + 4 * g) >> 1);  // channel tile n at word 8 n
+            // plain stores: the L2 merges the pieces of a row into whole lines (written with the
+            // non-temporal hint the pieces reach HBM separately, at about half the rate)
 #pragma unroll
             for (int n = 0; n < kNTq; ++n) {
-              uint32_t w[3];
-              pack_f24x4(acc[n], w);
-              dst[n * 12] = w[0];
-              dst[n * 12 + 1] = w[1];
-              dst[n * 12 + 2] = w[2];
+              u32x2 v;
+              v[0] = pknorm16(acc[n][0] * sc, acc[n][1] * sc);
+              v[1] = pknorm16(acc[n][2] * sc, acc[n][3] * sc);
+              *reinterpret_cast<u32x2 *>(mrow + 8 * n) = v;
             }
+            reinterpret_cast<unsigned char *>(row + DQK / 2)[4 * qq + g] =
+                static_cast<unsigned char>(eb);
           }
         }
       }
@@ -612,7 +631,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
                   smem);
   __syncthreads();  // every wave is done with the dq phase's LDS
   bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2,
-                       stage + i * K * (DQK / 4 * 3), t, smem);
+                       stage + i * K * kStageWords<DQK>, t, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -698,11 +717,14 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const int32_t *__restr
   f32x4 acc[kVec];
 #pragma unroll
   for (int c = 0; c < kVec; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int kW = DQK / 4 * 3;  // words per staged contribution
-  // four channels 4 lane + 256 c .. + 3 of contribution row r: words 3 lane + 192 c .. + 2
+  constexpr int kW = kStageWords<DQK>;
+  // four channels 4 lane + 256 c .. + 3 of staged row r (one block)
   auto load4 = [&](const uint32_t *r, int c) {
-    const uint32_t *w = r + 3 * lane + 192 * c;
-    return unpack_f24x4(w[0], w[1], w[2]);
+    const int ch = 4 * lane + 256 * c;
+    const u32x2 m = *reinterpret_cast<const u32x2 *>(r + ch / 2);
+    const unsigned char *ex = reinterpret_cast<const unsigned char *>(r + DQK / 2);
+    const uint32_t eb = ex[stage_exp_byte<DQK>(ch)];
+    return unpack_m16x4(m, stage_factor(eb));
   };
   int k = b;
   for (; k + 1 < e; k += 2) {  // two contributions in flight per iteration

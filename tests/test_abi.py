@@ -45,11 +45,11 @@ def test_workspace_queries(dsa):
     assert dsa.dsa_thd_metadata_workspace_size(32768) >= 5 * 32768 * 4
     assert dsa.dsa_thd_metadata_workspace_size(-1) == 0
     one_pass = dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576, 2048, 0)
-    assert one_pass >= 1000 * 64 * 4 + 1000 * 2048 * (576 * 3 + 4)
+    assert one_pass >= 1000 * 64 * 4 + 1000 * 2048 * (576 * 2 + 16 + 4)
     one_row = dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576, 2048, 1)
-    # passes of one row: two buffers, each 24-bit staged contributions + pair list + the
-    # counting-sort arrays of the 1000 latent rows
-    per_buf = 2048 * (576 * 3 + 4) + 1001 * 4 + 1000 * 4
+    # passes of one row: two buffers, each staged contribution rows (576 16-bit mantissas and
+    # 16 exponent bytes) + pair list + the counting-sort arrays of the 1000 latent rows
+    per_buf = 2048 * (576 * 2 + 16 + 4) + 1001 * 4 + 1000 * 4
     assert 2 * per_buf <= one_row - 1000 * 64 * 4 < 2 * per_buf + 12 * 256 + 512
     assert dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576, 2048, 5000) == one_pass
     assert dsa.dsa_sparse_mla_bwd_workspace_size(1000, 1000, 64, 576, 0, 0) == 0

@@ -134,7 +134,7 @@ class _Bufs:
         self.dq = torch.empty((T, H, Dqk), dtype=torch.bfloat16, device=dev)
         self.dkv = torch.empty((T, Dqk), dtype=torch.float32, device=dev)
         # the benchmark's single backward pass where it fits comfortably, else the default
-        one_pass = T * K * Dqk * 3 <= (200 << 30)
+        one_pass = T * K * (2 * Dqk + 16) <= (200 << 30)
         self.ws = torch.empty(dsa.bwd_workspace_bytes(T, T, H, Dqk, K, 0 if one_pass else None),
                               dtype=torch.uint8, device=dev)
 
