@@ -702,57 +702,78 @@ __global__ void pair_fill_kernel(const int32_t *__restrict__ idx,
 }
 
 // dkv[s] += sum of the staged contributions of latent row s.  One wave per row; lane l owns
-// channels 4 l + 256 c (c < DQK / 256 rounded up).
+// the 16-byte pieces l + 64 c of a staged row (channels 8 (l + 64 c) .. + 7: two blocks, whose
+// exponent bytes are adjacent), and four staged rows are in flight per step.
 template <int DQK>
 __global__ __launch_bounds__(256) void pair_reduce_kernel(const int32_t *__restrict__ off,
                                                           const int32_t *__restrict__ list,
                                                           const uint32_t *__restrict__ stage,
                                                           int64_t n_rows, float *__restrict__ dkv) {
-  constexpr int kVec = (DQK / 4 + 63) / 64;  // float4 per lane (3 for 576, 2 for 512)
+  constexpr int kPieces = DQK / 8;           // 16-byte pieces per staged row (72 or 64)
+  constexpr int kVec = (kPieces + 63) / 64;  // pieces per lane (2 or 1)
+  constexpr int kW = kStageWords<DQK>;
+  constexpr int kFly = 4;
   const int lane = threadIdx.x & 63;
-  const int64_t s = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * 4 +
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   if (s >= n_rows) return;
   const int b = off[s], e = off[s + 1];
   if (b == e) return;
-  f32x4 acc[kVec];
+  bool has[kVec];
+  int eoff[kVec];  // byte offset of the piece's exponent pair (even)
 #pragma unroll
-  for (int c = 0; c < kVec; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int kW = kStageWords<DQK>;
-  // four channels 4 lane + 256 c .. + 3 of staged row r (one block)
-  auto load4 = [&](const uint32_t *r, int c) {
-    const int ch = 4 * lane + 256 * c;
-    const u32x2 m = *reinterpret_cast<const u32x2 *>(r + ch / 2);
-    const unsigned char *ex = reinterpret_cast<const unsigned char *>(r + DQK / 2);
-    const uint32_t eb = ex[stage_exp_byte<DQK>(ch)];
-    return unpack_m16x4(m, stage_factor(eb));
+  for (int c = 0; c < kVec; ++c) {
+    has[c] = lane + 64 * c < kPieces;
+    eoff[c] = DQK * 2 + stage_exp_byte<DQK>(8 * (lane + 64 * c));
+  }
+  f32x4 acc[kVec][2];
+#pragma unroll
+  for (int c = 0; c < kVec; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int32_t pair, u32x4 (&m)[kVec], uint32_t (&ex)[kVec]) {
+    const uint32_t *r = stage + static_cast<int64_t>(pair) * kW;
+#pragma unroll
+    for (int c = 0; c < kVec; ++c) {
+      m[c] = u32x4{0u, 0u, 0u, 0u};
+      ex[c] = 0u;
+      if (has[c]) {
+        m[c] = *reinterpret_cast<const u32x4 *>(r + 4 * (lane + 64 * c));
+        ex[c] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const unsigned char *>(r) +
+                                                     eoff[c]);
+      }
+    }
+  };
+  auto add = [&](const u32x4 (&m)[kVec], const uint32_t (&ex)[kVec]) {
+#pragma unroll
+    for (int c = 0; c < kVec; ++c) {
+      acc[c][0] += unpack_m16x4(u32x2{m[c][0], m[c][1]}, stage_factor(ex[c] & 0xFFu));
+      acc[c][1] += unpack_m16x4(u32x2{m[c][2], m[c][3]}, stage_factor(ex[c] >> 8));
+    }
   };
   int k = b;
-  for (; k + 1 < e; k += 2) {  // two contributions in flight per iteration
-    const uint32_t *r0 = stage + static_cast<int64_t>(list[k]) * kW;
-    const uint32_t *r1 = stage + static_cast<int64_t>(list[k + 1]) * kW;
-    f32x4 v0[kVec], v1[kVec];
+  for (; k + kFly <= e; k += kFly) {
+    int32_t pr[kFly];  // one scalar load
 #pragma unroll
-    for (int c = 0; c < kVec; ++c) {
-      const int ch = 4 * lane + 256 * c;
-      v0[c] = ch < DQK ? load4(r0, c) : f32x4{0.f, 0.f, 0.f, 0.f};
-      v1[c] = ch < DQK ? load4(r1, c) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int i = 0; i < kFly; ++i) pr[i] = list[k + i];
+    u32x4 m[kFly][kVec];
+    uint32_t ex[kFly][kVec];
 #pragma unroll
-    for (int c = 0; c < kVec; ++c) acc[c] += v0[c] + v1[c];
+    for (int i = 0; i < kFly; ++i) load(pr[i], m[i], ex[i]);
+#pragma unroll
+    for (int i = 0; i < kFly; ++i) add(m[i], ex[i]);
   }
-  if (k < e) {
-    const uint32_t *r0 = stage + static_cast<int64_t>(list[k]) * kW;
-#pragma unroll
-    for (int c = 0; c < kVec; ++c) {
-      const int ch = 4 * lane + 256 * c;
-      if (ch < DQK) acc[c] += load4(r0, c);
-    }
+  for (; k < e; ++k) {
+    u32x4 m[kVec];
+    uint32_t ex[kVec];
+    load(list[k], m, ex);
+    add(m, ex);
   }
   float *d = dkv + s * DQK;
 #pragma unroll
   for (int c = 0; c < kVec; ++c) {
-    const int ch = 4 * lane + 256 * c;
-    if (ch < DQK) *reinterpret_cast<f32x4 *>(d + ch) += acc[c];
+    if (!has[c]) continue;
+    f32x4 *dst = reinterpret_cast<f32x4 *>(d + 8 * (lane + 64 * c));
+    dst[0] += acc[c][0];
+    dst[1] += acc[c][1];
   }
 }
 
