@@ -113,6 +113,7 @@ constexpr int kRowWaves = 8;
 constexpr int kDqBufs = 4;  // dq phase: a tile is read in two intervals
 constexpr int kCBufs = 3;   // contribution phase: a tile is read in one interval
 constexpr int kRing = 8;    // slot-index ring (tiles)
+static_assert(kRing == SlotRing::kTiles && kSlots == SlotRing::kSlots, "slot-index ring layout");
 constexpr int kSS = 72;     // staging row stride: 64 heads + 8 (bf16)
 constexpr int kMaxK = 4096; // largest top-k of the contribution phase's index list
 
@@ -139,18 +140,6 @@ struct RowSmem {
   static_assert(64 * kQStride * 2 <= kCStage, "q staging must fit the tile area");
   static_assert(kDqBytes <= 160 * 1024 && kCBytes <= 160 * 1024, "LDS per work group");
 };
-
-// slot indices of tile j (lanes 0..31 of a wave; -1 beyond the valid prefix) and the ring slot
-__device__ __forceinline__ int32_t load_tile_indices(const int32_t *__restrict__ irow, int lim,
-                                                     int j) {
-  const int lane = __lane_id();
-  const int slot = j * kSlots + lane;
-  return lane < kSlots && slot < lim ? irow[slot] : -1;
-}
-__device__ __forceinline__ void put_tile_indices(int32_t *ring, int j, int32_t v) {
-  const int lane = __lane_id();
-  if (lane < kSlots) ring[(j % kRing) * kSlots + lane] = v;
-}
 
 // This wave's share (loads k = 4 i + part) of the tile-c loads into buffer c % NBUF; rr lists
 // the tile's 32 latent rows (-1: invalid slot).
@@ -295,28 +284,19 @@ __device__ __forceinline__ void bwd_dq_row(
   if (wave < 4) {
     // ============================== SdP waves ==============================
     const int G = wave;
-    int32_t pending = -1;  // wave 0: indices four tiles ahead, one interval in flight
-    if (wave == 0) {
-      int32_t first[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) first[j] = load_tile_indices(irow, lim, j);
-      pending = load_tile_indices(irow, lim, 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) put_tile_indices(ring, j, first[j]);
-    }
+    SlotRing sr;  // wave 0 keeps the slot-index ring filled
+    if (wave == 0) sr.start(irow, lim, nchunks, ring);
     SdpHead<DQK> hd;
     hd.load(q, dout, lse, delta, H, t, G * 16 + hl);
     __syncthreads();  // S0: indices of the first tiles are in the ring
     __syncthreads();  // S1: the first tiles are loaded
+    hd.settle_all();  // see settle()
     TileFrag<DQK> fr;
     fr.init();
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1)
       if (c == nchunks) break;
-      if (wave == 0 && c + 5 <= nchunks) {  // ring slot of tile c - 4 is free
-        put_tile_indices(ring, c + 4, pending);
-        if (c + 5 < nchunks) pending = load_tile_indices(irow, lim, c + 5);
-      }
+      if (wave == 0) sr.step(irow, lim, nchunks, ring, c);
       float p[2][4], dz[2][4];
       hd.grads(smem + (c % kDqBufs) * TL::kBytes, fr, ring + (c % kRing) * kSlots, scale_log2,
                p, dz);

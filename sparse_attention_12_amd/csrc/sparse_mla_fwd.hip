@@ -229,6 +229,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
 #endif
 constexpr int kRoleNBuf = 4;
 constexpr int kRing = 8;  // slot-index ring (tiles)
+static_assert(kRing == SlotRing::kTiles && kSlots == SlotRing::kSlots, "slot-index ring layout");
 
 template <int DQK>
 struct RoleSmem {
@@ -273,24 +274,8 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
     const int G = wave;
     const int h = G * 16 + hl;
     // slot indices of tile j (lanes 0..31; -1 beyond the valid prefix)
-    auto load_indices = [&](int j) -> int32_t {
-      const int slot = j * kSlots + lane;
-      return lane < kSlots && slot < lim ? irow[slot] : -1;
-    };
-    auto put_indices = [&](int j, int32_t v) {
-      if (lane < kSlots) ring[(j % kRing) * kSlots + lane] = v;
-    };
-    // wave 0 keeps one tile's indices in flight: loaded an interval before they are written
-    // to the ring (four chunks ahead of their S work), so the load latency is never waited for
-    int32_t pending = -1;
-    if (wave == 0) {  // all five loads in flight together, then the ring writes
-      int32_t first[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) first[j] = load_indices(j);
-      pending = load_indices(4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) put_indices(j, first[j]);
-    }
+    SlotRing sr;  // wave 0 keeps the slot-index ring filled
+    if (wave == 0) sr.start(irow, lim, nchunks, ring);
     bf16x8 qf[kKSteps];  // head h, dims ks * 32 + g * 8 + [0, 8)
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
@@ -300,6 +285,8 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
     }
     __syncthreads();  // S0: indices of the first tiles are in the ring
     __syncthreads();  // S1: PV waves have issued the first tiles and waited for tile 0
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) settle(qf[ks]);  // see settle()
 
     TileFrag<DQK> fr;
     fr.init();
@@ -308,10 +295,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): tile c complete; PV waves are done with chunk c - 2
       if (c == nchunks) break;
-      if (wave == 0 && c + 5 <= nchunks) {  // ring slot of tile c - 4 is free
-        if (c + 4 < nchunks) put_indices(c + 4, pending);
-        if (c + 5 < nchunks) pending = load_indices(c + 5);
-      }
+      if (wave == 0) sr.step(irow, lim, nchunks, ring, c);
       const unsigned char *tile = smem + (c % kRoleNBuf) * TL::kBytes;
       // slot validity of this chunk, read before the MFMAs (the reads cannot move across the
       // scheduling fences below)
@@ -547,21 +531,9 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_pair_kernel(
     // ================================ S waves ================================
     const int hp = wave >> 1;  // head pair: heads 32 hp .. + 31
     const int mh = wave & 1;   // slot half: slots 16 mh .. + 15 of each chunk
-    auto load_indices = [&](int j) -> int32_t {
-      const int slot = j * kSlots + lane;
-      return lane < kSlots && slot < lim ? irow[slot] : -1;
-    };
-    auto put_indices = [&](int j, int32_t v) {
-      if (lane < kSlots) ring[(j % kRing) * kSlots + lane] = v;
-    };
-    int32_t pending = -1;
-    if (wave == 0) {  // all five loads in flight together, then the ring writes
-      int32_t first[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) first[j] = load_indices(j);
-      pending = load_indices(4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) put_indices(j, first[j]);
+    SlotRing sr;                // wave 0 keeps the slot-index ring filled
+    if (wave == 0) {
+      sr.start(irow, lim, nchunks, ring);
       if (lane == 0) *redo = 0;
     }
     bf16x8 qf[2][kKSteps];  // head 32 hp + 16 hg + hl, dims ks * 32 + g * 8 + [0, 8)
@@ -581,6 +553,10 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_pair_kernel(
     for (int j = 0; j < 4; ++j) sb[j] = TL::chunk_off(16 * mh + hl, j * 4 + g);
     __syncthreads();  // S0: indices of the first tiles are in the ring
     __syncthreads();  // S1: PV waves have issued the first tiles and waited for tile 0
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) settle(qf[hg][ks]);  // see settle()
 
     // logits (base 2) of chunk c for this wave's 16 slots (4 per lane: slot 16 mh + 4 g + i)
     // and 32 heads (hg); masked slots are -inf
@@ -638,10 +614,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_pair_kernel(
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): tile c complete; PV waves are done with chunk c - 2
       if (c == nchunks) break;
-      if (wave == 0 && c + 5 <= nchunks) {  // ring slot of tile c - 4 is free
-        if (c + 4 < nchunks) put_indices(c + 4, pending);
-        if (c + 5 < nchunks) pending = load_indices(c + 5);
-      }
+      if (wave == 0) sr.step(irow, lim, nchunks, ring, c);
       float x[2][4];
       logits(c, x);
 #pragma unroll

@@ -74,6 +74,51 @@ __device__ __forceinline__ void settle(T &v) {
   asm volatile("" : "+v"(v));
 }
 
+// Slot-index ring of one query row: tiles of 32 slots (latent row per slot, -1 for an invalid
+// slot or one beyond the row's valid prefix) in an LDS ring of 8 tiles.  One wave keeps it
+// filled with ordinary loads issued in batches of four tiles, one batch interval (four tiles)
+// before they are stored, so that no interval waits for a load it has just issued (such a wait
+// would hold the whole work group at the next barrier).  start() stores tiles 0..3 and issues
+// 4..7; step(c), at the top of interval c (every wave done with interval c - 1), stores tiles
+// c + 4 .. c + 7 when c is a multiple of 4, into the ring slots of tiles c - 4 .. c - 1, and
+// issues the next batch.
+struct SlotRing {
+  static constexpr int kSlots = 32, kTiles = 8, kBatch = 4;
+  int32_t pend[kBatch];
+  __device__ __forceinline__ static int32_t load(const int32_t *__restrict__ irow, int lim,
+                                                 int j) {
+    const int lane = __lane_id();
+    const int slot = j * kSlots + lane;
+    return lane < kSlots && slot < lim ? irow[slot] : -1;
+  }
+  __device__ __forceinline__ static void put(int32_t *ring, int j, int32_t v) {
+    const int lane = __lane_id();
+    if (lane < kSlots) ring[(j % kTiles) * kSlots + lane] = v;
+  }
+  __device__ __forceinline__ void start(const int32_t *__restrict__ irow, int lim, int nchunks,
+                                        int32_t *ring) {
+    int32_t first[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) first[j] = j < nchunks ? load(irow, lim, j) : -1;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+      pend[b] = kBatch + b < nchunks ? load(irow, lim, kBatch + b) : -1;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (j < nchunks) put(ring, j, first[j]);
+  }
+  __device__ __forceinline__ void step(const int32_t *__restrict__ irow, int lim, int nchunks,
+                                       int32_t *ring, int c) {
+    if ((c & (kBatch - 1)) != 0 || c + kBatch >= nchunks) return;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+      if (c + kBatch + b < nchunks) put(ring, c + kBatch + b, pend[b]);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+      pend[b] = c + 2 * kBatch + b < nchunks ? load(irow, lim, c + 2 * kBatch + b) : -1;
+  }
+};
+
 // Wait until at most N vector-memory operations of this wave (including dma16) are still in
 // flight (they complete in issue order).
 template <int N>
