@@ -63,6 +63,7 @@ struct IndexerSmem {
   __align__(16) int32_t cnt[kRows];  // candidates per row (appended with LDS atomics)
   uint32_t tau[kRows];                // per-row threshold: later keys enter only if above it
   int32_t has_tau[kRows];
+  int32_t compact[2];  // compaction due in step i: compact[i & 1] (written by wave 0 in step i - 1)
   __align__(16) unsigned char tile[IndexerCfg<D>::kNBuf][IndexerCfg<D>::kTileBytes];
 };
 // after the key stream the tile buffers hold 4 rows x (4 KB bitmap + 2 KB scratch list)
@@ -602,6 +603,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     sm.tau[threadIdx.x] = 0u;
     sm.cnt[threadIdx.x] = 0;
   }
+  if (threadIdx.x < 2) sm.compact[threadIdx.x] = 0;
   uint32_t *ck = sm.cand_key[row];
   int32_t *cp = sm.cand_pos[row];
   uint32_t my_tau = 0u;  // this row's threshold (wave-uniform copy)
@@ -633,8 +635,10 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   constexpr int kElems = NMT * 16;       // accumulator elements per lane
   constexpr int kSlice = kElems / NKK;   // of them finished per MFMA k-step
   static_assert(kElems % NKK == 0, "score slices");
+  // issue_kb >= 0: the tile at key issue_kb is loaded into buffer issue_buf behind the first
+  // k-step's MFMAs
   auto mfma_tile = [&](const unsigned char *tile, f32x16 (&cur)[NMT], const f32x16 (&prev)[NMT],
-                       auto with_prev) -> float {
+                       auto with_prev, int64_t issue_kb, int issue_buf) -> float {
     bf16x8 bf[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
@@ -644,6 +648,8 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
       for (int m = 0; m < NMT; ++m) cur[m] = mfma32(qa[m][kk], bf[kk], kk == 0 ? f32x16{} : cur[m]);
+      if (kk == 0 && issue_kb >= 0)
+        loads.issue(tile_lds + issue_buf * C::kTileBytes, k, issue_kb, last, wave);
       if constexpr (decltype(with_prev)::value) {
 #pragma unroll
         for (int j = 0; j < kSlice; j += 2) {
@@ -681,65 +687,92 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     }
   };
 
+  // Compaction of every row far enough above K.  Every wave calls it in the same step (the
+  // flag it follows was written by wave 0 in the previous step), after its MFMAs and before its
+  // appends, so the counts are stable while it runs; it ends with a barrier.
+  auto compact_rows = [&]() __attribute__((always_inline)) {
+    const int mine = __builtin_amdgcn_readfirstlane(sm.cnt[row]);
+    if (half == 0 && mine > (C::kCap + K) / 2) {
+      int n = mine;
+      uint32_t tau = my_tau;
+      bool has = prune_candidates(ck, cp, sm.hist[row], n, K, my_has_tau, tau);
+      if (n > C::kCap - 3 * kTileKeys) {  // too many ties to make room: exact selection
+        // exactly K kept, all at or above the K-th key kth (> the old threshold); a later key
+        // equal to kth loses the tie, but the threshold kth - 1 keeps every kept key above it
+        const uint32_t kth = select_exact(ck, cp, sm.hist[row], n, K, start, t);
+        if (kth > 0u) {
+          tau = kth - 1u;
+          has = true;
+        }
+      }
+      if (lane == 0) {
+        sm.tau[row] = tau;
+        sm.has_tau[row] = has ? 1 : 0;
+        sm.cnt[row] = n;
+      }
+    }
+    lds_barrier();  // new thresholds and counts are visible
+    my_has_tau = __builtin_amdgcn_readfirstlane(sm.has_tau[row]) != 0;
+    my_tau = __builtin_amdgcn_readfirstlane(sm.tau[row]);
+  };
+  // Wave 0 decides whether the next step compacts.  The counts it reads hold every append up to
+  // the previous step and perhaps some of this step's; until that compaction this step and the
+  // next one append at most two tiles per row, hence the margin of three tiles.  Every row far
+  // enough above K is compacted in the same round, so the rows of a group (whose counts grow
+  // alike) rarely stop the group more than once per round.
+  auto decide = [&](int slot) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const int4 cv = *reinterpret_cast<const int4 *>(sm.cnt);
+      const int mx = max(max(cv.x, cv.y), max(cv.z, cv.w));
+      if (lane == 0) sm.compact[slot] = mx > C::kCap - 3 * kTileKeys ? 1 : 0;
+    }
+  };
+
   // one tile: accumulate into `cur`, finish the pending tile held in `prev`
   int buf = 0;
+  int sidx = 0;            // step number
   bool have_prev = false;  // `prev` holds the accumulators of an unfinished tile
   int64_t key_prev = 0;
-  auto step = [&](int64_t kb, f32x16 (&cur)[NMT], f32x16 (&prev)[NMT]) {
+  auto step = [&](int64_t kb, f32x16 (&cur)[NMT], f32x16 (&prev)[NMT]) __attribute__((always_inline)) {
     if (kb > start) {
       if (kb + kTileKeys <= last) wait_vm<C::kLoadsPerWave>();  // the next tile may stay in flight
       else wait_tile();
       lds_barrier();  // this tile is complete everywhere; the previous one is free; every
                       // append made so far is visible
     }
-    if (kb + 2 * kTileKeys <= last) {
-      const int nb = buf >= C::kNBuf - 2 ? buf + 2 - C::kNBuf : buf + 2;
-      loads.issue(tile_lds + nb * C::kTileBytes, k, kb + 2 * kTileKeys, last, wave);
-    }
-
-    // ---- compaction, when a row may not have room for the keys of two tiles.  Every row far
-    // enough above K is compacted in the same round, so the rows of a group (whose counts grow
-    // alike) rarely stop the group more than once per round.
-    const int4 cv = *reinterpret_cast<const int4 *>(sm.cnt);
-    const int c0 = __builtin_amdgcn_readfirstlane(cv.x), c1 = __builtin_amdgcn_readfirstlane(cv.y);
-    const int c2 = __builtin_amdgcn_readfirstlane(cv.z), c3 = __builtin_amdgcn_readfirstlane(cv.w);
-    if (max(max(c0, c1), max(c2, c3)) > C::kCap - 2 * kTileKeys) {
-      const int mine = row == 0 ? c0 : row == 1 ? c1 : row == 2 ? c2 : c3;
-      if (half == 0 && mine > (C::kCap + K) / 2) {
-        int n = mine;
-        uint32_t tau = my_tau;
-        bool has = prune_candidates(ck, cp, sm.hist[row], n, K, my_has_tau, tau);
-        if (n > C::kCap - 3 * kTileKeys) {  // too many ties to make room: exact selection
-          // exactly K kept, all at or above the K-th key kth (> the old threshold); a later key
-          // equal to kth loses the tie, but the threshold kth - 1 keeps every kept key above it
-          const uint32_t kth = select_exact(ck, cp, sm.hist[row], n, K, start, t);
-          if (kth > 0u) {
-            tau = kth - 1u;
-            has = true;
-          }
-        }
-        if (lane == 0) {
-          sm.tau[row] = tau;
-          sm.has_tau[row] = has ? 1 : 0;
-          sm.cnt[row] = n;
-        }
-      }
-      lds_barrier();  // new thresholds and counts are visible
-      my_has_tau = __builtin_amdgcn_readfirstlane(sm.has_tau[row]) != 0;
-      my_tau = __builtin_amdgcn_readfirstlane(sm.tau[row]);
-    }
+    // this step's compaction flag; read now, used after the MFMAs
+    const int cflag = sm.compact[sidx & 1];
+    // the tile two ahead goes into the previous tile's buffer, issued behind the first MFMAs
+    const int64_t issue_kb = kb + 2 * kTileKeys <= last ? kb + 2 * kTileKeys : -1;
+    const int issue_buf = buf >= C::kNBuf - 2 ? buf + 2 - C::kNBuf : buf + 2;
 
     // ---- this wave's 32 keys of the tile
     const int64_t kbase = kb + half * 32;
     const bool do_cur = compute && kbase <= t;
     float sc = 0.0f;
-    if (do_cur && have_prev) sc = mfma_tile(sm.tile[buf], cur, prev, std::true_type{});
-    else if (do_cur) mfma_tile(sm.tile[buf], cur, prev, std::false_type{});
-    else if (have_prev) sc = score_only(prev);
+    if (do_cur && have_prev) {
+      sc = mfma_tile(sm.tile[buf], cur, prev, std::true_type{}, issue_kb, issue_buf);
+    } else if (do_cur) {
+      mfma_tile(sm.tile[buf], cur, prev, std::false_type{}, issue_kb, issue_buf);
+    } else {
+      if (issue_kb >= 0) loads.issue(tile_lds + issue_buf * C::kTileBytes, k, issue_kb, last, wave);
+      if (have_prev) sc = score_only(prev);
+    }
+    if (__builtin_amdgcn_readfirstlane(cflag)) compact_rows();
+    decide((sidx + 1) & 1);
     if (have_prev) append(sc, key_prev);
     have_prev = do_cur;
     key_prev = kbase + (lane & 31);
     buf = buf == C::kNBuf - 1 ? 0 : buf + 1;
+    ++sidx;
+  };
+  // the last tile: its append after the compaction (if any) decided in the last step
+  auto drain = [&](const f32x16 (&last_acc)[NMT]) __attribute__((always_inline)) {
+    float sc = 0.0f;
+    if (have_prev) sc = score_only(last_acc);
+    lds_barrier();  // every append of the key stream is visible; the flag is written
+    if (__builtin_amdgcn_readfirstlane(sm.compact[sidx & 1])) compact_rows();
+    if (have_prev) append(sc, key_prev);
   };
   f32x16 acc_a[NMT], acc_b[NMT];
   int64_t kb = start;
@@ -747,13 +780,13 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     step(kb, acc_a, acc_b);
     kb += kTileKeys;
     if (kb > last) {
-      if (have_prev) append(score_only(acc_a), key_prev);
+      drain(acc_a);
       break;
     }
     step(kb, acc_b, acc_a);
     kb += kTileKeys;
     if (kb > last) {
-      if (have_prev) append(score_only(acc_b), key_prev);
+      drain(acc_b);
       break;
     }
   }
