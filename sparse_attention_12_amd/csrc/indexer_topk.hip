@@ -635,6 +635,37 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   constexpr int kElems = NMT * 16;       // accumulator elements per lane
   constexpr int kSlice = kElems / NKK;   // of them finished per MFMA k-step
   static_assert(kElems % NKK == 0, "score slices");
+  // The two waves of a row share a SIMD.  The lower-half wave appends a tile's keys right
+  // after the MFMAs that finish their scores; the upper-half wave appends them one step later,
+  // before its MFMAs, so that one wave's appends overlap the other's MFMAs.  append_a tests the
+  // threshold and reserves the slots with an LDS atomic, append_b writes the entries.
+  float ap_sc = 0.0f;     // pending tile: this lane's partial score (half of the heads) ...
+  int64_t ap_key = 0;     // ... and key position
+  bool ap_on = false;     // a tile is pending
+  bool ap_pass = false;
+  uint64_t ap_mask = 0;
+  int ap_base = 0;
+  auto append_a = [&]() __attribute__((always_inline)) {
+    const float sc = ap_sc + swap_halves(ap_sc);
+    const uint32_t u = orderable(sc);
+    ap_sc = __uint_as_float(u);  // the key, for append_b
+    ap_pass = ap_on && lane < 32 && ap_key <= t && (!my_has_tau || u > my_tau);
+    ap_mask = __ballot(ap_pass);
+    ap_base = 0;
+    if (lane == 0 && ap_mask) ap_base = atomicAdd(&sm.cnt[row], __popcll(ap_mask));
+  };
+  auto append_b = [&]() __attribute__((always_inline)) {
+    if (ap_mask) {
+      const int base = __builtin_amdgcn_readfirstlane(ap_base);
+      if (ap_pass) {
+        const int o = base + __popcll(ap_mask & lt);
+        ck[o] = __float_as_uint(ap_sc);
+        cp[o] = static_cast<int32_t>(ap_key);
+      }
+    }
+    ap_on = false;
+  };
+
   // issue_kb >= 0: the tile at key issue_kb is loaded into buffer issue_buf behind the first
   // k-step's MFMAs
   auto mfma_tile = [&](const unsigned char *tile, f32x16 (&cur)[NMT], const f32x16 (&prev)[NMT],
@@ -669,22 +700,6 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
       s1 = fmaf(wv[(e + 1) >> 4][(e + 1) & 15], fmaxf(prev[(e + 1) >> 4][(e + 1) & 15], 0.0f), s1);
     }
     return s0 + s1;
-  };
-  auto append = [&](float sc, int64_t key) {
-    sc += swap_halves(sc);
-    const uint32_t u = orderable(sc);
-    const bool pass = lane < 32 && key <= t && (!my_has_tau || u > my_tau);
-    const uint64_t pm = __ballot(pass);
-    if (pm) {
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&sm.cnt[row], __popcll(pm));
-      base = __builtin_amdgcn_readfirstlane(base);
-      if (pass) {
-        const int o = base + __popcll(pm & lt);
-        ck[o] = u;
-        cp[o] = static_cast<int32_t>(key);
-      }
-    }
   };
 
   // Compaction of every row far enough above K.  Every wave calls it in the same step (the
@@ -746,6 +761,10 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     const int64_t issue_kb = kb + 2 * kTileKeys <= last ? kb + 2 * kTileKeys : -1;
     const int issue_buf = buf >= C::kNBuf - 2 ? buf + 2 - C::kNBuf : buf + 2;
 
+    if (half == 1) {  // the tile pending since the previous step
+      append_a();
+      append_b();
+    }
     // ---- this wave's 32 keys of the tile
     const int64_t kbase = kb + half * 32;
     const bool do_cur = compute && kbase <= t;
@@ -760,7 +779,13 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     }
     if (__builtin_amdgcn_readfirstlane(cflag)) compact_rows();
     decide((sidx + 1) & 1);
-    if (have_prev) append(sc, key_prev);
+    ap_sc = sc;  // prev's scores: appended now (lower half) or in the next step (upper half)
+    ap_key = key_prev;
+    ap_on = have_prev;
+    if (half == 0) {
+      append_a();
+      append_b();
+    }
     have_prev = do_cur;
     key_prev = kbase + (lane & 31);
     buf = buf == C::kNBuf - 1 ? 0 : buf + 1;
@@ -772,7 +797,13 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     if (have_prev) sc = score_only(last_acc);
     lds_barrier();  // every append of the key stream is visible; the flag is written
     if (__builtin_amdgcn_readfirstlane(sm.compact[sidx & 1])) compact_rows();
-    if (have_prev) append(sc, key_prev);
+    append_a();  // the upper half's pending tile
+    append_b();
+    ap_sc = sc;
+    ap_key = key_prev;
+    ap_on = have_prev;
+    append_a();
+    append_b();
   };
   f32x16 acc_a[NMT], acc_b[NMT];
   int64_t kb = start;
