@@ -707,29 +707,20 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_pair_kernel(
       for (int n = 0; n < 8; ++n) o[G][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): P of chunk c - 1 is ready
-      const bool load_next = c + 2 < nchunks;
-      uint32_t off[kLoadsW];
-      if (load_next) offsets(c + 2, off);
-      if (c == 0 && load_next) {
-#pragma unroll
-        for (int i = 0; i < kLoadsW; ++i) load(c + 2, i, off);
-      }
+      // tile c + 2 first: its issue (ring reads, address arithmetic) runs while the S waves
+      // start their MFMAs, and the MFMAs below overlap the S waves' softmax
+      if (c + 2 < nchunks) issue(c + 2);
       if (c > 0) {
         const int b = (c - 1) & 1;
         const unsigned char *tile = smem + ((c - 1) % kRoleNBuf) * TL::kBytes;
         bf16x8 pb[4];
 #pragma unroll
         for (int G = 0; G < 4; ++G) pb[G] = pbuf[(b * 4 + G) * 64 + lane];
-        static_assert(kLoadsW <= 16, "two loads per channel tile at most");
         bf16x8 va = fr.v_frag(tile, 8 * qq);
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
           bf16x8 vn = va;
           if (n + 1 < 8) vn = fr.v_frag(tile, 8 * qq + n + 1);
-          if (load_next) {
-            if (n < kLoadsW) load(c + 2, n, off);
-            if (n + 8 < kLoadsW) load(c + 2, n + 8, off);
-          }
 #pragma unroll
           for (int G = 0; G < 4; ++G) o[G][n] = mfma16(va, pb[G], o[G][n]);
           va = vn;
