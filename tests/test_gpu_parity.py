@@ -251,6 +251,35 @@ def test_fwd_rows_with_late_dominant_logits(H):
     checks.assert_close("dkv", _np(dkv), rdkv, checks.ATOL_OUT)
 
 
+@pytest.mark.parametrize("rows_per_pass", [17, 1])
+def test_bwd_passes_over_two_staging_buffers(rows_per_pass):
+    """A workspace that holds only a few query rows: the backward runs in passes over two
+    staging buffers, each pass's key-gradient reduction on the library's helper stream while
+    the next pass computes.  dq must equal the one-pass result exactly (rows are independent),
+    dkv up to summation order, and both must match the oracle."""
+    dsa = _dsa()
+    T, H, D, K = 150, 64, 576, 96
+    g = torch.Generator().manual_seed(31)
+    q = (torch.randn((T, H, D), generator=g) * 0.5).to(torch.bfloat16)
+    kv = (torch.randn((T, D), generator=g) * 0.5).to(torch.bfloat16)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    idx = _random_indices(T, T, K, 80, seed=32, minus_one_frac=0.1)
+    scale = 1.0 / math.sqrt(D)
+    qd, kvd, dd, idx_t = q.to(dev), kv.to(dev), dout.to(dev), torch.from_numpy(idx).to(dev)
+    out, lse = dsa.sparse_mla_fwd(qd, kvd, idx_t, scale)
+    dq1, dkv1 = dsa.sparse_mla_bwd(qd, kvd, idx_t, out, lse, dd, scale)
+    ws = torch.empty(dsa.bwd_workspace_bytes(T, T, H, D, K, rows_per_pass), dtype=torch.uint8,
+                     device=dev)
+    assert ws.numel() < dsa.bwd_workspace_bytes(T, T, H, D, K, 0)
+    dq2, dkv2 = dsa.sparse_mla_bwd(qd, kvd, idx_t, out, lse, dd, scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2)
+    assert (dkv1 - dkv2).abs().max().item() <= 1e-4
+    rdq, rdkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, scale)
+    checks.assert_close("dq", _np(dq2.float()), rdq, checks.ATOL_OUT)
+    checks.assert_close("dkv", _np(dkv2), rdkv, checks.ATOL_OUT)
+
+
 def test_tiny_workload_end_to_end():
     """Tiny workload: indexer (bit-exact) -> forward -> backward vs the oracle."""
     dsa = _dsa()
