@@ -8,10 +8,11 @@
 //
 // Kernels, for query rows processed in passes of R rows (R as large as the caller's workspace
 // allows):
-//   delta  : Delta[t,h] = sum_c dO[t,h,c] O[t,h,c]          (streaming, one wave per (t,h))
 //   rows   : one work group per query row, in two phases (layout of the waves below).  Both
 //            recompute S^T and dP^T per 32-slot chunk of gathered latent rows; the dq phase
-//            then forms dq = scale dZ . rows, the contribution phase C = scale dZ^T . q +
+//            first forms Delta[t,h] = sum_c dO[t,h,c] O[t,h,c] from the forward output (kept
+//            in the workspace for the second phase), then dq = scale dZ . rows; the
+//            contribution phase forms C = scale dZ^T . q +
 //            P^T . dO for every (query, slot) pair and stores C to a staging buffer (16-bit
 //            block floating point, see below).
 //   count / scan / fill : a counting sort of the pass's (query, slot) pairs by latent row.
@@ -59,25 +60,6 @@ __device__ __forceinline__ f32x4 unpack_m16x4(const u32x2 &m, float f) {
 }
 
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restrict__ out,
-                                                        const uint16_t *__restrict__ dout,
-                                                        int64_t rows, float *__restrict__ delta) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const u32x4 a = *reinterpret_cast<const u32x4 *>(out + r * kDv + lane * 8);
-  const u32x4 b = *reinterpret_cast<const u32x4 *>(dout + r * kDv + lane * 8);
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), s);
-    s = fmaf(__uint_as_float(a[i] & 0xFFFF0000u), __uint_as_float(b[i] & 0xFFFF0000u), s);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (lane == 0) delta[r] = s;
-}
-
 __global__ void fill_zero_kernel(float *__restrict__ p, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -171,10 +153,14 @@ template <int DQK>
 struct SdpHead {
   bf16x8 qf[DQK / 32], df[kDv / 32];
   float lse2, dlt;
-  __device__ __forceinline__ void load(const uint16_t *__restrict__ q,
-                                       const uint16_t *__restrict__ dout,
-                                       const float *__restrict__ lse,
-                                       const float *__restrict__ delta, int H, int64_t t, int h) {
+  // q and dO blocks of head h from global memory, its lse, and Delta = dO . O computed from the
+  // forward output (fp32 sums over the lane's eight channels of each block, then over the four
+  // lane groups).
+  __device__ __forceinline__ void load_delta_from_out(const uint16_t *__restrict__ q,
+                                                      const uint16_t *__restrict__ dout,
+                                                      const uint16_t *__restrict__ out,
+                                                      const float *__restrict__ lse, int H,
+                                                      int64_t t, int h) {
     const int g = __lane_id() >> 4;
     const bool hok = h < H;
 #pragma unroll
@@ -183,13 +169,27 @@ struct SdpHead {
       if (hok) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
       qf[ks] = as_bf16x8(v);
     }
+    float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < kDv / 32; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hok) v = *reinterpret_cast<const u32x4 *>(dout + ((t * H + h) * kDv + ks * 32 + g * 8));
+      u32x4 v = {0u, 0u, 0u, 0u}, o = {0u, 0u, 0u, 0u};
+      if (hok) {
+        v = *reinterpret_cast<const u32x4 *>(dout + ((t * H + h) * kDv + ks * 32 + g * 8));
+        o = *reinterpret_cast<const u32x4 *>(out + ((t * H + h) * kDv + ks * 32 + g * 8));
+      }
       df[ks] = as_bf16x8(v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d0 = fmaf(__uint_as_float(v[i] << 16), __uint_as_float(o[i] << 16), d0);
+        d1 = fmaf(__uint_as_float(v[i] & 0xFFFF0000u), __uint_as_float(o[i] & 0xFFFF0000u), d1);
+      }
     }
-    load_scalars(lse, delta, H, t, h);
+    float d = d0 + d1;
+    d += __shfl_xor(d, 16, 64);
+    d += __shfl_xor(d, 32, 64);
+    dlt = d;
+    const float l0 = hok ? lse[t * H + h] : -INFINITY;
+    lse2 = l0 == -INFINITY ? INFINITY : l0 * kLog2e;  // empty row or padded head: P = 0
   }
   __device__ __forceinline__ void load_scalars(const float *__restrict__ lse,
                                                const float *__restrict__ delta, int H, int64_t t,
@@ -266,7 +266,7 @@ template <int DQK>
 __device__ __forceinline__ void bwd_dq_row(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
-    const float *__restrict__ lse, const float *__restrict__ delta,
+    const uint16_t *__restrict__ out, const float *__restrict__ lse, float *__restrict__ delta,
     const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
     uint16_t *__restrict__ dq, int64_t t, unsigned char *smem) {
   using TL = Tile<DQK>;
@@ -287,7 +287,9 @@ __device__ __forceinline__ void bwd_dq_row(
     SlotRing sr;  // wave 0 keeps the slot-index ring filled
     if (wave == 0) sr.start(irow, lim, nchunks, ring);
     SdpHead<DQK> hd;
-    hd.load(q, dout, lse, delta, H, t, G * 16 + hl);
+    hd.load_delta_from_out(q, dout, out, lse, H, t, G * 16 + hl);
+    // Delta of the row's heads, for the contribution phase
+    if (g == 0 && G * 16 + hl < H) delta[t * H + G * 16 + hl] = hd.dlt;
     __syncthreads();  // S0: indices of the first tiles are in the ring
     __syncthreads();  // S1: the first tiles are loaded
     hd.settle_all();  // see settle()
@@ -601,15 +603,15 @@ template <int DQK>
 __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
-    const float *__restrict__ lse, const float *__restrict__ delta,
+    const uint16_t *__restrict__ out, const float *__restrict__ lse, float *__restrict__ delta,
     const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
     uint16_t *__restrict__ dq, uint32_t *__restrict__ stage, int64_t row0) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t i = blockIdx.x;
   const int64_t t = row0 + i;
-  bwd_dq_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2, dq, t,
-                  smem);
-  __syncthreads();  // every wave is done with the dq phase's LDS
+  bwd_dq_row<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, H, K, scale, scale_log2, dq,
+                  t, smem);
+  __syncthreads();  // every wave is done with the dq phase's LDS; the row's Delta is stored
   bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2,
                        stage + i * K * kStageWords<DQK>, t, smem);
 }
@@ -759,7 +761,8 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const int32_t *__restr
 
 template <int DQK>
 hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
-                       const int32_t *topk_length, const float *lse, const float *delta,
+                       const int32_t *topk_length, const uint16_t *out, const float *lse,
+                       float *delta,
                        const uint16_t *dout, int64_t row0, int64_t rows, int32_t H, int32_t K,
                        float scale, uint16_t *dq, uint32_t *stage, hipStream_t s) {
   const size_t smem = RowSmem<DQK>::bytes(K);
@@ -769,7 +772,7 @@ hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                                      static_cast<int>(smem));
   if (e != hipSuccess) return e;
   DSA_LAUNCH("sparse_mla_bwd_rows", kern, dim3(static_cast<unsigned>(rows)),
-             dim3(kRowWaves * 64), smem, s, q, kv, idx, topk_length, lse, delta, dout, H, K,
+             dim3(kRowWaves * 64), smem, s, q, kv, idx, topk_length, out, lse, delta, dout, H, K,
              scale, scale * kLog2e, dq, stage, row0);
   return hipGetLastError();
 }
@@ -826,7 +829,8 @@ hipError_t bwd_streams(BwdStreams *&out) {
 
 template <int DQK>
 hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
-                         const int32_t *topk_length, const float *lse, const float *delta,
+                         const int32_t *topk_length, const uint16_t *out, const float *lse,
+                         float *delta,
                          const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H, int32_t K,
                          float scale, uint16_t *dq, float *dkv, const BwdWorkspace &ws,
                          hipStream_t s) {
@@ -835,7 +839,7 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
   if (ws.nbuf == 1) {  // every pass in order on the caller's stream
     for (int64_t r0 = 0; e == hipSuccess && r0 < T_q; r0 += R) {
       const int64_t n = std::min<int64_t>(R, T_q - r0);
-      e = launch_rows<DQK>(q, kv, idx, topk_length, lse, delta, dout, r0, n, H, K, scale, dq,
+      e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, r0, n, H, K, scale, dq,
                            ws.buf[0].stage, s);
       if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[0], s);
       if (e == hipSuccess) e = launch_reduce<DQK>(T_kv, ws.buf[0], dkv, s);
@@ -856,7 +860,7 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
     const int64_t n = std::min<int64_t>(R, T_q - r0);
     const int b = p & 1;
     if (p >= 2 && (e = hipStreamWaitEvent(s, bs->red_done[b], 0)) != hipSuccess) break;
-    e = launch_rows<DQK>(q, kv, idx, topk_length, lse, delta, dout, r0, n, H, K, scale, dq,
+    e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, r0, n, H, K, scale, dq,
                          ws.buf[b].stage, s);
     if (e == hipSuccess) e = hipEventRecord(bs->rows_done[b], s);
     if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[b], bs->s2);
@@ -885,17 +889,14 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
                        dkv, n);
   }
   if (T_q == 0) return hipGetLastError();
-  const int64_t rows = T_q * H;
-  DSA_LAUNCH("sparse_mla_bwd_delta", bwd_delta_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0,
-                     s, out, dout, rows, ws.delta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (D_qk == 576)
-    return launch_passes<576>(q, kv, idx, topk_length, lse, ws.delta, dout, T_q, T_kv, H, K,
-                              scale, dq, dkv, ws, s);
+    return launch_passes<576>(q, kv, idx, topk_length, out, lse, ws.delta, dout, T_q, T_kv, H,
+                              K, scale, dq, dkv, ws, s);
   if (D_qk == 512)
-    return launch_passes<512>(q, kv, idx, topk_length, lse, ws.delta, dout, T_q, T_kv, H, K,
-                              scale, dq, dkv, ws, s);
+    return launch_passes<512>(q, kv, idx, topk_length, out, lse, ws.delta, dout, T_q, T_kv, H,
+                              K, scale, dq, dkv, ws, s);
   return hipErrorInvalidValue;
 }
 
