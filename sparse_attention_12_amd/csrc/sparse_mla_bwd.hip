@@ -15,7 +15,8 @@
 //            contribution phase forms C = scale dZ^T . q +
 //            P^T . dO for every (query, slot) pair and stores C to a staging buffer (16-bit
 //            block floating point, see below).
-//   count / scan / fill : a counting sort of the pass's (query, slot) pairs by latent row.
+//   scan / fill : a counting sort of the pass's (query, slot) pairs by latent row (the rows
+//            launch has counted them).
 //   reduce : one work group per latent row adds up its staged contributions and adds the sum
 //            to dkv (every row has a single owner, so no atomics touch dkv).
 // Compared with fp32 atomics on dkv (bounded by the L2 atomic units at about one 4-byte add
@@ -371,7 +372,7 @@ __device__ __forceinline__ void bwd_contrib_row(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
     const float *__restrict__ lse, const float *__restrict__ delta,
     const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
-    uint32_t *__restrict__ stage, int64_t t, unsigned char *smem) {
+    uint32_t *__restrict__ stage, int32_t *__restrict__ cnt, int64_t t, unsigned char *smem) {
   using TL = Tile<DQK>;
   using SM = RowSmem<DQK>;
   constexpr int kNTq = DQK / 64;  // channel tiles per quarter (9 or 8)
@@ -414,7 +415,9 @@ __device__ __forceinline__ void bwd_contrib_row(
     const int e = threadIdx.x + j * 512, hh = e / (DQK / 8), col = (e % (DQK / 8)) * 8;
     *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kQStride + col]) = qv[j];
   }
-  // dO and the slot rows (up to a whole number of tiles; the list lies outside the staging area)
+  // dO and the slot rows (up to a whole number of tiles; the list lies outside the staging area);
+  // each valid slot also counts one contribution for its latent row (the counting sort's first
+  // step: the atomics need no result and complete while the phase runs)
   auto store_o_rows = [&]() {
 #pragma unroll
     for (int j = 0; j < kOV; ++j) {
@@ -425,6 +428,7 @@ __device__ __forceinline__ void bwd_contrib_row(
     for (int j = 0; j < kIV; ++j) {
       const int e = threadIdx.x + j * 512;
       if (e < nchunks * kSlots) slot_rows[e] = iv[j];
+      if (iv[j] >= 0) atomicAdd(&cnt[iv[j]], 1);  // iv is -1 beyond the valid prefix
     }
   };
   __syncthreads();  // P0
@@ -605,7 +609,8 @@ __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
     const uint16_t *__restrict__ out, const float *__restrict__ lse, float *__restrict__ delta,
     const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
-    uint16_t *__restrict__ dq, uint32_t *__restrict__ stage, int64_t row0) {
+    uint16_t *__restrict__ dq, uint32_t *__restrict__ stage, int32_t *__restrict__ cnt,
+    int64_t row0) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t i = blockIdx.x;
   const int64_t t = row0 + i;
@@ -613,7 +618,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
                   t, smem);
   __syncthreads();  // every wave is done with the dq phase's LDS; the row's Delta is stored
   bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2,
-                       stage + i * K * kStageWords<DQK>, t, smem);
+                       stage + i * K * kStageWords<DQK>, cnt, t, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -633,14 +638,6 @@ __global__ void fill_zero_i32_kernel(int32_t *__restrict__ p, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t j = i; j < n; j += stride) p[j] = 0;
-}
-
-__global__ void pair_count_kernel(const int32_t *__restrict__ idx,
-                                  const int32_t *__restrict__ topk_length, int64_t row0,
-                                  int64_t rows, int K, int32_t *__restrict__ cnt) {
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  int32_t s;
-  if (pair_row(idx, topk_length, row0, rows, K, p, s)) atomicAdd(&cnt[s], 1);
 }
 
 // Exclusive scan of cnt[0, n) in place (cnt[n] receives the total) and cursor = the scan.
@@ -764,7 +761,7 @@ hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                        const int32_t *topk_length, const uint16_t *out, const float *lse,
                        float *delta,
                        const uint16_t *dout, int64_t row0, int64_t rows, int32_t H, int32_t K,
-                       float scale, uint16_t *dq, uint32_t *stage, hipStream_t s) {
+                       float scale, uint16_t *dq, const BwdPassBuffers &bb, hipStream_t s) {
   const size_t smem = RowSmem<DQK>::bytes(K);
   auto kern = bwd_rows_kernel<DQK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -773,20 +770,24 @@ hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   if (e != hipSuccess) return e;
   DSA_LAUNCH("sparse_mla_bwd_rows", kern, dim3(static_cast<unsigned>(rows)),
              dim3(kRowWaves * 64), smem, s, q, kv, idx, topk_length, out, lse, delta, dout, H, K,
-             scale, scale * kLog2e, dq, stage, row0);
+             scale, scale * kLog2e, dq, bb.stage, bb.off, row0);
   return hipGetLastError();
 }
 
-// Counting sort of pass [row0, row0 + rows) into buffer bb, on stream s.
+// Counting sort of pass [row0, row0 + rows) into buffer bb: the counts are cleared before the
+// rows launch (launch_count_zero), which counts each latent row's contributions; the scan and
+// the fill of the pair list follow it (launch_sort).
+hipError_t launch_count_zero(int64_t T_kv, const BwdPassBuffers &bb, hipStream_t s) {
+  const unsigned zb = static_cast<unsigned>(std::min<int64_t>((T_kv + 256) / 256, 65536));
+  DSA_LAUNCH("pair_zero", fill_zero_i32_kernel, dim3(zb), dim3(256), 0, s, bb.off, T_kv + 1);
+  return hipGetLastError();
+}
+
 hipError_t launch_sort(const int32_t *idx, const int32_t *topk_length, int64_t row0,
                        int64_t rows, int64_t T_kv, int32_t K, const BwdPassBuffers &bb,
                        hipStream_t s) {
   const int64_t pairs = rows * K;
   const unsigned pb = static_cast<unsigned>((pairs + 255) / 256);
-  const unsigned zb = static_cast<unsigned>(std::min<int64_t>((T_kv + 256) / 256, 65536));
-  DSA_LAUNCH("pair_zero", fill_zero_i32_kernel, dim3(zb), dim3(256), 0, s, bb.off, T_kv + 1);
-  DSA_LAUNCH("pair_count", pair_count_kernel, dim3(pb), dim3(256), 0, s, idx, topk_length, row0,
-             rows, K, bb.off);
   DSA_LAUNCH("pair_scan", pair_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, bb.off,
              bb.cursor, T_kv);
   DSA_LAUNCH("pair_fill", pair_fill_kernel, dim3(pb), dim3(256), 0, s, idx, topk_length, row0,
@@ -839,16 +840,18 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
   if (ws.nbuf == 1) {  // every pass in order on the caller's stream
     for (int64_t r0 = 0; e == hipSuccess && r0 < T_q; r0 += R) {
       const int64_t n = std::min<int64_t>(R, T_q - r0);
-      e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, r0, n, H, K, scale, dq,
-                           ws.buf[0].stage, s);
+      e = launch_count_zero(T_kv, ws.buf[0], s);
+      if (e == hipSuccess)
+        e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, r0, n, H, K, scale,
+                             dq, ws.buf[0], s);
       if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[0], s);
       if (e == hipSuccess) e = launch_reduce<DQK>(T_kv, ws.buf[0], dkv, s);
     }
     return e;
   }
-  // Two buffers: pass p computes (rows launch) on the caller's stream into buffer p % 2; its
-  // counting sort and reduction run on the helper stream, the reduction once the rows launch
-  // has finished, while the caller's stream goes on with pass p + 1.  Pass p + 2 reuses the
+  // Two buffers: pass p clears its counts and computes (rows launch) on the caller's stream into
+  // buffer p % 2; once the rows launch has finished, the scan, the list fill and the reduction
+  // run on the helper stream while the caller's stream goes on with pass p + 1.  Pass p + 2 reuses the
   // buffer after pass p's reduction.  The helper stream forks from the caller's stream first
   // (so that it also joins a stream capture) and the caller's stream joins it at the end.
   BwdStreams *bs = nullptr;
@@ -860,11 +863,13 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
     const int64_t n = std::min<int64_t>(R, T_q - r0);
     const int b = p & 1;
     if (p >= 2 && (e = hipStreamWaitEvent(s, bs->red_done[b], 0)) != hipSuccess) break;
-    e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, r0, n, H, K, scale, dq,
-                         ws.buf[b].stage, s);
+    e = launch_count_zero(T_kv, ws.buf[b], s);
+    if (e == hipSuccess)
+      e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, r0, n, H, K, scale,
+                           dq, ws.buf[b], s);
     if (e == hipSuccess) e = hipEventRecord(bs->rows_done[b], s);
-    if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[b], bs->s2);
     if (e == hipSuccess) e = hipStreamWaitEvent(bs->s2, bs->rows_done[b], 0);
+    if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[b], bs->s2);
     if (e == hipSuccess) e = launch_reduce<DQK>(T_kv, ws.buf[b], dkv, bs->s2);
     if (e == hipSuccess) e = hipEventRecord(bs->red_done[b], bs->s2);
   }
