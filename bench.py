@@ -56,7 +56,7 @@ def parse():
 # Source files whose kernels each timed kernel runs (a counter summary is used only while
 # their contents are unchanged).
 KERNEL_SOURCES = {
-    "indexer_topk": ["indexer_topk.hip", "dsa_common.h"],
+    "indexer_topk": ["indexer_topk.hip", "tile.h", "dsa_common.h"],
     "sparse_mla_fwd": ["sparse_mla_fwd.hip", "tile.h", "dsa_common.h"],
     "sparse_mla_bwd_rows": ["sparse_mla_bwd.hip", "tile.h", "dsa_common.h", "dsa_internal.h"],
     "sparse_mla_bwd_reduce": ["sparse_mla_bwd.hip", "dsa_common.h", "dsa_internal.h"],
