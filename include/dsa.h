@@ -118,7 +118,8 @@ int dsa_prepare_thd_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, in
  *
  *   q_idx [T, H_i, D_i] bf16   k_idx [T, D_i] bf16   w [T, H_i] fp32
  *   idx   [T, K] int32 (out)   len [T] int32 (out)
- * Supported: 1 <= H_i <= 64, D_i in {64, 128}, 1 <= K <= 2048.
+ * Supported: 1 <= H_i <= 64, D_i in {64, 128}, 1 <= K <= 2048,
+ * T <= INT32_MAX - 4096 (DSA_ERR_INVALID_VALUE otherwise).
  * ------------------------------------------------------------------------ */
 size_t dsa_indexer_topk_workspace_size(int64_t T, int32_t H_i, int32_t D_i, int32_t K);
 int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,

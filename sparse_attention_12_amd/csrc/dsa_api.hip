@@ -205,6 +205,10 @@ int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *
                 DSA_MAX_INDEXER_TOPK);
   const int64_t T = md->T;
   if (T == 0) return DSA_OK;
+  // key positions are 32-bit inside the kernel, including a few tiles of look-ahead
+  if (T > INT32_MAX - 4096)
+    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: T=%lld exceeds %d", static_cast<long long>(T),
+                INT32_MAX - 4096);
   if (!q_idx || !k_idx || !w || !idx || !len)
     return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: NULL tensor pointer");
   if (!aligned16(q_idx) || !aligned16(k_idx))

@@ -16,8 +16,9 @@
 // SIMD, so one's VALU epilogue overlaps the other's MFMAs.
 //
 // Streaming top-k: each row owns a candidate buffer of (orderable score, key position) pairs in
-// LDS.  A key is appended (at a slot taken with an LDS atomic, so in no particular order) when
-// its score exceeds the row's threshold tau (initially none).  When a row nears capacity it is
+// LDS, filled as two stacks (one per wave of the row, counts kept in registers, so no atomics;
+// entries in no particular order).  A key is appended when its score exceeds the row's
+// threshold tau (initially none).  When a row nears capacity it is
 // pruned with one 256-bin counting pass: the bin holding the K-th largest score gives a new
 // tau that never exceeds the true K-th largest score, and every candidate at or below it is
 // dropped.  Keys arrive in ascending position order, so a later key equal to the K-th score
@@ -60,7 +61,8 @@ struct IndexerSmem {
   uint32_t cand_key[kRows][IndexerCfg<D>::kCap];
   int32_t cand_pos[kRows][IndexerCfg<D>::kCap];
   __align__(16) uint32_t hist[kRows][kBins];
-  __align__(16) int32_t cnt[kRows];  // candidates per row (appended with LDS atomics)
+  __align__(16) int32_t cnt[kRows];   // entries of the lower stack of each row
+  __align__(16) int32_t cntb[kRows];  // entries of the upper stack of each row
   uint32_t tau[kRows];                // per-row threshold: later keys enter only if above it
   int32_t has_tau[kRows];
   int32_t compact[2];  // compaction due in step i: compact[i & 1] (written by wave 0 in step i - 1)
@@ -552,22 +554,24 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   extern __shared__ __align__(16) unsigned char smem_raw[];
   IndexerSmem<D> &sm = *reinterpret_cast<IndexerSmem<D> *>(smem_raw);
 
+  // Positions are 32-bit: the host limits T to INT32_MAX - 4096, so no key position computed
+  // below (at most last + 4 tiles) overflows.
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = wave & (kRows - 1);  // waves w and w + 4 share a row (and a SIMD)
   const int half = wave >> 2;
-  const int64_t last = groups[blockIdx.x];
-  const int64_t start = seq_start[last];
-  const int64_t first = last - (kRows - 1) > start ? last - (kRows - 1) : start;
-  const int64_t t = first + row;
+  const int last = groups[blockIdx.x];
+  const int start = seq_start[last];
+  const int first = last - (kRows - 1) > start ? last - (kRows - 1) : start;
+  const int t = first + row;
   const bool row_ok = t <= last;
-  const int64_t L = row_ok ? t - start + 1 : 0;
+  const int L = row_ok ? t - start + 1 : 0;
   const bool compute = row_ok && L > K;
 
   if (row_ok && !compute && half == 0) {
-    int32_t *out = idx_out + t * K;
-    for (int j = lane; j < K; j += 64) out[j] = j < L ? static_cast<int32_t>(start + j) : -1;
-    if (lane == 0) len_out[t] = static_cast<int32_t>(L);
+    int32_t *out = idx_out + static_cast<int64_t>(t) * K;
+    for (int j = lane; j < K; j += 64) out[j] = j < L ? start + j : -1;
+    if (lane == 0) len_out[t] = L;
   }
   if (last - start + 1 <= K) return;  // every row of the group is a whole prefix (uniform)
 
@@ -577,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   KeyTileLoads<D> loads;
   loads.init(wave);
   loads.issue(tile_lds, k, start, last, wave);
-  if (start + kTileKeys <= last) loads.issue(tile_lds + C::kTileBytes, k, start + kTileKeys, last, wave);
+  if (last - start >= kTileKeys) loads.issue(tile_lds + C::kTileBytes, k, start + kTileKeys, last, wave);
 
   // ---- this row's query block (A operand) and head weights
   bf16x8 qa[NMT][NKK];
@@ -589,26 +593,34 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (compute && h < H)
-        v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * D + kk * 16 + (lane >> 5) * 8));
+        v = *reinterpret_cast<const u32x4 *>(
+            q + ((static_cast<int64_t>(t) * H + h) * D + kk * 16 + (lane >> 5) * 8));
       qa[m][kk] = as_bf16x8(v);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int hh = m * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-      wv[m][i] = (compute && hh < H) ? w[t * H + hh] : 0.0f;
+      wv[m][i] = (compute && hh < H) ? w[static_cast<int64_t>(t) * H + hh] : 0.0f;
     }
   }
   if (threadIdx.x < kRows) {
     sm.has_tau[threadIdx.x] = 0;
     sm.tau[threadIdx.x] = 0u;
     sm.cnt[threadIdx.x] = 0;
+    sm.cntb[threadIdx.x] = 0;
   }
   if (threadIdx.x < 2) sm.compact[threadIdx.x] = 0;
   uint32_t *ck = sm.cand_key[row];
   int32_t *cp = sm.cand_pos[row];
+  // The candidate buffer of a row is two stacks: the lower-half wave appends upward from entry
+  // 0, the upper-half wave downward from entry kCap - 1.  Each wave keeps its own count in a
+  // register (no atomics) and publishes it in sm.cnt / sm.cntb for the capacity decision; a
+  // compaction or the final selection first moves the upper stack down behind the lower one.
+  int my_n = 0;
   uint32_t my_tau = 0u;  // this row's threshold (wave-uniform copy)
   bool my_has_tau = false;
-  const uint64_t lt = lanemask_lt();
+  // threshold for the append test: keys of finite scores are > 0, so 0 admits every key
+  uint32_t tau_eff = 0u;
   // B-operand LDS offsets of this lane (key row half*32 + lane%32, dims kk*16 + (lane/32)*8)
   const int krow = half * 32 + (lane & 31);
   int boff[NKK];
@@ -637,31 +649,26 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   static_assert(kElems % NKK == 0, "score slices");
   // The two waves of a row share a SIMD.  The lower-half wave appends a tile's keys right
   // after the MFMAs that finish their scores; the upper-half wave appends them one step later,
-  // before its MFMAs, so that one wave's appends overlap the other's MFMAs.  append_a tests the
-  // threshold and reserves the slots with an LDS atomic, append_b writes the entries.
-  float ap_sc = 0.0f;     // pending tile: this lane's partial score (half of the heads) ...
-  int64_t ap_key = 0;     // ... and key position
-  bool ap_on = false;     // a tile is pending
-  bool ap_pass = false;
-  uint64_t ap_mask = 0;
-  int ap_base = 0;
-  auto append_a = [&]() __attribute__((always_inline)) {
-    const float sc = ap_sc + swap_halves(ap_sc);
-    const uint32_t u = orderable(sc);
-    ap_sc = __uint_as_float(u);  // the key, for append_b
-    ap_pass = ap_on && lane < 32 && ap_key <= t && (!my_has_tau || u > my_tau);
-    ap_mask = __ballot(ap_pass);
-    ap_base = 0;
-    if (lane == 0 && ap_mask) ap_base = atomicAdd(&sm.cnt[row], __popcll(ap_mask));
-  };
-  auto append_b = [&]() __attribute__((always_inline)) {
-    if (ap_mask) {
-      const int base = __builtin_amdgcn_readfirstlane(ap_base);
-      if (ap_pass) {
-        const int o = base + __popcll(ap_mask & lt);
-        ck[o] = __float_as_uint(ap_sc);
-        cp[o] = static_cast<int32_t>(ap_key);
+  // before its MFMAs, so that one wave's appends overlap the other's MFMAs.
+  float ap_sc = 0.0f;  // pending tile: this lane's partial score (half of the heads) ...
+  int ap_key = 0;      // ... and key position
+  bool ap_on = false;  // a tile is pending
+  auto append = [&]() __attribute__((always_inline)) {
+    // lanes l and l + 32 hold the two head halves of key l; lanes 0..31 finish the sum
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ap_sc),
+                                                     __float_as_uint(ap_sc), false, false);
+    const uint32_t u = orderable(ap_sc + __uint_as_float(sw[1]));
+    const bool pass = ap_on && lane < 32 && ap_key <= t && u > tau_eff;
+    const uint64_t m = __ballot(pass);
+    if (m) {
+      const int o = my_n + static_cast<int>(__builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      if (pass) {
+        const int e = half == 0 ? o : C::kCap - 1 - o;
+        ck[e] = u;
+        cp[e] = ap_key;
       }
+      my_n += __popcll(m);
+      if (lane == 0) (half == 0 ? sm.cnt : sm.cntb)[row] = my_n;
     }
     ap_on = false;
   };
@@ -669,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   // issue_kb >= 0: the tile at key issue_kb is loaded into buffer issue_buf behind the first
   // k-step's MFMAs
   auto mfma_tile = [&](const unsigned char *tile, f32x16 (&cur)[NMT], const f32x16 (&prev)[NMT],
-                       auto with_prev, int64_t issue_kb, int issue_buf) -> float {
+                       auto with_prev, int issue_kb, int issue_buf) -> float {
     bf16x8 bf[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
@@ -702,33 +709,56 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     return s0 + s1;
   };
 
+  // The lower-half wave moves the upper stack of its row down behind its own entries (the
+  // ranges cannot be overlapped destructively: the copy runs upward and its destination
+  // always lies below its source); returns the row's entry count.  Called between barriers.
+  auto merge_stacks = [&](int n_lo, int n_hi) -> int {
+    for (int j = lane; j < n_hi; j += 64) {
+      const uint32_t kv = ck[C::kCap - n_hi + j];
+      const int32_t pv = cp[C::kCap - n_hi + j];
+      wave_sync();
+      ck[n_lo + j] = kv;
+      cp[n_lo + j] = pv;
+    }
+    wave_sync();
+    return n_lo + n_hi;
+  };
+
   // Compaction of every row far enough above K.  Every wave calls it in the same step (the
   // flag it follows was written by wave 0 in the previous step), after its MFMAs and before its
-  // appends, so the counts are stable while it runs; it ends with a barrier.
+  // appends; the first barrier makes every append before it visible, the last one the new
+  // thresholds and counts.
   auto compact_rows = [&]() __attribute__((always_inline)) {
-    const int mine = __builtin_amdgcn_readfirstlane(sm.cnt[row]);
-    if (half == 0 && mine > (C::kCap + K) / 2) {
-      int n = mine;
-      uint32_t tau = my_tau;
-      bool has = prune_candidates(ck, cp, sm.hist[row], n, K, my_has_tau, tau);
-      if (n > C::kCap - 3 * kTileKeys) {  // too many ties to make room: exact selection
-        // exactly K kept, all at or above the K-th key kth (> the old threshold); a later key
-        // equal to kth loses the tie, but the threshold kth - 1 keeps every kept key above it
-        const uint32_t kth = select_exact(ck, cp, sm.hist[row], n, K, start, t);
-        if (kth > 0u) {
-          tau = kth - 1u;
-          has = true;
+    lds_barrier();
+    if (half == 0) {
+      const int n_hi = __builtin_amdgcn_readfirstlane(sm.cntb[row]);
+      if (my_n + n_hi > (C::kCap + K) / 2) {
+        int n = merge_stacks(my_n, n_hi);
+        uint32_t tau = my_tau;
+        bool has = prune_candidates(ck, cp, sm.hist[row], n, K, my_has_tau, tau);
+        if (n > C::kCap - 3 * kTileKeys) {  // too many ties to make room: exact selection
+          // exactly K kept, all at or above the K-th key kth (> the old threshold); a later key
+          // equal to kth loses the tie, but the threshold kth - 1 keeps every kept key above it
+          const uint32_t kth = select_exact(ck, cp, sm.hist[row], n, K, start, t);
+          if (kth > 0u) {
+            tau = kth - 1u;
+            has = true;
+          }
         }
-      }
-      if (lane == 0) {
-        sm.tau[row] = tau;
-        sm.has_tau[row] = has ? 1 : 0;
-        sm.cnt[row] = n;
+        my_n = n;
+        if (lane == 0) {
+          sm.tau[row] = tau;
+          sm.has_tau[row] = has ? 1 : 0;
+          sm.cnt[row] = n;
+          sm.cntb[row] = 0;
+        }
       }
     }
     lds_barrier();  // new thresholds and counts are visible
     my_has_tau = __builtin_amdgcn_readfirstlane(sm.has_tau[row]) != 0;
     my_tau = __builtin_amdgcn_readfirstlane(sm.tau[row]);
+    tau_eff = my_has_tau ? my_tau : 0u;
+    if (half == 1) my_n = __builtin_amdgcn_readfirstlane(sm.cntb[row]);
   };
   // Wave 0 decides whether the next step compacts.  The counts it reads hold every append up to
   // the previous step and perhaps some of this step's; until that compaction this step and the
@@ -737,8 +767,9 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   // alike) rarely stop the group more than once per round.
   auto decide = [&](int slot) __attribute__((always_inline)) {
     if (wave == 0) {
-      const int4 cv = *reinterpret_cast<const int4 *>(sm.cnt);
-      const int mx = max(max(cv.x, cv.y), max(cv.z, cv.w));
+      const int4 ca = *reinterpret_cast<const int4 *>(sm.cnt);
+      const int4 cb = *reinterpret_cast<const int4 *>(sm.cntb);
+      const int mx = max(max(ca.x + cb.x, ca.y + cb.y), max(ca.z + cb.z, ca.w + cb.w));
       if (lane == 0) sm.compact[slot] = mx > C::kCap - 3 * kTileKeys ? 1 : 0;
     }
   };
@@ -747,10 +778,10 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   int buf = 0;
   int sidx = 0;            // step number
   bool have_prev = false;  // `prev` holds the accumulators of an unfinished tile
-  int64_t key_prev = 0;
-  auto step = [&](int64_t kb, f32x16 (&cur)[NMT], f32x16 (&prev)[NMT]) __attribute__((always_inline)) {
+  int key_prev = 0;
+  auto step = [&](int kb, f32x16 (&cur)[NMT], f32x16 (&prev)[NMT]) __attribute__((always_inline)) {
     if (kb > start) {
-      if (kb + kTileKeys <= last) wait_vm<C::kLoadsPerWave>();  // the next tile may stay in flight
+      if (last - kb >= kTileKeys) wait_vm<C::kLoadsPerWave>();  // the next tile may stay in flight
       else wait_tile();
       lds_barrier();  // this tile is complete everywhere; the previous one is free; every
                       // append made so far is visible
@@ -758,15 +789,12 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     // this step's compaction flag; read now, used after the MFMAs
     const int cflag = sm.compact[sidx & 1];
     // the tile two ahead goes into the previous tile's buffer, issued behind the first MFMAs
-    const int64_t issue_kb = kb + 2 * kTileKeys <= last ? kb + 2 * kTileKeys : -1;
+    const int issue_kb = last - kb >= 2 * kTileKeys ? kb + 2 * kTileKeys : -1;
     const int issue_buf = buf >= C::kNBuf - 2 ? buf + 2 - C::kNBuf : buf + 2;
 
-    if (half == 1) {  // the tile pending since the previous step
-      append_a();
-      append_b();
-    }
+    if (half == 1) append();  // the tile pending since the previous step
     // ---- this wave's 32 keys of the tile
-    const int64_t kbase = kb + half * 32;
+    const int kbase = kb + half * 32;
     const bool do_cur = compute && kbase <= t;
     float sc = 0.0f;
     if (do_cur && have_prev) {
@@ -782,10 +810,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     ap_sc = sc;  // prev's scores: appended now (lower half) or in the next step (upper half)
     ap_key = key_prev;
     ap_on = have_prev;
-    if (half == 0) {
-      append_a();
-      append_b();
-    }
+    if (half == 0) append();
     have_prev = do_cur;
     key_prev = kbase + (lane & 31);
     buf = buf == C::kNBuf - 1 ? 0 : buf + 1;
@@ -797,16 +822,14 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     if (have_prev) sc = score_only(last_acc);
     lds_barrier();  // every append of the key stream is visible; the flag is written
     if (__builtin_amdgcn_readfirstlane(sm.compact[sidx & 1])) compact_rows();
-    append_a();  // the upper half's pending tile
-    append_b();
+    append();  // the upper half's pending tile
     ap_sc = sc;
     ap_key = key_prev;
     ap_on = have_prev;
-    append_a();
-    append_b();
+    append();
   };
   f32x16 acc_a[NMT], acc_b[NMT];
-  int64_t kb = start;
+  int kb = start;
   while (true) {  // two tiles per trip so that the accumulator sets alternate without copies
     step(kb, acc_a, acc_b);
     kb += kTileKeys;
@@ -828,8 +851,9 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     uint32_t *bm = reinterpret_cast<uint32_t *>(&sm.tile[0][0]) + row * 1024;
     uint32_t *sk = reinterpret_cast<uint32_t *>(&sm.tile[0][0]) + 4 * 1024 + row * 2 * kScratch;
     int32_t *sp = reinterpret_cast<int32_t *>(sk + kScratch);
-    select_and_write(ck, cp, sm.hist[row], __builtin_amdgcn_readfirstlane(sm.cnt[row]), K,
-                     my_has_tau, my_tau, start, t, bm, sk, sp, idx_out + t * K);
+    const int n = merge_stacks(my_n, __builtin_amdgcn_readfirstlane(sm.cntb[row]));
+    select_and_write(ck, cp, sm.hist[row], n, K, my_has_tau, my_tau, start, t, bm, sk, sp,
+                     idx_out + static_cast<int64_t>(t) * K);
     if (lane == 0) len_out[t] = K;
   }
 }
