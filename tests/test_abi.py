@@ -81,6 +81,11 @@ def test_argument_errors_without_device(dsa):
                                 None) == pkg.DSA_ERR_INVALID_VALUE
     assert dsa.dsa_indexer_topk(16, 16, 16, C.byref(md), 65, 128, 16, 16, 16, None, 0,
                                 None) == pkg.DSA_ERR_INVALID_VALUE
+    # key positions are 32-bit in the kernel: T is limited to INT32_MAX - 4096
+    md.T = (1 << 31) - 1 - 4095
+    assert dsa.dsa_indexer_topk(16, 16, 16, C.byref(md), 64, 128, 16, 16, 16, None, 0,
+                                None) == pkg.DSA_ERR_INVALID_VALUE and "exceeds" in _err(dsa)
+    md.T = 8
     # forward: width, value width, heads, K, scale, alignment
     args = dict(q=16, kv=16, idx=16, tl=None, Tq=4, Tkv=4, H=16, Dqk=576, Dv=512, K=8, sc=0.1,
                 out=16, lse=16, s=None)
