@@ -50,11 +50,12 @@ def lib():
         L.oracle_indexer_topk_rows.restype = C.c_int
         L.oracle_sparse_mla_fwd.argtypes = [u16p, u16p, i32p, C.c_void_p, C.c_int64, C.c_int64,
                                             C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
-                                            C.c_int64, C.c_int64, f64p, f64p]
+                                            C.c_void_p, C.c_int64, C.c_int64, f64p, f64p]
         L.oracle_sparse_mla_fwd.restype = C.c_int
         L.oracle_sparse_mla_bwd.argtypes = [u16p, u16p, i32p, C.c_void_p, u16p, C.c_int64,
                                             C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                            C.c_double, C.c_int64, C.c_int64, f64p, f64p]
+                                            C.c_double, C.c_void_p, C.c_int64, C.c_int64, f64p,
+                                            f64p, C.c_void_p]
         L.oracle_sparse_mla_bwd.restype = C.c_int
         _lib = L
     return _lib
@@ -154,8 +155,20 @@ def _opt_i32(x):
     return a, a.ctypes.data
 
 
-def sparse_mla_fwd(q, kv, idx, topk_length, scale: float, d_v: int, rows=None):
-    """Returns (out [n,H,Dv] f64, lse [n,H] f64) for query rows [r0, r1)."""
+def _opt_sink(sink, H):
+    """Per-head sink logits as a double array [H] (exact widening), or None."""
+    if sink is None:
+        return None, None
+    a = np.ascontiguousarray(np.asarray(
+        sink.detach().cpu().numpy() if hasattr(sink, "detach") else sink, np.float64).reshape(-1))
+    if a.shape[0] != H:
+        raise ValueError("sink must hold one logit per head")
+    return a, a.ctypes.data
+
+
+def sparse_mla_fwd(q, kv, idx, topk_length, scale: float, d_v: int, rows=None, sink=None):
+    """Returns (out [n,H,Dv] f64, lse [n,H] f64) for query rows [r0, r1); `sink` [H] adds one
+    zero-valued logit per head to the softmax denominator."""
     qa = _u16(q)
     kva = _u16(kv).reshape(kv.shape[0], -1)
     ia = _np(idx, np.int32).reshape(qa.shape[0], -1)
@@ -164,17 +177,19 @@ def sparse_mla_fwd(q, kv, idx, topk_length, scale: float, d_v: int, rows=None):
     Tkv = kva.shape[0]
     K = ia.shape[1]
     r0, r1 = (0, Tq) if rows is None else rows
+    sk, skp = _opt_sink(sink, H)
     out = np.zeros((r1 - r0, H, d_v), np.float64)
     lse = np.zeros((r1 - r0, H), np.float64)
     _check(lib().oracle_sparse_mla_fwd(qa.reshape(-1), kva.reshape(-1), ia.reshape(-1), tlp, Tq,
-                                       Tkv, H, Dqk, d_v, K, float(scale), r0, r1, out, lse),
+                                       Tkv, H, Dqk, d_v, K, float(scale), skp, r0, r1, out, lse),
            "sparse_mla_fwd")
-    del tl
+    del tl, sk
     return out, lse
 
 
-def sparse_mla_bwd(q, kv, idx, topk_length, dout, scale: float, rows=None, dkv=None):
-    """Returns (dq [n,H,Dqk] f64, dkv [T_kv,Dqk] f64) for query rows [r0, r1).
+def sparse_mla_bwd(q, kv, idx, topk_length, dout, scale: float, rows=None, dkv=None, sink=None):
+    """Returns (dq [n,H,Dqk] f64, dkv [T_kv,Dqk] f64) for query rows [r0, r1), and with a
+    `sink` [H] also dsink [H] f64 (the sink logits' gradient summed over those rows).
 
     dkv accumulates the contributions of the given rows only (pass ``dkv`` to
     keep accumulating into an existing buffer)."""
@@ -191,8 +206,14 @@ def sparse_mla_bwd(q, kv, idx, topk_length, dout, scale: float, rows=None, dkv=N
     dq = np.zeros((r1 - r0, H, Dqk), np.float64)
     if dkv is None:
         dkv = np.zeros((Tkv, Dqk), np.float64)
+    sk, skp = _opt_sink(sink, H)
+    dsink = np.zeros(H, np.float64) if sink is not None else None
     _check(lib().oracle_sparse_mla_bwd(qa.reshape(-1), kva.reshape(-1), ia.reshape(-1), tlp,
-                                       da.reshape(-1), Tq, Tkv, H, Dqk, Dv, K, float(scale), r0,
-                                       r1, dq, dkv), "sparse_mla_bwd")
-    del tl
-    return dq, dkv
+                                       da.reshape(-1), Tq, Tkv, H, Dqk, Dv, K, float(scale), skp,
+                                       r0, r1, dq, dkv,
+                                       None if dsink is None else dsink.ctypes.data),
+           "sparse_mla_bwd")
+    del tl, sk
+    if sink is None:
+        return dq, dkv
+    return dq, dkv, dsink

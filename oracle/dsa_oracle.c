@@ -213,17 +213,25 @@ static int64_t row_slots(const int32_t *idx, const int32_t *topk_length, int64_t
 /* Softmax statistics and output of one (t,h): logits z_j = scale *
  * <q[t,h,:Dqk], kv[s_j,:Dqk]>, lse = log sum_j exp(z_j) (natural log), and
  * out = sum_j exp(z_j - lse) * kv[s_j,:Dv].  An empty row gives out = 0 and
- * lse = -inf.  z receives the logits. */
+ * lse = -inf.  z receives the logits.
+ *
+ * Attention sink ([API] _pad_attention_heads pads a per-head sink [H] with
+ * the query heads; its arithmetic is not written on the pages).  Reading
+ * taken: the sink is one more logit `sink` per head whose value vector is
+ * zero, so it enters only the softmax denominator:
+ *   lse = log(sum_j exp(z_j) + exp(sink)),  out = sum_j exp(z_j - lse) kv[s_j,:Dv].
+ * With no valid slot, lse = sink and out = 0; sink = -inf is no sink. */
 static void attend_one(const uint16_t *q, const uint16_t *kv, const int32_t *slots, int64_t n,
                        int64_t t, int32_t h, int32_t H, int32_t Dqk, int32_t Dv, double scale,
-                       double *z, double *out, double *lse) {
+                       const double *sink, double *z, double *out, double *lse) {
   const uint16_t *qr = q + ((size_t)t * H + h) * Dqk;
+  const double sk = sink ? sink[h] : -INFINITY;
   for (int32_t c = 0; c < Dv; ++c) out[c] = 0.0;
   if (n == 0) {
-    *lse = -INFINITY;
+    *lse = sk;
     return;
   }
-  double m = -INFINITY;
+  double m = sk;
   for (int64_t j = 0; j < n; ++j) {
     const uint16_t *kr = kv + (size_t)slots[j] * Dqk;
     double dot = 0.0;
@@ -233,6 +241,7 @@ static void attend_one(const uint16_t *q, const uint16_t *kv, const int32_t *slo
   }
   double sum = 0.0;
   for (int64_t j = 0; j < n; ++j) sum += exp(z[j] - m);
+  if (sink) sum += exp(sk - m);
   *lse = m + log(sum);
   for (int64_t j = 0; j < n; ++j) {
     double p = exp(z[j] - *lse);
@@ -245,8 +254,8 @@ static void attend_one(const uint16_t *q, const uint16_t *kv, const int32_t *slo
  * lse is [(rows) x H], both double, row-relative. */
 int oracle_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                           const int32_t *topk_length, int64_t T_q, int64_t T_kv, int32_t H,
-                          int32_t Dqk, int32_t Dv, int32_t K, double scale, int64_t row_begin,
-                          int64_t row_end, double *out, double *lse) {
+                          int32_t Dqk, int32_t Dv, int32_t K, double scale, const double *sink,
+                          int64_t row_begin, int64_t row_end, double *out, double *lse) {
   if (H < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk || K < 1 || row_begin < 0 || row_end > T_q ||
       row_begin > row_end)
     return ORACLE_EINVAL;
@@ -270,7 +279,7 @@ int oracle_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *
       }
       for (int32_t h = 0; h < H; ++h) {
         size_t r = (size_t)(t - row_begin) * H + h;
-        attend_one(q, kv, slots, n, t, h, H, Dqk, Dv, scale, z, out + r * Dv, lse + r);
+        attend_one(q, kv, slots, n, t, h, H, Dqk, Dv, scale, sink, z, out + r * Dv, lse + r);
       }
     }
     free(slots);
@@ -291,14 +300,20 @@ int oracle_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *
  *   dkv[s_j,:Dv]  += P_j dO[t,h,:]
  * dq is [(rows) x H x Dqk] (row-relative); dkv is the full [T_kv x Dqk]
  * buffer and is accumulated into (the caller zeroes it).  dkv of a key row is
- * complete only when every query row that selects it is inside the range. */
+ * complete only when every query row that selects it is inside the range.
+ *
+ * With a sink (see attend_one), P_j and Delta use the sink's lse and output;
+ * the sink's own probability is P_s = exp(sink - lse) and its value is zero,
+ * so its logit gradient is P_s (0 - Delta):
+ *   dsink[h] += -exp(sink[h] - lse[t,h]) * Delta[t,h]     (summed over t)
+ * accumulated into dsink [H] (the caller zeroes it). */
 int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                           const int32_t *topk_length, const uint16_t *dout, int64_t T_q,
                           int64_t T_kv, int32_t H, int32_t Dqk, int32_t Dv, int32_t K,
-                          double scale, int64_t row_begin, int64_t row_end, double *dq,
-                          double *dkv) {
+                          double scale, const double *sink, int64_t row_begin, int64_t row_end,
+                          double *dq, double *dkv, double *dsink) {
   if (H < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk || K < 1 || row_begin < 0 || row_end > T_q ||
-      row_begin > row_end)
+      row_begin > row_end || (sink && !dsink))
     return ORACLE_EINVAL;
   int err = ORACLE_OK;
 #pragma omp parallel
@@ -306,13 +321,14 @@ int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *
     int32_t *slots = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
     double *z = (double *)malloc(sizeof(double) * (size_t)K);
     double *o = (double *)malloc(sizeof(double) * (size_t)Dv);
+    double *dsk = (double *)malloc(sizeof(double) * (size_t)H); /* this row's dsink terms */
     /* this row's contribution to dkv, one Dqk vector per valid slot */
     double *contrib = (double *)malloc(sizeof(double) * (size_t)K * Dqk);
     /* rows add their contributions into dkv in row order, so dkv does not
      * depend on the thread count or scheduling */
 #pragma omp for schedule(dynamic, 1) ordered
     for (int64_t t = row_begin; t < row_end; ++t) {
-      int64_t n = (!slots || !z || !o || !contrib)
+      int64_t n = (!slots || !z || !o || !contrib || !dsk)
                       ? -2 : row_slots(idx, topk_length, t, K, T_kv, slots);
       if (n < 0) {
 #pragma omp atomic write
@@ -324,13 +340,14 @@ int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *
       memset(contrib, 0, sizeof(double) * (size_t)n * Dqk);
       for (int32_t h = 0; h < H; ++h) {
         double lse;
-        attend_one(q, kv, slots, n, t, h, H, Dqk, Dv, scale, z, o, &lse);
+        attend_one(q, kv, slots, n, t, h, H, Dqk, Dv, scale, sink, z, o, &lse);
         const uint16_t *qr = q + ((size_t)t * H + h) * Dqk;
         const uint16_t *dor = dout + ((size_t)t * H + h) * Dv;
         double *dqr = dq + ((size_t)(t - row_begin) * H + h) * Dqk;
         for (int32_t d = 0; d < Dqk; ++d) dqr[d] = 0.0;
         double delta = 0.0;
         for (int32_t c = 0; c < Dv; ++c) delta += bf16_to_double(dor[c]) * o[c];
+        dsk[h] = sink ? -exp(sink[h] - lse) * delta : 0.0;
         for (int64_t j = 0; j < n; ++j) {
           const uint16_t *kr = kv + (size_t)slots[j] * Dqk;
           double p = exp(z[j] - lse);
@@ -346,16 +363,21 @@ int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *
         }
       }
 #pragma omp ordered
-      for (int64_t j = 0; j < n; ++j) {
-        double *dst = dkv + (size_t)slots[j] * Dqk;
-        const double *cj = contrib + (size_t)j * Dqk;
-        for (int32_t d = 0; d < Dqk; ++d) dst[d] += cj[d];
+      {
+        for (int64_t j = 0; j < n; ++j) {
+          double *dst = dkv + (size_t)slots[j] * Dqk;
+          const double *cj = contrib + (size_t)j * Dqk;
+          for (int32_t d = 0; d < Dqk; ++d) dst[d] += cj[d];
+        }
+        if (sink)
+          for (int32_t h = 0; h < H; ++h) dsink[h] += dsk[h];
       }
     }
     free(slots);
     free(z);
     free(o);
     free(contrib);
+    free(dsk);
   }
   return err;
 }

@@ -81,3 +81,40 @@ def dense_attention(q, kv, cu, scale: float, d_v: int, dout=None):
         res["dq"] = qd.grad.numpy()
         res["dkv"] = kvd.grad.numpy()
     return res
+
+
+def dense_attention_sink(q, kv, cu, scale: float, d_v: int, sink, dout=None):
+    """Dense block-causal attention with a per-head sink, in float64 via torch SDPA.
+
+    The sink is realised as one extra key whose key and value vectors are zero, so its logit
+    scale * q . 0 = 0 is lifted to sink[h] by an additive mask, and it adds nothing to the
+    output.  Returns out, lse and, if dout is given, dq, dkv and dsink (autograd)."""
+    grad = dout is not None
+    qd = q.detach().to(torch.float64).clone().requires_grad_(grad)
+    kvd = kv.detach().to(torch.float64).clone().requires_grad_(grad)
+    sk = torch.as_tensor(np.asarray(sink, np.float64)).clone().requires_grad_(grad)
+    T, H, D = qd.shape
+    start = torch.as_tensor(segment_of(np.asarray(cu), T))
+    t = torch.arange(T)
+    causal = (t[None, :] >= start[:, None]) & (t[None, :] <= t[:, None])
+    zero_t = torch.zeros((T, T), dtype=torch.float64)
+    real = zero_t.masked_fill(~causal, float("-inf"))                  # [T, T]
+    bias = torch.cat([real.unsqueeze(0).expand(H, T, T),
+                      sk[:, None, None].expand(H, T, 1)], dim=2)       # [H, T, T+1]
+    keys = torch.cat([kvd, torch.zeros((1, D), dtype=torch.float64)], dim=0)
+    vals = torch.cat([kvd[:, :d_v], torch.zeros((1, d_v), dtype=torch.float64)], dim=0)
+    qh = qd.permute(1, 0, 2).unsqueeze(0)
+    kh = keys.unsqueeze(0).unsqueeze(0).expand(1, H, T + 1, D)
+    vh = vals.unsqueeze(0).unsqueeze(0).expand(1, H, T + 1, d_v)
+    out = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=bias.unsqueeze(0),
+                                                           scale=scale)
+    out = out.squeeze(0).permute(1, 0, 2)
+    logits = torch.einsum("thd,sd->hts", qd.detach(), keys.detach()) * scale + bias.detach()
+    lse = torch.logsumexp(logits, dim=-1).T
+    res = dict(out=out.detach().numpy(), lse=lse.numpy())
+    if grad:
+        out.backward(dout.detach().to(torch.float64))
+        res["dq"] = qd.grad.numpy()
+        res["dkv"] = kvd.grad.numpy()
+        res["dsink"] = sk.grad.numpy()
+    return res

@@ -353,3 +353,69 @@ def test_kpool_generator_structure():
             assert row[-3:].tolist() == [t - 2, t - 1, t]
             head = row[:-3]
             assert (np.diff(head) > 0).all() and head.max() <= t - 3 and head.min() >= 0
+
+
+# ---- attention sink: one zero-valued logit per head in the softmax denominator ([API]
+# _pad_attention_heads pads a sink [H] with the heads; the arithmetic is the reading taken)
+
+@pytest.mark.parametrize("cu,H,Dqk,Dv", [([0, 40], 4, 576, 512), ([0, 20, 33, 64], 3, 64, 48)])
+def test_sink_equals_dense_with_a_zero_valued_extra_key(cu, H, Dqk, Dv):
+    """Sink == dense block-causal attention over one more key (zero key and value vectors,
+    logit lifted to sink[h] by an additive mask): out, lse, dq, dkv and dsink (autograd)."""
+    T = cu[-1]
+    g = torch.Generator().manual_seed(7 + T)
+    q = (torch.randn((T, H, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    kv = (torch.randn((T, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    dout = torch.randn((T, H, Dv), generator=g).to(torch.bfloat16)
+    sink = torch.randn(H, generator=g).numpy().astype(np.float64)
+    sink[0] = 6.0                     # a sink that dominates most rows
+    scale = 1 / math.sqrt(Dqk)
+    idx = _all_causal_indices(cu, max(np.diff(cu)) + 2)
+    out, lse = oracle.sparse_mla_fwd(q, kv, idx, None, scale, Dv, sink=sink)
+    ref = pins.dense_attention_sink(q, kv, cu, scale, Dv, sink, dout=dout)
+    np.testing.assert_allclose(out, ref["out"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, ref["lse"], rtol=1e-12, atol=1e-12)
+    dq, dkv, dsink = oracle.sparse_mla_bwd(q, kv, idx, None, dout, scale, sink=sink)
+    np.testing.assert_allclose(dq, ref["dq"], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dkv, ref["dkv"], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dsink, ref["dsink"], rtol=1e-10, atol=1e-11)
+
+
+def test_sink_single_slot_closed_form_and_identities():
+    """One valid slot: out = kv[s] e^z / (e^z + e^sink), lse = logaddexp(z, sink).  Any row:
+    lse' = logaddexp(lse, sink) and out' = out exp(lse - lse') against the sink-free result;
+    sink = -inf is exactly no sink; an empty row gives lse = sink, out = 0 and no gradient."""
+    inp = gen.attention_inputs(1, cu_seqlens=[0, 8])
+    q, kv, dout, scale = inp["q"], inp["kv"], inp["dout"], inp["scale"]
+    H = q.shape[1]
+    sink = np.linspace(-3.0, 3.0, H)
+    idx = np.full((8, 4), -1, np.int32)
+    idx[:, 1] = np.arange(8)[::-1]
+    out, lse = oracle.sparse_mla_fwd(q, kv, idx, None, scale, 512, sink=sink)
+    qd, kvd = pins.bf16_to_f64(q), pins.bf16_to_f64(kv)
+    for t in range(8):
+        s = 7 - t
+        z = scale * qd[t] @ kvd[s]                                      # [H]
+        np.testing.assert_allclose(lse[t], np.logaddexp(z, sink), rtol=1e-13, atol=1e-13)
+        w = 1.0 / (1.0 + np.exp(sink - z))
+        np.testing.assert_allclose(out[t], w[:, None] * kvd[s, :512][None], rtol=1e-12,
+                                   atol=1e-13)
+    # identities on a row set with several slots
+    g = np.random.default_rng(3)
+    idx2 = np.full((8, 9), -1, np.int32)
+    for t in range(8):
+        idx2[t, :t + 1] = g.permutation(t + 1)
+    o0, l0 = oracle.sparse_mla_fwd(q, kv, idx2, None, scale, 512)
+    o1, l1 = oracle.sparse_mla_fwd(q, kv, idx2, None, scale, 512, sink=sink)
+    np.testing.assert_allclose(l1, np.logaddexp(l0, sink[None]), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o1, o0 * np.exp(l0 - l1)[..., None], rtol=1e-12, atol=1e-13)
+    om, lm = oracle.sparse_mla_fwd(q, kv, idx2, None, scale, 512, sink=np.full(H, -np.inf))
+    np.testing.assert_array_equal(om, o0)
+    np.testing.assert_array_equal(lm, l0)
+    # empty rows
+    empty = np.full((8, 3), -1, np.int32)
+    oe, le = oracle.sparse_mla_fwd(q, kv, empty, None, scale, 512, sink=sink)
+    assert not oe.any()
+    np.testing.assert_array_equal(le, np.broadcast_to(sink, le.shape))
+    dq, dkv, dsink = oracle.sparse_mla_bwd(q, kv, empty, None, dout, scale, sink=sink)
+    assert not dq.any() and not dkv.any() and not dsink.any()
