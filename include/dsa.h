@@ -195,6 +195,42 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                        float *dkv, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
+ * Attention sink (API reference _pad_attention_heads: a per-head sink [H] is
+ * padded together with the query heads; the page does not state its
+ * arithmetic).  Reading taken: sink[h] is one more logit of head h whose
+ * value vector is zero, so it enters only the softmax denominator:
+ *     lse'[t,h] = log(sum_j exp(z_j) + exp(sink[h]))
+ *     out'[t,h] = sum_j exp(z_j - lse'[t,h]) kv[s_j, 0:D_v]
+ * A row with no valid slot gives out' = 0, lse' = sink[h]; sink = -inf is
+ * no sink.
+ *
+ * dsa_sparse_mla_fwd_sink: arguments, layout and errors as
+ * dsa_sparse_mla_fwd, plus sink [H] fp32 (device, not NULL when T_q > 0).
+ * It runs the forward and then rescales out and lse in place (an exact
+ * identity: lse' = logaddexp(lse, sink), out' = out exp(lse - lse')), so
+ * out is read and written once more.
+ *
+ * dsa_sparse_mla_bwd_sink: arguments, layout, workspace and errors as
+ * dsa_sparse_mla_bwd, where out / lse are the sink forward's out' / lse',
+ * plus sink [H] fp32 and dsink [H] fp32 (device, not NULL).  dq and dkv are
+ * those of the attention with the sink, and
+ *     dsink[h] = -sum_t exp(sink[h] - lse'[t,h]) <dout[t,h], out'[t,h]>
+ * (the sink's probability times the gradient of its zero value).  With
+ * DSA_BWD_ACCUMULATE_DKV, dsink is added into as well; otherwise it is
+ * overwritten.  dsink is reproducible up to the order of its fp32 sums.
+ * ------------------------------------------------------------------------ */
+int dsa_sparse_mla_fwd_sink(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                            const int32_t *topk_length, int64_t T_q, int64_t T_kv, int32_t H,
+                            int32_t D_qk, int32_t D_v, int32_t K, float scale, const float *sink,
+                            uint16_t *out, float *lse, void *stream);
+int dsa_sparse_mla_bwd_sink(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                            const int32_t *topk_length, const uint16_t *out, const float *lse,
+                            const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H,
+                            int32_t D_qk, int32_t D_v, int32_t K, float scale, const float *sink,
+                            uint16_t *dq, float *dkv, float *dsink, uint32_t flags, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
  * Benchmark support (changes no result).  While armed, every kernel the library
  * enqueues records slots[i].start on its stream just before the kernel and
  * slots[i].stop just after it, and sets slots[i].name to a static string naming

@@ -71,6 +71,12 @@ def lib():
         L.dsa_sparse_mla_bwd.restype = C.c_int
         L.dsa_sparse_mla_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
                                          f32, vp, vp, u32, vp, sz, vp]
+        L.dsa_sparse_mla_fwd_sink.restype = C.c_int
+        L.dsa_sparse_mla_fwd_sink.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, f32,
+                                              vp, vp, vp, vp]
+        L.dsa_sparse_mla_bwd_sink.restype = C.c_int
+        L.dsa_sparse_mla_bwd_sink.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32,
+                                              i32, f32, vp, vp, vp, vp, u32, vp, sz, vp]
         L.dsa_record_kernel_events.restype = C.c_int
         L.dsa_record_kernel_events.argtypes = [vp, C.c_int, C.POINTER(C.c_int)]
         _lib = L
@@ -247,10 +253,19 @@ def _attn_shapes(op, q, kv, idx, topk_length):
     return kv, idx, Tq, H, Dqk, kv.shape[0], idx.shape[1]
 
 
+def _sink_arg(op, sink, H):
+    _require(op, sink)
+    _dtype(op, "sink", sink, torch.float32)
+    if sink.shape != (H,):
+        raise ValueError(f"{op}: sink must be [H] = [{H}] fp32")
+    return sink
+
+
 def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, topk_indices: torch.Tensor,
                    softmax_scale: float, topk_length: torch.Tensor | None = None,
-                   d_v: int = 512, out=None, lse=None):
-    """dsa_sparse_mla_fwd -> (out bf16 [T_q,H,512], lse fp32 [T_q,H])."""
+                   d_v: int = 512, out=None, lse=None, sink=None):
+    """dsa_sparse_mla_fwd -> (out bf16 [T_q,H,512], lse fp32 [T_q,H]); with `sink` (fp32 [H],
+    one zero-valued logit per head) dsa_sparse_mla_fwd_sink."""
     op = "sparse_mla_fwd"
     _require(op, q, kv, topk_indices, topk_length)
     kv, idx, Tq, H, Dqk, Tkv, K = _attn_shapes(op, q, kv, topk_indices, topk_length)
@@ -259,9 +274,15 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, topk_indices: torch.Tensor
     if lse is None:
         lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
     _require(op, out, lse)
-    _call(lib().dsa_sparse_mla_fwd, op, q.data_ptr(), kv.data_ptr(), idx.data_ptr(),
-          _ptr(topk_length), Tq, Tkv, H, Dqk, d_v, K, float(softmax_scale), out.data_ptr(),
-          lse.data_ptr(), _stream())
+    if sink is None:
+        _call(lib().dsa_sparse_mla_fwd, op, q.data_ptr(), kv.data_ptr(), idx.data_ptr(),
+              _ptr(topk_length), Tq, Tkv, H, Dqk, d_v, K, float(softmax_scale), out.data_ptr(),
+              lse.data_ptr(), _stream())
+    else:
+        _sink_arg(op, sink, H)
+        _call(lib().dsa_sparse_mla_fwd_sink, op, q.data_ptr(), kv.data_ptr(), idx.data_ptr(),
+              _ptr(topk_length), Tq, Tkv, H, Dqk, d_v, K, float(softmax_scale), sink.data_ptr(),
+              out.data_ptr(), lse.data_ptr(), _stream())
     return out, lse
 
 
@@ -283,13 +304,15 @@ def bwd_workspace_bytes(T_q: int, T_kv: int, H: int, D_qk: int, K: int,
 
 def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
                    topk_length=None, dkv=None, accumulate: bool = False, dq=None,
-                   check_indices: bool = False, workspace=None):
+                   check_indices: bool = False, workspace=None, sink=None, dsink=None):
     """dsa_sparse_mla_bwd -> (dq bf16 [T_q,H,D_qk], dkv fp32 [T_kv,D_qk]).
 
     With accumulate=True the gradients of the latent rows are added into `dkv`
     (query-chunked execution); otherwise dkv is overwritten.  `workspace` (uint8 device
     tensor) sets how many query rows a pass stages (see bwd_workspace_bytes); by default one
-    of DEFAULT_BWD_STAGE_BYTES is allocated."""
+    of DEFAULT_BWD_STAGE_BYTES is allocated.  With `sink` (fp32 [H]; out / lse then come from
+    the sink forward) this is dsa_sparse_mla_bwd_sink and returns (dq, dkv, dsink fp32 [H]);
+    accumulate=True adds into `dsink` too."""
     op = "sparse_mla_bwd"
     _require(op, q, kv, topk_indices, out, lse, dout, topk_length, dkv)
     kv2, idx, Tq, H, Dqk, Tkv, K = _attn_shapes(op, q, kv, topk_indices, topk_length)
@@ -313,8 +336,23 @@ def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
                                 dtype=torch.uint8, device=q.device)
     flags = (DSA_BWD_ACCUMULATE_DKV if accumulate else 0) | (
         DSA_DEBUG_CHECK_INDICES if check_indices else 0)
-    _call(lib().dsa_sparse_mla_bwd, op, q.data_ptr(), kv2.data_ptr(), idx.data_ptr(),
+    if sink is None:
+        _call(lib().dsa_sparse_mla_bwd, op, q.data_ptr(), kv2.data_ptr(), idx.data_ptr(),
+              _ptr(topk_length), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), Tq, Tkv, H, Dqk,
+              d_v, K, float(softmax_scale), dq.data_ptr(), dkv.data_ptr(), flags,
+              workspace.data_ptr(), workspace.numel(), _stream())
+        return dq, dkv
+    _sink_arg(op, sink, H)
+    if dsink is None:
+        if accumulate:
+            raise ValueError(f"{op}: accumulate=True needs a dsink buffer")
+        dsink = torch.empty((H,), dtype=torch.float32, device=q.device)
+    _require(op, dsink)
+    _dtype(op, "dsink", dsink, torch.float32)
+    if dsink.shape != (H,):
+        raise ValueError(f"{op}: dsink must be [H] fp32")
+    _call(lib().dsa_sparse_mla_bwd_sink, op, q.data_ptr(), kv2.data_ptr(), idx.data_ptr(),
           _ptr(topk_length), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), Tq, Tkv, H, Dqk,
-          d_v, K, float(softmax_scale), dq.data_ptr(), dkv.data_ptr(), flags,
-          workspace.data_ptr(), workspace.numel(), _stream())
-    return dq, dkv
+          d_v, K, float(softmax_scale), sink.data_ptr(), dq.data_ptr(), dkv.data_ptr(),
+          dsink.data_ptr(), flags, workspace.data_ptr(), workspace.numel(), _stream())
+    return dq, dkv, dsink

@@ -390,4 +390,41 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   return DSA_OK;
 }
 
+// ---------------------------------------------------------------------------------------
+int dsa_sparse_mla_fwd_sink(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                            const int32_t *topk_length, int64_t T_q, int64_t T_kv, int32_t H,
+                            int32_t D_qk, int32_t D_v, int32_t K, float scale, const float *sink,
+                            uint16_t *out, float *lse, void *stream) {
+  g_last_error.clear();
+  if (T_q > 0 && !sink) return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_fwd_sink: sink is NULL");
+  if (!aligned16(out))
+    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_fwd_sink: out must be 16-byte aligned");
+  if (int rc = dsa_sparse_mla_fwd(q, kv, idx, topk_length, T_q, T_kv, H, D_qk, D_v, K, scale, out,
+                                  lse, stream))
+    return rc;
+  hipError_t e = dsa::launch_sink_fwd(sink, T_q, H, D_v, out, lse,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparse_mla_fwd_sink: launch");
+  return DSA_OK;
+}
+
+int dsa_sparse_mla_bwd_sink(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                            const int32_t *topk_length, const uint16_t *out, const float *lse,
+                            const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H,
+                            int32_t D_qk, int32_t D_v, int32_t K, float scale, const float *sink,
+                            uint16_t *dq, float *dkv, float *dsink, uint32_t flags, void *ws,
+                            size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  if (!sink || !dsink)
+    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd_sink: sink and dsink must not be NULL");
+  if (int rc = dsa_sparse_mla_bwd(q, kv, idx, topk_length, out, lse, dout, T_q, T_kv, H, D_qk,
+                                  D_v, K, scale, dq, dkv, flags, ws, ws_bytes, stream))
+    return rc;
+  hipError_t e = dsa::launch_sink_bwd(sink, lse, out, dout, T_q, H, D_v, dsink,
+                                      (flags & DSA_BWD_ACCUMULATE_DKV) != 0,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparse_mla_bwd_sink: launch");
+  return DSA_OK;
+}
+
 }  // extern "C"

@@ -67,6 +67,13 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
                                  uint16_t *dq, float *dkv, bool accumulate,
                                  const BwdWorkspace &ws, hipStream_t s);
 
+// Attention sink: the forward epilogue (out, lse rescaled in place) and the sink gradient.
+hipError_t launch_sink_fwd(const float *sink, int64_t T_q, int32_t H, int32_t D_v,
+                           uint16_t *out, float *lse, hipStream_t s);
+hipError_t launch_sink_bwd(const float *sink, const float *lse, const uint16_t *out,
+                           const uint16_t *dout, int64_t T_q, int32_t H, int32_t D_v,
+                           float *dsink, bool accumulate, hipStream_t s);
+
 hipError_t launch_check_indices(const int32_t *idx, const int32_t *topk_length, int64_t T_q,
                                 int32_t K, int64_t T_kv, int32_t *bad_flag, hipStream_t s);
 

@@ -117,6 +117,17 @@ def test_argument_errors_without_device(dsa):
     assert bwd(K=4097) == pkg.DSA_ERR_INVALID_VALUE and "4096" in _err(dsa)
 
 
+def test_sink_entry_points_reject_missing_sink(dsa):
+    import sparse_attention_12_amd as pkg
+    assert dsa.dsa_sparse_mla_fwd_sink(16, 16, 16, None, 4, 4, 16, 576, 512, 8, 0.1, None, 16,
+                                       16, None) == pkg.DSA_ERR_INVALID_VALUE
+    assert "sink" in _err(dsa)
+    assert dsa.dsa_sparse_mla_bwd_sink(16, 16, 16, None, 16, 16, 16, 4, 4, 16, 576, 512, 8, 0.1,
+                                       16, 16, 16, None, 0, None, 0, None) == \
+        pkg.DSA_ERR_INVALID_VALUE
+    assert "dsink" in _err(dsa)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import sparse_attention_12_amd as pkg
     monkeypatch.setattr(pkg, "_lib", None)

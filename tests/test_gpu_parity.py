@@ -11,7 +11,7 @@ import torch
 
 import dsa_inputs as gen
 import oracle
-from tests import checks
+from tests import checks, pins
 
 pytestmark = pytest.mark.gpu
 
@@ -365,3 +365,92 @@ def test_debug_index_check_rejects_out_of_range():
     with pytest.raises(ValueError, match="out of range"):
         dsa.sparse_mla_bwd(q, kv, bad, out, lse, torch.zeros_like(out), 0.1,
                            check_indices=True)
+
+
+# ----------------------------------------------------------------------------------------
+# attention sink (one zero-valued logit per head in the softmax denominator)
+# ----------------------------------------------------------------------------------------
+
+def _sink_values(H, seed):
+    g = np.random.default_rng(seed)
+    s = (g.standard_normal(H) * 2.0).astype(np.float32)
+    s[0] = 8.0                # dominates every row of head 0
+    if H > 2:
+        s[1] = -np.inf        # no sink for head 1
+    return s
+
+
+def _dsink_bound(ro, rl, dout, sink):
+    """Bound on |dsink_gpu - dsink_oracle| from the arithmetic: the kernels form
+    Delta = dO . out' from the bf16 output (rounded to nearest, then rescaled and rounded once
+    more: relative error below 2^-8 per element), weighted by the sink probability; plus fp32
+    accumulation slack."""
+    p_sink = np.exp(np.where(np.isneginf(sink), -np.inf, sink)[None, :] - rl)
+    p_sink = np.where(np.isfinite(p_sink), p_sink, 0.0)
+    mag = (np.abs(pins.bf16_to_f64(dout)) * np.abs(ro)).sum(-1)          # [T, H]
+    return (p_sink * mag).sum(0) * 2.0 ** -7 + 1e-3
+
+
+@pytest.mark.parametrize("T,H,Dqk,K,n_valid", [(96, 16, 576, 64, 64), (200, 64, 576, 128, 77),
+                                               (130, 8, 512, 75, 70)])
+def test_sink_fwd_bwd_matches_oracle(T, H, Dqk, K, n_valid):
+    dsa = _dsa()
+    g = torch.Generator().manual_seed(T + 11 * H)
+    q = (torch.randn((T, H, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    kv = (torch.randn((T, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16)
+    idx = _random_indices(T, T, K, n_valid, seed=T + H, minus_one_frac=0.1)
+    sink = _sink_values(H, seed=H)
+    scale = 1.0 / math.sqrt(Dqk)
+    sk = torch.from_numpy(sink).to(dev)
+    idx_t = torch.from_numpy(idx).to(dev)
+    out, lse = dsa.sparse_mla_fwd(q.to(dev), kv.to(dev), idx_t, scale, sink=sk)
+    dq, dkv, dsink = dsa.sparse_mla_bwd(q.to(dev), kv.to(dev), idx_t, out, lse, dout.to(dev),
+                                        scale, sink=sk)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_mla_fwd(q, kv, idx, None, scale, 512, sink=sink)
+    checks.assert_close("out", _np(out.float()), ro, checks.ATOL_OUT)
+    checks.assert_close("lse", _np(lse), rl, checks.ATOL_LSE)
+    rdq, rdkv, rds = oracle.sparse_mla_bwd(q, kv, idx, None, dout, scale, sink=sink)
+    checks.assert_close("dq", _np(dq.float()), rdq, checks.ATOL_OUT)
+    checks.assert_close("dkv", _np(dkv), rdkv, checks.ATOL_OUT)
+    err = np.abs(_np(dsink).astype(np.float64) - rds)
+    bound = _dsink_bound(ro, rl, dout, sink)
+    assert (err <= bound).all(), f"dsink error {err.max():.3e} above its bound {bound.min():.3e}"
+    assert rds[1] == 0.0 and _np(dsink)[1] == 0.0   # the -inf sink has no gradient
+
+
+def test_sink_empty_rows_minus_inf_sink_and_chunks():
+    """Empty rows: out' = 0, lse' = sink, dq = 0.  sink = -inf everywhere equals no sink
+    bitwise.  Query chunks with accumulate sum dsink (and dkv) like the one-shot call."""
+    dsa = _dsa()
+    T, H, D, K = 300, 64, 576, 96
+    g = torch.Generator().manual_seed(21)
+    q = (torch.randn((T, H, D), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    kv = (torch.randn((T, D), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    dout = torch.randn((T, H, 512), generator=g).to(torch.bfloat16).to(dev)
+    idx = _random_indices(T, T, K, 80, seed=22)
+    idx[[0, 7, 150]] = -1                                  # three empty rows
+    idx_t = torch.from_numpy(idx).to(dev)
+    sink = torch.from_numpy(_sink_values(H, seed=5)).to(dev)
+    out, lse = dsa.sparse_mla_fwd(q, kv, idx_t, 0.04, sink=sink)
+    dq, dkv, dsink = dsa.sparse_mla_bwd(q, kv, idx_t, out, lse, dout, 0.04, sink=sink)
+    torch.cuda.synchronize()
+    for t in (0, 7, 150):
+        assert not out[t].any() and not dq[t].any()
+        assert torch.equal(lse[t], sink)
+    o0, l0 = dsa.sparse_mla_fwd(q, kv, idx_t, 0.04)
+    om, lm = dsa.sparse_mla_fwd(q, kv, idx_t, 0.04, sink=torch.full((H,), -math.inf, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(om, o0) and torch.equal(lm, l0)
+    dkv_c = torch.zeros_like(dkv)
+    ds_c = torch.zeros_like(dsink)
+    for r0, r1 in [(0, 128), (128, 300)]:
+        oc, lc = dsa.sparse_mla_fwd(q[r0:r1], kv, idx_t[r0:r1], 0.04, sink=sink)
+        assert torch.equal(oc, out[r0:r1]) and torch.equal(lc, lse[r0:r1])
+        dqc, _, _ = dsa.sparse_mla_bwd(q[r0:r1], kv, idx_t[r0:r1], oc, lc, dout[r0:r1], 0.04,
+                                       dkv=dkv_c, accumulate=True, sink=sink, dsink=ds_c)
+        assert torch.equal(dqc, dq[r0:r1])
+    torch.cuda.synchronize()
+    assert (dkv_c - dkv).abs().max().item() <= 1e-5 * dkv.abs().max().item() + 1e-4
+    assert (ds_c - dsink).abs().max().item() <= 1e-5 * dsink.abs().max().item() + 1e-4
