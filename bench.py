@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--bwd-passes", type=int, default=1,
                     help="query-row passes of the backward (several passes overlap a pass's "
                          "key-gradient reduction with the next pass's compute)")
+    ap.add_argument("--sink", action="store_true",
+                    help="run the step with a per-head attention sink (sink forward epilogue and "
+                         "sink gradient kernels added)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy a device buffer of BYTES bytes once with "
                          "an elementwise kernel (x * 1): a plain copy of known size, which "
@@ -257,6 +260,8 @@ def main():
     rows_per_pass = -(-T // max(1, args.bwd_passes))
     ws = torch.empty(dsa.bwd_workspace_bytes(T, T, H, Dqk, K, rows_per_pass=rows_per_pass),
                      dtype=torch.uint8, device=dev)
+    sink = gen.sink_logits(H, device=dev) if args.sink else None
+    dsink_buf = torch.empty((H,), dtype=torch.float32, device=dev) if args.sink else None
     kpool_valid = None
     if not has_indexer:
         kp = gen.kpool_indices(T, topk=K, tail=cfg.kpool_tail, device=dev)
@@ -273,12 +278,13 @@ def main():
             dsa.indexer_topk(inputs["q_idx"], inputs["k_idx"], inputs["w"], md, K, idx=idx_buf,
                              length=len_buf)
         dsa.sparse_mla_fwd(att["q"], att["kv"], idx_buf, cfg.scale, len_buf, out=out_buf,
-                           lse=lse_buf)
+                           lse=lse_buf, sink=sink)
         if timing:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record()
         dsa.sparse_mla_bwd(att["q"], att["kv"], idx_buf, out_buf, lse_buf, att["dout"],
-                           cfg.scale, len_buf, dkv=dkv_buf, dq=dq_buf, workspace=ws)
+                           cfg.scale, len_buf, dkv=dkv_buf, dq=dq_buf, workspace=ws, sink=sink,
+                           dsink=dsink_buf)
         if timing:
             ev[1].record()
             bwd_events.append(ev)
@@ -325,6 +331,13 @@ def main():
         comp["indexer"] = {"ms": t_idx, "tokens_per_s": T / (t_idx * 1e-3),
                            "tflops": counts["idx_flops"] / t_idx / 1e9,
                            "frac_mfma_peak": counts["idx_flops"] / t_idx / 1e9 / PEAK_BF16_TFLOPS}
+    if args.sink:
+        # HBM-streaming kernels: the epilogue reads and writes out [T,H,Dv] bf16 and lse; the
+        # gradient kernel reads out, dout and lse
+        for name, nbytes in (("sink_fwd", T * H * (4 * Dv + 8)), ("sink_bwd", T * H * (4 * Dv + 4))):
+            ms = avg(name)
+            comp[name] = {"ms": ms, "gbs": nbytes / ms / 1e6,
+                          "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
     kernels = {n: {"avg_ms": sum(v) / len(v), "launches": len(v)} for n, v in per_kernel.items()}
 
     # algorithmic work per launch of each hot kernel: MFMA flops, or HBM bytes for the
@@ -361,6 +374,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": T, "cu_seqlens": list(cfg.cu_seqlens),
                    "indexer": (f"{cfg.idx_heads}x{cfg.idx_dim}" if has_indexer else None),
                    "topk": K, "heads": H, "d_qk": Dqk, "d_v": Dv, "bwd_passes": args.bwd_passes,
+                   "attention_sink": bool(args.sink),
                    "parallelism": "none"},
         "components": comp, "kernels": kernels, "roofline": roofline,
     }

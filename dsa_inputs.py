@@ -136,6 +136,13 @@ def attention_inputs(cfg: int, cu_seqlens=None, device="cpu", layer=0, seed=None
                 scale=1.0 / math.sqrt(Dqk), d_v=w.d_v)
 
 
+def sink_logits(H: int, device="cpu", seed=None) -> torch.Tensor:
+    """Per-head attention-sink logits fp32 [H] ~ N(0,1) * 2 (the pages give no distribution;
+    this spread lets the sink dominate some heads and vanish in others)."""
+    g = _gen(seed if seed is not None else SEED_BASE + 0x200 + H, device)
+    return (torch.randn((H,), generator=g, device=device) * 2.0).to(torch.float32).contiguous()
+
+
 def kpool_indices(T: int, topk: int = 2051, tail: int = 3, device="cpu", seed=None,
                   row_block: int = 256) -> torch.Tensor:
     """Synthetic k-pool selection for a single causal sequence, int32 [T, topk].

@@ -19,7 +19,8 @@
 namespace dsa {
 namespace {
 
-constexpr int kWaves = 4;  // one (t, h) row per wave
+constexpr int kWaves = 4;
+constexpr int kFwdRows = 4;  // (t, h) rows per wave in the forward epilogue
 
 // logaddexp(a, b) in fp32 for a, b in [-inf, +inf) (both -inf: -inf).
 __device__ __forceinline__ float log_add_exp(float a, float b) {
@@ -28,29 +29,41 @@ __device__ __forceinline__ float log_add_exp(float a, float b) {
   return m + log1pf(expf(-fabsf(a - b)));
 }
 
-// Rows of D_v bf16 outputs, one wave per (t, h) row: each lane rescales 16-byte pieces in
-// place; lane 0 replaces lse.
+// Rows of D_v = 512 bf16 outputs (one 16-byte piece per lane), kFwdRows consecutive (t, h)
+// rows per wave: the wave loads all of its pieces first, then rescales and stores them in
+// place; lane j < kFwdRows replaces lse of row j.
 __global__ __launch_bounds__(64 * kWaves) void sink_fwd_kernel(const float *__restrict__ sink,
-                                                               int64_t rows, int H, int Dv,
+                                                               int64_t rows, int H,
                                                                uint16_t *__restrict__ out,
                                                                float *__restrict__ lse) {
+  constexpr int Dv = 512;
   const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int h = static_cast<int>(r % H);
-  const float l = lse[r];
-  const float l2 = log_add_exp(l, sink[h]);
-  const float f = l == -INFINITY ? 0.0f : expf(l - l2);  // empty row: the output stays 0
-  uint16_t *o = out + r * Dv;
-  for (int c = lane * 8; c < Dv; c += 64 * 8) {
-    u32x4 v = *reinterpret_cast<const u32x4 *>(o + c);
+  const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6)) * kFwdRows;
+  if (r0 >= rows) return;
+  const int n = static_cast<int>(min<int64_t>(kFwdRows, rows - r0));
+  u32x4 v[kFwdRows];
+  float f[kFwdRows];
+#pragma unroll
+  for (int j = 0; j < kFwdRows; ++j)
+    if (j < n) v[j] = *reinterpret_cast<const u32x4 *>(out + (r0 + j) * Dv + lane * 8);
+  float l2_mine = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kFwdRows; ++j) {
+    const float l = j < n ? lse[r0 + j] : 0.0f;
+    const float l2 = log_add_exp(l, sink[(r0 + j) % H]);
+    f[j] = l == -INFINITY ? 0.0f : expf(l - l2);  // empty row: the output stays 0
+    if (lane == j) l2_mine = l2;
+  }
+#pragma unroll
+  for (int j = 0; j < kFwdRows; ++j) {
+    if (j >= n) break;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      v[w] = pack_bf16x2(__uint_as_float(v[w] << 16) * f,
-                         __uint_as_float(v[w] & 0xFFFF0000u) * f);
-    *reinterpret_cast<u32x4 *>(o + c) = v;
+      v[j][w] = pack_bf16x2(__uint_as_float(v[j][w] << 16) * f[j],
+                            __uint_as_float(v[j][w] & 0xFFFF0000u) * f[j]);
+    *reinterpret_cast<u32x4 *>(out + (r0 + j) * Dv + lane * 8) = v[j];
   }
-  if (lane == 0) lse[r] = l2;
+  if (lane < n) lse[r0 + lane] = l2_mine;
 }
 
 // dsink[h] += -sum_t exp(sink[h] - lse[t,h]) (dO[t,h] . out[t,h]): waves stride over the
@@ -60,36 +73,48 @@ __global__ __launch_bounds__(64 * kWaves) void sink_bwd_kernel(const float *__re
                                                                const float *__restrict__ lse,
                                                                const uint16_t *__restrict__ out,
                                                                const uint16_t *__restrict__ dout,
-                                                               int64_t rows, int H, int Dv,
+                                                               int64_t rows, int H,
                                                                float *__restrict__ dsink) {
+  constexpr int Dv = 512;
   __shared__ float acc[64];
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < 64) acc[threadIdx.x] = 0.0f;
   __syncthreads();
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t r = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); r < rows;
+  // two rows per trip (D_v = 512: one 16-byte piece of out and of dout per lane and row),
+  // their four loads issued together
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves * 2;
+  for (int64_t r = (static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6)) * 2; r < rows;
        r += stride) {
-    const uint16_t *o = out + r * Dv;
-    const uint16_t *d = dout + r * Dv;
-    float dot = 0.0f;
-    for (int c = lane * 8; c < Dv; c += 64 * 8) {
-      const u32x4 ov = *reinterpret_cast<const u32x4 *>(o + c);
-      const u32x4 dv = *reinterpret_cast<const u32x4 *>(d + c);
+    const bool two = r + 1 < rows;
+    const u32x4 o0 = *reinterpret_cast<const u32x4 *>(out + r * Dv + lane * 8);
+    const u32x4 d0 = *reinterpret_cast<const u32x4 *>(dout + r * Dv + lane * 8);
+    u32x4 o1 = {0u, 0u, 0u, 0u}, d1 = {0u, 0u, 0u, 0u};
+    if (two) {
+      o1 = *reinterpret_cast<const u32x4 *>(out + (r + 1) * Dv + lane * 8);
+      d1 = *reinterpret_cast<const u32x4 *>(dout + (r + 1) * Dv + lane * 8);
+    }
+    float dot0 = 0.0f, dot1 = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        dot = fmaf(__uint_as_float(ov[w] << 16), __uint_as_float(dv[w] << 16), dot);
-        dot = fmaf(__uint_as_float(ov[w] & 0xFFFF0000u), __uint_as_float(dv[w] & 0xFFFF0000u),
-                   dot);
-      }
+    for (int w = 0; w < 4; ++w) {
+      dot0 = fmaf(__uint_as_float(o0[w] << 16), __uint_as_float(d0[w] << 16), dot0);
+      dot0 = fmaf(__uint_as_float(o0[w] & 0xFFFF0000u), __uint_as_float(d0[w] & 0xFFFF0000u),
+                  dot0);
+      dot1 = fmaf(__uint_as_float(o1[w] << 16), __uint_as_float(d1[w] << 16), dot1);
+      dot1 = fmaf(__uint_as_float(o1[w] & 0xFFFF0000u), __uint_as_float(d1[w] & 0xFFFF0000u),
+                  dot1);
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (lane == 0) {
-      const int h = static_cast<int>(r % H);
-      const float l = lse[r];
+    for (int off = 32; off >= 1; off >>= 1) {
+      dot0 += __shfl_xor(dot0, off, 64);
+      dot1 += __shfl_xor(dot1, off, 64);
+    }
+    if (lane < 2 && (lane == 0 || two)) {
+      const int64_t rr = r + lane;
+      const int h = static_cast<int>(rr % H);
+      const float l = lse[rr];
       // lse = -inf only when the row is empty and the sink is -inf: no term
       const float p = l == -INFINITY ? 0.0f : expf(sink[h] - l);
-      atomicAdd(&acc[h], -p * dot);
+      atomicAdd(&acc[h], -p * (lane == 0 ? dot0 : dot1));
     }
   }
   __syncthreads();
@@ -104,24 +129,26 @@ __global__ void sink_zero_kernel(float *__restrict__ p, int n) {
 
 hipError_t launch_sink_fwd(const float *sink, int64_t T_q, int32_t H, int32_t D_v,
                            uint16_t *out, float *lse, hipStream_t s) {
+  if (D_v != 512) return hipErrorInvalidValue;
   const int64_t rows = T_q * H;
   if (rows == 0) return hipSuccess;
-  const int64_t blocks = (rows + kWaves - 1) / kWaves;
+  const int64_t blocks = (rows + kWaves * kFwdRows - 1) / (kWaves * kFwdRows);
   DSA_LAUNCH("sink_fwd", sink_fwd_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves),
-             0, s, sink, rows, H, D_v, out, lse);
+             0, s, sink, rows, H, out, lse);
   return hipGetLastError();
 }
 
 hipError_t launch_sink_bwd(const float *sink, const float *lse, const uint16_t *out,
                            const uint16_t *dout, int64_t T_q, int32_t H, int32_t D_v,
                            float *dsink, bool accumulate, hipStream_t s) {
+  if (D_v != 512) return hipErrorInvalidValue;
   if (!accumulate) DSA_LAUNCH("sink_zero", sink_zero_kernel, dim3(1), dim3(64), 0, s, dsink, H);
   const int64_t rows = T_q * H;
   if (rows > 0) {
     // enough blocks to keep HBM busy; each block then adds H partial sums
-    const int64_t blocks = std::min<int64_t>((rows + kWaves - 1) / kWaves, 2048);
+    const int64_t blocks = std::min<int64_t>((rows + 2 * kWaves - 1) / (2 * kWaves), 2048);
     DSA_LAUNCH("sink_bwd", sink_bwd_kernel, dim3(static_cast<uint32_t>(blocks)),
-               dim3(64 * kWaves), 0, s, sink, lse, out, dout, rows, H, D_v, dsink);
+               dim3(64 * kWaves), 0, s, sink, lse, out, dout, rows, H, dsink);
   }
   return hipGetLastError();
 }
