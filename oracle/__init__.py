@@ -48,6 +48,10 @@ def lib():
                                                C.c_int32, C.c_int32, C.c_int32, C.c_int64,
                                                C.c_int64, C.c_int64, i32p, i32p, C.c_void_p]
         L.oracle_indexer_topk_rows.restype = C.c_int
+        L.oracle_indexer_topk_local.argtypes = [u16p, u16p, f32p, i32p, C.c_void_p, C.c_void_p,
+                                                C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                                C.c_int32, C.c_int32, C.c_int32, i32p, i32p]
+        L.oracle_indexer_topk_local.restype = C.c_int
         L.oracle_sparse_mla_fwd.argtypes = [u16p, u16p, i32p, C.c_void_p, C.c_int64, C.c_int64,
                                             C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
                                             C.c_void_p, C.c_int64, C.c_int64, f64p, f64p]
@@ -137,6 +141,34 @@ def indexer_topk_rows(q_rows, k_idx, w_rows, cu_seqlens, K: int, row_begin: int)
                                           row_begin, idx, ln, kth.ctypes.data),
            "indexer_topk_rows")
     return idx, ln, kth
+
+
+def indexer_topk_local(q_idx, k_idx, w, cu_seqlens, K: int, cu_seqlens_padded=None,
+                       query_indices=None, padding_mask=None):
+    """Local query rows (q_idx / w [T_q,...]) against gathered global keys (k_idx [T_k,D]) in
+    padded-storage coordinates.  Returns (idx int32 [T_q,K] global padded coordinates,
+    len int32 [T_q]); padding rows get len 0 and -1."""
+    qa = _u16(q_idx)
+    ka = _u16(k_idx)
+    wa = _np(w, np.float32)
+    cu = _np(cu_seqlens, np.int32)
+    cp, cpp = _opt_i32(cu_seqlens_padded)
+    qi, qip = _opt_i32(query_indices)
+    pm = pmp = None
+    if padding_mask is not None:
+        pm = np.ascontiguousarray(np.asarray(
+            padding_mask.cpu().numpy() if hasattr(padding_mask, "cpu") else padding_mask,
+            dtype=np.uint8))
+        pmp = pm.ctypes.data
+    Tq, H, D = qa.shape
+    Tk = ka.shape[0]
+    idx = np.zeros((Tq, K), np.int32)
+    ln = np.zeros(Tq, np.int32)
+    _check(lib().oracle_indexer_topk_local(qa.reshape(-1), ka.reshape(-1), wa.reshape(-1), cu,
+                                           cpp, qip, pmp, cu.size - 1, Tq, Tk, H, D, K, idx, ln),
+           "indexer_topk_local")
+    del cp, qi, pm
+    return idx, ln
 
 
 def indexer_score_rows(q_row, k_idx, w_row, s: int) -> float:

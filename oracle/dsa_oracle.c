@@ -182,6 +182,65 @@ int oracle_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
                                   len_out, kth_score);
 }
 
+/* Local query rows against gathered global keys ([API]
+ * prepare_cudnn_dsa_packed_metadata and cudnn_indexer_topk: query_indices
+ * hold the global padded-storage coordinate of each local query row,
+ * cu_seqlens_padded the padded storage boundaries of the sequences (absent:
+ * cu_seqlens), cu_seqlens their real lengths, padding_mask the local padding
+ * rows; indices come back in global padded-storage coordinates).  For local
+ * row i with coordinate p = qidx[i] (i itself when qidx is NULL): the sequence
+ * b has cu_pad[b] <= p < cu_pad[b+1], the row's position is pos = p -
+ * cu_pad[b], and the row is real when pos < cu[b+1] - cu[b] and pmask[i] is
+ * 0.  A real row scores the keys s = cu_pad[b] .. p (q and w row i, k row s)
+ * and keeps the n = min(K, pos + 1) best as above; any other row gets len 0
+ * and -1 everywhere.  q and w are [T_q x ...], k is [T_k x D]. */
+int oracle_indexer_topk_local(const uint16_t *q, const uint16_t *k, const float *w,
+                              const int32_t *cu, const int32_t *cu_pad, const int32_t *qidx,
+                              const uint8_t *pmask, int32_t B, int64_t T_q, int64_t T_k,
+                              int32_t H, int32_t D, int32_t K, int32_t *idx_out,
+                              int32_t *len_out) {
+  if (B < 1 || H < 1 || D < 1 || K < 1 || T_q < 0 || T_k < 0) return ORACLE_EINVAL;
+  if (!cu_pad) cu_pad = cu;
+  if (cu[0] != 0 || cu_pad[0] != 0 || cu_pad[B] > T_k) return ORACLE_EINVAL;
+  for (int32_t b = 0; b < B; ++b)
+    if (cu[b + 1] < cu[b] || cu_pad[b + 1] - cu_pad[b] < cu[b + 1] - cu[b]) return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < T_q; ++i) {
+    int32_t *row = idx_out + (size_t)i * K;
+    for (int32_t j = 0; j < K; ++j) row[j] = -1;
+    len_out[i] = 0;
+    int64_t p = qidx ? qidx[i] : i;
+    if (p < 0 || p >= cu_pad[B]) {
+#pragma omp atomic write
+      err = ORACLE_EINVAL;
+      continue;
+    }
+    int32_t b = B - 1;
+    while (cu_pad[b] > p) --b;  /* the last sequence starting at or before p */
+    int64_t start = cu_pad[b], pos = p - start;
+    if (pos >= cu[b + 1] - cu[b] || (pmask && pmask[i])) continue;
+    int64_t L = pos + 1;
+    scored_key *keys = (scored_key *)malloc(sizeof(scored_key) * (size_t)L);
+    if (!keys) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+      continue;
+    }
+    for (int64_t s = start; s <= p; ++s) {
+      keys[s - start].score = indexer_score_rows(q, k, w, H, D, 0, i, s);
+      keys[s - start].pos = (int32_t)s;
+    }
+    qsort(keys, (size_t)L, sizeof(scored_key), by_rank);
+    int64_t n = L < K ? L : K;
+    qsort(keys, (size_t)n, sizeof(scored_key), by_pos);
+    for (int64_t j = 0; j < n; ++j) row[j] = keys[j].pos;
+    len_out[i] = (int32_t)n;
+    free(keys);
+  }
+  return err;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Absorbed sparse MLA ([GLM52] "Why DSA needs fused kernels": all heads of  */
 /* a query share one top-k set, MQA-style; [API] cudnn_sparse_attention:     */

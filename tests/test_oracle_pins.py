@@ -419,3 +419,60 @@ def test_sink_single_slot_closed_form_and_identities():
     np.testing.assert_array_equal(le, np.broadcast_to(sink, le.shape))
     dq, dkv, dsink = oracle.sparse_mla_bwd(q, kv, empty, None, dout, scale, sink=sink)
     assert not dq.any() and not dkv.any() and not dsink.any()
+
+
+# ---- local query rows against gathered global keys in padded-storage coordinates ([API]
+# prepare_cudnn_dsa_packed_metadata: query_indices, cu_seqlens_padded, padding_mask)
+
+def _padded_layout(cu, cu_pad, k_compact, D, g):
+    """k in padded storage: sequence b's real keys at cu_pad[b] + j, random padding rows."""
+    k = torch.randn((cu_pad[-1], D), generator=g).to(torch.bfloat16)
+    for b in range(len(cu) - 1):
+        n = cu[b + 1] - cu[b]
+        k[cu_pad[b]:cu_pad[b] + n] = k_compact[cu[b]:cu[b + 1]]
+    return k
+
+
+def test_local_indexer_identity_padding_and_cp_split():
+    """Identity coordinates equal the compact oracle; a padded layout gives the compact result
+    with positions mapped to padded storage; two ranks' query subsets together give the full
+    result; rows in the padding (by position or by the mask) get len 0 and -1."""
+    cu, cu_pad, K, H, D = [0, 5, 30, 71], [0, 8, 40, 84], 9, 4, 64
+    T = cu[-1]
+    inp = gen.indexer_inputs(1, cu_seqlens=cu)
+    q, k, w = inp["q_idx"][:, :H], inp["k_idx"], inp["w"][:, :H].contiguous()
+    ref_i, ref_l, _ = oracle.indexer_topk(q.contiguous(), k, w, cu, K)
+    idx, ln = oracle.indexer_topk_local(q.contiguous(), k, w, cu, K)
+    np.testing.assert_array_equal(idx, ref_i)
+    np.testing.assert_array_equal(ln, ref_l)
+    # padded storage: every real token as a local query, coordinates cu_pad[b] + j
+    g = torch.Generator().manual_seed(4)
+    kp = _padded_layout(cu, cu_pad, k, D, g)
+    seq = np.searchsorted(np.array(cu), np.arange(T), side="right") - 1
+    shift = (np.array(cu_pad)[seq] - np.array(cu)[seq]).astype(np.int32)
+    coord = (np.arange(T) + shift).astype(np.int32)
+    idx_p, ln_p = oracle.indexer_topk_local(q.contiguous(), kp, w, cu, K, cu_seqlens_padded=cu_pad,
+                                            query_indices=coord)
+    expect = np.where(ref_i >= 0, ref_i + shift[:, None], -1)
+    np.testing.assert_array_equal(idx_p, expect)
+    np.testing.assert_array_equal(ln_p, ref_l)
+    # two ranks with zig-zag chunks of the local rows
+    chunks = np.array_split(np.arange(T), 4)
+    ranks = [np.concatenate([chunks[0], chunks[3]]), np.concatenate([chunks[1], chunks[2]])]
+    for rows in ranks:
+        i_r, l_r = oracle.indexer_topk_local(q[rows].contiguous(), kp, w[rows].contiguous(), cu,
+                                             K, cu_seqlens_padded=cu_pad,
+                                             query_indices=coord[rows])
+        np.testing.assert_array_equal(i_r, expect[rows])
+        np.testing.assert_array_equal(l_r, ref_l[rows])
+    # padding rows: coordinates beyond a sequence's real length, and masked rows
+    pad_coord = np.array([5, 7, 35, 39, 82, 12], np.int32)   # the last one is real (seq 1)
+    qr = q[:6].contiguous()
+    wr = w[:6].contiguous()
+    mask = np.array([0, 0, 0, 0, 0, 1], np.uint8)
+    i_p, l_p = oracle.indexer_topk_local(qr, kp, wr, cu, K, cu_seqlens_padded=cu_pad,
+                                         query_indices=pad_coord, padding_mask=mask)
+    assert (i_p == -1).all() and (l_p == 0).all()
+    i_u, l_u = oracle.indexer_topk_local(qr, kp, wr, cu, K, cu_seqlens_padded=cu_pad,
+                                         query_indices=pad_coord)
+    assert (l_u[:5] == 0).all() and l_u[5] == 5 and (i_u[5, :5] == np.arange(8, 13)).all()
