@@ -87,6 +87,10 @@ typedef struct dsa_thd_metadata {
   int64_t total_pairs;  /* sum_t L_t   (causal query-key pairs)              */
   int64_t total_valid;  /* sum_t min(K, L_t)                                  */
   int32_t n_groups;     /* sum over sequences of ceil(length / 4)             */
+  /* local query rows (dsa_prepare_local_metadata); NULL / T otherwise            */
+  int32_t *gpos;        /* [T]  key-tensor coordinate of each local query row  */
+  int32_t *group_first; /* [n_groups] first row of each indexer work group     */
+  int64_t total_key_tokens; /* rows of the key tensors (k_idx, kv)            */
 } dsa_thd_metadata;
 
 /* Bytes of workspace the metadata for T tokens needs. */
@@ -100,6 +104,32 @@ size_t dsa_thd_metadata_workspace_size(int64_t T);
  * DSA_ERR_WORKSPACE if ws is NULL or ws_bytes too small. */
 int dsa_prepare_thd_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t K,
                              void *ws, size_t ws_bytes, dsa_thd_metadata *md, void *stream);
+
+/* Local query rows against gathered global keys (API reference
+ * prepare_cudnn_dsa_packed_metadata: query_indices are global padded-storage
+ * coordinates of the local query rows, cu_seqlens_padded the padded storage
+ * boundaries, padding_mask the local padding rows; cudnn_indexer_topk then
+ * returns indices in global padded-storage coordinates).
+ *   cu_seqlens        device int32 [B+1], real lengths (cu[0] = 0, non-decreasing)
+ *   cu_seqlens_padded device int32 [B+1] or NULL (= cu_seqlens); each padded
+ *                     sequence at least as long as the real one, cu_pad[B] <= T_k
+ *   query_indices     device int32 [T_q] or NULL (identity: T_q = cu_pad[B])
+ *   padding_mask      device uint8 [T_q] or NULL; nonzero marks a padding row
+ * Local row i with coordinate p lies in sequence b (cu_pad[b] <= p <
+ * cu_pad[b+1]) at position pos = p - cu_pad[b]; it is real when pos < cu[b+1]
+ * - cu[b] and it is not masked, and then sees the keys cu_pad[b] .. p
+ * (causal_len = pos + 1); a padding row has causal_len 0, and the indexer
+ * gives it len 0 and -1 everywhere.  The metadata feeds dsa_indexer_topk with
+ * q_idx / w of T_q rows and k_idx of T_k rows.  Reads its inputs on the host
+ * and synchronises `stream` twice (inputs, then the upload of the tables).
+ * Errors: DSA_ERR_INVALID_VALUE for bad sizes, offsets or coordinates;
+ * DSA_ERR_WORKSPACE if ws is NULL or smaller than
+ * dsa_local_metadata_workspace_size(T_q). */
+size_t dsa_local_metadata_workspace_size(int64_t T_q);
+int dsa_prepare_local_metadata(const int32_t *cu_seqlens, const int32_t *cu_seqlens_padded,
+                               const int32_t *query_indices, const uint8_t *padding_mask,
+                               int32_t B, int64_t T_q, int64_t T_k, int32_t K, void *ws,
+                               size_t ws_bytes, dsa_thd_metadata *md, void *stream);
 
 /* --------------------------------------------------------------------------
  * Lightning indexer + top-k (GLM-5.2 page, "How DSA works": the indexer
@@ -117,6 +147,9 @@ int dsa_prepare_thd_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, in
  * idx[t, 0:n], idx[t, n:K] = -1, len[t] = n.  No score matrix is stored.
  *
  *   q_idx [T, H_i, D_i] bf16   k_idx [T, D_i] bf16   w [T, H_i] fp32
+ * (with metadata from dsa_prepare_local_metadata: q_idx, w, idx and len have
+ * T = md->T local rows, k_idx has md->total_key_tokens rows, and indices are
+ * key-tensor coordinates)
  *   idx   [T, K] int32 (out)   len [T] int32 (out)
  * Supported: 1 <= H_i <= 64, D_i in {64, 128}, 1 <= K <= 2048,
  * T <= INT32_MAX - 4096 (DSA_ERR_INVALID_VALUE otherwise).

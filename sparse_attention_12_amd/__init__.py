@@ -35,7 +35,8 @@ class _Metadata(C.Structure):
                 ("topk_length", C.c_void_p), ("row_order", C.c_void_p), ("groups", C.c_void_p),
                 ("T", C.c_int64), ("B", C.c_int32), ("K", C.c_int32), ("max_seqlen", C.c_int32),
                 ("all_rows_nonempty", C.c_int32), ("total_pairs", C.c_int64),
-                ("total_valid", C.c_int64), ("n_groups", C.c_int32)]
+                ("total_valid", C.c_int64), ("n_groups", C.c_int32), ("gpos", C.c_void_p),
+                ("group_first", C.c_void_p), ("total_key_tokens", C.c_int64)]
 
 
 _lib = None
@@ -58,6 +59,11 @@ def lib():
         L.dsa_thd_metadata_workspace_size.argtypes = [i64]
         L.dsa_prepare_thd_metadata.restype = C.c_int
         L.dsa_prepare_thd_metadata.argtypes = [vp, i32, i64, i32, vp, sz, C.POINTER(_Metadata), vp]
+        L.dsa_local_metadata_workspace_size.restype = sz
+        L.dsa_local_metadata_workspace_size.argtypes = [i64]
+        L.dsa_prepare_local_metadata.restype = C.c_int
+        L.dsa_prepare_local_metadata.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp, sz,
+                                                 C.POINTER(_Metadata), vp]
         L.dsa_indexer_topk_workspace_size.restype = sz
         L.dsa_indexer_topk_workspace_size.argtypes = [i64, i32, i32, i32]
         L.dsa_indexer_topk.restype = C.c_int
@@ -155,6 +161,10 @@ class ThdMetadata:
         return self._s.T
 
     @property
+    def total_key_tokens(self):
+        return self._s.total_key_tokens
+
+    @property
     def seq_start(self):
         return self._view("seq_start", self._s.T)
 
@@ -201,6 +211,40 @@ def prepare_thd_metadata(cu_seqlens: torch.Tensor, K: int = MAX_INDEXER_TOPK,
     return ThdMetadata(md, ws, cu_seqlens)
 
 
+def prepare_local_metadata(cu_seqlens: torch.Tensor, total_key_tokens: int,
+                           K: int = MAX_INDEXER_TOPK, cu_seqlens_padded=None, query_indices=None,
+                           padding_mask=None) -> ThdMetadata:
+    """dsa_prepare_local_metadata: local query rows (global padded-storage coordinates in
+    `query_indices`, int32 [T_q]; padding rows flagged in `padding_mask`, bool [T_q]) against
+    gathered global keys of `total_key_tokens` rows laid out by `cu_seqlens_padded`."""
+    op = "prepare_local_metadata"
+    _require(op, cu_seqlens, cu_seqlens_padded, query_indices, padding_mask)
+    _dtype(op, "cu_seqlens", cu_seqlens, torch.int32)
+    _dtype(op, "cu_seqlens_padded", cu_seqlens_padded, torch.int32)
+    _dtype(op, "query_indices", query_indices, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError(f"{op}: cu_seqlens must be 1-D with at least 2 entries")
+    B = cu_seqlens.numel() - 1
+    if cu_seqlens_padded is not None and cu_seqlens_padded.shape != cu_seqlens.shape:
+        raise ValueError(f"{op}: cu_seqlens_padded must match cu_seqlens")
+    if query_indices is not None:
+        T_q = query_indices.numel()
+    else:
+        T_q = int((cu_seqlens_padded if cu_seqlens_padded is not None else cu_seqlens)[-1].item())
+    pm = None
+    if padding_mask is not None:
+        if padding_mask.dtype != torch.bool or padding_mask.shape != (T_q,):
+            raise ValueError(f"{op}: padding_mask must be bool [T_q]")
+        pm = padding_mask.to(torch.uint8)
+    ws_bytes = lib().dsa_local_metadata_workspace_size(T_q)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=cu_seqlens.device)
+    md = _Metadata()
+    _call(lib().dsa_prepare_local_metadata, op, cu_seqlens.data_ptr(), _ptr(cu_seqlens_padded),
+          _ptr(query_indices), _ptr(pm), B, T_q, int(total_key_tokens), int(K), ws.data_ptr(),
+          ws_bytes, C.byref(md), _stream())
+    return ThdMetadata(md, ws, cu_seqlens)
+
+
 def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
                  meta: ThdMetadata, K: int = MAX_INDEXER_TOPK, idx=None, length=None):
     """dsa_indexer_topk -> (idx int32 [T,K] ascending with -1 suffix, len int32 [T])."""
@@ -212,9 +256,11 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     if q_idx.dim() != 3 or k_idx.dim() != 2 or w.dim() != 2:
         raise ValueError(f"{op}: expected q_idx [T,H,D], k_idx [T,D], w [T,H]")
     T, H, D = q_idx.shape
-    if k_idx.shape != (T, D) or w.shape != (T, H) or T != meta.T:
+    Tk = meta.total_key_tokens
+    if k_idx.shape != (Tk, D) or w.shape != (T, H) or T != meta.T:
         raise ValueError(f"{op}: shapes {tuple(q_idx.shape)}, {tuple(k_idx.shape)}, "
-                         f"{tuple(w.shape)} do not match T={meta.T}")
+                         f"{tuple(w.shape)} do not match T={meta.T} query rows and "
+                         f"{Tk} key rows")
     if not isinstance(K, int) or isinstance(K, bool):
         raise TypeError(f"{op}: K must be an int")
     if idx is None:

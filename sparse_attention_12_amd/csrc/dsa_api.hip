@@ -173,9 +173,166 @@ int dsa_prepare_thd_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, in
   const int32_t ng = n_index_groups(cu);
   md->groups = groups;
   md->n_groups = ng;
+  md->gpos = nullptr;
+  md->group_first = nullptr;
+  md->total_key_tokens = T;
   e = dsa::launch_thd_metadata(cu_seqlens, B, T, K, md->seq_start, md->causal_len,
                                md->topk_length, md->row_order, groups, ng, s);
   if (e != hipSuccess) return hip_fail(e, "prepare_thd_metadata: launch");
+  return DSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Local query rows against gathered global keys.  The inputs are read on the host (one
+// synchronisation); rows, groups and their order are built there and uploaded into the
+// workspace, which takes a second synchronisation so that no host buffer is read after it
+// has been released.  workspace: seq_start | causal_len | topk_length | row_order | groups |
+// group_first | gpos   (each 256-B aligned)
+size_t dsa_local_metadata_workspace_size(int64_t T_q) {
+  if (T_q < 0) return 0;
+  const size_t a = align_up(static_cast<size_t>(T_q) * sizeof(int32_t));
+  return 7 * a + 256;
+}
+
+int dsa_prepare_local_metadata(const int32_t *cu_seqlens, const int32_t *cu_seqlens_padded,
+                               const int32_t *query_indices, const uint8_t *padding_mask,
+                               int32_t B, int64_t T_q, int64_t T_k, int32_t K, void *ws,
+                               size_t ws_bytes, dsa_thd_metadata *md, void *stream) {
+  g_last_error.clear();
+  if (!md) return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: md is NULL");
+  if (B < 1) return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: B=%d must be >= 1", B);
+  if (T_q < 0 || T_q > INT32_MAX || T_k < 0 || T_k > INT32_MAX)
+    return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: T_q=%lld / T_k=%lld out of range",
+                static_cast<long long>(T_q), static_cast<long long>(T_k));
+  if (K < 1 || K > DSA_MAX_INDEXER_TOPK)
+    return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: K=%d not in [1, %d]", K,
+                DSA_MAX_INDEXER_TOPK);
+  if (!cu_seqlens)
+    return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: cu_seqlens is NULL");
+  const size_t need = dsa_local_metadata_workspace_size(T_q);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "prepare_local_metadata: workspace needs %zu bytes, got %zu",
+                need, ws ? ws_bytes : static_cast<size_t>(0));
+  if (int rc = check_device()) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  std::vector<int32_t> cu(static_cast<size_t>(B) + 1), cp(static_cast<size_t>(B) + 1);
+  std::vector<int32_t> gp(static_cast<size_t>(T_q));
+  std::vector<uint8_t> pm(padding_mask ? static_cast<size_t>(T_q) : 0);
+  hipError_t e = hipMemcpyAsync(cu.data(), cu_seqlens, cu.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && cu_seqlens_padded)
+    e = hipMemcpyAsync(cp.data(), cu_seqlens_padded, cp.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && query_indices && T_q > 0)
+    e = hipMemcpyAsync(gp.data(), query_indices, gp.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && padding_mask && T_q > 0)
+    e = hipMemcpyAsync(pm.data(), padding_mask, pm.size(), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "prepare_local_metadata: copy of the inputs");
+  if (!cu_seqlens_padded) cp = cu;
+  if (cu[0] != 0 || cp[0] != 0)
+    return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: offsets must start at 0");
+  for (int32_t b = 0; b < B; ++b) {
+    if (cu[b + 1] < cu[b] || cp[b + 1] < cp[b])
+      return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: offsets decrease at %d", b);
+    if (cp[b + 1] - cp[b] < cu[b + 1] - cu[b])
+      return fail(DSA_ERR_INVALID_VALUE,
+                  "prepare_local_metadata: padded sequence %d shorter than its real length", b);
+  }
+  if (cp[B] > T_k)
+    return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: offsets end at %d > T_k=%lld",
+                cp[B], static_cast<long long>(T_k));
+  if (!query_indices) {
+    if (T_q != cp[B])
+      return fail(DSA_ERR_INVALID_VALUE,
+                  "prepare_local_metadata: without query_indices T_q must equal %d", cp[B]);
+    for (int64_t i = 0; i < T_q; ++i) gp[i] = static_cast<int32_t>(i);
+  }
+  // rows
+  const size_t n = static_cast<size_t>(T_q);
+  std::vector<int32_t> start(n), clen(n), tlen(n);
+  int32_t max_len = 0;
+  int64_t pairs = 0, valid = 0;
+  bool nonempty = true;
+  for (size_t i = 0; i < n; ++i) {
+    const int32_t p = gp[i];
+    if (p < 0 || p >= cp[B])
+      return fail(DSA_ERR_INVALID_VALUE, "prepare_local_metadata: query_indices[%zu]=%d outside "
+                  "[0, %d)", i, p, cp[B]);
+    const int32_t b = static_cast<int32_t>(std::upper_bound(cp.begin(), cp.end(), p) -
+                                           cp.begin()) - 1;
+    const int32_t pos = p - cp[b];
+    const bool real = pos < cu[b + 1] - cu[b] && !(padding_mask && pm[i]);
+    start[i] = cp[b];
+    clen[i] = real ? pos + 1 : 0;
+    tlen[i] = std::min(clen[i], K);
+    max_len = std::max(max_len, clen[i]);
+    pairs += clen[i];
+    valid += tlen[i];
+    nonempty = nonempty && real;
+  }
+  // groups: runs of up to kIdxRowsPerGroup real rows, consecutive in both row and key
+  // position inside one sequence, cut so that each run ends a group; padding rows alone
+  std::vector<int32_t> glast, gfirst;
+  for (size_t i = 0; i < n;) {
+    size_t j = i;
+    if (clen[i] > 0)
+      while (j + 1 < n && clen[j + 1] > 0 && start[j + 1] == start[i] && gp[j + 1] == gp[j] + 1)
+        ++j;
+    // rows i..j form one run: groups end at j, j - 4, ...
+    for (int64_t last = static_cast<int64_t>(j); last >= static_cast<int64_t>(i);
+         last -= dsa::kIdxRowsPerGroup) {
+      glast.push_back(static_cast<int32_t>(last));
+      gfirst.push_back(static_cast<int32_t>(
+          std::max<int64_t>(last - (dsa::kIdxRowsPerGroup - 1), static_cast<int64_t>(i))));
+    }
+    i = j + 1;
+  }
+  // longest first (cost = keys of the last row), ties in row order
+  std::vector<int32_t> gorder(glast.size());
+  for (size_t g = 0; g < gorder.size(); ++g) gorder[g] = static_cast<int32_t>(g);
+  std::stable_sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b2) {
+    return clen[glast[a]] > clen[glast[b2]];
+  });
+  std::vector<int32_t> groups(glast.size()), group_first(glast.size());
+  for (size_t g = 0; g < gorder.size(); ++g) {
+    groups[g] = glast[gorder[g]];
+    group_first[g] = gfirst[gorder[g]];
+  }
+  std::vector<int32_t> order(n);
+  for (size_t i = 0; i < n; ++i) order[i] = static_cast<int32_t>(i);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b2) { return clen[a] > clen[b2]; });
+
+  char *base = reinterpret_cast<char *>(align_up(reinterpret_cast<uintptr_t>(ws)));
+  const size_t a = align_up(n * sizeof(int32_t));
+  md->seq_start = reinterpret_cast<int32_t *>(base);
+  md->causal_len = reinterpret_cast<int32_t *>(base + a);
+  md->topk_length = reinterpret_cast<int32_t *>(base + 2 * a);
+  md->row_order = reinterpret_cast<int32_t *>(base + 3 * a);
+  md->groups = reinterpret_cast<int32_t *>(base + 4 * a);
+  md->group_first = reinterpret_cast<int32_t *>(base + 5 * a);
+  md->gpos = reinterpret_cast<int32_t *>(base + 6 * a);
+  md->T = T_q;
+  md->B = B;
+  md->K = K;
+  md->max_seqlen = max_len;
+  md->all_rows_nonempty = nonempty ? 1 : 0;
+  md->total_pairs = pairs;
+  md->total_valid = valid;
+  md->n_groups = static_cast<int32_t>(groups.size());
+  md->total_key_tokens = T_k;
+  const std::pair<int32_t *, const std::vector<int32_t> *> up[] = {
+      {md->seq_start, &start}, {md->causal_len, &clen}, {md->topk_length, &tlen},
+      {md->row_order, &order}, {md->groups, &groups}, {md->group_first, &group_first},
+      {md->gpos, &gp}};
+  for (const auto &u : up)
+    if (!u.second->empty()) {
+      e = hipMemcpyAsync(u.first, u.second->data(), u.second->size() * 4, hipMemcpyHostToDevice,
+                         s);
+      if (e != hipSuccess) return hip_fail(e, "prepare_local_metadata: upload");
+    }
+  e = hipStreamSynchronize(s);  // the host vectors are released on return
+  if (e != hipSuccess) return hip_fail(e, "prepare_local_metadata: stream synchronize");
   return DSA_OK;
 }
 
@@ -206,16 +363,23 @@ int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *
   const int64_t T = md->T;
   if (T == 0) return DSA_OK;
   // key positions are 32-bit inside the kernel, including a few tiles of look-ahead
-  if (T > INT32_MAX - 4096)
-    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: T=%lld exceeds %d", static_cast<long long>(T),
-                INT32_MAX - 4096);
+  const int64_t Tmax = std::max<int64_t>(T, md->total_key_tokens);
+  if (Tmax > INT32_MAX - 4096)
+    return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: T=%lld exceeds %d",
+                static_cast<long long>(Tmax), INT32_MAX - 4096);
   if (!q_idx || !k_idx || !w || !idx || !len)
     return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: NULL tensor pointer");
   if (!aligned16(q_idx) || !aligned16(k_idx))
     return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: q_idx/k_idx must be 16-byte aligned");
   if (int rc = check_device()) return rc;
-  hipError_t e = dsa::launch_indexer_topk(q_idx, k_idx, w, md->seq_start, md->groups,
-                                          md->n_groups, T, H_i, D_i, K, idx, len,
+  dsa::IndexerRows rows;
+  rows.seq_start = md->seq_start;
+  rows.causal_len = md->causal_len;
+  rows.gpos = md->gpos;
+  rows.groups = md->groups;
+  rows.group_first = md->group_first;
+  rows.n_groups = md->n_groups;
+  hipError_t e = dsa::launch_indexer_topk(q_idx, k_idx, w, rows, H_i, D_i, K, idx, len,
                                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "indexer_topk: launch");
   return DSA_OK;

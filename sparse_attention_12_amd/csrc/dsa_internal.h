@@ -28,10 +28,21 @@ hipError_t launch_thd_metadata(const int32_t *cu, int32_t B, int64_t T, int32_t 
                                int32_t *row_order, int32_t *groups, int32_t n_groups,
                                hipStream_t s);
 
+// Query rows of one indexer call (device arrays of the metadata).  gpos / group_first are
+// NULL when every row is its own key position (one tensor of queries and keys); otherwise
+// gpos[i] is the key position of local row i and group_first[g] the first row of group g.
+struct IndexerRows {
+  const int32_t *seq_start;   // [T_q] key position of the row's sequence start
+  const int32_t *causal_len;  // [T_q] keys of the row (0: padding row)
+  const int32_t *gpos;        // [T_q] or NULL
+  const int32_t *groups;      // [n_groups] last row of each group
+  const int32_t *group_first; // [n_groups] or NULL
+  int32_t n_groups;
+};
+
 hipError_t launch_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
-                               const int32_t *seq_start, const int32_t *groups, int32_t n_groups,
-                               int64_t T, int32_t H, int32_t D, int32_t K, int32_t *idx,
-                               int32_t *len, hipStream_t s);
+                               const IndexerRows &r, int32_t H, int32_t D, int32_t K,
+                               int32_t *idx, int32_t *len, hipStream_t s);
 
 hipError_t launch_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                                  const int32_t *topk_length, int64_t T_q, int32_t H,

@@ -547,8 +547,10 @@ struct KeyTileLoads {
 template <int NMT, int D>
 __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
-    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ groups, int64_t T, int H,
-    int K, int32_t *__restrict__ idx_out, int32_t *__restrict__ len_out) {
+    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ causal_len,
+    const int32_t *__restrict__ gpos, const int32_t *__restrict__ groups,
+    const int32_t *__restrict__ group_first, int H, int K, int32_t *__restrict__ idx_out,
+    int32_t *__restrict__ len_out) {
   using C = IndexerCfg<D>;
   constexpr int NKK = D / 16;  // k-steps of the 32x32x16 MFMA
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -560,12 +562,18 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = wave & (kRows - 1);  // waves w and w + 4 share a row (and a SIMD)
   const int half = wave >> 2;
+  // Rows are local query rows (q, w and the output); key positions are global coordinates of
+  // the key tensor.  Without local coordinates (gpos NULL) the two coincide and a group is the
+  // run of up to kRows rows that ends at `last`, clipped at the sequence start.
   const int last = groups[blockIdx.x];
   const int start = seq_start[last];
-  const int first = last - (kRows - 1) > start ? last - (kRows - 1) : start;
-  const int t = first + row;
+  const int first = group_first ? group_first[blockIdx.x]
+                                : (last - (kRows - 1) > start ? last - (kRows - 1) : start);
+  const int lastg = gpos ? gpos[last] : last;  // key position of the group's last row
+  const int t = first + row;                   // this wave's local row
   const bool row_ok = t <= last;
-  const int L = row_ok ? t - start + 1 : 0;
+  const int tg = lastg - (last - t);           // its key position (rows of a group are consecutive)
+  const int L = row_ok ? causal_len[t] : 0;    // 0 for a padding row
   const bool compute = row_ok && L > K;
 
   if (row_ok && !compute && half == 0) {
@@ -573,15 +581,16 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     for (int j = lane; j < K; j += 64) out[j] = j < L ? start + j : -1;
     if (lane == 0) len_out[t] = L;
   }
-  if (last - start + 1 <= K) return;  // every row of the group is a whole prefix (uniform)
+  // every row of the group is a whole prefix or padding (uniform): the last row is the longest
+  if (causal_len[last] <= K) return;
 
   // tiles 0 and 1 in flight while the query block loads; tile it+2 is issued at the top of
   // iteration it
   const uint32_t tile_lds = lds_addr(&sm.tile[0][0]);
   KeyTileLoads<D> loads;
   loads.init(wave);
-  loads.issue(tile_lds, k, start, last, wave);
-  if (last - start >= kTileKeys) loads.issue(tile_lds + C::kTileBytes, k, start + kTileKeys, last, wave);
+  loads.issue(tile_lds, k, start, lastg, wave);
+  if (lastg - start >= kTileKeys) loads.issue(tile_lds + C::kTileBytes, k, start + kTileKeys, lastg, wave);
 
   // ---- this row's query block (A operand) and head weights
   bf16x8 qa[NMT][NKK];
@@ -658,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ap_sc),
                                                      __float_as_uint(ap_sc), false, false);
     const uint32_t u = orderable(ap_sc + __uint_as_float(sw[1]));
-    const bool pass = ap_on && lane < 32 && ap_key <= t && u > tau_eff;
+    const bool pass = ap_on && lane < 32 && ap_key <= tg && u > tau_eff;
     const uint64_t m = __ballot(pass);
     if (m) {
       const int o = my_n + static_cast<int>(__builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
@@ -687,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
 #pragma unroll
       for (int m = 0; m < NMT; ++m) cur[m] = mfma32(qa[m][kk], bf[kk], kk == 0 ? f32x16{} : cur[m]);
       if (kk == 0 && issue_kb >= 0)
-        loads.issue(tile_lds + issue_buf * C::kTileBytes, k, issue_kb, last, wave);
+        loads.issue(tile_lds + issue_buf * C::kTileBytes, k, issue_kb, lastg, wave);
       if constexpr (decltype(with_prev)::value) {
 #pragma unroll
         for (int j = 0; j < kSlice; j += 2) {
@@ -739,7 +748,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
         if (n > C::kCap - 3 * kTileKeys) {  // too many ties to make room: exact selection
           // exactly K kept, all at or above the K-th key kth (> the old threshold); a later key
           // equal to kth loses the tie, but the threshold kth - 1 keeps every kept key above it
-          const uint32_t kth = select_exact(ck, cp, sm.hist[row], n, K, start, t);
+          const uint32_t kth = select_exact(ck, cp, sm.hist[row], n, K, start, tg);
           if (kth > 0u) {
             tau = kth - 1u;
             has = true;
@@ -781,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   int key_prev = 0;
   auto step = [&](int kb, f32x16 (&cur)[NMT], f32x16 (&prev)[NMT]) __attribute__((always_inline)) {
     if (kb > start) {
-      if (last - kb >= kTileKeys) wait_vm<C::kLoadsPerWave>();  // the next tile may stay in flight
+      if (lastg - kb >= kTileKeys) wait_vm<C::kLoadsPerWave>();  // the next tile may stay in flight
       else wait_tile();
       lds_barrier();  // this tile is complete everywhere; the previous one is free; every
                       // append made so far is visible
@@ -789,20 +798,20 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     // this step's compaction flag; read now, used after the MFMAs
     const int cflag = sm.compact[sidx & 1];
     // the tile two ahead goes into the previous tile's buffer, issued behind the first MFMAs
-    const int issue_kb = last - kb >= 2 * kTileKeys ? kb + 2 * kTileKeys : -1;
+    const int issue_kb = lastg - kb >= 2 * kTileKeys ? kb + 2 * kTileKeys : -1;
     const int issue_buf = buf >= C::kNBuf - 2 ? buf + 2 - C::kNBuf : buf + 2;
 
     if (half == 1) append();  // the tile pending since the previous step
     // ---- this wave's 32 keys of the tile
     const int kbase = kb + half * 32;
-    const bool do_cur = compute && kbase <= t;
+    const bool do_cur = compute && kbase <= tg;
     float sc = 0.0f;
     if (do_cur && have_prev) {
       sc = mfma_tile(sm.tile[buf], cur, prev, std::true_type{}, issue_kb, issue_buf);
     } else if (do_cur) {
       mfma_tile(sm.tile[buf], cur, prev, std::false_type{}, issue_kb, issue_buf);
     } else {
-      if (issue_kb >= 0) loads.issue(tile_lds + issue_buf * C::kTileBytes, k, issue_kb, last, wave);
+      if (issue_kb >= 0) loads.issue(tile_lds + issue_buf * C::kTileBytes, k, issue_kb, lastg, wave);
       if (have_prev) sc = score_only(prev);
     }
     if (__builtin_amdgcn_readfirstlane(cflag)) compact_rows();
@@ -833,13 +842,13 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   while (true) {  // two tiles per trip so that the accumulator sets alternate without copies
     step(kb, acc_a, acc_b);
     kb += kTileKeys;
-    if (kb > last) {
+    if (kb > lastg) {
       drain(acc_a);
       break;
     }
     step(kb, acc_b, acc_a);
     kb += kTileKeys;
-    if (kb > last) {
+    if (kb > lastg) {
       drain(acc_b);
       break;
     }
@@ -852,39 +861,37 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     uint32_t *sk = reinterpret_cast<uint32_t *>(&sm.tile[0][0]) + 4 * 1024 + row * 2 * kScratch;
     int32_t *sp = reinterpret_cast<int32_t *>(sk + kScratch);
     const int n = merge_stacks(my_n, __builtin_amdgcn_readfirstlane(sm.cntb[row]));
-    select_and_write(ck, cp, sm.hist[row], n, K, my_has_tau, my_tau, start, t, bm, sk, sp,
+    select_and_write(ck, cp, sm.hist[row], n, K, my_has_tau, my_tau, start, tg, bm, sk, sp,
                      idx_out + static_cast<int64_t>(t) * K);
     if (lane == 0) len_out[t] = K;
   }
 }
 
 template <int NMT, int D>
-hipError_t launch(const uint16_t *q, const uint16_t *k, const float *w, const int32_t *seq_start,
-                  const int32_t *groups, int32_t n_groups, int64_t T, int32_t H, int32_t K,
-                  int32_t *idx, int32_t *len, hipStream_t s) {
+hipError_t launch(const uint16_t *q, const uint16_t *k, const float *w, const IndexerRows &r,
+                  int32_t H, int32_t K, int32_t *idx, int32_t *len, hipStream_t s) {
   const size_t smem = sizeof(IndexerSmem<D>);
   auto kern = indexer_topk_kernel<NMT, D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  DSA_LAUNCH("indexer_topk", kern, dim3(n_groups), dim3(kThreads), smem, s, q, k, w, seq_start,
-             groups, T, H, K, idx, len);
+  DSA_LAUNCH("indexer_topk", kern, dim3(r.n_groups), dim3(kThreads), smem, s, q, k, w,
+             r.seq_start, r.causal_len, r.gpos, r.groups, r.group_first, H, K, idx, len);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
-                               const int32_t *seq_start, const int32_t *groups, int32_t n_groups,
-                               int64_t T, int32_t H, int32_t D, int32_t K, int32_t *idx,
-                               int32_t *len, hipStream_t s) {
-  if (n_groups == 0) return hipSuccess;
+                               const IndexerRows &r, int32_t H, int32_t D, int32_t K,
+                               int32_t *idx, int32_t *len, hipStream_t s) {
+  if (r.n_groups == 0) return hipSuccess;
   const bool two = H > 32;
-  if (D == 128) return two ? launch<2, 128>(q, k, w, seq_start, groups, n_groups, T, H, K, idx, len, s)
-                           : launch<1, 128>(q, k, w, seq_start, groups, n_groups, T, H, K, idx, len, s);
-  if (D == 64) return two ? launch<2, 64>(q, k, w, seq_start, groups, n_groups, T, H, K, idx, len, s)
-                          : launch<1, 64>(q, k, w, seq_start, groups, n_groups, T, H, K, idx, len, s);
+  if (D == 128) return two ? launch<2, 128>(q, k, w, r, H, K, idx, len, s)
+                           : launch<1, 128>(q, k, w, r, H, K, idx, len, s);
+  if (D == 64) return two ? launch<2, 64>(q, k, w, r, H, K, idx, len, s)
+                          : launch<1, 64>(q, k, w, r, H, K, idx, len, s);
   return hipErrorInvalidValue;
 }
 

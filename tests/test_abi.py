@@ -117,6 +117,19 @@ def test_argument_errors_without_device(dsa):
     assert bwd(K=4097) == pkg.DSA_ERR_INVALID_VALUE and "4096" in _err(dsa)
 
 
+def test_local_metadata_argument_errors(dsa):
+    import sparse_attention_12_amd as pkg
+    md = pkg._Metadata()
+    assert dsa.dsa_prepare_local_metadata(16, None, 16, None, 0, 8, 8, 16, None, 0, C.byref(md),
+                                          None) == pkg.DSA_ERR_INVALID_VALUE
+    assert "B=0" in _err(dsa)
+    assert dsa.dsa_prepare_local_metadata(16, None, 16, None, 1, 8, 8, 2049, None, 0,
+                                          C.byref(md), None) == pkg.DSA_ERR_INVALID_VALUE
+    assert dsa.dsa_prepare_local_metadata(16, None, 16, None, 1, 8, 8, 16, None, 0, C.byref(md),
+                                          None) == pkg.DSA_ERR_WORKSPACE
+    assert dsa.dsa_local_metadata_workspace_size(8) >= 7 * 32
+
+
 def test_sink_entry_points_reject_missing_sink(dsa):
     import sparse_attention_12_amd as pkg
     assert dsa.dsa_sparse_mla_fwd_sink(16, 16, 16, None, 4, 4, 16, 576, 512, 8, 0.1, None, 16,

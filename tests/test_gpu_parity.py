@@ -454,3 +454,54 @@ def test_sink_empty_rows_minus_inf_sink_and_chunks():
     torch.cuda.synchronize()
     assert (dkv_c - dkv).abs().max().item() <= 1e-5 * dkv.abs().max().item() + 1e-4
     assert (ds_c - dsink).abs().max().item() <= 1e-5 * dsink.abs().max().item() + 1e-4
+
+
+# ----------------------------------------------------------------------------------------
+# local query rows against gathered global keys (padded-storage coordinates)
+# ----------------------------------------------------------------------------------------
+
+def test_local_indexer_padded_storage_two_ranks_bit_exact():
+    """Two ranks each own zig-zag chunks of the real tokens (global padded coordinates), plus a
+    few padding coordinates and one masked row; integer inputs make every top-k set unique, so
+    each rank's indices equal the oracle's exactly.  Rows reach 2000 keys (many tiles and
+    compaction rounds) and groups are cut at chunk and sequence boundaries."""
+    dsa = _dsa()
+    cu, cu_pad, K, H, D = [0, 700, 1900, 2450], [0, 768, 2000, 2560], 300, 64, 128
+    T, Tk = cu[-1], cu_pad[-1]
+    g = torch.Generator().manual_seed(31)
+    qf = torch.randint(-4, 5, (T, H, D), generator=g).to(torch.bfloat16)
+    wf = torch.tensor([0.5, 1.0, 2.0, 0.25])[torch.randint(0, 4, (T, H), generator=g)]
+    kc = torch.randint(-4, 5, (T, D), generator=g).to(torch.bfloat16)
+    kp = torch.randint(-4, 5, (Tk, D), generator=g).to(torch.bfloat16)   # padding rows: junk
+    seq = np.searchsorted(np.array(cu), np.arange(T), side="right") - 1
+    coord = (np.arange(T) + np.array(cu_pad)[seq] - np.array(cu)[seq]).astype(np.int32)
+    kp[torch.from_numpy(coord).long()] = kc
+    chunks = np.array_split(np.arange(T), 8)
+    ranks = [np.concatenate([chunks[0], chunks[3], chunks[4], chunks[7]]),
+             np.concatenate([chunks[1], chunks[2], chunks[5], chunks[6]])]
+    extra_coord = np.array([705, 720, 1999, 2555], np.int32)          # padding positions
+    for r, rows in enumerate(ranks):
+        qi = np.concatenate([coord[rows], extra_coord]).astype(np.int32)
+        qr = torch.cat([qf[rows], qf[:4]])
+        wr = torch.cat([wf[rows], wf[:4]])
+        mask = np.zeros(qi.size, bool)
+        mask[len(rows) // 2] = True                                     # one masked real row
+        md = dsa.prepare_local_metadata(torch.tensor(cu, dtype=torch.int32, device=dev), Tk, K,
+                                        cu_seqlens_padded=torch.tensor(cu_pad, dtype=torch.int32,
+                                                                       device=dev),
+                                        query_indices=torch.from_numpy(qi).to(dev),
+                                        padding_mask=torch.from_numpy(mask).to(dev))
+        idx, ln = dsa.indexer_topk(qr.to(dev).contiguous(), kp.to(dev), wr.to(dev).contiguous(),
+                                   md, K)
+        torch.cuda.synchronize()
+        ridx, rln = oracle.indexer_topk_local(qr.contiguous(), kp, wr.contiguous(), cu, K,
+                                              cu_seqlens_padded=cu_pad, query_indices=qi,
+                                              padding_mask=mask)
+        np.testing.assert_array_equal(_np(ln), rln, err_msg=f"rank {r} lengths")
+        np.testing.assert_array_equal(_np(idx), ridx, err_msg=f"rank {r} indices")
+        assert (rln[-4:] == 0).all() and rln[len(rows) // 2] == 0
+        # metadata of a real row: its sequence start in padded storage and its causal length
+        i = 0
+        b = seq[rows[i]]
+        assert int(md.seq_start[i]) == cu_pad[b]
+        assert int(md.causal_len[i]) == rows[i] - cu[b] + 1
