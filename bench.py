@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--bwd-passes", type=int, default=1,
                     help="query-row passes of the backward (several passes overlap a pass's "
                          "key-gradient reduction with the next pass's compute)")
+    ap.add_argument("--cp", type=int, default=1, metavar="N",
+                    help="time one GPU's share under N-way context parallelism: the query rows "
+                         "of rank 0 (zig-zag: chunks 0 and 2N-1 of every sequence split in 2N) "
+                         "against all keys, through the local-query metadata")
     ap.add_argument("--sink", action="store_true",
                     help="run the step with a per-head attention sink (sink forward epilogue and "
                          "sink gradient kernels added)")
@@ -248,6 +252,21 @@ def main():
     if has_indexer:
         inputs.update(gen.indexer_inputs(args.config, device=dev))
     att = gen.attention_inputs(args.config, device=dev)
+    T_keys = T
+    local_rows = None
+    if args.cp > 1:
+        if not has_indexer:
+            raise SystemExit("--cp needs a workload with an indexer stage")
+        # rank 0's rows under zig-zag context parallelism
+        parts = []
+        for b in range(len(cfg.cu_seqlens) - 1):
+            ch = np.array_split(np.arange(cfg.cu_seqlens[b], cfg.cu_seqlens[b + 1]), 2 * args.cp)
+            parts += [ch[0], ch[-1]]
+        local_rows = torch.from_numpy(np.concatenate(parts).astype(np.int32)).to(dev)
+        sel = local_rows.long()
+        inputs.update(q_idx=inputs["q_idx"][sel].contiguous(), w=inputs["w"][sel].contiguous())
+        att = dict(att, q=att["q"][sel].contiguous(), dout=att["dout"][sel].contiguous())
+        T = local_rows.numel()
     inputs.update(q=att["q"], kv=att["kv"], dout=att["dout"])
     H, Dqk, Dv = cfg.heads, cfg.d_qk, cfg.d_v
     idx_buf = torch.empty((T, K), dtype=torch.int32, device=dev)
@@ -255,10 +274,10 @@ def main():
     out_buf = torch.empty((T, H, Dv), dtype=torch.bfloat16, device=dev)
     lse_buf = torch.empty((T, H), dtype=torch.float32, device=dev)
     dq_buf = torch.empty_like(att["q"])
-    dkv_buf = torch.empty((T, Dqk), dtype=torch.float32, device=dev)
+    dkv_buf = torch.empty((T_keys, Dqk), dtype=torch.float32, device=dev)
     # backward workspace for --bwd-passes passes over the query rows
     rows_per_pass = -(-T // max(1, args.bwd_passes))
-    ws = torch.empty(dsa.bwd_workspace_bytes(T, T, H, Dqk, K, rows_per_pass=rows_per_pass),
+    ws = torch.empty(dsa.bwd_workspace_bytes(T, T_keys, H, Dqk, K, rows_per_pass=rows_per_pass),
                      dtype=torch.uint8, device=dev)
     sink = gen.sink_logits(H, device=dev) if args.sink else None
     dsink_buf = torch.empty((H,), dtype=torch.float32, device=dev) if args.sink else None
@@ -273,7 +292,10 @@ def main():
     bwd_events = []  # (start, stop) around each backward call while timing
 
     def step():
-        md = dsa.prepare_thd_metadata(cu, K, T=T)
+        if local_rows is None:
+            md = dsa.prepare_thd_metadata(cu, K, T=T)
+        else:
+            md = dsa.prepare_local_metadata(cu, T_keys, K, query_indices=local_rows)
         if has_indexer:
             dsa.indexer_topk(inputs["q_idx"], inputs["k_idx"], inputs["w"], md, K, idx=idx_buf,
                              length=len_buf)
@@ -297,6 +319,12 @@ def main():
     md_host = dict(total_valid=md.total_valid)
     counts = workload_counts(md_host, cfg, cfg.idx_heads or 0, cfg.idx_dim or 0, K, H, Dqk, Dv,
                              kpool_valid)
+    if local_rows is not None:
+        # scored pairs of the local rows: every causal key of a row with L > K
+        L_rows = md.causal_len.to(torch.int64)
+        pairs = int(L_rows[L_rows > K].sum().item())
+        counts.update(idx_pairs=pairs,
+                      idx_flops=float(pairs) * 2 * cfg.idx_heads * cfg.idx_dim)
 
     timer = KernelTimer(dsa.lib(), 40 * args.steps)
     timing = True
@@ -349,7 +377,7 @@ def main():
             "sparse_mla_fwd": ("mfma", counts["fwd_flops"]),
             "sparse_mla_bwd_rows": ("mfma", counts["bwd_flops"] / passes),
             "sparse_mla_bwd_reduce": ("hbm", (counts["valid"] * (Dqk * 2 + 20) / passes
-                                              + 2 * T * Dqk * 4))}
+                                              + 2 * T_keys * Dqk * 4))}
     dom = max((n for n in work if n in per_kernel), key=lambda n: sum(per_kernel[n]))
     bound, amount = work[dom]
     if bound == "mfma":
@@ -375,10 +403,12 @@ def main():
                    "indexer": (f"{cfg.idx_heads}x{cfg.idx_dim}" if has_indexer else None),
                    "topk": K, "heads": H, "d_qk": Dqk, "d_v": Dv, "bwd_passes": args.bwd_passes,
                    "attention_sink": bool(args.sink),
+                   "context_parallel": ({"ranks": args.cp, "rank": 0, "local_tokens": T,
+                                         "key_tokens": T_keys} if args.cp > 1 else None),
                    "parallelism": "none"},
         "components": comp, "kernels": kernels, "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and local_rows is None:
         inputs.update(idx=idx_buf, len=len_buf)
         try:
             res["cpu_baseline"] = cpu_baseline(inputs, counts, T, K, args.cpu_seconds)
