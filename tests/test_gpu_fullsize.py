@@ -256,3 +256,98 @@ def test_full_indexshare_T131072_four_layers():
         _check_dkv_tails(att, b.idx, b.len, b.dkv, list(w.cu_seqlens), w.scale, R=4)
         del att
         torch.cuda.empty_cache()
+
+
+def test_full_thd_T32768_context_parallel_rank0():
+    """One GPU's share under 2-way zig-zag context parallelism at the bench workload's size
+    (the launch configuration of `bench.py --cp 2`): rank 0's 16384 query rows, in global
+    coordinates, against all 32768 keys.  Every row's structure is checked (length, ascending,
+    inside its causal range), sampled rows against the oracle under the near-tie rule (the
+    split has no padding, so local row i is global row coord[i]), and the forward / backward
+    of sampled rows against the oracle."""
+    dsa = _dsa()
+    w = gen.workload(3)
+    _log(f"workload {w.name} rank 0 of 2")
+    K, T = w.topk, w.T
+    inp = gen.indexer_inputs(3, device=dev)
+    parts = []
+    for b in range(len(w.cu_seqlens) - 1):
+        ch = np.array_split(np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]), 4)
+        parts += [ch[0], ch[-1]]
+    coord = np.concatenate(parts).astype(np.int32)
+    sel = torch.from_numpy(coord).to(dev).long()
+    md = dsa.prepare_local_metadata(inp["cu_seqlens"], T, K, query_indices=sel.int())
+    idx, ln = dsa.indexer_topk(inp["q_idx"][sel].contiguous(), inp["k_idx"],
+                               inp["w"][sel].contiguous(), md, K)
+    torch.cuda.synchronize()
+    # structure of every row
+    cu = np.array(w.cu_seqlens)
+    start = cu[np.searchsorted(cu, coord, side="right") - 1]
+    L = coord - start + 1
+    gi, gl = _np(idx), _np(ln)
+    np.testing.assert_array_equal(gl, np.minimum(L, K))
+    valid = np.arange(K)[None, :] < gl[:, None]
+    assert ((gi >= start[:, None]) | ~valid).all() and ((gi <= coord[:, None]) | ~valid).all()
+    assert (np.where(valid, gi, -1) == gi).all()
+    d = np.diff(gi, axis=1)
+    assert ((d > 0) | ~valid[:, 1:]).all()
+    # sampled rows against the oracle: the rank's longest rows, rows around L = K, spread rows
+    r = np.unique(np.concatenate([np.arange(len(coord) - 3, len(coord)),
+                                  np.flatnonzero((L >= K - 1) & (L <= K + 1))[:4],
+                                  np.linspace(0, len(coord) - 1, 6).astype(np.int64)]))
+    q_rows = inp["q_idx"][sel[r]].cpu()
+    w_rows = inp["w"][sel[r]].cpu()
+    k_all = oracle._u16(inp["k_idx"].cpu())
+    mism = 0
+    for j, i in enumerate(r):
+        ridx, rln, kth = oracle.indexer_topk_rows(q_rows[j:j + 1], k_all, w_rows[j:j + 1], cu, K,
+                                                  int(coord[i]))
+        assert rln[0] == gl[i], f"local row {i}"
+        mism += checks.check_topk_near_tie(q_rows[j:j + 1], k_all, w_rows[j:j + 1],
+                                           gi[i:i + 1], ridx, kth, np.array([coord[i]]))
+    _log(f"indexer: {len(r)} sampled local rows, {mism} near-tie swaps")
+    # attention of the local rows against all latent rows, sampled rows against the oracle
+    att = gen.attention_inputs(3, device=dev)
+    q_l, dout_l = att["q"][sel].contiguous(), att["dout"][sel].contiguous()
+    out, lse = dsa.sparse_mla_fwd(q_l, att["kv"], idx, w.scale, ln)
+    dq, _ = dsa.sparse_mla_bwd(q_l, att["kv"], idx, out, lse, dout_l, w.scale, ln)
+    torch.cuda.synchronize()
+    rs = r[-4:]
+    ri = torch.from_numpy(rs).to(dev)
+    ro, rl = oracle.sparse_mla_fwd(q_l[ri].cpu(), att["kv"].cpu(), gi[rs], gl[rs], w.scale, w.d_v)
+    checks.assert_close("cp out", _np(out[ri].float()), ro, checks.ATOL_OUT)
+    checks.assert_close("cp lse", _np(lse[ri]), rl, checks.ATOL_LSE)
+    rdq, _ = oracle.sparse_mla_bwd(q_l[ri].cpu(), att["kv"].cpu(), gi[rs], gl[rs],
+                                   dout_l[ri].cpu(), w.scale)
+    checks.assert_close("cp dq", _np(dq[ri].float()), rdq, checks.ATOL_OUT)
+
+
+def test_full_thd_T32768_attention_sink_sampled_rows():
+    """The bench workload with a per-head sink (the launch configuration of `bench.py --sink`):
+    O', LSE' and dq of sampled rows against the oracle with the same sink; dsink is a sum over
+    every row and is checked at small sizes (tests/test_gpu_parity.py)."""
+    dsa = _dsa()
+    w = gen.workload(3)
+    _log(f"workload {w.name} with a sink")
+    b = _Bufs(w.T, w.topk, w.heads, w.d_qk, w.d_v)
+    inp, md = _run_indexer(3, b)
+    del inp
+    att = gen.attention_inputs(3, device=dev)
+    sink = gen.sink_logits(w.heads, device=dev)
+    out, lse = dsa.sparse_mla_fwd(att["q"], att["kv"], b.idx, w.scale, b.len, sink=sink)
+    dq, dkv, dsink = dsa.sparse_mla_bwd(att["q"], att["kv"], b.idx, out, lse, att["dout"],
+                                        w.scale, b.len, sink=sink)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dsink).all() and torch.isfinite(dkv).all()
+    rows = _attention_sample(w.cu_seqlens, n_spread=4, seed=7)
+    rows_t = torch.from_numpy(rows).to(dev)
+    q = att["q"][rows_t].cpu()
+    kv = att["kv"].cpu()
+    ii, ll = _np(b.idx[rows_t]), _np(b.len[rows_t])
+    sk = _np(sink).astype(np.float64)
+    ro, rl = oracle.sparse_mla_fwd(q, kv, ii, ll, w.scale, w.d_v, sink=sk)
+    e_o = checks.assert_close("sink out", _np(out[rows_t].float()), ro, checks.ATOL_OUT)
+    e_l = checks.assert_close("sink lse", _np(lse[rows_t]), rl, checks.ATOL_LSE)
+    rdq, _, _ = oracle.sparse_mla_bwd(q, kv, ii, ll, att["dout"][rows_t].cpu(), w.scale, sink=sk)
+    e_q = checks.assert_close("sink dq", _np(dq[rows_t].float()), rdq, checks.ATOL_OUT)
+    _log(f"sink rows {len(rows)}: out {e_o:.2e} lse {e_l:.2e} dq {e_q:.2e}")
