@@ -68,8 +68,13 @@ struct IndexerSmem {
   int32_t compact[2];  // compaction due in step i: compact[i & 1] (written by wave 0 in step i - 1)
   __align__(16) unsigned char tile[IndexerCfg<D>::kNBuf][IndexerCfg<D>::kTileBytes];
 };
-// after the key stream the tile buffers hold 4 rows x (4 KB bitmap + 2 KB scratch list)
+// after the key stream the tile buffers hold 4 rows x (4 KB bitmap + 2 KB scratch list), and
+// with 128-dim keys also 4 rows x a 4 KB (1024-bin) value histogram
+template <int D>
+constexpr int kFinalBins = D == 128 ? 1024 : 256;
 static_assert(IndexerCfg<64>::kNBuf * IndexerCfg<64>::kTileBytes >= 4 * (4096 + 2048), "tile area");
+static_assert(IndexerCfg<128>::kNBuf * IndexerCfg<128>::kTileBytes >= 4 * (4096 + 2048 + 4096),
+              "tile area");
 
 // Monotone map float -> uint32 (larger float -> larger key); +0 and -0 map alike.
 __device__ __forceinline__ uint32_t orderable(float f) {
@@ -159,6 +164,49 @@ __device__ __forceinline__ uint32_t bin_from_top(const uint32_t *hist, uint32_t 
     } else {
       a += hv[1];
       bin = 252 - 4 * lane;
+    }
+  }
+  above = __shfl(a, src, 64);
+  return __shfl(bin, src, 64);
+}
+
+// As bin_from_top for a histogram of NB bins (NB a multiple of 256): lane l owns the NB/64
+// bins NB-1-(NB/64) l downward.
+template <int NB>
+__device__ __forceinline__ uint32_t bin_from_top_n(const uint32_t *hist, uint32_t need,
+                                                   uint32_t &above) {
+  constexpr int P = NB / 64;  // bins per lane
+  const int lane = __lane_id();
+  const int lo = NB - P * (lane + 1);
+  uint32_t hv[P];
+#pragma unroll
+  for (int i = 0; i < P; i += 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(hist + lo + i);
+    hv[i] = v[0];
+    hv[i + 1] = v[1];
+    hv[i + 2] = v[2];
+    hv[i + 3] = v[3];
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) c += hv[i];
+  const uint32_t incl = wave_incl_scan(c);
+  const uint32_t excl = incl - c;
+  const bool mine = excl < need && need <= incl;
+  const int src = __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
+  uint32_t bin = 0, a = excl;
+  if (mine) {
+    bool found = false;
+#pragma unroll
+    for (int i = P - 1; i >= 0; --i) {  // from this lane's highest bin down
+      if (!found) {
+        if (a + hv[i] >= need) {
+          bin = static_cast<uint32_t>(lo + i);
+          found = true;
+        } else {
+          a += hv[i];
+        }
+      }
     }
   }
   above = __shfl(a, src, 64);
@@ -285,24 +333,29 @@ __device__ __forceinline__ float key_to_float(uint32_t u) {
 // 256 bins of equal width in score value over [lo, hi] (keys).  bin(u) is non-decreasing in
 // u (a rounded subtraction and a product with a positive constant are monotone), so
 // {u : bin(u) >= b} is a set of keys at or above some key.
-struct ValueBins {
+template <int NB>
+struct ValueBinsN {
   float flo, scale;
   __device__ __forceinline__ bool init(uint32_t lo, uint32_t hi) {
     flo = key_to_float(lo);
     const float fhi = key_to_float(hi);
-    scale = 256.0f / (fhi - flo);
+    scale = static_cast<float>(NB) / (fhi - flo);
     return fhi > flo && scale < INFINITY;
   }
   __device__ __forceinline__ int operator()(uint32_t u) const {
-    return max(min(static_cast<int>((key_to_float(u) - flo) * scale), 255), 0);
+    return max(min(static_cast<int>((key_to_float(u) - flo) * scale), NB - 1), 0);
   }
 };
+using ValueBins = ValueBinsN<256>;
 
-// 256-bin histogram of ck[0, cnt) (all keys within the bins' range).
-__device__ void value_histogram(const uint32_t *ck, int cnt, const ValueBins &vb,
+// NB-bin histogram of ck[0, cnt) (all keys within the bins' range).
+template <int NB = 256>
+__device__ void value_histogram(const uint32_t *ck, int cnt, const ValueBinsN<NB> &vb,
                                 uint32_t *hist) {
   const int lane = __lane_id();
-  *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < NB / 256; ++i)
+    *reinterpret_cast<u32x4 *>(hist + 256 * i + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
   wave_sync();
   for (int e = 4 * lane; e < cnt; e += 256) {
     const u32x4 v = *reinterpret_cast<const u32x4 *>(ck + e);
@@ -348,11 +401,13 @@ __device__ bool prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
 // emission loop.
 constexpr int kScratch = 256;
 
-__device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, int cnt, int K,
-                                 bool has_tau, uint32_t tau, int64_t start, int64_t t,
-                                 uint32_t *bm, uint32_t *sk, int32_t *sp, int32_t *out) {
+template <int NB>
+__device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, uint32_t *hist256,
+                                 int cnt, int K, bool has_tau, uint32_t tau, int64_t start,
+                                 int64_t t, uint32_t *bm, uint32_t *sk, int32_t *sp,
+                                 int32_t *out) {
   const int lane = __lane_id();
-  ValueBins vb;
+  ValueBinsN<NB> vb;
   int b = -1;        // bin of the K-th key; -1: every candidate in ck[0, cnt) is selected
   int nb = 0;        // scratch entries
   uint32_t keep4 = 0u;  // bit r: scratch entry lane + 64 r is selected
@@ -363,9 +418,9 @@ __device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
     bool fast = vb.init(lo, hi);
     uint32_t need = 0u;
     if (fast) {
-      value_histogram(ck, cnt, vb, hist);
+      value_histogram<NB>(ck, cnt, vb, hist);
       uint32_t above;
-      b = static_cast<int>(bin_from_top(hist, static_cast<uint32_t>(K), above));
+      b = static_cast<int>(bin_from_top_n<NB>(hist, static_cast<uint32_t>(K), above));
       need = static_cast<uint32_t>(K) - above;
       nb = static_cast<int>(hist[b]);
       fast = nb <= kScratch;
@@ -429,7 +484,7 @@ __device__ void select_and_write(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
         if (lane + 64 * r < nb && rank[r] < need) keep4 |= 1u << r;
     } else {
       int n = cnt;
-      select_exact(ck, cp, hist, n, K, start, t);
+      select_exact(ck, cp, hist256, n, K, start, t);
       cnt = K;
       b = -1;
       nb = 0;
@@ -856,13 +911,22 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
 
   lds_barrier();  // every append is visible; no tile load is in flight
   if (compute && half == 0) {
-    // the key tiles are free now: per row a 4 KB bitmap and a kScratch-entry scratch list
-    uint32_t *bm = reinterpret_cast<uint32_t *>(&sm.tile[0][0]) + row * 1024;
-    uint32_t *sk = reinterpret_cast<uint32_t *>(&sm.tile[0][0]) + 4 * 1024 + row * 2 * kScratch;
+    // the key tiles are free now: per row a 4 KB bitmap and a kScratch-entry scratch list, and
+    // with 128-dim keys (48 KB of tiles) a 1024-bin value histogram, whose narrower bins
+    // collide less in the LDS atomics than the 256 of the compactions
+    uint32_t *tiles = reinterpret_cast<uint32_t *>(&sm.tile[0][0]);
+    uint32_t *bm = tiles + row * 1024;
+    uint32_t *sk = tiles + 4 * 1024 + row * 2 * kScratch;
     int32_t *sp = reinterpret_cast<int32_t *>(sk + kScratch);
     const int n = merge_stacks(my_n, __builtin_amdgcn_readfirstlane(sm.cntb[row]));
-    select_and_write(ck, cp, sm.hist[row], n, K, my_has_tau, my_tau, start, tg, bm, sk, sp,
-                     idx_out + static_cast<int64_t>(t) * K);
+    if constexpr (kFinalBins<D> == 1024) {
+      select_and_write<1024>(ck, cp, tiles + 6 * 1024 + row * 1024, sm.hist[row], n, K,
+                             my_has_tau, my_tau, start, tg, bm, sk, sp,
+                             idx_out + static_cast<int64_t>(t) * K);
+    } else {
+      select_and_write<256>(ck, cp, sm.hist[row], sm.hist[row], n, K, my_has_tau, my_tau, start,
+                            tg, bm, sk, sp, idx_out + static_cast<int64_t>(t) * K);
+    }
     if (lane == 0) len_out[t] = K;
   }
 }
