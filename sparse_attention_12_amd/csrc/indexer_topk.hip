@@ -19,7 +19,7 @@
 // LDS, filled as two stacks (one per wave of the row, counts kept in registers, so no atomics;
 // entries in no particular order).  A key is appended when its score exceeds the row's
 // threshold tau (initially none).  When a row nears capacity it is
-// pruned with one 256-bin counting pass: the bin holding the K-th largest score gives a new
+// pruned with one 512-bin counting pass: the bin holding the K-th largest score gives a new
 // tau that never exceeds the true K-th largest score, and every candidate at or below it is
 // dropped.  Keys arrive in ascending position order, so a later key equal to the K-th score
 // would lose the tie to the candidates already kept: the strict test score > tau is exact.  At
@@ -42,12 +42,14 @@ constexpr int kWaves = 2 * kRows;        // two waves per row
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileKeys = 64;
 constexpr int kBins = 256;
+// value bins of a compaction: narrower bins collide less in the LDS atomics
+constexpr int kPruneBins = 512;
 
 template <int D>
 struct IndexerCfg {
   static constexpr int kNBuf = 3;  // key tile buffers
   // candidate entries per row: as many as fit next to the key tiles in 160 KB of LDS
-  static constexpr int kCap = D == 128 ? 3328 : 4096;
+  static constexpr int kCap = D == 128 ? 3320 : 4088;
   static constexpr int kChunks = D / 8;                      // 16-byte chunks per key
   static constexpr int kTileBytes = kTileKeys * D * 2;
   static constexpr int kLoads = kTileKeys * kChunks / 64;    // wave-wide DMAs per tile
@@ -60,7 +62,7 @@ template <int D>
 struct IndexerSmem {
   uint32_t cand_key[kRows][IndexerCfg<D>::kCap];
   int32_t cand_pos[kRows][IndexerCfg<D>::kCap];
-  __align__(16) uint32_t hist[kRows][kBins];
+  __align__(16) uint32_t hist[kRows][kPruneBins];
   __align__(16) int32_t cnt[kRows];   // entries of the lower stack of each row
   __align__(16) int32_t cntb[kRows];  // entries of the upper stack of each row
   uint32_t tau[kRows];                // per-row threshold: later keys enter only if above it
@@ -330,7 +332,7 @@ __device__ __forceinline__ float key_to_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-// 256 bins of equal width in score value over [lo, hi] (keys).  bin(u) is non-decreasing in
+// NB bins of equal width in score value over [lo, hi] (keys).  bin(u) is non-decreasing in
 // u (a rounded subtraction and a product with a positive constant are monotone), so
 // {u : bin(u) >= b} is a set of keys at or above some key.
 template <int NB>
@@ -377,11 +379,11 @@ __device__ bool prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int 
   uint32_t lo, hi;
   key_range(ck, cnt, lo, hi);
   if (has_tau) lo = tau + 1u;  // every candidate is above the current threshold
-  ValueBins vb;
+  ValueBinsN<kPruneBins> vb;
   if (!vb.init(lo, hi)) return has_tau;
-  value_histogram(ck, cnt, vb, hist);
+  value_histogram<kPruneBins>(ck, cnt, vb, hist);
   uint32_t above;
-  const int b = static_cast<int>(bin_from_top(hist, static_cast<uint32_t>(K), above));
+  const int b = static_cast<int>(bin_from_top_n<kPruneBins>(hist, static_cast<uint32_t>(K), above));
   if (b == 0) return has_tau;  // nothing below the K-th key's bin
   uint32_t dmax;
   cnt = compact_candidates(ck, cp, cnt, [vb, b](uint32_t u, int32_t) { return vb(u) >= b; },
