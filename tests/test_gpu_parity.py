@@ -505,3 +505,52 @@ def test_local_indexer_padded_storage_two_ranks_bit_exact():
         b = seq[rows[i]]
         assert int(md.seq_start[i]) == cu_pad[b]
         assert int(md.causal_len[i]) == rows[i] - cu[b] + 1
+
+
+def test_local_indexer_unordered_rows_duplicates_and_errors():
+    """Local rows in any order (groups of one row where neighbours are not consecutive keys),
+    a coordinate listed twice, and float inputs: every row equals the oracle up to near ties.
+    Coordinates outside the padded storage and offsets that are not ordered are rejected."""
+    dsa = _dsa()
+    cu, cu_pad, K, H, D = [0, 300, 1200], [0, 320, 1300], 128, 64, 128
+    T, Tk = cu[-1], cu_pad[-1]
+    inp = gen.indexer_inputs(2, cu_seqlens=cu)
+    kc = inp["k_idx"]
+    g = torch.Generator().manual_seed(12)
+    kp = torch.randn((Tk, D), generator=g).to(torch.bfloat16)
+    seq = np.searchsorted(np.array(cu), np.arange(T), side="right") - 1
+    coord = (np.arange(T) + np.array(cu_pad)[seq] - np.array(cu)[seq]).astype(np.int32)
+    kp[torch.from_numpy(coord).long()] = kc
+    perm = np.random.default_rng(5).permutation(T)[:400]
+    rows = np.concatenate([perm, perm[:1]])                     # the first row twice
+    qi = coord[rows]
+    qr = inp["q_idx"][torch.from_numpy(rows).long()].contiguous()
+    wr = inp["w"][torch.from_numpy(rows).long()].contiguous()
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+    cp_d = torch.tensor(cu_pad, dtype=torch.int32, device=dev)
+    md = dsa.prepare_local_metadata(cu_d, Tk, K, cu_seqlens_padded=cp_d,
+                                    query_indices=torch.from_numpy(qi).to(dev))
+    idx, ln = dsa.indexer_topk(qr.to(dev), kp.to(dev), wr.to(dev), md, K)
+    torch.cuda.synchronize()
+    gi, gl = _np(idx), _np(ln)
+    assert np.array_equal(gi[0], gi[-1]) and gl[0] == gl[-1]
+    # oracle on the compact layout (local row i is compact row rows[i]), mapped to padded
+    shift = (np.array(cu_pad)[seq] - np.array(cu)[seq])[rows]
+    for i in range(0, len(rows), 37):
+        t = int(rows[i])
+        ridx, rln, kth = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"], cu, K,
+                                             rows=(t, t + 1))
+        assert rln[0] == gl[i]
+        ridx_p = np.where(ridx >= 0, ridx + shift[i], -1)
+        # compare in compact coordinates (the near-tie check scores against the compact keys)
+        gi_c = np.where(gi[i:i + 1] >= 0, gi[i:i + 1] - shift[i], -1)
+        checks.check_topk_near_tie(inp["q_idx"][t:t + 1], inp["k_idx"], inp["w"][t:t + 1],
+                                   gi_c, ridx, kth, np.array([t]))
+        assert ((gi[i] >= 0) == (ridx_p[0] >= 0)).all()
+    with pytest.raises(ValueError, match="outside"):
+        dsa.prepare_local_metadata(cu_d, Tk, K, cu_seqlens_padded=cp_d,
+                                   query_indices=torch.tensor([5, Tk + 3], dtype=torch.int32,
+                                                              device=dev))
+    with pytest.raises(ValueError, match="shorter"):
+        dsa.prepare_local_metadata(cu_d, Tk, K, cu_seqlens_padded=torch.tensor(
+            [0, 200, 1300], dtype=torch.int32, device=dev))
