@@ -13,6 +13,9 @@ forward and backward per second); `components` breaks it down per stage with alg
 TFLOP/s and the fraction of the bf16 dense MFMA peak; `roofline` describes the kernel with the
 largest share of the step time, timed with HIP events recorded by the library around each of
 its kernel launches; `cpu_baseline` times the CPU oracle on a bounded row sample.
+`ms_per_step` is the wall-clock mean over the timed steps, `median_ms_per_step` the median of
+per-step HIP events, and `cold_ms_per_step` one more step after 1 GiB has been written to
+evict the inputs from L2 and the 256 MB last-level cache (not part of `value`).
 """
 
 from __future__ import annotations
@@ -330,13 +333,31 @@ def main():
     timing = True
     timer.arm()
     torch.cuda.synchronize()
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    step_ev[0].record()
+    for i in range(args.steps):
         step()
+        step_ev[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     timer.disarm()
     per_kernel = timer.totals()
+    step_ms = sorted(step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps))
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else \
+        0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
+    # one cold step: 1 GiB written first evicts the inputs from L2 and the 256 MB MALL
+    timing = False
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush.fill_(1.0)
+    cold_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    cold_ev[0].record()
+    step()
+    cold_ev[1].record()
+    torch.cuda.synchronize()
+    cold_ms = cold_ev[0].elapsed_time(cold_ev[1])
+    del flush
 
     ms_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
@@ -397,7 +418,8 @@ def main():
 
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": ms_step, "median_ms_per_step": median_ms,
+        "cold_ms_per_step": cold_ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "cu_seqlens": list(cfg.cu_seqlens),
                    "indexer": (f"{cfg.idx_heads}x{cfg.idx_dim}" if has_indexer else None),
