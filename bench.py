@@ -296,7 +296,9 @@ def main():
 
     def step():
         if local_rows is None:
-            md = dsa.prepare_thd_metadata(cu, K, T=T)
+            # the metadata's top-k width is an indexer width (at most 2048); a workload without
+            # an indexer (k-pool indices, width 2051) takes its lengths from its indices
+            md = dsa.prepare_thd_metadata(cu, min(K, dsa.MAX_INDEXER_TOPK), T=T)
         else:
             md = dsa.prepare_local_metadata(cu, T_keys, K, query_indices=local_rows)
         if has_indexer:
@@ -370,11 +372,16 @@ def main():
     t_fwd = avg("sparse_mla_fwd")
     # the backward's own wall time (its passes overlap on two streams, so kernel times overlap)
     t_bwd = sum(a.elapsed_time(b) for a, b in bwd_events) / len(bwd_events)
+    # latent rows gathered per valid slot: once in the forward, twice in the backward (its dq
+    # and key-gradient phases); these bytes mostly come from L2 and the last-level cache
+    row_bytes = counts["valid"] * Dqk * 2
     comp = {
         "fwd": {"ms": t_fwd, "tflops": counts["fwd_flops"] / t_fwd / 1e9,
-                "frac_mfma_peak": counts["fwd_flops"] / t_fwd / 1e9 / PEAK_BF16_TFLOPS},
+                "frac_mfma_peak": counts["fwd_flops"] / t_fwd / 1e9 / PEAK_BF16_TFLOPS,
+                "gather_gbs": row_bytes / t_fwd / 1e6},
         "bwd": {"ms": t_bwd, "tflops": counts["bwd_flops"] / t_bwd / 1e9,
-                "frac_mfma_peak": counts["bwd_flops"] / t_bwd / 1e9 / PEAK_BF16_TFLOPS},
+                "frac_mfma_peak": counts["bwd_flops"] / t_bwd / 1e9 / PEAK_BF16_TFLOPS,
+                "gather_gbs": 2 * row_bytes / t_bwd / 1e6},
     }
     if has_indexer:
         comp["indexer"] = {"ms": t_idx, "tokens_per_s": T / (t_idx * 1e-3),
