@@ -46,9 +46,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
-    ap.add_argument("--bwd-passes", type=int, default=1,
+    ap.add_argument("--bwd-passes", type=int, default=0,
                     help="query-row passes of the backward (several passes overlap a pass's "
-                         "key-gradient reduction with the next pass's compute)")
+                         "key-gradient reduction with the next pass's compute); 0: the fewest "
+                         "whose workspace fits in 60%% of the free device memory")
     ap.add_argument("--cp", type=int, default=1, metavar="N",
                     help="time one GPU's share under N-way context parallelism: the query rows "
                          "of rank 0 (zig-zag: chunks 0 and 2N-1 of every sequence split in 2N) "
@@ -279,6 +280,12 @@ def main():
     dq_buf = torch.empty_like(att["q"])
     dkv_buf = torch.empty((T_keys, Dqk), dtype=torch.float32, device=dev)
     # backward workspace for --bwd-passes passes over the query rows
+    if args.bwd_passes <= 0:
+        free = torch.cuda.mem_get_info()[0]
+        args.bwd_passes = 1
+        while (args.bwd_passes < T and dsa.bwd_workspace_bytes(
+                T, T_keys, H, Dqk, K, rows_per_pass=-(-T // args.bwd_passes)) > 0.6 * free):
+            args.bwd_passes *= 2
     rows_per_pass = -(-T // max(1, args.bwd_passes))
     ws = torch.empty(dsa.bwd_workspace_bytes(T, T_keys, H, Dqk, K, rows_per_pass=rows_per_pass),
                      dtype=torch.uint8, device=dev)
