@@ -50,6 +50,9 @@ def parse():
                     help="query-row passes of the backward (several passes overlap a pass's "
                          "key-gradient reduction with the next pass's compute); 0: the fewest "
                          "whose workspace fits in 60%% of the free device memory")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="attention layers per step sharing one indexer pass (IndexShare); 0: "
+                         "the workload's own count (4 for the 131072-token block, else 1)")
     ap.add_argument("--cp", type=int, default=1, metavar="N",
                     help="time one GPU's share under N-way context parallelism: the query rows "
                          "of rank 0 (zig-zag: chunks 0 and 2N-1 of every sequence split in 2N) "
@@ -256,6 +259,10 @@ def main():
     if has_indexer:
         inputs.update(gen.indexer_inputs(args.config, device=dev))
     att = gen.attention_inputs(args.config, device=dev)
+    n_layers = args.layers if args.layers > 0 else cfg.layers
+    # every further layer has its own q, latent rows and output gradient (drawn per layer)
+    extra_layers = [gen.attention_inputs(args.config, device=dev, layer=l)
+                    for l in range(1, n_layers)]
     T_keys = T
     local_rows = None
     if args.cp > 1:
@@ -270,6 +277,8 @@ def main():
         sel = local_rows.long()
         inputs.update(q_idx=inputs["q_idx"][sel].contiguous(), w=inputs["w"][sel].contiguous())
         att = dict(att, q=att["q"][sel].contiguous(), dout=att["dout"][sel].contiguous())
+        extra_layers = [dict(a, q=a["q"][sel].contiguous(), dout=a["dout"][sel].contiguous())
+                        for a in extra_layers]
         T = local_rows.numel()
     inputs.update(q=att["q"], kv=att["kv"], dout=att["dout"])
     H, Dqk, Dv = cfg.heads, cfg.d_qk, cfg.d_v
@@ -311,17 +320,18 @@ def main():
         if has_indexer:
             dsa.indexer_topk(inputs["q_idx"], inputs["k_idx"], inputs["w"], md, K, idx=idx_buf,
                              length=len_buf)
-        dsa.sparse_mla_fwd(att["q"], att["kv"], idx_buf, cfg.scale, len_buf, out=out_buf,
-                           lse=lse_buf, sink=sink)
-        if timing:
-            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            ev[0].record()
-        dsa.sparse_mla_bwd(att["q"], att["kv"], idx_buf, out_buf, lse_buf, att["dout"],
-                           cfg.scale, len_buf, dkv=dkv_buf, dq=dq_buf, workspace=ws, sink=sink,
-                           dsink=dsink_buf)
-        if timing:
-            ev[1].record()
-            bwd_events.append(ev)
+        for a in [att] + extra_layers:  # the layers reuse the indexer's indices
+            dsa.sparse_mla_fwd(a["q"], a["kv"], idx_buf, cfg.scale, len_buf, out=out_buf,
+                               lse=lse_buf, sink=sink)
+            if timing:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[0].record()
+            dsa.sparse_mla_bwd(a["q"], a["kv"], idx_buf, out_buf, lse_buf, a["dout"],
+                               cfg.scale, len_buf, dkv=dkv_buf, dq=dq_buf, workspace=ws,
+                               sink=sink, dsink=dsink_buf)
+            if timing:
+                ev[1].record()
+                bwd_events.append(ev)
         return md
 
     timing = False
@@ -338,7 +348,7 @@ def main():
         counts.update(idx_pairs=pairs,
                       idx_flops=float(pairs) * 2 * cfg.idx_heads * cfg.idx_dim)
 
-    timer = KernelTimer(dsa.lib(), 40 * args.steps)
+    timer = KernelTimer(dsa.lib(), 64 * args.steps * n_layers * max(1, args.bwd_passes))
     timing = True
     timer.arm()
     torch.cuda.synchronize()
@@ -438,7 +448,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": T, "cu_seqlens": list(cfg.cu_seqlens),
                    "indexer": (f"{cfg.idx_heads}x{cfg.idx_dim}" if has_indexer else None),
                    "topk": K, "heads": H, "d_qk": Dqk, "d_v": Dv, "bwd_passes": args.bwd_passes,
-                   "attention_sink": bool(args.sink),
+                   "attention_sink": bool(args.sink), "attention_layers": n_layers,
                    "context_parallel": ({"ranks": args.cp, "rank": 0, "local_tokens": T,
                                          "key_tokens": T_keys} if args.cp > 1 else None),
                    "parallelism": "none"},
