@@ -22,14 +22,18 @@
  *     enqueues work on it and returns; results are valid once the stream has
  *     executed the work.  The single exception is dsa_prepare_thd_metadata,
  *     which synchronises once to read the sequence offsets.
- *   - Every call returns a dsa_status.  On error nothing is enqueued and a
- *     message for the calling thread is available from dsa_last_error().
+ *   - Every call returns a dsa_status, and on error a message for the calling
+ *     thread is available from dsa_last_error().  An error found by the
+ *     argument checks returns before anything is enqueued.  A HIP error from a
+ *     launch can come after earlier kernels of the same call were enqueued
+ *     (the backward's passes): the call's outputs are then undefined.
  *     Argument checks never read device memory (no hidden synchronisation);
  *     index CONTENTS are trusted: an index outside [0, T_kv) other than -1 is
  *     undefined behaviour unless DSA_DEBUG_CHECK_INDICES is set in `flags`.
  *   - Outputs that depend on floating-point summation order: O, LSE and dq are
- *     bitwise reproducible run to run; dkv is accumulated with atomics and is
- *     reproducible only up to summation order.
+ *     bitwise reproducible run to run.  dkv is not: each latent row's
+ *     contributions are summed in fp32 in the order of a list that device
+ *     atomics build, so dkv is reproducible only up to summation order.
  */
 #ifndef DSA_H_
 #define DSA_H_

@@ -443,7 +443,7 @@ int dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   return DSA_OK;
 }
 
-// Backward workspace layout: delta [T_q, H] fp32 | debug flag | then one or two pass buffers,
+// Backward workspace layout: delta [T_q, H] fp32 | debug flag and largest |kv| | then one or two pass buffers,
 // each off [T_kv + 1] | cursor [T_kv] | list [R * K] int32 | stage [R * K] rows of
 // bwd_stage_row_bytes(D_qk); every segment 256-byte aligned.  One buffer when a single pass
 // covers every query row; otherwise two, so that a pass's reduction overlaps the next pass's
@@ -526,6 +526,7 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   w.delta = reinterpret_cast<float *>(p);
   p += align_up(static_cast<size_t>(T_q) * static_cast<size_t>(H) * sizeof(float));
   w.flag = reinterpret_cast<int32_t *>(p);
+  w.vmax = reinterpret_cast<uint32_t *>(p + 64);
   p += 256;
   w.nbuf = nbuf;
   for (int b = 0; b < 2; ++b) {

@@ -12,6 +12,8 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -36,6 +38,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // D[(lane/16)*4 + i][lane%16] = c[i].
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 fp16 MFMA (same operand layout as mfma16).
+__device__ __forceinline__ f32x4 mfma16h(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// two floats -> packed fp16 bits, round to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(const u32x4 &v) {
+  return __builtin_bit_cast(f16x8, v);
 }
 
 // 32x32x16 bf16 MFMA: A rows = lane%32, B cols = lane%32, k = (lane/32)*8 + [0,8);

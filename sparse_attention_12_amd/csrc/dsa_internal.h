@@ -66,6 +66,7 @@ constexpr size_t bwd_stage_row_bytes(int32_t D_qk) { return static_cast<size_t>(
 struct BwdWorkspace {
   float *delta;           // [T_q, H]
   int32_t *flag;          // debug index check
+  uint32_t *vmax;         // largest |kv| (bf16 magnitude bits), for the fp16 operand scales
   BwdPassBuffers buf[2];
   int nbuf;               // 1 or 2
   int64_t rows_per_pass;  // query rows per pass (>= 1)

@@ -107,10 +107,11 @@ struct RowSmem {
   static constexpr int kDqZ = kDqBufs * kTileB;
   static constexpr int kDqRing = kDqZ + 2 * 4 * 64 * 16;
   static constexpr int kDqBytes = kDqRing + kRing * kSlots * 4;
-  // contribution phase: tiles[3] | staging[2][zh, zl, ph, pl][32 slots][kSS] bf16 | slot
-  // rows (K entries rounded up to a whole tile);
-  // the row's q ([64][DQK + 16]) and dO ([64][512 + 16]) pass through the tile area first
-  static constexpr int kCStageBytes = 4 * kSlots * kSS * 2;
+  // contribution phase: tiles[3] | staging[2][z', P][32 slots][kSS] fp16 | slot rows (K
+  // entries rounded up to a whole tile); the row's q ([64][DQK + 16]) and dO ([64][512 + 16])
+  // pass through the tile area first, and the staging area starts with the prologue's exchange
+  // of the row's largest |q| and |dO| (16 words)
+  static constexpr int kCStageBytes = 2 * kSlots * kSS * 2;
   static constexpr int kCStage = kCBufs * kTileB;
   static constexpr int kCRows = kCStage + 2 * kCStageBytes;
   static constexpr int kCBytes = kCRows + kMaxK * 4;
@@ -192,6 +193,25 @@ struct SdpHead {
     const float l0 = hok ? lse[t * H + h] : -INFINITY;
     lse2 = l0 == -INFINITY ? INFINITY : l0 * kLog2e;  // empty row or padded head: P = 0
   }
+  // q and dO blocks of head h from global memory
+  __device__ __forceinline__ void load_q_dout(const uint16_t *__restrict__ q,
+                                              const uint16_t *__restrict__ dout, int H, int64_t t,
+                                              int h) {
+    const int g = __lane_id() >> 4;
+    const bool hok = h < H;
+#pragma unroll
+    for (int ks = 0; ks < DQK / 32; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hok) v = *reinterpret_cast<const u32x4 *>(q + ((t * H + h) * DQK + ks * 32 + g * 8));
+      qf[ks] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kDv / 32; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hok) v = *reinterpret_cast<const u32x4 *>(dout + ((t * H + h) * kDv + ks * 32 + g * 8));
+      df[ks] = as_bf16x8(v);
+    }
+  }
   __device__ __forceinline__ void load_scalars(const float *__restrict__ lse,
                                                const float *__restrict__ delta, int H, int64_t t,
                                                int h) {
@@ -221,10 +241,11 @@ struct SdpHead {
     settle(lse2);
     settle(dlt);
   }
-  // P and dZ of the 32 slots of `tile` in the S^T fragment layout (slot 16 mt + 4 g + i)
+  // P and dZ of the 32 slots of `tile` in the S^T fragment layout (slot 16 mt + 4 g + i);
+  // pdp accumulates this lane's share of sum_j P_j dP_j
   __device__ __forceinline__ void grads(const unsigned char *tile, const TileFrag<DQK> &fr,
                                         const int32_t *rr, float scale_log2, float p[2][4],
-                                        float dz[2][4]) const {
+                                        float dz[2][4], float &pdp) const {
     constexpr int kKS = DQK / 32;
     const int g = __lane_id() >> 4;
     f32x4 s[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
@@ -258,6 +279,8 @@ struct SdpHead {
       p[1][i] = static_cast<int32_t>(rv1[i]) >= 0 ? __builtin_amdgcn_exp2f(s1[i] * scale_log2 - lse2) : 0.0f;
       dz[0][i] = p[0][i] * (dp[0][i] - dlt);
       dz[1][i] = p[1][i] * (dp[1][i] - dlt);
+      pdp = fmaf(p[0][i], dp[0][i], pdp);
+      pdp = fmaf(p[1][i], dp[1][i], pdp);
     }
   }
 };
@@ -289,22 +312,27 @@ __device__ __forceinline__ void bwd_dq_row(
     if (wave == 0) sr.start(irow, lim, nchunks, ring);
     SdpHead<DQK> hd;
     hd.load_delta_from_out(q, dout, out, lse, H, t, G * 16 + hl);
-    // Delta of the row's heads, for the contribution phase
-    if (g == 0 && G * 16 + hl < H) delta[t * H + G * 16 + hl] = hd.dlt;
     __syncthreads();  // S0: indices of the first tiles are in the ring
     __syncthreads();  // S1: the first tiles are loaded
     hd.settle_all();  // see settle()
     TileFrag<DQK> fr;
     fr.init();
+    float pdp = 0.0f;  // this lane's part of sum_j P_j dP_j for head G * 16 + hl
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1)
       if (c == nchunks) break;
       if (wave == 0) sr.step(irow, lim, nchunks, ring, c);
       float p[2][4], dz[2][4];
       hd.grads(smem + (c % kDqBufs) * TL::kBytes, fr, ring + (c % kRing) * kSlots, scale_log2,
-               p, dz);
+               p, dz, pdp);
       zbuf[((c & 1) * 4 + G) * 64 + lane] = pack_slots(dz);
     }
+    // Delta of the key-gradient phase: sum_j P_j dP_j over the row's slots, equal to dO . O in
+    // exact arithmetic but free of the rounding of the bf16 output (which dominates the key
+    // gradient's error when many queries read one latent row)
+    pdp += __shfl_xor(pdp, 16, 64);
+    pdp += __shfl_xor(pdp, 32, 64);
+    if (g == 0 && G * 16 + hl < H) delta[t * H + G * 16 + hl] = pdp;
     lds_barrier();  // Z
   } else {
     // ============================== dq waves ===============================
@@ -364,6 +392,54 @@ __device__ __forceinline__ void bwd_dq_row(
 }
 
 // ---------------------------------------------------------------------------------------
+// Per-row power-of-two scales of the contribution phase's fp16 operands.  The products are
+//   C = scale dZ^T . q + P^T . dO
+// with P in [0, 1].  dO and q are converted to fp16 as dO' = dO 2^-gd, q' = q 2^-gq, and scale dZ
+// as z' = scale dZ 2^(gq - gd), so that both products accumulate 2^-gd C in one fp32 accumulator.
+// gq puts the row's largest |q| in [2^14, 2^15): bf16 -> fp16 is then exact except for elements
+// more than 2^28 below it.  gd does the same for dO, raised when needed so that z' cannot leave the
+// fp16 range: |dP_j| <= 512 max|dO| max|kv| and |Delta| <= max_j |dP_j|, so
+// |scale dZ| <= scale 1024 max|dO| max|kv| =: bound, and 2^(gq - gd) bound <= 2^15.
+struct C16Scales {
+  int gq, gd;
+  __device__ __forceinline__ static int expo(float x) {  // floor(log2 x) for normal x > 0
+    return static_cast<int>((__float_as_uint(x) >> 23) & 0xFF) - 127;
+  }
+  __device__ __forceinline__ void init(uint32_t mq_bits, uint32_t md_bits, uint32_t mv_bits,
+                                       float scale) {
+    const float mq = bf16_to_f32(static_cast<uint16_t>(mq_bits));
+    const float md = bf16_to_f32(static_cast<uint16_t>(md_bits));
+    const float mv = bf16_to_f32(static_cast<uint16_t>(mv_bits));
+    // bf16 subnormals have a zero exponent field: expo() then reads -127, which only makes the
+    // scaled maximum smaller
+    gq = mq > 0.0f ? expo(mq) - 14 : 0;
+    gd = md > 0.0f ? expo(md) - 14 : 0;
+    const float bound = scale * 1024.0f * md * mv;
+    if (bound > 0.0f) gd = max(gd, gq + expo(fminf(bound, 3.0e38f)) + 1 - 15);
+  }
+};
+
+// eight bf16 values (bit patterns) times 2^-g, as fp16 bit patterns, in place
+__device__ __forceinline__ void bf16_to_f16_scaled_inplace(u32x4 &w, int g) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = pack_f16x2(ldexpf(__uint_as_float(w[i] << 16), -g),
+                      ldexpf(__uint_as_float(w[i] & 0xFFFF0000u), -g));
+}
+
+// largest bf16 magnitude (bits) among the eight values of v
+__device__ __forceinline__ uint32_t absmax_bits(const u32x4 &v, uint32_t m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o, 64)));
+  return m;
+}
+
 // Key-gradient contributions of query row t, stored to staged row `slot` of stage for every
 // valid slot.
 template <int DQK>
@@ -371,13 +447,15 @@ __device__ __forceinline__ void bwd_contrib_row(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
     const float *__restrict__ lse, const float *__restrict__ delta,
-    const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
-    uint32_t *__restrict__ stage, int32_t *__restrict__ cnt, int64_t t, unsigned char *smem) {
+    const uint16_t *__restrict__ dout, const uint32_t *__restrict__ vmax, int H, int K,
+    float scale, float scale_log2, uint32_t *__restrict__ stage, int32_t *__restrict__ cnt,
+    int64_t t, unsigned char *smem) {
   using TL = Tile<DQK>;
   using SM = RowSmem<DQK>;
   constexpr int kNTq = DQK / 64;  // channel tiles per quarter (9 or 8)
   uint16_t *qstage = reinterpret_cast<uint16_t *>(smem);  // prologue only
-  uint16_t *stg = reinterpret_cast<uint16_t *>(smem + SM::kCStage);
+  _Float16 *stg = reinterpret_cast<_Float16 *>(smem + SM::kCStage);
+  uint32_t *mx = reinterpret_cast<uint32_t *>(smem + SM::kCStage);  // prologue only
   int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + SM::kCRows);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -387,9 +465,10 @@ __device__ __forceinline__ void bwd_contrib_row(
   const int32_t *irow = idx + t * K;
   const int nchunks = (lim + kSlots - 1) / kSlots;
 
-  // ---- prologue: the row's q, then dO, pass through LDS ([head][channel], padded heads zero):
-  // the SdP waves read their head blocks from it, the contribution waves head-contraction
-  // fragments of their channels.  Every global load of the prologue is issued first.
+  // ---- prologue: the row's q, then dO, pass through LDS ([head][channel], padded heads zero)
+  // as scaled fp16, from which the contribution waves read head-contraction fragments of their
+  // channels; the SdP waves load their bf16 head blocks from global memory (the dq phase has
+  // just read them).  The largest |q| and |dO| of the row are exchanged through LDS at P0.
   constexpr int kQV = 64 * (DQK / 8) / 512, kOV = 64 * (kDv / 8) / 512, kIV = kMaxK / 512;
   u32x4 qv[kQV], ov[kOV];
   int32_t iv[kIV];
@@ -410,9 +489,35 @@ __device__ __forceinline__ void bwd_contrib_row(
     const int e = threadIdx.x + j * 512;
     iv[j] = e < lim ? irow[e] : -1;
   }
+  const uint32_t mv_bits = *vmax;
+  {
+    uint32_t mq = 0u, md = 0u;
+#pragma unroll
+    for (int j = 0; j < kQV; ++j) mq = absmax_bits(qv[j], mq);
+#pragma unroll
+    for (int j = 0; j < kOV; ++j) md = absmax_bits(ov[j], md);
+    mq = wave_max_u32(mq);
+    md = wave_max_u32(md);
+    if (lane == 0) {
+      mx[wave] = mq;
+      mx[8 + wave] = md;
+    }
+  }
+  __syncthreads();  // P0: the maxima are exchanged
+  C16Scales sc16;
+  {
+    uint32_t mq = 0u, md = 0u;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      mq = max(mq, mx[w]);
+      md = max(md, mx[8 + w]);
+    }
+    sc16.init(mq, md, mv_bits, scale);
+  }
 #pragma unroll
   for (int j = 0; j < kQV; ++j) {
     const int e = threadIdx.x + j * 512, hh = e / (DQK / 8), col = (e % (DQK / 8)) * 8;
+    bf16_to_f16_scaled_inplace(qv[j], sc16.gq);
     *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kQStride + col]) = qv[j];
   }
   // dO and the slot rows (up to a whole number of tiles; the list lies outside the staging area);
@@ -422,6 +527,7 @@ __device__ __forceinline__ void bwd_contrib_row(
 #pragma unroll
     for (int j = 0; j < kOV; ++j) {
       const int e = threadIdx.x + j * 512, hh = e / (kDv / 8), col = (e % (kDv / 8)) * 8;
+      bf16_to_f16_scaled_inplace(ov[j], sc16.gd);
       *reinterpret_cast<u32x4 *>(&qstage[hh * SM::kOStride + col]) = ov[j];
     }
 #pragma unroll
@@ -431,7 +537,6 @@ __device__ __forceinline__ void bwd_contrib_row(
       if (iv[j] >= 0) atomicAdd(&cnt[iv[j]], 1);  // iv is -1 beyond the valid prefix
     }
   };
-  __syncthreads();  // P0
 
   // The two roles are separate branches from here on (their register sets never overlap).
   if (wave < 4) {
@@ -440,12 +545,12 @@ __device__ __forceinline__ void bwd_contrib_row(
     const int h = G * 16 + hl;
     SdpHead<DQK> hd;
     hd.load_scalars(lse, delta, H, t, h);
-    hd.q_from_lds(qstage, SM::kQStride, h);
-    __syncthreads();  // P1
+    __syncthreads();  // P1: q (fp16) is staged
+    hd.load_q_dout(q, dout, H, t, h);
+    __syncthreads();  // P2: the contribution waves have read q
     store_o_rows();
-    __syncthreads();  // P2
-    hd.o_from_lds(qstage, SM::kOStride, h);
-    __syncthreads();  // P3: the q / dO staging is read (the tile area is free)
+    __syncthreads();  // P3: dO (fp16) is staged
+    __syncthreads();  // P4: the staging is read (the tile area is free)
     const uint32_t tiles_lds = lds_addr(smem);
     constexpr int kLoadsW = TL::kLoads / 4;
     hd.settle_all();  // before the first tile load (see settle())
@@ -458,28 +563,24 @@ __device__ __forceinline__ void bwd_contrib_row(
     __syncthreads();  // S1: tile 0 loaded
     TileFrag<DQK> fr;
     fr.init();
+    const int zexp = sc16.gq - sc16.gd;  // z' = scale dZ 2^zexp
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): tile c complete; contribution waves are done with chunk c - 2
       if (c == nchunks) break;
       if (c + 2 < nchunks)  // into tile c - 1's buffer
         issue_tile<DQK, kCBufs>(tiles_lds, kv, slot_rows + (c + 2) * kSlots, c + 2, G);
-      float p[2][4], dz[2][4];
-      hd.grads(smem + (c % kCBufs) * TL::kBytes, fr, slot_rows + c * kSlots, scale_log2, p, dz);
-      uint16_t *zs = stg + (c & 1) * (SM::kCStageBytes / 2);
-      uint16_t *zl = zs + kSlots * kSS;
-      uint16_t *ps = zl + kSlots * kSS;
-      uint16_t *pl = ps + kSlots * kSS;
+      float p[2][4], dz[2][4], pdp = 0.0f;
+      hd.grads(smem + (c % kCBufs) * TL::kBytes, fr, slot_rows + c * kSlots, scale_log2, p, dz,
+               pdp);
+      _Float16 *zs = stg + (c & 1) * (SM::kCStageBytes / 2);
+      _Float16 *ps = zs + kSlots * kSS;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int o = (mt * 16 + g * 4 + i) * kSS + h;
-          const float z = dz[mt][i] * scale;
-          const uint16_t zh = f32_to_bf16(z), ph = f32_to_bf16(p[mt][i]);
-          zs[o] = zh;
-          zl[o] = f32_to_bf16(z - bf16_to_f32(zh));
-          ps[o] = ph;
-          pl[o] = f32_to_bf16(p[mt][i] - bf16_to_f32(ph));
+          zs[o] = static_cast<_Float16>(ldexpf(dz[mt][i] * scale, zexp));
+          ps[o] = static_cast<_Float16>(p[mt][i]);
         }
       if (c + 2 < nchunks) wait_vm<kLoadsW>();  // tile c + 1 before the next barrier
       else wait_tile();
@@ -489,7 +590,9 @@ __device__ __forceinline__ void bwd_contrib_row(
     // ========================== contribution waves =========================
     const int qq = wave - 4;
     const int ch0 = qq * 16 * kNTq;
-    bf16x8 qh[2][kNTq], oh[2][kNTq];
+    // head-contraction fragments of the scaled fp16 q' and dO'
+    u32x4 qh[2][kNTq], oh[2][kNTq];
+    __syncthreads();  // P1
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -497,35 +600,32 @@ __device__ __forceinline__ void bwd_contrib_row(
         const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kQStride + ch0 + n * 16 + cq * 4];
         const u32x2 lo = lds_read_tr16(base);
         const u32x2 hi = lds_read_tr16(base + 4 * SM::kQStride);
-        qh[kh][n] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        qh[kh][n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
-    __syncthreads();  // P1
+    __syncthreads();  // P2: q is read (dO overwrites it)
     store_o_rows();
-    __syncthreads();  // P2
+    __syncthreads();  // P3
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int n = 0; n < kNTq; ++n) {
         const int ch = ch0 + n * 16;
-        u32x4 v = {0u, 0u, 0u, 0u};
+        oh[kh][n] = u32x4{0u, 0u, 0u, 0u};
         if (ch < kDv) {
           const uint16_t *base = &qstage[(kh * 32 + g * 8 + r) * SM::kOStride + ch + cq * 4];
           const u32x2 lo = lds_read_tr16(base);
           const u32x2 hi = lds_read_tr16(base + 4 * SM::kOStride);
-          v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          oh[kh][n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        oh[kh][n] = as_bf16x8(v);
       }
-    __syncthreads();  // P3
+    __syncthreads();  // P4
     __syncthreads();  // S1
     for (int c = 0; c <= nchunks; ++c) {
       lds_barrier();  // B(c - 1): P / dZ of chunk c - 1 are staged
       if (c > 0) {
         const int cc = c - 1;
-        const uint16_t *zs = stg + (cc & 1) * (SM::kCStageBytes / 2);
-        const uint16_t *zl = zs + kSlots * kSS;
-        const uint16_t *ps = zl + kSlots * kSS;
-        const uint16_t *pl = ps + kSlots * kSS;
+        const _Float16 *zs = stg + (cc & 1) * (SM::kCStageBytes / 2);
+        const _Float16 *ps = zs + kSlots * kSS;
         const int32_t *rr = slot_rows + cc * kSlots;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -535,34 +635,32 @@ __device__ __forceinline__ void bwd_contrib_row(
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh) {
             const int off = (mt * 16 + hl) * kSS + kh * 32 + g * 8;
-            const bf16x8 za = as_bf16x8(*reinterpret_cast<const u32x4 *>(&zs[off]));
-            const bf16x8 zb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&zl[off]));
-            const bf16x8 pa = as_bf16x8(*reinterpret_cast<const u32x4 *>(&ps[off]));
-            const bf16x8 pb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&pl[off]));
-            // C^T = q^T . (scale dZ) + dO^T . P: the head-contraction fragments serve as the A
+            const f16x8 za = as_f16x8(*reinterpret_cast<const u32x4 *>(&zs[off]));
+            const f16x8 pa = as_f16x8(*reinterpret_cast<const u32x4 *>(&ps[off]));
+            // 2^-gd C^T = q'^T . z' + dO'^T . P: the head-contraction fragments serve as the A
             // operand (rows = channels) and the staged [slot][head] fragments as B (columns =
-            // slots), so that each lane ends with four consecutive channels of one slot.  Four
-            // passes over the channel tiles keep consecutive MFMAs independent (the dO
-            // fragments of RoPE channels are zero; skipping them would need a branch per MFMA).
+            // slots), so that each lane ends with four consecutive channels of one slot.  Two
+            // passes over the channel tiles keep consecutive MFMAs independent (the dO fragments
+            // of RoPE channels are zero; skipping them would need a branch per MFMA).
 #pragma unroll
-            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(qh[kh][n], za, acc[n]);
+            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16h(as_f16x8(qh[kh][n]), za, acc[n]);
 #pragma unroll
-            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(qh[kh][n], zb, acc[n]);
-#pragma unroll
-            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(oh[kh][n], pa, acc[n]);
-#pragma unroll
-            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16(oh[kh][n], pb, acc[n]);
+            for (int n = 0; n < kNTq; ++n) acc[n] = mfma16h(as_f16x8(oh[kh][n]), pa, acc[n]);
           }
-          // acc[n][0..3] -> staged row cc*32 + 16mt + hl, channels ch0 + 16n + 4g .. + 3, one
-          // block per lane (valid slots only)
+          // C = acc 2^gd, channels ch0 + 16n + 4g .. + 3 of staged row cc*32 + 16mt + hl: one
+          // block per lane (valid slots only).  The mantissas are those of acc against its own
+          // block exponent; the factor 2^gd only moves the stored exponent.
           if (rr[mt * 16 + hl] >= 0) {
-            float mx = 0.0f;
+            float mxa = 0.0f;
 #pragma unroll
             for (int n = 0; n < kNTq; ++n)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[n][i]));
-            const uint32_t eb = min(__float_as_uint(mx) >> 23, 253u);
-            const float sc = __uint_as_float((253u - eb) << 23);  // 2^-e
+              for (int i = 0; i < 4; ++i) mxa = fmaxf(mxa, fabsf(acc[n][i]));
+            const int ea = static_cast<int>(min(__float_as_uint(mxa) >> 23, 253u));
+            const int ec = ea + sc16.gd;  // exponent field of the block's largest |C|
+            const uint32_t eb = static_cast<uint32_t>(min(max(ec, 0), 253));
+            // 2^-e of acc; a block below the smallest normal fp32 is stored as zero
+            const float sc = ec >= 0 ? __uint_as_float(static_cast<uint32_t>(253 - ea) << 23) : 0.0f;
             uint32_t *row =
                 stage + static_cast<int64_t>(cc * kSlots + mt * 16 + hl) * kStageWords<DQK>;
             uint32_t *mrow = row + ((ch0 + 4 * g) >> 1);  // channel tile n at word 8 n
@@ -584,6 +682,19 @@ __device__ __forceinline__ void bwd_contrib_row(
     }
     lds_barrier();  // Z
   }
+}
+
+// Largest |kv| over n bf16 values (n a multiple of 8), as bf16 magnitude bits, into *out (which
+// holds 0 before the launch).
+__global__ __launch_bounds__(256) void kv_absmax_kernel(const uint16_t *__restrict__ kv, int64_t n8,
+                                                        uint32_t *__restrict__ out) {
+  uint32_t m = 0u;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8;
+       i += stride)
+    m = absmax_bits(*reinterpret_cast<const u32x4 *>(kv + 8 * i), m);
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0 && m > 0u) atomicMax(out, m);
 }
 
 __global__ void check_indices_kernel(const int32_t *__restrict__ idx,
@@ -608,16 +719,16 @@ __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length,
     const uint16_t *__restrict__ out, const float *__restrict__ lse, float *__restrict__ delta,
-    const uint16_t *__restrict__ dout, int H, int K, float scale, float scale_log2,
-    uint16_t *__restrict__ dq, uint32_t *__restrict__ stage, int32_t *__restrict__ cnt,
-    int64_t row0) {
+    const uint16_t *__restrict__ dout, const uint32_t *__restrict__ vmax, int H, int K,
+    float scale, float scale_log2, uint16_t *__restrict__ dq, uint32_t *__restrict__ stage,
+    int32_t *__restrict__ cnt, int64_t row0) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t i = blockIdx.x;
   const int64_t t = row0 + i;
   bwd_dq_row<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, H, K, scale, scale_log2, dq,
                   t, smem);
   __syncthreads();  // every wave is done with the dq phase's LDS; the row's Delta is stored
-  bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, H, K, scale, scale_log2,
+  bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, vmax, H, K, scale, scale_log2,
                        stage + i * K * kStageWords<DQK>, cnt, t, smem);
 }
 
@@ -759,9 +870,9 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const int32_t *__restr
 template <int DQK>
 hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                        const int32_t *topk_length, const uint16_t *out, const float *lse,
-                       float *delta,
-                       const uint16_t *dout, int64_t row0, int64_t rows, int32_t H, int32_t K,
-                       float scale, uint16_t *dq, const BwdPassBuffers &bb, hipStream_t s) {
+                       float *delta, const uint16_t *dout, const uint32_t *vmax, int64_t row0,
+                       int64_t rows, int32_t H, int32_t K, float scale, uint16_t *dq,
+                       const BwdPassBuffers &bb, hipStream_t s) {
   const size_t smem = RowSmem<DQK>::bytes(K);
   auto kern = bwd_rows_kernel<DQK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -769,8 +880,8 @@ hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                                      static_cast<int>(smem));
   if (e != hipSuccess) return e;
   DSA_LAUNCH("sparse_mla_bwd_rows", kern, dim3(static_cast<unsigned>(rows)),
-             dim3(kRowWaves * 64), smem, s, q, kv, idx, topk_length, out, lse, delta, dout, H, K,
-             scale, scale * kLog2e, dq, bb.stage, bb.off, row0);
+             dim3(kRowWaves * 64), smem, s, q, kv, idx, topk_length, out, lse, delta, dout, vmax,
+             H, K, scale, scale * kLog2e, dq, bb.stage, bb.off, row0);
   return hipGetLastError();
 }
 
@@ -842,8 +953,8 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
       const int64_t n = std::min<int64_t>(R, T_q - r0);
       e = launch_count_zero(T_kv, ws.buf[0], s);
       if (e == hipSuccess)
-        e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, r0, n, H, K, scale,
-                             dq, ws.buf[0], s);
+        e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, ws.vmax, r0, n, H,
+                             K, scale, dq, ws.buf[0], s);
       if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[0], s);
       if (e == hipSuccess) e = launch_reduce<DQK>(T_kv, ws.buf[0], dkv, s);
     }
@@ -865,8 +976,8 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
     if (p >= 2 && (e = hipStreamWaitEvent(s, bs->red_done[b], 0)) != hipSuccess) break;
     e = launch_count_zero(T_kv, ws.buf[b], s);
     if (e == hipSuccess)
-      e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, r0, n, H, K, scale,
-                           dq, ws.buf[b], s);
+      e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, ws.vmax, r0, n, H, K,
+                           scale, dq, ws.buf[b], s);
     if (e == hipSuccess) e = hipEventRecord(bs->rows_done[b], s);
     if (e == hipSuccess) e = hipStreamWaitEvent(bs->s2, bs->rows_done[b], 0);
     if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[b], bs->s2);
@@ -894,6 +1005,15 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
                        dkv, n);
   }
   if (T_q == 0) return hipGetLastError();
+  // largest |kv|, for the scales of the contribution phase's fp16 operands
+  DSA_LAUNCH("kv_absmax_zero", fill_zero_i32_kernel, dim3(1), dim3(64), 0, s,
+             reinterpret_cast<int32_t *>(ws.vmax), static_cast<int64_t>(1));
+  {
+    const int64_t n8 = T_kv * D_qk / 8;
+    const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, 2048);
+    DSA_LAUNCH("kv_absmax", kv_absmax_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+               s, kv, n8, ws.vmax);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (D_qk == 576)

@@ -221,12 +221,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
 // tile stays in use for two intervals; four tile buffers keep two tiles in flight.  Only the
 // PV waves issue the (compiler-invisible) tile loads and only the S waves issue ordinary
 // global loads, so each wave's explicit load-count waits stay exact.
-#ifndef FWD_S_AHEAD
-#define FWD_S_AHEAD 2
-#endif
-#ifndef FWD_S_FENCE
-#define FWD_S_FENCE 1
-#endif
 constexpr int kRoleNBuf = 4;
 constexpr int kRing = 8;  // slot-index ring (tiles)
 static_assert(kRing == SlotRing::kTiles && kSlots == SlotRing::kSlots, "slot-index ring layout");
@@ -305,7 +299,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
       // ---- S^T = rows . q^T  (four chains: slot half mt, k-step parity); fragment reads run
       // kAhead k-steps ahead of the MFMAs (an LDS read under load takes longer than a few
       // MFMAs, so a shallow read-ahead leaves the MFMA pipe waiting)
-      constexpr int kAhead = FWD_S_AHEAD;
+      constexpr int kAhead = 2;
       f32x4 acc[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
                          {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
       bf16x8 a0[kAhead + 1], a1[kAhead + 1];
@@ -316,7 +310,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
       }
       // the scheduling fences keep this order (the compiler would otherwise pull each read
       // down next to its MFMA)
-      if (FWD_S_FENCE) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         if (ks + kAhead < kKSteps) {
@@ -325,7 +319,7 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
         }
         acc[0][ks & 1] = mfma16(a0[ks % (kAhead + 1)], qf[ks], acc[0][ks & 1]);
         acc[1][ks & 1] = mfma16(a1[ks % (kAhead + 1)], qf[ks], acc[1][ks & 1]);
-        if (FWD_S_FENCE) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const f32x4 sv0 = acc[0][0] + acc[0][1], sv1 = acc[1][0] + acc[1][1];
       // ---- online softmax (base 2) with a lazily raised reference max: the reference only

@@ -78,12 +78,21 @@ def check_topk_structure_device(idx, ln, seq_start, K: int):
 
 
 def max_abs(a, b) -> float:
+    """Largest |a - b|.  Equal infinities (an empty row's LSE) count as zero error; a NaN on
+    either side that the other side does not share, or unequal infinities, make it inf, so
+    that assert_close fails on them."""
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
-    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    a, b = np.broadcast_arrays(a, b)
+    if a.size == 0:
+        return 0.0
+    na, nb = np.isnan(a), np.isnan(b)
+    if (na != nb).any():
+        return float("inf")
+    same = (np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))) | (na & nb)
     with np.errstate(invalid="ignore"):
-        d = np.where(both_inf, 0.0, np.abs(a - b))
-    return float(np.nanmax(d)) if d.size else 0.0
+        d = np.where(same, 0.0, np.abs(a - b))
+    return float(d.max())
 
 
 def assert_close(name, gpu, ref, atol):

@@ -122,6 +122,28 @@ def _check_dkv_tails(att, idx, ln, dkv, cu, scale, R):
     _log(f"dkv tails (R={R}): {worst:.2e}")
 
 
+def _check_dkv_sequence(att, idx, ln, dkv, s, e, scale):
+    """Complete dkv of every key row of sequence [s, e): its contributors are exactly the query
+    rows [s, e), so the oracle over those rows gives the exact gradient.  Logs the worst error
+    by contributor count (key row r is read by at most e - r queries)."""
+    sl = slice(s, e)
+    _, rdkv = oracle.sparse_mla_bwd(att["q"][sl].cpu(), att["kv"].cpu(), _np(idx[sl]),
+                                    None if ln is None else _np(ln[sl]), att["dout"][sl].cpu(),
+                                    scale)
+    got = _np(dkv[sl])
+    ref = rdkv[s:e]
+    assert not np.isnan(got).any(), f"NaN in dkv rows [{s},{e})"
+    err = np.abs(got - ref).max(axis=1)
+    ncon = e - np.arange(s, e)
+    parts = []
+    for lo, hi in ((1, 16), (16, 128), (128, 512), (512, 2048), (2048, 1 << 30)):
+        m = (ncon >= lo) & (ncon < hi)
+        if m.any():
+            parts.append(f"[{lo},{min(hi, e - s + 1)}) {err[m].max():.2e}")
+    _log(f"dkv rows [{s},{e}) by contributors: " + ", ".join(parts))
+    checks.assert_close(f"dkv rows [{s},{e})", got, ref, checks.ATOL_OUT)
+
+
 class _Bufs:
     """Output buffers and workspace laid out as the benchmark allocates them."""
 
@@ -185,6 +207,8 @@ def test_full_thd_T32768_step():
     _check_rows_fwd_bwd(att, b.idx, b.len, b.out, b.lse, b.dq, _attention_sample(w.cu_seqlens),
                         w.scale, w.d_v)
     _check_dkv_tails(att, b.idx, b.len, b.dkv, list(w.cu_seqlens), w.scale, R=6)
+    # key rows read by up to 1024 queries: every row of the first sequence
+    _check_dkv_sequence(att, b.idx, b.len, b.dkv, w.cu_seqlens[0], w.cu_seqlens[1], w.scale)
 
 
 def test_full_nope_kpool_T65536():

@@ -97,6 +97,39 @@ def test_indexer_matches_brute_force(int_inputs, cu, K, H, D):
         assert kth[t] == pytest.approx(row[ln[t] - 1], rel=1e-12, abs=1e-12)
 
 
+@pytest.mark.parametrize("int_inputs", [True, False])
+def test_indexer_rows_with_offset_matches_brute_force(int_inputs):
+    """indexer_topk_rows sees only the q / w of rows [r0, r1) (r0 inside a sequence, as the
+    full-size GPU checks call it): its indices, lengths and k-th scores must equal brute force
+    over the whole batch, and indexer_topk over the same rows."""
+    cu = [0, 40, 41, 130, 200]
+    T, K, H, D = cu[-1], 24, 8, 32
+    g = torch.Generator().manual_seed(4321 + int(int_inputs))
+    if int_inputs:
+        q = torch.randint(-4, 5, (T, H, D), generator=g).to(torch.bfloat16)
+        k = torch.randint(-4, 5, (T, D), generator=g).to(torch.bfloat16)
+        w = torch.tensor([0.5, 1.0, 2.0])[torch.randint(0, 3, (T, H), generator=g)]
+    else:
+        q = torch.randn((T, H, D), generator=g).to(torch.bfloat16)
+        k = torch.randn((T, D), generator=g).to(torch.bfloat16)
+        w = torch.randn((T, H), generator=g) / 8
+    cua = np.array(cu, np.int32)
+    scores = pins.brute_indexer_scores(q, k, w, cua)
+    bidx, bln = pins.brute_topk(scores, K)
+    for r0, r1 in [(57, 90), (41, 42), (150, 200), (0, 5), (39, 45)]:
+        idx, ln, kth = oracle.indexer_topk_rows(q[r0:r1].contiguous(), k, w[r0:r1].contiguous(),
+                                                cua, K, r0)
+        np.testing.assert_array_equal(idx, bidx[r0:r1])
+        np.testing.assert_array_equal(ln, bln[r0:r1])
+        for i, t in enumerate(range(r0, r1)):
+            row = np.sort(scores[t][np.isfinite(scores[t])])[::-1]
+            assert kth[i] == pytest.approx(row[ln[i] - 1], rel=1e-12, abs=1e-12)
+        a_idx, a_ln, a_kth = oracle.indexer_topk(q, k, w, cua, K, rows=(r0, r1))
+        np.testing.assert_array_equal(idx, a_idx)
+        np.testing.assert_array_equal(ln, a_ln)
+        np.testing.assert_array_equal(kth, a_kth)
+
+
 def test_indexer_short_rows_closed_form():
     """Rows with at most K causal keys return exactly their whole prefix."""
     w_ = gen.workload(1)
