@@ -232,6 +232,31 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                        float *dkv, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, results and errors as dsa_sparse_mla_bwd, without
+ * the workspace: the library uses a fixed scratch array in its code object
+ * (dsa_sparse_mla_bwd_noalloc_scratch_bytes(), 256 MiB), of which every GPU
+ * that loads the library holds its own copy until the process ends.  The
+ * first call on a device looks up that device's copy (hipGetSymbolAddress);
+ * no call allocates or frees device memory.  The query rows are processed in
+ * passes of as many rows as the scratch holds (one staging buffer, all on
+ * `stream`; no helper stream), so large problems take many passes.  Sizes
+ * whose Delta [T_q, H] and one row's staging do not fit the scratch return
+ * DSA_ERR_INVALID_VALUE with the bytes needed.  Every call on one GPU shares
+ * that GPU's scratch: calls that overlap in time on one GPU (two streams, two
+ * threads) race and give undefined results.  The scratch keeps the last
+ * call's contents; every part the kernels read is written or cleared by the
+ * same call first.
+ * ------------------------------------------------------------------------ */
+size_t dsa_sparse_mla_bwd_noalloc_scratch_bytes(void);
+int dsa_sparse_mla_bwd_noalloc(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                               const int32_t *topk_length, const uint16_t *out, const float *lse,
+                               const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H,
+                               int32_t D_qk, int32_t D_v, int32_t K, float scale, uint16_t *dq,
+                               float *dkv, uint32_t flags, void *stream);
+
+/* --------------------------------------------------------------------------
  * Attention sink (API reference _pad_attention_heads: a per-head sink [H] is
  * padded together with the query heads; the page does not state its
  * arithmetic).  Reading taken: sink[h] is one more logit of head h whose

@@ -83,6 +83,11 @@ def lib():
         L.dsa_sparse_mla_bwd_sink.restype = C.c_int
         L.dsa_sparse_mla_bwd_sink.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32,
                                               i32, f32, vp, vp, vp, vp, u32, vp, sz, vp]
+        L.dsa_sparse_mla_bwd_noalloc_scratch_bytes.argtypes = []
+        L.dsa_sparse_mla_bwd_noalloc_scratch_bytes.restype = sz
+        L.dsa_sparse_mla_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32,
+                                                 i32, i32, f32, vp, vp, u32, vp]
+        L.dsa_sparse_mla_bwd_noalloc.restype = C.c_int
         L.dsa_record_kernel_events.restype = C.c_int
         L.dsa_record_kernel_events.argtypes = [vp, C.c_int, C.POINTER(C.c_int)]
         _lib = L
@@ -402,3 +407,29 @@ def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
           d_v, K, float(softmax_scale), sink.data_ptr(), dq.data_ptr(), dkv.data_ptr(),
           dsink.data_ptr(), flags, workspace.data_ptr(), workspace.numel(), _stream())
     return dq, dkv, dsink
+
+
+def sparse_mla_bwd_noalloc(q, kv, topk_indices, out, lse, dout, softmax_scale: float, dq, dkv,
+                           topk_length=None, accumulate: bool = False):
+    """dsa_sparse_mla_bwd_noalloc: the backward without a workspace (the library's fixed
+    per-GPU scratch), for callers that cannot allocate.  dq (bf16 [T_q,H,D_qk]) and dkv (fp32
+    [T_kv,D_qk]) are caller-provided outputs; nothing is allocated.  Calls that overlap in time
+    on one GPU share that scratch and race."""
+    op = "sparse_mla_bwd_noalloc"
+    _require(op, q, kv, topk_indices, out, lse, dout, topk_length, dkv, dq)
+    kv2, idx, Tq, H, Dqk, Tkv, K = _attn_shapes(op, q, kv, topk_indices, topk_length)
+    _dtype(op, "out", out, torch.bfloat16)
+    _dtype(op, "dout", dout, torch.bfloat16)
+    _dtype(op, "lse", lse, torch.float32)
+    _dtype(op, "dkv", dkv, torch.float32)
+    _dtype(op, "dq", dq, torch.bfloat16)
+    d_v = out.shape[-1]
+    if out.shape != (Tq, H, d_v) or dout.shape != out.shape or lse.shape != (Tq, H):
+        raise ValueError(f"{op}: out/dout must be [T_q,H,D_v] and lse [T_q,H]")
+    if dkv.numel() != Tkv * Dqk or dq.shape != q.shape:
+        raise ValueError(f"{op}: dq must match q and dkv hold [T_kv, D_qk] fp32")
+    flags = DSA_BWD_ACCUMULATE_DKV if accumulate else 0
+    _call(lib().dsa_sparse_mla_bwd_noalloc, op, q.data_ptr(), kv2.data_ptr(), idx.data_ptr(),
+          _ptr(topk_length), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), Tq, Tkv, H, Dqk,
+          d_v, K, float(softmax_scale), dq.data_ptr(), dkv.data_ptr(), flags, _stream())
+    return dq, dkv

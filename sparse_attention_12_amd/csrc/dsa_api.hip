@@ -474,30 +474,31 @@ size_t dsa_sparse_mla_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t H, i
   return bwd_total_bytes(T_q, T_kv, H, D_qk, K, std::max<int64_t>(R, 1));
 }
 
-int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
-                       const int32_t *topk_length, const uint16_t *out, const float *lse,
-                       const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H,
-                       int32_t D_qk, int32_t D_v, int32_t K, float scale, uint16_t *dq,
-                       float *dkv, uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
-  g_last_error.clear();
-  if (int rc = check_attention_args("sparse_mla_bwd", q, kv, idx, T_q, T_kv, H, D_qk, D_v, K,
-                                    scale, 64))
+// Argument checks, pass planning, workspace carving and launch of the backward.  With
+// two_buffers false every pass uses one staging buffer on the caller's stream (no helper
+// stream), and a workspace that holds less than one row per pass is reported as `small_code`.
+static int bwd_run(const char *who, const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                   const int32_t *topk_length, const uint16_t *out, const float *lse,
+                   const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk,
+                   int32_t D_v, int32_t K, float scale, uint16_t *dq, float *dkv, uint32_t flags,
+                   void *ws, size_t ws_bytes, bool two_buffers, int small_code, void *stream) {
+  if (int rc = check_attention_args(who, q, kv, idx, T_q, T_kv, H, D_qk, D_v, K, scale, 64))
     return rc;
-  if (K > 4096) return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: K=%d exceeds 4096", K);
+  if (K > 4096) return fail(DSA_ERR_INVALID_VALUE, "%s: K=%d exceeds 4096", who, K);
   if (flags & ~(DSA_BWD_ACCUMULATE_DKV | DSA_DEBUG_CHECK_INDICES))
-    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: unknown flags 0x%x", flags);
+    return fail(DSA_ERR_INVALID_VALUE, "%s: unknown flags 0x%x", who, flags);
   if (T_q > 0 && (!out || !lse || !dout || !dq))
-    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: NULL tensor pointer");
-  if (T_kv > 0 && !dkv) return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: dkv is NULL");
+    return fail(DSA_ERR_INVALID_VALUE, "%s: NULL tensor pointer", who);
+  if (T_kv > 0 && !dkv) return fail(DSA_ERR_INVALID_VALUE, "%s: dkv is NULL", who);
   if (!aligned16(out) || !aligned16(dout) || !aligned16(dkv))
-    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd: out/dout/dkv must be 16-byte aligned");
+    return fail(DSA_ERR_INVALID_VALUE, "%s: out/dout/dkv must be 16-byte aligned", who);
   // rows per pass: all of them in one buffer if the workspace holds that, else as many as two
   // buffers hold, else as many as one buffer holds (pair ids are int32)
   const int64_t R_max = std::min<int64_t>(T_q, INT32_MAX / K);
   const size_t need = bwd_fixed_bytes(T_q, H) + bwd_pass_bytes(1, T_kv, D_qk, K);
   if (T_q > 0 && (!ws || ws_bytes < need))
-    return fail(DSA_ERR_WORKSPACE, "sparse_mla_bwd: workspace needs at least %zu bytes, got %zu",
-                need, ws ? ws_bytes : static_cast<size_t>(0));
+    return fail(small_code, "%s: workspace needs at least %zu bytes, got %zu", who, need,
+                ws ? ws_bytes : static_cast<size_t>(0));
   int64_t R = 0;
   int nbuf = 1;
   if (T_q > 0) {
@@ -512,7 +513,7 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
     };
     if (R_max == T_q && fixed + bwd_pass_bytes(T_q, T_kv, D_qk, K) <= ws_bytes) {
       R = T_q;
-    } else if ((R = largest(2)) >= 1) {
+    } else if (two_buffers && (R = largest(2)) >= 1) {
       nbuf = 2;
     } else {
       R = std::max<int64_t>(largest(1), 1);
@@ -551,8 +552,53 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   hipError_t e = dsa::launch_sparse_mla_bwd(q, kv, idx, topk_length, out, lse, dout, T_q, T_kv,
                                             H, D_qk, K, scale, dq, dkv,
                                             (flags & DSA_BWD_ACCUMULATE_DKV) != 0, w, s);
-  if (e != hipSuccess) return hip_fail(e, "sparse_mla_bwd: launch");
+  if (e != hipSuccess) {
+    char what[64];
+    snprintf(what, sizeof what, "%s: launch", who);
+    return hip_fail(e, what);
+  }
   return DSA_OK;
+}
+
+int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                       const int32_t *topk_length, const uint16_t *out, const float *lse,
+                       const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H,
+                       int32_t D_qk, int32_t D_v, int32_t K, float scale, uint16_t *dq,
+                       float *dkv, uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  return bwd_run("sparse_mla_bwd", q, kv, idx, topk_length, out, lse, dout, T_q, T_kv, H, D_qk,
+                 D_v, K, scale, dq, dkv, flags, ws, ws_bytes, true, DSA_ERR_WORKSPACE, stream);
+}
+
+size_t dsa_sparse_mla_bwd_noalloc_scratch_bytes(void) { return dsa::kNoAllocScratchBytes; }
+
+int dsa_sparse_mla_bwd_noalloc(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                               const int32_t *topk_length, const uint16_t *out, const float *lse,
+                               const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H,
+                               int32_t D_qk, int32_t D_v, int32_t K, float scale, uint16_t *dq,
+                               float *dkv, uint32_t flags, void *stream) {
+  g_last_error.clear();
+  const char *who = "sparse_mla_bwd_noalloc";
+  if (int rc = check_attention_args(who, q, kv, idx, T_q, T_kv, H, D_qk, D_v, K, scale, 64))
+    return rc;
+  // sizes the scratch cannot hold are rejected before the device is touched
+  if (T_q > 0 && K <= 4096) {
+    const size_t need = bwd_fixed_bytes(T_q, H) + bwd_pass_bytes(1, T_kv, D_qk, K);
+    if (need > dsa::kNoAllocScratchBytes)
+      return fail(DSA_ERR_INVALID_VALUE,
+                  "%s: these sizes need at least %zu bytes of scratch; the library's scratch "
+                  "holds %zu",
+                  who, need, dsa::kNoAllocScratchBytes);
+  }
+  void *ws = nullptr;
+  if (T_q > 0) {
+    if (int rc = check_device()) return rc;
+    hipError_t e = dsa::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "sparse_mla_bwd_noalloc: scratch address");
+  }
+  return bwd_run(who, q, kv, idx, topk_length, out, lse, dout, T_q, T_kv, H, D_qk, D_v, K, scale,
+                 dq, dkv, flags, ws, dsa::kNoAllocScratchBytes, false, DSA_ERR_INVALID_VALUE,
+                 stream);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -79,6 +79,12 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
                                  uint16_t *dq, float *dkv, bool accumulate,
                                  const BwdWorkspace &ws, hipStream_t s);
 
+// Fixed device scratch of the allocation-free backward, per GPU (bytes), and the device address
+// of the calling thread's current GPU's copy (looked up on first use per device).
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(256) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void **ptr);
+
 // Attention sink: the forward epilogue (out, lse rescaled in place) and the sink gradient.
 hipError_t launch_sink_fwd(const float *sink, int64_t T_q, int32_t H, int32_t D_v,
                            uint16_t *out, float *lse, hipStream_t s);

@@ -22,6 +22,7 @@
 // Compared with fp32 atomics on dkv (bounded by the L2 atomic units at about one 4-byte add
 // per channel per clock), staging moves about 4 bytes of HBM traffic per contribution element.
 #include <algorithm>
+#include <mutex>
 
 #include "dsa_common.h"
 #include "dsa_internal.h"
@@ -1023,6 +1024,32 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
     return launch_passes<512>(q, kv, idx, topk_length, out, lse, ws.delta, dout, T_q, T_kv, H,
                               K, scale, dq, dkv, ws, s);
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------------------
+// Scratch of the allocation-free backward (dsa_sparse_mla_bwd_noalloc): a fixed array in the
+// code object, of which every GPU that loads the library holds its own copy until the process
+// ends.  Host code never uses the array's name as an address: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *per_dev[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_dev[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_dev[dev] = p;
+  }
+  *ptr = per_dev[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_check_indices(const int32_t *idx, const int32_t *topk_length, int64_t T_q,

@@ -148,3 +148,16 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         pkg.lib()
     assert not pkg.is_available()
+
+
+def test_noalloc_backward_rejects_sizes_beyond_its_scratch(dsa):
+    """The allocation-free backward checks its sizes against the fixed scratch before it
+    touches a device (the pointers below are never dereferenced)."""
+    scratch = dsa.dsa_sparse_mla_bwd_noalloc_scratch_bytes()
+    assert scratch == 256 << 20
+    fake = C.c_void_p(1 << 20)
+    T = (scratch // (64 * 4)) + 1  # Delta [T, 64] fp32 alone exceeds the scratch
+    rc = dsa.dsa_sparse_mla_bwd_noalloc(fake, fake, fake, None, fake, fake, fake, T, T, 64, 576,
+                                        512, 2048, C.c_float(0.04), fake, fake, 0, None)
+    assert rc == 1  # DSA_ERR_INVALID_VALUE
+    assert "scratch" in _err(dsa)
