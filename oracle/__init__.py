@@ -6,7 +6,8 @@ oracle never imports the product: the two share nothing except the seeded
 input generators in dsa_inputs.py.
 
 Thin ctypes/numpy wrappers around oracle/dsa_oracle.c (fp64 definitions of
-the THD metadata, indexer top-k, sparse MLA forward and backward).  bf16
+the THD metadata, indexer top-k, sparse MLA forward and backward, and the
+indexer's KL training loss with its gradients).  bf16
 tensors are passed as their uint16 bit patterns.  See dsa_oracle.c for the
 page passages each function follows.
 """
@@ -61,6 +62,11 @@ def lib():
                                             C.c_double, C.c_void_p, C.c_int64, C.c_int64, f64p,
                                             f64p, C.c_void_p]
         L.oracle_sparse_mla_bwd.restype = C.c_int
+        L.oracle_indexer_kl.argtypes = [u16p, u16p, i32p, C.c_void_p, C.c_int64, C.c_int64,
+                                        C.c_int32, C.c_int32, C.c_int32, C.c_double, C.c_void_p,
+                                        u16p, u16p, f32p, C.c_int32, C.c_int32, C.c_double,
+                                        C.c_int64, C.c_int64, f64p, f64p, f64p, f64p, f64p]
+        L.oracle_indexer_kl.restype = C.c_int
         _lib = L
     return _lib
 
@@ -249,3 +255,38 @@ def sparse_mla_bwd(q, kv, idx, topk_length, dout, scale: float, rows=None, dkv=N
     if sink is None:
         return dq, dkv
     return dq, dkv, dsink
+
+
+def indexer_kl(q, kv, idx, topk_length, scale: float, q_idx, k_idx, w, g: float = 1.0,
+               rows=None, sink=None, dk_idx=None):
+    """Indexer KL loss and its gradients for query rows [r0, r1): a dict with target
+    [n,K], loss [n], dq_idx [n,Hi,Di], dw [n,Hi] (row-relative) and dk_idx [T_kv,Di]
+    (accumulated over the given rows; pass ``dk_idx`` to keep accumulating)."""
+    qa = _u16(q)
+    kva = _u16(kv).reshape(kv.shape[0], -1)
+    ia = _np(idx, np.int32).reshape(qa.shape[0], -1)
+    tl, tlp = _opt_i32(topk_length)
+    qi = _u16(q_idx)
+    ki = _u16(k_idx).reshape(k_idx.shape[0], -1)
+    wa = _np(w, np.float32)
+    Tq, H, Dqk = qa.shape
+    Tkv = kva.shape[0]
+    K = ia.shape[1]
+    Hi, Di = qi.shape[1], qi.shape[2]
+    if ki.shape[0] != Tkv or ki.shape[1] != Di or qi.shape[0] != Tq or wa.shape != (Tq, Hi):
+        raise ValueError("indexer_kl: k_idx must have the rows of kv, q_idx / w the rows of q")
+    r0, r1 = (0, Tq) if rows is None else rows
+    n = r1 - r0
+    sk, skp = _opt_sink(sink, H)
+    target = np.zeros((n, K), np.float64)
+    loss = np.zeros(n, np.float64)
+    dq_idx = np.zeros((n, Hi, Di), np.float64)
+    dw = np.zeros((n, Hi), np.float64)
+    if dk_idx is None:
+        dk_idx = np.zeros((Tkv, Di), np.float64)
+    _check(lib().oracle_indexer_kl(qa.reshape(-1), kva.reshape(-1), ia.reshape(-1), tlp, Tq,
+                                   Tkv, H, Dqk, K, float(scale), skp, qi.reshape(-1),
+                                   ki.reshape(-1), wa.reshape(-1), Hi, Di, float(g), r0, r1,
+                                   target, loss, dq_idx, dw, dk_idx), "indexer_kl")
+    del tl, sk
+    return dict(target=target, loss=loss, dq_idx=dq_idx, dw=dw, dk_idx=dk_idx)

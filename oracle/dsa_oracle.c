@@ -440,3 +440,161 @@ int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *
   }
   return err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Indexer training loss ([GLM52] "How DSA works": the indexer emits an      */
+/* auxiliary KL loss that aligns its score distribution with the main        */
+/* attention's, on a graph separate from the main model's; "GLM-5.2 training  */
+/* results": sparse formulation, coefficient 0.001; "cuDNN fused DSA         */
+/* kernels": a score-recompute kernel feeds the loss).                        */
+/* ------------------------------------------------------------------------ */
+
+/* The loss formula is not written on the pages.  Reading taken, for query
+ * row t with valid slots j (as for attention) and key rows s_j:
+ *   target   p_t(j) = sum_h P[t,h,j] / sum_j' sum_h P[t,h,j'],  with P the main
+ *            attention's probabilities exp(z_thj - lse[t,h]) recomputed from
+ *            q, kv and the row's own lse (sink: see attend_one; its mass is
+ *            not part of the target, which is renormalised over the slots);
+ *   indexer  u_t(j) = exp(I(t,s_j)) / sum_j' exp(I(t,s_j'))  (I as above);
+ *   loss_t = sum_j p_t(j) (log p_t(j) - log u_t(j))  (KL(p || u), 0 log 0 = 0).
+ * The target carries no gradient.  With upstream gradient g of sum_t loss_t:
+ *   dI(t,j)     = g (u_t(j) - p_t(j))
+ *   dw[t,h]     = sum_j dI(t,j) max(0, d_thj),      d_thj = <q_idx[t,h], k_idx[s_j]>
+ *   dq_idx[t,h] = sum_j dI(t,j) w[t,h] [d_thj > 0] k_idx[s_j]
+ *   dk_idx[s]  += sum over (t,j) with s_j = s of sum_h dI(t,j) w[t,h] [d_thj > 0] q_idx[t,h]
+ * (the derivative of max(0, x) at 0 is taken as 0).  A row with no valid slot
+ * has target 0, loss 0 and no gradient.
+ *
+ * For query rows [row_begin, row_end): target [(rows) x K] (0 at invalid
+ * slots), loss [rows], dq_idx [(rows) x Hi x Di], dw [(rows) x Hi] are
+ * row-relative; dk_idx [T_kv x Di] is accumulated into (the caller zeroes it)
+ * in row order.  k_idx has T_kv rows (the key rows of kv). */
+int oracle_indexer_kl(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                      const int32_t *topk_length, int64_t T_q, int64_t T_kv, int32_t H,
+                      int32_t Dqk, int32_t K, double scale, const double *sink,
+                      const uint16_t *q_idx, const uint16_t *k_idx, const float *w, int32_t Hi,
+                      int32_t Di, double g, int64_t row_begin, int64_t row_end, double *target,
+                      double *loss, double *dq_idx, double *dw, double *dk_idx) {
+  if (H < 1 || Dqk < 1 || K < 1 || Hi < 1 || Di < 1 || row_begin < 0 || row_end > T_q ||
+      row_begin > row_end)
+    return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    int32_t *slots = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    int32_t *where = (int32_t *)malloc(sizeof(int32_t) * (size_t)K); /* slot position j */
+    double *z = (double *)malloc(sizeof(double) * (size_t)K);
+    double *o = (double *)malloc(sizeof(double) * (size_t)Dqk);
+    double *pt = (double *)malloc(sizeof(double) * (size_t)K);
+    double *ii = (double *)malloc(sizeof(double) * (size_t)K);
+    double *di = (double *)malloc(sizeof(double) * (size_t)K);
+    double *dots = (double *)malloc(sizeof(double) * (size_t)K * Hi);
+    double *contrib = (double *)malloc(sizeof(double) * (size_t)K * Di);
+#pragma omp for schedule(dynamic, 1) ordered
+    for (int64_t t = row_begin; t < row_end; ++t) {
+      int64_t n = -2;
+      if (slots && where && z && o && pt && ii && di && dots && contrib) {
+        /* valid slots and their positions j in the row */
+        int64_t lim = topk_length ? topk_length[t] : K;
+        n = (lim < 0 || lim > K) ? -1 : 0;
+        for (int64_t j = 0; n >= 0 && j < lim; ++j) {
+          int32_t s = idx[(size_t)t * K + j];
+          if (s == -1) continue;
+          if (s < 0 || s >= T_kv) { n = -1; break; }
+          slots[n] = s;
+          where[n++] = (int32_t)j;
+        }
+      }
+      if (n < 0) {
+#pragma omp atomic write
+        err = n == -2 ? ORACLE_ENOMEM : ORACLE_EINVAL;
+#pragma omp ordered
+        {}
+        continue;
+      }
+      const size_t r = (size_t)(t - row_begin);
+      double *trow = target + r * K;
+      for (int32_t j = 0; j < K; ++j) trow[j] = 0.0;
+      for (int32_t h = 0; h < Hi; ++h) {
+        dw[r * Hi + h] = 0.0;
+        for (int32_t d = 0; d < Di; ++d) dq_idx[(r * Hi + h) * Di + d] = 0.0;
+      }
+      loss[r] = 0.0;
+      /* target: head sum of the attention probabilities, renormalised */
+      for (int64_t j = 0; j < n; ++j) pt[j] = 0.0;
+      for (int32_t h = 0; h < H; ++h) {
+        double lse;
+        attend_one(q, kv, slots, n, t, h, H, Dqk, 1, scale, sink, z, o, &lse);
+        for (int64_t j = 0; j < n; ++j) pt[j] += exp(z[j] - lse);
+      }
+      double tot = 0.0;
+      for (int64_t j = 0; j < n; ++j) tot += pt[j];
+      for (int64_t j = 0; j < n; ++j) {
+        pt[j] = tot > 0.0 ? pt[j] / tot : 0.0;
+        trow[where[j]] = pt[j];
+      }
+      /* indexer scores on the slots and their log-softmax */
+      const uint16_t *qr = q_idx + (size_t)t * Hi * Di;
+      const float *wr = w + (size_t)t * Hi;
+      double m = -INFINITY;
+      for (int64_t j = 0; j < n; ++j) {
+        const uint16_t *kr = k_idx + (size_t)slots[j] * Di;
+        double score = 0.0;
+        for (int32_t h = 0; h < Hi; ++h) {
+          double dot = 0.0;
+          for (int32_t d = 0; d < Di; ++d)
+            dot += bf16_to_double(qr[(size_t)h * Di + d]) * bf16_to_double(kr[d]);
+          dots[(size_t)j * Hi + h] = dot;
+          score += (double)wr[h] * (dot > 0.0 ? dot : 0.0);
+        }
+        ii[j] = score;
+        if (score > m) m = score;
+      }
+      double zsum = 0.0;
+      for (int64_t j = 0; j < n; ++j) zsum += exp(ii[j] - m);
+      const double logz = m + log(zsum);
+      double lsum = 0.0;
+      for (int64_t j = 0; j < n; ++j) {
+        const double logu = ii[j] - logz;
+        if (pt[j] > 0.0) lsum += pt[j] * (log(pt[j]) - logu);
+        di[j] = g * (exp(logu) - pt[j]);
+      }
+      loss[r] = lsum;
+      /* indexer backward */
+      memset(contrib, 0, sizeof(double) * (size_t)n * Di);
+      for (int64_t j = 0; j < n; ++j) {
+        const uint16_t *kr = k_idx + (size_t)slots[j] * Di;
+        double *cj = contrib + (size_t)j * Di;
+        for (int32_t h = 0; h < Hi; ++h) {
+          const double dot = dots[(size_t)j * Hi + h];
+          dw[r * Hi + h] += di[j] * (dot > 0.0 ? dot : 0.0);
+          if (!(dot > 0.0)) continue;
+          const double gh = di[j] * (double)wr[h];
+          double *dqr = dq_idx + (r * Hi + h) * Di;
+          for (int32_t d = 0; d < Di; ++d) {
+            dqr[d] += gh * bf16_to_double(kr[d]);
+            cj[d] += gh * bf16_to_double(qr[(size_t)h * Di + d]);
+          }
+        }
+      }
+#pragma omp ordered
+      {
+        for (int64_t j = 0; j < n; ++j) {
+          double *dst = dk_idx + (size_t)slots[j] * Di;
+          const double *cj = contrib + (size_t)j * Di;
+          for (int32_t d = 0; d < Di; ++d) dst[d] += cj[d];
+        }
+      }
+    }
+    free(slots);
+    free(where);
+    free(z);
+    free(o);
+    free(pt);
+    free(ii);
+    free(di);
+    free(dots);
+    free(contrib);
+  }
+  return err;
+}

@@ -509,3 +509,133 @@ def test_local_indexer_identity_padding_and_cp_split():
     i_u, l_u = oracle.indexer_topk_local(qr, kp, wr, cu, K, cu_seqlens_padded=cu_pad,
                                          query_indices=pad_coord)
     assert (l_u[:5] == 0).all() and l_u[5] == 5 and (i_u[5, :5] == np.arange(8, 13)).all()
+
+
+# ----------------------------------------------------------------------------
+# indexer KL loss (training path)
+# ----------------------------------------------------------------------------
+
+def _kl_case(T, H, Dqk, K, Hi, Di, n_valid, seed, cu=None):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn((T, H, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    kv = (torch.randn((T, Dqk), generator=g) * 0.5).to(torch.bfloat16)
+    q_idx = torch.randn((T, Hi, Di), generator=g).to(torch.bfloat16)
+    k_idx = torch.randn((T, Di), generator=g).to(torch.bfloat16)
+    w = torch.randn((T, Hi), generator=g) / 8
+    cu = cu or [0, T]
+    start = pins.segment_of(np.array(cu), T)
+    r = np.random.default_rng(seed)
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        L = t - start[t] + 1
+        n = min(n_valid, L)
+        idx[t, :n] = np.sort(start[t] + r.choice(L, size=n, replace=False))
+    return q, kv, idx, q_idx, k_idx, w
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_indexer_kl_matches_dense_autograd(sink):
+    """Loss, target and gradients equal a dense fp64 route through torch autograd: attention
+    probabilities restricted to the selected keys, their head sum renormalised, the indexer's
+    log-softmax over the same keys, KL(target || indexer) with the target detached."""
+    T, H, Dqk, K, Hi, Di = 48, 4, 64, 24, 8, 32
+    cu = [0, 17, 48]
+    q, kv, idx, q_idx, k_idx, w = _kl_case(T, H, Dqk, K, Hi, Di, 20, seed=11 + int(sink), cu=cu)
+    scale = 0.2
+    sk = np.array([0.3, -1.0, 2.0, -0.5]) if sink else None
+    ora = oracle.indexer_kl(q, kv, idx, None, scale, q_idx, k_idx, w, g=1.0, sink=sk)
+    # dense route
+    qd, kvd = pins.bf16_to_f64(q), pins.bf16_to_f64(kv)
+    qi = torch.tensor(pins.bf16_to_f64(q_idx), requires_grad=True)
+    ki = torch.tensor(pins.bf16_to_f64(k_idx), requires_grad=True)
+    wd = torch.tensor(w.numpy().astype(np.float64), requires_grad=True)
+    mask = torch.zeros((T, T), dtype=torch.bool)
+    for t in range(T):
+        sel = idx[t][idx[t] >= 0]
+        mask[t, torch.from_numpy(sel.astype(np.int64))] = True
+    z = scale * torch.einsum("thd,sd->ths", torch.from_numpy(qd), torch.from_numpy(kvd))
+    z = z.masked_fill(~mask[:, None, :], -math.inf)
+    if sink:
+        zs = torch.cat([z, torch.from_numpy(sk)[None, :, None].expand(T, H, 1)], dim=-1)
+        P = torch.exp(z - torch.logsumexp(zs, dim=-1, keepdim=True))
+    else:
+        P = torch.softmax(z, dim=-1)
+    pt = P.sum(1)
+    pt = pt / pt.sum(-1, keepdim=True)
+    dots = torch.einsum("thd,sd->ths", qi, ki)
+    I = torch.einsum("th,ths->ts", wd, torch.relu(dots))
+    logu = torch.log_softmax(I.masked_fill(~mask, -math.inf), dim=-1)
+    terms = torch.where(mask & (pt > 0), pt * (torch.log(pt) - logu), torch.zeros_like(pt))
+    loss_t = terms.sum(-1)
+    loss_t.sum().backward()
+    np.testing.assert_allclose(ora["loss"], loss_t.detach().numpy(), rtol=1e-10, atol=1e-12)
+    tgt = np.zeros((T, K))
+    for t in range(T):
+        for j in range(K):
+            if idx[t, j] >= 0:
+                tgt[t, j] = pt[t, idx[t, j]].item()
+    np.testing.assert_allclose(ora["target"], tgt, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(ora["dw"], wd.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(ora["dq_idx"], qi.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(ora["dk_idx"], ki.grad.numpy(), rtol=1e-9, atol=1e-12)
+    assert (ora["loss"] >= -1e-15).all()
+
+
+def test_indexer_kl_head_weight_finite_differences():
+    """dw against central differences of the loss in the fp32 head weights (the loss is smooth
+    in w: the ReLU acts on q_idx . k_idx only), with exactly representable steps."""
+    T, H, Dqk, K, Hi, Di = 20, 2, 32, 16, 4, 16
+    q, kv, idx, q_idx, k_idx, w = _kl_case(T, H, Dqk, K, Hi, Di, 12, seed=5)
+    w = torch.round(w * 1024) / 1024
+    scale = 0.3
+    base = oracle.indexer_kl(q, kv, idx, None, scale, q_idx, k_idx, w, g=1.0)
+    eps = 2.0 ** -12
+    for t, h in [(3, 0), (9, 2), (15, 1), (19, 3)]:
+        wp, wm = w.clone(), w.clone()
+        wp[t, h] += eps
+        wm[t, h] -= eps
+        lp = oracle.indexer_kl(q, kv, idx, None, scale, q_idx, k_idx, wp, rows=(t, t + 1))
+        lm = oracle.indexer_kl(q, kv, idx, None, scale, q_idx, k_idx, wm, rows=(t, t + 1))
+        fd = (lp["loss"][0] - lm["loss"][0]) / (2 * eps)
+        assert fd == pytest.approx(base["dw"][t, h], rel=1e-5, abs=1e-9)
+
+
+def test_indexer_kl_closed_forms():
+    """q_idx = 0: every indexer score is 0, the indexer distribution is uniform over the n valid
+    slots, loss = sum p log p + log n, and no gradient reaches q_idx, k_idx or w (the ReLU's
+    argument is 0 everywhere).  A row with one valid slot has loss 0."""
+    T, H, Dqk, K, Hi, Di = 24, 4, 64, 10, 4, 32
+    q, kv, idx, q_idx, k_idx, w = _kl_case(T, H, Dqk, K, Hi, Di, 10, seed=7)
+    zero = torch.zeros_like(q_idx)
+    r = oracle.indexer_kl(q, kv, idx, None, 0.25, zero, k_idx, w, g=1.0)
+    for t in range(T):
+        n = int((idx[t] >= 0).sum())
+        p = r["target"][t][idx[t] >= 0]
+        assert p.sum() == pytest.approx(1.0, abs=1e-14)
+        expect = float((p[p > 0] * np.log(p[p > 0])).sum() + math.log(n))
+        assert r["loss"][t] == pytest.approx(expect, abs=1e-13)
+    assert not r["dq_idx"].any() and not r["dw"].any() and not r["dk_idx"].any()
+    r1 = oracle.indexer_kl(q, kv, idx, None, 0.25, q_idx, k_idx, w, g=1.0)
+    assert r1["loss"][0] == 0.0 and not r1["dq_idx"][0].any() and not r1["dw"][0].any()
+
+
+def test_indexer_kl_chunks_and_head_permutation():
+    """Query chunks give the same rows and key gradients that sum to the one-shot result;
+    permuting indexer heads together with their weights permutes dq_idx and dw only."""
+    T, H, Dqk, K, Hi, Di = 40, 4, 64, 16, 8, 32
+    q, kv, idx, q_idx, k_idx, w = _kl_case(T, H, Dqk, K, Hi, Di, 14, seed=9)
+    full = oracle.indexer_kl(q, kv, idx, None, 0.2, q_idx, k_idx, w, g=0.5)
+    a = oracle.indexer_kl(q, kv, idx, None, 0.2, q_idx, k_idx, w, g=0.5, rows=(0, 13))
+    b = oracle.indexer_kl(q, kv, idx, None, 0.2, q_idx, k_idx, w, g=0.5, rows=(13, T),
+                          dk_idx=a["dk_idx"].copy())
+    np.testing.assert_array_equal(np.concatenate([a["loss"], b["loss"]]), full["loss"])
+    np.testing.assert_array_equal(np.concatenate([a["dq_idx"], b["dq_idx"]]), full["dq_idx"])
+    np.testing.assert_allclose(b["dk_idx"], full["dk_idx"], rtol=1e-13, atol=1e-15)
+    perm = torch.randperm(Hi, generator=torch.Generator().manual_seed(3))
+    p = oracle.indexer_kl(q, kv, idx, None, 0.2, q_idx[:, perm].contiguous(), k_idx,
+                          w[:, perm].contiguous(), g=0.5)
+    np.testing.assert_allclose(p["loss"], full["loss"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(p["dq_idx"], full["dq_idx"][:, perm.numpy()], rtol=1e-12,
+                               atol=1e-15)
+    np.testing.assert_allclose(p["dw"], full["dw"][:, perm.numpy()], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(p["dk_idx"], full["dk_idx"], rtol=1e-11, atol=1e-14)
