@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--sink", action="store_true",
                     help="run the step with a per-head attention sink (sink forward epilogue and "
                          "sink gradient kernels added)")
+    ap.add_argument("--indexer-loss", action="store_true",
+                    help="add the indexer's KL training loss to the step: the score recompute "
+                         "of the attention target and the indexer backward (coefficient 0.001 "
+                         "over the rows)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy a device buffer of BYTES bytes once with "
                          "an elementwise kernel (x * 1): a plain copy of known size, which "
@@ -147,6 +151,12 @@ class KernelTimer:
             assert self.hip.hipEventElapsedTime(C.byref(ms), s.start, s.stop) == 0
             out.setdefault(s.name.decode(), []).append(ms.value)
         return out
+
+
+def ms_step_events(step_ev):
+    """Mean step time from the per-step events."""
+    n = len(step_ev) - 1
+    return sum(step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(n)) / n
 
 
 def workload_counts(md_host, cfg, H_i, D_i, K, H, Dqk, Dv, kpool=None):
@@ -308,7 +318,17 @@ def main():
         kpool_valid = int(len_buf.sum().item())
         del kp
 
+    kl = args.indexer_loss
+    if kl and not has_indexer:
+        raise SystemExit("--indexer-loss needs a workload with an indexer stage")
+    if kl:
+        tgt_buf = torch.empty((T, K), dtype=torch.float32, device=dev)
+        dk_idx_buf = torch.empty((T_keys, cfg.idx_dim), dtype=torch.float32, device=dev)
+        kl_ws = torch.empty(dsa.indexer_kl_bwd_workspace_bytes(T, T_keys, K), dtype=torch.uint8,
+                            device=dev)
+        kl_grad = 0.001 / T
     bwd_events = []  # (start, stop) around each backward call while timing
+    kl_events = []   # (start, stop) around the indexer loss while timing
 
     def step():
         if local_rows is None:
@@ -320,9 +340,23 @@ def main():
         if has_indexer:
             dsa.indexer_topk(inputs["q_idx"], inputs["k_idx"], inputs["w"], md, K, idx=idx_buf,
                              length=len_buf)
-        for a in [att] + extra_layers:  # the layers reuse the indexer's indices
+        for li, a in enumerate([att] + extra_layers):  # the layers reuse the indexer's indices
             dsa.sparse_mla_fwd(a["q"], a["kv"], idx_buf, cfg.scale, len_buf, out=out_buf,
                                lse=lse_buf, sink=sink)
+            if kl and li == 0:
+                # the indexer's KL loss against the first layer's attention
+                if timing:
+                    kev = (torch.cuda.Event(enable_timing=True),
+                           torch.cuda.Event(enable_timing=True))
+                    kev[0].record()
+                dsa.indexer_kl_target(a["q"], a["kv"], idx_buf, lse_buf, cfg.scale, len_buf,
+                                      target=tgt_buf)
+                dsa.indexer_kl_bwd(inputs["q_idx"], inputs["k_idx"], inputs["w"], idx_buf,
+                                   tgt_buf, kl_grad, len_buf, dk_idx=dk_idx_buf,
+                                   workspace=kl_ws)
+                if timing:
+                    kev[1].record()
+                    kl_events.append(kev)
             if timing:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 ev[0].record()
@@ -404,6 +438,16 @@ def main():
         comp["indexer"] = {"ms": t_idx, "tokens_per_s": T / (t_idx * 1e-3),
                            "tflops": counts["idx_flops"] / t_idx / 1e9,
                            "frac_mfma_peak": counts["idx_flops"] / t_idx / 1e9 / PEAK_BF16_TFLOPS}
+    if kl:
+        # MFMA work per valid slot: the target's logits (2 H D_qk), the indexer dot products in
+        # both passes, dq_idx and the key-gradient contributions (4 x 2 H_i D_i)
+        kl_flops = counts["valid"] * (2.0 * H * Dqk + 8.0 * cfg.idx_heads * cfg.idx_dim)
+        t_kl = sum(a.elapsed_time(b) for a, b in kl_events) / len(kl_events)
+        comp["indexer_loss"] = {"ms": t_kl, "share_of_step": t_kl / ms_step_events(step_ev),
+                                "target_ms": avg("indexer_kl_target"),
+                                "bwd_rows_ms": avg("indexer_kl_bwd"),
+                                "tflops": kl_flops / t_kl / 1e9,
+                                "frac_mfma_peak": kl_flops / t_kl / 1e9 / PEAK_BF16_TFLOPS}
     if args.sink:
         # HBM-streaming kernels: the epilogue reads and writes out [T,H,Dv] bf16 and lse; the
         # gradient kernel reads out, dout and lse
@@ -449,6 +493,7 @@ def main():
                    "indexer": (f"{cfg.idx_heads}x{cfg.idx_dim}" if has_indexer else None),
                    "topk": K, "heads": H, "d_qk": Dqk, "d_v": Dv, "bwd_passes": args.bwd_passes,
                    "attention_sink": bool(args.sink), "attention_layers": n_layers,
+                   "indexer_loss": bool(kl),
                    "context_parallel": ({"ranks": args.cp, "rank": 0, "local_tokens": T,
                                          "key_tokens": T_keys} if args.cp > 1 else None),
                    "parallelism": "none"},

@@ -232,6 +232,55 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                        float *dkv, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
+ * Indexer training loss (GLM-5.2 page, "How DSA works": the indexer emits an
+ * auxiliary KL loss that aligns its score distribution with the main
+ * attention's, on a graph separate from the main model's; "GLM-5.2 training
+ * results": sparse formulation, coefficient 0.001, computed with a
+ * score-recompute step and an indexer backward; "cuDNN fused DSA kernels").
+ * The pages give no formula.  Reading implemented, for query row t with the
+ * attention's valid slots j (idx[t,j] != -1, j < topk_length) and key rows s_j:
+ *   target  p(j) = sum_h P[t,h,j] / sum_j' sum_h P[t,h,j'], P = exp(z - lse)
+ *           (the attention probabilities, recomputed; no gradient)
+ *   indexer u(j) = softmax over j of I(t, s_j)   (I as for dsa_indexer_topk)
+ *   loss[t] = sum_j p(j) (log p(j) - log u(j))        (KL(p || u))
+ * The caller applies the loss coefficient (0.001 on the page) and any
+ * normalisation through `grad`, the gradient of its loss with respect to
+ * sum_t loss[t]; then dI(t,j) = grad (u(j) - p(j)) and
+ *   dw[t,h]     = sum_j dI max(0, d_thj),      d_thj = q_idx[t,h] . k_idx[s_j]
+ *   dq_idx[t,h] = sum_j dI w[t,h] [d_thj > 0] k_idx[s_j]
+ *   dk_idx[s]  += sum over (t,j) with s_j = s of sum_h dI w[t,h] [d_thj > 0] q_idx[t,h]
+ *
+ * dsa_indexer_kl_target: target [T_q, K] fp32 (0 at invalid slots and for rows
+ * without a valid slot) from q, kv, idx, topk_length and the forward's lse
+ * (with a sink, lse' of the sink forward: the sink's mass is then left out and
+ * the target renormalised over the slots).  Arguments and limits as
+ * dsa_sparse_mla_fwd.
+ *
+ * dsa_indexer_kl_bwd: from q_idx [T_q, H_i, 128] bf16, k_idx [T_kv, 128] bf16
+ * (the key rows of kv), w [T_q, H_i] fp32, idx / topk_length as for attention
+ * and the target: loss [T_q] fp32, dq_idx [T_q, H_i, 128] bf16, dw [T_q, H_i]
+ * fp32 (overwritten) and dk_idx [T_kv, 128] fp32 (overwritten, or added into
+ * with DSA_BWD_ACCUMULATE_DKV).  The key gradient is staged per (query, slot)
+ * as for dsa_sparse_mla_bwd (16-bit block floating point rows) and summed per
+ * key row after a counting sort; it is reproducible up to summation order.
+ * Workspace: dsa_indexer_kl_bwd_workspace_size(..., rows_per_pass) bytes for
+ * passes of rows_per_pass query rows (<= 0: one pass); any ws_bytes of at
+ * least the size for one row works, larger ones take fewer passes.
+ * Supported: 1 <= H_i <= 64, D_i = 128, 1 <= K <= 4096, finite grad.
+ * ------------------------------------------------------------------------ */
+int dsa_indexer_kl_target(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                          const int32_t *topk_length, const float *lse, int64_t T_q,
+                          int64_t T_kv, int32_t H, int32_t D_qk, int32_t K, float scale,
+                          float *target, void *stream);
+size_t dsa_indexer_kl_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t K,
+                                         int64_t rows_per_pass);
+int dsa_indexer_kl_bwd(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
+                       const int32_t *idx, const int32_t *topk_length, const float *target,
+                       int64_t T_q, int64_t T_kv, int32_t H_i, int32_t D_i, int32_t K,
+                       float grad, float *loss, uint16_t *dq_idx, float *dw, float *dk_idx,
+                       uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
  * Allocation-free backward, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Arguments, results and errors as dsa_sparse_mla_bwd, without

@@ -83,6 +83,14 @@ def lib():
         L.dsa_sparse_mla_bwd_sink.restype = C.c_int
         L.dsa_sparse_mla_bwd_sink.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32,
                                               i32, f32, vp, vp, vp, vp, u32, vp, sz, vp]
+        L.dsa_indexer_kl_target.restype = C.c_int
+        L.dsa_indexer_kl_target.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, vp,
+                                             vp]
+        L.dsa_indexer_kl_bwd_workspace_size.restype = sz
+        L.dsa_indexer_kl_bwd_workspace_size.argtypes = [i64, i64, i32, i64]
+        L.dsa_indexer_kl_bwd.restype = C.c_int
+        L.dsa_indexer_kl_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, vp,
+                                         vp, vp, vp, u32, vp, sz, vp]
         L.dsa_sparse_mla_bwd_noalloc_scratch_bytes.argtypes = []
         L.dsa_sparse_mla_bwd_noalloc_scratch_bytes.restype = sz
         L.dsa_sparse_mla_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32,
@@ -433,3 +441,69 @@ def sparse_mla_bwd_noalloc(q, kv, topk_indices, out, lse, dout, softmax_scale: f
           _ptr(topk_length), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), Tq, Tkv, H, Dqk,
           d_v, K, float(softmax_scale), dq.data_ptr(), dkv.data_ptr(), flags, _stream())
     return dq, dkv
+
+
+def indexer_kl_target(q, kv, topk_indices, lse, softmax_scale: float, topk_length=None,
+                      target=None):
+    """dsa_indexer_kl_target -> target fp32 [T_q, K]: the head-summed attention probabilities of
+    every valid slot, renormalised per row (the KL loss's target; no gradient)."""
+    op = "indexer_kl_target"
+    _require(op, q, kv, topk_indices, lse, topk_length, target)
+    kv2, idx, Tq, H, Dqk, Tkv, K = _attn_shapes(op, q, kv, topk_indices, topk_length)
+    _dtype(op, "lse", lse, torch.float32)
+    if lse.shape != (Tq, H):
+        raise ValueError(f"{op}: lse must be [T_q, H]")
+    if target is None:
+        target = torch.empty((Tq, K), dtype=torch.float32, device=q.device)
+    _dtype(op, "target", target, torch.float32)
+    if target.shape != (Tq, K):
+        raise ValueError(f"{op}: target must be [T_q, K] fp32")
+    _call(lib().dsa_indexer_kl_target, op, q.data_ptr(), kv2.data_ptr(), idx.data_ptr(),
+          _ptr(topk_length), lse.data_ptr(), Tq, Tkv, H, Dqk, K, float(softmax_scale),
+          target.data_ptr(), _stream())
+    return target
+
+
+def indexer_kl_bwd_workspace_bytes(T_q: int, T_kv: int, K: int,
+                                   rows_per_pass: int = 0) -> int:
+    return lib().dsa_indexer_kl_bwd_workspace_size(T_q, T_kv, K, rows_per_pass)
+
+
+def indexer_kl_bwd(q_idx, k_idx, w, topk_indices, target, grad: float = 1.0, topk_length=None,
+                   dk_idx=None, accumulate: bool = False, workspace=None):
+    """dsa_indexer_kl_bwd -> (loss fp32 [T_q], dq_idx bf16 [T_q,H_i,128], dw fp32 [T_q,H_i],
+    dk_idx fp32 [T_kv,128]); `grad` is the gradient of the caller's loss with respect to
+    sum_t loss[t] (for example the coefficient 0.001 divided by the number of rows)."""
+    op = "indexer_kl_bwd"
+    _require(op, q_idx, k_idx, w, topk_indices, target, topk_length, dk_idx)
+    _dtype(op, "q_idx", q_idx, torch.bfloat16)
+    _dtype(op, "k_idx", k_idx, torch.bfloat16)
+    _dtype(op, "w", w, torch.float32)
+    _dtype(op, "topk_indices", topk_indices, torch.int32)
+    _dtype(op, "target", target, torch.float32)
+    _dtype(op, "topk_length", topk_length, torch.int32)
+    _dtype(op, "dk_idx", dk_idx, torch.float32)
+    if q_idx.dim() != 3 or k_idx.dim() != 2:
+        raise ValueError(f"{op}: q_idx must be [T_q,H_i,D_i] and k_idx [T_kv,D_i]")
+    Tq, Hi, Di = q_idx.shape
+    Tkv = k_idx.shape[0]
+    idx = topk_indices.reshape(Tq, -1)
+    K = idx.shape[1]
+    if k_idx.shape[1] != Di or w.shape != (Tq, Hi) or target.shape != (Tq, K):
+        raise ValueError(f"{op}: shapes of k_idx, w or target do not match q_idx / topk_indices")
+    if dk_idx is None:
+        if accumulate:
+            raise ValueError(f"{op}: accumulate=True needs a dk_idx buffer")
+        dk_idx = torch.empty((Tkv, Di), dtype=torch.float32, device=q_idx.device)
+    loss = torch.empty((Tq,), dtype=torch.float32, device=q_idx.device)
+    dq_idx = torch.empty_like(q_idx)
+    dw = torch.empty_like(w)
+    if workspace is None:
+        workspace = torch.empty(max(indexer_kl_bwd_workspace_bytes(Tq, Tkv, K), 1),
+                                dtype=torch.uint8, device=q_idx.device)
+    _call(lib().dsa_indexer_kl_bwd, op, q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr(),
+          idx.data_ptr(), _ptr(topk_length), target.data_ptr(), Tq, Tkv, Hi, Di, K,
+          float(grad), loss.data_ptr(), dq_idx.data_ptr(), dw.data_ptr(), dk_idx.data_ptr(),
+          DSA_BWD_ACCUMULATE_DKV if accumulate else 0, workspace.data_ptr(), workspace.numel(),
+          _stream())
+    return loss, dq_idx, dw, dk_idx

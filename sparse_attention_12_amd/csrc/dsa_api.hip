@@ -570,6 +570,97 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                  D_v, K, scale, dq, dkv, flags, ws, ws_bytes, true, DSA_ERR_WORKSPACE, stream);
 }
 
+// ---------------------------------------------------------------------------------------
+// Indexer KL loss.  kl_bwd workspace: off [T_kv + 1] | cursor [T_kv] | list [R * K] | stage
+// [R * K] rows of bwd_stage_row_bytes(128), every segment 256-byte aligned.
+static size_t kl_pass_bytes(int64_t rows, int64_t T_kv, int32_t K) {
+  const size_t pairs = static_cast<size_t>(rows) * static_cast<size_t>(K);
+  return 256 + align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t)) +
+         align_up(static_cast<size_t>(T_kv) * sizeof(int32_t)) + align_up(pairs * sizeof(int32_t)) +
+         align_up(pairs * dsa::bwd_stage_row_bytes(128));
+}
+
+size_t dsa_indexer_kl_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t K,
+                                         int64_t rows_per_pass) {
+  if (T_q < 0 || T_kv < 0 || K < 1) return 0;
+  int64_t R = rows_per_pass <= 0 || rows_per_pass > T_q ? T_q : rows_per_pass;
+  R = std::min<int64_t>(R, INT32_MAX / K);
+  return kl_pass_bytes(std::max<int64_t>(R, 1), T_kv, K);
+}
+
+int dsa_indexer_kl_target(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                          const int32_t *topk_length, const float *lse, int64_t T_q,
+                          int64_t T_kv, int32_t H, int32_t D_qk, int32_t K, float scale,
+                          float *target, void *stream) {
+  g_last_error.clear();
+  const char *who = "indexer_kl_target";
+  if (int rc = check_attention_args(who, q, kv, idx, T_q, T_kv, H, D_qk, 512, K, scale, 64))
+    return rc;
+  if (K > 4096) return fail(DSA_ERR_INVALID_VALUE, "%s: K=%d exceeds 4096", who, K);
+  if (T_q > 0 && (!lse || !target))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: NULL lse or target", who);
+  if (int rc = check_device()) return rc;
+  hipError_t e = dsa::launch_indexer_kl_target(q, kv, idx, topk_length, lse, T_q, H, D_qk, K,
+                                               scale, target, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "indexer_kl_target: launch");
+  return DSA_OK;
+}
+
+int dsa_indexer_kl_bwd(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
+                       const int32_t *idx, const int32_t *topk_length, const float *target,
+                       int64_t T_q, int64_t T_kv, int32_t H_i, int32_t D_i, int32_t K,
+                       float grad, float *loss, uint16_t *dq_idx, float *dw, float *dk_idx,
+                       uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  const char *who = "indexer_kl_bwd";
+  if (T_q < 0 || T_kv < 0 || T_q > INT32_MAX || T_kv > INT32_MAX)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: T_q / T_kv out of range", who);
+  if (H_i < 1 || H_i > 64) return fail(DSA_ERR_INVALID_VALUE, "%s: H_i=%d not in [1, 64]", who, H_i);
+  if (D_i != 128) return fail(DSA_ERR_INVALID_VALUE, "%s: D_i=%d must be 128", who, D_i);
+  if (K < 1 || K > 4096) return fail(DSA_ERR_INVALID_VALUE, "%s: K=%d not in [1, 4096]", who, K);
+  if (!(grad == grad) || grad == INFINITY || grad == -INFINITY)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: grad must be finite", who);
+  if (flags & ~DSA_BWD_ACCUMULATE_DKV)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: unknown flags 0x%x", who, flags);
+  if (T_q > 0 && T_kv < 1)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: T_kv must be >= 1 when T_q > 0", who);
+  if (T_kv * static_cast<int64_t>(D_i) * 2 > static_cast<int64_t>(UINT32_MAX))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: k_idx exceeds 4 GiB", who);
+  if (T_q > 0 && (!q_idx || !k_idx || !w || !idx || !target || !loss || !dq_idx || !dw))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: NULL tensor pointer", who);
+  if (T_kv > 0 && !dk_idx) return fail(DSA_ERR_INVALID_VALUE, "%s: dk_idx is NULL", who);
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(dq_idx) || !aligned16(dk_idx))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: q_idx/k_idx/dq_idx/dk_idx must be 16-byte aligned",
+                who);
+  const size_t need = kl_pass_bytes(1, T_kv, K);
+  if (T_q > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "%s: workspace needs at least %zu bytes, got %zu", who, need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  int64_t R = 1;
+  if (T_q > 0) {
+    const int64_t R_max = std::min<int64_t>(T_q, INT32_MAX / K);
+    const size_t per_row = static_cast<size_t>(K) * (dsa::bwd_stage_row_bytes(128) + 4);
+    R = std::min<int64_t>(R_max, static_cast<int64_t>((ws_bytes - kl_pass_bytes(0, T_kv, K)) /
+                                                      per_row) + 1);
+    while (R > 1 && kl_pass_bytes(R, T_kv, K) > ws_bytes) --R;
+  }
+  if (int rc = check_device()) return rc;
+  dsa::BwdPassBuffers bb;
+  char *p = reinterpret_cast<char *>(align_up(reinterpret_cast<uintptr_t>(ws)));
+  bb.off = reinterpret_cast<int32_t *>(p);
+  p += align_up(static_cast<size_t>(T_kv + 1) * sizeof(int32_t));
+  bb.cursor = reinterpret_cast<int32_t *>(p);
+  p += align_up(static_cast<size_t>(T_kv) * sizeof(int32_t));
+  bb.list = reinterpret_cast<int32_t *>(p);
+  p += align_up(static_cast<size_t>(R) * static_cast<size_t>(K) * sizeof(int32_t));
+  bb.stage = reinterpret_cast<uint32_t *>(p);
+  hipError_t e = dsa::launch_indexer_kl_bwd(
+      q_idx, k_idx, w, idx, topk_length, target, T_q, T_kv, H_i, K, grad, loss, dq_idx, dw,
+      dk_idx, (flags & DSA_BWD_ACCUMULATE_DKV) != 0, bb, R, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "indexer_kl_bwd: launch");
+  return DSA_OK;
+}
+
 size_t dsa_sparse_mla_bwd_noalloc_scratch_bytes(void) { return dsa::kNoAllocScratchBytes; }
 
 int dsa_sparse_mla_bwd_noalloc(const uint16_t *q, const uint16_t *kv, const int32_t *idx,

@@ -79,6 +79,30 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
                                  uint16_t *dq, float *dkv, bool accumulate,
                                  const BwdWorkspace &ws, hipStream_t s);
 
+// Counting sort of the (query, slot) pairs of query rows [row0, row0 + rows) by key row, and
+// the per-key-row sum of their staged contributions into dst [n_rows, D] (D = 128: the indexer
+// key gradient); the staging kernel counts each key row's pairs into bb.off after count_zero.
+hipError_t launch_pair_count_zero(int64_t n_rows, const BwdPassBuffers &bb, hipStream_t s);
+hipError_t launch_pair_sort(const int32_t *idx, const int32_t *topk_length, int64_t row0,
+                            int64_t rows, int64_t n_rows, int32_t K, const BwdPassBuffers &bb,
+                            hipStream_t s);
+hipError_t launch_pair_reduce(int32_t D, int64_t n_rows, const BwdPassBuffers &bb, float *dst,
+                              hipStream_t s);
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
+
+// Indexer KL loss: the attention target (score recompute) and the indexer backward over the
+// pass buffers (see dsa.h).
+hipError_t launch_indexer_kl_target(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                                    const int32_t *topk_length, const float *lse, int64_t T_q,
+                                    int32_t H, int32_t D_qk, int32_t K, float scale,
+                                    float *target, hipStream_t s);
+hipError_t launch_indexer_kl_bwd(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,
+                                 const int32_t *idx, const int32_t *topk_length,
+                                 const float *target, int64_t T_q, int64_t T_kv, int32_t H_i,
+                                 int32_t K, float grad, float *loss, uint16_t *dq_idx, float *dw,
+                                 float *dk_idx, bool accumulate, const BwdPassBuffers &bb,
+                                 int64_t rows_per_pass, hipStream_t s);
+
 // Fixed device scratch of the allocation-free backward, per GPU (bytes), and the device address
 // of the calling thread's current GPU's copy (looked up on first use per device).
 constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(256) << 20;

@@ -26,6 +26,7 @@
 
 #include "dsa_common.h"
 #include "dsa_internal.h"
+#include "stage.h"
 #include "tile.h"
 
 namespace dsa {
@@ -33,33 +34,6 @@ namespace {
 
 constexpr int kSlots = 32;
 constexpr int kDv = 512;
-
-// Staged contributions are 16-bit block floating point.  A block is the D_qk / 16 channels
-// that one lane of a contribution wave holds for one slot (channels 16 kNTq qq + 16 n + 4 g + i
-// of wave qq, lane group g).  With 2^e the smallest power of two above the block's largest
-// magnitude (e = the float exponent field of that magnitude, minus 126), channel x is kept as
-// the signed 16-bit m = round(32767 x / 2^e) and read back as m 2^e / 32767: an error of at
-// most 2^-15 of the block's largest magnitude.  A staged row is D_qk mantissas in channel
-// order, then 16 exponent bytes (byte 4 qq + g: the field of the block's largest magnitude,
-// at most 253).
-template <int DQK>
-constexpr int kStageWords = DQK / 2 + 4;  // 32-bit words per staged row
-template <int DQK>
-__device__ __forceinline__ int stage_exp_byte(int ch) {  // exponent byte of channel ch
-  return ch / (DQK / 4) * 4 + ((ch >> 2) & 3);
-}
-__device__ __forceinline__ uint32_t pknorm16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(a, b));
-}
-__device__ __forceinline__ float stage_factor(uint32_t eb) {  // 2^e / 32767
-  return __uint_as_float((eb + 1u) << 23) * (1.0f / 32767.0f);
-}
-__device__ __forceinline__ f32x4 unpack_m16x4(const u32x2 &m, float f) {
-  return f32x4{static_cast<float>(static_cast<int32_t>(m[0] << 16) >> 16) * f,
-               static_cast<float>(static_cast<int32_t>(m[0]) >> 16) * f,
-               static_cast<float>(static_cast<int32_t>(m[1] << 16) >> 16) * f,
-               static_cast<float>(static_cast<int32_t>(m[1]) >> 16) * f};
-}
 
 // ---------------------------------------------------------------------------------------
 __global__ void fill_zero_kernel(float *__restrict__ p, int64_t n) {
@@ -889,29 +863,39 @@ hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx
 // Counting sort of pass [row0, row0 + rows) into buffer bb: the counts are cleared before the
 // rows launch (launch_count_zero), which counts each latent row's contributions; the scan and
 // the fill of the pair list follow it (launch_sort).
-hipError_t launch_count_zero(int64_t T_kv, const BwdPassBuffers &bb, hipStream_t s) {
+// Kernel names for the benchmark's event hooks: the attention backward's, or the indexer
+// loss's (same kernels on its own pass buffers).
+struct SortNames {
+  const char *zero, *scan, *fill, *reduce;
+};
+constexpr SortNames kBwdNames = {"pair_zero", "pair_scan", "pair_fill", "sparse_mla_bwd_reduce"};
+constexpr SortNames kKlNames = {"kl_pair_zero", "kl_pair_scan", "kl_pair_fill",
+                                "indexer_kl_reduce"};
+
+hipError_t launch_count_zero(int64_t T_kv, const BwdPassBuffers &bb, hipStream_t s,
+                             const SortNames &nm = kBwdNames) {
   const unsigned zb = static_cast<unsigned>(std::min<int64_t>((T_kv + 256) / 256, 65536));
-  DSA_LAUNCH("pair_zero", fill_zero_i32_kernel, dim3(zb), dim3(256), 0, s, bb.off, T_kv + 1);
+  DSA_LAUNCH(nm.zero, fill_zero_i32_kernel, dim3(zb), dim3(256), 0, s, bb.off, T_kv + 1);
   return hipGetLastError();
 }
 
 hipError_t launch_sort(const int32_t *idx, const int32_t *topk_length, int64_t row0,
                        int64_t rows, int64_t T_kv, int32_t K, const BwdPassBuffers &bb,
-                       hipStream_t s) {
+                       hipStream_t s, const SortNames &nm = kBwdNames) {
   const int64_t pairs = rows * K;
   const unsigned pb = static_cast<unsigned>((pairs + 255) / 256);
-  DSA_LAUNCH("pair_scan", pair_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, bb.off,
-             bb.cursor, T_kv);
-  DSA_LAUNCH("pair_fill", pair_fill_kernel, dim3(pb), dim3(256), 0, s, idx, topk_length, row0,
-             rows, K, bb.cursor, bb.list);
+  DSA_LAUNCH(nm.scan, pair_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, bb.off, bb.cursor,
+             T_kv);
+  DSA_LAUNCH(nm.fill, pair_fill_kernel, dim3(pb), dim3(256), 0, s, idx, topk_length, row0, rows,
+             K, bb.cursor, bb.list);
   return hipGetLastError();
 }
 
 template <int DQK>
-hipError_t launch_reduce(int64_t T_kv, const BwdPassBuffers &bb, float *dkv, hipStream_t s) {
-  DSA_LAUNCH("sparse_mla_bwd_reduce", pair_reduce_kernel<DQK>,
-             dim3(static_cast<unsigned>((T_kv + 3) / 4)), dim3(256), 0, s, bb.off, bb.list,
-             bb.stage, T_kv, dkv);
+hipError_t launch_reduce(int64_t T_kv, const BwdPassBuffers &bb, float *dkv, hipStream_t s,
+                         const SortNames &nm = kBwdNames) {
+  DSA_LAUNCH(nm.reduce, pair_reduce_kernel<DQK>, dim3(static_cast<unsigned>((T_kv + 3) / 4)),
+             dim3(256), 0, s, bb.off, bb.list, bb.stage, T_kv, dkv);
   return hipGetLastError();
 }
 
@@ -1050,6 +1034,30 @@ hipError_t noalloc_scratch(void **ptr) {
   }
   *ptr = per_dev[dev];
   return hipSuccess;
+}
+
+hipError_t launch_pair_count_zero(int64_t n_rows, const BwdPassBuffers &bb, hipStream_t s) {
+  return launch_count_zero(n_rows, bb, s, kKlNames);
+}
+
+hipError_t launch_pair_sort(const int32_t *idx, const int32_t *topk_length, int64_t row0,
+                            int64_t rows, int64_t n_rows, int32_t K, const BwdPassBuffers &bb,
+                            hipStream_t s) {
+  return launch_sort(idx, topk_length, row0, rows, n_rows, K, bb, s, kKlNames);
+}
+
+hipError_t launch_pair_reduce(int32_t D, int64_t n_rows, const BwdPassBuffers &bb, float *dst,
+                              hipStream_t s) {
+  if (D == 128) return launch_reduce<128>(n_rows, bb, dst, s, kKlNames);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+  DSA_LAUNCH("kl_dk_zero", fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+             p, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_check_indices(const int32_t *idx, const int32_t *topk_length, int64_t T_q,

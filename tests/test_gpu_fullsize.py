@@ -375,3 +375,45 @@ def test_full_thd_T32768_attention_sink_sampled_rows():
     rdq, _, _ = oracle.sparse_mla_bwd(q, kv, ii, ll, att["dout"][rows_t].cpu(), w.scale, sink=sk)
     e_q = checks.assert_close("sink dq", _np(dq[rows_t].float()), rdq, checks.ATOL_OUT)
     _log(f"sink rows {len(rows)}: out {e_o:.2e} lse {e_l:.2e} dq {e_q:.2e}")
+
+
+def test_full_thd_T32768_indexer_kl_loss():
+    """The indexer KL training path at the bench workload (the launch configuration of
+    `bench.py --indexer-loss`): score recompute and indexer backward on the indexer's own top-k;
+    target, loss, dq_idx and dw of sampled rows against the oracle, and the complete dk_idx of
+    every key row of the first sequence (all its contributors are query rows 0..1023)."""
+    from tests import test_gpu_kl as kl
+    dsa = _dsa()
+    w = gen.workload(3)
+    _log(f"workload {w.name} with the indexer loss")
+    b = _Bufs(w.T, w.topk, w.heads, w.d_qk, w.d_v)
+    inp, md = _run_indexer(3, b)
+    att = gen.attention_inputs(3, device=dev)
+    dsa.sparse_mla_fwd(att["q"], att["kv"], b.idx, w.scale, b.len, out=b.out, lse=b.lse)
+    target = dsa.indexer_kl_target(att["q"], att["kv"], b.idx, b.lse, w.scale, b.len)
+    grad = 0.001 / w.T
+    loss, dq_idx, dw, dk_idx = dsa.indexer_kl_bwd(inp["q_idx"], inp["k_idx"], inp["w"], b.idx,
+                                                  target, grad, b.len)
+    torch.cuda.synchronize()
+    assert torch.isfinite(loss).all() and torch.isfinite(dk_idx).all()
+    q_c, kv_c = att["q"].cpu(), att["kv"].cpu()
+    qi_c, ki_c, w_c = inp["q_idx"].cpu(), inp["k_idx"].cpu(), inp["w"].cpu()
+    idx_c, len_c = _np(b.idx), _np(b.len)
+    # sampled rows: each row's own quantities are complete from the row alone
+    rows = _attention_sample(w.cu_seqlens, n_spread=4, seed=11)
+    for t in rows:
+        t = int(t)
+        ref = oracle.indexer_kl(q_c, kv_c, idx_c, len_c, w.scale, qi_c, ki_c, w_c, g=grad,
+                                rows=(t, t + 1))
+        gpu = dict(target=_np(target[t:t + 1]), loss=_np(loss[t:t + 1]),
+                   dq_idx=_np(dq_idx[t:t + 1].float()), dw=_np(dw[t:t + 1]))
+        kl._check("target", gpu["target"], ref["target"], 1e-4)
+        kl._check("dq_idx", gpu["dq_idx"], ref["dq_idx"], 4e-3)
+        kl._check("dw", gpu["dw"], ref["dw"], 1e-3)
+        assert abs(gpu["loss"][0] - ref["loss"][0]) <= 1e-4 * (1 + abs(ref["loss"][0])), t
+    # every key row of the first sequence
+    s, e = w.cu_seqlens[0], w.cu_seqlens[1]
+    ref = oracle.indexer_kl(q_c, kv_c, idx_c, len_c, w.scale, qi_c, ki_c, w_c, g=grad,
+                            rows=(s, e))
+    err = kl._check("dk_idx first sequence", _np(dk_idx[s:e]), ref["dk_idx"][s:e], 1e-3)
+    _log(f"indexer loss: {len(rows)} sampled rows ok, dk_idx rows [{s},{e}) {err:.2e}")
