@@ -321,6 +321,8 @@ def main():
     kl = args.indexer_loss
     if kl and not has_indexer:
         raise SystemExit("--indexer-loss needs a workload with an indexer stage")
+    if kl and args.sink:
+        raise SystemExit("--indexer-loss and --sink are measured separately")
     if kl:
         tgt_buf = torch.empty((T, K), dtype=torch.float32, device=dev)
         dk_idx_buf = torch.empty((T_keys, cfg.idx_dim), dtype=torch.float32, device=dev)
@@ -343,29 +345,30 @@ def main():
         for li, a in enumerate([att] + extra_layers):  # the layers reuse the indexer's indices
             dsa.sparse_mla_fwd(a["q"], a["kv"], idx_buf, cfg.scale, len_buf, out=out_buf,
                                lse=lse_buf, sink=sink)
+            if timing:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[0].record()
+            # with the indexer loss, the first layer's backward also writes the loss's target
+            # (the fused KL-score path: the head sums of the probabilities it recomputes)
+            dsa.sparse_mla_bwd(a["q"], a["kv"], idx_buf, out_buf, lse_buf, a["dout"],
+                               cfg.scale, len_buf, dkv=dkv_buf, dq=dq_buf, workspace=ws,
+                               sink=sink, dsink=dsink_buf,
+                               kl_target=tgt_buf if kl and li == 0 else None)
+            if timing:
+                ev[1].record()
+                bwd_events.append(ev)
             if kl and li == 0:
-                # the indexer's KL loss against the first layer's attention
+                # the indexer's KL loss and its backward against the first layer's attention
                 if timing:
                     kev = (torch.cuda.Event(enable_timing=True),
                            torch.cuda.Event(enable_timing=True))
                     kev[0].record()
-                dsa.indexer_kl_target(a["q"], a["kv"], idx_buf, lse_buf, cfg.scale, len_buf,
-                                      target=tgt_buf)
                 dsa.indexer_kl_bwd(inputs["q_idx"], inputs["k_idx"], inputs["w"], idx_buf,
                                    tgt_buf, kl_grad, len_buf, dk_idx=dk_idx_buf,
                                    workspace=kl_ws)
                 if timing:
                     kev[1].record()
                     kl_events.append(kev)
-            if timing:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[0].record()
-            dsa.sparse_mla_bwd(a["q"], a["kv"], idx_buf, out_buf, lse_buf, a["dout"],
-                               cfg.scale, len_buf, dkv=dkv_buf, dq=dq_buf, workspace=ws,
-                               sink=sink, dsink=dsink_buf)
-            if timing:
-                ev[1].record()
-                bwd_events.append(ev)
         return md
 
     timing = False
@@ -439,12 +442,13 @@ def main():
                            "tflops": counts["idx_flops"] / t_idx / 1e9,
                            "frac_mfma_peak": counts["idx_flops"] / t_idx / 1e9 / PEAK_BF16_TFLOPS}
     if kl:
-        # MFMA work per valid slot: the target's logits (2 H D_qk), the indexer dot products in
-        # both passes, dq_idx and the key-gradient contributions (4 x 2 H_i D_i)
-        kl_flops = counts["valid"] * (2.0 * H * Dqk + 8.0 * cfg.idx_heads * cfg.idx_dim)
+        # MFMA work per valid slot of the indexer backward: the dot products in both passes,
+        # dq_idx and the key-gradient contributions (4 x 2 H_i D_i); the target comes out of
+        # the attention backward (its extra time is inside the backward's)
+        kl_flops = counts["valid"] * 8.0 * cfg.idx_heads * cfg.idx_dim
         t_kl = sum(a.elapsed_time(b) for a, b in kl_events) / len(kl_events)
         comp["indexer_loss"] = {"ms": t_kl, "share_of_step": t_kl / ms_step_events(step_ev),
-                                "target_ms": avg("indexer_kl_target"),
+                                "target": "fused into the attention backward",
                                 "bwd_rows_ms": avg("indexer_kl_bwd"),
                                 "tflops": kl_flops / t_kl / 1e9,
                                 "frac_mfma_peak": kl_flops / t_kl / 1e9 / PEAK_BF16_TFLOPS}

@@ -272,6 +272,17 @@ int dsa_indexer_kl_target(const uint16_t *q, const uint16_t *kv, const int32_t *
                           const int32_t *topk_length, const float *lse, int64_t T_q,
                           int64_t T_kv, int32_t H, int32_t D_qk, int32_t K, float scale,
                           float *target, void *stream);
+/* The fused KL-score path: dsa_sparse_mla_bwd that also writes the target of
+ * dsa_indexer_kl_target (target [T_q, K] fp32, not NULL when T_q > 0), summed
+ * over heads from the probabilities the backward recomputes anyway (staged in
+ * fp16: relative error about 2^-12 per term).  Arguments, workspace and errors
+ * otherwise as dsa_sparse_mla_bwd. */
+int dsa_sparse_mla_bwd_kl_target(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                                 const int32_t *topk_length, const uint16_t *out,
+                                 const float *lse, const uint16_t *dout, int64_t T_q,
+                                 int64_t T_kv, int32_t H, int32_t D_qk, int32_t D_v, int32_t K,
+                                 float scale, uint16_t *dq, float *dkv, float *target,
+                                 uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 size_t dsa_indexer_kl_bwd_workspace_size(int64_t T_q, int64_t T_kv, int32_t K,
                                          int64_t rows_per_pass);
 int dsa_indexer_kl_bwd(const uint16_t *q_idx, const uint16_t *k_idx, const float *w,

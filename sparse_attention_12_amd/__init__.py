@@ -86,6 +86,9 @@ def lib():
         L.dsa_indexer_kl_target.restype = C.c_int
         L.dsa_indexer_kl_target.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, vp,
                                              vp]
+        L.dsa_sparse_mla_bwd_kl_target.restype = C.c_int
+        L.dsa_sparse_mla_bwd_kl_target.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32,
+                                                    i32, i32, f32, vp, vp, vp, u32, vp, sz, vp]
         L.dsa_indexer_kl_bwd_workspace_size.restype = sz
         L.dsa_indexer_kl_bwd_workspace_size.argtypes = [i64, i64, i32, i64]
         L.dsa_indexer_kl_bwd.restype = C.c_int
@@ -363,7 +366,8 @@ def bwd_workspace_bytes(T_q: int, T_kv: int, H: int, D_qk: int, K: int,
 
 def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
                    topk_length=None, dkv=None, accumulate: bool = False, dq=None,
-                   check_indices: bool = False, workspace=None, sink=None, dsink=None):
+                   check_indices: bool = False, workspace=None, sink=None, dsink=None,
+                   kl_target=None):
     """dsa_sparse_mla_bwd -> (dq bf16 [T_q,H,D_qk], dkv fp32 [T_kv,D_qk]).
 
     With accumulate=True the gradients of the latent rows are added into `dkv`
@@ -371,7 +375,8 @@ def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
     tensor) sets how many query rows a pass stages (see bwd_workspace_bytes); by default one
     of DEFAULT_BWD_STAGE_BYTES is allocated.  With `sink` (fp32 [H]; out / lse then come from
     the sink forward) this is dsa_sparse_mla_bwd_sink and returns (dq, dkv, dsink fp32 [H]);
-    accumulate=True adds into `dsink` too."""
+    accumulate=True adds into `dsink` too.  With `kl_target` (fp32 [T_q, K]) this is
+    dsa_sparse_mla_bwd_kl_target, which also writes the indexer KL loss's target."""
     op = "sparse_mla_bwd"
     _require(op, q, kv, topk_indices, out, lse, dout, topk_length, dkv)
     kv2, idx, Tq, H, Dqk, Tkv, K = _attn_shapes(op, q, kv, topk_indices, topk_length)
@@ -395,6 +400,19 @@ def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
                                 dtype=torch.uint8, device=q.device)
     flags = (DSA_BWD_ACCUMULATE_DKV if accumulate else 0) | (
         DSA_DEBUG_CHECK_INDICES if check_indices else 0)
+    if kl_target is not None:
+        if sink is not None:
+            raise ValueError(f"{op}: kl_target with a sink is not supported in one call")
+        _require(op, q, kl_target)
+        _dtype(op, "kl_target", kl_target, torch.float32)
+        if kl_target.shape != (Tq, K):
+            raise ValueError(f"{op}: kl_target must be [T_q, K] fp32")
+        _call(lib().dsa_sparse_mla_bwd_kl_target, op, q.data_ptr(), kv2.data_ptr(),
+              idx.data_ptr(), _ptr(topk_length), out.data_ptr(), lse.data_ptr(),
+              dout.data_ptr(), Tq, Tkv, H, Dqk, d_v, K, float(softmax_scale), dq.data_ptr(),
+              dkv.data_ptr(), kl_target.data_ptr(), flags, workspace.data_ptr(),
+              workspace.numel(), _stream())
+        return dq, dkv
     if sink is None:
         _call(lib().dsa_sparse_mla_bwd, op, q.data_ptr(), kv2.data_ptr(), idx.data_ptr(),
               _ptr(topk_length), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), Tq, Tkv, H, Dqk,

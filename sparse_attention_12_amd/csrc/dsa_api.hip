@@ -481,7 +481,8 @@ static int bwd_run(const char *who, const uint16_t *q, const uint16_t *kv, const
                    const int32_t *topk_length, const uint16_t *out, const float *lse,
                    const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H, int32_t D_qk,
                    int32_t D_v, int32_t K, float scale, uint16_t *dq, float *dkv, uint32_t flags,
-                   void *ws, size_t ws_bytes, bool two_buffers, int small_code, void *stream) {
+                   void *ws, size_t ws_bytes, bool two_buffers, int small_code, void *stream,
+                   float *kl_target = nullptr) {
   if (int rc = check_attention_args(who, q, kv, idx, T_q, T_kv, H, D_qk, D_v, K, scale, 64))
     return rc;
   if (K > 4096) return fail(DSA_ERR_INVALID_VALUE, "%s: K=%d exceeds 4096", who, K);
@@ -551,7 +552,8 @@ static int bwd_run(const char *who, const uint16_t *q, const uint16_t *kv, const
     if (int rc = debug_check_indices(idx, topk_length, T_q, K, T_kv, w.flag, s)) return rc;
   hipError_t e = dsa::launch_sparse_mla_bwd(q, kv, idx, topk_length, out, lse, dout, T_q, T_kv,
                                             H, D_qk, K, scale, dq, dkv,
-                                            (flags & DSA_BWD_ACCUMULATE_DKV) != 0, w, s);
+                                            (flags & DSA_BWD_ACCUMULATE_DKV) != 0, w, s,
+                                            kl_target);
   if (e != hipSuccess) {
     char what[64];
     snprintf(what, sizeof what, "%s: launch", who);
@@ -659,6 +661,20 @@ int dsa_indexer_kl_bwd(const uint16_t *q_idx, const uint16_t *k_idx, const float
       dk_idx, (flags & DSA_BWD_ACCUMULATE_DKV) != 0, bb, R, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "indexer_kl_bwd: launch");
   return DSA_OK;
+}
+
+int dsa_sparse_mla_bwd_kl_target(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                                 const int32_t *topk_length, const uint16_t *out,
+                                 const float *lse, const uint16_t *dout, int64_t T_q,
+                                 int64_t T_kv, int32_t H, int32_t D_qk, int32_t D_v, int32_t K,
+                                 float scale, uint16_t *dq, float *dkv, float *target,
+                                 uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  if (T_q > 0 && !target)
+    return fail(DSA_ERR_INVALID_VALUE, "sparse_mla_bwd_kl_target: target is NULL");
+  return bwd_run("sparse_mla_bwd_kl_target", q, kv, idx, topk_length, out, lse, dout, T_q, T_kv,
+                 H, D_qk, D_v, K, scale, dq, dkv, flags, ws, ws_bytes, true, DSA_ERR_WORKSPACE,
+                 stream, target);
 }
 
 size_t dsa_sparse_mla_bwd_noalloc_scratch_bytes(void) { return dsa::kNoAllocScratchBytes; }

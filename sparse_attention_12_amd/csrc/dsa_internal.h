@@ -77,7 +77,8 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
                                  const float *lse, const uint16_t *dout, int64_t T_q,
                                  int64_t T_kv, int32_t H, int32_t D_qk, int32_t K, float scale,
                                  uint16_t *dq, float *dkv, bool accumulate,
-                                 const BwdWorkspace &ws, hipStream_t s);
+                                 const BwdWorkspace &ws, hipStream_t s,
+                                 float *kl_target = nullptr);
 
 // Counting sort of the (query, slot) pairs of query rows [row0, row0 + rows) by key row, and
 // the per-key-row sum of their staged contributions into dst [n_rows, D] (D = 128: the indexer

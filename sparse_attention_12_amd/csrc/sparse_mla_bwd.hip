@@ -424,7 +424,7 @@ __device__ __forceinline__ void bwd_contrib_row(
     const float *__restrict__ lse, const float *__restrict__ delta,
     const uint16_t *__restrict__ dout, const uint32_t *__restrict__ vmax, int H, int K,
     float scale, float scale_log2, uint32_t *__restrict__ stage, int32_t *__restrict__ cnt,
-    int64_t t, unsigned char *smem) {
+    float *__restrict__ target, int64_t t, unsigned char *smem) {
   using TL = Tile<DQK>;
   using SM = RowSmem<DQK>;
   constexpr int kNTq = DQK / 64;  // channel tiles per quarter (9 or 8)
@@ -564,6 +564,7 @@ __device__ __forceinline__ void bwd_contrib_row(
   } else {
     // ========================== contribution waves =========================
     const int qq = wave - 4;
+    float tgt_total = 0.0f;  // wave 0 of this role: the row's KL-target sum (lanes < 32)
     const int ch0 = qq * 16 * kNTq;
     // head-contraction fragments of the scaled fp16 q' and dO'
     u32x4 qh[2][kNTq], oh[2][kNTq];
@@ -602,6 +603,20 @@ __device__ __forceinline__ void bwd_contrib_row(
         const _Float16 *zs = stg + (cc & 1) * (SM::kCStageBytes / 2);
         const _Float16 *ps = zs + kSlots * kSS;
         const int32_t *rr = slot_rows + cc * kSlots;
+        if (target && qq == 0 && lane < kSlots) {
+          // KL-loss target: head sum of the staged P of slot cc*32 + lane (unnormalised here,
+          // renormalised over the row at the end; invalid slots hold P = 0)
+          const int j = cc * kSlots + lane;
+          float v = 0.0f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const f16x8 pv = as_f16x8(*reinterpret_cast<const u32x4 *>(&ps[lane * kSS + 8 * b]));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v += static_cast<float>(pv[e]);
+          }
+          if (j < K) target[t * K + j] = v;
+          tgt_total += v;
+        }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           f32x4 acc[kNTq];
@@ -656,6 +671,17 @@ __device__ __forceinline__ void bwd_contrib_row(
       if (c == nchunks) break;
     }
     lds_barrier();  // Z
+    if (target && qq == 0) {
+      // renormalise the row's target over its slots (each lane rereads what it wrote) and
+      // zero the slots past the last chunk
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) tgt_total += __shfl_xor(tgt_total, o, 64);
+      const float inv = tgt_total > 0.0f ? 1.0f / tgt_total : 0.0f;
+      float *trow = target + t * K;
+      if (lane < kSlots)
+        for (int j = lane; j < nchunks * kSlots && j < K; j += kSlots) trow[j] *= inv;
+      for (int j = nchunks * kSlots + lane; j < K; j += 64) trow[j] = 0.0f;
+    }
   }
 }
 
@@ -696,7 +722,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
     const uint16_t *__restrict__ out, const float *__restrict__ lse, float *__restrict__ delta,
     const uint16_t *__restrict__ dout, const uint32_t *__restrict__ vmax, int H, int K,
     float scale, float scale_log2, uint16_t *__restrict__ dq, uint32_t *__restrict__ stage,
-    int32_t *__restrict__ cnt, int64_t row0) {
+    int32_t *__restrict__ cnt, float *__restrict__ target, int64_t row0) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t i = blockIdx.x;
   const int64_t t = row0 + i;
@@ -704,7 +730,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void bwd_rows_kernel(
                   t, smem);
   __syncthreads();  // every wave is done with the dq phase's LDS; the row's Delta is stored
   bwd_contrib_row<DQK>(q, kv, idx, topk_length, lse, delta, dout, vmax, H, K, scale, scale_log2,
-                       stage + i * K * kStageWords<DQK>, cnt, t, smem);
+                       stage + i * K * kStageWords<DQK>, cnt, target, t, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -847,7 +873,7 @@ hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                        const int32_t *topk_length, const uint16_t *out, const float *lse,
                        float *delta, const uint16_t *dout, const uint32_t *vmax, int64_t row0,
                        int64_t rows, int32_t H, int32_t K, float scale, uint16_t *dq,
-                       const BwdPassBuffers &bb, hipStream_t s) {
+                       float *target, const BwdPassBuffers &bb, hipStream_t s) {
   const size_t smem = RowSmem<DQK>::bytes(K);
   auto kern = bwd_rows_kernel<DQK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -856,7 +882,7 @@ hipError_t launch_rows(const uint16_t *q, const uint16_t *kv, const int32_t *idx
   if (e != hipSuccess) return e;
   DSA_LAUNCH("sparse_mla_bwd_rows", kern, dim3(static_cast<unsigned>(rows)),
              dim3(kRowWaves * 64), smem, s, q, kv, idx, topk_length, out, lse, delta, dout, vmax,
-             H, K, scale, scale * kLog2e, dq, bb.stage, bb.off, row0);
+             H, K, scale, scale * kLog2e, dq, bb.stage, bb.off, target, row0);
   return hipGetLastError();
 }
 
@@ -929,8 +955,8 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
                          const int32_t *topk_length, const uint16_t *out, const float *lse,
                          float *delta,
                          const uint16_t *dout, int64_t T_q, int64_t T_kv, int32_t H, int32_t K,
-                         float scale, uint16_t *dq, float *dkv, const BwdWorkspace &ws,
-                         hipStream_t s) {
+                         float scale, uint16_t *dq, float *dkv, float *target,
+                         const BwdWorkspace &ws, hipStream_t s) {
   hipError_t e = hipSuccess;
   const int64_t R = ws.rows_per_pass;
   if (ws.nbuf == 1) {  // every pass in order on the caller's stream
@@ -939,7 +965,7 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
       e = launch_count_zero(T_kv, ws.buf[0], s);
       if (e == hipSuccess)
         e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, ws.vmax, r0, n, H,
-                             K, scale, dq, ws.buf[0], s);
+                             K, scale, dq, target, ws.buf[0], s);
       if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[0], s);
       if (e == hipSuccess) e = launch_reduce<DQK>(T_kv, ws.buf[0], dkv, s);
     }
@@ -962,7 +988,7 @@ hipError_t launch_passes(const uint16_t *q, const uint16_t *kv, const int32_t *i
     e = launch_count_zero(T_kv, ws.buf[b], s);
     if (e == hipSuccess)
       e = launch_rows<DQK>(q, kv, idx, topk_length, out, lse, delta, dout, ws.vmax, r0, n, H, K,
-                           scale, dq, ws.buf[b], s);
+                           scale, dq, target, ws.buf[b], s);
     if (e == hipSuccess) e = hipEventRecord(bs->rows_done[b], s);
     if (e == hipSuccess) e = hipStreamWaitEvent(bs->s2, bs->rows_done[b], 0);
     if (e == hipSuccess) e = launch_sort(idx, topk_length, r0, n, T_kv, K, ws.buf[b], bs->s2);
@@ -982,7 +1008,7 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
                                  const float *lse, const uint16_t *dout, int64_t T_q,
                                  int64_t T_kv, int32_t H, int32_t D_qk, int32_t K, float scale,
                                  uint16_t *dq, float *dkv, bool accumulate,
-                                 const BwdWorkspace &ws, hipStream_t s) {
+                                 const BwdWorkspace &ws, hipStream_t s, float *target) {
   if (!accumulate && T_kv > 0) {
     const int64_t n = T_kv * D_qk;
     const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
@@ -1003,10 +1029,10 @@ hipError_t launch_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const in
   if (e != hipSuccess) return e;
   if (D_qk == 576)
     return launch_passes<576>(q, kv, idx, topk_length, out, lse, ws.delta, dout, T_q, T_kv, H,
-                              K, scale, dq, dkv, ws, s);
+                              K, scale, dq, dkv, target, ws, s);
   if (D_qk == 512)
     return launch_passes<512>(q, kv, idx, topk_length, out, lse, ws.delta, dout, T_q, T_kv, H,
-                              K, scale, dq, dkv, ws, s);
+                              K, scale, dq, dkv, target, ws, s);
   return hipErrorInvalidValue;
 }
 

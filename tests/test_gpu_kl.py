@@ -171,3 +171,31 @@ def test_kl_empty_and_single_slot_rows():
     _compare(gpu, ref)
     assert gpu["loss"][3] == 0.0 and not gpu["target"][3].any() and not gpu["dq_idx"][3].any()
     assert gpu["target"][4, 5] == 1.0 and abs(gpu["loss"][4]) <= 1e-6
+
+
+@pytest.mark.parametrize("T,H,Dqk,K,n_valid,passes", [(200, 64, 576, 128, 77, 1),
+                                                       (130, 8, 512, 75, 70, 3)])
+def test_fused_target_from_the_attention_backward(T, H, Dqk, K, n_valid, passes):
+    """dsa_sparse_mla_bwd_kl_target: dq and dkv as the plain backward, and the KL target within
+    the target tolerance of the oracle (its P is staged in fp16: about 2^-12 per term)."""
+    dsa = _dsa()
+    q, kv, q_idx, k_idx, w, idx = _inputs(T, H, Dqk, K, n_valid, 8, seed=T + 3)
+    idx[5] = -1  # a row without a valid slot
+    scale = 1.0 / math.sqrt(Dqk)
+    qd, kvd, idd = q.to(dev), kv.to(dev), torch.from_numpy(idx).to(dev)
+    dout = torch.randn((T, H, 512), generator=torch.Generator().manual_seed(T)).to(
+        torch.bfloat16).to(dev)
+    out, lse = dsa.sparse_mla_fwd(qd, kvd, idd, scale)
+    ws = torch.empty(dsa.bwd_workspace_bytes(T, T, H, Dqk, K, rows_per_pass=-(-T // passes)),
+                     dtype=torch.uint8, device=dev)
+    dq0, dkv0 = dsa.sparse_mla_bwd(qd, kvd, idd, out, lse, dout, scale, workspace=ws)
+    tgt = torch.full((T, K), 5.0, dtype=torch.float32, device=dev)  # overwritten everywhere
+    dq1, dkv1 = dsa.sparse_mla_bwd(qd, kvd, idd, out, lse, dout, scale, workspace=ws,
+                                   kl_target=tgt)
+    torch.cuda.synchronize()
+    assert torch.equal(dq0, dq1)
+    assert (dkv0 - dkv1).abs().max().item() <= 1e-5 * dkv0.abs().max().item() + 1e-6
+    ref = oracle.indexer_kl(q, kv, idx, None, scale, q_idx, k_idx, w)
+    e = _check("fused target", _np(tgt), ref["target"], 1e-4)
+    assert not _np(tgt)[5].any()
+    print(f"fused target {e:.2e}", flush=True)
