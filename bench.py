@@ -111,6 +111,30 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+def measured_mfma(kernel: str, workload: str):
+    """Counter-based MFMA figures of `kernel` from the committed summary
+    profiles/<kernel>_<workload>_mfma.md (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
+    SQ_INSTS_VALU_MFMA_MOPS_*, SQ_INSTS_VALU / SQ_INSTS_MFMA), or None when there is none or
+    it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_mfma.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != source_digest(kernel):
+        return None
+    try:
+        return {"mfma_busy": float(fields["mfma_busy"]),
+                "mfma_flops_executed": float(fields["mfma_flops_executed"]),
+                "valu_per_mfma": float(fields["valu_per_mfma"])}
+    except (KeyError, ValueError):
+        return None
+
+
 class KernelTimer:
     """Arms dsa_record_kernel_events with a pool of HIP events (created through the HIP
     runtime that torch already loaded)."""
@@ -460,6 +484,11 @@ def main():
             comp[name] = {"ms": ms, "gbs": nbytes / ms / 1e6,
                           "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
     kernels = {n: {"avg_ms": sum(v) / len(v), "launches": len(v)} for n, v in per_kernel.items()}
+    # counter-based MFMA utilisation beside the algorithmic fractions (committed summaries)
+    for comp_name, kern in (("indexer", "indexer_topk"), ("fwd", "sparse_mla_fwd"),
+                            ("bwd", "sparse_mla_bwd_rows")):
+        if comp_name in comp:
+            comp[comp_name]["counters"] = measured_mfma(kern, cfg.name)
 
     # algorithmic work per launch of each hot kernel: MFMA flops, or HBM bytes for the
     # reduction of the staged key-gradient contributions (a staged row of 2 bytes per channel
