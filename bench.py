@@ -258,16 +258,48 @@ def cpu_baseline(inputs, counts, T, K, budget_s):
     n_f, (t_fwd, f_fwd, v_f) = sized(lambda n: attention(n, False), threads)
     n_b, (t_bwd, f_bwd, v_b) = sized(lambda n: attention(n, True), threads)
     idx_rate, fwd_rate, bwd_rate = f_idx / t_idx, f_fwd / t_fwd, f_bwd / t_bwd
-    full_s = counts["idx_flops"] / idx_rate + counts["fwd_flops"] / fwd_rate + \
-        counts["bwd_flops"] / bwd_rate
+
+    def step_seconds(ri, rf, rb):
+        return counts["idx_flops"] / ri + counts["fwd_flops"] / rf + counts["bwd_flops"] / rb
+
+    full_s = step_seconds(idx_rate, fwd_rate, bwd_rate)
+    # the same oracle on one thread (OpenMP's thread count set through libgomp for the calls
+    # below), on samples an eighth of the size
+    single = None
+    try:
+        gomp = C.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        try:
+            t1i, f1i = indexer(max(1, n_i // 8))
+            t1f, f1f, _ = attention(max(1, n_f // 8), False)
+            t1b, f1b, _ = attention(max(1, n_b // 8), True)
+        finally:
+            gomp.omp_set_num_threads(threads)
+        r1 = (f1i / t1i, f1f / t1f, f1b / t1b)
+        single = {"value": T / step_seconds(*r1), "indexer_tflops": r1[0] / 1e12,
+                  "fwd_tflops": r1[1] / 1e12, "bwd_tflops": r1[2] / 1e12,
+                  "seconds": t1i + t1f + t1b}
+    except OSError:
+        pass
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": T / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "cpu_model": cpu_model,
         "sample": (f"fp64 oracle on the last rows of the {max_rows}-token sequence: indexer "
                    f"top-k of {n_i} rows ({t_idx:.1f}s), forward of {n_f} rows / {v_f} valid "
                    f"slots ({t_fwd:.1f}s), backward of {n_b} rows / {v_b} valid slots "
-                   f"({t_bwd:.1f}s); per-stage flop rates extrapolated to the whole step"),
+                   f"({t_bwd:.1f}s); per-stage flop rates extrapolated to the whole step; "
+                   f"single_thread: the same on one thread, samples of an eighth"),
         "indexer_tflops": idx_rate / 1e12, "fwd_tflops": fwd_rate / 1e12,
-        "bwd_tflops": bwd_rate / 1e12,
+        "bwd_tflops": bwd_rate / 1e12, "single_thread": single,
     }
 
 

@@ -373,7 +373,10 @@ def sparse_mla_bwd(q, kv, topk_indices, out, lse, dout, softmax_scale: float,
     With accumulate=True the gradients of the latent rows are added into `dkv`
     (query-chunked execution); otherwise dkv is overwritten.  `workspace` (uint8 device
     tensor) sets how many query rows a pass stages (see bwd_workspace_bytes); by default one
-    of DEFAULT_BWD_STAGE_BYTES is allocated.  With `sink` (fp32 [H]; out / lse then come from
+    the workspace is sized to the call: one pass over every query row when its staging (about
+    T_q * K * (2 * D_qk + 20) bytes) fits DEFAULT_BWD_STAGE_BYTES, else passes over two
+    buffers that share that cap (allocated through torch's caching allocator, so repeated
+    calls of one shape reuse the memory).  With `sink` (fp32 [H]; out / lse then come from
     the sink forward) this is dsa_sparse_mla_bwd_sink and returns (dq, dkv, dsink fp32 [H]);
     accumulate=True adds into `dsink` too.  With `kl_target` (fp32 [T_q, K]) this is
     dsa_sparse_mla_bwd_kl_target, which also writes the indexer KL loss's target."""
