@@ -598,3 +598,74 @@ int oracle_indexer_kl(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
   }
   return err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* k-pool indexer ([PR2388] "Why": GLM-5.3-Flash's k-pool selection appends   */
+/* the query's incomplete tail pool, so the top-k width is 2048 + 3 = 2051).  */
+/* ------------------------------------------------------------------------ */
+
+/* The pool selection is not spelled out on the pages.  Reading taken: the
+ * keys of every sequence form pools of `pool` consecutive keys from the
+ * sequence start; the caller supplies one indexer key per complete pool
+ * (k_pool rows in sequence order, sequence b's pools from row cp[b] with
+ * cp[b] = sum over b' < b of floor(len_b' / pool)).  Query row t of sequence
+ * b sees the P = floor((t - cu[b] + 1) / pool) pools that end at or before t,
+ * scores pool i as I(t,i) = sum_h w[t,h] max(0, q[t,h] . k_pool[cp[b]+i]),
+ * keeps the n = min(K_pools, P) best (ties -> lower pool), and emits their
+ * keys in ascending order followed by the incomplete tail pool's keys
+ * cu[b] + pool P .. t (at most pool - 1 of them); the rest of the width
+ * W = K_pools pool + pool - 1 is -1 and len = pool n + (t - cu[b] + 1 - pool P).
+ * pool = 1 is the token-level indexer.  idx_out is [T x W], len_out [T]. */
+int oracle_kpool_indexer(const uint16_t *q, const uint16_t *k_pool, const float *w,
+                         const int32_t *cu, int32_t B, int64_t T, int32_t H, int32_t D,
+                         int32_t pool, int32_t K_pools, int32_t *idx_out, int32_t *len_out) {
+  if (B < 1 || H < 1 || D < 1 || pool < 1 || K_pools < 1) return ORACLE_EINVAL;
+  if (cu[0] != 0 || (int64_t)cu[B] != T) return ORACLE_EINVAL;
+  for (int32_t b = 0; b < B; ++b)
+    if (cu[b + 1] < cu[b]) return ORACLE_EINVAL;
+  const int64_t W = (int64_t)K_pools * pool + pool - 1;
+  int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t t = 0; t < T; ++t) {
+    int32_t b = 0;
+    int64_t cp = 0; /* first pool row of sequence b */
+    while (!(cu[b] <= t && t < cu[b + 1])) {
+      cp += (cu[b + 1] - cu[b]) / pool;
+      ++b;
+    }
+    const int64_t start = cu[b], pos = t - start;
+    const int64_t P = (pos + 1) / pool;
+    int32_t *row = idx_out + (size_t)t * W;
+    for (int64_t j = 0; j < W; ++j) row[j] = -1;
+    int64_t n = P < K_pools ? P : K_pools;
+    scored_key *pools = P > 0 ? (scored_key *)malloc(sizeof(scored_key) * (size_t)P) : NULL;
+    if (P > 0 && !pools) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+      continue;
+    }
+    for (int64_t i = 0; i < P; ++i) {
+      double total = 0.0;
+      for (int32_t h = 0; h < H; ++h) {
+        double dot = 0.0;
+        const uint16_t *qr = q + ((size_t)t * H + h) * D;
+        const uint16_t *kr = k_pool + (size_t)(cp + i) * D;
+        for (int32_t d = 0; d < D; ++d) dot += bf16_to_double(qr[d]) * bf16_to_double(kr[d]);
+        total += (double)w[(size_t)t * H + h] * (dot > 0.0 ? dot : 0.0);
+      }
+      pools[i].score = total + 0.0;
+      pools[i].pos = (int32_t)i;
+    }
+    if (P > 0) {
+      qsort(pools, (size_t)P, sizeof(scored_key), by_rank);
+      qsort(pools, (size_t)n, sizeof(scored_key), by_pos);
+    }
+    int64_t o = 0;
+    for (int64_t j = 0; j < n; ++j)
+      for (int32_t r = 0; r < pool; ++r) row[o++] = (int32_t)(start + (int64_t)pools[j].pos * pool + r);
+    for (int64_t s = start + P * pool; s <= t; ++s) row[o++] = (int32_t)s;
+    len_out[t] = (int32_t)o;
+    free(pools);
+  }
+  return err;
+}

@@ -639,3 +639,80 @@ def test_indexer_kl_chunks_and_head_permutation():
                                atol=1e-15)
     np.testing.assert_allclose(p["dw"], full["dw"][:, perm.numpy()], rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(p["dk_idx"], full["dk_idx"], rtol=1e-11, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# k-pool indexer
+# ----------------------------------------------------------------------------
+
+def _kpool_case(cu, pool, H, D, int_inputs, seed):
+    T = cu[-1]
+    n_pools = sum((cu[b + 1] - cu[b]) // pool for b in range(len(cu) - 1))
+    g = torch.Generator().manual_seed(seed)
+    if int_inputs:
+        q = torch.randint(-4, 5, (T, H, D), generator=g).to(torch.bfloat16)
+        kp = torch.randint(-4, 5, (n_pools, D), generator=g).to(torch.bfloat16)
+        w = torch.tensor([0.5, 1.0, 2.0])[torch.randint(0, 3, (T, H), generator=g)]
+    else:
+        q = torch.randn((T, H, D), generator=g).to(torch.bfloat16)
+        kp = torch.randn((n_pools, D), generator=g).to(torch.bfloat16)
+        w = torch.randn((T, H), generator=g) / 8
+    return q, kp, w
+
+
+def _kpool_brute(q, kp, w, cu, pool, K_pools):
+    """Pool scores by einsum, ranking by (score desc, pool asc), expansion to keys and the
+    incomplete tail pool, written from the reading with numpy."""
+    qd, kd = pins.bf16_to_f64(q), pins.bf16_to_f64(kp)
+    wd = w.numpy().astype(np.float64)
+    T = cu[-1]
+    W = K_pools * pool + pool - 1
+    idx = np.full((T, W), -1, np.int32)
+    ln = np.zeros(T, np.int32)
+    cp = 0
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        npool = (s1 - s0) // pool
+        scores = np.einsum("th,thp->tp", wd[s0:s1],
+                           np.maximum(np.einsum("thd,pd->thp", qd[s0:s1], kd[cp:cp + npool]), 0))
+        for t in range(s0, s1):
+            P = (t - s0 + 1) // pool
+            sc = scores[t - s0, :P]
+            order = np.lexsort((np.arange(P), -sc))[:min(K_pools, P)]
+            keys = [s0 + i * pool + r for i in np.sort(order) for r in range(pool)]
+            keys += list(range(s0 + P * pool, t + 1))
+            idx[t, :len(keys)] = keys
+            ln[t] = len(keys)
+        cp += npool
+    return idx, ln
+
+
+@pytest.mark.parametrize("int_inputs", [True, False])
+@pytest.mark.parametrize("cu,pool,K_pools", [([0, 97], 4, 8), ([0, 40, 41, 130, 203], 4, 5),
+                                             ([0, 64, 150], 3, 7)])
+def test_kpool_indexer_matches_brute_force(int_inputs, cu, pool, K_pools):
+    q, kp, w = _kpool_case(cu, pool, 4, 32, int_inputs, seed=cu[-1] + pool + K_pools)
+    idx, ln = oracle.kpool_indexer(q, kp, w, np.array(cu, np.int32), pool, K_pools)
+    bidx, bln = _kpool_brute(q, kp, w, cu, pool, K_pools)
+    np.testing.assert_array_equal(idx, bidx)
+    np.testing.assert_array_equal(ln, bln)
+    # structure: ascending, causal, len = pool min(K_pools, P) + tail
+    start = pins.segment_of(np.array(cu), cu[-1])
+    for t in range(cu[-1]):
+        pos = t - start[t]
+        P = (pos + 1) // pool
+        assert ln[t] == pool * min(K_pools, P) + (pos + 1 - pool * P)
+        v = idx[t, :ln[t]]
+        assert (np.diff(v) > 0).all() and (v >= start[t]).all() and (v <= t).all()
+        if P <= K_pools:  # every complete pool and the tail: the whole causal prefix
+            assert v.tolist() == list(range(start[t], t + 1))
+
+
+def test_kpool_indexer_with_unit_pools_is_the_token_indexer():
+    """pool = 1 with the token keys as pool keys: the token-level indexer's result."""
+    cu = [0, 50, 131]
+    q, k, w = _kpool_case(cu, 1, 4, 32, False, seed=77)
+    idx, ln = oracle.kpool_indexer(q, k, w, np.array(cu, np.int32), 1, 24)
+    ridx, rln, _ = oracle.indexer_topk(q, k, w, np.array(cu, np.int32), 24)
+    np.testing.assert_array_equal(idx, ridx)
+    np.testing.assert_array_equal(ln, rln)
