@@ -68,8 +68,8 @@ def lib():
                                         C.c_int64, C.c_int64, f64p, f64p, f64p, f64p, f64p]
         L.oracle_indexer_kl.restype = C.c_int
         L.oracle_kpool_indexer.argtypes = [u16p, u16p, f32p, i32p, C.c_int32, C.c_int64,
-                                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, i32p,
-                                           i32p]
+                                           C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                           C.c_int64, C.c_int64, i32p, i32p, C.c_void_p]
         L.oracle_kpool_indexer.restype = C.c_int
         _lib = L
     return _lib
@@ -296,9 +296,10 @@ def indexer_kl(q, kv, idx, topk_length, scale: float, q_idx, k_idx, w, g: float 
     return dict(target=target, loss=loss, dq_idx=dq_idx, dw=dw, dk_idx=dk_idx)
 
 
-def kpool_indexer(q_idx, k_pool, w, cu_seqlens, pool: int, K_pools: int):
-    """k-pool top-k of every row: (idx int32 [T, K_pools*pool + pool - 1], len int32 [T]);
-    k_pool holds one key per complete pool of each sequence, in sequence order."""
+def kpool_indexer(q_idx, k_pool, w, cu_seqlens, pool: int, K_pools: int, rows=None):
+    """k-pool top-k of rows [r0, r1) (default all): (idx int32 [n, K_pools*pool + pool - 1],
+    len int32 [n], kth f64 [n] the n-th best pool score); k_pool holds one key per complete
+    pool of each sequence, in sequence order."""
     q = _u16(q_idx)
     k = _u16(k_pool)
     wt = _np(w, np.float32)
@@ -308,9 +309,13 @@ def kpool_indexer(q_idx, k_pool, w, cu_seqlens, pool: int, K_pools: int):
     if k.shape[0] != n_pools:
         raise ValueError(f"kpool_indexer: k_pool must hold {n_pools} rows (one per complete pool)")
     W = K_pools * pool + pool - 1
-    idx = np.zeros((T, W), np.int32)
-    ln = np.zeros(T, np.int32)
+    r0, r1 = (0, T) if rows is None else rows
+    idx = np.zeros((r1 - r0, W), np.int32)
+    ln = np.zeros(r1 - r0, np.int32)
+    kth = np.zeros(r1 - r0, np.float64)
     _check(lib().oracle_kpool_indexer(q.reshape(-1), k.reshape(-1), wt.reshape(-1), cu,
-                                      cu.shape[0] - 1, T, H, D, pool, K_pools, idx, ln),
-           "kpool_indexer")
-    return idx, ln
+                                      cu.shape[0] - 1, T, H, D, pool, K_pools, r0, r1, idx, ln,
+                                      kth.ctypes.data), "kpool_indexer")
+    if rows is None:
+        return idx, ln
+    return idx, ln, kth

@@ -615,18 +615,23 @@ int oracle_indexer_kl(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
  * keys in ascending order followed by the incomplete tail pool's keys
  * cu[b] + pool P .. t (at most pool - 1 of them); the rest of the width
  * W = K_pools pool + pool - 1 is -1 and len = pool n + (t - cu[b] + 1 - pool P).
- * pool = 1 is the token-level indexer.  idx_out is [T x W], len_out [T]. */
+ * pool = 1 is the token-level indexer.  For query rows [row_begin, row_end)
+ * (row-relative outputs): idx_out [rows x W], len_out [rows], kth_score
+ * (nullable) the n-th best pool score of each row (0 without a pool). */
 int oracle_kpool_indexer(const uint16_t *q, const uint16_t *k_pool, const float *w,
                          const int32_t *cu, int32_t B, int64_t T, int32_t H, int32_t D,
-                         int32_t pool, int32_t K_pools, int32_t *idx_out, int32_t *len_out) {
-  if (B < 1 || H < 1 || D < 1 || pool < 1 || K_pools < 1) return ORACLE_EINVAL;
+                         int32_t pool, int32_t K_pools, int64_t row_begin, int64_t row_end,
+                         int32_t *idx_out, int32_t *len_out, double *kth_score) {
+  if (B < 1 || H < 1 || D < 1 || pool < 1 || K_pools < 1 || row_begin < 0 || row_end > T ||
+      row_begin > row_end)
+    return ORACLE_EINVAL;
   if (cu[0] != 0 || (int64_t)cu[B] != T) return ORACLE_EINVAL;
   for (int32_t b = 0; b < B; ++b)
     if (cu[b + 1] < cu[b]) return ORACLE_EINVAL;
   const int64_t W = (int64_t)K_pools * pool + pool - 1;
   int err = ORACLE_OK;
-#pragma omp parallel for schedule(dynamic, 4)
-  for (int64_t t = 0; t < T; ++t) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = row_begin; t < row_end; ++t) {
     int32_t b = 0;
     int64_t cp = 0; /* first pool row of sequence b */
     while (!(cu[b] <= t && t < cu[b + 1])) {
@@ -635,7 +640,7 @@ int oracle_kpool_indexer(const uint16_t *q, const uint16_t *k_pool, const float 
     }
     const int64_t start = cu[b], pos = t - start;
     const int64_t P = (pos + 1) / pool;
-    int32_t *row = idx_out + (size_t)t * W;
+    int32_t *row = idx_out + (size_t)(t - row_begin) * W;
     for (int64_t j = 0; j < W; ++j) row[j] = -1;
     int64_t n = P < K_pools ? P : K_pools;
     scored_key *pools = P > 0 ? (scored_key *)malloc(sizeof(scored_key) * (size_t)P) : NULL;
@@ -656,15 +661,17 @@ int oracle_kpool_indexer(const uint16_t *q, const uint16_t *k_pool, const float 
       pools[i].score = total + 0.0;
       pools[i].pos = (int32_t)i;
     }
+    if (kth_score) kth_score[t - row_begin] = 0.0;
     if (P > 0) {
       qsort(pools, (size_t)P, sizeof(scored_key), by_rank);
+      if (kth_score) kth_score[t - row_begin] = pools[n - 1].score;
       qsort(pools, (size_t)n, sizeof(scored_key), by_pos);
     }
     int64_t o = 0;
     for (int64_t j = 0; j < n; ++j)
       for (int32_t r = 0; r < pool; ++r) row[o++] = (int32_t)(start + (int64_t)pools[j].pos * pool + r);
     for (int64_t s = start + P * pool; s <= t; ++s) row[o++] = (int32_t)s;
-    len_out[t] = (int32_t)o;
+    len_out[t - row_begin] = (int32_t)o;
     free(pools);
   }
   return err;

@@ -706,6 +706,24 @@ def test_kpool_indexer_matches_brute_force(int_inputs, cu, pool, K_pools):
         assert (np.diff(v) > 0).all() and (v >= start[t]).all() and (v <= t).all()
         if P <= K_pools:  # every complete pool and the tail: the whole causal prefix
             assert v.tolist() == list(range(start[t], t + 1))
+    # a row range (as the full-size GPU checks call it) and its k-th pool scores
+    r0, r1 = cu[-1] // 3, cu[-1]
+    ridx, rln, kth = oracle.kpool_indexer(q, kp, w, np.array(cu, np.int32), pool, K_pools,
+                                          rows=(r0, r1))
+    np.testing.assert_array_equal(ridx, bidx[r0:r1])
+    np.testing.assert_array_equal(rln, bln[r0:r1])
+    qd, kd = pins.bf16_to_f64(q), pins.bf16_to_f64(kp)
+    cps = np.concatenate([[0], np.cumsum(np.diff(cu) // pool)])
+    for t in range(r0, r1):
+        b = int(np.searchsorted(cu, t, side="right") - 1)
+        P = (t - cu[b] + 1) // pool
+        if P == 0:
+            assert kth[t - r0] == 0.0
+            continue
+        sc = (w.numpy()[t][:, None].astype(np.float64) *
+              np.maximum(qd[t] @ kd[cps[b]:cps[b] + P].T, 0)).sum(0)
+        assert kth[t - r0] == pytest.approx(np.sort(sc)[::-1][min(K_pools, P) - 1], rel=1e-12,
+                                            abs=1e-12)
 
 
 def test_kpool_indexer_with_unit_pools_is_the_token_indexer():
