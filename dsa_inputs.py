@@ -120,6 +120,29 @@ def indexer_inputs(cfg: int, cu_seqlens=None, device="cpu", seed=None):
                 cu_seqlens=cu_seqlens_tensor(w, device), topk=w.topk)
 
 
+def kpool_indexer_inputs(cfg: int, cu_seqlens=None, device="cpu", seed=None, pool=4,
+                         heads=64, dim=128, int_inputs=False):
+    """k-pool indexer query [T,Hi,Di] bf16, one pooled indexer key per complete pool of each
+    sequence [T_pool,Di] bf16 (T_pool = sum of floor(length / pool)), weights [T,Hi] fp32.
+    Float inputs: q, k ~ N(0,1), weights ~ N(0,1)/8; integer inputs as workload 1."""
+    w = workload(cfg, cu_seqlens)
+    T = w.T
+    n_pools = sum((w.cu_seqlens[b + 1] - w.cu_seqlens[b]) // pool
+                  for b in range(len(w.cu_seqlens) - 1))
+    g = _gen((seed if seed is not None else SEED_BASE + cfg + 0x300), device)
+    if int_inputs:
+        q = torch.randint(-4, 5, (T, heads, dim), generator=g, device=device).to(torch.bfloat16)
+        k = torch.randint(-4, 5, (n_pools, dim), generator=g, device=device).to(torch.bfloat16)
+        choice = torch.randint(0, 3, (T, heads), generator=g, device=device)
+        wt = torch.tensor([0.5, 1.0, 2.0], device=device)[choice].to(torch.float32)
+    else:
+        q = torch.randn((T, heads, dim), generator=g, device=device).to(torch.bfloat16)
+        k = torch.randn((n_pools, dim), generator=g, device=device).to(torch.bfloat16)
+        wt = (torch.randn((T, heads), generator=g, device=device) / 8.0).to(torch.float32)
+    return dict(q_idx=q.contiguous(), k_pool=k.contiguous(), w=wt.contiguous(),
+                cu_seqlens=cu_seqlens_tensor(w, device), pool=pool)
+
+
 def attention_inputs(cfg: int, cu_seqlens=None, device="cpu", layer=0, seed=None,
                      heads=None, d_qk=None):
     """Absorbed query [T,H,Dqk], latent rows [T,Dqk], output grad [T,H,Dv] (bf16)."""

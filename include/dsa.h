@@ -95,6 +95,9 @@ typedef struct dsa_thd_metadata {
   int32_t *gpos;        /* [T]  key-tensor coordinate of each local query row  */
   int32_t *group_first; /* [n_groups] first row of each indexer work group     */
   int64_t total_key_tokens; /* rows of the key tensors (k_idx, kv)            */
+  /* k-pool rows (dsa_prepare_kpool_metadata); NULL / 0 otherwise                */
+  int32_t *key_start;   /* [T]  first token of the row's sequence               */
+  int32_t pool;         /* keys per pool                                        */
 } dsa_thd_metadata;
 
 /* Bytes of workspace the metadata for T tokens needs. */
@@ -134,6 +137,41 @@ int dsa_prepare_local_metadata(const int32_t *cu_seqlens, const int32_t *cu_seql
                                const int32_t *query_indices, const uint8_t *padding_mask,
                                int32_t B, int64_t T_q, int64_t T_k, int32_t K, void *ws,
                                size_t ws_bytes, dsa_thd_metadata *md, void *stream);
+
+/* --------------------------------------------------------------------------
+ * k-pool indexer (SkyRL PR 2388, "Why": GLM-5.3-Flash's k-pool selection
+ * appends the query's incomplete tail pool, so its top-k width is
+ * 2048 + 3 = 2051).  The pool selection is not spelled out on the page.
+ * Reading implemented: the keys of every sequence form pools of `pool`
+ * consecutive keys from the sequence start, and the caller supplies one
+ * indexer key per complete pool, k_pool [T_pool, D_i] bf16 with sequence b's
+ * pools from row cp[b] = sum over b' < b of floor(len_b' / pool).  Query row
+ * t of sequence b (position pos = t - cu[b]) sees the P = floor((pos + 1) /
+ * pool) pools ending at or before t, scores pool i as
+ *     I(t,i) = sum_h w[t,h] * max(0, q_idx[t,h] . k_pool[cp[b] + i])
+ * (as dsa_indexer_topk, ties to the lower pool), keeps the n = min(K_pools, P)
+ * best and writes their keys in ascending order, then the incomplete tail
+ * pool's keys cu[b] + pool P .. t (at most pool - 1); idx [T, W] with
+ * W = K_pools * pool + pool - 1, -1 after len = pool n + (pos + 1 - pool P).
+ *
+ * dsa_prepare_kpool_metadata: rows, pool coordinates and indexer work groups
+ * (rows that see the same pools) from cu_seqlens (device int32 [B+1]; one
+ * synchronisation to read it, one after the upload of the tables); fills md
+ * (md->total_key_tokens = T_pool, md->pool, md->key_start).  1 <= pool <= 16,
+ * 1 <= K_pools <= 2048.
+ * dsa_kpool_indexer_topk: q_idx [T, H_i, D_i], k_pool [T_pool, D_i], w [T, H_i]
+ * with that metadata (limits of dsa_indexer_topk) -> idx, len; workspace of
+ * dsa_kpool_indexer_topk_workspace_size(T, K_pools) bytes (the pool
+ * selection before it is expanded to keys).
+ * ------------------------------------------------------------------------ */
+size_t dsa_kpool_metadata_workspace_size(int64_t T);
+int dsa_prepare_kpool_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t pool,
+                               int32_t K_pools, void *ws, size_t ws_bytes, dsa_thd_metadata *md,
+                               void *stream);
+size_t dsa_kpool_indexer_topk_workspace_size(int64_t T, int32_t K_pools);
+int dsa_kpool_indexer_topk(const uint16_t *q_idx, const uint16_t *k_pool, const float *w,
+                           const dsa_thd_metadata *md, int32_t H_i, int32_t D_i, int32_t K_pools,
+                           int32_t *idx, int32_t *len, void *ws, size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
  * Lightning indexer + top-k (GLM-5.2 page, "How DSA works": the indexer

@@ -36,7 +36,8 @@ class _Metadata(C.Structure):
                 ("T", C.c_int64), ("B", C.c_int32), ("K", C.c_int32), ("max_seqlen", C.c_int32),
                 ("all_rows_nonempty", C.c_int32), ("total_pairs", C.c_int64),
                 ("total_valid", C.c_int64), ("n_groups", C.c_int32), ("gpos", C.c_void_p),
-                ("group_first", C.c_void_p), ("total_key_tokens", C.c_int64)]
+                ("group_first", C.c_void_p), ("total_key_tokens", C.c_int64),
+                ("key_start", C.c_void_p), ("pool", C.c_int32)]
 
 
 _lib = None
@@ -64,6 +65,16 @@ def lib():
         L.dsa_prepare_local_metadata.restype = C.c_int
         L.dsa_prepare_local_metadata.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp, sz,
                                                  C.POINTER(_Metadata), vp]
+        L.dsa_kpool_metadata_workspace_size.restype = sz
+        L.dsa_kpool_metadata_workspace_size.argtypes = [i64]
+        L.dsa_prepare_kpool_metadata.restype = C.c_int
+        L.dsa_prepare_kpool_metadata.argtypes = [vp, i32, i64, i32, i32, vp, sz,
+                                                 C.POINTER(_Metadata), vp]
+        L.dsa_kpool_indexer_topk_workspace_size.restype = sz
+        L.dsa_kpool_indexer_topk_workspace_size.argtypes = [i64, i32]
+        L.dsa_kpool_indexer_topk.restype = C.c_int
+        L.dsa_kpool_indexer_topk.argtypes = [vp, vp, vp, C.POINTER(_Metadata), i32, i32, i32, vp,
+                                             vp, vp, sz, vp]
         L.dsa_indexer_topk_workspace_size.restype = sz
         L.dsa_indexer_topk_workspace_size.argtypes = [i64, i32, i32, i32]
         L.dsa_indexer_topk.restype = C.c_int
@@ -291,6 +302,60 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     _call(lib().dsa_indexer_topk, op, q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr(),
           C.byref(meta._s), H, D, K, idx.data_ptr(), length.data_ptr(), ws.data_ptr(), ws_bytes,
           _stream())
+    return idx, length
+
+
+def prepare_kpool_metadata(cu_seqlens: torch.Tensor, pool: int = 4,
+                           K_pools: int = 512) -> ThdMetadata:
+    """dsa_prepare_kpool_metadata: k-pool rows of a packed batch (pools of `pool` keys from each
+    sequence start, one indexer key per complete pool); meta.total_key_tokens is the number
+    of pool keys the indexer reads."""
+    op = "prepare_kpool_metadata"
+    _require(op, cu_seqlens)
+    _dtype(op, "cu_seqlens", cu_seqlens, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError(f"{op}: cu_seqlens must be 1-D with at least 2 entries")
+    B = cu_seqlens.numel() - 1
+    T = int(cu_seqlens[-1].item())
+    ws_bytes = lib().dsa_kpool_metadata_workspace_size(T)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=cu_seqlens.device)
+    md = _Metadata()
+    _call(lib().dsa_prepare_kpool_metadata, op, cu_seqlens.data_ptr(), B, T, int(pool),
+          int(K_pools), ws.data_ptr(), ws_bytes, C.byref(md), _stream())
+    return ThdMetadata(md, ws, cu_seqlens)
+
+
+def kpool_indexer_topk(q_idx: torch.Tensor, k_pool: torch.Tensor, w: torch.Tensor,
+                       meta: ThdMetadata, K_pools: int = 512, idx=None, length=None):
+    """dsa_kpool_indexer_topk -> (idx int32 [T, K_pools*pool + pool - 1] ascending key
+    positions with a -1 suffix, len int32 [T])."""
+    op = "kpool_indexer_topk"
+    _require(op, q_idx, k_pool, w)
+    _dtype(op, "q_idx", q_idx, torch.bfloat16)
+    _dtype(op, "k_pool", k_pool, torch.bfloat16)
+    _dtype(op, "w", w, torch.float32)
+    if q_idx.dim() != 3 or k_pool.dim() != 2 or w.dim() != 2:
+        raise ValueError(f"{op}: expected q_idx [T,H,D], k_pool [T_pool,D], w [T,H]")
+    T, H, D = q_idx.shape
+    pool = meta._s.pool
+    if pool < 1:
+        raise ValueError(f"{op}: metadata is not from prepare_kpool_metadata")
+    if k_pool.shape != (meta.total_key_tokens, D) or w.shape != (T, H) or T != meta.T:
+        raise ValueError(f"{op}: shapes do not match the metadata (T={meta.T}, "
+                         f"{meta.total_key_tokens} pools)")
+    W = K_pools * pool + pool - 1
+    if idx is None:
+        idx = torch.empty((T, W), dtype=torch.int32, device=q_idx.device)
+    if length is None:
+        length = torch.empty((T,), dtype=torch.int32, device=q_idx.device)
+    _require(op, idx, length)
+    if idx.shape != (T, W) or length.shape != (T,):
+        raise ValueError(f"{op}: output shapes do not match")
+    ws_bytes = lib().dsa_kpool_indexer_topk_workspace_size(T, int(K_pools))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q_idx.device)
+    _call(lib().dsa_kpool_indexer_topk, op, q_idx.data_ptr(), k_pool.data_ptr(), w.data_ptr(),
+          C.byref(meta._s), H, D, int(K_pools), idx.data_ptr(), length.data_ptr(),
+          ws.data_ptr(), ws_bytes, _stream())
     return idx, length
 
 

@@ -175,6 +175,8 @@ int dsa_prepare_thd_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, in
   md->n_groups = ng;
   md->gpos = nullptr;
   md->group_first = nullptr;
+  md->key_start = nullptr;
+  md->pool = 0;
   md->total_key_tokens = T;
   e = dsa::launch_thd_metadata(cu_seqlens, B, T, K, md->seq_start, md->causal_len,
                                md->topk_length, md->row_order, groups, ng, s);
@@ -321,6 +323,8 @@ int dsa_prepare_local_metadata(const int32_t *cu_seqlens, const int32_t *cu_seql
   md->total_valid = valid;
   md->n_groups = static_cast<int32_t>(groups.size());
   md->total_key_tokens = T_k;
+  md->key_start = nullptr;
+  md->pool = 0;
   const std::pair<int32_t *, const std::vector<int32_t> *> up[] = {
       {md->seq_start, &start}, {md->causal_len, &clen}, {md->topk_length, &tlen},
       {md->row_order, &order}, {md->groups, &groups}, {md->group_first, &group_first},
@@ -334,6 +338,129 @@ int dsa_prepare_local_metadata(const int32_t *cu_seqlens, const int32_t *cu_seql
   e = hipStreamSynchronize(s);  // the host vectors are released on return
   if (e != hipSuccess) return hip_fail(e, "prepare_local_metadata: stream synchronize");
   return DSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// k-pool rows.  workspace: seq_start (pool coordinate of the sequence's first pool) |
+// causal_len (complete pools the row sees) | topk_length | row_order | groups | group_first |
+// gpos (pool coordinate of the row's last complete pool) | key_start (each 256-B aligned)
+size_t dsa_kpool_metadata_workspace_size(int64_t T) {
+  if (T < 0) return 0;
+  const size_t a = align_up(static_cast<size_t>(T) * sizeof(int32_t));
+  return 8 * a + 256;
+}
+
+int dsa_prepare_kpool_metadata(const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t pool,
+                               int32_t K_pools, void *ws, size_t ws_bytes, dsa_thd_metadata *md,
+                               void *stream) {
+  g_last_error.clear();
+  const char *who = "prepare_kpool_metadata";
+  if (!md) return fail(DSA_ERR_INVALID_VALUE, "%s: md is NULL", who);
+  if (B < 1) return fail(DSA_ERR_INVALID_VALUE, "%s: B=%d must be >= 1", who, B);
+  if (T < 0 || T > INT32_MAX - 4096)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: T=%lld out of range", who, static_cast<long long>(T));
+  if (pool < 1 || pool > 16) return fail(DSA_ERR_INVALID_VALUE, "%s: pool=%d not in [1, 16]", who, pool);
+  if (K_pools < 1 || K_pools > DSA_MAX_INDEXER_TOPK)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: K_pools=%d not in [1, %d]", who, K_pools,
+                DSA_MAX_INDEXER_TOPK);
+  if (!cu_seqlens) return fail(DSA_ERR_INVALID_VALUE, "%s: cu_seqlens is NULL", who);
+  const size_t need = dsa_kpool_metadata_workspace_size(T);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  if (int rc = check_device()) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> cu(static_cast<size_t>(B) + 1);
+  hipError_t e = hipMemcpyAsync(cu.data(), cu_seqlens, cu.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "prepare_kpool_metadata: copy of cu_seqlens");
+  if (cu[0] != 0 || static_cast<int64_t>(cu[B]) != T)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: cu_seqlens must run from 0 to T=%lld", who,
+                static_cast<long long>(T));
+  for (int32_t b = 0; b < B; ++b)
+    if (cu[b + 1] < cu[b]) return fail(DSA_ERR_INVALID_VALUE, "%s: offsets decrease at %d", who, b);
+  const size_t n = static_cast<size_t>(T);
+  std::vector<int32_t> start(n), clen(n), tlen(n), gp(n), kst(n);
+  std::vector<int32_t> glast, gfirst;
+  int64_t cp = 0, pairs = 0, valid = 0;
+  int32_t max_len = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t s0 = cu[b], s1 = cu[b + 1];
+    for (int32_t t = s0; t < s1; ++t) {
+      const int32_t P = (t - s0 + 1) / pool;
+      start[t] = static_cast<int32_t>(cp);
+      clen[t] = P;
+      tlen[t] = std::min(P, K_pools);
+      gp[t] = static_cast<int32_t>(cp) + P - 1;
+      kst[t] = s0;
+      pairs += P;
+      valid += tlen[t];
+      max_len = std::max(max_len, P);
+    }
+    // work groups: consecutive rows that see the same pools, at most kIdxRowsPerGroup each
+    for (int32_t t = s0; t < s1;) {
+      int32_t u = t;
+      while (u + 1 < s1 && clen[u + 1] == clen[t] && u + 1 - t < dsa::kIdxRowsPerGroup) ++u;
+      glast.push_back(u);
+      gfirst.push_back(t);
+      t = u + 1;
+    }
+    cp += (s1 - s0) / pool;
+  }
+  if (cp > INT32_MAX - 4096) return fail(DSA_ERR_INVALID_VALUE, "%s: too many pools", who);
+  std::vector<int32_t> gorder(glast.size());
+  for (size_t g = 0; g < gorder.size(); ++g) gorder[g] = static_cast<int32_t>(g);
+  std::stable_sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b2) {
+    return clen[glast[a]] > clen[glast[b2]];
+  });
+  std::vector<int32_t> groups(glast.size()), group_first(glast.size());
+  for (size_t g = 0; g < gorder.size(); ++g) {
+    groups[g] = glast[gorder[g]];
+    group_first[g] = gfirst[gorder[g]];
+  }
+  std::vector<int32_t> order(n);
+  for (size_t i = 0; i < n; ++i) order[i] = static_cast<int32_t>(i);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b2) { return clen[a] > clen[b2]; });
+  char *base = reinterpret_cast<char *>(align_up(reinterpret_cast<uintptr_t>(ws)));
+  const size_t a = align_up(n * sizeof(int32_t));
+  md->seq_start = reinterpret_cast<int32_t *>(base);
+  md->causal_len = reinterpret_cast<int32_t *>(base + a);
+  md->topk_length = reinterpret_cast<int32_t *>(base + 2 * a);
+  md->row_order = reinterpret_cast<int32_t *>(base + 3 * a);
+  md->groups = reinterpret_cast<int32_t *>(base + 4 * a);
+  md->group_first = reinterpret_cast<int32_t *>(base + 5 * a);
+  md->gpos = reinterpret_cast<int32_t *>(base + 6 * a);
+  md->key_start = reinterpret_cast<int32_t *>(base + 7 * a);
+  md->T = T;
+  md->B = B;
+  md->K = K_pools;
+  md->max_seqlen = max_len;
+  md->all_rows_nonempty = 1;
+  md->total_pairs = pairs;
+  md->total_valid = valid;
+  md->n_groups = static_cast<int32_t>(groups.size());
+  md->total_key_tokens = cp;
+  md->pool = pool;
+  const std::pair<int32_t *, const std::vector<int32_t> *> up[] = {
+      {md->seq_start, &start}, {md->causal_len, &clen}, {md->topk_length, &tlen},
+      {md->row_order, &order}, {md->groups, &groups}, {md->group_first, &group_first},
+      {md->gpos, &gp}, {md->key_start, &kst}};
+  for (const auto &u : up)
+    if (!u.second->empty()) {
+      e = hipMemcpyAsync(u.first, u.second->data(), u.second->size() * 4, hipMemcpyHostToDevice,
+                         s);
+      if (e != hipSuccess) return hip_fail(e, "prepare_kpool_metadata: upload");
+    }
+  e = hipStreamSynchronize(s);  // the host vectors are released on return
+  if (e != hipSuccess) return hip_fail(e, "prepare_kpool_metadata: stream synchronize");
+  return DSA_OK;
+}
+
+size_t dsa_kpool_indexer_topk_workspace_size(int64_t T, int32_t K_pools) {
+  if (T < 0 || K_pools < 1) return 0;
+  return align_up(static_cast<size_t>(T) * static_cast<size_t>(K_pools) * sizeof(int32_t)) +
+         align_up(static_cast<size_t>(T) * sizeof(int32_t)) + 256;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -353,6 +480,9 @@ int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *
   (void)ws_bytes;
   if (!md || (md->T > 0 && (!md->seq_start || !md->groups)))
     return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: metadata missing");
+  if (md->pool > 0)
+    return fail(DSA_ERR_INVALID_VALUE,
+                "indexer_topk: k-pool metadata; use dsa_kpool_indexer_topk");
   if (H_i < 1 || H_i > 64)
     return fail(DSA_ERR_INVALID_VALUE, "indexer_topk: H_i=%d not in [1, 64]", H_i);
   if (D_i != 64 && D_i != 128)
@@ -382,6 +512,52 @@ int dsa_indexer_topk(const uint16_t *q_idx, const uint16_t *k_idx, const float *
   hipError_t e = dsa::launch_indexer_topk(q_idx, k_idx, w, rows, H_i, D_i, K, idx, len,
                                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "indexer_topk: launch");
+  return DSA_OK;
+}
+
+int dsa_kpool_indexer_topk(const uint16_t *q_idx, const uint16_t *k_pool, const float *w,
+                           const dsa_thd_metadata *md, int32_t H_i, int32_t D_i, int32_t K_pools,
+                           int32_t *idx, int32_t *len, void *ws, size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  const char *who = "kpool_indexer_topk";
+  if (!md || md->pool < 1 || (md->T > 0 && (!md->seq_start || !md->groups || !md->key_start)))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: k-pool metadata missing", who);
+  if (K_pools != md->K)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: K_pools=%d differs from the metadata's %d", who,
+                K_pools, md->K);
+  if (H_i < 1 || H_i > 64) return fail(DSA_ERR_INVALID_VALUE, "%s: H_i=%d not in [1, 64]", who, H_i);
+  if (D_i != 64 && D_i != 128)
+    return fail(DSA_ERR_INVALID_VALUE, "%s: D_i=%d must be 64 or 128", who, D_i);
+  const int64_t T = md->T;
+  if (T == 0) return DSA_OK;
+  const size_t need = dsa_kpool_indexer_topk_workspace_size(T, K_pools);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  if (!q_idx || !w || !idx || !len || (md->total_key_tokens > 0 && !k_pool))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: NULL tensor pointer", who);
+  if (!aligned16(q_idx) || !aligned16(k_pool))
+    return fail(DSA_ERR_INVALID_VALUE, "%s: q_idx/k_pool must be 16-byte aligned", who);
+  if (int rc = check_device()) return rc;
+  char *p = reinterpret_cast<char *>(align_up(reinterpret_cast<uintptr_t>(ws)));
+  int32_t *pidx = reinterpret_cast<int32_t *>(p);
+  int32_t *plen = reinterpret_cast<int32_t *>(
+      p + align_up(static_cast<size_t>(T) * static_cast<size_t>(K_pools) * sizeof(int32_t)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dsa::IndexerRows rows;
+  rows.seq_start = md->seq_start;
+  rows.causal_len = md->causal_len;
+  rows.gpos = md->gpos;
+  rows.groups = md->groups;
+  rows.group_first = md->group_first;
+  rows.n_groups = md->n_groups;
+  // rows without a complete pool get len 0 from the indexer without reading k_pool
+  hipError_t e = dsa::launch_indexer_topk(q_idx, k_pool, w, rows, H_i, D_i, K_pools, pidx, plen,
+                                          s);
+  if (e == hipSuccess)
+    e = dsa::launch_kpool_expand(pidx, plen, md->seq_start, md->causal_len, md->key_start, T,
+                                 K_pools, md->pool, idx, len, s);
+  if (e != hipSuccess) return hip_fail(e, "kpool_indexer_topk: launch");
   return DSA_OK;
 }
 

@@ -44,6 +44,13 @@ hipError_t launch_indexer_topk(const uint16_t *q, const uint16_t *k, const float
                                const IndexerRows &r, int32_t H, int32_t D, int32_t K,
                                int32_t *idx, int32_t *len, hipStream_t s);
 
+// k-pool rows: pool selection (pidx [T, Kp] pool coordinates, plen [T]) -> key indices
+// idx [T, Kp * pool + pool - 1] and lengths, appending each row's incomplete tail pool.
+hipError_t launch_kpool_expand(const int32_t *pidx, const int32_t *plen,
+                               const int32_t *pool_start, const int32_t *n_pools,
+                               const int32_t *key_start, int64_t T, int32_t Kp, int32_t pool,
+                               int32_t *idx, int32_t *len, hipStream_t s);
+
 hipError_t launch_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                                  const int32_t *topk_length, int64_t T_q, int32_t H,
                                  int32_t D_qk, int32_t K, float scale, uint16_t *out, float *lse,

@@ -629,7 +629,9 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   const int lastg = gpos ? gpos[last] : last;  // key position of the group's last row
   const int t = first + row;                   // this wave's local row
   const bool row_ok = t <= last;
-  const int tg = lastg - (last - t);           // its key position (rows of a group are consecutive)
+  // its key position: a row's own coordinate (the rows of a group may share one, as k-pool
+  // rows that see the same pools do; the group's last row has the largest)
+  const int tg = gpos ? (row_ok ? gpos[t] : lastg) : t;
   const int L = row_ok ? causal_len[t] : 0;    // 0 for a padding row
   const bool compute = row_ok && L > K;
 
@@ -948,6 +950,45 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const float *w, const In
 }
 
 }  // namespace
+
+// k-pool rows: the selected pools (pool coordinates, ascending) -> their keys, then the row's
+// incomplete tail pool; one wave per row.
+__global__ __launch_bounds__(256) void kpool_expand_kernel(
+    const int32_t *__restrict__ pidx, const int32_t *__restrict__ plen,
+    const int32_t *__restrict__ pool_start, const int32_t *__restrict__ n_pools,
+    const int32_t *__restrict__ key_start, int64_t T, int Kp, int pool,
+    int32_t *__restrict__ idx, int32_t *__restrict__ len) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const int W = Kp * pool + pool - 1;
+  const int n = plen[t];
+  const int ps = pool_start[t], ks = key_start[t];
+  const int P = n_pools[t];
+  const int tail = static_cast<int>(t - ks) + 1 - P * pool;  // keys after the last complete pool
+  const int32_t *prow = pidx + t * Kp;
+  int32_t *row = idx + t * W;
+  for (int j = lane; j < W; j += 64) {
+    int32_t v = -1;
+    if (j < n * pool) {
+      v = ks + (prow[j / pool] - ps) * pool + j % pool;
+    } else if (j < n * pool + tail) {
+      v = ks + P * pool + (j - n * pool);
+    }
+    row[j] = v;
+  }
+  if (lane == 0) len[t] = n * pool + tail;
+}
+
+hipError_t launch_kpool_expand(const int32_t *pidx, const int32_t *plen,
+                               const int32_t *pool_start, const int32_t *n_pools,
+                               const int32_t *key_start, int64_t T, int32_t Kp, int32_t pool,
+                               int32_t *idx, int32_t *len, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  DSA_LAUNCH("kpool_expand", kpool_expand_kernel, dim3(static_cast<unsigned>((T + 3) / 4)),
+             dim3(256), 0, s, pidx, plen, pool_start, n_pools, key_start, T, Kp, pool, idx, len);
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer_topk(const uint16_t *q, const uint16_t *k, const float *w,
                                const IndexerRows &r, int32_t H, int32_t D, int32_t K,
