@@ -64,6 +64,9 @@ def parse():
                     help="add the indexer's KL training loss to the step: the score recompute "
                          "of the attention target and the indexer backward (coefficient 0.001 "
                          "over the rows)")
+    ap.add_argument("--synthetic-indices", action="store_true",
+                    help="k-pool workload: feed the attention seeded random causal indices "
+                         "instead of running the k-pool indexer in the step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy a device buffer of BYTES bytes once with "
                          "an elementwise kernel (x * 1): a plain copy of known size, which "
@@ -183,6 +186,17 @@ def ms_step_events(step_ev):
     return sum(step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(n)) / n
 
 
+def kpool_pairs(cu_seqlens, pool, K_pools):
+    """Pool scores of a k-pool indexer pass: every complete pool a row sees, for the rows that
+    see more than K_pools of them (the others keep all their pools without scoring)."""
+    import numpy as np
+    pairs = 0
+    for L in np.diff(np.array(cu_seqlens, np.int64)):
+        P = (np.arange(L) + 1) // pool
+        pairs += int(P[P > K_pools].sum())
+    return pairs
+
+
 def workload_counts(md_host, cfg, H_i, D_i, K, H, Dqk, Dv, kpool=None):
     """Algorithmic work of one step (see the module docstring of the pass)."""
     import numpy as np
@@ -191,9 +205,12 @@ def workload_counts(md_host, cfg, H_i, D_i, K, H, Dqk, Dv, kpool=None):
     # indexer: rows with L > K need every causal score; rows with L <= K are decided
     # without scoring (they keep their whole prefix)
     idx_pairs = 0
-    for L in lens:
-        if L > K:
-            idx_pairs += (L * (L + 1) // 2) - (K * (K + 1) // 2)
+    if cfg.pool > 0:
+        idx_pairs = kpool_pairs(cfg.cu_seqlens, cfg.pool, (K - cfg.pool + 1) // cfg.pool)
+    else:
+        for L in lens:
+            if L > K:
+                idx_pairs += (L * (L + 1) // 2) - (K * (K + 1) // 2)
     valid = md_host["total_valid"] if kpool is None else kpool
     return dict(
         idx_pairs=int(idx_pairs),
@@ -206,7 +223,7 @@ def workload_counts(md_host, cfg, H_i, D_i, K, H, Dqk, Dv, kpool=None):
     )
 
 
-def cpu_baseline(inputs, counts, T, K, budget_s):
+def cpu_baseline(inputs, counts, T, K, budget_s, pool=0):
     """Time the oracle (as it stands) on a bounded sample of the same workload: the longest
     rows of the last sequence, sized from a small calibration run so that the three stages
     take about budget_s seconds together; per-stage flop rates extrapolate to the whole step."""
@@ -216,7 +233,7 @@ def cpu_baseline(inputs, counts, T, K, budget_s):
 
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     q_idx = inputs["q_idx"].cpu()
-    k_idx = inputs["k_idx"].cpu()
+    k_idx = (inputs["k_pool"] if pool else inputs["k_idx"]).cpu()
     w = inputs["w"].cpu()
     cu = inputs["cu_seqlens"].cpu()
     last = int(cu[-1]) - 1
@@ -231,9 +248,16 @@ def cpu_baseline(inputs, counts, T, K, budget_s):
     def indexer(n):
         r0 = last - n + 1
         t0 = time.perf_counter()
-        oracle.indexer_topk(q_idx, k_idx, w, cu, K, rows=(r0, last + 1))
+        if pool:
+            oracle.kpool_indexer(q_idx, k_idx, w, cu, pool, (K - pool + 1) // pool,
+                                 rows=(r0, last + 1))
+        else:
+            oracle.indexer_topk(q_idx, k_idx, w, cu, K, rows=(r0, last + 1))
         dt = time.perf_counter() - t0
-        keys = sum(t - start + 1 for t in range(r0, last + 1))
+        if pool:
+            keys = sum((t - start + 1) // pool for t in range(r0, last + 1))
+        else:
+            keys = sum(t - start + 1 for t in range(r0, last + 1))
         return dt, keys * 2.0 * Hi * Di
 
     def attention(n, backward):
@@ -293,7 +317,8 @@ def cpu_baseline(inputs, counts, T, K, budget_s):
     return {
         "value": T / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "cpu_model": cpu_model,
-        "sample": (f"fp64 oracle on the last rows of the {max_rows}-token sequence: indexer "
+        "sample": (f"fp64 oracle on the last rows of the {max_rows}-token sequence: "
+                   f"{'k-pool ' if pool else ''}indexer "
                    f"top-k of {n_i} rows ({t_idx:.1f}s), forward of {n_f} rows / {v_f} valid "
                    f"slots ({t_fwd:.1f}s), backward of {n_b} rows / {v_b} valid slots "
                    f"({t_bwd:.1f}s); per-stage flop rates extrapolated to the whole step; "
@@ -321,8 +346,15 @@ def main():
     torch.manual_seed(0)
     cu = gen.cu_seqlens_tensor(cfg, dev)
     has_indexer = cfg.idx_heads is not None
+    # the k-pool indexer: pools of cfg.pool keys, the K_pools best plus the tail pool (width K)
+    kpool = cfg.pool > 0 and not args.synthetic_indices
+    has_indexer = has_indexer and not args.synthetic_indices
+    K_pools = (K - cfg.pool + 1) // cfg.pool if cfg.pool > 0 else 0
     inputs = dict(cu_seqlens=cu, scale=cfg.scale)
-    if has_indexer:
+    if kpool:
+        inputs.update(gen.kpool_indexer_inputs(args.config, device=dev, heads=cfg.idx_heads,
+                                               dim=cfg.idx_dim))
+    elif has_indexer:
         inputs.update(gen.indexer_inputs(args.config, device=dev))
     att = gen.attention_inputs(args.config, device=dev)
     n_layers = args.layers if args.layers > 0 else cfg.layers
@@ -332,7 +364,7 @@ def main():
     T_keys = T
     local_rows = None
     if args.cp > 1:
-        if not has_indexer:
+        if not has_indexer or kpool:
             raise SystemExit("--cp needs a workload with an indexer stage")
         # rank 0's rows under zig-zag context parallelism
         parts = []
@@ -367,7 +399,7 @@ def main():
     sink = gen.sink_logits(H, device=dev) if args.sink else None
     dsink_buf = torch.empty((H,), dtype=torch.float32, device=dev) if args.sink else None
     kpool_valid = None
-    if not has_indexer:
+    if not has_indexer and cfg.pool > 0:
         kp = gen.kpool_indices(T, topk=K, tail=cfg.kpool_tail, device=dev)
         idx_buf.copy_(kp)
         len_buf.copy_((kp >= 0).sum(1).to(torch.int32))
@@ -375,7 +407,7 @@ def main():
         del kp
 
     kl = args.indexer_loss
-    if kl and not has_indexer:
+    if kl and (not has_indexer or kpool):
         raise SystemExit("--indexer-loss needs a workload with an indexer stage")
     if kl and args.sink:
         raise SystemExit("--indexer-loss and --sink are measured separately")
@@ -389,13 +421,17 @@ def main():
     kl_events = []   # (start, stop) around the indexer loss while timing
 
     def step():
-        if local_rows is None:
-            # the metadata's top-k width is an indexer width (at most 2048); a workload without
-            # an indexer (k-pool indices, width 2051) takes its lengths from its indices
+        if kpool:
+            md = dsa.prepare_kpool_metadata(cu, cfg.pool, K_pools)
+            dsa.kpool_indexer_topk(inputs["q_idx"], inputs["k_pool"], inputs["w"], md, K_pools,
+                                   idx=idx_buf, length=len_buf)
+        elif local_rows is None:
+            # the metadata's top-k width is an indexer width (at most 2048); synthetic k-pool
+            # indices (width 2051) carry their own lengths
             md = dsa.prepare_thd_metadata(cu, min(K, dsa.MAX_INDEXER_TOPK), T=T)
         else:
             md = dsa.prepare_local_metadata(cu, T_keys, K, query_indices=local_rows)
-        if has_indexer:
+        if has_indexer and not kpool:
             dsa.indexer_topk(inputs["q_idx"], inputs["k_idx"], inputs["w"], md, K, idx=idx_buf,
                              length=len_buf)
         for li, a in enumerate([att] + extra_layers):  # the layers reuse the indexer's indices
@@ -432,8 +468,10 @@ def main():
         md = step()
     torch.cuda.synchronize()
     md_host = dict(total_valid=md.total_valid)
-    counts = workload_counts(md_host, cfg, cfg.idx_heads or 0, cfg.idx_dim or 0, K, H, Dqk, Dv,
-                             kpool_valid)
+    if kpool:
+        kpool_valid = int(len_buf.sum().item())  # key slots the attention reads
+    counts = workload_counts(md_host, cfg, cfg.idx_heads if has_indexer else 0,
+                             cfg.idx_dim if has_indexer else 0, K, H, Dqk, Dv, kpool_valid)
     if local_rows is not None:
         # scored pairs of the local rows: every causal key of a row with L > K
         L_rows = md.causal_len.to(torch.int64)
@@ -479,6 +517,8 @@ def main():
         return sum(v) / len(v) if v else float("nan")
 
     t_idx = avg("indexer_topk")
+    if kpool:  # the expansion of the selected pools to their keys belongs to the indexer
+        t_idx += avg("kpool_expand")
     t_fwd = avg("sparse_mla_fwd")
     # the backward's own wall time (its passes overlap on two streams, so kernel times overlap)
     t_bwd = sum(a.elapsed_time(b) for a, b in bwd_events) / len(bwd_events)
@@ -555,7 +595,9 @@ def main():
         "cold_ms_per_step": cold_ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "cu_seqlens": list(cfg.cu_seqlens),
-                   "indexer": (f"{cfg.idx_heads}x{cfg.idx_dim}" if has_indexer else None),
+                   "indexer": ((f"{cfg.idx_heads}x{cfg.idx_dim}"
+                                + (f", pools of {cfg.pool}, {K_pools} best + tail pool"
+                                   if kpool else "")) if has_indexer else None),
                    "topk": K, "heads": H, "d_qk": Dqk, "d_v": Dv, "bwd_passes": args.bwd_passes,
                    "attention_sink": bool(args.sink), "attention_layers": n_layers,
                    "indexer_loss": bool(kl),
@@ -567,7 +609,8 @@ def main():
     if not args.no_cpu_baseline and local_rows is None:
         inputs.update(idx=idx_buf, len=len_buf)
         try:
-            res["cpu_baseline"] = cpu_baseline(inputs, counts, T, K, args.cpu_seconds)
+            res["cpu_baseline"] = cpu_baseline(inputs, counts, T, K, args.cpu_seconds,
+                                               pool=cfg.pool if kpool else 0)
         except Exception as e:  # the GPU figure stands on its own
             res["cpu_baseline"] = {"error": repr(e)}
     print(json.dumps(res))

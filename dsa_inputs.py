@@ -13,8 +13,10 @@ Shapes and value distributions follow the five workloads of the DSA hot path:
      (64 heads x 128), top-k 2048, forward only;
   3  packed THD batch of 32768 tokens in four sequences (1024, 3072, 12288,
      16384), forward and backward;
-  4  GLM-5.3-Flash NoPE shard: T=65536, H=8, q/k width 512, top-k width 2051
-     built from a random causal subset plus the three most recent tokens;
+  4  GLM-5.3-Flash NoPE shard: T=65536, H=8, q/k width 512, top-k width 2051;
+     its indices come from the k-pool indexer (64 heads x 128 over pools of 4
+     keys, the 512 best pools plus the tail pool), or for attention-only cases
+     from a random causal subset plus the three most recent tokens;
   5  IndexShare block: T=131072, indexer once, four attention layers.
 
 The indexer shape (64 heads of width 128, k=2048) is the one the Megatron
@@ -54,6 +56,7 @@ class Workload:
     backward: bool
     layers: int = 1
     kpool_tail: int = 0          # >0: synthetic k-pool indices (random subset + tail)
+    pool: int = 0                # >0: the indexer selects pools of this many keys (k-pool)
     notes: str = field(default="")
 
     @property
@@ -70,8 +73,8 @@ WORKLOADS = {
     2: Workload("v32-T8192", (0, 8192), 64, 128, 2048, False, 64, 576, 512, 0.5, False),
     3: Workload("thd-T32768", (0, 1024, 4096, 16384, 32768), 64, 128, 2048, False,
                 64, 576, 512, 0.5, True),
-    4: Workload("nope-kpool-T65536", (0, 65536), None, None, 2051, False, 8, 512, 512, 0.5,
-                True, kpool_tail=3),
+    4: Workload("nope-kpool-T65536", (0, 65536), 64, 128, 2051, False, 8, 512, 512, 0.5,
+                True, kpool_tail=3, pool=4),
     5: Workload("indexshare-T131072", (0, 131072), 64, 128, 2048, False, 64, 576, 512, 0.5,
                 True, layers=4),
 }
@@ -104,7 +107,7 @@ def indexer_inputs(cfg: int, cu_seqlens=None, device="cpu", seed=None):
     1/sqrt(heads) and 1/sqrt(dim) factors).
     """
     w = workload(cfg, cu_seqlens)
-    assert w.idx_heads is not None, "workload has no indexer stage"
+    assert w.idx_heads is not None and w.pool == 0, "workload has no token-level indexer"
     T, Hi, Di = w.T, w.idx_heads, w.idx_dim
     g = _gen((seed if seed is not None else SEED_BASE + cfg), device)
     if w.idx_int_inputs:
@@ -120,13 +123,15 @@ def indexer_inputs(cfg: int, cu_seqlens=None, device="cpu", seed=None):
                 cu_seqlens=cu_seqlens_tensor(w, device), topk=w.topk)
 
 
-def kpool_indexer_inputs(cfg: int, cu_seqlens=None, device="cpu", seed=None, pool=4,
+def kpool_indexer_inputs(cfg: int, cu_seqlens=None, device="cpu", seed=None, pool=None,
                          heads=64, dim=128, int_inputs=False):
     """k-pool indexer query [T,Hi,Di] bf16, one pooled indexer key per complete pool of each
     sequence [T_pool,Di] bf16 (T_pool = sum of floor(length / pool)), weights [T,Hi] fp32.
     Float inputs: q, k ~ N(0,1), weights ~ N(0,1)/8; integer inputs as workload 1."""
     w = workload(cfg, cu_seqlens)
     T = w.T
+    if pool is None:
+        pool = w.pool if w.pool > 0 else 4
     n_pools = sum((w.cu_seqlens[b + 1] - w.cu_seqlens[b]) // pool
                   for b in range(len(w.cu_seqlens) - 1))
     g = _gen((seed if seed is not None else SEED_BASE + cfg + 0x300), device)
