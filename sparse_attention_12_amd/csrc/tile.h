@@ -7,7 +7,8 @@
 // chunks inside each row without any register traffic:
 //     physical chunk = logical chunk ^ swz(row)
 // swz keeps a chunk inside its aligned group of 8 (576-wide rows) or 16 (512-wide rows) and
-// spreads the rows read by one MFMA fragment, row-wise or transposed, over distinct LDS banks.
+// spreads the rows read by one MFMA fragment, row-wise or transposed, over the LDS banks
+// without conflicts.
 //
 // Slots whose index is -1 (or beyond the valid prefix) are filled from latent row 0 so that no
 // load is out of bounds; the kernels mask those slots (probability 0) so the values never
@@ -144,16 +145,17 @@ struct Tile {
   static constexpr int kBytes = kSlots * kRowBytes;
   static constexpr int kLoads = kSlots * kChunks / 64;  // wave-wide DMA instructions per tile
 
-  // Chunk XOR of a row.  Two read patterns must be free of LDS bank conflicts (64 banks of 4
-  // bytes = 16 chunk slots): 16-byte reads of one logical chunk from 16 consecutive rows (MFMA
-  // fragments of rows), and the transposing 8-byte reads of two adjacent chunks from 8
-  // consecutive rows (fragments of columns).  A 576-wide row is 1152 bytes, so odd rows start
-  // 8 chunk slots over: the 3-bit swz must be distinct over the rows of each parity within 16
-  // rows, and swz / 2 distinct (with the parity) within 8 rows.  512-wide rows all start on the
-  // same bank: the 4-bit swz must be distinct within 16 rows, and swz / 2 within 8 rows.
+  // Chunk XOR of a row.  Two read patterns must be free of LDS bank conflicts: 16-byte reads
+  // of one logical chunk from 16 consecutive rows, four adjacent chunks across the four lane
+  // groups (MFMA fragments of rows), and the transposing 8-byte reads of two adjacent chunks
+  // from 4 consecutive rows in each lane group (fragments of columns).  The XOR stays inside
+  // the chunk's aligned group of 8 (576-wide rows) or 16 (512-wide rows).  Chosen by
+  // measurement on gfx950 (SQ_LDS_BANK_CONFLICT over repeated reads of each pattern): row & 7
+  // (576) and (row & 7) << 1 (512) leave both patterns without conflicts, while a swizzle built
+  // for 64 four-byte banks served by 16 consecutive lanes stalled half of the row-fragment
+  // reads' LDS cycles.
   __device__ static __forceinline__ int swz(int row) {
-    return DQK == 576 ? ((((row >> 1) & 3) << 1) | ((row >> 3) & 1))
-                      : (((row & 7) << 1) | ((row >> 3) & 1));
+    return DQK == 576 ? (row & 7) : ((row & 7) << 1);
   }
   // byte offset of logical (row, chunk)
   __device__ static __forceinline__ int chunk_off(int row, int chunk) {
