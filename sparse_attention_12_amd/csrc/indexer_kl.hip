@@ -12,7 +12,7 @@
 //   dw[t,h] = sum_j dI max(0, d),  dq_idx[t,h] = sum_j dI w [d > 0] k_idx[s_j],
 //   dk_idx[s] += sum_(t,j: s_j = s) sum_h dI w [d > 0] q_idx[t,h]      (d = q_idx[t,h] . k_idx[s_j]).
 //
-// Kernels (one work group of four waves per query row, wave G holding heads 16 G .. + 15):
+// Kernels (one work group per query row):
 //   kl_target : S^T = rows . q^T per 32-slot tile of gathered latent rows (as the attention
 //               backward recomputes it), P = exp(S - lse), the head sum per slot (lanes, then
 //               waves through LDS), renormalised over the row -> target [T_q, K] fp32.
@@ -23,7 +23,9 @@
 //               the tile), dw, and the key-gradient contribution C = q_idx^T . G of every slot
 //               (G staged in LDS as a bf16 pair hi + lo, about 16 significant bits), which is
 //               stored as a 16-bit block floating point row and summed per key row after a
-//               counting sort, as for the attention's latent rows.
+//               counting sort, as for the attention's latent rows.  Four score waves (16 heads
+//               each) load the tiles and do everything but C; four contribution waves form and
+//               store C one chunk behind.
 #include <algorithm>
 
 #include "dsa_common.h"
@@ -36,7 +38,6 @@ namespace {
 
 constexpr int kSlots = 32;
 constexpr int kWaves = 4;
-constexpr int kNBuf = 3;
 constexpr int kDi = 128;   // indexer head dim of the training path
 constexpr int kSS = 72;    // G staging row stride (64 heads + 8, bf16)
 
@@ -211,88 +212,103 @@ void kl_target_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------------------
+// kl_bwd: one work group of 8 waves per query row.  Score waves 0..3 (head group G = wave)
+// stream the row's k_idx tiles with direct loads (kBwdNBuf buffers, three tiles in flight) and
+// compute the dot products, the scores (pass 1), and in pass 2 G and dq_idx; contribution waves
+// 4..7 (dims 32 qd .. + 31, qd = wave - 4) form C = q_idx^T . G one chunk behind from the staged
+// G and store it.  The stores stay out of the score waves, whose explicit waits for tile loads
+// would otherwise also wait for them (the vector-memory counter does not tell loads from stores).
+constexpr int kBwdScoreWaves = 4;
+constexpr int kBwdWaves = 8;
+constexpr int kBwdNBuf = 5;
+
 struct KlSmem {
-  static constexpr int kTiles = kNBuf * Tile<kDi>::kBytes;         // k_idx tiles
+  static constexpr int kTiles = kBwdNBuf * Tile<kDi>::kBytes;      // k_idx tiles
   static constexpr int kStage = kTiles;                            // [2][hi, lo][32][kSS] bf16
   static constexpr int kStageBytes = 2 * kSlots * kSS * 2;         // one buffer (hi + lo)
   static constexpr int kPart = kStage + 2 * kStageBytes;           // [2][4][32] fp32
-  static constexpr int kRows = kPart + 2 * kWaves * kSlots * 4;    // slot rows [Kr] int32
+  static constexpr int kRows = kPart + 2 * kBwdScoreWaves * kSlots * 4;  // slot rows [Kr] int32
   static size_t bytes(int K) {
     const size_t kr = static_cast<size_t>(K + kSlots - 1) / kSlots * kSlots;
-    return kRows + kr * 4 /* slot rows */ + kr * 4 /* scores, then dI */ + kr * 4 /* target */;
+    return kRows + kr * 4 /* slot rows */ + kr * 4 /* scores, then dI */;
   }
 };
 
-__global__ __launch_bounds__(kWaves * 64) void kl_bwd_kernel(
+__global__ __launch_bounds__(kBwdWaves * 64, 4) void kl_bwd_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const float *__restrict__ w, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ topk_length, const float *__restrict__ target, int Hi, int K,
     float grad, float *__restrict__ loss, uint16_t *__restrict__ dq_idx, float *__restrict__ dw,
     uint32_t *__restrict__ stage, int32_t *__restrict__ cnt, int64_t row0) {
   using TL = Tile<kDi>;
-  using TS = TileStream<kDi, kWaves, kNBuf>;
+  using TS = TileStream<kDi, kBwdScoreWaves, kBwdNBuf>;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t *stg = reinterpret_cast<uint16_t *>(smem + KlSmem::kStage);
   float *part = reinterpret_cast<float *>(smem + KlSmem::kPart);
   int32_t *slot_rows = reinterpret_cast<int32_t *>(smem + KlSmem::kRows);
   const int Kr = rows_rounded(K);
   float *ibuf = reinterpret_cast<float *>(smem + KlSmem::kRows + Kr * 4);
-  float *tbuf = ibuf + Kr;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool scorer = wave < kBwdScoreWaves;
   const int g = lane >> 4, hl = lane & 15;
   const int64_t i_row = blockIdx.x;
   const int64_t t = row0 + i_row;
   const int lim = topk_length ? topk_length[t] : K;
   const int32_t *irow = idx + t * K;
   const int nch = (lim + kSlots - 1) / kSlots;
-  // slot rows, the target row and one count per valid slot for the key rows' counting sort
-  for (int j = threadIdx.x; j < nch * kSlots; j += kWaves * 64) {
+  // slot rows and one count per valid slot for the key rows' counting sort
+  for (int j = threadIdx.x; j < nch * kSlots; j += kBwdWaves * 64) {
     const int32_t sj = j < lim ? irow[j] : -1;
     slot_rows[j] = sj;
-    tbuf[j] = sj >= 0 ? target[t * K + j] : 0.0f;
     if (sj >= 0) atomicAdd(&cnt[sj], 1);
   }
-  // B operands of the dot products: head h, dims 32 ks + 8 g + [0, 8)
-  const int h = wave * 16 + hl;
-  const bool hok = h < Hi;
+  // score waves: B operands of the dot products, head h, dims 32 ks + 8 g + [0, 8)
+  const int h = (wave & 3) * 16 + hl;
+  const bool hok = scorer && h < Hi;
   bf16x8 qf[kDi / 32];
-#pragma unroll
-  for (int ks = 0; ks < kDi / 32; ++ks) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (hok) v = *reinterpret_cast<const u32x4 *>(q_idx + ((t * Hi + h) * kDi + ks * 32 + g * 8));
-    qf[ks] = as_bf16x8(v);
-  }
-  const float wv = hok ? w[t * Hi + h] : 0.0f;
-  // A operands of C^T = q_idx^T . G: dims 32 wave + 16 m + hl, heads 32 kh + 8 g + [0, 8)
+  float wv = 0.0f;
+  // contribution waves: A operands of C^T = q_idx^T . G, dims 32 qd + 16 m + hl, heads
+  // 32 kh + 8 g + [0, 8)
   bf16x8 qa[2][2];
+  if (scorer) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int dim = 32 * wave + 16 * m + hl;
-      uint16_t e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int hh = 32 * kh + 8 * g + j;
-        e[j] = hh < Hi ? q_idx[(t * Hi + hh) * kDi + dim] : static_cast<uint16_t>(0);
-      }
-      qa[m][kh] = as_bf16x8(u32x4{e[0] | (static_cast<uint32_t>(e[1]) << 16),
-                                  e[2] | (static_cast<uint32_t>(e[3]) << 16),
-                                  e[4] | (static_cast<uint32_t>(e[5]) << 16),
-                                  e[6] | (static_cast<uint32_t>(e[7]) << 16)});
+    for (int ks = 0; ks < kDi / 32; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hok) v = *reinterpret_cast<const u32x4 *>(q_idx + ((t * Hi + h) * kDi + ks * 32 + g * 8));
+      qf[ks] = as_bf16x8(v);
     }
+    wv = hok ? w[t * Hi + h] : 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < kDi / 32; ++ks) settle(qf[ks]);
+    for (int ks = 0; ks < kDi / 32; ++ks) settle(qf[ks]);
+  } else {
+    const int qd = wave - kBwdScoreWaves;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) settle(qa[m][kh]);
-  __syncthreads();  // slot rows and target
+      for (int kh = 0; kh < 2; ++kh) {
+        const int dim = 32 * qd + 16 * m + hl;
+        uint16_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int hh = 32 * kh + 8 * g + j;
+          e[j] = hh < Hi ? q_idx[(t * Hi + hh) * kDi + dim] : static_cast<uint16_t>(0);
+        }
+        qa[m][kh] = as_bf16x8(u32x4{e[0] | (static_cast<uint32_t>(e[1]) << 16),
+                                    e[2] | (static_cast<uint32_t>(e[3]) << 16),
+                                    e[4] | (static_cast<uint32_t>(e[5]) << 16),
+                                    e[6] | (static_cast<uint32_t>(e[7]) << 16)});
+      }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) settle(qa[m][kh]);
+  }
+  __syncthreads();  // slot rows
 
   TS ts;
-  ts.init(smem, wave);
+  if (scorer) ts.init(smem, wave);
   TileFrag<kDi> fr;
   fr.init();
   // D^T = k rows . q_idx^T for the 32 slots of a tile (d[mt][i]: slot 16 mt + 4 g + i, head h)
@@ -304,40 +320,59 @@ __global__ __launch_bounds__(kWaves * 64) void kl_bwd_kernel(
       d[1] = mfma16(fr.a_frag(tile, 1, ks), qf[ks], d[1]);
     }
   };
-  auto gather_part = [&](int c) {  // wave 0: the scores of chunk c from the four waves
+  auto gather_part = [&](int c) {  // wave 0: the scores of chunk c from the four score waves
     if (wave == 0 && lane < kSlots) {
       float v = 0.0f;
 #pragma unroll
-      for (int w4 = 0; w4 < kWaves; ++w4) v += part[((c & 1) * kWaves + w4) * kSlots + lane];
+      for (int w4 = 0; w4 < kBwdScoreWaves; ++w4) v += part[((c & 1) * kBwdScoreWaves + w4) * kSlots + lane];
       ibuf[c * kSlots + lane] = slot_rows[c * kSlots + lane] >= 0 ? v : -INFINITY;
     }
   };
+  // tile c complete (up to three later tiles stay in flight) and published to the work group;
+  // every wave is then done with tile c - 1, whose buffer the caller refills
+  auto acquire = [&](int c) {
+    const int ahead = min(kBwdNBuf - 2, nch - 1 - c);
+    if (ahead >= 3) wait_vm<3 * TS::L>();
+    else if (ahead == 2) wait_vm<2 * TS::L>();
+    else if (ahead == 1) wait_vm<TS::L>();
+    else wait_vm<0>();
+    lds_barrier();
+  };
+  auto issue_first = [&]() {  // tiles 0 .. kBwdNBuf - 2 of a pass
+#pragma unroll
+    for (int c = 0; c < kBwdNBuf - 1; ++c)
+      if (c < nch) ts.issue(c, k_idx, slot_rows);
+  };
 
-  // ---- pass 1: indexer scores of the row's slots
-  if (nch > 0) ts.issue(0, k_idx, slot_rows);
-  if (nch > 1) ts.issue(1, k_idx, slot_rows);
+  // ---- pass 1: indexer scores of the row's slots (the contribution waves only keep step with
+  // the barriers)
+  if (scorer) issue_first();
   for (int c = 0; c < nch; ++c) {
-    TS::acquire(c, nch);
+    if (!scorer) {
+      lds_barrier();
+      continue;
+    }
+    acquire(c);
     if (c > 0) gather_part(c - 1);
-    if (c + 2 < nch) ts.issue(c + 2, k_idx, slot_rows);
+    if (c + kBwdNBuf - 1 < nch) ts.issue(c + kBwdNBuf - 1, k_idx, slot_rows);
     f32x4 d[2];
-    dots(smem + (c % kNBuf) * TL::kBytes, d);
+    dots(smem + (c % kBwdNBuf) * TL::kBytes, d);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float v = sum16(wv * fmaxf(d[mt][i], 0.0f));
-        if (hl == 0) part[((c & 1) * kWaves + wave) * kSlots + mt * 16 + g * 4 + i] = v;
+        if (hl == 0) part[((c & 1) * kBwdScoreWaves + wave) * kSlots + mt * 16 + g * 4 + i] = v;
       }
   }
   lds_barrier();  // every wave is done with the tiles and with the last chunk's partial scores
   if (nch > 0) gather_part(nch - 1);
   // pass 2's first tiles load while the softmax runs
-  if (nch > 0) ts.issue(0, k_idx, slot_rows);
-  if (nch > 1) ts.issue(1, k_idx, slot_rows);
+  if (scorer) issue_first();
   lds_barrier();  // scores complete
-  // ---- the row's softmax over its slots, the loss and dI (wave 0)
-  if (wave == 0) {
+  // ---- the row's softmax over its slots, the loss and dI (the first contribution wave, which
+  // has no tile loads in flight to wait for with its target loads)
+  if (wave == kBwdScoreWaves) {
     const int n = nch * kSlots;
     float m = -INFINITY;
     for (int j = lane; j < n; j += 64) m = fmaxf(m, ibuf[j]);
@@ -352,9 +387,9 @@ __global__ __launch_bounds__(kWaves * 64) void kl_bwd_kernel(
     for (int j = lane; j < n; j += 64) {
       const float I = ibuf[j];
       float di = 0.0f;
-      if (I != -INFINITY) {
+      if (I != -INFINITY) {  // a valid slot (j < lim)
         const float logu = I - logz;
-        const float p = tbuf[j];
+        const float p = target[t * K + j];
         if (p > 0.0f) ls += p * (__logf(p) - logu);
         di = grad * (__expf(logu) - p);
       }
@@ -365,15 +400,76 @@ __global__ __launch_bounds__(kWaves * 64) void kl_bwd_kernel(
     if (lane == 0) loss[t] = nch > 0 ? ls : 0.0f;
   }
   // ---- pass 2: gradients
-  f32x4 dq[kDi / 16];  // dq_idx^T[dim 16 n + 4 g + i][head h]
+  if (scorer) {
+    f32x4 dq[kDi / 16];  // dq_idx^T[dim 16 n + 4 g + i][head h]
 #pragma unroll
-  for (int n = 0; n < kDi / 16; ++n) dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dwa = 0.0f;
-  for (int c = 0; c <= nch; ++c) {
-    if (c < nch) TS::acquire(c, nch);  // also: dI is published (c = 0), G of chunk c - 1 staged
-    else lds_barrier();
-    if (c > 0) {
-      // C^T[dims 32 wave .. + 31 x 32 slots] of chunk c - 1 from the staged G (hi + lo)
+    for (int n = 0; n < kDi / 16; ++n) dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dwa = 0.0f;
+    for (int c = 0; c <= nch; ++c) {
+      // also: dI is published (c = 0); every wave is done with chunk c - 1's tile, and the
+      // contribution waves with the G staged two chunks back
+      if (c < nch) acquire(c);
+      else lds_barrier();
+      if (c == nch) break;
+      if (c + kBwdNBuf - 1 < nch) ts.issue(c + kBwdNBuf - 1, k_idx, slot_rows);
+      const unsigned char *tile = smem + (c % kBwdNBuf) * TL::kBytes;
+      f32x4 d[2];
+      dots(tile, d);
+      float gv[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const f32x4 di = *reinterpret_cast<const f32x4 *>(ibuf + c * kSlots + mt * 16 + g * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gv[mt][i] = d[mt][i] > 0.0f ? di[i] * wv : 0.0f;
+          dwa = fmaf(di[i], fmaxf(d[mt][i], 0.0f), dwa);
+        }
+      }
+      // G as a bf16 pair hi + lo: B operands of dq^T and the staged [slot][head] copy for C
+      float gl[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gl[mt][i] = gv[mt][i] - bf16_to_f32(f32_to_bf16(gv[mt][i]));
+      const bf16x8 gh8 = pack_slots(gv), gl8 = pack_slots(gl);
+#pragma unroll
+      for (int n = 0; n < kDi / 16; ++n) {
+        const bf16x8 va = fr.v_frag(tile, n);
+        dq[n] = mfma16(va, gh8, dq[n]);
+        dq[n] = mfma16(va, gl8, dq[n]);
+      }
+      uint16_t *zh = stg + (c & 1) * (KlSmem::kStageBytes / 2);
+      uint16_t *zl = zh + kSlots * kSS;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int o = (mt * 16 + g * 4 + i) * kSS + h;
+          const uint16_t hi = f32_to_bf16(gv[mt][i]);
+          zh[o] = hi;
+          zl[o] = f32_to_bf16(gv[mt][i] - bf16_to_f32(hi));
+        }
+    }
+    // ---- dq_idx (bf16) and dw of this wave's heads
+    if (hok) {
+      uint16_t *row = dq_idx + (t * Hi + h) * kDi + g * 4;
+#pragma unroll
+      for (int n = 0; n < kDi / 16; ++n) {
+        u32x2 v;
+        v[0] = pack_bf16x2(dq[n][0], dq[n][1]);
+        v[1] = pack_bf16x2(dq[n][2], dq[n][3]);
+        *reinterpret_cast<u32x2 *>(row + n * 16) = v;
+      }
+    }
+    dwa += __shfl_xor(dwa, 16, 64);
+    dwa += __shfl_xor(dwa, 32, 64);
+    if (hok && g == 0) dw[t * Hi + h] = dwa;
+  } else {
+    const int qd = wave - kBwdScoreWaves;
+    for (int c = 0; c <= nch; ++c) {
+      lds_barrier();  // G of chunk c - 1 is staged
+      if (c == 0) continue;
+      // C^T[dims 32 qd .. + 31 x 32 slots] of chunk c - 1 from the staged G (hi + lo)
       const int cc = c - 1;
       const uint16_t *zh = stg + (cc & 1) * (KlSmem::kStageBytes / 2);
       const uint16_t *zl = zh + kSlots * kSS;
@@ -393,7 +489,7 @@ __global__ __launch_bounds__(kWaves * 64) void kl_bwd_kernel(
           }
         }
         // staged row of slot cc*32 + 16 mt + hl: this lane's block is dims
-        // 32 wave + 16 m + 4 g + i (block 4 wave + g)
+        // 32 qd + 16 m + 4 g + i (block 4 qd + g)
         if (rr[mt * 16 + hl] >= 0) {
           float mx = 0.0f;
 #pragma unroll
@@ -408,67 +504,14 @@ __global__ __launch_bounds__(kWaves * 64) void kl_bwd_kernel(
             u32x2 v;
             v[0] = pknorm16(acc[m][0] * sc, acc[m][1] * sc);
             v[1] = pknorm16(acc[m][2] * sc, acc[m][3] * sc);
-            *reinterpret_cast<u32x2 *>(row + ((32 * wave + 16 * m + 4 * g) >> 1)) = v;
+            *reinterpret_cast<u32x2 *>(row + ((32 * qd + 16 * m + 4 * g) >> 1)) = v;
           }
-          reinterpret_cast<unsigned char *>(row + kDi / 2)[4 * wave + g] =
+          reinterpret_cast<unsigned char *>(row + kDi / 2)[4 * qd + g] =
               static_cast<unsigned char>(eb);
         }
       }
     }
-    if (c == nch) break;
-    if (c + 2 < nch) ts.issue(c + 2, k_idx, slot_rows);
-    const unsigned char *tile = smem + (c % kNBuf) * TL::kBytes;
-    f32x4 d[2];
-    dots(tile, d);
-    float gv[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const f32x4 di = *reinterpret_cast<const f32x4 *>(ibuf + c * kSlots + mt * 16 + g * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gv[mt][i] = d[mt][i] > 0.0f ? di[i] * wv : 0.0f;
-        dwa = fmaf(di[i], fmaxf(d[mt][i], 0.0f), dwa);
-      }
-    }
-    // G as a bf16 pair hi + lo: B operands of dq^T and the staged [slot][head] copy for C
-    float gl[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gl[mt][i] = gv[mt][i] - bf16_to_f32(f32_to_bf16(gv[mt][i]));
-    const bf16x8 gh8 = pack_slots(gv), gl8 = pack_slots(gl);
-#pragma unroll
-    for (int n = 0; n < kDi / 16; ++n) {
-      const bf16x8 va = fr.v_frag(tile, n);
-      dq[n] = mfma16(va, gh8, dq[n]);
-      dq[n] = mfma16(va, gl8, dq[n]);
-    }
-    uint16_t *zh = stg + (c & 1) * (KlSmem::kStageBytes / 2);
-    uint16_t *zl = zh + kSlots * kSS;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = (mt * 16 + g * 4 + i) * kSS + h;
-        const uint16_t hi = f32_to_bf16(gv[mt][i]);
-        zh[o] = hi;
-        zl[o] = f32_to_bf16(gv[mt][i] - bf16_to_f32(hi));
-      }
   }
-  // ---- dq_idx (bf16) and dw of this wave's heads
-  if (hok) {
-    uint16_t *row = dq_idx + (t * Hi + h) * kDi + g * 4;
-#pragma unroll
-    for (int n = 0; n < kDi / 16; ++n) {
-      u32x2 v;
-      v[0] = pack_bf16x2(dq[n][0], dq[n][1]);
-      v[1] = pack_bf16x2(dq[n][2], dq[n][3]);
-      *reinterpret_cast<u32x2 *>(row + n * 16) = v;
-    }
-  }
-  dwa += __shfl_xor(dwa, 16, 64);
-  dwa += __shfl_xor(dwa, 32, 64);
-  if (hok && g == 0) dw[t * Hi + h] = dwa;
 }
 
 }  // namespace
@@ -510,7 +553,7 @@ hipError_t launch_indexer_kl_bwd(const uint16_t *q_idx, const uint16_t *k_idx, c
     const int64_t n = std::min<int64_t>(rows_per_pass, T_q - r0);
     e = launch_pair_count_zero(T_kv, bb, s);
     if (e != hipSuccess) break;
-    DSA_LAUNCH("indexer_kl_bwd", kl_bwd_kernel, dim3(static_cast<unsigned>(n)), dim3(kWaves * 64),
+    DSA_LAUNCH("indexer_kl_bwd", kl_bwd_kernel, dim3(static_cast<unsigned>(n)), dim3(kBwdWaves * 64),
                smem, s, q_idx, k_idx, w, idx, topk_length, target, H_i, K, grad, loss, dq_idx, dw,
                bb.stage, bb.off, r0);
     if ((e = hipGetLastError()) != hipSuccess) break;
