@@ -68,15 +68,15 @@ void kernel_begin(hipStream_t s, const char *name) {
   if (!st.slots || *st.n_used >= st.n_slots) return;
   dsa_kernel_timing &slot = st.slots[*st.n_used];
   slot.name = name;
-  hipEventRecord(static_cast<hipEvent_t>(slot.start), s);
-  st.open = true;
+  // a slot whose start could not be recorded is left unused
+  st.open = hipEventRecord(static_cast<hipEvent_t>(slot.start), s) == hipSuccess;
 }
 
 void kernel_end(hipStream_t s) {
   TimingState &st = g_timing;
   if (!st.open) return;
-  hipEventRecord(static_cast<hipEvent_t>(st.slots[*st.n_used].stop), s);
-  ++*st.n_used;
+  if (hipEventRecord(static_cast<hipEvent_t>(st.slots[*st.n_used].stop), s) == hipSuccess)
+    ++*st.n_used;
   st.open = false;
 }
 
