@@ -41,7 +41,6 @@ constexpr int kRows = kIdxRowsPerGroup;  // query rows per work group
 constexpr int kWaves = 2 * kRows;        // two waves per row
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileKeys = 64;
-constexpr int kBins = 256;
 // value bins of a compaction: narrower bins collide less in the LDS atomics
 constexpr int kPruneBins = 512;
 
@@ -68,8 +67,11 @@ struct IndexerSmem {
   uint32_t tau[kRows];                // per-row threshold: later keys enter only if above it
   int32_t has_tau[kRows];
   int32_t compact[2];  // compaction due in step i: compact[i & 1] (written by wave 0 in step i - 1)
+  uint32_t xlo[kRows][2], xhi[kRows][2], xdrop[kRows][2];  // a compaction's per-stack results
   __align__(16) unsigned char tile[IndexerCfg<D>::kNBuf][IndexerCfg<D>::kTileBytes];
 };
+static_assert(sizeof(IndexerSmem<128>) <= 160 * 1024 && sizeof(IndexerSmem<64>) <= 160 * 1024,
+              "indexer LDS");
 // after the key stream the tile buffers hold 4 rows x (4 KB bitmap + 2 KB scratch list), and
 // with 128-dim keys also 4 rows x a 4 KB (1024-bin) value histogram
 template <int D>
@@ -368,28 +370,104 @@ __device__ void value_histogram(const uint32_t *ck, int cnt, const ValueBinsN<NB
   wave_sync();
 }
 
-// Streaming compaction: drops candidates that can no longer reach the top K, keeping at least
-// K of them, in one counting pass.  The keys above the current threshold are binned by value
-// over [threshold, largest key]; the bin b holding the K-th largest key leaves at least K keys
-// in bins >= b, so every key in a lower bin lies below the K-th largest and can be dropped,
-// and so can any later key that is not above the largest dropped key, which becomes the new
-// threshold `tau`.  Returns whether a threshold is set; `cnt` becomes the number kept (>= K).
-__device__ bool prune_candidates(uint32_t *ck, int32_t *cp, uint32_t *hist, int &cnt, int K,
-                                 bool has_tau, uint32_t &tau) {
-  uint32_t lo, hi;
-  key_range(ck, cnt, lo, hi);
-  if (has_tau) lo = tau + 1u;  // every candidate is above the current threshold
-  ValueBinsN<kPruneBins> vb;
-  if (!vb.init(lo, hi)) return has_tau;
-  value_histogram<kPruneBins>(ck, cnt, vb, hist);
-  uint32_t above;
-  const int b = static_cast<int>(bin_from_top_n<kPruneBins>(hist, static_cast<uint32_t>(K), above));
-  if (b == 0) return has_tau;  // nothing below the K-th key's bin
-  uint32_t dmax;
-  cnt = compact_candidates(ck, cp, cnt, [vb, b](uint32_t u, int32_t) { return vb(u) >= b; },
-                           dmax);
-  tau = has_tau ? max(tau, dmax) : dmax;
-  return true;
+// ---- the two stacks of a row's candidate buffer, seen from the wave that fills each ----------
+// The lower-half wave's stack holds entries 0 .. n-1 of the buffer; the upper-half wave's stack
+// holds its i-th entry at cap - 1 - i.  A Stack presents either as entries 0 .. n-1, read four
+// at a time (four consecutive entries of the upper stack are one reversed 16-byte vector, since
+// cap is a multiple of 4).
+struct Stack {
+  uint32_t *ck;
+  int32_t *cp;
+  int cap;
+  bool up;
+  __device__ __forceinline__ int at(int i) const { return up ? cap - 1 - i : i; }
+  __device__ __forceinline__ u32x4 keys4(int e) const {
+    if (!up) return *reinterpret_cast<const u32x4 *>(ck + e);
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(ck + cap - 4 - e);
+    return u32x4{v[3], v[2], v[1], v[0]};
+  }
+  __device__ __forceinline__ u32x4 pos4(int e) const {
+    if (!up) return *reinterpret_cast<const u32x4 *>(cp + e);
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(cp + cap - 4 - e);
+    return u32x4{v[3], v[2], v[1], v[0]};
+  }
+};
+
+// Smallest and largest key of a stack (lo = 0xFFFFFFFF, hi = 0 for an empty one).
+__device__ __forceinline__ void stack_range(const Stack &st, int cnt, uint32_t &lo, uint32_t &hi) {
+  const int lane = __lane_id();
+  lo = 0xFFFFFFFFu;
+  hi = 0u;
+  for (int e = 4 * lane; e < cnt; e += 256) {
+    const u32x4 v = st.keys4(e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e + j < cnt) {
+        lo = min(lo, v[j]);
+        hi = max(hi, v[j]);
+      }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off, 64)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off, 64)));
+  }
+}
+
+// Adds a stack's keys to an NB-bin value histogram that the caller has cleared.
+template <int NB>
+__device__ void stack_histogram(const Stack &st, int cnt, const ValueBinsN<NB> &vb,
+                                uint32_t *hist) {
+  const int lane = __lane_id();
+  for (int e = 4 * lane; e < cnt; e += 256) {
+    const u32x4 v = st.keys4(e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e + j < cnt) atomicAdd(&hist[vb(v[j])], 1u);
+  }
+}
+
+// As compact_candidates, on a stack: the kept entries become the stack's first entries.
+template <typename Keep>
+__device__ int compact_stack(const Stack &st, int cnt, Keep keep, uint32_t &dropped_max) {
+  const int lane = __lane_id();
+  const uint64_t lt = lanemask_lt();
+  int written = 0;
+  uint32_t dmax = 0u;
+  for (int base = 0; base < cnt; base += 256) {
+    const int e = base + 4 * lane;
+    u32x4 v = {0u, 0u, 0u, 0u}, p = {0u, 0u, 0u, 0u};
+    if (e < cnt) {
+      v = st.keys4(e);
+      p = st.pos4(e);
+    }
+    bool kp[4];
+    uint64_t m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = e + j < cnt;
+      kp[j] = in && keep(v[j], static_cast<int32_t>(p[j]));
+      if (in && !kp[j]) dmax = max(dmax, v[j]);
+      m[j] = __ballot(kp[j]);
+    }
+    int off = written;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kp[j]) {
+        const int o = st.at(off + __popcll(m[j] & lt));
+        st.ck[o] = v[j];
+        st.cp[o] = static_cast<int32_t>(p[j]);
+      }
+      off += __popcll(m[j]);
+    }
+    written = off;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    dmax = max(dmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dmax), off, 64)));
+  dropped_max = dmax;
+  wave_sync();
+  return written;
 }
 
 // Final selection of exactly K of the row's cnt >= K candidates and their output in ascending
@@ -792,41 +870,91 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     return n_lo + n_hi;
   };
 
-  // Compaction of every row far enough above K.  Every wave calls it in the same step (the
-  // flag it follows was written by wave 0 in the previous step), after its MFMAs and before its
-  // appends; the first barrier makes every append before it visible, the last one the new
-  // thresholds and counts.
+  // Compaction of every row far enough above K, by both waves of the row, each on its own
+  // stack.  Every wave calls it in the same step (the flag it follows was written by wave 0 in
+  // the previous step), after its MFMAs and before its appends, and passes the same five
+  // barriers: appends visible | key ranges and cleared histogram | histogram | kept entries and
+  // the largest dropped key of each stack | the new threshold and counts.
+  //   The keys above the current threshold (all of them before the first one) are binned by
+  // value over [threshold, largest key]; the bin b holding the K-th largest key leaves at least
+  // K keys in bins >= b, so every key in a lower bin lies below the K-th largest and is dropped,
+  // and so is any later key that is not above the largest key dropped, which becomes the new
+  // threshold.
   auto compact_rows = [&]() __attribute__((always_inline)) {
     lds_barrier();
-    if (half == 0) {
-      const int n_hi = __builtin_amdgcn_readfirstlane(sm.cntb[row]);
-      if (my_n + n_hi > (C::kCap + K) / 2) {
-        int n = merge_stacks(my_n, n_hi);
-        uint32_t tau = my_tau;
-        bool has = prune_candidates(ck, cp, sm.hist[row], n, K, my_has_tau, tau);
-        if (n > C::kCap - 3 * kTileKeys) {  // too many ties to make room: exact selection
-          // exactly K kept, all at or above the K-th key kth (> the old threshold); a later key
-          // equal to kth loses the tie, but the threshold kth - 1 keeps every kept key above it
-          const uint32_t kth = select_exact(ck, cp, sm.hist[row], n, K, start, tg);
-          if (kth > 0u) {
-            tau = kth - 1u;
-            has = true;
-          }
+    const int n_lo = __builtin_amdgcn_readfirstlane(sm.cnt[row]);
+    const int n_hi = __builtin_amdgcn_readfirstlane(sm.cntb[row]);
+    const bool go = n_lo + n_hi > (C::kCap + K) / 2;
+    const Stack st{ck, cp, C::kCap, half == 1};
+    uint32_t *hist = sm.hist[row];
+    if (go) {
+      uint32_t lo, hi;
+      stack_range(st, my_n, lo, hi);
+      *reinterpret_cast<u32x4 *>(hist + (kPruneBins / 2) * half + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+      if (lane == 0) {
+        sm.xlo[row][half] = lo;
+        sm.xhi[row][half] = hi;
+      }
+    }
+    lds_barrier();
+    ValueBinsN<kPruneBins> vb;
+    bool binned = false;
+    if (go) {
+      uint32_t lo = min(sm.xlo[row][0], sm.xlo[row][1]);
+      const uint32_t hi = max(sm.xhi[row][0], sm.xhi[row][1]);
+      if (my_has_tau) lo = my_tau + 1u;  // every candidate is above the current threshold
+      binned = vb.init(lo, hi);
+      if (binned) stack_histogram<kPruneBins>(st, my_n, vb, hist);
+    }
+    lds_barrier();
+    bool pruned = false;
+    if (binned) {
+      uint32_t above;
+      const int b = static_cast<int>(bin_from_top_n<kPruneBins>(hist, static_cast<uint32_t>(K), above));
+      if (b > 0) {
+        uint32_t dmax;
+        my_n = compact_stack(st, my_n, [vb, b](uint32_t u, int32_t) { return vb(u) >= b; }, dmax);
+        pruned = true;
+        if (lane == 0) {
+          sm.xdrop[row][half] = dmax;
+          (half == 0 ? sm.cnt : sm.cntb)[row] = my_n;
+        }
+      }
+    }
+    lds_barrier();
+    if (go && half == 0) {
+      uint32_t tau = my_tau;
+      bool has = my_has_tau;
+      if (pruned) {
+        const uint32_t dmax = max(sm.xdrop[row][0], sm.xdrop[row][1]);
+        tau = has ? max(tau, dmax) : dmax;
+        has = true;
+      }
+      int n_hi2 = __builtin_amdgcn_readfirstlane(sm.cntb[row]);
+      if (my_n + n_hi2 > C::kCap - 3 * kTileKeys) {  // too many ties to make room: exact selection
+        // exactly K kept, all at or above the K-th key kth (> the old threshold); a later key
+        // equal to kth loses the tie, but the threshold kth - 1 keeps every kept key above it
+        int n = merge_stacks(my_n, n_hi2);
+        const uint32_t kth = select_exact(ck, cp, hist, n, K, start, tg);
+        if (kth > 0u) {
+          tau = kth - 1u;
+          has = true;
         }
         my_n = n;
-        if (lane == 0) {
-          sm.tau[row] = tau;
-          sm.has_tau[row] = has ? 1 : 0;
-          sm.cnt[row] = n;
-          sm.cntb[row] = 0;
-        }
+        n_hi2 = 0;
+      }
+      if (lane == 0) {
+        sm.tau[row] = tau;
+        sm.has_tau[row] = has ? 1 : 0;
+        sm.cnt[row] = my_n;
+        sm.cntb[row] = n_hi2;
       }
     }
     lds_barrier();  // new thresholds and counts are visible
     my_has_tau = __builtin_amdgcn_readfirstlane(sm.has_tau[row]) != 0;
     my_tau = __builtin_amdgcn_readfirstlane(sm.tau[row]);
     tau_eff = my_has_tau ? my_tau : 0u;
-    if (half == 1) my_n = __builtin_amdgcn_readfirstlane(sm.cntb[row]);
+    my_n = __builtin_amdgcn_readfirstlane(half == 0 ? sm.cnt[row] : sm.cntb[row]);
   };
   // Wave 0 decides whether the next step compacts.  The counts it reads hold every append up to
   // the previous step and perhaps some of this step's; until that compaction this step and the
