@@ -16,6 +16,10 @@ its kernel launches; `cpu_baseline` times the CPU oracle on a bounded row sample
 `ms_per_step` is the wall-clock mean over the timed steps, `median_ms_per_step` the median of
 per-step HIP events, and `cold_ms_per_step` one more step after 1 GiB has been written to
 evict the inputs from L2 and the 256 MB last-level cache (not part of `value`).
+`gather_ceiling` is the rate at which the GPU gathers uniformly random rows of the step's
+latent table through LDS the way the attention kernels do, with nothing else to do (measured
+after the timed steps); `components.*.gather_vs_ceiling` sets the forward's and backward's
+gather rates against it.
 """
 
 from __future__ import annotations
@@ -508,6 +512,26 @@ def main():
     torch.cuda.synchronize()
     cold_ms = cold_ev[0].elapsed_time(cold_ev[1])
     del flush
+    # gather ceiling: uniformly random rows of the step's latent table (up to 2^23 of them),
+    # streamed through LDS as the attention kernels gather them and used for nothing else
+    # (dsa_gather_probe); the median of three runs
+    n_g = max(1 << 20, min(counts["valid"], 1 << 23)) // 2048 * 2048
+    g_rows = torch.randint(0, T_keys, (n_g,), device=dev, dtype=torch.int32,
+                           generator=torch.Generator(device=dev).manual_seed(0x6A7E))
+    dsa.gather_probe(att["kv"], g_rows)
+    g_ms = []
+    for _ in range(3):
+        gev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        gev[0].record()
+        dsa.gather_probe(att["kv"], g_rows)
+        gev[1].record()
+        torch.cuda.synchronize()
+        g_ms.append(gev[0].elapsed_time(gev[1]))
+    g_ms = sorted(g_ms)[1]
+    gather_ceiling = {"gbs": n_g * Dqk * 2 / g_ms / 1e6, "ms": g_ms, "rows": n_g,
+                      "row_bytes": Dqk * 2, "table_mb": T_keys * Dqk * 2 / 1e6,
+                      "frac_hbm_peak": n_g * Dqk * 2 / g_ms / 1e6 / PEAK_HBM_GBS}
+    del g_rows
 
     ms_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
@@ -533,6 +557,8 @@ def main():
                 "frac_mfma_peak": counts["bwd_flops"] / t_bwd / 1e9 / PEAK_BF16_TFLOPS,
                 "gather_gbs": 2 * row_bytes / t_bwd / 1e6},
     }
+    for c in ("fwd", "bwd"):
+        comp[c]["gather_vs_ceiling"] = comp[c]["gather_gbs"] / gather_ceiling["gbs"]
     if has_indexer:
         comp["indexer"] = {"ms": t_idx, "tokens_per_s": T / (t_idx * 1e-3),
                            "tflops": counts["idx_flops"] / t_idx / 1e9,
@@ -605,6 +631,7 @@ def main():
                                          "key_tokens": T_keys} if args.cp > 1 else None),
                    "parallelism": "none"},
         "components": comp, "kernels": kernels, "roofline": roofline,
+        "gather_ceiling": gather_ceiling,
     }
     if not args.no_cpu_baseline and local_rows is None:
         inputs.update(idx=idx_buf, len=len_buf)

@@ -408,6 +408,27 @@ typedef struct dsa_kernel_timing {
 
 int dsa_record_kernel_events(dsa_kernel_timing *slots, int n_slots, int *n_used);
 
+/* --------------------------------------------------------------------------
+ * Benchmark support: gather ceiling (not a step of the method; it measures the
+ * memory path of the attention kernels' latent-row gathers, one row per valid
+ * top-k slot, GLM-5.2 page "Why DSA needs fused kernels").  Streams the rows
+ * idx[0 .. n) of table [rows, width] bf16 through LDS in tiles of 32 rows with
+ * the attention kernels' direct loads, tile layout and buffering, and computes
+ * nothing with them but one checksum word per work group of 2048 listed rows:
+ * sink[g] = XOR over the 32-row tiles c of the group and the 256 threads l of the
+ * four 32-bit words of the 16-byte piece at byte 16 l of tile c as laid out in
+ * LDS (tile row l / (width/8), row chunk (l mod (width/8)) XOR swizzle(row), the
+ * swizzle of the attention kernels' tiles).  A row index of -1 (or a slot beyond
+ * n in a group's last tile) loads row 0.
+ *   table [rows, width] bf16, 16-byte aligned, width in {512, 576},
+ *   rows * width * 2 < 4 GiB; idx [n] int32, entries in [0, rows) or -1 (index
+ *   contents are trusted); sink [dsa_gather_probe_groups(n)] uint32 (out).
+ * Errors: DSA_ERR_INVALID_VALUE for bad sizes or NULL / misaligned pointers.
+ * ------------------------------------------------------------------------ */
+int64_t dsa_gather_probe_groups(int64_t n);
+int dsa_gather_probe(const uint16_t *table, int64_t rows, int32_t width, const int32_t *idx,
+                     int64_t n, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

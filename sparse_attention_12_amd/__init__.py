@@ -112,6 +112,10 @@ def lib():
         L.dsa_sparse_mla_bwd_noalloc.restype = C.c_int
         L.dsa_record_kernel_events.restype = C.c_int
         L.dsa_record_kernel_events.argtypes = [vp, C.c_int, C.POINTER(C.c_int)]
+        L.dsa_gather_probe_groups.restype = i64
+        L.dsa_gather_probe_groups.argtypes = [i64]
+        L.dsa_gather_probe.restype = C.c_int
+        L.dsa_gather_probe.argtypes = [vp, i64, i32, vp, i64, vp, vp]
         _lib = L
     return _lib
 
@@ -593,3 +597,25 @@ def indexer_kl_bwd(q_idx, k_idx, w, topk_indices, target, grad: float = 1.0, top
           DSA_BWD_ACCUMULATE_DKV if accumulate else 0, workspace.data_ptr(), workspace.numel(),
           _stream())
     return loss, dq_idx, dw, dk_idx
+
+
+def gather_probe(table: torch.Tensor, rows: torch.Tensor, sink=None):
+    """dsa_gather_probe: streams table[rows] (bf16 [T_kv, 512 or 576], rows int32 [n]) through
+    LDS as the attention kernels gather latent rows, and returns one checksum word per work
+    group of 2048 listed rows (int32 [dsa_gather_probe_groups(n)], the uint32 bits)."""
+    op = "gather_probe"
+    _require(op, table, rows, sink)
+    _dtype(op, "table", table, torch.bfloat16)
+    _dtype(op, "rows", rows, torch.int32)
+    if table.dim() != 2 or rows.dim() != 1:
+        raise ValueError(f"{op}: table must be [T_kv, width] and rows [n]")
+    n = rows.shape[0]
+    g = lib().dsa_gather_probe_groups(n)
+    if sink is None:
+        sink = torch.empty((max(g, 1),), dtype=torch.int32, device=table.device)
+    _dtype(op, "sink", sink, torch.int32)
+    if sink.numel() < g:
+        raise ValueError(f"{op}: sink holds {sink.numel()} words, {g} needed")
+    _call(lib().dsa_gather_probe, op, table.data_ptr(), table.shape[0], table.shape[1],
+          rows.data_ptr(), n, sink.data_ptr(), _stream())
+    return sink[:g]

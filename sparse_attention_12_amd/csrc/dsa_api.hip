@@ -853,6 +853,31 @@ int dsa_sparse_mla_bwd_kl_target(const uint16_t *q, const uint16_t *kv, const in
                  stream, target);
 }
 
+int64_t dsa_gather_probe_groups(int64_t n) {
+  return n <= 0 ? 0 : (n + dsa::kGatherProbeRows - 1) / dsa::kGatherProbeRows;
+}
+
+int dsa_gather_probe(const uint16_t *table, int64_t rows, int32_t width, const int32_t *idx,
+                     int64_t n, uint32_t *sink, void *stream) {
+  g_last_error.clear();
+  if (width != 512 && width != 576)
+    return fail(DSA_ERR_INVALID_VALUE, "gather_probe: width=%d not in {512, 576}", width);
+  if (rows < 1 || rows * static_cast<int64_t>(width) * 2 > static_cast<int64_t>(UINT32_MAX))
+    return fail(DSA_ERR_INVALID_VALUE, "gather_probe: rows=%lld out of range",
+                static_cast<long long>(rows));
+  if (n < 0 || dsa_gather_probe_groups(n) > INT32_MAX)
+    return fail(DSA_ERR_INVALID_VALUE, "gather_probe: n=%lld out of range",
+                static_cast<long long>(n));
+  if (n > 0 && (!table || !idx || !sink))
+    return fail(DSA_ERR_INVALID_VALUE, "gather_probe: NULL pointer");
+  if (!aligned16(table)) return fail(DSA_ERR_INVALID_VALUE, "gather_probe: table not 16-byte aligned");
+  if (int rc = check_device()) return rc;
+  hipError_t e = dsa::launch_gather_probe(table, width, idx, n, sink,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather_probe: launch");
+  return DSA_OK;
+}
+
 size_t dsa_sparse_mla_bwd_noalloc_scratch_bytes(void) { return dsa::kNoAllocScratchBytes; }
 
 int dsa_sparse_mla_bwd_noalloc(const uint16_t *q, const uint16_t *kv, const int32_t *idx,

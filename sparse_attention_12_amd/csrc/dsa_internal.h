@@ -23,6 +23,11 @@ void kernel_end(hipStream_t s);
 // Rows of one indexer work group (consecutive query rows of one sequence).
 constexpr int kIdxRowsPerGroup = 4;
 
+// Listed rows per work group of the gather probe.
+constexpr int64_t kGatherProbeRows = 2048;
+hipError_t launch_gather_probe(const uint16_t *table, int32_t width, const int32_t *idx,
+                               int64_t n, uint32_t *sink, hipStream_t s);
+
 hipError_t launch_thd_metadata(const int32_t *cu, int32_t B, int64_t T, int32_t K,
                                int32_t *seq_start, int32_t *causal_len, int32_t *topk_length,
                                int32_t *row_order, int32_t *groups, int32_t n_groups,

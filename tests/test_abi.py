@@ -141,6 +141,23 @@ def test_sink_entry_points_reject_missing_sink(dsa):
     assert "dsink" in _err(dsa)
 
 
+def test_gather_probe_groups_and_argument_errors(dsa):
+    assert [dsa.dsa_gather_probe_groups(n) for n in (-5, 0, 1, 2048, 2049, 4096)] == \
+        [0, 0, 1, 1, 2, 2]
+    fake = C.c_void_p(1 << 20)
+    assert dsa.dsa_gather_probe(fake, 100, 500, fake, 10, fake, None) == 1
+    assert "width" in _err(dsa)
+    assert dsa.dsa_gather_probe(fake, 0, 576, fake, 10, fake, None) == 1
+    assert "rows" in _err(dsa)
+    assert dsa.dsa_gather_probe(fake, (4 << 30) // 1024, 512, fake, 10, fake, None) == 1
+    assert "rows" in _err(dsa)
+    assert dsa.dsa_gather_probe(fake, 100, 576, fake, -1, fake, None) == 1
+    assert dsa.dsa_gather_probe(None, 100, 576, fake, 10, fake, None) == 1
+    assert "NULL" in _err(dsa)
+    assert dsa.dsa_gather_probe(C.c_void_p((1 << 20) + 8), 100, 576, fake, 10, fake, None) == 1
+    assert "aligned" in _err(dsa)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import sparse_attention_12_amd as pkg
     monkeypatch.setattr(pkg, "_lib", None)
