@@ -41,11 +41,19 @@ constexpr int kWaves = 4;
 constexpr int kDi = 128;   // indexer head dim of the training path
 constexpr int kSS = 72;    // G staging row stride (64 heads + 8, bf16)
 
-__device__ __forceinline__ float sum16(float v) {  // sum over the 16 lanes of a lane group
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
+// v of another lane of the same row of 16 lanes (a DPP move: no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a lane group, in every lane of it: the two quad swaps (quad_perm
+// [1,0,3,2] and [2,3,0,1]) sum each quad, rotating the row by 4 and then 8 lanes adds the
+// other three quads.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x128>(v);
   return v;
 }
 
