@@ -58,9 +58,9 @@ __global__ void fill_zero_kernel(float *__restrict__ p, int64_t n) {
 //     transposed row fragment feeds four MFMAs.  They also issue the latent-row tile loads.
 //   contribution phase, waves 4..7 (channel quarter qq): C[32 slots x channels] =
 //     scale dZ^T . q + P^T . dO one chunk behind, with q / dO held as head-contraction
-//     fragments and scale dZ / P staged in LDS as bf16 ([slot][head]), each as a pair hi + lo
-//     (hi = bf16(x), lo = bf16(x - hi), about 16 significant bits): with either rounded to 8
-//     bits a latent row picked by many queries collects an error near the 2e-2 bar.  C is
+//     fragments and scale dZ / P staged in LDS ([slot][head]), all as fp16 under per-row
+//     power-of-two scales (C16Scales: 11 significant bits; with P or dZ rounded to bf16's 8
+//     bits a latent row picked by many queries collects an error near the 2e-2 bar).  C is
 //     stored as 16-bit block floating point (see kStageWords).
 // Tile loads (direct to LDS, waited for with explicit load counts) come from waves that issue no
 // other vector-memory operation, so that those counts stay exact and the compiler's own waits
