@@ -227,10 +227,11 @@ def workload_counts(md_host, cfg, H_i, D_i, K, H, Dqk, Dv, kpool=None):
     )
 
 
-def cpu_baseline(inputs, counts, T, K, budget_s, pool=0):
+def cpu_baseline(inputs, counts, T, K, budget_s, pool=0, kl=False, sink=None):
     """Time the oracle (as it stands) on a bounded sample of the same workload: the longest
-    rows of the last sequence, sized from a small calibration run so that the three stages
-    take about budget_s seconds together; per-stage flop rates extrapolate to the whole step."""
+    rows of the last sequence, sized from a small calibration run so that the stages take
+    about budget_s seconds together; per-stage flop rates extrapolate to the whole step (with
+    `kl`, the indexer's KL loss and backward as a fourth stage, extrapolated per valid slot)."""
     import numpy as np  # noqa: F401
 
     import oracle
@@ -246,7 +247,7 @@ def cpu_baseline(inputs, counts, T, K, budget_s, pool=0):
     q_all, idx_all, ln_all, do_all = inputs["q"], inputs["idx"], inputs["len"], inputs["dout"]
     kv = inputs["kv"].cpu()
     H, Dqk = q_all.shape[1], q_all.shape[2]
-    per_stage = budget_s / 3.0
+    per_stage = budget_s / (4.0 if kl else 3.0)
     max_rows = last - start + 1
 
     def indexer(n):
@@ -270,12 +271,21 @@ def cpu_baseline(inputs, counts, T, K, budget_s, pool=0):
         nvalid = int(ln.sum())
         t0 = time.perf_counter()
         if backward:
-            oracle.sparse_mla_bwd(q, kv, idx, ln, dout, inputs["scale"])
+            oracle.sparse_mla_bwd(q, kv, idx, ln, dout, inputs["scale"], sink=sink)
         else:
-            oracle.sparse_mla_fwd(q, kv, idx, ln, inputs["scale"], 512)
+            oracle.sparse_mla_fwd(q, kv, idx, ln, inputs["scale"], 512, sink=sink)
         dt = time.perf_counter() - t0
         per = (3 * Dqk + 2 * 512) if backward else (Dqk + 512)
         return dt, nvalid * 2.0 * H * per, nvalid
+
+    def kl_loss(n):
+        # target (the attention probabilities, recomputed), loss and the indexer backward
+        r0 = last - n + 1
+        nvalid = int(ln_all[r0:last + 1].sum())
+        t0 = time.perf_counter()
+        oracle.indexer_kl(q_all.cpu(), kv, idx_all.cpu(), ln_all.cpu(), inputs["scale"], q_idx,
+                          k_idx, w, g=1.0, rows=(r0, last + 1))
+        return time.perf_counter() - t0, nvalid
 
     def sized(run, n0):
         dt = run(n0)[0]  # calibration (also warms the library and caches)
@@ -286,11 +296,16 @@ def cpu_baseline(inputs, counts, T, K, budget_s, pool=0):
     n_f, (t_fwd, f_fwd, v_f) = sized(lambda n: attention(n, False), threads)
     n_b, (t_bwd, f_bwd, v_b) = sized(lambda n: attention(n, True), threads)
     idx_rate, fwd_rate, bwd_rate = f_idx / t_idx, f_fwd / t_fwd, f_bwd / t_bwd
+    kl_slot_s = None
+    if kl:
+        n_k, (t_kl, v_kl) = sized(kl_loss, threads)
+        kl_slot_s = t_kl / max(v_kl, 1)  # seconds per valid slot
 
-    def step_seconds(ri, rf, rb):
-        return counts["idx_flops"] / ri + counts["fwd_flops"] / rf + counts["bwd_flops"] / rb
+    def step_seconds(ri, rf, rb, kls=None):
+        return (counts["idx_flops"] / ri + counts["fwd_flops"] / rf + counts["bwd_flops"] / rb
+                + (kls * counts["valid"] if kls else 0.0))
 
-    full_s = step_seconds(idx_rate, fwd_rate, bwd_rate)
+    full_s = step_seconds(idx_rate, fwd_rate, bwd_rate, kl_slot_s)
     # the same oracle on one thread (OpenMP's thread count set through libgomp for the calls
     # below), on samples an eighth of the size
     single = None
@@ -301,12 +316,14 @@ def cpu_baseline(inputs, counts, T, K, budget_s, pool=0):
             t1i, f1i = indexer(max(1, n_i // 8))
             t1f, f1f, _ = attention(max(1, n_f // 8), False)
             t1b, f1b, _ = attention(max(1, n_b // 8), True)
+            t1k, v1k = kl_loss(max(1, n_k // 8)) if kl else (0.0, 1)
         finally:
             gomp.omp_set_num_threads(threads)
         r1 = (f1i / t1i, f1f / t1f, f1b / t1b)
-        single = {"value": T / step_seconds(*r1), "indexer_tflops": r1[0] / 1e12,
+        single = {"value": T / step_seconds(*r1, t1k / max(v1k, 1) if kl else None),
+                  "indexer_tflops": r1[0] / 1e12,
                   "fwd_tflops": r1[1] / 1e12, "bwd_tflops": r1[2] / 1e12,
-                  "seconds": t1i + t1f + t1b}
+                  "seconds": t1i + t1f + t1b + t1k}
     except OSError:
         pass
     cpu_model = None
@@ -325,10 +342,14 @@ def cpu_baseline(inputs, counts, T, K, budget_s, pool=0):
                    f"{'k-pool ' if pool else ''}indexer "
                    f"top-k of {n_i} rows ({t_idx:.1f}s), forward of {n_f} rows / {v_f} valid "
                    f"slots ({t_fwd:.1f}s), backward of {n_b} rows / {v_b} valid slots "
-                   f"({t_bwd:.1f}s); per-stage flop rates extrapolated to the whole step; "
-                   f"single_thread: the same on one thread, samples of an eighth"),
+                   f"({t_bwd:.1f}s)"
+                   + (f", indexer KL loss and backward of {n_k} rows / {v_kl} valid slots "
+                      f"({t_kl:.1f}s, extrapolated per valid slot)" if kl else "")
+                   + "; per-stage flop rates extrapolated to the whole step; "
+                   "single_thread: the same on one thread, samples of an eighth"),
         "indexer_tflops": idx_rate / 1e12, "fwd_tflops": fwd_rate / 1e12,
         "bwd_tflops": bwd_rate / 1e12, "single_thread": single,
+        "indexer_loss_us_per_row": (kl_slot_s * counts["valid"] / T * 1e6) if kl else None,
     }
 
 
@@ -637,7 +658,8 @@ def main():
         inputs.update(idx=idx_buf, len=len_buf)
         try:
             res["cpu_baseline"] = cpu_baseline(inputs, counts, T, K, args.cpu_seconds,
-                                               pool=cfg.pool if kpool else 0)
+                                               pool=cfg.pool if kpool else 0, kl=kl,
+                                               sink=sink.cpu() if sink is not None else None)
         except Exception as e:  # the GPU figure stands on its own
             res["cpu_baseline"] = {"error": repr(e)}
     print(json.dumps(res))
