@@ -227,12 +227,15 @@ def workload_counts(md_host, cfg, H_i, D_i, K, H, Dqk, Dv, kpool=None):
     )
 
 
-def cpu_baseline(inputs, counts, T, K, budget_s, pool=0, kl=False, sink=None):
+def cpu_baseline(inputs, counts, T, K, budget_s, pool=0, kl=False, sink=None, local_rows=None):
     """Time the oracle (as it stands) on a bounded sample of the same workload: the longest
     rows of the last sequence, sized from a small calibration run so that the stages take
     about budget_s seconds together; per-stage flop rates extrapolate to the whole step (with
-    `kl`, the indexer's KL loss and backward as a fourth stage, extrapolated per valid slot)."""
-    import numpy as np  # noqa: F401
+    `kl`, the indexer's KL loss and backward as a fourth stage, extrapolated per valid slot).
+    With `local_rows` (one GPU's query rows under context parallelism, global coordinates)
+    the sample is the last local rows, which lie at the end of the last sequence, and the
+    indexer leg is the oracle's local-query indexer."""
+    import numpy as np
 
     import oracle
 
@@ -241,18 +244,29 @@ def cpu_baseline(inputs, counts, T, K, budget_s, pool=0, kl=False, sink=None):
     k_idx = (inputs["k_pool"] if pool else inputs["k_idx"]).cpu()
     w = inputs["w"].cpu()
     cu = inputs["cu_seqlens"].cpu()
-    last = int(cu[-1]) - 1
     start = int(cu[-2])
+    if local_rows is not None:
+        gl = local_rows.cpu().numpy().astype(np.int64)
+        last = len(gl) - 1  # rows are local: the sample is the last local rows
+        n_tail = int((gl >= start).sum())  # local rows in the last sequence (they end the list)
+        assert (gl[len(gl) - n_tail:] >= start).all()
+    else:
+        last = int(cu[-1]) - 1
     Hi, Di = q_idx.shape[1], q_idx.shape[2]
     q_all, idx_all, ln_all, do_all = inputs["q"], inputs["idx"], inputs["len"], inputs["dout"]
     kv = inputs["kv"].cpu()
     H, Dqk = q_all.shape[1], q_all.shape[2]
     per_stage = budget_s / (4.0 if kl else 3.0)
-    max_rows = last - start + 1
+    max_rows = n_tail if local_rows is not None else last - start + 1
 
     def indexer(n):
         r0 = last - n + 1
         t0 = time.perf_counter()
+        if local_rows is not None:
+            rows_g = gl[r0:last + 1]
+            oracle.indexer_topk_local(q_idx[r0:last + 1], k_idx, w[r0:last + 1], cu, K,
+                                      query_indices=rows_g.astype(np.int32))
+            return time.perf_counter() - t0, float((rows_g - start + 1).sum()) * 2.0 * Hi * Di
         if pool:
             oracle.kpool_indexer(q_idx, k_idx, w, cu, pool, (K - pool + 1) // pool,
                                  rows=(r0, last + 1))
@@ -338,8 +352,10 @@ def cpu_baseline(inputs, counts, T, K, budget_s, pool=0, kl=False, sink=None):
     return {
         "value": T / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "cpu_model": cpu_model,
-        "sample": (f"fp64 oracle on the last rows of the {max_rows}-token sequence: "
-                   f"{'k-pool ' if pool else ''}indexer "
+        "sample": ((f"fp64 oracle on the last of this GPU's {max_rows} local rows of the last "
+                    f"sequence: " if local_rows is not None else
+                    f"fp64 oracle on the last rows of the {max_rows}-token sequence: ")
+                   + f"{'k-pool ' if pool else ''}indexer "
                    f"top-k of {n_i} rows ({t_idx:.1f}s), forward of {n_f} rows / {v_f} valid "
                    f"slots ({t_fwd:.1f}s), backward of {n_b} rows / {v_b} valid slots "
                    f"({t_bwd:.1f}s)"
@@ -654,12 +670,13 @@ def main():
         "components": comp, "kernels": kernels, "roofline": roofline,
         "gather_ceiling": gather_ceiling,
     }
-    if not args.no_cpu_baseline and local_rows is None:
+    if not args.no_cpu_baseline:
         inputs.update(idx=idx_buf, len=len_buf)
         try:
             res["cpu_baseline"] = cpu_baseline(inputs, counts, T, K, args.cpu_seconds,
                                                pool=cfg.pool if kpool else 0, kl=kl,
-                                               sink=sink.cpu() if sink is not None else None)
+                                               sink=sink.cpu() if sink is not None else None,
+                                               local_rows=local_rows)
         except Exception as e:  # the GPU figure stands on its own
             res["cpu_baseline"] = {"error": repr(e)}
     print(json.dumps(res))
