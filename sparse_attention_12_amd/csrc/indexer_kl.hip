@@ -16,8 +16,9 @@
 //   kl_target : S^T = rows . q^T per 32-slot tile of gathered latent rows (as the attention
 //               backward recomputes it), P = exp(S - lse), the head sum per slot (lanes, then
 //               waves through LDS), renormalised over the row -> target [T_q, K] fp32.
-//   kl_bwd    : pass 1 recomputes the indexer scores of the row's slots (16x16x32 MFMAs on
-//               gathered k_idx rows, ReLU, weights and head sum in fp32) into LDS; the row's
+//   kl_bwd    : pass 1 recomputes the indexer scores of the row's slots (32x32x16 MFMAs on
+//               gathered k_idx rows with the heads on the M axis, two waves of 32 heads; ReLU,
+//               weights and head sum in fp32 registers) into LDS; the row's
 //               softmax, loss and dI follow; pass 2 recomputes the dot products, forms
 //               G = dI w [d > 0] and accumulates dq_idx^T += k_idx^T . G^T (transposing reads of
 //               the tile), dw, and the key-gradient contribution C = q_idx^T . G of every slot
@@ -41,21 +42,6 @@ constexpr int kWaves = 4;
 constexpr int kDi = 128;   // indexer head dim of the training path
 constexpr int kSS = 72;    // G staging row stride (64 heads + 8, bf16)
 
-// v of another lane of the same row of 16 lanes (a DPP move: no LDS round trip)
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// Sum over the 16 lanes of a lane group, in every lane of it: the two quad swaps (quad_perm
-// [1,0,3,2] and [2,3,0,1]) sum each quad, rotating the row by 4 and then 8 lanes adds the
-// other three quads.
-__device__ __forceinline__ float sum16(float v) {
-  v += dpp_f32<0xB1>(v);
-  v += dpp_f32<0x4E>(v);
-  v += dpp_f32<0x124>(v);
-  v += dpp_f32<0x128>(v);
-  return v;
-}
 
 __device__ __forceinline__ int rows_rounded(int K) { return (K + kSlots - 1) / kSlots * kSlots; }
 
@@ -277,6 +263,13 @@ __global__ __launch_bounds__(kBwdWaves * 64, 4) void kl_bwd_kernel(
   const bool hok = scorer && h < Hi;
   bf16x8 qf[kDi / 32];
   float wv = 0.0f;
+  // pass 1 (score waves 0 and 1): heads 32 wave .. + 31 on the M axis of 32x32x16 MFMAs, so
+  // that a lane ends with 16 heads of one slot and the head sum is register arithmetic and one
+  // swap with the lane 32 apart.  A: head 32 wave + lane % 32, dims 16 kk + 8 (lane / 32) +
+  // [0, 8); wm: the weights of the heads (i / 4) 8 + (lane / 32) 4 + i % 4 of the output.
+  const bool p1 = wave < 2;
+  bf16x8 qm[kDi / 16];
+  float wm[16];
   // contribution waves: A operands of C^T = q_idx^T . G, dims 32 qd + 16 m + hl, heads
   // 32 kh + 8 g + [0, 8)
   bf16x8 qa[2][2];
@@ -288,8 +281,25 @@ __global__ __launch_bounds__(kBwdWaves * 64, 4) void kl_bwd_kernel(
       qf[ks] = as_bf16x8(v);
     }
     wv = hok ? w[t * Hi + h] : 0.0f;
+    const int hm = 32 * wave + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < kDi / 16; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (p1 && hm < Hi)
+        v = *reinterpret_cast<const u32x4 *>(q_idx + ((t * Hi + hm) * kDi + kk * 16 + (lane >> 5) * 8));
+      qm[kk] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int hh = 32 * wave + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      wm[i] = p1 && hh < Hi ? w[t * Hi + hh] : 0.0f;
+    }
 #pragma unroll
     for (int ks = 0; ks < kDi / 32; ++ks) settle(qf[ks]);
+#pragma unroll
+    for (int kk = 0; kk < kDi / 16; ++kk) settle(qm[kk]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) settle(wm[i]);
   } else {
     const int qd = wave - kBwdScoreWaves;
 #pragma unroll
@@ -328,11 +338,10 @@ __global__ __launch_bounds__(kBwdWaves * 64, 4) void kl_bwd_kernel(
       d[1] = mfma16(fr.a_frag(tile, 1, ks), qf[ks], d[1]);
     }
   };
-  auto gather_part = [&](int c) {  // wave 0: the scores of chunk c from the four score waves
+  auto gather_part = [&](int c) {  // wave 0: the scores of chunk c from the two head halves
     if (wave == 0 && lane < kSlots) {
-      float v = 0.0f;
-#pragma unroll
-      for (int w4 = 0; w4 < kBwdScoreWaves; ++w4) v += part[((c & 1) * kBwdScoreWaves + w4) * kSlots + lane];
+      const float v = part[((c & 1) * kBwdScoreWaves + 0) * kSlots + lane] +
+                      part[((c & 1) * kBwdScoreWaves + 1) * kSlots + lane];
       ibuf[c * kSlots + lane] = slot_rows[c * kSlots + lane] >= 0 ? v : -INFINITY;
     }
   };
@@ -363,15 +372,23 @@ __global__ __launch_bounds__(kBwdWaves * 64, 4) void kl_bwd_kernel(
     acquire(c);
     if (c > 0) gather_part(c - 1);
     if (c + kBwdNBuf - 1 < nch) ts.issue(c + kBwdNBuf - 1, k_idx, slot_rows);
-    f32x4 d[2];
-    dots(smem + (c % kBwdNBuf) * TL::kBytes, d);
+    if (p1) {
+      // D[head][slot] = q_idx . rows^T, B = the tile's row fragments (slot lane % 32, chunk
+      // 2 kk + lane / 32)
+      const unsigned char *tile = smem + (c % kBwdNBuf) * TL::kBytes;
+      f32x16 acc = {};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = sum16(wv * fmaxf(d[mt][i], 0.0f));
-        if (hl == 0) part[((c & 1) * kBwdScoreWaves + wave) * kSlots + mt * 16 + g * 4 + i] = v;
+      for (int kk = 0; kk < kDi / 16; ++kk) {
+        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+            tile + TL::chunk_off(lane & 31, 2 * kk + (lane >> 5))));
+        acc = mfma32(qm[kk], b, acc);
       }
+      float sc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc = fmaf(wm[i], fmaxf(acc[i], 0.0f), sc);
+      sc += swap_halves(sc);  // the other 16 heads of this half
+      if (lane < kSlots) part[((c & 1) * kBwdScoreWaves + wave) * kSlots + lane] = sc;
+    }
   }
   lds_barrier();  // every wave is done with the tiles and with the last chunk's partial scores
   if (nch > 0) gather_part(nch - 1);
