@@ -26,8 +26,9 @@
  *   [PR2388] SkyRL PR 2388 (GLM-5.3-Flash NoPE sparse MLA), "Why", "Change".
  *   [PR2423] SkyRL PR 2423 (query-chunked sparse attention), "Summary".
  *
- * The indexer score itself is not written out on the pages ([GLM52] only says
- * the indexer "scores the query-key relevance" per query); the reading taken is
+ * The indexer score itself is not written out on the pages ([GLM52] "How DSA
+ * works" only describes the indexer as rating how relevant each key is to a query);
+ * the reading taken is
  *     I(t,s) = sum_h w[t,h] * max(0, sum_d q[t,h,d] * k[s,d]),
  * with the head weights used exactly as handed over ([API] cudnn_indexer_topk,
  * head_weights: the caller owns the 1/sqrt(H) and 1/sqrt(D) scaling).
