@@ -139,9 +139,9 @@ int dsa_prepare_local_metadata(const int32_t *cu_seqlens, const int32_t *cu_seql
                                size_t ws_bytes, dsa_thd_metadata *md, void *stream);
 
 /* --------------------------------------------------------------------------
- * k-pool indexer (SkyRL PR 2388, "Why": GLM-5.3-Flash's k-pool selection
- * appends the query's incomplete tail pool, so its top-k width is
- * 2048 + 3 = 2051).  The pool selection is not spelled out on the page.
+ * k-pool indexer (SkyRL PR 2388, "Why": GLM-5.3-Flash selects keys by pools
+ * and adds the still-incomplete pool at the end of the query, which is why its
+ * top-k width is 2048 + 3 = 2051).  The pool selection is not spelled out on the page.
  * Reading implemented: the keys of every sequence form pools of `pool`
  * consecutive keys from the sequence start, and the caller supplies one
  * indexer key per complete pool, k_pool [T_pool, D_i] bf16 with sequence b's
@@ -174,8 +174,8 @@ int dsa_kpool_indexer_topk(const uint16_t *q_idx, const uint16_t *k_pool, const 
                            int32_t *idx, int32_t *len, void *ws, size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
- * Lightning indexer + top-k (GLM-5.2 page, "How DSA works": the indexer
- * scores query-key relevance and emits the top-k token indices per query;
+ * Lightning indexer + top-k (GLM-5.2 page, "How DSA works": the indexer rates
+ * how relevant each key is to a query and hands the k best keys on;
  * API reference cudnn_indexer_topk and _compact_and_sort_indices).
  *
  * Score of query row t and key s of the same sequence with s <= t:
@@ -270,9 +270,9 @@ int dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *idx
                        float *dkv, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
- * Indexer training loss (GLM-5.2 page, "How DSA works": the indexer emits an
- * auxiliary KL loss that aligns its score distribution with the main
- * attention's, on a graph separate from the main model's; "GLM-5.2 training
+ * Indexer training loss (GLM-5.2 page, "How DSA works": an extra KL loss pulls
+ * the indexer's score distribution toward that of the main attention, and it
+ * is trained on a graph of its own; "GLM-5.2 training
  * results": sparse formulation, coefficient 0.001, computed with a
  * score-recompute step and an indexer backward; "cuDNN fused DSA kernels").
  * The pages give no formula.  Reading implemented, for query row t with the

@@ -443,11 +443,11 @@ int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *
 }
 
 /* ------------------------------------------------------------------------ */
-/* Indexer training loss ([GLM52] "How DSA works": the indexer emits an      */
-/* auxiliary KL loss that aligns its score distribution with the main        */
-/* attention's, on a graph separate from the main model's; "GLM-5.2 training  */
-/* results": sparse formulation, coefficient 0.001; "cuDNN fused DSA         */
-/* kernels": a score-recompute kernel feeds the loss).                        */
+/* Indexer training loss ([GLM52] "How DSA works": an extra KL loss pulls the */
+/* indexer's score distribution toward the main attention's, on a graph of   */
+/* its own; "GLM-5.2 training results": sparse formulation, coefficient      */
+/* 0.001; "cuDNN fused DSA kernels": a score-recompute kernel feeds the      */
+/* loss).                                                                     */
 /* ------------------------------------------------------------------------ */
 
 /* The loss formula is not written on the pages.  Reading taken, for query
@@ -601,8 +601,8 @@ int oracle_indexer_kl(const uint16_t *q, const uint16_t *kv, const int32_t *idx,
 }
 
 /* ------------------------------------------------------------------------ */
-/* k-pool indexer ([PR2388] "Why": GLM-5.3-Flash's k-pool selection appends   */
-/* the query's incomplete tail pool, so the top-k width is 2048 + 3 = 2051).  */
+/* k-pool indexer ([PR2388] "Why": GLM-5.3-Flash picks keys by pools and adds */
+/* the query's still-incomplete last pool, hence top-k width 2048 + 3).      */
 /* ------------------------------------------------------------------------ */
 
 /* The pool selection is not spelled out on the pages.  Reading taken: the
