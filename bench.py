@@ -577,10 +577,16 @@ def main():
         v = per_kernel.get(name, [])
         return sum(v) / len(v) if v else float("nan")
 
-    t_idx = avg("indexer_topk")
+    def avg_or_zero(name):
+        v = per_kernel.get(name, [])
+        return sum(v) / len(v) if v else 0.0
+
+    # each kernel's second launch (rows whose speculative threshold or fixed softmax reference
+    # failed are recomputed there) belongs to its stage
+    t_idx = avg("indexer_topk") + avg_or_zero("indexer_topk_redo")
     if kpool:  # the expansion of the selected pools to their keys belongs to the indexer
         t_idx += avg("kpool_expand")
-    t_fwd = avg("sparse_mla_fwd")
+    t_fwd = avg("sparse_mla_fwd") + avg_or_zero("sparse_mla_fwd_redo")
     # the backward's own wall time (its passes overlap on two streams, so kernel times overlap)
     t_bwd = sum(a.elapsed_time(b) for a, b in bwd_events) / len(bwd_events)
     # latent rows gathered per valid slot: once in the forward, twice in the backward (its dq

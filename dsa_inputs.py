@@ -123,6 +123,37 @@ def indexer_inputs(cfg: int, cu_seqlens=None, device="cpu", seed=None):
                 cu_seqlens=cu_seqlens_tensor(w, device), topk=w.topk)
 
 
+def indexer_trend_inputs(cu_seqlens, trend: str, heads=64, dim=128, block=256, device="cpu",
+                         seed=None):
+    """Integer indexer inputs whose scores follow a trend along each sequence.
+
+    Key s at offset p = s - start of its sequence is c(p) * v, with v a fixed vector of 1s and
+    2s and c(p) = max(1, 64 - p // block) ("falling") or min(64, 1 + p // block) ("rising");
+    every query row has entries in [0, 2] with a 1 in its first column and weights from
+    {0.5, 1, 2}, all positive, so a row's scores are c(p) times a positive row constant (exact
+    in fp32).  Falling scores put a row's largest keys at its start, unlike a uniform sample;
+    rising ones at its end.  Shapes as indexer_inputs; cu_seqlens is a list of offsets."""
+    assert trend in ("falling", "rising")
+    cu = [int(x) for x in cu_seqlens]
+    T = cu[-1]
+    g = _gen(seed if seed is not None else SEED_BASE + 0x500, device)
+    v = torch.randint(1, 3, (dim,), generator=g, device=device).to(torch.float32)
+    p = torch.zeros(T, dtype=torch.int64, device=device)
+    for b in range(len(cu) - 1):
+        p[cu[b]:cu[b + 1]] = torch.arange(cu[b + 1] - cu[b], device=device)
+    if trend == "falling":
+        c = torch.clamp(64 - p // block, min=1)
+    else:
+        c = torch.clamp(1 + p // block, max=64)
+    k = (c.to(torch.float32)[:, None] * v[None, :]).to(torch.bfloat16)
+    q = torch.randint(0, 3, (T, heads, dim), generator=g, device=device)
+    q[:, :, 0] = 1
+    choice = torch.randint(0, 3, (T, heads), generator=g, device=device)
+    wt = torch.tensor([0.5, 1.0, 2.0], device=device)[choice].to(torch.float32)
+    return dict(q_idx=q.to(torch.bfloat16).contiguous(), k_idx=k.contiguous(),
+                w=wt.contiguous(), cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=device))
+
+
 def kpool_indexer_inputs(cfg: int, cu_seqlens=None, device="cpu", seed=None, pool=None,
                          heads=64, dim=128, int_inputs=False):
     """k-pool indexer query [T,Hi,Di] bf16, one pooled indexer key per complete pool of each

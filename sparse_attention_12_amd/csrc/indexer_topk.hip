@@ -41,6 +41,7 @@ constexpr int kRows = kIdxRowsPerGroup;  // query rows per work group
 constexpr int kWaves = 2 * kRows;        // two waves per row
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileKeys = 64;
+constexpr int kRedoGroups = 256;  // work groups of the second launch (one per CU)
 // value bins of a compaction: narrower bins collide less in the LDS atomics
 constexpr int kPruneBins = 512;
 
@@ -679,13 +680,34 @@ struct KeyTileLoads {
   }
 };
 
+// Target rank of a compaction of a row of L keys after about ns of them (an upper bound) have
+// been seen.  Without speculation it is K: every entry at or above the K-th largest key so far is
+// kept, which can never drop a key of the final top-K.  With speculation it is the rank x, among
+// the keys seen, of a threshold that the rest of the row is still expected to pass often enough:
+// if the keys seen were a uniform sample of the row's scores, a fraction x / ns of all L keys
+// would lie above the x-th largest, up to a relative sampling error of about 1 / sqrt(x).  x is
+// the smallest rank for which L x / ns, lowered by five such errors, still exceeds K by five
+// standard deviations of a count of K (solving y^2 - 5 y - a = 0 for y = sqrt(x)).  Only the
+// check at the end of the row makes this exact: a row that ends with fewer than K entries above
+// its threshold lost some of its top-K keys and is recomputed without speculation.
+__device__ __forceinline__ int compaction_rank(bool spec, int K, int L, int ns) {
+  if (!spec || ns >= L) return K;
+  const float kf = static_cast<float>(K);
+  const float a = (kf + 5.0f * sqrtf(kf)) * static_cast<float>(ns) / static_cast<float>(L);
+  const float y = 0.5f * (5.0f + sqrtf(25.0f + 4.0f * a));
+  const float x = ceilf(y * y);
+  return x >= kf ? K : max(1, static_cast<int>(x));
+}
+
+// The rows of group g.  spec: compactions may use a speculative target rank (see
+// compaction_rank); a row whose speculation failed gets the length -1 instead of its output.
 template <int NMT, int D>
-__global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
+__device__ __forceinline__ void indexer_group(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
     const int32_t *__restrict__ seq_start, const int32_t *__restrict__ causal_len,
     const int32_t *__restrict__ gpos, const int32_t *__restrict__ groups,
     const int32_t *__restrict__ group_first, int H, int K, int32_t *__restrict__ idx_out,
-    int32_t *__restrict__ len_out) {
+    int32_t *__restrict__ len_out, int g, bool spec) {
   using C = IndexerCfg<D>;
   constexpr int NKK = D / 16;  // k-steps of the 32x32x16 MFMA
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -700,9 +722,9 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   // Rows are local query rows (q, w and the output); key positions are global coordinates of
   // the key tensor.  Without local coordinates (gpos NULL) the two coincide and a group is the
   // run of up to kRows rows that ends at `last`, clipped at the sequence start.
-  const int last = groups[blockIdx.x];
+  const int last = groups[g];
   const int start = seq_start[last];
-  const int first = group_first ? group_first[blockIdx.x]
+  const int first = group_first ? group_first[g]
                                 : (last - (kRows - 1) > start ? last - (kRows - 1) : start);
   const int lastg = gpos ? gpos[last] : last;  // key position of the group's last row
   const int t = first + row;                   // this wave's local row
@@ -876,11 +898,12 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
   // barriers: appends visible | key ranges and cleared histogram | histogram | kept entries and
   // the largest dropped key of each stack | the new threshold and counts.
   //   The keys above the current threshold (all of them before the first one) are binned by
-  // value over [threshold, largest key]; the bin b holding the K-th largest key leaves at least
-  // K keys in bins >= b, so every key in a lower bin lies below the K-th largest and is dropped,
+  // value over [threshold, largest key]; the bin b holding the R-th largest key leaves at least
+  // R keys in bins >= b, so every key in a lower bin lies below the R-th largest and is dropped,
   // and so is any later key that is not above the largest key dropped, which becomes the new
-  // threshold.
-  auto compact_rows = [&]() __attribute__((always_inline)) {
+  // threshold.  R is the row's compaction rank after the keys before kb: K without
+  // speculation, so that no key of the final top-K is dropped.
+  auto compact_rows = [&](int kb) __attribute__((always_inline)) {
     lds_barrier();
     const int n_lo = __builtin_amdgcn_readfirstlane(sm.cnt[row]);
     const int n_hi = __builtin_amdgcn_readfirstlane(sm.cntb[row]);
@@ -910,7 +933,8 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     bool pruned = false;
     if (binned) {
       uint32_t above;
-      const int b = static_cast<int>(bin_from_top_n<kPruneBins>(hist, static_cast<uint32_t>(K), above));
+      const int R = __builtin_amdgcn_readfirstlane(compaction_rank(spec, K, L, kb - start));
+      const int b = static_cast<int>(bin_from_top_n<kPruneBins>(hist, static_cast<uint32_t>(R), above));
       if (b > 0) {
         uint32_t dmax;
         my_n = compact_stack(st, my_n, [vb, b](uint32_t u, int32_t) { return vb(u) >= b; }, dmax);
@@ -1001,7 +1025,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
       if (issue_kb >= 0) loads.issue(tile_lds + issue_buf * C::kTileBytes, k, issue_kb, lastg, wave);
       if (have_prev) sc = score_only(prev);
     }
-    if (__builtin_amdgcn_readfirstlane(cflag)) compact_rows();
+    if (__builtin_amdgcn_readfirstlane(cflag)) compact_rows(kb);
     decide((sidx + 1) & 1);
     ap_sc = sc;  // prev's scores: appended now (lower half) or in the next step (upper half)
     ap_key = key_prev;
@@ -1017,7 +1041,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     float sc = 0.0f;
     if (have_prev) sc = score_only(last_acc);
     lds_barrier();  // every append of the key stream is visible; the flag is written
-    if (__builtin_amdgcn_readfirstlane(sm.compact[sidx & 1])) compact_rows();
+    if (__builtin_amdgcn_readfirstlane(sm.compact[sidx & 1])) compact_rows(start + L);
     append();  // the upper half's pending tile
     ap_sc = sc;
     ap_key = key_prev;
@@ -1051,6 +1075,12 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
     uint32_t *sk = tiles + 4 * 1024 + row * 2 * kScratch;
     int32_t *sp = reinterpret_cast<int32_t *>(sk + kScratch);
     const int n = merge_stacks(my_n, __builtin_amdgcn_readfirstlane(sm.cntb[row]));
+    // Every key above the final threshold is an entry; fewer than K of them means that a
+    // speculative compaction dropped keys of the top-K: the row is left to the second launch.
+    if (n < K) {
+      if (lane == 0) len_out[t] = -1;
+      return;
+    }
     if constexpr (kFinalBins<D> == 1024) {
       select_and_write<1024>(ck, cp, tiles + 6 * 1024 + row * 1024, sm.hist[row], n, K,
                              my_has_tau, my_tau, start, tg, bm, sk, sp,
@@ -1064,16 +1094,70 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
 }
 
 template <int NMT, int D>
+__global__ __launch_bounds__(kThreads) void indexer_topk_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
+    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ causal_len,
+    const int32_t *__restrict__ gpos, const int32_t *__restrict__ groups,
+    const int32_t *__restrict__ group_first, int H, int K, int32_t *__restrict__ idx_out,
+    int32_t *__restrict__ len_out) {
+  indexer_group<NMT, D>(q, k, w, seq_start, causal_len, gpos, groups, group_first, H, K, idx_out,
+                        len_out, blockIdx.x, true);
+}
+
+// Second launch: recomputes, without speculation, every group that has a row of length -1.
+// Each work group checks the groups blockIdx.x + i gridDim.x, 64 at a time (one per lane, the
+// same in every wave, so the decisions are uniform), and then runs the flagged ones.
+template <int NMT, int D>
+__global__ __launch_bounds__(kThreads) void indexer_topk_redo_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
+    const int32_t *__restrict__ seq_start, const int32_t *__restrict__ causal_len,
+    const int32_t *__restrict__ gpos, const int32_t *__restrict__ groups,
+    const int32_t *__restrict__ group_first, int H, int K, int32_t *__restrict__ idx_out,
+    int32_t *__restrict__ len_out, int n_groups) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t base = 0; blockIdx.x + base * gridDim.x < n_groups; base += 64) {
+    const int64_t gl = blockIdx.x + (base + lane) * gridDim.x;
+    bool bad = false;
+    if (gl < n_groups) {
+      const int last = groups[gl];
+      const int start = seq_start[last];
+      const int first = group_first ? group_first[gl]
+                                    : (last - (kRows - 1) > start ? last - (kRows - 1) : start);
+      for (int t = first; t <= last; ++t) bad |= len_out[t] < 0;
+    }
+    uint64_t m = __ballot(bad);
+    while (m != 0u) {
+      const int i = __builtin_ctzll(m);
+      m &= m - 1u;
+      __syncthreads();  // the previous group is done with the LDS
+      indexer_group<NMT, D>(q, k, w, seq_start, causal_len, gpos, groups, group_first, H, K,
+                            idx_out, len_out, static_cast<int>(blockIdx.x + (base + i) * gridDim.x),
+                            false);
+    }
+  }
+}
+
+template <int NMT, int D>
 hipError_t launch(const uint16_t *q, const uint16_t *k, const float *w, const IndexerRows &r,
                   int32_t H, int32_t K, int32_t *idx, int32_t *len, hipStream_t s) {
   const size_t smem = sizeof(IndexerSmem<D>);
   auto kern = indexer_topk_kernel<NMT, D>;
+  auto redo = indexer_topk_redo_kernel<NMT, D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(redo),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
   DSA_LAUNCH("indexer_topk", kern, dim3(r.n_groups), dim3(kThreads), smem, s, q, k, w,
              r.seq_start, r.causal_len, r.gpos, r.groups, r.group_first, H, K, idx, len);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int redo_groups = r.n_groups < kRedoGroups ? r.n_groups : kRedoGroups;
+  DSA_LAUNCH("indexer_topk_redo", redo, dim3(redo_groups), dim3(kThreads), smem, s, q, k, w,
+             r.seq_start, r.causal_len, r.gpos, r.groups, r.group_first, H, K, idx, len,
+             r.n_groups);
   return hipGetLastError();
 }
 

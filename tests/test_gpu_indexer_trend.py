@@ -1,0 +1,100 @@
+"""GPU parity of the indexer on scores with a trend along each sequence.
+
+The indexer's compactions may raise a row's threshold speculatively, from the keys seen so far;
+a row whose later keys score lower than that sample suggests ends with fewer than K keys above
+its threshold and is recomputed by the second launch.  Falling scores force that path on every
+long row, rising ones the opposite (many compactions, no recompute).  Integer inputs make every
+score exact, so the indices must match the oracle bit for bit; for falling scores the answer
+is also known in closed form (the first K keys of the row: ties go to the lower position).
+
+Every input comes from dsa_inputs (seeded); expected values come from oracle/ only.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as gen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+dev = "cuda"
+
+
+def _dsa():
+    import sparse_attention_12_amd as dsa
+    return dsa
+
+
+def _run(inp, K, times=None):
+    """The indexer on inp; with `times` (a dict), the durations of its two launches (ms)."""
+    dsa = _dsa()
+    md = dsa.prepare_thd_metadata(inp["cu_seqlens"].to(dev), K)
+    args = (inp["q_idx"].to(dev), inp["k_idx"].to(dev), inp["w"].to(dev))
+    torch.cuda.synchronize()
+    timer = None
+    if times is not None:
+        from bench import KernelTimer
+        timer = KernelTimer(dsa.lib(), 8)
+        timer.arm()
+    try:
+        idx, ln = dsa.indexer_topk(*args, md, K)
+        torch.cuda.synchronize()
+    finally:
+        if timer is not None:
+            timer.disarm()
+    if timer is not None:
+        times.update({n: sum(v) for n, v in timer.totals().items()})
+    return idx.cpu().numpy(), ln.cpu().numpy()
+
+
+def _sample_rows(cu, n=6):
+    rows = []
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        rows += list(np.unique(np.linspace(s0, s1 - 1, n).astype(np.int64)))
+    return rows
+
+
+# block: keys per score level; a speculative threshold then lands inside a level below the
+# K-th key's, and every key of that level is kept, so K must not be a sum of whole levels that
+# the threshold reaches (with 512 and levels of 256 the kept levels make exactly K)
+@pytest.mark.parametrize("cu,K,block", [([0, 16384], 2048, 256),
+                                        ([0, 3000, 12000, 12001, 20000], 2048, 256),
+                                        ([0, 9000], 512, 64)])
+def test_falling_scores_first_keys(cu, K, block):
+    inp = gen.indexer_trend_inputs(cu, "falling", block=block)
+    times = {}
+    idx, ln = _run(inp, K, times)
+    # the rows long enough to speculate failed and were recomputed: the second launch did real
+    # work (with scores like a uniform sample it takes a hundredth of the first)
+    assert times["indexer_topk_redo"] > 0.2 * times["indexer_topk"], times
+    T = cu[-1]
+    start = np.zeros(T, np.int64)
+    for b in range(len(cu) - 1):
+        start[cu[b]:cu[b + 1]] = cu[b]
+    L = np.arange(T) - start + 1
+    n = np.minimum(L, K)
+    np.testing.assert_array_equal(ln, n)
+    j = np.arange(K)[None, :]
+    exp = np.where(j < n[:, None], start[:, None] + j, -1)
+    np.testing.assert_array_equal(idx, exp)
+    for t in _sample_rows(cu, 3):
+        ridx, rln, _ = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"],
+                                           inp["cu_seqlens"], K, rows=(int(t), int(t) + 1))
+        np.testing.assert_array_equal(idx[t:t + 1], ridx)
+        np.testing.assert_array_equal(ln[t:t + 1], rln)
+
+
+@pytest.mark.parametrize("cu,K", [([0, 16384], 2048), ([0, 5000, 11000], 1024)])
+def test_rising_scores_against_oracle(cu, K):
+    inp = gen.indexer_trend_inputs(cu, "rising")
+    times = {}
+    idx, ln = _run(inp, K, times)
+    assert times["indexer_topk_redo"] < 0.1 * times["indexer_topk"], times
+    for t in _sample_rows(cu, 8):
+        ridx, rln, _ = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"],
+                                           inp["cu_seqlens"], K, rows=(int(t), int(t) + 1))
+        np.testing.assert_array_equal(idx[t:t + 1], ridx, err_msg=f"row {t}")
+        np.testing.assert_array_equal(ln[t:t + 1], rln)
