@@ -187,6 +187,10 @@ int dsa_kpool_indexer_topk(const uint16_t *q_idx, const uint16_t *k_pool, const 
  * Output for row t: the n = min(K, L_t) keys with the largest I (equal scores:
  * lower position first), written as ascending global row positions in
  * idx[t, 0:n], idx[t, n:K] = -1, len[t] = n.  No score matrix is stored.
+ * The call enqueues two kernels on the stream: the second recomputes the rows
+ * for which the first one's speculative candidate threshold proved too high
+ * (between the two, such a row holds len = -1); both outputs are final once
+ * the call's work on the stream has finished.
  *
  *   q_idx [T, H_i, D_i] bf16   k_idx [T, D_i] bf16   w [T, H_i] fp32
  * (with metadata from dsa_prepare_local_metadata: q_idx, w, idx and len have
