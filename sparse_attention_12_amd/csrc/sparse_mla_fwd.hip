@@ -222,6 +222,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_fwd_kernel(
 // PV waves issue the (compiler-invisible) tile loads and only the S waves issue ordinary
 // global loads, so each wave's explicit load-count waits stay exact.
 constexpr int kRoleNBuf = 4;
+constexpr int kRedoGroups = 256;  // work groups of the second launch (one per CU)
 constexpr int kRing = 8;  // slot-index ring (tiles)
 static_assert(kRing == SlotRing::kTiles && kSlots == SlotRing::kSlots, "slot-index ring layout");
 
@@ -236,11 +237,12 @@ struct RoleSmem {
   static constexpr int kBytes = kRingOff + kRing * kSlots * 4;
 };
 
+// One query row t with a running maximum per head (the rows that the fast kernel flagged).
 template <int DQK>
-__global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
+__device__ __forceinline__ void roles_row(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
-    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse, int redo_only) {
+    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse, int64_t t) {
   using TL = Tile<DQK>;
   using SM = RoleSmem<DQK>;
   constexpr int kKSteps = DQK / 32;
@@ -254,14 +256,11 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t t = blockIdx.x;
   const int g = lane >> 4;
   const int hl = lane & 15;
   const int lim = topk_length ? topk_length[t] : K;
   const int32_t *irow = idx + t * K;
   const int nchunks = (lim + kSlots - 1) / kSlots;
-  // redo mode: only the rows that the fast kernel flagged (first LSE entry NaN)
-  if (redo_only && !__builtin_isnan(lse[t * H])) return;
 
   if (wave < 4) {
     // ================================ S waves ================================
@@ -469,6 +468,29 @@ __global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
           *reinterpret_cast<u32x2 *>(orow + n * 16) = v;
         }
       }
+    }
+  }
+}
+
+// Second launch: the rows whose first LSE entry the fast kernel left as NaN.  Each work group
+// checks the rows blockIdx.x + i gridDim.x, 64 at a time (one per lane, the same in every wave,
+// so the decisions are uniform), and computes the flagged ones.
+template <int DQK>
+__global__ __launch_bounds__(512) void sparse_mla_fwd_roles_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ topk_length, int H, int K,
+    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse, int64_t T_q) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t base = 0; blockIdx.x + base * gridDim.x < T_q; base += 64) {
+    const int64_t tl = blockIdx.x + (base + lane) * gridDim.x;
+    const bool flagged = tl < T_q && __builtin_isnan(lse[tl * H]);
+    uint64_t m = __ballot(flagged);
+    while (m != 0u) {
+      const int i = __builtin_ctzll(m);
+      m &= m - 1u;
+      __syncthreads();  // the previous row is done with the LDS
+      roles_row<DQK>(q, kv, idx, topk_length, H, K, scale_log2, out, lse,
+                     blockIdx.x + (base + i) * gridDim.x);
     }
   }
 }
@@ -763,8 +785,9 @@ hipError_t launch_roles(const uint16_t *q, const uint16_t *kv, const int32_t *id
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  DSA_LAUNCH("sparse_mla_fwd_redo", kern, dim3(static_cast<unsigned>(T_q)), dim3(512), smem, s,
-             q, kv, idx, topk_length, H, K, scale * kLog2e, out, lse, 1);
+  const unsigned redo_groups = static_cast<unsigned>(T_q < kRedoGroups ? T_q : kRedoGroups);
+  DSA_LAUNCH("sparse_mla_fwd_redo", kern, dim3(redo_groups), dim3(512), smem, s, q, kv, idx,
+             topk_length, H, K, scale * kLog2e, out, lse, T_q);
   return hipGetLastError();
 }
 
