@@ -81,10 +81,12 @@ static_assert(IndexerCfg<64>::kNBuf * IndexerCfg<64>::kTileBytes >= 4 * (4096 + 
 static_assert(IndexerCfg<128>::kNBuf * IndexerCfg<128>::kTileBytes >= 4 * (4096 + 2048 + 4096),
               "tile area");
 
-// Monotone map float -> uint32 (larger float -> larger key); +0 and -0 map alike.
+// Monotone map float -> uint32 (larger float -> larger key).  -0 would map just below +0; no
+// score is -0: each half-sum starts at +0 and adds fmaf(w, max(x, 0), s) terms, whose exact
+// value is 0 only as w * (+-0) + s with s = +0 (giving +0 in round-to-nearest), and a sum of
+// two such values is -0 only if both are.
 __device__ __forceinline__ uint32_t orderable(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (f == 0.0f) u = 0u;
+  const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
@@ -661,16 +663,18 @@ struct KeyTileLoads {
     }
   }
   // tile_lds: LDS byte address of the destination tile buffer
-  __device__ __forceinline__ void issue(uint32_t tile_lds, const uint16_t *k, int64_t kb,
-                                        int64_t last, int wave) const {
+  // kb, last: key positions (32-bit: the host limits T to INT32_MAX - 4096)
+  __device__ __forceinline__ void issue(uint32_t tile_lds, const uint16_t *k, int kb, int last,
+                                        int wave) const {
     using C = IndexerCfg<D>;
-    const unsigned char *base = reinterpret_cast<const unsigned char *>(k) + kb * (D * 2);
+    const unsigned char *base =
+        reinterpret_cast<const unsigned char *>(k) + static_cast<int64_t>(kb) * (D * 2);
     const uint32_t dst = tile_lds + wave * C::kLoadsPerWave * 1024;
     if (kb + (kTileKeys - 1) <= last) {
 #pragma unroll
       for (int i = 0; i < C::kLoadsPerWave; ++i) dma16_sv(base, voff[i], dst + i * 1024);
     } else {
-      const int lim = static_cast<int>(last - kb);  // in [0, 63)
+      const int lim = last - kb;  // in [0, 63)
 #pragma unroll
       for (int i = 0; i < C::kLoadsPerWave; ++i) {
         const int over = key[i] - lim;
