@@ -98,3 +98,45 @@ def test_rising_scores_against_oracle(cu, K):
                                            inp["cu_seqlens"], K, rows=(int(t), int(t) + 1))
         np.testing.assert_array_equal(idx[t:t + 1], ridx, err_msg=f"row {t}")
         np.testing.assert_array_equal(ln[t:t + 1], rln)
+
+
+def test_kpool_falling_pool_scores_first_pools():
+    """The k-pool indexer (the same kernel over pooled keys, rows in key coordinates) with pool
+    scores falling along the sequence: every row that sees enough pools to speculate is
+    recomputed, and keeps its first K_pools pools, then its tail pool (closed form), equal to
+    the oracle on sampled rows."""
+    dsa = _dsa()
+    T, pool, K_pools = 40000, 4, 512
+    cu = [0, T]
+    n_pools = T // pool
+    kin = gen.indexer_trend_inputs([0, n_pools], "falling", heads=8, block=64)
+    qin = gen.indexer_trend_inputs(cu, "falling", heads=8)
+    q, kp, w = qin["q_idx"], kin["k_idx"], qin["w"]
+    md = dsa.prepare_kpool_metadata(torch.tensor(cu, dtype=torch.int32, device=dev), pool, K_pools)
+    from bench import KernelTimer
+    timer = KernelTimer(dsa.lib(), 8)
+    timer.arm()
+    try:
+        idx_d, ln_d = dsa.kpool_indexer_topk(q.to(dev), kp.to(dev), w.to(dev), md, K_pools)
+        torch.cuda.synchronize()
+    finally:
+        timer.disarm()
+    times = {n: sum(v) for n, v in timer.totals().items()}
+    assert times["indexer_topk_redo"] > 0.2 * times["indexer_topk"], times
+    idx, ln = idx_d.cpu().numpy(), ln_d.cpu().numpy()
+    t = np.arange(T)
+    P = (t + 1) // pool
+    n = np.minimum(P, K_pools)
+    tail = t + 1 - P * pool
+    np.testing.assert_array_equal(ln, n * pool + tail)
+    W = K_pools * pool + pool - 1
+    j = np.arange(W)[None, :]
+    exp = np.where(j < (n * pool)[:, None], j,
+                   np.where(j < (n * pool + tail)[:, None],
+                            (P * pool)[:, None] + j - (n * pool)[:, None], -1))
+    np.testing.assert_array_equal(idx, exp)
+    for r in [0, 2051, 2052, 15000, T - 1]:
+        ridx, rln, _ = oracle.kpool_indexer(q, kp, w, torch.tensor(cu, dtype=torch.int32), pool,
+                                            K_pools, rows=(r, r + 1))
+        np.testing.assert_array_equal(idx[r:r + 1], ridx)
+        np.testing.assert_array_equal(ln[r:r + 1], rln)
