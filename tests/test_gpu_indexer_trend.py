@@ -140,3 +140,33 @@ def test_kpool_falling_pool_scores_first_pools():
                                             K_pools, rows=(r, r + 1))
         np.testing.assert_array_equal(idx[r:r + 1], ridx)
         np.testing.assert_array_equal(ln[r:r + 1], rln)
+
+
+def test_mixed_batch_recomputes_only_failed_groups():
+    """A falling-score sequence packed with a random one: the second launch recomputes the
+    groups of the first sequence and leaves the second alone; both are checked (closed form
+    for the first, the oracle with the near-tie rule on sampled rows of the second)."""
+    from tests import checks
+    L0, L1, K = 16384, 12288, 2048
+    a = gen.indexer_trend_inputs([0, L0], "falling")
+    b = gen.indexer_inputs(3, cu_seqlens=[0, L1])
+    inp = dict(q_idx=torch.cat([a["q_idx"], b["q_idx"]]).contiguous(),
+               k_idx=torch.cat([a["k_idx"], b["k_idx"]]).contiguous(),
+               w=torch.cat([a["w"], b["w"]]).contiguous(),
+               cu_seqlens=torch.tensor([0, L0, L0 + L1], dtype=torch.int32))
+    times = {}
+    idx, ln = _run(inp, K, times)
+    assert times["indexer_topk_redo"] > 0.1 * times["indexer_topk"], times
+    L = np.arange(L0) + 1
+    n = np.minimum(L, K)
+    j = np.arange(K)[None, :]
+    np.testing.assert_array_equal(ln[:L0], n)
+    np.testing.assert_array_equal(idx[:L0], np.where(j < n[:, None], j, -1))
+    rows = np.unique(np.concatenate([np.linspace(L0, L0 + L1 - 1, 12).astype(np.int64),
+                                     [L0 + K - 1, L0 + K, L0 + L1 - 1]]))
+    for t in rows:
+        ridx, rln, kth = oracle.indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"],
+                                             inp["cu_seqlens"], K, rows=(int(t), int(t) + 1))
+        assert ln[t] == rln[0]
+        checks.check_topk_near_tie(inp["q_idx"][t:t + 1], inp["k_idx"], inp["w"][t:t + 1],
+                                   idx[t:t + 1], ridx, kth, np.array([t]))
