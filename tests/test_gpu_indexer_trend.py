@@ -143,9 +143,10 @@ def test_kpool_falling_pool_scores_first_pools():
 
 
 def test_mixed_batch_recomputes_only_failed_groups():
-    """A falling-score sequence packed with a random one: the second launch recomputes the
-    groups of the first sequence and leaves the second alone; both are checked (closed form
-    for the first, the oracle with the near-tie rule on sampled rows of the second)."""
+    """A falling-score sequence packed with a random one: rows of both kinds in one launch,
+    the second launch recomputing the failed groups among them; both sequences are checked
+    (closed form for the first, the oracle with the near-tie rule on sampled rows of the
+    second)."""
     from tests import checks
     L0, L1, K = 16384, 12288, 2048
     a = gen.indexer_trend_inputs([0, L0], "falling")
