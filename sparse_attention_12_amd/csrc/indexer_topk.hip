@@ -22,10 +22,13 @@
 // pruned with one 512-bin counting pass: the bin holding the K-th largest score gives a new
 // tau that never exceeds the true K-th largest score, and every candidate at or below it is
 // dropped.  Keys arrive in ascending position order, so a later key equal to the K-th score
-// would lose the tie to the candidates already kept: the strict test score > tau is exact.  At
-// the end an exact selection (256-bin histograms narrowing the K-th score, ties resolved to the
-// lower positions) keeps exactly K candidates, and a bitmap over the row's key range writes
-// their positions in ascending order.
+// would lose the tie to the candidates already kept: the strict test score > tau is exact.  On
+// long rows a pruning may instead keep fewer than K (compaction_rank): the threshold that a
+// uniform sample of the row would still pass K times over.  At the end an exact selection
+// (histograms narrowing the K-th score, ties resolved to the lower positions) keeps exactly K
+// candidates, and a bitmap over the row's key range writes their positions in ascending order;
+// a row left with fewer than K candidates (a speculative pruning went too far) is marked and
+// recomputed without speculation by a second launch.
 //
 // Rows with L_t <= K select their whole causal prefix, which is written without scoring.
 #include <type_traits>
