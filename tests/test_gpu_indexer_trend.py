@@ -87,6 +87,21 @@ def test_falling_scores_first_keys(cu, K, block):
         np.testing.assert_array_equal(ln[t:t + 1], rln)
 
 
+@pytest.mark.parametrize("heads,dim", [(16, 128), (64, 64), (24, 64)])
+def test_falling_scores_other_shapes(heads, dim):
+    """The kernel instances for up to 32 heads (one 32-row MFMA tile) and for 64-wide indexer
+    keys take the same speculation and second launch: closed form on every row."""
+    cu, K = [0, 12000], 1024
+    inp = gen.indexer_trend_inputs(cu, "falling", heads=heads, dim=dim, block=128)
+    times = {}
+    idx, ln = _run(inp, K, times)
+    assert times["indexer_topk_redo"] > 0.2 * times["indexer_topk"], times
+    n = np.minimum(np.arange(cu[-1]) + 1, K)
+    j = np.arange(K)[None, :]
+    np.testing.assert_array_equal(ln, n)
+    np.testing.assert_array_equal(idx, np.where(j < n[:, None], j, -1))
+
+
 @pytest.mark.parametrize("cu,K", [([0, 16384], 2048), ([0, 5000, 11000], 1024)])
 def test_rising_scores_against_oracle(cu, K):
     inp = gen.indexer_trend_inputs(cu, "rising")
