@@ -186,3 +186,48 @@ def test_mixed_batch_recomputes_only_failed_groups():
         assert ln[t] == rln[0]
         checks.check_topk_near_tie(inp["q_idx"][t:t + 1], inp["k_idx"], inp["w"][t:t + 1],
                                    idx[t:t + 1], ridx, kth, np.array([t]))
+
+
+def test_local_rows_falling_scores_two_ranks():
+    """Local query rows in global padded coordinates (two ranks' zig-zag chunks, padding rows
+    and one masked row) with falling scores: the second launch recomputes the long rows through
+    the local-row metadata; every real row keeps the first K keys of its sequence in padded
+    storage, padding and masked rows are empty."""
+    dsa = _dsa()
+    cu, cu_pad, K = [0, 14000], [0, 14336], 1024
+    T, Tk = cu[-1], cu_pad[-1]
+    inp = gen.indexer_trend_inputs(cu, "falling", block=128)
+    kp = torch.zeros((Tk, inp["k_idx"].shape[1]), dtype=torch.bfloat16)
+    kp[:T] = inp["k_idx"]                       # one sequence from 0: coordinates equal rows
+    kp[T:] = 7.0                                # padding rows: junk that must never be picked
+    chunks = np.array_split(np.arange(T), 4)
+    ranks = [np.concatenate([chunks[0], chunks[3]]), np.concatenate([chunks[1], chunks[2]])]
+    for r, rows in enumerate(ranks):
+        qi = np.concatenate([rows, [14100, 14335]]).astype(np.int32)    # two padding positions
+        qr = torch.cat([inp["q_idx"][rows], inp["q_idx"][:2]]).contiguous()
+        wr = torch.cat([inp["w"][rows], inp["w"][:2]]).contiguous()
+        mask = np.zeros(qi.size, bool)
+        mask[len(rows) // 2] = True
+        md = dsa.prepare_local_metadata(torch.tensor(cu, dtype=torch.int32, device=dev), Tk, K,
+                                        cu_seqlens_padded=torch.tensor(cu_pad, dtype=torch.int32,
+                                                                       device=dev),
+                                        query_indices=torch.from_numpy(qi).to(dev),
+                                        padding_mask=torch.from_numpy(mask).to(dev))
+        from bench import KernelTimer
+        timer = KernelTimer(dsa.lib(), 8)
+        timer.arm()
+        try:
+            idx_d, ln_d = dsa.indexer_topk(qr.to(dev), kp.to(dev), wr.to(dev), md, K)
+            torch.cuda.synchronize()
+        finally:
+            timer.disarm()
+        times = {n: sum(v) for n, v in timer.totals().items()}
+        assert times["indexer_topk_redo"] > 0.1 * times["indexer_topk"], times
+        idx, ln = idx_d.cpu().numpy(), ln_d.cpu().numpy()
+        n = np.minimum(qi.astype(np.int64) + 1, K)
+        n[len(rows):] = 0
+        n[len(rows) // 2] = 0
+        j = np.arange(K)[None, :]
+        np.testing.assert_array_equal(ln, n, err_msg=f"rank {r} lengths")
+        np.testing.assert_array_equal(idx, np.where(j < n[:, None], j, -1),
+                                      err_msg=f"rank {r} indices")
