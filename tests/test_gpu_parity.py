@@ -280,6 +280,59 @@ def test_bwd_passes_over_two_staging_buffers(rows_per_pass):
     checks.assert_close("dkv", _np(dkv2), rdkv, checks.ATOL_OUT)
 
 
+def test_fwd_bwd_wide_dynamic_range():
+    """Rows of q, dO and the latent rows scaled by powers of two over several octaves: the
+    backward's per-row fp16 operand scales (largest |q| and |dO| of the row, largest |kv|) and
+    the 16-bit block staging must keep every row's relative accuracy.  Each tensor is compared
+    row by row against the oracle, relative to that row's largest magnitude (the absolute bar
+    of the other tests assumes unit-scale values)."""
+    dsa = _dsa()
+    T, H, Dqk, K = 300, 64, 576, 128
+    g = torch.Generator().manual_seed(4242)
+    qs = torch.pow(2.0, torch.randint(-5, 4, (T, 1, 1), generator=g).float())
+    ds = torch.pow(2.0, torch.randint(-6, 7, (T, 1, 1), generator=g).float())
+    ks = torch.pow(2.0, torch.randint(-3, 3, (T, 1), generator=g).float())
+    q = (torch.randn((T, H, Dqk), generator=g) * 0.5 * qs).to(torch.bfloat16)
+    kv = (torch.randn((T, Dqk), generator=g) * 0.5 * ks).to(torch.bfloat16)
+    dout = (torch.randn((T, H, 512), generator=g) * ds).to(torch.bfloat16)
+    idx = _random_indices(T, T, K, K, 4242)
+    scale = 1.0 / math.sqrt(Dqk)
+    idx_t = torch.from_numpy(idx).to(dev)
+    out, lse = dsa.sparse_mla_fwd(q.to(dev), kv.to(dev), idx_t, scale)
+    dq, dkv = dsa.sparse_mla_bwd(q.to(dev), kv.to(dev), idx_t, out, lse, dout.to(dev), scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_mla_fwd(q, kv, idx, None, scale, 512)
+    rdq, rdkv = oracle.sparse_mla_bwd(q, kv, idx, None, dout, scale)
+    checks.assert_close("lse", _np(lse), rl, checks.ATOL_LSE)
+
+    def rel_rows(name, got, ref, tol, floor):
+        """Row error within tol of the row's largest |ref|, or of `floor` (the size of one
+        term of the row before cancellation) where the row cancels to about zero."""
+        got = got.reshape(got.shape[0], -1).astype(np.float64)
+        ref = ref.reshape(ref.shape[0], -1).astype(np.float64)
+        assert np.isfinite(got).all(), f"{name}: non-finite values"
+        err = np.abs(got - ref).max(1)
+        lim = tol * np.maximum(np.abs(ref).max(1), floor)
+        zero = lim == 0.0                      # rows that no slot touches: exactly zero
+        assert (err[zero] == 0.0).all(), f"{name}: nonzero values in rows that must be zero"
+        worst = float((err[~zero] / lim[~zero]).max()) * tol if (~zero).any() else 0.0
+        print(f"{name}: worst row error {worst:.3e} of its scale")
+        assert (err[~zero] <= lim[~zero]).all(), f"{name}: worst row error {worst:.3e} of its scale"
+
+    # dq of (t, h) cancels to about zero where the softmax is peaked; there its error is set by
+    # Delta = dO . O formed from the bf16 output (each term rounded by up to 2^-9 of itself),
+    # which enters dq as scale * dDelta * sum_j P_j kv_j: the floor below is 4 times that bound
+    kf = oracle._np(kv.float(), np.float64)
+    of = _np(out.float()).astype(np.float64)
+    dfl = oracle._np(dout.float(), np.float64)
+    d_delta = 2.0 ** -9 * np.abs(dfl * of).sum(-1)                       # [T, H]
+    dq_floor = 4.0 * scale * d_delta * np.abs(kf).max() / 1e-2
+    rel_rows("out", _np(out.float()), ro, 1e-2, 0.0)
+    rel_rows("dq", _np(dq.float()).reshape(T * H, -1), rdq.reshape(T * H, -1), 1e-2,
+             dq_floor.reshape(-1))
+    rel_rows("dkv", _np(dkv), rdkv, 2e-2, 0.0)
+
+
 def test_tiny_workload_end_to_end():
     """Tiny workload: indexer (bit-exact) -> forward -> backward vs the oracle."""
     dsa = _dsa()
