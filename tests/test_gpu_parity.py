@@ -195,7 +195,10 @@ def _fwd_bwd_case(T, H, Dqk, K, n_valid, seed, minus_one_frac=0.0, use_len=False
 
 @pytest.mark.parametrize("T,H,Dqk,K,n_valid", [(96, 16, 576, 64, 64), (200, 64, 576, 128, 77),
                                                (130, 8, 512, 75, 70), (64, 20, 576, 40, 33),
-                                               (50, 64, 512, 2051, 2051)])
+                                               (50, 64, 512, 2051, 2051),
+                                               # head counts at the kernels' boundaries
+                                               (70, 1, 576, 40, 40), (70, 32, 512, 64, 50),
+                                               (70, 33, 576, 64, 64), (70, 48, 576, 96, 90)])
 def test_fwd_bwd_matches_oracle(T, H, Dqk, K, n_valid):
     _fwd_bwd_case(T, H, Dqk, K, n_valid, seed=T * 7 + H)
 
