@@ -120,11 +120,13 @@ def test_indexer_float_inputs_near_tie(cu, K, H, D):
                                    idx[t:t + 1], ridx, kth, np.array([t]))
 
 
-def test_indexer_integer_inputs_thd_long_rows_bit_exact():
-    """Integer inputs over long rows (many compaction rounds) and several sequences: exact."""
+@pytest.mark.parametrize("H,D", [(64, 128), (1, 128), (32, 64), (33, 128)])
+def test_indexer_integer_inputs_thd_long_rows_bit_exact(H, D):
+    """Integer inputs over long rows (many compaction rounds) and several sequences: exact; at
+    the head counts and key widths where the kernel instances change."""
     cu = [0, 70, 2500, 2501, 9000]
     g = torch.Generator().manual_seed(77)
-    T, H, D, K = cu[-1], 64, 128, 512
+    T, K = cu[-1], 512
     q = torch.randint(-4, 5, (T, H, D), generator=g).to(torch.bfloat16)
     k = torch.randint(-4, 5, (T, D), generator=g).to(torch.bfloat16)
     w = torch.tensor([0.5, 1.0, 2.0, 0.25])[torch.randint(0, 4, (T, H), generator=g)]
